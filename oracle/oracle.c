@@ -1,0 +1,354 @@
+/*
+ * CPU ORACLE for error-feedback gradient compression.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, single-threaded
+ * statement of what the GPU library must compute.  Only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may load it; the GPU library never
+ * does, and this file includes nothing from it.
+ *
+ * Build:  gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * x86-64 scalar SSE float arithmetic is IEEE binary32, round to nearest even,
+ * with subnormals kept (no FTZ/DAZ), so every float expression below rounds
+ * exactly once per operation and no multiply is fused into an add.
+ *
+ * Sources ("pages"):
+ *   [SPARSE] "梯度稀疏化：只传输重要的梯度元素" (gradient sparsification: send only
+ *            the important gradient elements).
+ *   [ONEBIT] "1bit Adam梯度压缩技术原理与分布式训练优化" (1-bit Adam gradient
+ *            compression and distributed training).
+ *
+ * Readings taken where the pages leave a step open are marked READING.
+ * Every function here has a pin in tests/ (brute force, closed forms,
+ * invariants or an independent library routine); none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_EINVAL 1
+#define ORC_ENOMEM 2
+
+static uint32_t f2u(float x) { uint32_t u; memcpy(&u, &x, 4); return u; }
+
+/* Magnitude key: the IEEE bit pattern without its sign bit.  For finite
+ * values it orders exactly like |x| (+0 and -0 share key 0); +inf sits above
+ * every finite value and NaN above +inf.
+ * READING: the pages rank by absolute value and never say how to compare
+ * +-0, inf or NaN; this key gives every value a fixed place. */
+static uint32_t mag_key(float x) { return f2u(x) & 0x7fffffffu; }
+
+static int is_nonfinite(float x) { return (f2u(x) & 0x7f800000u) == 0x7f800000u; }
+
+typedef struct { uint32_t key; int64_t i; } ranked;
+
+/* Ranking order of the selection: larger magnitude first; equal magnitudes
+ * are ranked by lower index first.
+ * READING: the pages do not say which of several equal magnitudes survives;
+ * lower index first makes the kept set unique. */
+static int rank_cmp(const void* pa, const void* pb) {
+    const ranked* a = (const ranked*)pa;
+    const ranked* b = (const ranked*)pb;
+    if (a->key != b->key) return a->key > b->key ? -1 : 1;
+    if (a->i != b->i) return a->i < b->i ? -1 : 1;
+    return 0;
+}
+
+/*
+ * Top-k sparsification with error feedback, one tensor.
+ * [SPARSE] "详细算法流程：带误差补偿的Top-k稀疏化" (step-by-step algorithm),
+ * steps 2-4, and "必不可少的误差补偿" (error compensation):
+ *   x = g + e                        (add the carried residual back)
+ *   keep the k entries of largest |x|, zero the others  ->  x~
+ *   e' = x - x~                      (what was not sent this step)
+ * [SPARSE] "梯度稀疏化的基本原理" step 3 and "Top-k 稀疏化": the message is the
+ * k kept values plus their int32 positions.
+ * READINGS: the sent value is x (residual included), not the raw g; indices
+ * are written in ascending order; at a kept position e' is exactly +0.0
+ * (x - x evaluated exactly); 0 <= k <= n.
+ * Returns the count of non-finite x in *nonfinite (may be NULL).
+ */
+int orc_topk(const float* g, float* e, int64_t n, int64_t k,
+             float* vals, int32_t* idx, uint32_t* nonfinite) {
+    if (n < 0 || k < 0 || k > n || n > 0x7fffffffLL) return ORC_EINVAL;
+    float* x = (float*)malloc((size_t)(n ? n : 1) * sizeof(float));
+    ranked* order = (ranked*)malloc((size_t)(n ? n : 1) * sizeof(ranked));
+    unsigned char* keep = (unsigned char*)calloc((size_t)(n ? n : 1), 1);
+    if (!x || !order || !keep) { free(x); free(order); free(keep); return ORC_ENOMEM; }
+
+    uint32_t bad = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        x[i] = g[i] + e[i];
+        bad += (uint32_t)is_nonfinite(x[i]);
+        order[i].key = mag_key(x[i]);
+        order[i].i = i;
+    }
+    qsort(order, (size_t)n, sizeof(ranked), rank_cmp);
+    for (int64_t j = 0; j < k; ++j) keep[order[j].i] = 1;
+
+    int64_t out = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (keep[i]) {
+            vals[out] = x[i];
+            idx[out] = (int32_t)i;
+            ++out;
+            e[i] = 0.0f;
+        } else {
+            e[i] = x[i];
+        }
+    }
+    if (nonfinite) *nonfinite = bad;
+    free(x); free(order); free(keep);
+    return ORC_OK;
+}
+
+/*
+ * Layer-wise top-k: every tensor of a packed gradient is sparsified on its own
+ * with its own k.  [SPARSE] "分层阈值与自适应稀疏率" and "分层自适应Top-k"
+ * (per-layer top-k); [ONEBIT] "4.2 通信协议优化" item 1 (many tensors packed
+ * into one contiguous buffer).
+ * seg_off[nseg+1] are element offsets into the packed buffer, seg_k[nseg] the
+ * per-tensor k.  Outputs are concatenated in tensor order.
+ * READING: indices are positions in the packed buffer (tensor offset + local).
+ */
+int orc_topk_segmented(const float* g, float* e, int32_t nseg,
+                       const int64_t* seg_off, const int64_t* seg_k,
+                       float* vals, int32_t* idx, uint32_t* nonfinite) {
+    if (nseg < 0) return ORC_EINVAL;
+    int64_t out = 0;
+    uint32_t bad_total = 0;
+    for (int32_t s = 0; s < nseg; ++s) {
+        int64_t off = seg_off[s], n = seg_off[s + 1] - seg_off[s], k = seg_k[s];
+        uint32_t bad = 0;
+        int rc = orc_topk(g + off, e + off, n, k, vals + out, idx + out, &bad);
+        if (rc) return rc;
+        for (int64_t j = 0; j < k; ++j) idx[out + j] += (int32_t)off;
+        out += k;
+        bad_total += bad;
+    }
+    if (nonfinite) *nonfinite = bad_total;
+    return ORC_OK;
+}
+
+/*
+ * 1-bit sign compression with an averaged error buffer and momentum.
+ * [ONEBIT] "2.1 量化与误差补偿机制" (quantisation and error compensation):
+ *   q     = sign(g + e)
+ *   delta = (g + e) - q
+ *   e'    = beta1 * e + (1 - beta1) * delta
+ * [ONEBIT] "2.2 动量修正策略" (momentum correction):
+ *   m'    = beta1 * m + (1 - beta1) * q
+ * [ONEBIT] "3.2 核心算法实现细节" (implementation details): the gradient is
+ * clipped to +-clip (5.0 by default) before quantisation, a NaN check follows
+ * the error update, the quantised gradient is stored as int8; the error update
+ * is written as (e * beta1) + (delta * (1 - beta1)).
+ * [ONEBIT] "1. 梯度压缩技术背景": 32 bits become 1 bit per element.
+ * READINGS: the clip applies to the raw gradient before e is added; sign(+-0)
+ * and sign(NaN) are 0; each product and each sum is rounded to float32 on its
+ * own (no fused multiply-add); (1 - beta1) is itself a float32 value; the
+ * packed bit is 1 exactly when q = +1, least significant bit first, pad bits
+ * zero; non-finite e' and m' are counted, not trapped.
+ * sign_out and bits may be NULL.
+ */
+int orc_sign(const float* g, float* e, float* m, int64_t n, float beta1, float clip,
+             int8_t* sign_out, uint8_t* bits, uint32_t* nonfinite) {
+    if (n < 0) return ORC_EINVAL;
+    const float c = 1.0f - beta1;
+    uint32_t bad = 0;
+    if (bits) memset(bits, 0, (size_t)((n + 7) / 8));
+    for (int64_t i = 0; i < n; ++i) {
+        float gi = g[i];
+        if (gi > clip) gi = clip;
+        else if (gi < -clip) gi = -clip;
+        float x = gi + e[i];
+        int s = (x > 0.0f) - (x < 0.0f);
+        float q = (float)s;
+        float delta = x - q;
+        float ea = beta1 * e[i];
+        float eb = c * delta;
+        float en = ea + eb;
+        float ma = beta1 * m[i];
+        float mb = c * q;
+        float mn = ma + mb;
+        e[i] = en;
+        m[i] = mn;
+        bad += (uint32_t)is_nonfinite(en) + (uint32_t)is_nonfinite(mn);
+        if (sign_out) sign_out[i] = (int8_t)s;
+        if (bits && s == 1) bits[i >> 3] |= (uint8_t)(1u << (i & 7));
+    }
+    if (nonfinite) *nonfinite = bad;
+    return ORC_OK;
+}
+
+/*
+ * Receiver-side aggregation: the values of all packets are added into the
+ * dense buffer at their indices.  [SPARSE] "梯度稀疏化的基本原理" (sum the
+ * values that share an index) and "详细算法流程" step 6.
+ * Packet p occupies entries [pk_off[p], pk_off[p+1]) of vals/idx.
+ * READINGS: G keeps its previous contents (the caller zeroes it); additions to
+ * one index happen in packet order, one rounding each.
+ */
+int orc_decode(float* G, int64_t n, int32_t npk, const float* vals,
+               const int32_t* idx, const int64_t* pk_off) {
+    if (n < 0 || npk < 0) return ORC_EINVAL;
+    for (int32_t p = 0; p < npk; ++p) {
+        for (int64_t j = pk_off[p]; j < pk_off[p + 1]; ++j) {
+            int64_t i = idx[j];
+            if (i < 0 || i >= n) return ORC_EINVAL;
+            G[i] = G[i] + vals[j];
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Parameter update with the aggregated gradient: w = w - lr * G.
+ * [SPARSE] "详细算法流程" step 7.
+ * READING: lr * G is rounded to float32, then subtracted (two roundings).
+ */
+int orc_sgd(float* w, const float* G, int64_t n, float lr) {
+    if (n < 0) return ORC_EINVAL;
+    for (int64_t i = 0; i < n; ++i) {
+        float step = lr * G[i];
+        w[i] = w[i] - step;
+    }
+    return ORC_OK;
+}
+
+/*
+ * Bitmap index encoding: one bit per element position.
+ * [SPARSE] "索引编码压缩" (index encoding), the bitmap item.
+ * READING: bit (i mod 8) of byte i/8, least significant bit first; ceil(n/8)
+ * bytes; pad bits zero.
+ */
+int orc_bitmap_encode(const int32_t* idx, int64_t k, int64_t n, uint8_t* bits) {
+    if (n < 0 || k < 0) return ORC_EINVAL;
+    memset(bits, 0, (size_t)((n + 7) / 8));
+    for (int64_t j = 0; j < k; ++j) {
+        int64_t i = idx[j];
+        if (i < 0 || i >= n) return ORC_EINVAL;
+        bits[i >> 3] |= (uint8_t)(1u << (i & 7));
+    }
+    return ORC_OK;
+}
+
+/* Decode: every set bit, in ascending position.  Writes at most k_cap indices;
+ * the number of set bits goes to *k_out. */
+int orc_bitmap_decode(const uint8_t* bits, int64_t n, int32_t* idx, int64_t k_cap, int64_t* k_out) {
+    if (n < 0 || k_cap < 0) return ORC_EINVAL;
+    int64_t k = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (bits[i >> 3] & (1u << (i & 7))) {
+            if (k < k_cap) idx[k] = (int32_t)i;
+            ++k;
+        }
+    }
+    *k_out = k;
+    return ORC_OK;
+}
+
+/*
+ * Delta + variable-length index encoding.
+ * [SPARSE] "索引编码压缩", the run-length / delta item: differences of
+ * consecutive indices, each written with a variable number of bytes.
+ * READINGS: the first difference is taken from 0; raw differences (no -1);
+ * each difference is an unsigned LEB128 number (7 value bits per byte, low
+ * group first, high bit set on every byte but the last), minimal length.
+ * Requires strictly increasing indices >= 0.  *nbytes gets the stream length.
+ */
+int orc_delta_encode(const int32_t* idx, int64_t k, uint8_t* out, int64_t* nbytes) {
+    if (k < 0) return ORC_EINVAL;
+    int64_t pos = 0;
+    int64_t prev = 0;
+    for (int64_t j = 0; j < k; ++j) {
+        int64_t cur = idx[j];
+        if (cur < 0 || (j > 0 && cur <= prev)) return ORC_EINVAL;
+        uint32_t d = (uint32_t)(cur - prev);
+        for (;;) {
+            uint8_t byte = (uint8_t)(d & 0x7fu);
+            d >>= 7;
+            if (d) { out[pos++] = (uint8_t)(byte | 0x80u); }
+            else   { out[pos++] = byte; break; }
+        }
+        prev = cur;
+    }
+    *nbytes = pos;
+    return ORC_OK;
+}
+
+/* Decode k differences and sum them back into indices. */
+int orc_delta_decode(const uint8_t* in, int64_t nbytes, int64_t k, int32_t* idx) {
+    if (k < 0 || nbytes < 0) return ORC_EINVAL;
+    int64_t pos = 0;
+    int64_t acc = 0;
+    for (int64_t j = 0; j < k; ++j) {
+        uint64_t d = 0;
+        int shift = 0;
+        for (;;) {
+            if (pos >= nbytes || shift > 28) return ORC_EINVAL;
+            uint8_t byte = in[pos++];
+            d |= (uint64_t)(byte & 0x7fu) << shift;
+            shift += 7;
+            if (!(byte & 0x80u)) break;
+        }
+        acc += (int64_t)d;
+        if (acc > 0x7fffffffLL) return ORC_EINVAL;
+        idx[j] = (int32_t)acc;
+    }
+    return ORC_OK;
+}
+
+/*
+ * Block-sparse index encoding with 256-element blocks.
+ * [SPARSE] "索引编码压缩", the block item: one bit marks whether a block holds
+ * any kept element; positions inside a block are sent only for blocks that
+ * hold some.
+ * READINGS: nb = ceil(n/256) blocks; mask bit b (least significant first,
+ * ceil(nb/8) bytes) is set iff block b is non-empty; for each non-empty block
+ * in ascending order one byte holds (count - 1); each kept index contributes
+ * one byte (index - 256*block), in index order.  Values keep index order.
+ * Requires strictly increasing indices in [0, n).  *nblk = non-empty blocks.
+ */
+int orc_blocks_encode(const int32_t* idx, int64_t k, int64_t n, uint8_t* mask,
+                      uint8_t* counts_m1, uint8_t* offs, int64_t* nblk) {
+    if (n < 0 || k < 0) return ORC_EINVAL;
+    int64_t nb = (n + 255) / 256;
+    memset(mask, 0, (size_t)((nb + 7) / 8));
+    int64_t blocks = 0;
+    int64_t j = 0;
+    while (j < k) {
+        int64_t i = idx[j];
+        if (i < 0 || i >= n || (j > 0 && i <= idx[j - 1])) return ORC_EINVAL;
+        int64_t b = i / 256;
+        int64_t cnt = 0;
+        while (j < k && idx[j] / 256 == b) {
+            if (idx[j] >= n || (cnt > 0 && idx[j] <= idx[j - 1])) return ORC_EINVAL;
+            offs[j] = (uint8_t)(idx[j] - 256 * b);
+            ++cnt;
+            ++j;
+        }
+        mask[b >> 3] |= (uint8_t)(1u << (b & 7));
+        counts_m1[blocks++] = (uint8_t)(cnt - 1);
+    }
+    *nblk = blocks;
+    return ORC_OK;
+}
+
+/* Inverse of orc_blocks_encode: rebuilds k ascending indices.  k_cap bounds the
+ * output; *k_out gets the number of indices the stream describes. */
+int orc_blocks_decode(const uint8_t* mask, const uint8_t* counts_m1, const uint8_t* offs,
+                      int64_t n, int32_t* idx, int64_t k_cap, int64_t* k_out) {
+    if (n < 0 || k_cap < 0) return ORC_EINVAL;
+    int64_t nb = (n + 255) / 256;
+    int64_t blocks = 0, k = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+        if (!(mask[b >> 3] & (1u << (b & 7)))) continue;
+        int64_t cnt = (int64_t)counts_m1[blocks++] + 1;
+        for (int64_t t = 0; t < cnt; ++t, ++k) {
+            if (k < k_cap) idx[k] = (int32_t)(256 * b + offs[k]);
+        }
+    }
+    *k_out = k;
+    return ORC_OK;
+}
