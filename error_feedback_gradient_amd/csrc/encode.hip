@@ -1,0 +1,555 @@
+// Index encodings of sparse packets, gfx950.
+//
+// "Gradient sparsification" page, index-encoding section: a bitmap with one
+// bit per position, differences of consecutive indices in a variable-length
+// code, and block-sparse marking (one bit per block, in-block positions only
+// for non-empty blocks).
+//
+// Every variable-length output is built in three steps so that it is
+// deterministic: per-chunk counts (one block per 4096 items), an exclusive
+// scan of the chunk counts, then an ordered write where each thread owns 16
+// consecutive items and a block scan gives its output offset.
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace efg {
+namespace enc {
+
+constexpr int kBlock = 256;
+constexpr int kPer = 16;
+constexpr int kChunk = kBlock * kPer;  // items per block-unit
+constexpr int kMaxGrid = 4096;
+constexpr int kScanBlock = 1024;
+
+inline unsigned grid_for(int64_t items, int64_t per_block) {
+    int64_t g = cdiv(std::max<int64_t>(items, 1), per_block);
+    return static_cast<unsigned>(std::min<int64_t>(g, kMaxGrid));
+}
+
+__global__ void k_zero_u32(uint32_t* p) { *p = 0; }
+
+__global__ __launch_bounds__(kBlock) void k_fill_bytes(uint8_t* __restrict__ p, int64_t n, uint8_t v) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    const int64_t head = std::min<int64_t>(n, (16 - (reinterpret_cast<uintptr_t>(p) & 15u)) & 15u);
+    const int64_t nv = (n - head) / 16;
+    const uint32_t w = 0x01010101u * v;
+    uint4* p4 = reinterpret_cast<uint4*>(p + head);
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nv; i += stride)
+        p4[i] = make_uint4(w, w, w, w);
+    if (blockIdx.x == 0) {
+        if (threadIdx.x < head) p[threadIdx.x] = v;
+        for (int64_t i = head + nv * 16 + threadIdx.x; i < n; i += kBlock) p[i] = v;
+    }
+}
+
+// Exclusive scan in place of a[0..m) (uint32 or uint64); total -> *tot (if set)
+// and, converted, -> *tot64 (if set).
+template <typename T>
+__global__ __launch_bounds__(kScanBlock) void k_scan(T* __restrict__ a, int64_t m, T* __restrict__ tot,
+                                                     int64_t* __restrict__ tot64) {
+    __shared__ T lds[kScanBlock / kWave + 1];
+    const int64_t per = (m + kScanBlock - 1) / kScanBlock;
+    const int64_t i0 = std::min<int64_t>(m, per * threadIdx.x), i1 = std::min<int64_t>(m, i0 + per);
+    T sum = 0;
+    for (int64_t i = i0; i < i1; ++i) sum += a[i];
+    T total;
+    T run = block_excl_scan<kScanBlock>(sum, lds, &total);
+    for (int64_t i = i0; i < i1; ++i) {
+        const T t = a[i];
+        a[i] = run;
+        run += t;
+    }
+    if (threadIdx.x == 0) {
+        if (tot) *tot = total;
+        if (tot64) *tot64 = static_cast<int64_t>(total);
+    }
+}
+
+// ------------------------------------------------------------------ bitmap
+__global__ __launch_bounds__(kBlock) void k_bitmap_set(const int32_t* __restrict__ idx, int64_t k, int64_t n,
+                                                       uint8_t* __restrict__ bits) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < k; j += stride) {
+        const int64_t i = idx[j];
+        if (i < 0 || i >= n) continue;
+        const int64_t byte = i >> 3;
+        if (j > 0) {
+            const int64_t ip = idx[j - 1];
+            if (ip >= 0 && ip < n && (ip >> 3) == byte) continue;  // not the first entry of its byte
+        }
+        uint32_t v = 0;
+        for (int64_t t = j; t < k && t < j + 8; ++t) {
+            const int64_t it = idx[t];
+            if (it < 0 || it >= n || (it >> 3) != byte) break;
+            v |= 1u << (it & 7);
+        }
+        bits[byte] = static_cast<uint8_t>(v);
+    }
+}
+
+// per-chunk popcount of bytes [c*kChunk, ...) limited to nbits bits
+__device__ __forceinline__ uint32_t byte_bits(const uint8_t* bits, int64_t nbits, int64_t byte) {
+    if (byte * 8 >= nbits) return 0;
+    uint32_t v = bits[byte];
+    const int64_t valid = nbits - byte * 8;
+    if (valid < 8) v &= (1u << valid) - 1u;
+    return v;
+}
+
+__global__ __launch_bounds__(kBlock) void k_bm_count(const uint8_t* __restrict__ bits, int64_t nbits,
+                                                     int64_t nchunks, uint32_t* __restrict__ cnt) {
+    __shared__ uint32_t lds[kBlock / kWave + 1];
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        uint32_t s = 0;
+        const int64_t b0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) s += __popc(byte_bits(bits, nbits, b0 + t));
+        uint32_t total;
+        block_excl_scan<kBlock>(s, lds, &total);
+        if (threadIdx.x == 0) cnt[c] = total;
+    }
+}
+
+// writes set-bit positions (plus `add`, as int32) at out[off ...], bounded by cap;
+// with `blk` set the positions go to a uint32 list instead
+__global__ __launch_bounds__(kBlock) void k_bm_write(const uint8_t* __restrict__ bits, int64_t nbits,
+                                                     int64_t nchunks, const uint32_t* __restrict__ cnt,
+                                                     int32_t* __restrict__ out, int64_t cap) {
+    __shared__ uint32_t lds[kBlock / kWave + 1];
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t b0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t v[kPer];
+        uint32_t s = 0;
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            v[t] = byte_bits(bits, nbits, b0 + t);
+            s += __popc(v[t]);
+        }
+        uint32_t total;
+        int64_t pos = static_cast<int64_t>(cnt[c]) + block_excl_scan<kBlock>(s, lds, &total);
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            uint32_t w = v[t];
+            while (w) {
+                const int b = __ffs(w) - 1;
+                w &= w - 1;
+                if (pos < cap) out[pos] = static_cast<int32_t>((b0 + t) * 8 + b);
+                ++pos;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ delta
+__device__ __forceinline__ uint32_t leb_len(uint32_t d) {
+    return d < (1u << 7) ? 1u : d < (1u << 14) ? 2u : d < (1u << 21) ? 3u : d < (1u << 28) ? 4u : 5u;
+}
+
+__device__ __forceinline__ uint32_t delta_at(const int32_t* idx, int64_t j) {
+    const int64_t prev = j > 0 ? static_cast<int64_t>(idx[j - 1]) : 0;
+    return static_cast<uint32_t>(static_cast<int64_t>(idx[j]) - prev);
+}
+
+__global__ __launch_bounds__(kBlock) void k_de_count(const int32_t* __restrict__ idx, int64_t k, int64_t nchunks,
+                                                     uint32_t* __restrict__ cnt) {
+    __shared__ uint32_t lds[kBlock / kWave + 1];
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t s = 0;
+        for (int t = 0; t < kPer && j0 + t < k; ++t) s += leb_len(delta_at(idx, j0 + t));
+        uint32_t total;
+        block_excl_scan<kBlock>(s, lds, &total);
+        if (threadIdx.x == 0) cnt[c] = total;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_de_write(const int32_t* __restrict__ idx, int64_t k, int64_t nchunks,
+                                                     const uint32_t* __restrict__ cnt, uint8_t* __restrict__ out) {
+    __shared__ uint32_t lds[kBlock / kWave + 1];
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t s = 0;
+        for (int t = 0; t < kPer && j0 + t < k; ++t) s += leb_len(delta_at(idx, j0 + t));
+        uint32_t total;
+        int64_t pos = static_cast<int64_t>(cnt[c]) + block_excl_scan<kBlock>(s, lds, &total);
+        for (int t = 0; t < kPer && j0 + t < k; ++t) {
+            uint32_t d = delta_at(idx, j0 + t);
+            for (;;) {
+                const uint32_t low = d & 0x7fu;
+                d >>= 7;
+                if (d) {
+                    out[pos++] = static_cast<uint8_t>(low | 0x80u);
+                } else {
+                    out[pos++] = static_cast<uint8_t>(low);
+                    break;
+                }
+            }
+        }
+    }
+}
+
+// value of the varint that ends at terminator byte p (walks back over at most 4
+// continuation bytes); sets *bad when the varint is longer than 5 bytes
+__device__ __forceinline__ uint64_t varint_ending_at(const uint8_t* in, int64_t p, bool* bad) {
+    int64_t q = p;
+    while (q > 0 && (in[q - 1] & 0x80u) && p - q < 4) --q;
+    if (q > 0 && (in[q - 1] & 0x80u)) *bad = true;  // more than 5 bytes
+    uint64_t v = 0;
+    for (int64_t t = p; t >= q; --t) v = (v << 7) | (in[t] & 0x7fu);
+    return v;
+}
+
+__global__ __launch_bounds__(kBlock) void k_dd_count(const uint8_t* __restrict__ in, int64_t nbytes,
+                                                     int64_t nchunks, uint32_t* __restrict__ tcnt,
+                                                     uint64_t* __restrict__ dsum, uint32_t* __restrict__ status) {
+    __shared__ uint32_t lds[kBlock / kWave + 1];
+    __shared__ uint64_t lds64[kBlock / kWave + 1];
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t b0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t s = 0;
+        uint64_t d = 0;
+        bool bad = false;
+        for (int t = 0; t < kPer && b0 + t < nbytes; ++t) {
+            if (!(in[b0 + t] & 0x80u)) {
+                ++s;
+                d += varint_ending_at(in, b0 + t, &bad);
+            }
+        }
+        if (bad && status) atomicOr(status, 1u);
+        uint32_t total;
+        uint64_t total64;
+        block_excl_scan<kBlock>(s, lds, &total);
+        block_excl_scan<kBlock>(d, lds64, &total64);
+        if (threadIdx.x == 0) {
+            tcnt[c] = total;
+            dsum[c] = total64;
+        }
+    }
+}
+
+__global__ void k_dd_check(const uint8_t* __restrict__ in, int64_t nbytes, int64_t k,
+                           const uint32_t* __restrict__ ttot, uint32_t* __restrict__ status) {
+    bool bad = static_cast<int64_t>(*ttot) != k;
+    if (nbytes > 0 && (in[nbytes - 1] & 0x80u)) bad = true;  // unterminated last varint
+    if (bad) atomicOr(status, 1u);
+}
+
+__global__ __launch_bounds__(kBlock) void k_dd_write(const uint8_t* __restrict__ in, int64_t nbytes,
+                                                     int64_t nchunks, const uint32_t* __restrict__ tcnt,
+                                                     const uint64_t* __restrict__ dsum, int64_t k,
+                                                     int32_t* __restrict__ idx, uint32_t* __restrict__ status) {
+    __shared__ uint32_t lds[kBlock / kWave + 1];
+    __shared__ uint64_t lds64[kBlock / kWave + 1];
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t b0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t s = 0;
+        uint64_t d = 0;
+        bool bad = false;
+        for (int t = 0; t < kPer && b0 + t < nbytes; ++t) {
+            if (!(in[b0 + t] & 0x80u)) {
+                ++s;
+                d += varint_ending_at(in, b0 + t, &bad);
+            }
+        }
+        uint32_t total;
+        uint64_t total64;
+        int64_t ord = static_cast<int64_t>(tcnt[c]) + block_excl_scan<kBlock>(s, lds, &total);
+        uint64_t acc = dsum[c] + block_excl_scan<kBlock>(d, lds64, &total64);
+        for (int t = 0; t < kPer && b0 + t < nbytes; ++t) {
+            if (!(in[b0 + t] & 0x80u)) {
+                acc += varint_ending_at(in, b0 + t, &bad);
+                if (acc > 0x7fffffffull) bad = true;
+                if (ord < k) idx[ord] = static_cast<int32_t>(acc);
+                ++ord;
+            }
+        }
+        if (bad && status) atomicOr(status, 1u);
+    }
+}
+
+// ------------------------------------------------------------------ blocks
+__device__ __forceinline__ bool blk_leader(const int32_t* idx, int64_t j, int64_t n, int64_t* blk) {
+    const int64_t i = idx[j];
+    if (i < 0 || i >= n) return false;
+    *blk = i >> 8;
+    if (j == 0) return true;
+    const int64_t ip = idx[j - 1];
+    return !(ip >= 0 && ip < n && (ip >> 8) == (i >> 8));
+}
+
+__global__ __launch_bounds__(kBlock) void k_be_count(const int32_t* __restrict__ idx, int64_t k, int64_t n,
+                                                     int64_t nchunks, uint8_t* __restrict__ offs,
+                                                     uint8_t* __restrict__ flags, uint32_t* __restrict__ cnt) {
+    __shared__ uint32_t lds[kBlock / kWave + 1];
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t s = 0;
+        for (int t = 0; t < kPer && j0 + t < k; ++t) {
+            const int64_t i = idx[j0 + t];
+            offs[j0 + t] = static_cast<uint8_t>(i & 255);
+            int64_t b;
+            if (blk_leader(idx, j0 + t, n, &b)) {
+                ++s;
+                flags[b] = 1;
+            }
+        }
+        uint32_t total;
+        block_excl_scan<kBlock>(s, lds, &total);
+        if (threadIdx.x == 0) cnt[c] = total;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_be_write(const int32_t* __restrict__ idx, int64_t k, int64_t n,
+                                                     int64_t nchunks, const uint32_t* __restrict__ cnt,
+                                                     uint8_t* __restrict__ counts_m1, int64_t cap) {
+    __shared__ uint32_t lds[kBlock / kWave + 1];
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t s = 0;
+        for (int t = 0; t < kPer && j0 + t < k; ++t) {
+            int64_t b;
+            s += blk_leader(idx, j0 + t, n, &b) ? 1u : 0u;
+        }
+        uint32_t total;
+        int64_t ord = static_cast<int64_t>(cnt[c]) + block_excl_scan<kBlock>(s, lds, &total);
+        for (int t = 0; t < kPer && j0 + t < k; ++t) {
+            int64_t b;
+            if (!blk_leader(idx, j0 + t, n, &b)) continue;
+            int64_t e = j0 + t + 1;
+            while (e < k && e - (j0 + t) < 256 && idx[e] >= 0 && idx[e] < n && (idx[e] >> 8) == b) ++e;
+            if (ord < cap) counts_m1[ord] = static_cast<uint8_t>(e - (j0 + t) - 1);
+            ++ord;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_be_mask(const uint8_t* __restrict__ flags, int64_t nb,
+                                                    uint8_t* __restrict__ mask) {
+    const int64_t nm = (nb + 7) / 8;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nm; i += stride) {
+        uint32_t v = 0;
+        for (int t = 0; t < 8; ++t)
+            if (i * 8 + t < nb && flags[i * 8 + t]) v |= 1u << t;
+        mask[i] = static_cast<uint8_t>(v);
+    }
+}
+
+// per chunk of non-empty blocks: sum of (count_m1 + 1), limited to the device-side block count
+__global__ __launch_bounds__(kBlock) void k_bd_count(const uint8_t* __restrict__ counts_m1,
+                                                     const uint32_t* __restrict__ nblk, int64_t mcap,
+                                                     int64_t nchunks, uint32_t* __restrict__ csum) {
+    __shared__ uint32_t lds[kBlock / kWave + 1];
+    const int64_t m = std::min<int64_t>(*nblk, mcap);
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t s = 0;
+        for (int t = 0; t < kPer && j0 + t < m; ++t) s += counts_m1[j0 + t] + 1u;
+        uint32_t total;
+        block_excl_scan<kBlock>(s, lds, &total);
+        if (threadIdx.x == 0) csum[c] = total;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_bd_write(const uint8_t* __restrict__ counts_m1,
+                                                     const uint8_t* __restrict__ offs,
+                                                     const int32_t* __restrict__ blk,
+                                                     const uint32_t* __restrict__ nblk, int64_t mcap,
+                                                     int64_t nchunks, const uint32_t* __restrict__ csum, int64_t k,
+                                                     int32_t* __restrict__ idx) {
+    __shared__ uint32_t lds[kBlock / kWave + 1];
+    const int64_t m = std::min<int64_t>(*nblk, mcap);
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t s = 0;
+        for (int t = 0; t < kPer && j0 + t < m; ++t) s += counts_m1[j0 + t] + 1u;
+        uint32_t total;
+        int64_t pos = static_cast<int64_t>(csum[c]) + block_excl_scan<kBlock>(s, lds, &total);
+        for (int t = 0; t < kPer && j0 + t < m; ++t) {
+            const int64_t base = static_cast<int64_t>(blk[j0 + t]) * 256;
+            const uint32_t cntb = counts_m1[j0 + t] + 1u;
+            for (uint32_t u = 0; u < cntb; ++u, ++pos)
+                if (pos < k) idx[pos] = static_cast<int32_t>(base + offs[pos]);
+        }
+    }
+}
+
+}  // namespace enc
+}  // namespace efg
+
+using namespace efg;
+using namespace efg::enc;
+
+extern "C" {
+
+int encode_bitmap(const int32_t* idx, int64_t k, int64_t n, uint8_t* bits, void* stream) {
+    if (n < 0 || n > kMaxElems || k < 0) return fail(EF_EINVAL, "encode_bitmap: bad sizes n=%lld k=%lld",
+                                                     (long long)n, (long long)k);
+    if (n > 0 && !bits) return fail(EF_EINVAL, "encode_bitmap: bits must not be NULL");
+    if (k > 0 && !idx) return fail(EF_EINVAL, "encode_bitmap: idx must not be NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t nbytes = (n + 7) / 8;
+    if (nbytes == 0) return EF_OK;
+    EF_TRY(launch("bitmap_clear", k_fill_bytes, dim3(grid_for(nbytes, kBlock * 16)), dim3(kBlock), s, bits, nbytes,
+                  static_cast<uint8_t>(0)));
+    if (k == 0) return EF_OK;
+    return launch("bitmap_set", k_bitmap_set, dim3(grid_for(k, kBlock)), dim3(kBlock), s, idx, k, n, bits);
+}
+
+size_t decode_bitmap_workspace_bytes(int64_t n) {
+    if (n < 0) return 0;
+    const int64_t nchunks = std::max<int64_t>(1, cdiv((n + 7) / 8, kChunk));
+    return round_up(static_cast<size_t>(nchunks + 1) * 4, 256);
+}
+
+static int bitmap_decode_into(const uint8_t* bits, int64_t nbits, int32_t* out, int64_t cap, int64_t* k_out,
+                              uint32_t* k_out32, uint32_t* cnt, hipStream_t s) {
+    const int64_t nbytes = (nbits + 7) / 8;
+    const int64_t nchunks = std::max<int64_t>(1, cdiv(nbytes, kChunk));
+    EF_TRY(launch("bitmap_count", k_bm_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, bits, nbits, nchunks, cnt));
+    EF_TRY(launch("bitmap_scan", k_scan<uint32_t>, dim3(1), dim3(kScanBlock), s, cnt, nchunks, k_out32, k_out));
+    return launch("bitmap_write", k_bm_write, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, bits, nbits, nchunks,
+                  static_cast<const uint32_t*>(cnt), out, cap);
+}
+
+int decode_bitmap(const uint8_t* bits, int64_t n, int32_t* idx, int64_t k_cap, int64_t* k_out, void* ws,
+                  size_t ws_bytes, void* stream) {
+    if (n < 0 || n > kMaxElems || k_cap < 0) return fail(EF_EINVAL, "decode_bitmap: bad sizes");
+    if (!k_out) return fail(EF_EINVAL, "decode_bitmap: k_out must not be NULL");
+    if (n > 0 && !bits) return fail(EF_EINVAL, "decode_bitmap: bits must not be NULL");
+    if (k_cap > 0 && !idx) return fail(EF_EINVAL, "decode_bitmap: idx must not be NULL");
+    const size_t need = decode_bitmap_workspace_bytes(n);
+    if (!ws || ws_bytes < need) return fail(EF_EWS, "decode_bitmap: workspace %zu < %zu bytes", ws_bytes, need);
+    return bitmap_decode_into(bits, n, idx, k_cap, k_out, nullptr, static_cast<uint32_t*>(ws),
+                              static_cast<hipStream_t>(stream));
+}
+
+int64_t encode_delta_bound(int64_t k) { return k < 0 ? 0 : 5 * k; }
+
+size_t delta_workspace_bytes(int64_t m) {
+    if (m < 0) return 0;
+    const int64_t nchunks = std::max<int64_t>(1, cdiv(m, kChunk));
+    // uint32 counts, uint64 sums, two totals
+    return round_up(static_cast<size_t>(nchunks + 1) * 4, 256) + round_up(static_cast<size_t>(nchunks + 1) * 8, 256) +
+           256;
+}
+
+int encode_delta(const int32_t* idx, int64_t k, uint8_t* out, int64_t* nbytes_out, void* ws, size_t ws_bytes,
+                 void* stream) {
+    if (k < 0 || k > kMaxElems) return fail(EF_EINVAL, "encode_delta: bad k");
+    if (!nbytes_out) return fail(EF_EINVAL, "encode_delta: nbytes_out must not be NULL");
+    if (k > 0 && (!idx || !out)) return fail(EF_EINVAL, "encode_delta: idx and out must not be NULL");
+    const size_t need = delta_workspace_bytes(k);
+    if (!ws || ws_bytes < need) return fail(EF_EWS, "encode_delta: workspace %zu < %zu bytes", ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t* cnt = static_cast<uint32_t*>(ws);
+    const int64_t nchunks = std::max<int64_t>(1, cdiv(k, kChunk));
+    EF_TRY(launch("delta_count", k_de_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, idx, k, nchunks, cnt));
+    EF_TRY(launch("delta_scan", k_scan<uint32_t>, dim3(1), dim3(kScanBlock), s, cnt, nchunks,
+                  static_cast<uint32_t*>(nullptr), nbytes_out));
+    if (k == 0) return EF_OK;
+    return launch("delta_write", k_de_write, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, idx, k, nchunks,
+                  static_cast<const uint32_t*>(cnt), out);
+}
+
+int decode_delta(const uint8_t* in, int64_t nbytes, int64_t k, int32_t* idx, uint32_t* status, void* ws,
+                 size_t ws_bytes, void* stream) {
+    if (k < 0 || k > kMaxElems || nbytes < 0) return fail(EF_EINVAL, "decode_delta: bad sizes");
+    if (nbytes > 0 && !in) return fail(EF_EINVAL, "decode_delta: in must not be NULL");
+    if (k > 0 && !idx) return fail(EF_EINVAL, "decode_delta: idx must not be NULL");
+    const size_t need = delta_workspace_bytes(nbytes);
+    if (!ws || ws_bytes < need) return fail(EF_EWS, "decode_delta: workspace %zu < %zu bytes", ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t nchunks = std::max<int64_t>(1, cdiv(nbytes, kChunk));
+    uint8_t* W = static_cast<uint8_t*>(ws);
+    uint32_t* tcnt = reinterpret_cast<uint32_t*>(W);
+    uint64_t* dsum = reinterpret_cast<uint64_t*>(W + round_up(static_cast<size_t>(nchunks + 1) * 4, 256));
+    uint32_t* ttot = reinterpret_cast<uint32_t*>(W + need - 256);
+    if (status) EF_TRY(launch("delta_zero", k_zero_u32, dim3(1), dim3(1), s, status));
+    EF_TRY(launch("delta_dcount", k_dd_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, in, nbytes, nchunks, tcnt,
+                  dsum, status));
+    EF_TRY(launch("delta_dscan32", k_scan<uint32_t>, dim3(1), dim3(kScanBlock), s, tcnt, nchunks, ttot,
+                  static_cast<int64_t*>(nullptr)));
+    EF_TRY(launch("delta_dscan64", k_scan<uint64_t>, dim3(1), dim3(kScanBlock), s, dsum, nchunks,
+                  static_cast<uint64_t*>(nullptr), static_cast<int64_t*>(nullptr)));
+    if (status)
+        EF_TRY(launch("delta_check", k_dd_check, dim3(1), dim3(1), s, in, nbytes, k,
+                      static_cast<const uint32_t*>(ttot), status));
+    if (nbytes == 0) return EF_OK;
+    return launch("delta_dwrite", k_dd_write, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, in, nbytes, nchunks,
+                  static_cast<const uint32_t*>(tcnt), static_cast<const uint64_t*>(dsum), k, idx, status);
+}
+
+// workspace: block flags (nb bytes), chunk counts, block list, block count
+size_t blocks_workspace_bytes(int64_t k, int64_t n) {
+    if (k < 0 || n < 0) return 0;
+    const int64_t nb = cdiv(n, 256);
+    const int64_t m = std::max<int64_t>(std::max<int64_t>(k, nb), 1);
+    const int64_t nchunks = cdiv(m, kChunk) + cdiv((nb + 7) / 8 + 1, kChunk) + 1;
+    return round_up(static_cast<size_t>(nb) + 16, 256) + round_up(static_cast<size_t>(nchunks + 1) * 4, 256) +
+           round_up(static_cast<size_t>(nb + 1) * 4, 256) + 256;
+}
+
+int encode_blocks(const int32_t* idx, int64_t k, int64_t n, uint8_t* mask, uint8_t* counts_m1, uint8_t* offs,
+                  int64_t* nblk_out, void* ws, size_t ws_bytes, void* stream) {
+    if (n < 0 || n > kMaxElems || k < 0) return fail(EF_EINVAL, "encode_blocks: bad sizes");
+    if (!nblk_out) return fail(EF_EINVAL, "encode_blocks: nblk_out must not be NULL");
+    if (n > 0 && !mask) return fail(EF_EINVAL, "encode_blocks: mask must not be NULL");
+    if (k > 0 && (!idx || !counts_m1 || !offs)) return fail(EF_EINVAL, "encode_blocks: NULL output");
+    const size_t need = blocks_workspace_bytes(k, n);
+    if (!ws || ws_bytes < need) return fail(EF_EWS, "encode_blocks: workspace %zu < %zu bytes", ws_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t nb = cdiv(n, 256);
+    uint8_t* W = static_cast<uint8_t*>(ws);
+    uint8_t* flags = W;
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(W + round_up(static_cast<size_t>(nb) + 16, 256));
+    const int64_t nchunks = std::max<int64_t>(1, cdiv(k, kChunk));
+    if (nb > 0)
+        EF_TRY(launch("blocks_clear", k_fill_bytes, dim3(grid_for(nb, kBlock * 16)), dim3(kBlock), s, flags, nb,
+                      static_cast<uint8_t>(0)));
+    EF_TRY(launch("blocks_count", k_be_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, idx, k, n, nchunks, offs,
+                  flags, cnt));
+    EF_TRY(launch("blocks_scan", k_scan<uint32_t>, dim3(1), dim3(kScanBlock), s, cnt, nchunks,
+                  static_cast<uint32_t*>(nullptr), nblk_out));
+    if (k > 0)
+        EF_TRY(launch("blocks_write", k_be_write, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, idx, k, n, nchunks,
+                      static_cast<const uint32_t*>(cnt), counts_m1, std::min(k, nb)));
+    if (nb == 0) return EF_OK;
+    return launch("blocks_mask", k_be_mask, dim3(grid_for((nb + 7) / 8, kBlock)), dim3(kBlock), s,
+                  static_cast<const uint8_t*>(flags), nb, mask);
+}
+
+int decode_blocks(const uint8_t* mask, const uint8_t* counts_m1, const uint8_t* offs, int64_t n, int64_t k,
+                  int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    if (n < 0 || n > kMaxElems || k < 0) return fail(EF_EINVAL, "decode_blocks: bad sizes");
+    if (n > 0 && !mask) return fail(EF_EINVAL, "decode_blocks: mask must not be NULL");
+    if (k > 0 && (!idx || !counts_m1 || !offs)) return fail(EF_EINVAL, "decode_blocks: NULL argument");
+    const size_t need = blocks_workspace_bytes(k, n);
+    if (!ws || ws_bytes < need) return fail(EF_EWS, "decode_blocks: workspace %zu < %zu bytes", ws_bytes, need);
+    const int64_t nb = cdiv(n, 256);
+    if (nb == 0 || k == 0) return EF_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* W = static_cast<uint8_t*>(ws);
+    const int64_t m = std::max<int64_t>(std::max<int64_t>(k, nb), 1);
+    const int64_t nchunks_all = cdiv(m, kChunk) + cdiv((nb + 7) / 8 + 1, kChunk) + 1;
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(W + round_up(static_cast<size_t>(nb) + 16, 256));
+    int32_t* blk = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(cnt) +
+                                              round_up(static_cast<size_t>(nchunks_all + 1) * 4, 256));
+    uint32_t* nblk = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(blk) +
+                                                 round_up(static_cast<size_t>(nb + 1) * 4, 256));
+    // 1. list of non-empty blocks from the mask
+    EF_TRY(bitmap_decode_into(mask, nb, blk, nb, nullptr, nblk, cnt, s));
+    // 2. prefix of block counts, 3. indices
+    const int64_t nchunks = std::max<int64_t>(1, cdiv(std::min(k, nb), kChunk));
+    const int64_t mcap = std::min(k, nb);
+    EF_TRY(launch("blocks_dcount", k_bd_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, counts_m1,
+                  static_cast<const uint32_t*>(nblk), mcap, nchunks, cnt));
+    EF_TRY(launch("blocks_dscan", k_scan<uint32_t>, dim3(1), dim3(kScanBlock), s, cnt, nchunks,
+                  static_cast<uint32_t*>(nullptr), static_cast<int64_t*>(nullptr)));
+    return launch("blocks_dwrite", k_bd_write, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, counts_m1, offs,
+                  static_cast<const int32_t*>(blk), static_cast<const uint32_t*>(nblk), mcap, nchunks,
+                  static_cast<const uint32_t*>(cnt), k, idx);
+}
+
+}  // extern "C"

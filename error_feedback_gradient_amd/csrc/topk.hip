@@ -1,0 +1,968 @@
+// Top-k sparsification with error feedback (flat and layer-wise), gfx950.
+//
+// What is computed ("Gradient sparsification" page, step-by-step algorithm
+// steps 2-4, error-compensation and top-k sections): x = g + e; keep the k
+// entries of largest |x| (ties: lower index first); send them with their
+// indices in ascending order; e = x where dropped, +0 where kept.
+//
+// How (per tensor, "segment"; the flat call is one segment):
+//   1. sample     a strided sample of x = g + e is histogrammed on the top 12
+//                 bits of its magnitude key; a threshold key T_lo is chosen so
+//                 that about 2k elements of the tensor are expected above it.
+//   2. stream     ONE pass over the tensor: read g and e (128-bit loads),
+//                 write e := x (128-bit stores), and append every element with
+//                 key >= T_lo to a per-wave candidate slot, in index order, by
+//                 wave ballots.  This is the only full pass: 12 bytes/element.
+//   3. scan       per-tensor candidate totals; the tensor drops to the exact
+//                 fallback when a slot overflowed or fewer than k candidates
+//                 were found (both decided on the device; later kernels skip
+//                 the path not taken).
+//   4. compact    candidate slots -> one dense, index-ordered list.
+//   5. radix      exact k-th largest key T over the candidates: three digit
+//                 passes (11, 10, 10 bits) with LDS-privatised histograms.
+//   6. emit       entries with key > T, plus the first r entries with key == T
+//                 in index order, are written in index order; e[idx] = +0.
+// The fallback runs steps 5-6 over the whole tensor (x now sits in e).
+// Only integer atomics are used, so results do not depend on timing.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "common.hpp"
+
+namespace efg {
+namespace topk {
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kRegion = 16384;          // elements per wave in the streaming pass
+constexpr int kUnroll = 4;              // float4 loads in flight per lane and array
+constexpr int kSampleChunk = 256;       // contiguous elements per sample chunk
+constexpr int kSampleChunksMax = 4096;
+constexpr int kSampleChunksMin = 256;
+constexpr int kSampleChunksPerWave = 4;
+constexpr int kSampleBlockChunks = kSampleChunksPerWave * kWavesPerBlock;
+constexpr int kSampleBins = 4096;
+constexpr int kSampleShift = 19;        // 31-bit key >> 19 = 12 bits
+constexpr int kChunk = 4096;            // entries per block-unit in select and emit
+constexpr int kPerThread = kChunk / kBlock;
+constexpr int kRadixBins = 2048;
+constexpr int kMaxGrid = 2048;
+
+enum : int32_t { MODE_NORMAL = 0, MODE_NONE = 1, MODE_ALL = 2 };
+
+struct alignas(16) SegPlan {
+    int64_t off;        // first element in the packed buffer
+    int64_t n;          // elements
+    int64_t k;          // kept
+    int64_t out_off;    // first output slot
+    int64_t cand_base;  // first candidate slot entry
+    int32_t region_begin, nregions;
+    int32_t cap;        // candidate slots per region
+    int32_t mode;
+    int32_t sample_chunks, sample_rank, exhaustive, direct;
+    int32_t raw_chunks, pad0, pad1, pad2;
+    int32_t pad3[4];
+};
+static_assert(sizeof(SegPlan) == 112, "SegPlan layout");
+
+struct alignas(16) SegState {
+    uint32_t tlo, overflow, fallback, ncand;
+    uint32_t dense_off, cchunk_begin, cchunks, prefix;
+    uint32_t want, T, r, pad[5];
+};
+static_assert(sizeof(SegState) == 64, "SegState layout");
+
+struct alignas(16) Header {
+    uint32_t any_fallback;
+    uint32_t total_cchunks;
+    uint32_t pad[62];
+};
+static_assert(sizeof(Header) == 256, "Header layout");
+
+// ------------------------------------------------------------------ host plan
+struct Plan {
+    int32_t nseg = 0;
+    int64_t R = 0;      // regions (waves of the streaming pass)
+    int64_t SB = 0;     // sample blocks
+    int64_t QR = 0;     // raw chunks (fallback units)
+    int64_t QC = 0;     // bound on candidate chunks
+    int64_t Ctot = 0;   // candidate slot entries
+    bool any_normal = false;
+    std::vector<SegPlan> seg;
+    std::vector<int32_t> rb, sbb, rcb;  // prefix tables, nseg+1 each
+};
+
+struct Layout {
+    size_t plan, rb, sbb, rcb, static_end;
+    size_t header, state, shist, rhist, zero_end;
+    size_t ccb, region_cnt, region_off, cval, cidx, dval, didx, cgt, ceq, rgt, req;
+    size_t total;
+};
+
+static Layout make_layout(const Plan& p) {
+    Layout L{};
+    size_t at = 0;
+    auto take = [&](size_t bytes) { size_t o = at; at = round_up(at + bytes, 256); return o; };
+    const size_t ns = static_cast<size_t>(p.nseg);
+    L.plan = take(ns * sizeof(SegPlan));
+    L.rb = at; at += (ns + 1) * 4;
+    L.sbb = at; at += (ns + 1) * 4;
+    L.rcb = at; at += (ns + 1) * 4;
+    at = round_up(at, 256);
+    L.static_end = at;
+    L.header = take(sizeof(Header));
+    L.state = take(ns * sizeof(SegState));
+    L.shist = take(ns * kSampleBins * 4);
+    L.rhist = take(ns * kRadixBins * 4);
+    L.zero_end = at;
+    L.ccb = take((ns + 1) * 4);
+    L.region_cnt = take(static_cast<size_t>(p.R) * 4);
+    L.region_off = take(static_cast<size_t>(p.R) * 4);
+    L.cval = take(static_cast<size_t>(p.Ctot) * 4);
+    L.cidx = take(static_cast<size_t>(p.Ctot) * 4);
+    L.dval = take(static_cast<size_t>(p.Ctot) * 4);
+    L.didx = take(static_cast<size_t>(p.Ctot) * 4);
+    L.cgt = take(static_cast<size_t>(p.QC) * 4);
+    L.ceq = take(static_cast<size_t>(p.QC) * 4);
+    L.rgt = take(static_cast<size_t>(p.QR) * 4);
+    L.req = take(static_cast<size_t>(p.QR) * 4);
+    L.total = at;
+    return L;
+}
+
+// Builds the per-tensor plan; validates the tables.
+static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& p) {
+    if (nseg < 0) return fail(EF_EINVAL, "nseg must be >= 0 (got %d)", nseg);
+    if (nseg > 0 && (!off || !ks)) return fail(EF_EINVAL, "segment tables must not be NULL");
+    if (nseg > 0 && off[0] < 0) return fail(EF_EINVAL, "seg_off[0] must be >= 0");
+    if (nseg > 0 && off[nseg] > kMaxElems) return fail(EF_EINVAL, "packed buffer exceeds 2^31-1 elements");
+    p = Plan{};
+    p.nseg = nseg;
+    p.seg.resize(nseg);
+    p.rb.assign(nseg + 1, 0);
+    p.sbb.assign(nseg + 1, 0);
+    p.rcb.assign(nseg + 1, 0);
+    int64_t out = 0;
+    for (int32_t s = 0; s < nseg; ++s) {
+        const int64_t n = off[s + 1] - off[s];
+        const int64_t k = ks[s];
+        if (n < 0) return fail(EF_EINVAL, "seg_off must be non-decreasing (segment %d)", s);
+        if (k < 0 || k > n) return fail(EF_EINVAL, "segment %d: k=%lld outside [0, n=%lld]", s, (long long)k, (long long)n);
+        SegPlan& P = p.seg[s];
+        memset(&P, 0, sizeof P);
+        P.off = off[s];
+        P.n = n;
+        P.k = k;
+        P.out_off = out;
+        out += k;
+        P.mode = (k == 0) ? MODE_NONE : (k == n ? MODE_ALL : MODE_NORMAL);
+        P.nregions = static_cast<int32_t>(cdiv(n, kRegion));
+        if (P.mode == MODE_NORMAL) {
+            const int64_t chunks = cdiv(n, kSampleChunk);
+            int64_t S = std::min<int64_t>(kSampleChunksMax, chunks / 8);
+            S = std::min<int64_t>(chunks, std::max<int64_t>(kSampleChunksMin, S));
+            const bool exhaustive = (S == chunks);
+            const int64_t S_el = exhaustive ? n : S * kSampleChunk;
+            int64_t m;
+            if (exhaustive) {
+                m = std::min<int64_t>(n, 2 * k + 64);
+            } else {
+                m = static_cast<int64_t>(ceil(2.0 * static_cast<double>(k) * static_cast<double>(S_el) /
+                                              static_cast<double>(n))) + 64;
+                m = std::min<int64_t>(S_el, m);
+            }
+            const double rho = static_cast<double>(m) / static_cast<double>(S_el);
+            const int64_t region_len = std::min<int64_t>(n, kRegion);
+            if (rho * 3.0 >= 0.5) {
+                // dense selection: candidates would not save anything; go
+                // straight to the exact full-pass path
+                P.direct = 1;
+                P.cap = 0;
+            } else {
+                int64_t cap = static_cast<int64_t>(ceil(kRegion * rho * 3.0)) + 64;
+                cap = static_cast<int64_t>(round_up(static_cast<size_t>(cap), 4));
+                P.cap = static_cast<int32_t>(std::min<int64_t>(cap, region_len));
+                P.sample_chunks = static_cast<int32_t>(S);
+                P.sample_rank = static_cast<int32_t>(m);
+                P.exhaustive = exhaustive ? 1 : 0;
+            }
+            P.raw_chunks = static_cast<int32_t>(cdiv(n, kChunk));
+            p.any_normal = true;
+        }
+        P.cand_base = p.Ctot;
+        p.Ctot += static_cast<int64_t>(P.nregions) * P.cap;
+        p.QC += cdiv(static_cast<int64_t>(P.nregions) * P.cap, kChunk);
+        P.region_begin = static_cast<int32_t>(p.R);
+        p.rb[s] = static_cast<int32_t>(p.R);
+        p.R += P.nregions;
+        p.sbb[s] = static_cast<int32_t>(p.SB);
+        p.SB += cdiv(P.sample_chunks, kSampleBlockChunks);
+        p.rcb[s] = static_cast<int32_t>(p.QR);
+        p.QR += P.raw_chunks;
+    }
+    p.rb[nseg] = static_cast<int32_t>(p.R);
+    p.sbb[nseg] = static_cast<int32_t>(p.SB);
+    p.rcb[nseg] = static_cast<int32_t>(p.QR);
+    p.QC += 1;
+    return EF_OK;
+}
+
+// ------------------------------------------------------------------ kernels
+__global__ __launch_bounds__(kBlock) void k_init(uint4* zero, int64_t nvec, uint32_t* nonfinite) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec; i += stride)
+        zero[i] = make_uint4(0, 0, 0, 0);
+    if (nonfinite && blockIdx.x == 0 && threadIdx.x == 0) *nonfinite = 0;
+}
+
+// 1. sample histogram of x = g + e on the top 12 key bits
+__global__ __launch_bounds__(kBlock) void k_sample(const float* __restrict__ g, const float* __restrict__ e,
+                                                   const SegPlan* __restrict__ plan, int32_t nseg,
+                                                   const int32_t* __restrict__ sbb, uint32_t* __restrict__ shist) {
+    __shared__ uint32_t h[kSampleBins];
+    const int b = blockIdx.x;
+    const int s = upper_index(sbb, nseg, b);
+    const int64_t off = plan[s].off, n = plan[s].n;
+    const int S = plan[s].sample_chunks;
+    const bool exhaustive = plan[s].exhaustive != 0;
+    for (int i = threadIdx.x; i < kSampleBins; i += kBlock) h[i] = 0;
+    __syncthreads();
+    const int w = threadIdx.x / kWave;
+    const int l = lane();
+    const int c0 = (b - sbb[s]) * kSampleBlockChunks + w * kSampleChunksPerWave;
+    float xs[kSampleChunksPerWave][4];
+    bool ok[kSampleChunksPerWave][4];
+#pragma unroll
+    for (int u = 0; u < kSampleChunksPerWave; ++u) {
+        const int c = c0 + u;
+        int64_t start = 0;
+        if (exhaustive) start = static_cast<int64_t>(c) * kSampleChunk;
+        else if (S > 1) start = static_cast<int64_t>(c) * (n - kSampleChunk) / (S - 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t loc = start + j * kWave + l;
+            ok[u][j] = (c < S) && (loc < n);
+            xs[u][j] = ok[u][j] ? (g[off + loc] + e[off + loc]) : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kSampleChunksPerWave; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (ok[u][j]) atomicAdd(&h[key_of(xs[u][j]) >> kSampleShift], 1u);
+    __syncthreads();
+    uint32_t* gh = shist + static_cast<size_t>(s) * kSampleBins;
+    for (int i = threadIdx.x; i < kSampleBins; i += kBlock)
+        if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+// Finds, in a histogram of PER*kBlock bins, the bin d such
+// that the count strictly above d is < want <= count from d upward.  Every
+// thread of the block must call it; returns true in exactly one thread when the
+// total reaches want, with *d and *above set there.
+template <int PER>
+__device__ __forceinline__ bool find_rank_bin(const uint32_t* hist, uint32_t want, int* d, uint32_t* above,
+                                              uint32_t* lds) {
+    constexpr int per = PER;
+    const int r = kBlock - 1 - static_cast<int>(threadIdx.x);  // thread 0 owns the top range
+    uint32_t c[PER];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        c[i] = hist[r * per + i];
+        sum += c[i];
+    }
+    uint32_t total;
+    uint32_t run = block_excl_scan<kBlock>(sum, lds, &total);
+    bool found = false;
+#pragma unroll
+    for (int i = per - 1; i >= 0; --i) {
+        if (!found && run < want && run + c[i] >= want) {
+            found = true;
+            *d = r * per + i;
+            *above = run;
+        }
+        run += c[i];
+    }
+    return found;
+}
+
+__global__ __launch_bounds__(kBlock) void k_sample_select(const SegPlan* __restrict__ plan,
+                                                          const uint32_t* __restrict__ shist,
+                                                          SegState* __restrict__ st) {
+    __shared__ uint32_t lds[kWavesPerBlock + 1];
+    const int s = blockIdx.x;
+    if (plan[s].mode != MODE_NORMAL || plan[s].direct) return;
+    const uint32_t m = static_cast<uint32_t>(plan[s].sample_rank);
+    int d;
+    uint32_t above;
+    const bool f = find_rank_bin<kSampleBins / kBlock>(shist + static_cast<size_t>(s) * kSampleBins, m, &d, &above, lds);
+    if (f) st[s].tlo = static_cast<uint32_t>(d) << kSampleShift;
+    // if the sample held fewer than m keys (cannot happen: m <= sample size) tlo stays 0
+}
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Appends the hits of one group of 64 lanes x NV consecutive elements to the
+// wave's candidate slot, preserving index order: lane l owns elements
+// [base + NV*l, base + NV*l + NV).
+template <int NV>
+__device__ __forceinline__ void append_hits(const float (&x)[NV], const bool (&hit)[NV], int64_t gidx0,
+                                            uint32_t& cnt, uint32_t cap, float* __restrict__ cv,
+                                            int32_t* __restrict__ ci) {
+    uint64_t bal[NV];
+    uint64_t any = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        bal[j] = __ballot(hit[j]);
+        any |= bal[j];
+    }
+    if (!any) return;
+    uint32_t pos = cnt;
+    uint32_t tot = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        pos += count_below(bal[j]);
+        tot += popc64(bal[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        if (hit[j]) {
+            if (pos < cap) {
+                cv[pos] = x[j];
+                ci[pos] = static_cast<int32_t>(gidx0 + j);
+            }
+            ++pos;
+        }
+    }
+    cnt += tot;
+}
+
+template <int MODE>
+__device__ __forceinline__ void stream_region(const float* __restrict__ g, float* __restrict__ e, int64_t gbeg,
+                                              int64_t gend, uint32_t tlo, uint32_t cap, float* __restrict__ cv,
+                                              int32_t* __restrict__ ci, float* __restrict__ vals,
+                                              int32_t* __restrict__ idx, int64_t out_base, uint32_t& cnt,
+                                              uint32_t& nf) {
+    const int l = lane();
+    // body [a, b) is 16-byte aligned (g and e are 16-byte aligned)
+    int64_t a = (gbeg + 3) & ~static_cast<int64_t>(3);
+    int64_t bnd = gend & ~static_cast<int64_t>(3);
+    if (a > bnd) a = bnd = gend;  // region shorter than one aligned quad
+    auto scalar_part = [&](int64_t from, int64_t to) {
+        // at most 3 elements, one per lane
+        const int64_t i = from + l;
+        const bool ok = i < to;
+        float xv[1] = {0.0f};
+        bool hit[1] = {false};
+        if (ok) {
+            xv[0] = g[i] + e[i];
+            const uint32_t key = key_of(xv[0]);
+            nf += key >= 0x7f800000u;
+            if (MODE == MODE_ALL) {
+                e[i] = 0.0f;
+                vals[out_base + (i - gbeg)] = xv[0];
+                idx[out_base + (i - gbeg)] = static_cast<int32_t>(i);
+            } else {
+                e[i] = xv[0];
+                hit[0] = (MODE == MODE_NORMAL) && key >= tlo;
+            }
+        }
+        if (MODE == MODE_NORMAL) {
+            // lanes hold consecutive single elements: lane l <-> index from + l
+            append_hits<1>(xv, hit, from + l, cnt, cap, cv, ci);
+        }
+    };
+    if (gbeg < a) scalar_part(gbeg, a);
+    const f4* __restrict__ g4 = reinterpret_cast<const f4*>(g + a);
+    f4* __restrict__ e4 = reinterpret_cast<f4*>(e + a);
+    const int64_t nv = (bnd - a) >> 2;
+    for (int64_t base = 0; base < nv; base += kWave * kUnroll) {
+        f4 gv[kUnroll], ev[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = base + u * kWave + l;
+            if (j < nv) {
+                gv[u] = __builtin_nontemporal_load(g4 + j);
+                ev[u] = __builtin_nontemporal_load(e4 + j);
+            } else {
+                gv[u] = f4{0.f, 0.f, 0.f, 0.f};
+                ev[u] = f4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = base + u * kWave + l;
+            const bool ok = j < nv;
+            f4 x = gv[u] + ev[u];
+            float xs[4] = {x.x, x.y, x.z, x.w};
+            bool hit[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t key = key_of(xs[t]);
+                nf += (ok && key >= 0x7f800000u) ? 1u : 0u;
+                hit[t] = (MODE == MODE_NORMAL) && ok && key >= tlo;
+            }
+            if (ok) {
+                if (MODE == MODE_ALL) {
+                    __builtin_nontemporal_store(f4{0.f, 0.f, 0.f, 0.f}, e4 + j);
+                    const int64_t i0 = a + 4 * j;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        vals[out_base + (i0 + t - gbeg)] = xs[t];
+                        idx[out_base + (i0 + t - gbeg)] = static_cast<int32_t>(i0 + t);
+                    }
+                } else {
+                    __builtin_nontemporal_store(x, e4 + j);
+                }
+            }
+            if (MODE == MODE_NORMAL) append_hits<4>(xs, hit, a + 4 * j, cnt, cap, cv, ci);
+        }
+    }
+    if (bnd < gend) scalar_part(bnd, gend);
+}
+
+// 2. the streaming pass; one wave per region
+__global__ __launch_bounds__(kBlock) void k_stream(const float* __restrict__ g, float* __restrict__ e,
+                                                   const SegPlan* __restrict__ plan, int32_t nseg,
+                                                   const int32_t* __restrict__ rb, int64_t R,
+                                                   SegState* __restrict__ st, uint32_t* __restrict__ region_cnt,
+                                                   float* __restrict__ cval, int32_t* __restrict__ cidx,
+                                                   float* __restrict__ vals, int32_t* __restrict__ idx,
+                                                   uint32_t* __restrict__ nonfinite) {
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
+    if (w >= R) return;
+    const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
+    const SegPlan& P = plan[s];
+    const int64_t rl = w - rb[s];
+    const int64_t lbeg = rl * kRegion;
+    const int64_t lend = min(lbeg + static_cast<int64_t>(kRegion), P.n);
+    const int64_t gbeg = P.off + lbeg, gend = P.off + lend;
+    const int mode = P.mode;
+    uint32_t cnt = 0, nf = 0;
+    const uint32_t cap = static_cast<uint32_t>(P.cap);
+    float* cv = cval + P.cand_base + rl * P.cap;
+    int32_t* ci = cidx + P.cand_base + rl * P.cap;
+    if (mode == MODE_NORMAL) {
+        // a direct (dense) selection collects nothing: tlo above every key
+        const uint32_t tlo = P.direct ? 0xffffffffu : st[s].tlo;
+        stream_region<MODE_NORMAL>(g, e, gbeg, gend, tlo, cap, cv, ci, vals, idx, 0, cnt, nf);
+    } else if (mode == MODE_ALL) {
+        stream_region<MODE_ALL>(g, e, gbeg, gend, 0, 0, cv, ci, vals, idx, P.out_off + lbeg, cnt, nf);
+    } else {
+        stream_region<MODE_NONE>(g, e, gbeg, gend, 0, 0, cv, ci, vals, idx, 0, cnt, nf);
+    }
+    nf = wave_sum(nf);
+    if (lane() == 0) {
+        region_cnt[w] = cnt < cap ? cnt : cap;
+        if (cnt > cap) atomicOr(&st[s].overflow, 1u);
+        if (nf && nonfinite) atomicAdd(nonfinite, nf);
+    }
+}
+
+// 3. region offsets, per-tensor candidate totals and the path decision
+constexpr int kScanBlock = 1024;
+__global__ __launch_bounds__(kScanBlock) void k_scan_regions(const SegPlan* __restrict__ plan, int32_t nseg,
+                                                             const int32_t* __restrict__ rb, int64_t R,
+                                                             const uint32_t* __restrict__ region_cnt,
+                                                             uint32_t* __restrict__ region_off,
+                                                             SegState* __restrict__ st, uint32_t* __restrict__ ccb,
+                                                             Header* __restrict__ hdr, uint32_t force_fallback) {
+    __shared__ uint32_t lds[kScanBlock / kWave + 1];
+    const int64_t per = (R + kScanBlock - 1) / kScanBlock;
+    const int64_t r0 = min(R, per * threadIdx.x), r1 = min(R, r0 + per);
+    uint32_t sum = 0;
+    for (int64_t r = r0; r < r1; ++r) sum += region_cnt[r];
+    uint32_t total;
+    uint32_t run = block_excl_scan<kScanBlock>(sum, lds, &total);
+    for (int64_t r = r0; r < r1; ++r) {
+        region_off[r] = run;
+        run += region_cnt[r];
+    }
+    __syncthreads();
+    uint32_t carry = 0, anyfb = 0;
+    for (int32_t t0 = 0; t0 < nseg; t0 += kScanBlock) {
+        const int32_t s = t0 + threadIdx.x;
+        uint32_t cchunks = 0;
+        if (s < nseg && plan[s].mode == MODE_NORMAL) {
+            const int64_t b = rb[s], en = rb[s + 1];
+            const uint32_t d0 = b < R ? region_off[b] : total;
+            const uint32_t d1 = en < R ? region_off[en] : total;
+            const uint32_t nc = d1 - d0;
+            const bool fb = force_fallback || plan[s].direct || st[s].overflow ||
+                            static_cast<int64_t>(nc) < plan[s].k;
+            st[s].fallback = fb ? 1u : 0u;
+            st[s].ncand = nc;
+            st[s].dense_off = d0;
+            st[s].want = static_cast<uint32_t>(plan[s].k);
+            st[s].prefix = 0;
+            cchunks = fb ? 0u : (nc + kChunk - 1) / kChunk;
+            st[s].cchunks = cchunks;
+            anyfb |= fb ? 1u : 0u;
+        }
+        uint32_t tt;
+        const uint32_t ex = block_excl_scan<kScanBlock>(cchunks, lds, &tt);
+        if (s < nseg) {
+            ccb[s] = carry + ex;
+            st[s].cchunk_begin = carry + ex;
+        }
+        carry += tt;
+    }
+    if (anyfb) atomicOr(&hdr->any_fallback, 1u);
+    if (threadIdx.x == 0) {
+        ccb[nseg] = carry;
+        hdr->total_cchunks = carry;
+    }
+}
+
+// 4. candidate slots -> dense index-ordered list
+__global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ plan, int32_t nseg,
+                                                    const int32_t* __restrict__ rb, int64_t R,
+                                                    const SegState* __restrict__ st,
+                                                    const uint32_t* __restrict__ region_cnt,
+                                                    const uint32_t* __restrict__ region_off,
+                                                    const float* __restrict__ cval, const int32_t* __restrict__ cidx,
+                                                    float* __restrict__ dval, int32_t* __restrict__ didx) {
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
+    if (w >= R) return;
+    const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
+    if (plan[s].mode != MODE_NORMAL || st[s].fallback) return;
+    const uint32_t cnt = region_cnt[w];
+    const int64_t src = plan[s].cand_base + (w - rb[s]) * plan[s].cap;
+    const uint32_t dst = region_off[w];
+    for (uint32_t j = lane(); j < cnt; j += kWave) {
+        dval[dst + j] = cval[src + j];
+        didx[dst + j] = cidx[src + j];
+    }
+}
+
+// Radix digit of `key` in pass p (11, 10, 10 bits from the top) and whether the
+// key matches the digits already fixed.
+__device__ __forceinline__ bool radix_digit(int pass, uint32_t key, uint32_t prefix, uint32_t* d) {
+    if (pass == 0) {
+        *d = key >> 20;
+        return true;
+    }
+    if (pass == 1) {
+        *d = (key >> 10) & 1023u;
+        return (key >> 20) == prefix;
+    }
+    *d = key & 1023u;
+    return (key >> 10) == prefix;
+}
+
+__device__ __forceinline__ void flush_hist(uint32_t* h, uint32_t* gh, int nb) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb; i += kBlock) {
+        if (h[i]) atomicAdd(&gh[i], h[i]);
+        h[i] = 0;
+    }
+    __syncthreads();
+}
+
+// 5a. radix histogram over dense candidates
+__global__ __launch_bounds__(kBlock) void k_hist_cand(int pass, int32_t nseg, const SegState* __restrict__ st,
+                                                      const uint32_t* __restrict__ ccb, const Header* __restrict__ hdr,
+                                                      const float* __restrict__ dval, uint32_t* __restrict__ rhist) {
+    __shared__ uint32_t h[kRadixBins];
+    const int nb = pass == 0 ? 2048 : 1024;
+    for (int i = threadIdx.x; i < kRadixBins; i += kBlock) h[i] = 0;
+    __syncthreads();
+    const uint32_t total = hdr->total_cchunks;
+    for (uint32_t q = blockIdx.x; q < total; q += gridDim.x) {
+        const int s = upper_index(ccb, nseg, q);
+        const uint32_t prefix = st[s].prefix;
+        const uint32_t lq = q - ccb[s];
+        const uint32_t base = st[s].dense_off + lq * kChunk;
+        const uint32_t cnt = min(static_cast<uint32_t>(kChunk), st[s].ncand - lq * kChunk);
+        for (uint32_t j = threadIdx.x; j < cnt; j += kBlock) {
+            uint32_t d;
+            if (radix_digit(pass, key_of(dval[base + j]), prefix, &d)) atomicAdd(&h[d], 1u);
+        }
+        flush_hist(h, rhist + static_cast<size_t>(s) * kRadixBins, nb);
+    }
+}
+
+// 5b. radix histogram over whole tensors on the fallback path (x is in e)
+__global__ __launch_bounds__(kBlock) void k_hist_raw(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
+                                                     const SegState* __restrict__ st,
+                                                     const int32_t* __restrict__ rcb, int64_t QR,
+                                                     const Header* __restrict__ hdr, const float* __restrict__ e,
+                                                     uint32_t* __restrict__ rhist) {
+    if (!hdr->any_fallback) return;
+    __shared__ uint32_t h[kRadixBins];
+    const int nb = pass == 0 ? 2048 : 1024;
+    for (int i = threadIdx.x; i < kRadixBins; i += kBlock) h[i] = 0;
+    __syncthreads();
+    for (int64_t q = blockIdx.x; q < QR; q += gridDim.x) {
+        const int s = upper_index(rcb, nseg, static_cast<int32_t>(q));
+        if (!st[s].fallback) continue;
+        const uint32_t prefix = st[s].prefix;
+        const int64_t lbeg = (q - rcb[s]) * kChunk;
+        const int64_t cnt = min(static_cast<int64_t>(kChunk), plan[s].n - lbeg);
+        const float* x = e + plan[s].off + lbeg;
+        for (int64_t j = threadIdx.x; j < cnt; j += kBlock) {
+            uint32_t d;
+            if (radix_digit(pass, key_of(x[j]), prefix, &d)) atomicAdd(&h[d], 1u);
+        }
+        flush_hist(h, rhist + static_cast<size_t>(s) * kRadixBins, nb);
+    }
+}
+
+// 5c. fix one digit per tensor
+__global__ __launch_bounds__(kBlock) void k_digit(int pass, const SegPlan* __restrict__ plan,
+                                                  SegState* __restrict__ st, uint32_t* __restrict__ rhist) {
+    __shared__ uint32_t lds[kWavesPerBlock + 1];
+    const int s = blockIdx.x;
+    if (plan[s].mode != MODE_NORMAL) return;
+    const int nb = pass == 0 ? 2048 : 1024;
+    uint32_t* gh = rhist + static_cast<size_t>(s) * kRadixBins;
+    const uint32_t want = st[s].want;
+    const uint32_t prefix = st[s].prefix;
+    int d;
+    uint32_t above;
+    const bool f = pass == 0 ? find_rank_bin<2048 / kBlock>(gh, want, &d, &above, lds)
+                             : find_rank_bin<1024 / kBlock>(gh, want, &d, &above, lds);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb; i += kBlock) gh[i] = 0;
+    if (f) {
+        const uint32_t np = pass == 0 ? static_cast<uint32_t>(d) : ((prefix << 10) | static_cast<uint32_t>(d));
+        st[s].prefix = np;
+        st[s].want = want - above;
+        if (pass == 2) {
+            st[s].T = np;
+            st[s].r = want - above;
+        }
+    }
+}
+
+// 6a. per-unit counts of keys above T and equal to T
+template <bool RAW>
+__device__ __forceinline__ void unit_counts(const float* src, uint32_t cnt, uint32_t T, uint32_t* gt, uint32_t* eq) {
+    uint32_t a = 0, b = 0;
+    for (uint32_t j = threadIdx.x; j < cnt; j += kBlock) {
+        const uint32_t key = key_of(src[j]);
+        a += key > T;
+        b += key == T;
+    }
+    a = wave_sum(a);
+    b = wave_sum(b);
+    __shared__ uint32_t sa[kWavesPerBlock], sb[kWavesPerBlock];
+    if (lane() == 0) {
+        sa[threadIdx.x / kWave] = a;
+        sb[threadIdx.x / kWave] = b;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t ta = 0, tb = 0;
+        for (int i = 0; i < kWavesPerBlock; ++i) {
+            ta += sa[i];
+            tb += sb[i];
+        }
+        *gt = ta;
+        *eq = tb;
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kBlock) void k_count_cand(int32_t nseg, const SegState* __restrict__ st,
+                                                       const uint32_t* __restrict__ ccb,
+                                                       const Header* __restrict__ hdr, const float* __restrict__ dval,
+                                                       uint32_t* __restrict__ cgt, uint32_t* __restrict__ ceq) {
+    const uint32_t total = hdr->total_cchunks;
+    for (uint32_t q = blockIdx.x; q < total; q += gridDim.x) {
+        const int s = upper_index(ccb, nseg, q);
+        const uint32_t lq = q - ccb[s];
+        const uint32_t cnt = min(static_cast<uint32_t>(kChunk), st[s].ncand - lq * kChunk);
+        unit_counts<false>(dval + st[s].dense_off + lq * kChunk, cnt, st[s].T, cgt + q, ceq + q);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_count_raw(const SegPlan* __restrict__ plan, int32_t nseg,
+                                                      const SegState* __restrict__ st,
+                                                      const int32_t* __restrict__ rcb, int64_t QR,
+                                                      const Header* __restrict__ hdr, const float* __restrict__ e,
+                                                      uint32_t* __restrict__ rgt, uint32_t* __restrict__ req) {
+    if (!hdr->any_fallback) return;
+    for (int64_t q = blockIdx.x; q < QR; q += gridDim.x) {
+        const int s = upper_index(rcb, nseg, static_cast<int32_t>(q));
+        if (!st[s].fallback) continue;
+        const int64_t lbeg = (q - rcb[s]) * kChunk;
+        const uint32_t cnt = static_cast<uint32_t>(min(static_cast<int64_t>(kChunk), plan[s].n - lbeg));
+        unit_counts<true>(e + plan[s].off + lbeg, cnt, st[s].T, rgt + q, req + q);
+    }
+}
+
+// 6b. exclusive scan of the unit counts of each tensor (packed gt:eq in 64 bits)
+__global__ __launch_bounds__(kBlock) void k_emit_scan(const SegPlan* __restrict__ plan,
+                                                      const SegState* __restrict__ st,
+                                                      const int32_t* __restrict__ rcb, uint32_t* __restrict__ cgt,
+                                                      uint32_t* __restrict__ ceq, uint32_t* __restrict__ rgt,
+                                                      uint32_t* __restrict__ req) {
+    __shared__ uint64_t lds[kWavesPerBlock + 1];
+    const int s = blockIdx.x;
+    if (plan[s].mode != MODE_NORMAL) return;
+    uint32_t *a, *b;
+    int64_t n;
+    if (st[s].fallback) {
+        a = rgt + rcb[s];
+        b = req + rcb[s];
+        n = plan[s].raw_chunks;
+    } else {
+        a = cgt + st[s].cchunk_begin;
+        b = ceq + st[s].cchunk_begin;
+        n = st[s].cchunks;
+    }
+    uint64_t carry = 0;
+    for (int64_t t0 = 0; t0 < n; t0 += kBlock) {
+        const int64_t i = t0 + threadIdx.x;
+        const uint64_t v = i < n ? ((static_cast<uint64_t>(a[i]) << 32) | b[i]) : 0;
+        uint64_t tot;
+        const uint64_t ex = block_excl_scan<kBlock>(v, lds, &tot) + carry;
+        if (i < n) {
+            a[i] = static_cast<uint32_t>(ex >> 32);
+            b[i] = static_cast<uint32_t>(ex);
+        }
+        carry += tot;
+    }
+}
+
+// 6c. ordered write of the kept entries
+template <bool RAW>
+__device__ __forceinline__ void unit_write(const float* __restrict__ src_v, const int32_t* __restrict__ src_i,
+                                           int64_t idx_base, uint32_t cnt, uint32_t T, uint32_t r, uint32_t G0,
+                                           uint32_t E0, float* __restrict__ e, float* __restrict__ vals,
+                                           int32_t* __restrict__ idx, int64_t out_off, int64_t kseg) {
+    __shared__ uint64_t lds[kWavesPerBlock + 1];
+    const uint32_t j0 = threadIdx.x * kPerThread;
+    float v[kPerThread];
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        v[i] = (j0 + i < cnt) ? src_v[j0 + i] : 0.0f;
+        const uint32_t key = key_of(v[i]);
+        const bool ok = j0 + i < cnt;
+        ngt += ok && key > T;
+        neq += ok && key == T;
+    }
+    uint64_t tot;
+    const uint64_t before = block_excl_scan<kBlock>((static_cast<uint64_t>(ngt) << 32) | neq, lds, &tot);
+    uint32_t gtb = G0 + static_cast<uint32_t>(before >> 32);
+    uint32_t eqb = E0 + static_cast<uint32_t>(before);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        if (j0 + i >= cnt) continue;
+        const uint32_t key = key_of(v[i]);
+        int64_t pos = -1;
+        if (key > T) {
+            pos = static_cast<int64_t>(gtb) + min(r, eqb);
+            ++gtb;
+        } else if (key == T) {
+            if (eqb < r) pos = static_cast<int64_t>(gtb) + eqb;
+            ++eqb;
+        }
+        if (pos >= 0 && pos < kseg) {
+            const int64_t id = RAW ? idx_base + j0 + i : static_cast<int64_t>(src_i[j0 + i]);
+            vals[out_off + pos] = v[i];
+            idx[out_off + pos] = static_cast<int32_t>(id);
+            e[id] = 0.0f;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_write_cand(const SegPlan* __restrict__ plan, int32_t nseg,
+                                                       const SegState* __restrict__ st,
+                                                       const uint32_t* __restrict__ ccb,
+                                                       const Header* __restrict__ hdr, const float* __restrict__ dval,
+                                                       const int32_t* __restrict__ didx,
+                                                       const uint32_t* __restrict__ cgt,
+                                                       const uint32_t* __restrict__ ceq, float* __restrict__ e,
+                                                       float* __restrict__ vals, int32_t* __restrict__ idx) {
+    const uint32_t total = hdr->total_cchunks;
+    for (uint32_t q = blockIdx.x; q < total; q += gridDim.x) {
+        const int s = upper_index(ccb, nseg, q);
+        const uint32_t lq = q - ccb[s];
+        const uint32_t cnt = min(static_cast<uint32_t>(kChunk), st[s].ncand - lq * kChunk);
+        const uint32_t base = st[s].dense_off + lq * kChunk;
+        unit_write<false>(dval + base, didx + base, 0, cnt, st[s].T, st[s].r, cgt[q], ceq[q], e, vals, idx,
+                          plan[s].out_off, plan[s].k);
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_write_raw(const SegPlan* __restrict__ plan, int32_t nseg,
+                                                      const SegState* __restrict__ st,
+                                                      const int32_t* __restrict__ rcb, int64_t QR,
+                                                      const Header* __restrict__ hdr, const uint32_t* __restrict__ rgt,
+                                                      const uint32_t* __restrict__ req, float* __restrict__ e,
+                                                      float* __restrict__ vals, int32_t* __restrict__ idx) {
+    if (!hdr->any_fallback) return;
+    for (int64_t q = blockIdx.x; q < QR; q += gridDim.x) {
+        const int s = upper_index(rcb, nseg, static_cast<int32_t>(q));
+        if (!st[s].fallback) continue;
+        const int64_t lbeg = (q - rcb[s]) * kChunk;
+        const uint32_t cnt = static_cast<uint32_t>(min(static_cast<int64_t>(kChunk), plan[s].n - lbeg));
+        const int64_t gb = plan[s].off + lbeg;
+        unit_write<true>(e + gb, nullptr, gb, cnt, st[s].T, st[s].r, rgt[q], req[q], e, vals, idx,
+                         plan[s].out_off, plan[s].k);
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ host driver
+static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* idx, void* ws, size_t ws_bytes,
+               uint32_t* nonfinite, uint32_t flags, hipStream_t s) {
+    const Layout L = make_layout(P);
+    if (P.R == 0) {
+        // nothing to stream: only the counter needs clearing
+        if (nonfinite) EF_TRY(launch("topk_init", k_init, dim3(1), dim3(kBlock), s, static_cast<uint4*>(nullptr),
+                                     static_cast<int64_t>(0), nonfinite));
+        return EF_OK;
+    }
+    if (!ws) return fail(EF_EWS, "workspace is NULL (%zu bytes needed)", L.total);
+    if (ws_bytes < L.total) return fail(EF_EWS, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+    if (!aligned256(ws)) return fail(EF_EINVAL, "workspace must be 256-byte aligned");
+    uint8_t* W = static_cast<uint8_t*>(ws);
+    auto at = [&](size_t o) { return W + o; };
+
+    // static tables: plan, region/sample/raw-chunk prefix tables
+    {
+        std::vector<uint32_t> words(L.static_end / 4, 0u);
+        uint8_t* h = reinterpret_cast<uint8_t*>(words.data());
+        memcpy(h + L.plan, P.seg.data(), P.seg.size() * sizeof(SegPlan));
+        memcpy(h + L.rb, P.rb.data(), P.rb.size() * 4);
+        memcpy(h + L.sbb, P.sbb.data(), P.sbb.size() * 4);
+        memcpy(h + L.rcb, P.rcb.data(), P.rcb.size() * 4);
+        EF_TRY(upload_words(W, words.data(), words.size(), s));
+    }
+    const int64_t nzero = static_cast<int64_t>((L.zero_end - L.header) / 16);
+    const unsigned zgrid = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, cdiv(nzero, kBlock))));
+    EF_TRY(launch("topk_init", k_init, dim3(zgrid), dim3(kBlock), s, reinterpret_cast<uint4*>(at(L.header)), nzero,
+                  nonfinite));
+
+    const SegPlan* plan = reinterpret_cast<const SegPlan*>(at(L.plan));
+    const int32_t* rb = reinterpret_cast<const int32_t*>(at(L.rb));
+    const int32_t* sbb = reinterpret_cast<const int32_t*>(at(L.sbb));
+    const int32_t* rcb = reinterpret_cast<const int32_t*>(at(L.rcb));
+    Header* hdr = reinterpret_cast<Header*>(at(L.header));
+    SegState* st = reinterpret_cast<SegState*>(at(L.state));
+    uint32_t* shist = reinterpret_cast<uint32_t*>(at(L.shist));
+    uint32_t* rhist = reinterpret_cast<uint32_t*>(at(L.rhist));
+    uint32_t* ccb = reinterpret_cast<uint32_t*>(at(L.ccb));
+    uint32_t* region_cnt = reinterpret_cast<uint32_t*>(at(L.region_cnt));
+    uint32_t* region_off = reinterpret_cast<uint32_t*>(at(L.region_off));
+    float* cval = reinterpret_cast<float*>(at(L.cval));
+    int32_t* cidx = reinterpret_cast<int32_t*>(at(L.cidx));
+    float* dval = reinterpret_cast<float*>(at(L.dval));
+    int32_t* didx = reinterpret_cast<int32_t*>(at(L.didx));
+    uint32_t* cgt = reinterpret_cast<uint32_t*>(at(L.cgt));
+    uint32_t* ceq = reinterpret_cast<uint32_t*>(at(L.ceq));
+    uint32_t* rgt = reinterpret_cast<uint32_t*>(at(L.rgt));
+    uint32_t* req = reinterpret_cast<uint32_t*>(at(L.req));
+    const int32_t nseg = P.nseg;
+
+    if (P.any_normal && P.SB > 0) {
+        EF_TRY(launch("topk_sample", k_sample, dim3(static_cast<unsigned>(P.SB)), dim3(kBlock), s, g,
+                      static_cast<const float*>(e), plan, nseg, sbb, shist));
+        EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
+                      static_cast<const uint32_t*>(shist), st));
+    }
+    const unsigned sgrid = static_cast<unsigned>(cdiv(P.R, kWavesPerBlock));
+    EF_TRY(launch("topk_stream", k_stream, dim3(sgrid), dim3(kBlock), s, g, e, plan, nseg, rb, P.R, st, region_cnt,
+                  cval, cidx, vals, idx, nonfinite));
+    if (!P.any_normal) return EF_OK;
+
+    EF_TRY(launch("topk_scan_regions", k_scan_regions, dim3(1), dim3(kScanBlock), s, plan, nseg, rb, P.R,
+                  static_cast<const uint32_t*>(region_cnt), region_off, st, ccb, hdr,
+                  static_cast<uint32_t>((flags & EF_FLAG_FORCE_FALLBACK) ? 1u : 0u)));
+    EF_TRY(launch("topk_compact", k_compact, dim3(sgrid), dim3(kBlock), s, plan, nseg, rb, P.R,
+                  static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
+                  static_cast<const uint32_t*>(region_off), static_cast<const float*>(cval),
+                  static_cast<const int32_t*>(cidx), dval, didx));
+    const unsigned gc = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, P.QC)));
+    const unsigned gr = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, P.QR)));
+    for (int pass = 0; pass < 3; ++pass) {
+        EF_TRY(launch("topk_hist_cand", k_hist_cand, dim3(gc), dim3(kBlock), s, pass, nseg,
+                      static_cast<const SegState*>(st), static_cast<const uint32_t*>(ccb),
+                      static_cast<const Header*>(hdr), static_cast<const float*>(dval), rhist));
+        EF_TRY(launch("topk_hist_raw", k_hist_raw, dim3(gr), dim3(kBlock), s, pass, plan, nseg,
+                      static_cast<const SegState*>(st), rcb, P.QR, static_cast<const Header*>(hdr),
+                      static_cast<const float*>(e), rhist));
+        EF_TRY(launch("topk_digit", k_digit, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, pass, plan, st,
+                      rhist));
+    }
+    EF_TRY(launch("topk_count_cand", k_count_cand, dim3(gc), dim3(kBlock), s, nseg, static_cast<const SegState*>(st),
+                  static_cast<const uint32_t*>(ccb), static_cast<const Header*>(hdr),
+                  static_cast<const float*>(dval), cgt, ceq));
+    EF_TRY(launch("topk_count_raw", k_count_raw, dim3(gr), dim3(kBlock), s, plan, nseg,
+                  static_cast<const SegState*>(st), rcb, P.QR, static_cast<const Header*>(hdr),
+                  static_cast<const float*>(e), rgt, req));
+    EF_TRY(launch("topk_emit_scan", k_emit_scan, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
+                  static_cast<const SegState*>(st), rcb, cgt, ceq, rgt, req));
+    EF_TRY(launch("topk_write_cand", k_write_cand, dim3(gc), dim3(kBlock), s, plan, nseg,
+                  static_cast<const SegState*>(st), static_cast<const uint32_t*>(ccb),
+                  static_cast<const Header*>(hdr), static_cast<const float*>(dval),
+                  static_cast<const int32_t*>(didx), static_cast<const uint32_t*>(cgt),
+                  static_cast<const uint32_t*>(ceq), e, vals, idx));
+    EF_TRY(launch("topk_write_raw", k_write_raw, dim3(gr), dim3(kBlock), s, plan, nseg,
+                  static_cast<const SegState*>(st), rcb, P.QR, static_cast<const Header*>(hdr),
+                  static_cast<const uint32_t*>(rgt), static_cast<const uint32_t*>(req), e, vals, idx));
+    return EF_OK;
+}
+
+static int check_common(const float* g, const float* e, int64_t total, int64_t ksum, const float* vals,
+                        const int32_t* idx, uint32_t flags) {
+    if (flags & ~EF_FLAG_FORCE_FALLBACK) return fail(EF_EINVAL, "unknown flags 0x%x", flags);
+    if (total > 0 && (!g || !e)) return fail(EF_EINVAL, "g and e must not be NULL");
+    if (total > 0 && (!aligned16(g) || !aligned16(e))) return fail(EF_EINVAL, "g and e must be 16-byte aligned");
+    if (ksum > 0 && (!vals || !idx)) return fail(EF_EINVAL, "vals and idx must not be NULL when k > 0");
+    return EF_OK;
+}
+
+}  // namespace topk
+}  // namespace efg
+
+using namespace efg;
+
+extern "C" {
+
+size_t ef_topk_workspace_bytes(int64_t n, int64_t k) {
+    if (n < 0 || k < 0 || k > n || n > kMaxElems) return 0;
+    int64_t off[2] = {0, n}, ks[1] = {k};
+    topk::Plan p;
+    if (topk::make_plan(1, off, ks, p) != EF_OK) return 0;
+    return topk::make_layout(p).total;
+}
+
+int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals, int32_t* idx, void* ws,
+                     size_t ws_bytes, uint32_t* nonfinite, uint32_t flags, void* stream) {
+    if (n < 0 || n > kMaxElems) return fail(EF_EINVAL, "n=%lld outside [0, 2^31-1]", (long long)n);
+    if (k < 0 || k > n) return fail(EF_EINVAL, "k=%lld outside [0, n=%lld]", (long long)k, (long long)n);
+    EF_TRY(topk::check_common(g, e, n, k, vals, idx, flags));
+    int64_t off[2] = {0, n}, ks[1] = {k};
+    topk::Plan p;
+    EF_TRY(topk::make_plan(1, off, ks, p));
+    return topk::run(g, e, p, vals, idx, ws, ws_bytes, nonfinite, flags, static_cast<hipStream_t>(stream));
+}
+
+size_t ef_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* seg_off, const int64_t* seg_k) {
+    topk::Plan p;
+    if (topk::make_plan(nseg, seg_off, seg_k, p) != EF_OK) return 0;
+    return topk::make_layout(p).total;
+}
+
+int ef_topk_compress_segmented(const float* g, float* e, int32_t nseg, const int64_t* seg_off,
+                               const int64_t* seg_k, float* vals, int32_t* idx, void* ws, size_t ws_bytes,
+                               uint32_t* nonfinite, uint32_t flags, void* stream) {
+    topk::Plan p;
+    EF_TRY(topk::make_plan(nseg, seg_off, seg_k, p));
+    int64_t ksum = 0;
+    for (int32_t s = 0; s < nseg; ++s) ksum += seg_k[s];
+    EF_TRY(topk::check_common(g, e, nseg > 0 ? seg_off[nseg] : 0, ksum, vals, idx, flags));
+    return topk::run(g, e, p, vals, idx, ws, ws_bytes, nonfinite, flags, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -200,3 +200,22 @@ def sorted_unique_indices(n: int, k: int, *key: int) -> np.ndarray:
             s.update(r.integers(0, n, size=k - len(s)).tolist())
         return np.array(sorted(s), dtype=np.int32)
     return np.sort(r.permutation(n)[:k]).astype(np.int32)
+
+
+def large_gradient_device(step: int, n: int, device, chunk: int = 1 << 27):
+    """Same law as large_gradient (exp(-7 + 2 z) magnitudes, random signs), drawn
+    on the device with torch's seeded generator so that benchmark inputs for
+    many steps at N = 1.3e9 cost milliseconds.  The values differ from the
+    numpy stream; parity tests use large_gradient."""
+    import torch
+
+    gz = torch.Generator(device=device)
+    gz.manual_seed(LARGE * 1_000_003 + step)
+    out = torch.empty(n, dtype=torch.float32, device=device)
+    for lo in range(0, n, chunk):
+        m = min(chunk, n - lo)
+        z = torch.randn(m, generator=gz, device=device, dtype=torch.float32).double()
+        mag = torch.exp(z.mul_(2.0).add_(-7.0)).float()
+        neg = torch.randint(0, 2, (m,), generator=gz, device=device, dtype=torch.uint8).bool()
+        out[lo:lo + m] = torch.where(neg, -mag, mag)
+    return out

@@ -1,0 +1,213 @@
+/*
+ * efgrad — error-feedback gradient compression on one MI355X (gfx950).
+ *
+ * C ABI of libefgrad.so.  Every entry point takes plain pointers and sizes.
+ *
+ * Conventions shared by all calls
+ * -------------------------------
+ *  - Pointers are DEVICE pointers unless the comment says "host".  All device
+ *    buffers belong to the caller; the library never allocates or frees them.
+ *    Scratch memory comes from a caller-provided device workspace whose size
+ *    the matching *_workspace_bytes() host query returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only ENQUEUES work on that stream and returns; results are
+ *    valid once the caller synchronises the stream.  No call waits for the
+ *    device and none copies data device -> host.
+ *  - Sizes are int64_t.  Element indices are int32_t, so arrays that are
+ *    indexed hold at most 2^31 - 1 elements.
+ *  - float arrays read or written element-wise in bulk (g, e, m, w, G) must be
+ *    16-byte aligned.  Outputs must not alias inputs unless stated.
+ *  - Results are bit-identical from run to run and do not depend on launch
+ *    configuration: no floating-point atomics are used anywhere.
+ *  - Return value: EF_OK, or an error status with a message available from
+ *    ef_last_error() (thread-local).  Argument checks happen on the host before
+ *    anything is enqueued; on an error nothing is enqueued.
+ *  - Floating-point data problems (Inf/NaN) are not call errors: the calls that
+ *    can meet them count them into an optional device uint32 `nonfinite`
+ *    (overwritten by each call).
+ *
+ * Sources cited below ("pages"):
+ *   [SPARSE] "梯度稀疏化：只传输重要的梯度元素" — gradient sparsification.
+ *   [ONEBIT] "1bit Adam梯度压缩技术原理与分布式训练优化" — 1-bit Adam.
+ */
+#ifndef EFGRAD_H
+#define EFGRAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EF_OK 0
+#define EF_EINVAL 1   /* bad argument (null pointer, size, alignment, k > n, ...) */
+#define EF_EWS 2      /* workspace missing or smaller than the size query says   */
+#define EF_EHIP 3     /* the HIP runtime rejected a launch                        */
+#define EF_ENOTIMPL 4 /* entry point not available in this build                  */
+
+/* Debug flag for the top-k calls: take the exact full-pass selection path for
+ * every tensor even when the sampled candidate path would have succeeded. */
+#define EF_FLAG_FORCE_FALLBACK 1u
+
+/* Message describing the last error returned on the calling thread. */
+const char* ef_last_error(void);
+/* Library version string. */
+const char* ef_version(void);
+
+/* ------------------------------------------------------------------------
+ * Top-k sparsification with error feedback.
+ * [SPARSE] section "详细算法流程：带误差补偿的Top-k稀疏化" (step-by-step
+ * algorithm) steps 2-5, "必不可少的误差补偿" (error compensation),
+ * "梯度稀疏化的基本原理" (basic principle) step 3, "Top-k 稀疏化".
+ *
+ * For i in [0, n):  x_i = g_i + e_i  (float32, round to nearest even).
+ * The kept set S holds the k entries ranked first when entries are ordered by
+ * larger |x| first (compared as the IEEE bit pattern without the sign bit, so
+ * +0 == -0 and NaN > +Inf > every finite value) and, for equal |x|, by lower
+ * index first.
+ *   idx[0..k)  = S in ascending order                     (int32, output)
+ *   vals[0..k) = x at those indices, bit for bit          (float32, output)
+ *   e_i        = +0.0 for i in S, x_i otherwise           (in place)
+ *   *nonfinite = number of i with x_i = +-Inf or NaN      (nullable)
+ * g is read only.  0 <= k <= n <= 2^31 - 1.  vals/idx may be NULL when k = 0.
+ * ws: device workspace of at least ef_topk_workspace_bytes(n, k) bytes, 256-byte
+ * aligned; its contents on entry do not matter.
+ * flags: 0 or EF_FLAG_FORCE_FALLBACK.
+ * ------------------------------------------------------------------------ */
+size_t ef_topk_workspace_bytes(int64_t n, int64_t k);
+int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals,
+                     int32_t* idx, void* ws, size_t ws_bytes, uint32_t* nonfinite,
+                     uint32_t flags, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Layer-wise top-k over many tensors packed in one buffer: the operation of
+ * ef_topk_compress applied to every tensor on its own, all in one launch
+ * sequence.  [SPARSE] "分层阈值与自适应稀疏率" and "分层自适应Top-k" (per-layer
+ * top-k); [ONEBIT] "4.2 通信协议优化" item 1 (packing many tensors into one
+ * contiguous buffer).
+ *
+ * seg_off (host, nseg+1 int64): tensor s occupies g/e[seg_off[s], seg_off[s+1]);
+ *   non-decreasing, seg_off[nseg] <= 2^31 - 1.
+ * seg_k (host, nseg int64): 0 <= seg_k[s] <= seg_off[s+1] - seg_off[s].
+ * Output: tensor s's kept entries go to vals/idx[K_s, K_s + seg_k[s]) with
+ *   K_s = seg_k[0] + ... + seg_k[s-1]; indices are positions in the packed
+ *   buffer (seg_off[s] + local index), so idx is ascending overall.
+ * *nonfinite counts over all tensors.  The host tables are read during the
+ * call only.
+ * ------------------------------------------------------------------------ */
+size_t ef_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* seg_off,
+                                         const int64_t* seg_k);
+int ef_topk_compress_segmented(const float* g, float* e, int32_t nseg,
+                               const int64_t* seg_off, const int64_t* seg_k,
+                               float* vals, int32_t* idx, void* ws, size_t ws_bytes,
+                               uint32_t* nonfinite, uint32_t flags, void* stream);
+
+/* ------------------------------------------------------------------------
+ * 1-bit sign compression with averaged error feedback and momentum.
+ * [ONEBIT] "2.1 量化与误差补偿机制" (quantisation and error compensation),
+ * "2.2 动量修正策略" (momentum correction), "3.2 核心算法实现细节"
+ * (clip before quantisation, NaN check, int8 storage), section 1 (32 -> 1 bit).
+ *
+ * Per element, float32, each product and sum rounded on its own (no FMA):
+ *   gc = min(max(g, -clip), clip)          NaN passes through; clip = +Inf: off
+ *   x  = gc + e
+ *   q  = sign(x) in {-1, 0, +1}            sign(+-0) = sign(NaN) = 0
+ *   c  = 1 - beta1                         (a float32 value)
+ *   e  = beta1*e + c*(x - q)               (in place)
+ *   m  = beta1*m + c*q                     (in place)
+ *   sign_out[i] = q                        (int8, nullable)
+ *   bits[i/8] bit (i%8) = (q == +1)        (uint8[ceil(n/8)], LSB first, pad 0, nullable)
+ *   *nonfinite = count of non-finite new e plus non-finite new m (nullable)
+ * 0 <= n <= 2^31 - 1; 0 <= beta1 <= 1; clip > 0.
+ * ------------------------------------------------------------------------ */
+int ef_sign_compress(const float* g, float* e, float* m, int64_t n, float beta1,
+                     float clip, int8_t* sign_out, uint8_t* bits, uint32_t* nonfinite,
+                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * Receiver-side aggregation of sparse packets.  [SPARSE] "梯度稀疏化的基本原理"
+ * (values sharing an index are summed) and "详细算法流程" step 6.
+ *
+ * Packet p holds entries [pk_off[p], pk_off[p+1]) of vals/idx (device int64
+ * table of npk+1 entries).  For p = 0 .. npk-1 in order, for each entry:
+ *   G[idx] = G[idx] + val        (float32, one rounding per addition)
+ * G keeps its incoming contents (zero it first for a plain sum).  Within one
+ * packet indices must be strictly increasing and in [0, n) (the order top-k
+ * emits).  An entry outside [0, n), or not above the entry before it in its
+ * packet, is skipped and counted in *invalid (device uint32, nullable,
+ * overwritten); with unordered packets other entries may be missed too, but no
+ * write ever lands outside G.  pk_off must be non-decreasing with pk_off[0] >= 0;
+ * it is read on the device.
+ * ------------------------------------------------------------------------ */
+int sparse_decode_accumulate(float* G, int64_t n, int32_t npk, const float* vals,
+                             const int32_t* idx, const int64_t* pk_off,
+                             uint32_t* invalid, void* stream);
+
+/* Parameter update, [SPARSE] "详细算法流程" step 7:
+ *   w_i = w_i - (lr * G_i)     (product rounded to float32, then the subtraction) */
+int sgd_apply(float* w, const float* G, int64_t n, float lr, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Index encodings, [SPARSE] "索引编码压缩" (index encoding).  Inputs are index
+ * lists as top-k emits them: strictly increasing, in [0, n).
+ * ------------------------------------------------------------------------ */
+
+/* Bitmap: bits[i/8] bit (i%8) set iff i is listed; ceil(n/8) bytes, pad bits 0.
+ * Indices outside [0, n) are ignored. */
+int encode_bitmap(const int32_t* idx, int64_t k, int64_t n, uint8_t* bits, void* stream);
+
+/* Every set bit of bits[ceil(n/8)] in ascending order.  Writes at most k_cap
+ * indices; *k_out (device int64) = number of set bits. */
+size_t decode_bitmap_workspace_bytes(int64_t n);
+int decode_bitmap(const uint8_t* bits, int64_t n, int32_t* idx, int64_t k_cap,
+                  int64_t* k_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Delta + varint: d_0 = idx_0, d_j = idx_j - idx_{j-1}; each d is written as a
+ * minimal unsigned LEB128 number (7 bits per byte, low group first, high bit
+ * set on all bytes but the last).  out needs encode_delta_bound(k) = 5k bytes;
+ * *nbytes_out (device int64) = stream length. */
+int64_t encode_delta_bound(int64_t k);
+size_t delta_workspace_bytes(int64_t k_or_nbytes);
+int encode_delta(const int32_t* idx, int64_t k, uint8_t* out, int64_t* nbytes_out,
+                 void* ws, size_t ws_bytes, void* stream);
+/* Parses exactly k varints from in[0, nbytes) and sums them back into idx[k].
+ * *status (device uint32, nullable) = 0 if the stream held k well-formed
+ * varints, else 1 (idx is then undefined where the stream was bad). */
+int decode_delta(const uint8_t* in, int64_t nbytes, int64_t k, int32_t* idx,
+                 uint32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/* Block-sparse, 256-element blocks: nb = ceil(n/256).
+ *   mask[ceil(nb/8)]: bit b (LSB first) set iff block b holds a listed index
+ *   counts_m1[]     : for each non-empty block in ascending order, count - 1
+ *                     (capacity min(k, nb))
+ *   offs[k]         : idx_j - 256*(idx_j/256), in list order
+ *   *nblk_out (device int64): number of non-empty blocks. */
+size_t blocks_workspace_bytes(int64_t k, int64_t n);
+int encode_blocks(const int32_t* idx, int64_t k, int64_t n, uint8_t* mask,
+                  uint8_t* counts_m1, uint8_t* offs, int64_t* nblk_out, void* ws,
+                  size_t ws_bytes, void* stream);
+/* Inverse: rebuilds the k ascending indices described by mask/counts_m1/offs.
+ * k is the number of indices the stream holds (the packet length). */
+int decode_blocks(const uint8_t* mask, const uint8_t* counts_m1, const uint8_t* offs,
+                  int64_t n, int64_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing with HIP events on the stream each kernel is launched on.
+ * ef_profile_enable(1, only) starts recording an event pair around every later
+ * kernel launch of the process whose label contains `only` (host string; NULL
+ * or "" = every launch); ef_profile_enable(0, NULL) stops and clears.
+ * ef_profile_read() waits for the recorded events and returns the summed
+ * duration (ms) and launch count of recorded kernels whose label contains
+ * `name`.  Meant for benchmarks: each recorded launch costs two event records.
+ * Labels are "topk_stream", "topk_sample", ..., "sign_ef", "decode_scatter",
+ * "sgd_apply", "bitmap_*", "delta_*", "blocks_*".
+ * ------------------------------------------------------------------------ */
+int ef_profile_enable(int on, const char* only);
+int ef_profile_read(const char* name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EFGRAD_H */

@@ -1,0 +1,213 @@
+"""GPU parity of the top-k error-feedback path against the CPU oracle.
+
+Outputs (vals, idx, updated e, non-finite count) must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import error_feedback_gradient_amd as efg
+import gen
+import oracle
+from gpu_util import assert_bits_equal, device, host, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(g, e, k, flags=0):
+    dev = device()
+    gd, ed = to_dev(g, dev), to_dev(e, dev)
+    nf = torch.zeros(1, dtype=torch.int32, device=dev)
+    vals, idx = efg.ef_topk_compress(gd, ed, k, nonfinite=nf, flags=flags)
+    return host(vals), host(idx), host(ed), int(host(nf)[0])
+
+
+def check(g, e, k, flags=0, what=""):
+    v, i, en, nf = run_gpu(g, e, k, flags)
+    ov, oi, oe, onf = oracle.topk(g, e, k)
+    assert_bits_equal(i, oi, f"idx {what}")
+    assert_bits_equal(v, ov, f"vals {what}")
+    assert_bits_equal(en, oe, f"e {what}")
+    assert nf == onf, (what, nf, onf)
+
+
+SIZES = [1, 2, 3, 5, 63, 64, 65, 255, 257, 1000, 4099, 16383, 16384, 16385, 50_001, 100_003, 300_007]
+
+
+def inputs(n, kind, seed):
+    if kind == "normal":
+        return gen.normal_small(n, 100, seed, n), gen.normal_small(n, 101, seed, n, scale=0.3)
+    if kind == "ties":
+        return gen.uniform_ties(n, 5, 102, seed, n), gen.uniform_ties(n, 2, 103, seed, n)
+    if kind == "specials":
+        return gen.specials(n, 104, seed, n), gen.normal_small(n, 105, seed, n)
+    if kind == "allsame":
+        return np.full(n, 1.5, np.float32), np.zeros(n, np.float32)
+    if kind == "lognormal":
+        return gen.large_gradient(seed, n=n), np.zeros(n, np.float32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("kind", ["normal", "ties", "specials", "allsame", "lognormal"])
+def test_small_sizes(n, kind):
+    g, e = inputs(n, kind, 1)
+    for k in sorted({0, 1, max(0, n - 1), n, n // 3, max(1, n // 1000), max(1, n // 100)}):
+        check(g, e, k, what=f"n={n} {kind} k={k}")
+
+
+@pytest.mark.parametrize("n,k", [(1000, 10), (100_003, 997), (300_007, 300), (65_536, 3000)])
+@pytest.mark.parametrize("kind", ["normal", "ties", "allsame"])
+def test_forced_fallback(n, k, kind):
+    g, e = inputs(n, kind, 2)
+    check(g, e, k, flags=efg.EF_FLAG_FORCE_FALLBACK, what=f"fallback n={n} k={k} {kind}")
+
+
+def test_clustered_magnitudes_overflow_to_fallback():
+    # all large values sit in one region: per-region candidate slots overflow
+    n, k = 2_000_000, 20_000
+    g = gen.normal_small(n, 110, 0, scale=1e-3)
+    g[500_000:540_000] = gen.normal_small(40_000, 111, 0, scale=10.0)
+    e = np.zeros(n, np.float32)
+    check(g, e, k, what="clustered")
+
+
+def test_flat_chain_ten_steps():
+    """N = 1,000,000 N(0,1), k = 10,000, residual carried over 10 steps."""
+    dev = device()
+    n, k = gen.FLAT_N, gen.FLAT_K
+    e_ref = np.zeros(n, np.float32)
+    ed = torch.zeros(n, dtype=torch.float32, device=dev)
+    ws = efg.workspace(efg.ef_topk_workspace_bytes(n, k), dev)
+    for t in range(gen.FLAT_STEPS):
+        g = gen.flat_gradient(t)
+        vals, idx = efg.ef_topk_compress(to_dev(g, dev), ed, k, ws=ws)
+        ov, oi, e_ref, _ = oracle.topk(g, e_ref, k)
+        assert_bits_equal(host(idx), oi, f"idx step {t}")
+        assert_bits_equal(host(vals), ov, f"vals step {t}")
+        assert_bits_equal(host(ed), e_ref, f"e step {t}")
+
+
+def test_repeatable_bitwise():
+    dev = device()
+    n, k = 3_000_017, 3001
+    g = gen.large_gradient(7, n=n)
+    e0 = gen.normal_small(n, 120, scale=1e-3)
+    outs = []
+    for _ in range(2):
+        ed = to_dev(e0, dev)
+        v, i = efg.ef_topk_compress(to_dev(g, dev), ed, k)
+        outs.append((host(v), host(i), host(ed)))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(np.asarray(a).view(np.uint32 if a.dtype == np.float32 else a.dtype),
+                              np.asarray(b).view(np.uint32 if b.dtype == np.float32 else b.dtype))
+
+
+def test_guard_zones_untouched():
+    dev = device()
+    n, k = 100_003, 1000
+    g, e = inputs(n, "normal", 9)
+    pad = 4096
+    gd = torch.full((n + 2 * pad,), 7.0, device=dev)
+    ed = torch.full((n + 2 * pad,), 7.0, device=dev)
+    gd[pad:pad + n] = to_dev(g, dev)
+    ed[pad:pad + n] = to_dev(e, dev)
+    vbuf = torch.full((k + 2 * pad,), 7.0, device=dev)
+    ibuf = torch.full((k + 2 * pad,), 7, dtype=torch.int32, device=dev)
+    efg.ef_topk_compress(gd[pad:pad + n], ed[pad:pad + n], k, vals=vbuf[pad:pad + k], idx=ibuf[pad:pad + k])
+    for buf in (gd, ed, vbuf):
+        h = host(buf)
+        assert np.all(h[:pad] == 7.0) and np.all(h[-pad:] == 7.0)
+    hi = host(ibuf)
+    assert np.all(hi[:pad] == 7) and np.all(hi[-pad:] == 7)
+    ov, oi, oe, _ = oracle.topk(g, e, k)
+    assert_bits_equal(host(vbuf)[pad:pad + k], ov, "vals in guarded buffer")
+
+
+# ------------------------------------------------------------- segmented
+def seg_check(sizes, ks, seed, kind="normal", flags=0):
+    dev = device()
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(off[-1])
+    g, e = inputs(n, kind, seed) if n > 0 else (np.zeros(0, np.float32), np.zeros(0, np.float32))
+    ed = to_dev(e, dev)
+    nf = torch.zeros(1, dtype=torch.int32, device=dev)
+    v, i = efg.ef_topk_compress_segmented(to_dev(g, dev), ed, off, ks, nonfinite=nf, flags=flags)
+    ov, oi, oe, onf = oracle.topk_segmented(g, e, off, ks)
+    assert_bits_equal(host(i), oi, "seg idx")
+    assert_bits_equal(host(v), ov, "seg vals")
+    assert_bits_equal(host(ed), oe, "seg e")
+    assert int(host(nf)[0]) == onf
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "specials"])
+def test_segmented_ragged(kind):
+    # unaligned offsets, empty tensors, k = 0 and k = n tensors, sizes across region boundaries
+    sizes = [7, 0, 1, 300, 64, 1001, 5, 16385, 3, 40_000, 0, 70_001, 2]
+    ks = [3, 0, 1, 0, 64, 17, 5, 160, 2, 400, 0, 701, 2]
+    seg_check(sizes, ks, 3, kind)
+    seg_check(sizes, ks, 4, kind, flags=efg.EF_FLAG_FORCE_FALLBACK)
+
+
+def test_segmented_many_small():
+    r = gen.rng(130)
+    sizes = r.integers(1, 3000, size=700).tolist()
+    ks = [int(r.integers(0, s + 1)) for s in sizes]
+    seg_check(sizes, ks, 5)
+
+
+def test_segmented_bert_two_steps():
+    """The BERT-base layout (194 tensors, 108,888,576 elements), two chained steps."""
+    dev = device()
+    off, ks = gen.bert_segments()
+    n = int(off[-1])
+    ed = torch.zeros(n, dtype=torch.float32, device=dev)
+    e_ref = np.zeros(n, np.float32)
+    ws = efg.workspace(efg.ef_topk_segmented_workspace_bytes(off, ks), dev)
+    for t in range(2):
+        g = gen.bert_gradient(t)
+        v, i = efg.ef_topk_compress_segmented(to_dev(g, dev), ed, off, ks, ws=ws)
+        say(f"bert step {t}: oracle ...")
+        ov, oi, e_ref, _ = oracle.topk_segmented(g, e_ref, off, ks)
+        assert_bits_equal(host(i), oi, f"bert idx step {t}")
+        assert_bits_equal(host(v), ov, f"bert vals step {t}")
+        assert_bits_equal(host(ed), e_ref, f"bert e step {t}")
+
+
+# ------------------------------------------------------------- full size
+def test_large_invariants_two_steps():
+    """N = 1.3e9, k = 1.3e6: the result is pinned by the invariants that make the
+    kept set unique (exactly k; every kept key >= every dropped key; ties by
+    lower index; vals are x bit for bit; e is x where dropped and +0 where kept),
+    with x = g + e evaluated on the host by numpy."""
+    dev = device()
+    n, k = gen.LARGE_N, gen.LARGE_K
+    free, _ = torch.cuda.mem_get_info(dev)
+    if free < 3 * 4 * n + (1 << 30):
+        pytest.skip("not enough device memory")
+    ed = torch.zeros(n, dtype=torch.float32, device=dev)
+    e_prev = np.zeros(n, np.float32)
+    ws = efg.workspace(efg.ef_topk_workspace_bytes(n, k), dev)
+    gd = torch.empty(n, dtype=torch.float32, device=dev)
+    g = np.empty(n, np.float32)
+    for t in range(2):
+        gen.large_gradient(t, out=g)
+        gd.copy_(torch.from_numpy(g))
+        v, i = efg.ef_topk_compress(gd, ed, k, ws=ws)
+        vh, ih, eh = host(v), host(i), host(ed)
+        say(f"large step {t}: checking invariants")
+        x = g + e_prev
+        key = x.view(np.uint32) & np.uint32(0x7FFFFFFF)
+        assert ih.size == k and np.all(np.diff(ih) > 0) and ih[0] >= 0 and ih[-1] < n
+        assert_bits_equal(vh, x[ih], f"large vals step {t}")
+        kept = np.zeros(n, bool)
+        kept[ih] = True
+        T = key[ih].min()
+        drop_max = np.max(key[~kept])
+        assert T >= drop_max
+        if T == drop_max:
+            assert ih[key[ih] == T].max() < np.nonzero((key == T) & ~kept)[0].min()
+        want_e = x.copy()
+        want_e[ih] = 0.0
+        assert_bits_equal(eh, want_e, f"large e step {t}")
+        e_prev = want_e  # host-computed state, equal to the GPU's bit for bit
+        del x, key, kept, eh
