@@ -219,3 +219,17 @@ def large_gradient_device(step: int, n: int, device, chunk: int = 1 << 27):
         neg = torch.randint(0, 2, (m,), generator=gz, device=device, dtype=torch.uint8).bool()
         out[lo:lo + m] = torch.where(neg, -mag, mag)
     return out
+
+
+def sign_gradient_device(step: int, n: int, device):
+    """Same law as sign_gradient (1e-3 N(0,1) with a Bernoulli(0.01) set of
+    entries times 100), drawn on the device with torch's seeded generator for
+    long full-size chains; the values differ from the numpy stream."""
+    import torch
+
+    gz = torch.Generator(device=device)
+    gz.manual_seed(SIGN * 1_000_003 + step)
+    z = torch.randn(n, generator=gz, device=device, dtype=torch.float32).double().mul_(1e-3)
+    hit = torch.rand(n, generator=gz, device=device, dtype=torch.float32) < 0.01
+    z[hit] *= 100.0
+    return z.float()
