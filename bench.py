@@ -33,6 +33,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic():
+    """HBM bytes per launch of the streaming kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes, or None if the kernel sources changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "topk_stream_large_1p3e9_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = b"".join(open(os.path.join(ROOT, p), "rb").read() for p in rec["sources"])
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["traffic_bytes"]
+
+
 def cpu_baseline(n_sample: int, k_sample: int):
     """The oracle as it stands, single-threaded, on the first n_sample elements
     of the step-0 gradient (numpy stream), e = 0."""
@@ -139,9 +155,9 @@ def main():
     efg.profile_enable(True)
     step(0)
     torch.cuda.synchronize()
-    labels = ["topk_init", "upload", "topk_sample", "topk_sample_select", "topk_stream", "topk_scan_regions",
-              "topk_compact", "topk_hist_cand", "topk_hist_raw", "topk_digit", "topk_count_cand", "topk_count_raw",
-              "topk_emit_scan", "topk_write_cand", "topk_write_raw", "blocks_"]
+    labels = ["upload", "topk_init", "topk_sample_hist", "topk_sample_select", "topk_stream", "topk_scan_groups",
+              "topk_compact", "topk_restore", "topk_hist", "topk_digit", "topk_count", "topk_emit_scan", "topk_write",
+              "blocks_clear", "blocks_count", "blocks_scan", "blocks_write", "blocks_mask"]
     breakdown = {}
     for lab in labels:
         ms, cnt = efg.profile_read(lab)
@@ -194,7 +210,8 @@ def main():
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS,
-            "traffic": None,
+            "traffic": measured_traffic(),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "avg_ms": stream_avg_ms,
             "launches": launches,
         },

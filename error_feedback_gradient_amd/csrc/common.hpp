@@ -44,6 +44,13 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 constexpr int64_t kMaxElems = 0x7fffffffLL;
 
+// A few hundred host words passed to a kernel by value.
+constexpr uint32_t kWordChunk = 500;
+struct WordChunk {
+    uint32_t n;
+    uint32_t w[kWordChunk];
+};
+
 // Upload up to a few KB of host words into device memory through kernel
 // arguments (copied by the runtime at launch, so the host buffer is free as
 // soon as the call returns and no pinned staging or host wait is needed).

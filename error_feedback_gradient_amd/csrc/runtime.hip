@@ -73,20 +73,15 @@ ProfScope::~ProfScope() {
 }
 
 // ------------------------------------------------------------------ utilities
-struct WordChunk {
-    uint32_t n;
-    uint32_t w[500];
-};
-
 __global__ void k_upload(uint32_t* dst, WordChunk c) {
     for (uint32_t i = threadIdx.x; i < c.n; i += blockDim.x) dst[i] = c.w[i];
 }
 
 int upload_words(void* dst, const uint32_t* src, size_t nwords, hipStream_t s) {
     uint32_t* d = static_cast<uint32_t*>(dst);
-    for (size_t at = 0; at < nwords; at += 500) {
+    for (size_t at = 0; at < nwords; at += kWordChunk) {
         WordChunk c;
-        c.n = static_cast<uint32_t>(nwords - at < 500 ? nwords - at : 500);
+        c.n = static_cast<uint32_t>(nwords - at < kWordChunk ? nwords - at : kWordChunk);
         memcpy(c.w, src + at, c.n * sizeof(uint32_t));
         EF_TRY(launch("upload", k_upload, dim3(1), dim3(256), s, d + at, c));
     }

@@ -7,27 +7,37 @@
 //
 // How (per tensor, "segment"; the flat call is one segment):
 //   1. sample     a strided sample of x = g + e is histogrammed on the top 12
-//                 bits of its magnitude key; a threshold key T_lo is chosen so
-//                 that about 2k elements of the tensor are expected above it.
-//   2. stream     ONE pass over the tensor: read g and e (128-bit loads),
-//                 write e := x (128-bit stores), and append every element with
-//                 key >= T_lo to a per-wave candidate slot, in index order, by
-//                 wave ballots.  This is the only full pass: 12 bytes/element.
-//   3. scan       per-tensor candidate totals; the tensor drops to the exact
-//                 fallback when a slot overflowed or fewer than k candidates
-//                 were found (both decided on the device; later kernels skip
-//                 the path not taken).
-//   4. compact    candidate slots -> one dense, index-ordered list.
-//   5. radix      exact k-th largest key T over the candidates: three digit
-//                 passes (11, 10, 10 bits) with LDS-privatised histograms.
+//                 bits of its magnitude key.  Two bin edges are read off it:
+//                 T_lo, with (by a wide statistical margin) at least k
+//                 elements of the tensor above it, and T_hi, with (very
+//                 likely) fewer than k above it.
+//   2. stream     ONE pass over the tensor, one wave per 4096 elements: read
+//                 g and e (128-bit non-temporal loads, 8 in flight per lane
+//                 and array), write e (128-bit stores), and append every
+//                 element with key >= T_lo to the wave's candidate slot, in
+//                 index order, with wave ballots.  Candidates with key >= T_hi
+//                 are almost surely kept, so the stream already writes e = 0
+//                 for them.  This is the only full pass: 12 bytes/element.
+//   3. scan       per-tensor candidate totals from per-group counts; a tensor
+//                 drops to the exact fallback when a slot overflowed or fewer
+//                 than k candidates were found (decided on the device; later
+//                 kernels skip the path not taken).
+//   4. compact    per group of 256 regions: candidate slots -> one dense,
+//                 index-ordered list, plus the first radix histogram.
+//   5. radix      exact k-th largest key T over the candidates: digit passes
+//                 of 11, 10 and 10 bits with LDS-privatised histograms.
 //   6. emit       entries with key > T, plus the first r entries with key == T
-//                 in index order, are written in index order; e[idx] = +0.
-// The fallback runs steps 5-6 over the whole tensor (x now sits in e).
-// Only integer atomics are used, so results do not depend on timing.
+//                 in index order, are written in index order.  Their residual
+//                 becomes +0 unless the stream already cleared it; a dropped
+//                 candidate that the stream cleared gets x back.
+// The fallback first puts x back wherever the stream cleared it, then runs
+// steps 5-6 over the whole tensor (x sits in e).  Only integer atomics are
+// used, so results do not depend on timing.
 #include <math.h>
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 
 #include "common.hpp"
@@ -35,21 +45,36 @@
 namespace efg {
 namespace topk {
 
-constexpr int kBlock = 256;
+constexpr int kBlock = 256;                        // threads of the select / emit kernels
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kRegion = 16384;          // elements per wave in the streaming pass
-constexpr int kUnroll = 4;              // float4 loads in flight per lane and array
-constexpr int kSampleChunk = 256;       // contiguous elements per sample chunk
+// Streaming-pass shape, measured on MI355X: 4096-element regions per wave,
+// 8 x 128-bit loads in flight per lane and array, 1024-thread blocks.
+#ifndef EFG_STREAM_BLOCK
+#define EFG_STREAM_BLOCK 1024
+#endif
+#ifndef EFG_STREAM_REGION
+#define EFG_STREAM_REGION 4096
+#endif
+#ifndef EFG_STREAM_UNROLL
+#define EFG_STREAM_UNROLL 8
+#endif
+constexpr int kStreamBlock = EFG_STREAM_BLOCK;     // threads of the streaming kernel
+constexpr int kStreamWaves = kStreamBlock / kWave;
+constexpr int kRegion = EFG_STREAM_REGION;         // elements per wave in the streaming pass
+constexpr int kUnroll = EFG_STREAM_UNROLL;         // 128-bit loads in flight per lane and array
+constexpr int kGroup = 256;                        // regions per group (candidate totals, compaction)
+constexpr int kSampleChunk = 256;                  // contiguous elements per sample chunk
 constexpr int kSampleChunksMax = 4096;
 constexpr int kSampleChunksMin = 256;
 constexpr int kSampleChunksPerWave = 4;
 constexpr int kSampleBlockChunks = kSampleChunksPerWave * kWavesPerBlock;
 constexpr int kSampleBins = 4096;
-constexpr int kSampleShift = 19;        // 31-bit key >> 19 = 12 bits
-constexpr int kChunk = 4096;            // entries per block-unit in select and emit
+constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
+constexpr int kChunk = 4096;                       // entries per block-unit in select and emit
 constexpr int kPerThread = kChunk / kBlock;
 constexpr int kRadixBins = 2048;
 constexpr int kMaxGrid = 2048;
+constexpr uint32_t kNoKey = 0xffffffffu;           // above every 31-bit key
 
 enum : int32_t { MODE_NORMAL = 0, MODE_NONE = 1, MODE_ALL = 2 };
 
@@ -59,19 +84,22 @@ struct alignas(16) SegPlan {
     int64_t k;          // kept
     int64_t out_off;    // first output slot
     int64_t cand_base;  // first candidate slot entry
-    int32_t region_begin, nregions;
+    int32_t region_begin, nregions, group_begin, ngroups;
     int32_t cap;        // candidate slots per region
     int32_t mode;
-    int32_t sample_chunks, sample_rank, exhaustive, direct;
-    int32_t raw_chunks, pad0, pad1, pad2;
-    int32_t pad3[4];
+    int32_t sample_chunks, sample_rank;
+    int32_t sample_rank_hi, exhaustive, direct, raw_chunks;
+    int32_t pad[6];
 };
 static_assert(sizeof(SegPlan) == 112, "SegPlan layout");
 
 struct alignas(16) SegState {
-    uint32_t tlo, overflow, fallback, ncand;
-    uint32_t dense_off, cchunk_begin, cchunks, prefix;
-    uint32_t want, T, r, pad[5];
+    uint32_t tlo;       // keys >= tlo become candidates
+    uint32_t thi;       // stored candidates with key >= thi get e = 0 in the stream
+    uint32_t overflow, fallback;
+    uint32_t ncand, dense_off, cchunk_begin, cchunks;
+    uint32_t prefix, want, T, r;
+    uint32_t pad[4];
 };
 static_assert(sizeof(SegState) == 64, "SegState layout");
 
@@ -86,19 +114,20 @@ static_assert(sizeof(Header) == 256, "Header layout");
 struct Plan {
     int32_t nseg = 0;
     int64_t R = 0;      // regions (waves of the streaming pass)
+    int64_t G = 0;      // region groups
     int64_t SB = 0;     // sample blocks
     int64_t QR = 0;     // raw chunks (fallback units)
     int64_t QC = 0;     // bound on candidate chunks
     int64_t Ctot = 0;   // candidate slot entries
     bool any_normal = false;
     std::vector<SegPlan> seg;
-    std::vector<int32_t> rb, sbb, rcb;  // prefix tables, nseg+1 each
+    std::vector<int32_t> rb, gbb, sbb, rcb;  // prefix tables, nseg+1 each
 };
 
 struct Layout {
-    size_t plan, rb, sbb, rcb, static_end;
-    size_t header, state, shist, rhist, zero_end;
-    size_t ccb, region_cnt, region_off, cval, cidx, dval, didx, cgt, ceq, rgt, req;
+    size_t plan, rb, gbb, sbb, rcb, static_end;
+    size_t header, state, shist, rhist, grp_cnt, zero_end;
+    size_t ccb, grp_off, region_cnt, cval, cidx, dval, didx, cgt, ceq, rgt, req;
     size_t total;
 };
 
@@ -109,6 +138,7 @@ static Layout make_layout(const Plan& p) {
     const size_t ns = static_cast<size_t>(p.nseg);
     L.plan = take(ns * sizeof(SegPlan));
     L.rb = at; at += (ns + 1) * 4;
+    L.gbb = at; at += (ns + 1) * 4;
     L.sbb = at; at += (ns + 1) * 4;
     L.rcb = at; at += (ns + 1) * 4;
     at = round_up(at, 256);
@@ -117,10 +147,11 @@ static Layout make_layout(const Plan& p) {
     L.state = take(ns * sizeof(SegState));
     L.shist = take(ns * kSampleBins * 4);
     L.rhist = take(ns * kRadixBins * 4);
+    L.grp_cnt = take(static_cast<size_t>(p.G) * 4);
     L.zero_end = at;
     L.ccb = take((ns + 1) * 4);
+    L.grp_off = take(static_cast<size_t>(p.G) * 4);
     L.region_cnt = take(static_cast<size_t>(p.R) * 4);
-    L.region_off = take(static_cast<size_t>(p.R) * 4);
     L.cval = take(static_cast<size_t>(p.Ctot) * 4);
     L.cidx = take(static_cast<size_t>(p.Ctot) * 4);
     L.dval = take(static_cast<size_t>(p.Ctot) * 4);
@@ -138,18 +169,20 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
     if (nseg < 0) return fail(EF_EINVAL, "nseg must be >= 0 (got %d)", nseg);
     if (nseg > 0 && (!off || !ks)) return fail(EF_EINVAL, "segment tables must not be NULL");
     if (nseg > 0 && off[0] < 0) return fail(EF_EINVAL, "seg_off[0] must be >= 0");
+    for (int32_t s = 0; s < nseg; ++s)
+        if (off[s + 1] < off[s]) return fail(EF_EINVAL, "seg_off must be non-decreasing (segment %d)", s);
     if (nseg > 0 && off[nseg] > kMaxElems) return fail(EF_EINVAL, "packed buffer exceeds 2^31-1 elements");
     p = Plan{};
     p.nseg = nseg;
     p.seg.resize(nseg);
     p.rb.assign(nseg + 1, 0);
+    p.gbb.assign(nseg + 1, 0);
     p.sbb.assign(nseg + 1, 0);
     p.rcb.assign(nseg + 1, 0);
     int64_t out = 0;
     for (int32_t s = 0; s < nseg; ++s) {
         const int64_t n = off[s + 1] - off[s];
         const int64_t k = ks[s];
-        if (n < 0) return fail(EF_EINVAL, "seg_off must be non-decreasing (segment %d)", s);
         if (k < 0 || k > n) return fail(EF_EINVAL, "segment %d: k=%lld outside [0, n=%lld]", s, (long long)k, (long long)n);
         SegPlan& P = p.seg[s];
         memset(&P, 0, sizeof P);
@@ -160,33 +193,44 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
         out += k;
         P.mode = (k == 0) ? MODE_NONE : (k == n ? MODE_ALL : MODE_NORMAL);
         P.nregions = static_cast<int32_t>(cdiv(n, kRegion));
+        P.ngroups = static_cast<int32_t>(cdiv(P.nregions, kGroup));
         if (P.mode == MODE_NORMAL) {
+            // Sample: every element of small tensors, else 1/8 of the 256-element
+            // chunks (at least 256 and at most 4096 chunks), evenly spaced.
             const int64_t chunks = cdiv(n, kSampleChunk);
             int64_t S = std::min<int64_t>(kSampleChunksMax, chunks / 8);
             S = std::min<int64_t>(chunks, std::max<int64_t>(kSampleChunksMin, S));
             const bool exhaustive = (S == chunks);
             const int64_t S_el = exhaustive ? n : S * kSampleChunk;
-            int64_t m;
+            int64_t m, m_hi;
             if (exhaustive) {
-                m = std::min<int64_t>(n, 2 * k + 64);
+                // exact histogram: the bin holding the k-th largest key bounds T from below,
+                // the bin above it bounds it from above
+                m = k;
+                m_hi = k;
             } else {
-                m = static_cast<int64_t>(ceil(2.0 * static_cast<double>(k) * static_cast<double>(S_el) /
-                                              static_cast<double>(n))) + 64;
+                // mu = expected sample count above the k-th largest key; rank m is
+                // above that by 8 standard deviations plus 64, rank m_hi below it
+                const double mu = static_cast<double>(k) * static_cast<double>(S_el) / static_cast<double>(n);
+                m = static_cast<int64_t>(ceil(mu + 8.0 * sqrt(mu))) + 64;
                 m = std::min<int64_t>(S_el, m);
+                m_hi = static_cast<int64_t>(floor(mu - 4.0 * sqrt(mu))) - 16;
+                if (m_hi < 1) m_hi = 0;
             }
             const double rho = static_cast<double>(m) / static_cast<double>(S_el);
             const int64_t region_len = std::min<int64_t>(n, kRegion);
             if (rho * 3.0 >= 0.5) {
-                // dense selection: candidates would not save anything; go
-                // straight to the exact full-pass path
+                // dense selection: candidates would not save anything; take the
+                // exact full-pass path directly
                 P.direct = 1;
                 P.cap = 0;
             } else {
-                int64_t cap = static_cast<int64_t>(ceil(kRegion * rho * 3.0)) + 64;
+                int64_t cap = static_cast<int64_t>(ceil(kRegion * rho * 3.0)) + 32;
                 cap = static_cast<int64_t>(round_up(static_cast<size_t>(cap), 4));
                 P.cap = static_cast<int32_t>(std::min<int64_t>(cap, region_len));
                 P.sample_chunks = static_cast<int32_t>(S);
                 P.sample_rank = static_cast<int32_t>(m);
+                P.sample_rank_hi = static_cast<int32_t>(m_hi);
                 P.exhaustive = exhaustive ? 1 : 0;
             }
             P.raw_chunks = static_cast<int32_t>(cdiv(n, kChunk));
@@ -196,14 +240,18 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
         p.Ctot += static_cast<int64_t>(P.nregions) * P.cap;
         p.QC += cdiv(static_cast<int64_t>(P.nregions) * P.cap, kChunk);
         P.region_begin = static_cast<int32_t>(p.R);
+        P.group_begin = static_cast<int32_t>(p.G);
         p.rb[s] = static_cast<int32_t>(p.R);
+        p.gbb[s] = static_cast<int32_t>(p.G);
         p.R += P.nregions;
+        p.G += P.ngroups;
         p.sbb[s] = static_cast<int32_t>(p.SB);
         p.SB += cdiv(P.sample_chunks, kSampleBlockChunks);
         p.rcb[s] = static_cast<int32_t>(p.QR);
         p.QR += P.raw_chunks;
     }
     p.rb[nseg] = static_cast<int32_t>(p.R);
+    p.gbb[nseg] = static_cast<int32_t>(p.G);
     p.sbb[nseg] = static_cast<int32_t>(p.SB);
     p.rcb[nseg] = static_cast<int32_t>(p.QR);
     p.QC += 1;
@@ -211,11 +259,16 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
 }
 
 // ------------------------------------------------------------------ kernels
-__global__ __launch_bounds__(kBlock) void k_init(uint4* zero, int64_t nvec, uint32_t* nonfinite) {
+// Clears the per-call state and writes the first chunk of the plan tables.
+__global__ __launch_bounds__(kBlock) void k_init(uint4* zero, int64_t nvec, uint32_t* nonfinite, uint32_t* dst,
+                                                 WordChunk c) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec; i += stride)
         zero[i] = make_uint4(0, 0, 0, 0);
-    if (nonfinite && blockIdx.x == 0 && threadIdx.x == 0) *nonfinite = 0;
+    if (blockIdx.x == 0) {
+        for (uint32_t i = threadIdx.x; i < c.n; i += kBlock) dst[i] = c.w[i];
+        if (nonfinite && threadIdx.x == 0) *nonfinite = 0;
+    }
 }
 
 // 1. sample histogram of x = g + e on the top 12 key bits
@@ -259,30 +312,29 @@ __global__ __launch_bounds__(kBlock) void k_sample(const float* __restrict__ g, 
         if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
-// Finds, in a histogram of PER*kBlock bins, the bin d such
-// that the count strictly above d is < want <= count from d upward.  Every
-// thread of the block must call it; returns true in exactly one thread when the
-// total reaches want, with *d and *above set there.
+// Finds, in a histogram of PER*kBlock bins, the bin d such that the count
+// strictly above d is < want <= count from d upward.  Every thread of the block
+// must call it; returns true in exactly one thread when the total reaches
+// want, with *d and *above set there.
 template <int PER>
 __device__ __forceinline__ bool find_rank_bin(const uint32_t* hist, uint32_t want, int* d, uint32_t* above,
                                               uint32_t* lds) {
-    constexpr int per = PER;
     const int r = kBlock - 1 - static_cast<int>(threadIdx.x);  // thread 0 owns the top range
     uint32_t c[PER];
     uint32_t sum = 0;
 #pragma unroll
-    for (int i = 0; i < per; ++i) {
-        c[i] = hist[r * per + i];
+    for (int i = 0; i < PER; ++i) {
+        c[i] = hist[r * PER + i];
         sum += c[i];
     }
     uint32_t total;
     uint32_t run = block_excl_scan<kBlock>(sum, lds, &total);
     bool found = false;
 #pragma unroll
-    for (int i = per - 1; i >= 0; --i) {
+    for (int i = PER - 1; i >= 0; --i) {
         if (!found && run < want && run + c[i] >= want) {
             found = true;
-            *d = r * per + i;
+            *d = r * PER + i;
             *above = run;
         }
         run += c[i];
@@ -294,31 +346,48 @@ __global__ __launch_bounds__(kBlock) void k_sample_select(const SegPlan* __restr
                                                           const uint32_t* __restrict__ shist,
                                                           SegState* __restrict__ st) {
     __shared__ uint32_t lds[kWavesPerBlock + 1];
+    __shared__ uint32_t s_tlo, s_thi;
     const int s = blockIdx.x;
     if (plan[s].mode != MODE_NORMAL || plan[s].direct) return;
-    const uint32_t m = static_cast<uint32_t>(plan[s].sample_rank);
+    if (threadIdx.x == 0) {
+        s_tlo = 0;        // nothing found: every element is a candidate
+        s_thi = kNoKey;   // nothing found: no element is cleared in the stream
+    }
+    __syncthreads();
+    const uint32_t* h = shist + static_cast<size_t>(s) * kSampleBins;
     int d;
     uint32_t above;
-    const bool f = find_rank_bin<kSampleBins / kBlock>(shist + static_cast<size_t>(s) * kSampleBins, m, &d, &above, lds);
-    if (f) st[s].tlo = static_cast<uint32_t>(d) << kSampleShift;
-    // if the sample held fewer than m keys (cannot happen: m <= sample size) tlo stays 0
+    if (find_rank_bin<kSampleBins / kBlock>(h, static_cast<uint32_t>(plan[s].sample_rank), &d, &above, lds))
+        s_tlo = static_cast<uint32_t>(d) << kSampleShift;
+    const uint32_t mhi = static_cast<uint32_t>(plan[s].sample_rank_hi);
+    if (mhi > 0) {
+        if (find_rank_bin<kSampleBins / kBlock>(h, mhi, &d, &above, lds))
+            s_thi = static_cast<uint32_t>(d + 1) << kSampleShift;  // upper edge: fewer than mhi samples above
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        st[s].tlo = s_tlo;
+        st[s].thi = s_thi;
+    }
 }
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 // Appends the hits of one group of 64 lanes x NV consecutive elements to the
 // wave's candidate slot, preserving index order: lane l owns elements
-// [base + NV*l, base + NV*l + NV).
+// [gidx0, gidx0 + NV) and lanes are in index order.  stored[j] tells whether
+// element j went into the slot (false once the slot is full).
 template <int NV>
 __device__ __forceinline__ void append_hits(const float (&x)[NV], const bool (&hit)[NV], int64_t gidx0,
                                             uint32_t& cnt, uint32_t cap, float* __restrict__ cv,
-                                            int32_t* __restrict__ ci) {
+                                            int32_t* __restrict__ ci, bool (&stored)[NV]) {
     uint64_t bal[NV];
     uint64_t any = 0;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         bal[j] = __ballot(hit[j]);
         any |= bal[j];
+        stored[j] = false;
     }
     if (!any) return;
     uint32_t pos = cnt;
@@ -334,6 +403,7 @@ __device__ __forceinline__ void append_hits(const float (&x)[NV], const bool (&h
             if (pos < cap) {
                 cv[pos] = x[j];
                 ci[pos] = static_cast<int32_t>(gidx0 + j);
+                stored[j] = true;
             }
             ++pos;
         }
@@ -341,51 +411,61 @@ __device__ __forceinline__ void append_hits(const float (&x)[NV], const bool (&h
     cnt += tot;
 }
 
+// e value written by the stream for one element
+template <int MODE>
+__device__ __forceinline__ float stream_e(float x, uint32_t key, bool stored, uint32_t thi) {
+    if (MODE == MODE_ALL) return 0.0f;
+    if (MODE == MODE_NORMAL && stored && key >= thi) return 0.0f;
+    return x;
+}
+
 template <int MODE>
 __device__ __forceinline__ void stream_region(const float* __restrict__ g, float* __restrict__ e, int64_t gbeg,
-                                              int64_t gend, uint32_t tlo, uint32_t cap, float* __restrict__ cv,
-                                              int32_t* __restrict__ ci, float* __restrict__ vals,
-                                              int32_t* __restrict__ idx, int64_t out_base, uint32_t& cnt,
-                                              uint32_t& nf) {
+                                              int64_t gend, uint32_t tlo, uint32_t thi, uint32_t cap,
+                                              float* __restrict__ cv, int32_t* __restrict__ ci,
+                                              float* __restrict__ vals, int32_t* __restrict__ idx,
+                                              int64_t out_base, uint32_t& cnt, uint32_t& nf) {
     const int l = lane();
-    // body [a, b) is 16-byte aligned (g and e are 16-byte aligned)
+    // body [a, bnd) is 16-byte aligned (g and e are 16-byte aligned)
     int64_t a = (gbeg + 3) & ~static_cast<int64_t>(3);
     int64_t bnd = gend & ~static_cast<int64_t>(3);
     if (a > bnd) a = bnd = gend;  // region shorter than one aligned quad
     auto scalar_part = [&](int64_t from, int64_t to) {
-        // at most 3 elements, one per lane
+        // at most 3 elements, one per lane; lane l <-> index from + l
         const int64_t i = from + l;
         const bool ok = i < to;
         float xv[1] = {0.0f};
         bool hit[1] = {false};
+        uint32_t key = 0;
         if (ok) {
             xv[0] = g[i] + e[i];
-            const uint32_t key = key_of(xv[0]);
+            key = key_of(xv[0]);
             nf += key >= 0x7f800000u;
+            hit[0] = (MODE == MODE_NORMAL) && key >= tlo;
+        }
+        bool stored[1] = {false};
+        if (MODE == MODE_NORMAL) append_hits<1>(xv, hit, from + l, cnt, cap, cv, ci, stored);
+        if (ok) {
+            e[i] = stream_e<MODE>(xv[0], key, stored[0], thi);
             if (MODE == MODE_ALL) {
-                e[i] = 0.0f;
                 vals[out_base + (i - gbeg)] = xv[0];
                 idx[out_base + (i - gbeg)] = static_cast<int32_t>(i);
-            } else {
-                e[i] = xv[0];
-                hit[0] = (MODE == MODE_NORMAL) && key >= tlo;
             }
-        }
-        if (MODE == MODE_NORMAL) {
-            // lanes hold consecutive single elements: lane l <-> index from + l
-            append_hits<1>(xv, hit, from + l, cnt, cap, cv, ci);
         }
     };
     if (gbeg < a) scalar_part(gbeg, a);
     const f4* __restrict__ g4 = reinterpret_cast<const f4*>(g + a);
     f4* __restrict__ e4 = reinterpret_cast<f4*>(e + a);
     const int64_t nv = (bnd - a) >> 2;
-    for (int64_t base = 0; base < nv; base += kWave * kUnroll) {
+    // one iteration: kUnroll float4 of g and of e per lane, all loads issued
+    // before the first use; GUARD only for the last, partial iteration
+    auto iteration = [&](int64_t base, auto guard) {
+        constexpr bool GUARD = decltype(guard)::value;
         f4 gv[kUnroll], ev[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t j = base + u * kWave + l;
-            if (j < nv) {
+            if (!GUARD || j < nv) {
                 gv[u] = __builtin_nontemporal_load(g4 + j);
                 ev[u] = __builtin_nontemporal_load(e4 + j);
             } else {
@@ -396,44 +476,53 @@ __device__ __forceinline__ void stream_region(const float* __restrict__ g, float
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t j = base + u * kWave + l;
-            const bool ok = j < nv;
-            f4 x = gv[u] + ev[u];
+            const bool ok = !GUARD || j < nv;
+            const f4 x = gv[u] + ev[u];
             float xs[4] = {x.x, x.y, x.z, x.w};
+            uint32_t key[4];
             bool hit[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const uint32_t key = key_of(xs[t]);
-                nf += (ok && key >= 0x7f800000u) ? 1u : 0u;
-                hit[t] = (MODE == MODE_NORMAL) && ok && key >= tlo;
+                key[t] = key_of(xs[t]);
+                nf += (ok && key[t] >= 0x7f800000u) ? 1u : 0u;
+                hit[t] = (MODE == MODE_NORMAL) && ok && key[t] >= tlo;
             }
+            bool stored[4] = {false, false, false, false};
+            if (MODE == MODE_NORMAL) append_hits<4>(xs, hit, a + 4 * j, cnt, cap, cv, ci, stored);
             if (ok) {
+                const f4 eo = {stream_e<MODE>(xs[0], key[0], stored[0], thi),
+                               stream_e<MODE>(xs[1], key[1], stored[1], thi),
+                               stream_e<MODE>(xs[2], key[2], stored[2], thi),
+                               stream_e<MODE>(xs[3], key[3], stored[3], thi)};
+                __builtin_nontemporal_store(eo, e4 + j);
                 if (MODE == MODE_ALL) {
-                    __builtin_nontemporal_store(f4{0.f, 0.f, 0.f, 0.f}, e4 + j);
                     const int64_t i0 = a + 4 * j;
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         vals[out_base + (i0 + t - gbeg)] = xs[t];
                         idx[out_base + (i0 + t - gbeg)] = static_cast<int32_t>(i0 + t);
                     }
-                } else {
-                    __builtin_nontemporal_store(x, e4 + j);
                 }
             }
-            if (MODE == MODE_NORMAL) append_hits<4>(xs, hit, a + 4 * j, cnt, cap, cv, ci);
         }
-    }
+    };
+    constexpr int64_t kStep = kWave * kUnroll;
+    const int64_t nfull = nv / kStep * kStep;
+    for (int64_t base = 0; base < nfull; base += kStep) iteration(base, std::false_type{});
+    if (nfull < nv) iteration(nfull, std::true_type{});
     if (bnd < gend) scalar_part(bnd, gend);
 }
 
-// 2. the streaming pass; one wave per region
-__global__ __launch_bounds__(kBlock) void k_stream(const float* __restrict__ g, float* __restrict__ e,
-                                                   const SegPlan* __restrict__ plan, int32_t nseg,
-                                                   const int32_t* __restrict__ rb, int64_t R,
-                                                   SegState* __restrict__ st, uint32_t* __restrict__ region_cnt,
-                                                   float* __restrict__ cval, int32_t* __restrict__ cidx,
-                                                   float* __restrict__ vals, int32_t* __restrict__ idx,
-                                                   uint32_t* __restrict__ nonfinite) {
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
+// 2. the streaming pass; one wave per region of kRegion elements
+__global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict__ g, float* __restrict__ e,
+                                                         const SegPlan* __restrict__ plan, int32_t nseg,
+                                                         const int32_t* __restrict__ rb, int64_t R,
+                                                         SegState* __restrict__ st,
+                                                         uint32_t* __restrict__ region_cnt,
+                                                         uint32_t* __restrict__ grp_cnt, float* __restrict__ cval,
+                                                         int32_t* __restrict__ cidx, float* __restrict__ vals,
+                                                         int32_t* __restrict__ idx, uint32_t* __restrict__ nonfinite) {
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * kStreamWaves + threadIdx.x / kWave;
     if (w >= R) return;
     const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
     const SegPlan& P = plan[s];
@@ -447,50 +536,53 @@ __global__ __launch_bounds__(kBlock) void k_stream(const float* __restrict__ g, 
     float* cv = cval + P.cand_base + rl * P.cap;
     int32_t* ci = cidx + P.cand_base + rl * P.cap;
     if (mode == MODE_NORMAL) {
-        // a direct (dense) selection collects nothing: tlo above every key
-        const uint32_t tlo = P.direct ? 0xffffffffu : st[s].tlo;
-        stream_region<MODE_NORMAL>(g, e, gbeg, gend, tlo, cap, cv, ci, vals, idx, 0, cnt, nf);
+        // a direct (dense) selection collects nothing
+        const uint32_t tlo = P.direct ? kNoKey : st[s].tlo;
+        const uint32_t thi = P.direct ? kNoKey : st[s].thi;
+        stream_region<MODE_NORMAL>(g, e, gbeg, gend, tlo, thi, cap, cv, ci, vals, idx, 0, cnt, nf);
     } else if (mode == MODE_ALL) {
-        stream_region<MODE_ALL>(g, e, gbeg, gend, 0, 0, cv, ci, vals, idx, P.out_off + lbeg, cnt, nf);
+        stream_region<MODE_ALL>(g, e, gbeg, gend, 0, 0, 0, cv, ci, vals, idx, P.out_off + lbeg, cnt, nf);
     } else {
-        stream_region<MODE_NONE>(g, e, gbeg, gend, 0, 0, cv, ci, vals, idx, 0, cnt, nf);
+        stream_region<MODE_NONE>(g, e, gbeg, gend, 0, 0, 0, cv, ci, vals, idx, 0, cnt, nf);
     }
     nf = wave_sum(nf);
     if (lane() == 0) {
-        region_cnt[w] = cnt < cap ? cnt : cap;
+        const uint32_t kept = cnt < cap ? cnt : cap;
+        region_cnt[w] = kept;
         if (cnt > cap) atomicOr(&st[s].overflow, 1u);
+        if (kept) atomicAdd(&grp_cnt[P.group_begin + rl / kGroup], kept);
         if (nf && nonfinite) atomicAdd(nonfinite, nf);
     }
 }
 
-// 3. region offsets, per-tensor candidate totals and the path decision
+// 3. group offsets, per-tensor candidate totals and the path decision
 constexpr int kScanBlock = 1024;
-__global__ __launch_bounds__(kScanBlock) void k_scan_regions(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                             const int32_t* __restrict__ rb, int64_t R,
-                                                             const uint32_t* __restrict__ region_cnt,
-                                                             uint32_t* __restrict__ region_off,
-                                                             SegState* __restrict__ st, uint32_t* __restrict__ ccb,
-                                                             Header* __restrict__ hdr, uint32_t force_fallback) {
+__global__ __launch_bounds__(kScanBlock) void k_scan_groups(const SegPlan* __restrict__ plan, int32_t nseg,
+                                                            const int32_t* __restrict__ gbb, int64_t G,
+                                                            const uint32_t* __restrict__ grp_cnt,
+                                                            uint32_t* __restrict__ grp_off,
+                                                            SegState* __restrict__ st, uint32_t* __restrict__ ccb,
+                                                            Header* __restrict__ hdr, uint32_t force_fallback) {
     __shared__ uint32_t lds[kScanBlock / kWave + 1];
-    const int64_t per = (R + kScanBlock - 1) / kScanBlock;
-    const int64_t r0 = min(R, per * threadIdx.x), r1 = min(R, r0 + per);
-    uint32_t sum = 0;
-    for (int64_t r = r0; r < r1; ++r) sum += region_cnt[r];
-    uint32_t total;
-    uint32_t run = block_excl_scan<kScanBlock>(sum, lds, &total);
-    for (int64_t r = r0; r < r1; ++r) {
-        region_off[r] = run;
-        run += region_cnt[r];
+    uint32_t carry = 0;
+    for (int64_t t0 = 0; t0 < G; t0 += kScanBlock) {
+        const int64_t i = t0 + threadIdx.x;
+        const uint32_t v = i < G ? grp_cnt[i] : 0u;
+        uint32_t tt;
+        const uint32_t ex = block_excl_scan<kScanBlock>(v, lds, &tt);
+        if (i < G) grp_off[i] = carry + ex;
+        carry += tt;
     }
+    const uint32_t total = carry;
     __syncthreads();
-    uint32_t carry = 0, anyfb = 0;
+    uint32_t cc = 0, anyfb = 0;
     for (int32_t t0 = 0; t0 < nseg; t0 += kScanBlock) {
         const int32_t s = t0 + threadIdx.x;
         uint32_t cchunks = 0;
         if (s < nseg && plan[s].mode == MODE_NORMAL) {
-            const int64_t b = rb[s], en = rb[s + 1];
-            const uint32_t d0 = b < R ? region_off[b] : total;
-            const uint32_t d1 = en < R ? region_off[en] : total;
+            const int64_t b = gbb[s], en = gbb[s + 1];
+            const uint32_t d0 = b < G ? grp_off[b] : total;
+            const uint32_t d1 = en < G ? grp_off[en] : total;
             const uint32_t nc = d1 - d0;
             const bool fb = force_fallback || plan[s].direct || st[s].overflow ||
                             static_cast<int64_t>(nc) < plan[s].k;
@@ -506,36 +598,80 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_regions(const SegPlan* __re
         uint32_t tt;
         const uint32_t ex = block_excl_scan<kScanBlock>(cchunks, lds, &tt);
         if (s < nseg) {
-            ccb[s] = carry + ex;
-            st[s].cchunk_begin = carry + ex;
+            ccb[s] = cc + ex;
+            st[s].cchunk_begin = cc + ex;
         }
-        carry += tt;
+        cc += tt;
     }
     if (anyfb) atomicOr(&hdr->any_fallback, 1u);
     if (threadIdx.x == 0) {
-        ccb[nseg] = carry;
-        hdr->total_cchunks = carry;
+        ccb[nseg] = cc;
+        hdr->total_cchunks = cc;
     }
 }
 
-// 4. candidate slots -> dense index-ordered list
+// 4. per group of regions: candidate slots -> dense index-ordered list, and the
+//    first radix histogram (top 11 key bits) of the tensor
 __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                    const int32_t* __restrict__ rb, int64_t R,
+                                                    const int32_t* __restrict__ gbb, const int32_t* __restrict__ rb,
                                                     const SegState* __restrict__ st,
                                                     const uint32_t* __restrict__ region_cnt,
-                                                    const uint32_t* __restrict__ region_off,
+                                                    const uint32_t* __restrict__ grp_off,
                                                     const float* __restrict__ cval, const int32_t* __restrict__ cidx,
-                                                    float* __restrict__ dval, int32_t* __restrict__ didx) {
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
-    if (w >= R) return;
-    const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
+                                                    float* __restrict__ dval, int32_t* __restrict__ didx,
+                                                    uint32_t* __restrict__ rhist) {
+    __shared__ uint32_t loff[kGroup];
+    __shared__ uint32_t h[kRadixBins];
+    __shared__ uint32_t lds[kWavesPerBlock + 1];
+    const int gi = blockIdx.x;
+    const int s = upper_index(gbb, nseg, gi);
     if (plan[s].mode != MODE_NORMAL || st[s].fallback) return;
-    const uint32_t cnt = region_cnt[w];
-    const int64_t src = plan[s].cand_base + (w - rb[s]) * plan[s].cap;
-    const uint32_t dst = region_off[w];
-    for (uint32_t j = lane(); j < cnt; j += kWave) {
-        dval[dst + j] = cval[src + j];
-        didx[dst + j] = cidx[src + j];
+    const int gl = gi - gbb[s];
+    const int64_t r0 = rb[s] + static_cast<int64_t>(gl) * kGroup;  // first region (global)
+    const int nr = min(kGroup, plan[s].nregions - gl * kGroup);
+    const int t = threadIdx.x;
+    const uint32_t c = t < nr ? region_cnt[r0 + t] : 0u;
+    uint32_t total;
+    const uint32_t ex = block_excl_scan<kBlock>(c, lds, &total);
+    loff[t] = ex;
+    for (int i = t; i < kRadixBins; i += kBlock) h[i] = 0;
+    __syncthreads();
+    const uint32_t dbase = grp_off[gi];
+    const int64_t slot0 = plan[s].cand_base + (r0 - rb[s]) * plan[s].cap;
+    const int64_t cap = plan[s].cap;
+    for (uint32_t q = t; q < total; q += kBlock) {
+        const int r = upper_index(loff, nr, q);
+        const int64_t src = slot0 + r * cap + (q - loff[r]);
+        const float v = cval[src];
+        dval[dbase + q] = v;
+        didx[dbase + q] = cidx[src];
+        atomicAdd(&h[key_of(v) >> 20], 1u);
+    }
+    __syncthreads();
+    uint32_t* gh = rhist + static_cast<size_t>(s) * kRadixBins;
+    for (int i = t; i < kRadixBins; i += kBlock)
+        if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+// 4b. fallback tensors only: put back x where the stream already wrote e = 0
+__global__ __launch_bounds__(kBlock) void k_restore(const SegPlan* __restrict__ plan, int32_t nseg,
+                                                    const int32_t* __restrict__ rb, int64_t R,
+                                                    const SegState* __restrict__ st, const Header* __restrict__ hdr,
+                                                    const uint32_t* __restrict__ region_cnt,
+                                                    const float* __restrict__ cval,
+                                                    const int32_t* __restrict__ cidx, float* __restrict__ e) {
+    if (!hdr->any_fallback) return;
+    const int64_t nw = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+    for (int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; w < R; w += nw) {
+        const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
+        if (plan[s].mode != MODE_NORMAL || !st[s].fallback) continue;
+        const uint32_t thi = st[s].thi;
+        const uint32_t cnt = region_cnt[w];
+        const int64_t slot = plan[s].cand_base + (w - rb[s]) * plan[s].cap;
+        for (uint32_t j = lane(); j < cnt; j += kWave) {
+            const float v = cval[slot + j];
+            if (key_of(v) >= thi) e[cidx[slot + j]] = v;
+        }
     }
 }
 
@@ -554,65 +690,83 @@ __device__ __forceinline__ bool radix_digit(int pass, uint32_t key, uint32_t pre
     return (key >> 10) == prefix;
 }
 
-__device__ __forceinline__ void flush_hist(uint32_t* h, uint32_t* gh, int nb) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < nb; i += kBlock) {
-        if (h[i]) atomicAdd(&gh[i], h[i]);
-        h[i] = 0;
+// Work units of the select / emit kernels: candidate chunks of fast tensors
+// (kChunk entries of the dense list) followed by raw chunks of fallback
+// tensors (kChunk elements of x, which sits in e).
+struct Unit {
+    int s;
+    bool raw;
+    bool skip;
+    const float* v;        // values
+    const int32_t* id;     // indices (candidate units)
+    int64_t idx_base;      // first index (raw units)
+    uint32_t cnt;
+    uint32_t slot;         // index into cgt/ceq or rgt/req
+};
+
+__device__ __forceinline__ Unit unit_of(int64_t q, int64_t Qc, const SegPlan* plan, int32_t nseg,
+                                        const SegState* st, const uint32_t* ccb, const int32_t* rcb,
+                                        const float* dval, const int32_t* didx, const float* e) {
+    Unit u;
+    if (q < Qc) {
+        const uint32_t qq = static_cast<uint32_t>(q);
+        u.s = upper_index(ccb, nseg, qq);
+        const uint32_t lq = qq - ccb[u.s];
+        const uint32_t base = st[u.s].dense_off + lq * kChunk;
+        u.raw = false;
+        u.skip = false;
+        u.v = dval + base;
+        u.id = didx + base;
+        u.idx_base = 0;
+        u.cnt = min(static_cast<uint32_t>(kChunk), st[u.s].ncand - lq * kChunk);
+        u.slot = qq;
+    } else {
+        const int32_t qq = static_cast<int32_t>(q - Qc);
+        u.s = upper_index(rcb, nseg, qq);
+        const int64_t lbeg = static_cast<int64_t>(qq - rcb[u.s]) * kChunk;
+        u.raw = true;
+        u.skip = !st[u.s].fallback;
+        u.idx_base = plan[u.s].off + lbeg;
+        u.v = e + u.idx_base;
+        u.id = nullptr;
+        u.cnt = static_cast<uint32_t>(min(static_cast<int64_t>(kChunk), plan[u.s].n - lbeg));
+        u.slot = static_cast<uint32_t>(qq);
     }
-    __syncthreads();
+    return u;
 }
 
-// 5a. radix histogram over dense candidates
-__global__ __launch_bounds__(kBlock) void k_hist_cand(int pass, int32_t nseg, const SegState* __restrict__ st,
-                                                      const uint32_t* __restrict__ ccb, const Header* __restrict__ hdr,
-                                                      const float* __restrict__ dval, uint32_t* __restrict__ rhist) {
+// 5a. radix histograms (pass 0 only for fallback tensors: the compaction did it for the others)
+__global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
+                                                 const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
+                                                 const int32_t* __restrict__ rcb, int64_t QR,
+                                                 const Header* __restrict__ hdr, const float* __restrict__ dval,
+                                                 const float* __restrict__ e, uint32_t* __restrict__ rhist) {
     __shared__ uint32_t h[kRadixBins];
+    const int64_t Qc = pass > 0 ? hdr->total_cchunks : 0;
+    const int64_t Q = Qc + (hdr->any_fallback ? QR : 0);
+    if (Q == 0) return;
     const int nb = pass == 0 ? 2048 : 1024;
     for (int i = threadIdx.x; i < kRadixBins; i += kBlock) h[i] = 0;
     __syncthreads();
-    const uint32_t total = hdr->total_cchunks;
-    for (uint32_t q = blockIdx.x; q < total; q += gridDim.x) {
-        const int s = upper_index(ccb, nseg, q);
-        const uint32_t prefix = st[s].prefix;
-        const uint32_t lq = q - ccb[s];
-        const uint32_t base = st[s].dense_off + lq * kChunk;
-        const uint32_t cnt = min(static_cast<uint32_t>(kChunk), st[s].ncand - lq * kChunk);
-        for (uint32_t j = threadIdx.x; j < cnt; j += kBlock) {
+    for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
+        const Unit u = unit_of(q, Qc, plan, nseg, st, ccb, rcb, dval, nullptr, e);
+        if (u.skip) continue;
+        const uint32_t prefix = st[u.s].prefix;
+        for (uint32_t j = threadIdx.x; j < u.cnt; j += kBlock) {
             uint32_t d;
-            if (radix_digit(pass, key_of(dval[base + j]), prefix, &d)) atomicAdd(&h[d], 1u);
+            if (radix_digit(pass, key_of(u.v[j]), prefix, &d)) atomicAdd(&h[d], 1u);
         }
-        flush_hist(h, rhist + static_cast<size_t>(s) * kRadixBins, nb);
+        __syncthreads();
+        uint32_t* gh = rhist + static_cast<size_t>(u.s) * kRadixBins;
+        for (int i = threadIdx.x; i < nb; i += kBlock) {
+            if (h[i]) atomicAdd(&gh[i], h[i]);
+            h[i] = 0;
+        }
+        __syncthreads();
     }
 }
 
-// 5b. radix histogram over whole tensors on the fallback path (x is in e)
-__global__ __launch_bounds__(kBlock) void k_hist_raw(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
-                                                     const SegState* __restrict__ st,
-                                                     const int32_t* __restrict__ rcb, int64_t QR,
-                                                     const Header* __restrict__ hdr, const float* __restrict__ e,
-                                                     uint32_t* __restrict__ rhist) {
-    if (!hdr->any_fallback) return;
-    __shared__ uint32_t h[kRadixBins];
-    const int nb = pass == 0 ? 2048 : 1024;
-    for (int i = threadIdx.x; i < kRadixBins; i += kBlock) h[i] = 0;
-    __syncthreads();
-    for (int64_t q = blockIdx.x; q < QR; q += gridDim.x) {
-        const int s = upper_index(rcb, nseg, static_cast<int32_t>(q));
-        if (!st[s].fallback) continue;
-        const uint32_t prefix = st[s].prefix;
-        const int64_t lbeg = (q - rcb[s]) * kChunk;
-        const int64_t cnt = min(static_cast<int64_t>(kChunk), plan[s].n - lbeg);
-        const float* x = e + plan[s].off + lbeg;
-        for (int64_t j = threadIdx.x; j < cnt; j += kBlock) {
-            uint32_t d;
-            if (radix_digit(pass, key_of(x[j]), prefix, &d)) atomicAdd(&h[d], 1u);
-        }
-        flush_hist(h, rhist + static_cast<size_t>(s) * kRadixBins, nb);
-    }
-}
-
-// 5c. fix one digit per tensor
+// 5b. fix one digit per tensor
 __global__ __launch_bounds__(kBlock) void k_digit(int pass, const SegPlan* __restrict__ plan,
                                                   SegState* __restrict__ st, uint32_t* __restrict__ rhist) {
     __shared__ uint32_t lds[kWavesPerBlock + 1];
@@ -640,59 +794,43 @@ __global__ __launch_bounds__(kBlock) void k_digit(int pass, const SegPlan* __res
 }
 
 // 6a. per-unit counts of keys above T and equal to T
-template <bool RAW>
-__device__ __forceinline__ void unit_counts(const float* src, uint32_t cnt, uint32_t T, uint32_t* gt, uint32_t* eq) {
-    uint32_t a = 0, b = 0;
-    for (uint32_t j = threadIdx.x; j < cnt; j += kBlock) {
-        const uint32_t key = key_of(src[j]);
-        a += key > T;
-        b += key == T;
-    }
-    a = wave_sum(a);
-    b = wave_sum(b);
+__global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ plan, int32_t nseg,
+                                                  const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
+                                                  const int32_t* __restrict__ rcb, int64_t QR,
+                                                  const Header* __restrict__ hdr, const float* __restrict__ dval,
+                                                  const float* __restrict__ e, uint32_t* __restrict__ cgt,
+                                                  uint32_t* __restrict__ ceq, uint32_t* __restrict__ rgt,
+                                                  uint32_t* __restrict__ req) {
     __shared__ uint32_t sa[kWavesPerBlock], sb[kWavesPerBlock];
-    if (lane() == 0) {
-        sa[threadIdx.x / kWave] = a;
-        sb[threadIdx.x / kWave] = b;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t ta = 0, tb = 0;
-        for (int i = 0; i < kWavesPerBlock; ++i) {
-            ta += sa[i];
-            tb += sb[i];
+    const int64_t Qc = hdr->total_cchunks;
+    const int64_t Q = Qc + (hdr->any_fallback ? QR : 0);
+    for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
+        const Unit u = unit_of(q, Qc, plan, nseg, st, ccb, rcb, dval, nullptr, e);
+        if (u.skip) continue;
+        const uint32_t T = st[u.s].T;
+        uint32_t a = 0, b = 0;
+        for (uint32_t j = threadIdx.x; j < u.cnt; j += kBlock) {
+            const uint32_t key = key_of(u.v[j]);
+            a += key > T;
+            b += key == T;
         }
-        *gt = ta;
-        *eq = tb;
-    }
-    __syncthreads();
-}
-
-__global__ __launch_bounds__(kBlock) void k_count_cand(int32_t nseg, const SegState* __restrict__ st,
-                                                       const uint32_t* __restrict__ ccb,
-                                                       const Header* __restrict__ hdr, const float* __restrict__ dval,
-                                                       uint32_t* __restrict__ cgt, uint32_t* __restrict__ ceq) {
-    const uint32_t total = hdr->total_cchunks;
-    for (uint32_t q = blockIdx.x; q < total; q += gridDim.x) {
-        const int s = upper_index(ccb, nseg, q);
-        const uint32_t lq = q - ccb[s];
-        const uint32_t cnt = min(static_cast<uint32_t>(kChunk), st[s].ncand - lq * kChunk);
-        unit_counts<false>(dval + st[s].dense_off + lq * kChunk, cnt, st[s].T, cgt + q, ceq + q);
-    }
-}
-
-__global__ __launch_bounds__(kBlock) void k_count_raw(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                      const SegState* __restrict__ st,
-                                                      const int32_t* __restrict__ rcb, int64_t QR,
-                                                      const Header* __restrict__ hdr, const float* __restrict__ e,
-                                                      uint32_t* __restrict__ rgt, uint32_t* __restrict__ req) {
-    if (!hdr->any_fallback) return;
-    for (int64_t q = blockIdx.x; q < QR; q += gridDim.x) {
-        const int s = upper_index(rcb, nseg, static_cast<int32_t>(q));
-        if (!st[s].fallback) continue;
-        const int64_t lbeg = (q - rcb[s]) * kChunk;
-        const uint32_t cnt = static_cast<uint32_t>(min(static_cast<int64_t>(kChunk), plan[s].n - lbeg));
-        unit_counts<true>(e + plan[s].off + lbeg, cnt, st[s].T, rgt + q, req + q);
+        a = wave_sum(a);
+        b = wave_sum(b);
+        if (lane() == 0) {
+            sa[threadIdx.x / kWave] = a;
+            sb[threadIdx.x / kWave] = b;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t ta = 0, tb = 0;
+            for (int i = 0; i < kWavesPerBlock; ++i) {
+                ta += sa[i];
+                tb += sb[i];
+            }
+            (u.raw ? rgt : cgt)[u.slot] = ta;
+            (u.raw ? req : ceq)[u.slot] = tb;
+        }
+        __syncthreads();
     }
 }
 
@@ -730,84 +868,63 @@ __global__ __launch_bounds__(kBlock) void k_emit_scan(const SegPlan* __restrict_
     }
 }
 
-// 6c. ordered write of the kept entries
-template <bool RAW>
-__device__ __forceinline__ void unit_write(const float* __restrict__ src_v, const int32_t* __restrict__ src_i,
-                                           int64_t idx_base, uint32_t cnt, uint32_t T, uint32_t r, uint32_t G0,
-                                           uint32_t E0, float* __restrict__ e, float* __restrict__ vals,
-                                           int32_t* __restrict__ idx, int64_t out_off, int64_t kseg) {
+// 6c. ordered write of the kept entries.  Candidate units also settle the
+// residual of entries the stream cleared early (key >= thi): a kept one keeps
+// e = 0, a dropped one gets x back.
+__global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ plan, int32_t nseg,
+                                                  const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
+                                                  const int32_t* __restrict__ rcb, int64_t QR,
+                                                  const Header* __restrict__ hdr, const float* __restrict__ dval,
+                                                  const int32_t* __restrict__ didx, const uint32_t* __restrict__ cgt,
+                                                  const uint32_t* __restrict__ ceq, const uint32_t* __restrict__ rgt,
+                                                  const uint32_t* __restrict__ req, float* __restrict__ e,
+                                                  float* __restrict__ vals, int32_t* __restrict__ idx) {
     __shared__ uint64_t lds[kWavesPerBlock + 1];
-    const uint32_t j0 = threadIdx.x * kPerThread;
-    float v[kPerThread];
-    uint32_t ngt = 0, neq = 0;
+    const int64_t Qc = hdr->total_cchunks;
+    const int64_t Q = Qc + (hdr->any_fallback ? QR : 0);
+    for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
+        const Unit u = unit_of(q, Qc, plan, nseg, st, ccb, rcb, dval, didx, e);
+        if (u.skip) continue;
+        const uint32_t T = st[u.s].T, r = st[u.s].r;
+        const uint32_t thi = u.raw ? kNoKey : st[u.s].thi;
+        const uint32_t G0 = (u.raw ? rgt : cgt)[u.slot], E0 = (u.raw ? req : ceq)[u.slot];
+        const int64_t out_off = plan[u.s].out_off, kseg = plan[u.s].k;
+        const uint32_t j0 = threadIdx.x * kPerThread;
+        float v[kPerThread];
+        uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-        v[i] = (j0 + i < cnt) ? src_v[j0 + i] : 0.0f;
-        const uint32_t key = key_of(v[i]);
-        const bool ok = j0 + i < cnt;
-        ngt += ok && key > T;
-        neq += ok && key == T;
-    }
-    uint64_t tot;
-    const uint64_t before = block_excl_scan<kBlock>((static_cast<uint64_t>(ngt) << 32) | neq, lds, &tot);
-    uint32_t gtb = G0 + static_cast<uint32_t>(before >> 32);
-    uint32_t eqb = E0 + static_cast<uint32_t>(before);
+        for (int i = 0; i < kPerThread; ++i) {
+            const bool ok = j0 + i < u.cnt;
+            v[i] = ok ? u.v[j0 + i] : 0.0f;
+            const uint32_t key = key_of(v[i]);
+            ngt += ok && key > T;
+            neq += ok && key == T;
+        }
+        uint64_t tot;
+        const uint64_t before = block_excl_scan<kBlock>((static_cast<uint64_t>(ngt) << 32) | neq, lds, &tot);
+        uint32_t gtb = G0 + static_cast<uint32_t>(before >> 32);
+        uint32_t eqb = E0 + static_cast<uint32_t>(before);
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-        if (j0 + i >= cnt) continue;
-        const uint32_t key = key_of(v[i]);
-        int64_t pos = -1;
-        if (key > T) {
-            pos = static_cast<int64_t>(gtb) + min(r, eqb);
-            ++gtb;
-        } else if (key == T) {
-            if (eqb < r) pos = static_cast<int64_t>(gtb) + eqb;
-            ++eqb;
+        for (int i = 0; i < kPerThread; ++i) {
+            if (j0 + i >= u.cnt) continue;
+            const uint32_t key = key_of(v[i]);
+            int64_t pos = -1;
+            if (key > T) {
+                pos = static_cast<int64_t>(gtb) + min(r, eqb);
+                ++gtb;
+            } else if (key == T) {
+                if (eqb < r) pos = static_cast<int64_t>(gtb) + eqb;
+                ++eqb;
+            }
+            const int64_t id = u.raw ? u.idx_base + j0 + i : static_cast<int64_t>(u.id[j0 + i]);
+            if (pos >= 0 && pos < kseg) {
+                vals[out_off + pos] = v[i];
+                idx[out_off + pos] = static_cast<int32_t>(id);
+                if (key < thi) e[id] = 0.0f;
+            } else if (pos < 0 && key >= thi) {
+                e[id] = v[i];
+            }
         }
-        if (pos >= 0 && pos < kseg) {
-            const int64_t id = RAW ? idx_base + j0 + i : static_cast<int64_t>(src_i[j0 + i]);
-            vals[out_off + pos] = v[i];
-            idx[out_off + pos] = static_cast<int32_t>(id);
-            e[id] = 0.0f;
-        }
-    }
-}
-
-__global__ __launch_bounds__(kBlock) void k_write_cand(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                       const SegState* __restrict__ st,
-                                                       const uint32_t* __restrict__ ccb,
-                                                       const Header* __restrict__ hdr, const float* __restrict__ dval,
-                                                       const int32_t* __restrict__ didx,
-                                                       const uint32_t* __restrict__ cgt,
-                                                       const uint32_t* __restrict__ ceq, float* __restrict__ e,
-                                                       float* __restrict__ vals, int32_t* __restrict__ idx) {
-    const uint32_t total = hdr->total_cchunks;
-    for (uint32_t q = blockIdx.x; q < total; q += gridDim.x) {
-        const int s = upper_index(ccb, nseg, q);
-        const uint32_t lq = q - ccb[s];
-        const uint32_t cnt = min(static_cast<uint32_t>(kChunk), st[s].ncand - lq * kChunk);
-        const uint32_t base = st[s].dense_off + lq * kChunk;
-        unit_write<false>(dval + base, didx + base, 0, cnt, st[s].T, st[s].r, cgt[q], ceq[q], e, vals, idx,
-                          plan[s].out_off, plan[s].k);
-        __syncthreads();
-    }
-}
-
-__global__ __launch_bounds__(kBlock) void k_write_raw(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                      const SegState* __restrict__ st,
-                                                      const int32_t* __restrict__ rcb, int64_t QR,
-                                                      const Header* __restrict__ hdr, const uint32_t* __restrict__ rgt,
-                                                      const uint32_t* __restrict__ req, float* __restrict__ e,
-                                                      float* __restrict__ vals, int32_t* __restrict__ idx) {
-    if (!hdr->any_fallback) return;
-    for (int64_t q = blockIdx.x; q < QR; q += gridDim.x) {
-        const int s = upper_index(rcb, nseg, static_cast<int32_t>(q));
-        if (!st[s].fallback) continue;
-        const int64_t lbeg = (q - rcb[s]) * kChunk;
-        const uint32_t cnt = static_cast<uint32_t>(min(static_cast<int64_t>(kChunk), plan[s].n - lbeg));
-        const int64_t gb = plan[s].off + lbeg;
-        unit_write<true>(e + gb, nullptr, gb, cnt, st[s].T, st[s].r, rgt[q], req[q], e, vals, idx,
-                         plan[s].out_off, plan[s].k);
         __syncthreads();
     }
 }
@@ -816,10 +933,13 @@ __global__ __launch_bounds__(kBlock) void k_write_raw(const SegPlan* __restrict_
 static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* idx, void* ws, size_t ws_bytes,
                uint32_t* nonfinite, uint32_t flags, hipStream_t s) {
     const Layout L = make_layout(P);
+    WordChunk none;
+    none.n = 0;
     if (P.R == 0) {
         // nothing to stream: only the counter needs clearing
-        if (nonfinite) EF_TRY(launch("topk_init", k_init, dim3(1), dim3(kBlock), s, static_cast<uint4*>(nullptr),
-                                     static_cast<int64_t>(0), nonfinite));
+        if (nonfinite)
+            EF_TRY(launch("topk_init", k_init, dim3(1), dim3(kBlock), s, static_cast<uint4*>(nullptr),
+                          static_cast<int64_t>(0), nonfinite, static_cast<uint32_t*>(nullptr), none));
         return EF_OK;
     }
     if (!ws) return fail(EF_EWS, "workspace is NULL (%zu bytes needed)", L.total);
@@ -828,32 +948,39 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     uint8_t* W = static_cast<uint8_t*>(ws);
     auto at = [&](size_t o) { return W + o; };
 
-    // static tables: plan, region/sample/raw-chunk prefix tables
+    // static tables: plan and prefix tables; the first chunk rides on k_init
+    std::vector<uint32_t> words(L.static_end / 4, 0u);
     {
-        std::vector<uint32_t> words(L.static_end / 4, 0u);
         uint8_t* h = reinterpret_cast<uint8_t*>(words.data());
         memcpy(h + L.plan, P.seg.data(), P.seg.size() * sizeof(SegPlan));
         memcpy(h + L.rb, P.rb.data(), P.rb.size() * 4);
+        memcpy(h + L.gbb, P.gbb.data(), P.gbb.size() * 4);
         memcpy(h + L.sbb, P.sbb.data(), P.sbb.size() * 4);
         memcpy(h + L.rcb, P.rcb.data(), P.rcb.size() * 4);
-        EF_TRY(upload_words(W, words.data(), words.size(), s));
     }
+    WordChunk first;
+    first.n = static_cast<uint32_t>(std::min<size_t>(words.size(), kWordChunk));
+    memcpy(first.w, words.data(), first.n * 4);
+    if (words.size() > first.n)
+        EF_TRY(upload_words(W + first.n * 4, words.data() + first.n, words.size() - first.n, s));
     const int64_t nzero = static_cast<int64_t>((L.zero_end - L.header) / 16);
     const unsigned zgrid = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, cdiv(nzero, kBlock))));
     EF_TRY(launch("topk_init", k_init, dim3(zgrid), dim3(kBlock), s, reinterpret_cast<uint4*>(at(L.header)), nzero,
-                  nonfinite));
+                  nonfinite, reinterpret_cast<uint32_t*>(W), first));
 
     const SegPlan* plan = reinterpret_cast<const SegPlan*>(at(L.plan));
     const int32_t* rb = reinterpret_cast<const int32_t*>(at(L.rb));
+    const int32_t* gbb = reinterpret_cast<const int32_t*>(at(L.gbb));
     const int32_t* sbb = reinterpret_cast<const int32_t*>(at(L.sbb));
     const int32_t* rcb = reinterpret_cast<const int32_t*>(at(L.rcb));
     Header* hdr = reinterpret_cast<Header*>(at(L.header));
     SegState* st = reinterpret_cast<SegState*>(at(L.state));
     uint32_t* shist = reinterpret_cast<uint32_t*>(at(L.shist));
     uint32_t* rhist = reinterpret_cast<uint32_t*>(at(L.rhist));
+    uint32_t* grp_cnt = reinterpret_cast<uint32_t*>(at(L.grp_cnt));
     uint32_t* ccb = reinterpret_cast<uint32_t*>(at(L.ccb));
+    uint32_t* grp_off = reinterpret_cast<uint32_t*>(at(L.grp_off));
     uint32_t* region_cnt = reinterpret_cast<uint32_t*>(at(L.region_cnt));
-    uint32_t* region_off = reinterpret_cast<uint32_t*>(at(L.region_off));
     float* cval = reinterpret_cast<float*>(at(L.cval));
     int32_t* cidx = reinterpret_cast<int32_t*>(at(L.cidx));
     float* dval = reinterpret_cast<float*>(at(L.dval));
@@ -865,50 +992,45 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     const int32_t nseg = P.nseg;
 
     if (P.any_normal && P.SB > 0) {
-        EF_TRY(launch("topk_sample", k_sample, dim3(static_cast<unsigned>(P.SB)), dim3(kBlock), s, g,
+        EF_TRY(launch("topk_sample_hist", k_sample, dim3(static_cast<unsigned>(P.SB)), dim3(kBlock), s, g,
                       static_cast<const float*>(e), plan, nseg, sbb, shist));
         EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
                       static_cast<const uint32_t*>(shist), st));
     }
-    const unsigned sgrid = static_cast<unsigned>(cdiv(P.R, kWavesPerBlock));
-    EF_TRY(launch("topk_stream", k_stream, dim3(sgrid), dim3(kBlock), s, g, e, plan, nseg, rb, P.R, st, region_cnt,
-                  cval, cidx, vals, idx, nonfinite));
+    EF_TRY(launch("topk_stream", k_stream, dim3(static_cast<unsigned>(cdiv(P.R, kStreamWaves))), dim3(kStreamBlock),
+                  s, g, e, plan, nseg, rb, P.R, st, region_cnt, grp_cnt, cval, cidx, vals, idx, nonfinite));
     if (!P.any_normal) return EF_OK;
 
-    EF_TRY(launch("topk_scan_regions", k_scan_regions, dim3(1), dim3(kScanBlock), s, plan, nseg, rb, P.R,
-                  static_cast<const uint32_t*>(region_cnt), region_off, st, ccb, hdr,
+    EF_TRY(launch("topk_scan_groups", k_scan_groups, dim3(1), dim3(kScanBlock), s, plan, nseg, gbb, P.G,
+                  static_cast<const uint32_t*>(grp_cnt), grp_off, st, ccb, hdr,
                   static_cast<uint32_t>((flags & EF_FLAG_FORCE_FALLBACK) ? 1u : 0u)));
-    EF_TRY(launch("topk_compact", k_compact, dim3(sgrid), dim3(kBlock), s, plan, nseg, rb, P.R,
+    EF_TRY(launch("topk_compact", k_compact, dim3(static_cast<unsigned>(P.G)), dim3(kBlock), s, plan, nseg, gbb, rb,
                   static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
-                  static_cast<const uint32_t*>(region_off), static_cast<const float*>(cval),
-                  static_cast<const int32_t*>(cidx), dval, didx));
-    const unsigned gc = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, P.QC)));
-    const unsigned gr = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, P.QR)));
+                  static_cast<const uint32_t*>(grp_off), static_cast<const float*>(cval),
+                  static_cast<const int32_t*>(cidx), dval, didx, rhist));
+    const unsigned gres = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, cdiv(P.R, kWavesPerBlock))));
+    EF_TRY(launch("topk_restore", k_restore, dim3(gres), dim3(kBlock), s, plan, nseg, rb, P.R,
+                  static_cast<const SegState*>(st), static_cast<const Header*>(hdr),
+                  static_cast<const uint32_t*>(region_cnt), static_cast<const float*>(cval),
+                  static_cast<const int32_t*>(cidx), e));
+    const unsigned gu = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, P.QC + P.QR)));
     for (int pass = 0; pass < 3; ++pass) {
-        EF_TRY(launch("topk_hist_cand", k_hist_cand, dim3(gc), dim3(kBlock), s, pass, nseg,
-                      static_cast<const SegState*>(st), static_cast<const uint32_t*>(ccb),
-                      static_cast<const Header*>(hdr), static_cast<const float*>(dval), rhist));
-        EF_TRY(launch("topk_hist_raw", k_hist_raw, dim3(gr), dim3(kBlock), s, pass, plan, nseg,
-                      static_cast<const SegState*>(st), rcb, P.QR, static_cast<const Header*>(hdr),
+        EF_TRY(launch("topk_hist", k_hist, dim3(gu), dim3(kBlock), s, pass, plan, nseg,
+                      static_cast<const SegState*>(st), static_cast<const uint32_t*>(ccb), rcb, P.QR,
+                      static_cast<const Header*>(hdr), static_cast<const float*>(dval),
                       static_cast<const float*>(e), rhist));
         EF_TRY(launch("topk_digit", k_digit, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, pass, plan, st,
                       rhist));
     }
-    EF_TRY(launch("topk_count_cand", k_count_cand, dim3(gc), dim3(kBlock), s, nseg, static_cast<const SegState*>(st),
-                  static_cast<const uint32_t*>(ccb), static_cast<const Header*>(hdr),
-                  static_cast<const float*>(dval), cgt, ceq));
-    EF_TRY(launch("topk_count_raw", k_count_raw, dim3(gr), dim3(kBlock), s, plan, nseg,
-                  static_cast<const SegState*>(st), rcb, P.QR, static_cast<const Header*>(hdr),
-                  static_cast<const float*>(e), rgt, req));
+    EF_TRY(launch("topk_count", k_count, dim3(gu), dim3(kBlock), s, plan, nseg, static_cast<const SegState*>(st),
+                  static_cast<const uint32_t*>(ccb), rcb, P.QR, static_cast<const Header*>(hdr),
+                  static_cast<const float*>(dval), static_cast<const float*>(e), cgt, ceq, rgt, req));
     EF_TRY(launch("topk_emit_scan", k_emit_scan, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
                   static_cast<const SegState*>(st), rcb, cgt, ceq, rgt, req));
-    EF_TRY(launch("topk_write_cand", k_write_cand, dim3(gc), dim3(kBlock), s, plan, nseg,
-                  static_cast<const SegState*>(st), static_cast<const uint32_t*>(ccb),
-                  static_cast<const Header*>(hdr), static_cast<const float*>(dval),
-                  static_cast<const int32_t*>(didx), static_cast<const uint32_t*>(cgt),
-                  static_cast<const uint32_t*>(ceq), e, vals, idx));
-    EF_TRY(launch("topk_write_raw", k_write_raw, dim3(gr), dim3(kBlock), s, plan, nseg,
-                  static_cast<const SegState*>(st), rcb, P.QR, static_cast<const Header*>(hdr),
+    EF_TRY(launch("topk_write", k_write, dim3(gu), dim3(kBlock), s, plan, nseg, static_cast<const SegState*>(st),
+                  static_cast<const uint32_t*>(ccb), rcb, P.QR, static_cast<const Header*>(hdr),
+                  static_cast<const float*>(dval), static_cast<const int32_t*>(didx),
+                  static_cast<const uint32_t*>(cgt), static_cast<const uint32_t*>(ceq),
                   static_cast<const uint32_t*>(rgt), static_cast<const uint32_t*>(req), e, vals, idx));
     return EF_OK;
 }

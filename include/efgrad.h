@@ -201,7 +201,7 @@ int decode_blocks(const uint8_t* mask, const uint8_t* counts_m1, const uint8_t* 
  * ef_profile_read() waits for the recorded events and returns the summed
  * duration (ms) and launch count of recorded kernels whose label contains
  * `name`.  Meant for benchmarks: each recorded launch costs two event records.
- * Labels are "topk_stream", "topk_sample", ..., "sign_ef", "decode_scatter",
+ * Labels are "topk_stream", "topk_sample_hist", ..., "sign_ef", "decode_scatter",
  * "sgd_apply", "bitmap_*", "delta_*", "blocks_*".
  * ------------------------------------------------------------------------ */
 int ef_profile_enable(int on, const char* only);
