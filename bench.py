@@ -96,11 +96,17 @@ def main():
     ap.add_argument("--k", type=int, default=None, help="override k (testing only)")
     ap.add_argument("--cpu-sample", type=int, default=40_000_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="large", choices=["large", "flat", "bert", "sign", "decode"],
+                    help="large (default, the headline) or one of the other workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this library measures one GPU's share of the gradient; --gpus {args.gpus} is not "
               "supported (run with --gpus 1).", file=sys.stderr, flush=True)
         sys.exit(2)
+
+    if args.workload != "large":
+        other_workload(args)
+        return
 
     import torch
 
@@ -225,6 +231,148 @@ def main():
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def time_steps(step, W, K, kernel_label):
+    """Runs W untimed and K timed steps; returns (ms per step, mean ms of the kernel
+    labelled kernel_label, its launch count) with HIP events on the current stream."""
+    import torch
+
+    import error_feedback_gradient_amd as efg
+
+    for t in range(W):
+        step(t)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    efg.profile_enable(True, kernel_label)
+    torch.cuda.synchronize()
+    start.record()
+    for t in range(W, W + K):
+        step(t)
+    stop.record()
+    torch.cuda.synchronize()
+    kms, launches = efg.profile_read(kernel_label)
+    efg.profile_enable(False)
+    return start.elapsed_time(stop) / K, kms / max(1, launches), launches
+
+
+def other_workload(args):
+    """One JSON line for a non-headline workload (per-kernel roofline evidence)."""
+    import numpy as np
+    import torch
+
+    import error_feedback_gradient_amd as efg
+    import gen
+    import oracle
+
+    dev = torch.device("cuda:0")
+    W, K = args.warmup, args.steps
+    wl = args.workload
+    cpu = None
+    if wl == "flat":
+        n, k = gen.FLAT_N, gen.FLAT_K
+        grads = [torch.from_numpy(gen.flat_gradient(t)).to(dev) for t in range(W + K)]
+        e = torch.zeros(n, device=dev)
+        ws = efg.workspace(efg.ef_topk_workspace_bytes(n, k), dev)
+        vals = torch.empty(k, device=dev)
+        idx = torch.empty(k, dtype=torch.int32, device=dev)
+        step = lambda t: efg.ef_topk_compress(grads[t], e, k, vals=vals, idx=idx, ws=ws)
+        label, bpe, units, unit = "topk_stream", 12, n, "elems/s"
+        metric = "EF top-k compress elems/s, flat N=1e6 fp32, k=1e4"
+        desc = "flat fp32 gradient N=1e6 N(0,1), k=1e4 (1%), residual carried"
+        if not args.no_cpu_baseline:
+            g0 = gen.flat_gradient(0)
+            t0 = time.perf_counter()
+            oracle.topk(g0, np.zeros(n, np.float32), k)
+            cpu = (n, time.perf_counter() - t0, f"one full step, N = {n:,}, k = {k:,}")
+    elif wl == "bert":
+        off, ks = gen.bert_segments()
+        n = int(off[-1])
+        grads = [torch.from_numpy(gen.bert_gradient(t)).to(dev) for t in range(W + K)]
+        e = torch.zeros(n, device=dev)
+        ws = efg.workspace(efg.ef_topk_segmented_workspace_bytes(off, ks), dev)
+        K_ = int(ks.sum())
+        vals = torch.empty(K_, device=dev)
+        idx = torch.empty(K_, dtype=torch.int32, device=dev)
+        step = lambda t: efg.ef_topk_compress_segmented(grads[t], e, off, ks, vals=vals, idx=idx, ws=ws)
+        label, bpe, units, unit = "topk_stream", 12, n, "elems/s"
+        metric = "Layer-wise EF top-k compress elems/s, BERT-base 194 tensors fp32"
+        desc = "BERT-base layer-wise top-k (194 tensors, 108,888,576 elements, K=368,208), residual carried"
+        if not args.no_cpu_baseline:
+            g0 = gen.bert_gradient(0)
+            t0 = time.perf_counter()
+            oracle.topk_segmented(g0, np.zeros(n, np.float32), off, ks)
+            cpu = (n, time.perf_counter() - t0, "one full layer-wise step over all 194 tensors")
+    elif wl == "sign":
+        n = gen.SIGN_N
+        grads = [gen.sign_gradient_device(t, n, dev) for t in range(W + K)]
+        e = torch.zeros(n, device=dev)
+        m = torch.zeros(n, device=dev)
+        sgn = torch.empty(n, dtype=torch.int8, device=dev)
+        bits = torch.empty((n + 7) // 8, dtype=torch.uint8, device=dev)
+        step = lambda t: efg.ef_sign_compress(grads[t], e, m, gen.SIGN_BETA1, gen.SIGN_CLIP, sign_out=sgn, bits=bits)
+        label, bpe, units, unit = "sign_ef", 21.125, n, "elems/s"
+        metric = "1-bit sign EF + momentum elems/s, N=340M fp32"
+        desc = "1-bit sign EF + momentum, N=340M, int8 sign + packed bits, beta1=0.9, clip 5"
+        if not args.no_cpu_baseline:
+            ns = 40_000_000
+            g0 = gen.sign_gradient(0, n=ns)
+            z = np.zeros(ns, np.float32)
+            t0 = time.perf_counter()
+            oracle.sign(g0, z, z, gen.SIGN_BETA1, gen.SIGN_CLIP)
+            cpu = (ns, time.perf_counter() - t0, f"first {ns:,} elements of the step-0 gradient")
+    else:
+        n, P, kp = gen.DECODE_N, gen.DECODE_PACKETS, gen.DECODE_K
+        idx_l, val_l = [], []
+        for p in range(P):
+            g = gen.decode_packet_gradient(p)
+            sel = np.sort(np.argpartition(-np.abs(g), kp - 1)[:kp]).astype(np.int32)
+            idx_l.append(sel)
+            val_l.append(g[sel])
+        vals = torch.from_numpy(np.concatenate(val_l)).to(dev)
+        idx = torch.from_numpy(np.concatenate(idx_l)).to(dev)
+        pk_off = torch.arange(0, (P + 1) * kp, kp, dtype=torch.int64, device=dev)
+        G = torch.zeros(n, device=dev)
+        w = torch.from_numpy(gen.decode_weights()).to(dev)
+
+        def step(t):
+            G.zero_()
+            efg.sparse_decode_accumulate(G, vals, idx, pk_off)
+            efg.sgd_apply(w, G, gen.DECODE_LR)
+        label, bpe, units, unit = "sgd_apply", 12, n, "elems/s"
+        metric = "Sparse decode (16 packets) + SGD elems/s, N=25.6M fp32"
+        desc = "16 top-0.1% packets (25,600 entries each) scatter-added in packet order into G[25.6M], then w -= 0.1 G"
+        if not args.no_cpu_baseline:
+            Gh = np.zeros(n, np.float32)
+            w0 = gen.decode_weights()
+            offs = np.arange(0, (P + 1) * kp, kp, dtype=np.int64)
+            t0 = time.perf_counter()
+            Gr = oracle.decode(Gh, np.concatenate(val_l), np.concatenate(idx_l), offs)
+            oracle.sgd(w0, Gr, gen.DECODE_LR)
+            cpu = (n, time.perf_counter() - t0, "one full decode + SGD step")
+    ms, kms, launches = time_steps(step, W, K, label)
+    extra = {}
+    if wl == "decode":
+        _, dms, dl = time_steps(step, 1, K, "decode_scatter")
+        extra["decode_scatter_ms"] = dms
+        extra["decode_entries_per_s"] = P * kp / (dms * 1e-3)
+    achieved = bpe * units / (kms * 1e-3) / 1e9
+    res = {
+        "metric": metric, "value": units / (ms * 1e-3), "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": {"workload": desc, "n": units},
+        "roofline": {"kernel": label, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "avg_ms": kms, "launches": launches,
+                     "bytes_per_elem": bpe},
+    }
+    res.update(extra)
+    if cpu is not None:
+        cores = 1
+        res["cpu_baseline"] = {"value": cpu[0] / cpu[1], "unit": unit, "cores": cores, "kind": "oracle",
+                               "sample": cpu[2] + f"; {cpu[1]:.2f} s"}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":
