@@ -5,18 +5,38 @@
 // (clip before quantisation, NaN check after the error update, int8 storage);
 // section 1 (32 bits -> 1 bit per element).
 //
-// One streaming pass: each lane owns 8 consecutive elements (two 128-bit loads
-// per array), so its 8 sign bits are exactly one output byte and its 8 int8
-// signs one 64-bit store.  21.125 bytes move per element with both optional
-// outputs (read g, e, m; write e, m, int8, 1 bit).  Every product and sum is
-// rounded on its own: the library is compiled with -ffp-contract=off.
+// One streaming pass, one wave per contiguous region: each lane handles one
+// float4 of g, e and m per unroll step (128-bit non-temporal loads and
+// stores), writes its four int8 signs as one 32-bit store, and pairs with its
+// neighbour lane to form one byte of packed bits.  21.125 bytes move per
+// element with both optional outputs (read g, e, m; write e, m, int8, 1 bit).
+// Every product and sum is rounded on its own: the library is compiled with
+// -ffp-contract=off.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace efg {
 namespace sign {
 
-constexpr int kBlock = 256;
-constexpr int kMaxGrid = 16384;
+// Shape of the streaming kernel, measured on MI355X (fastest of a sweep over
+// regions 2048-16384, unroll 2-16, blocks 256-1024): one wave per region of EFG_SIGN_REGION
+// elements, EFG_SIGN_UNROLL float4 of each of g, e, m in flight per lane.
+#ifndef EFG_SIGN_BLOCK
+#define EFG_SIGN_BLOCK 512
+#endif
+#ifndef EFG_SIGN_REGION
+#define EFG_SIGN_REGION 8192
+#endif
+#ifndef EFG_SIGN_UNROLL
+#define EFG_SIGN_UNROLL 16
+#endif
+constexpr int kBlock = EFG_SIGN_BLOCK;
+constexpr int kWaves = kBlock / kWave;
+constexpr int kRegion = EFG_SIGN_REGION;  // multiple of 8 * 64
+constexpr int kUnroll = EFG_SIGN_UNROLL;
+static_assert(kRegion % 512 == 0, "regions must hold whole 8-element groups per lane pair");
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -48,46 +68,76 @@ __device__ __forceinline__ uint32_t nonfinite2(float a, float b) {
 
 __global__ void k_zero_u32(uint32_t* p) { *p = 0; }
 
+// Elements [0, n8) (n8 = n rounded down to 8) in regions of kRegion per wave:
+// lane l of unroll step u holds float4 j = base + 64u + l, i.e. elements
+// 4j..4j+3; lanes 2i and 2i+1 together hold one whole output byte of bits.
+// The last n - n8 elements are done by the first lane of wave 0.
 __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, float* __restrict__ e,
                                                  float* __restrict__ m, int64_t n, float beta1, float c,
                                                  float clip, int8_t* __restrict__ sgn, uint8_t* __restrict__ bits,
                                                  uint32_t* __restrict__ nonfinite) {
-    const int64_t groups = n >> 3;  // full groups of 8
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
+    const int64_t n8 = n & ~static_cast<int64_t>(7);
+    const int64_t beg = w * kRegion;
+    if (beg >= n8 && w != 0) return;
+    const int64_t end = min(beg + static_cast<int64_t>(kRegion), n8);
+    const int l = lane();
     uint32_t nf = 0;
-    const f4* g4 = reinterpret_cast<const f4*>(g);
-    f4* e4 = reinterpret_cast<f4*>(e);
-    f4* m4 = reinterpret_cast<f4*>(m);
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < groups; i += stride) {
-        const f4 ga = __builtin_nontemporal_load(g4 + 2 * i), gb = __builtin_nontemporal_load(g4 + 2 * i + 1);
-        const f4 ea = __builtin_nontemporal_load(e4 + 2 * i), eb = __builtin_nontemporal_load(e4 + 2 * i + 1);
-        const f4 ma = __builtin_nontemporal_load(m4 + 2 * i), mb = __builtin_nontemporal_load(m4 + 2 * i + 1);
-        const float gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-        const float ev[8] = {ea.x, ea.y, ea.z, ea.w, eb.x, eb.y, eb.z, eb.w};
-        const float mv[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
-        float eo[8], mo[8];
-        uint64_t s8 = 0;
-        uint32_t byte = 0;
+    const int64_t nv = beg < end ? (end - beg) >> 2 : 0;  // even
+    const f4* g4 = reinterpret_cast<const f4*>(g + beg);
+    f4* e4 = reinterpret_cast<f4*>(e + beg);
+    f4* m4 = reinterpret_cast<f4*>(m + beg);
+    uint32_t* s4 = sgn ? reinterpret_cast<uint32_t*>(sgn + beg) : nullptr;
+    uint8_t* b8 = bits ? bits + (beg >> 3) : nullptr;
+    auto iteration = [&](int64_t base, auto guard) {
+        constexpr bool GUARD = decltype(guard)::value;
+        f4 gv[kUnroll], ev[kUnroll], mv[kUnroll];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const Out o = step(gv[t], ev[t], mv[t], beta1, c, clip);
-            eo[t] = o.e;
-            mo[t] = o.m;
-            nf += nonfinite2(o.e, o.m);
-            s8 |= static_cast<uint64_t>(static_cast<uint8_t>(static_cast<int8_t>(o.s))) << (8 * t);
-            byte |= (o.s == 1 ? 1u : 0u) << t;
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = base + u * kWave + l;
+            if (!GUARD || j < nv) {
+                gv[u] = __builtin_nontemporal_load(g4 + j);
+                ev[u] = __builtin_nontemporal_load(e4 + j);
+                mv[u] = __builtin_nontemporal_load(m4 + j);
+            } else {
+                gv[u] = ev[u] = mv[u] = f4{0.f, 0.f, 0.f, 0.f};
+            }
         }
-        __builtin_nontemporal_store(f4{eo[0], eo[1], eo[2], eo[3]}, e4 + 2 * i);
-        __builtin_nontemporal_store(f4{eo[4], eo[5], eo[6], eo[7]}, e4 + 2 * i + 1);
-        __builtin_nontemporal_store(f4{mo[0], mo[1], mo[2], mo[3]}, m4 + 2 * i);
-        __builtin_nontemporal_store(f4{mo[4], mo[5], mo[6], mo[7]}, m4 + 2 * i + 1);
-        if (sgn) reinterpret_cast<uint64_t*>(sgn)[i] = s8;
-        if (bits) bits[i] = static_cast<uint8_t>(byte);
-    }
-    // tail: the last n % 8 elements, handled by the first thread of block 0
-    if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 7)) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = base + u * kWave + l;
+            const bool ok = !GUARD || j < nv;
+            const float ga[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
+            const float ea[4] = {ev[u].x, ev[u].y, ev[u].z, ev[u].w};
+            const float ma[4] = {mv[u].x, mv[u].y, mv[u].z, mv[u].w};
+            float eo[4], mo[4];
+            uint32_t s4v = 0, nib = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const Out o = step(ga[t], ea[t], ma[t], beta1, c, clip);
+                eo[t] = o.e;
+                mo[t] = o.m;
+                nf += ok ? nonfinite2(o.e, o.m) : 0u;
+                s4v |= static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(o.s))) << (8 * t);
+                nib |= (o.s == 1 ? 1u : 0u) << t;
+            }
+            const uint32_t hi = __shfl_xor(nib, 1, kWave);  // the odd lane's nibble
+            if (ok) {
+                __builtin_nontemporal_store(f4{eo[0], eo[1], eo[2], eo[3]}, e4 + j);
+                __builtin_nontemporal_store(f4{mo[0], mo[1], mo[2], mo[3]}, m4 + j);
+                if (s4) s4[j] = s4v;
+                if (b8 && !(l & 1)) b8[j >> 1] = static_cast<uint8_t>(nib | (hi << 4));
+            }
+        }
+    };
+    constexpr int64_t kStep = kWave * kUnroll;
+    const int64_t nfull = nv / kStep * kStep;
+    for (int64_t base = 0; base < nfull; base += kStep) iteration(base, std::false_type{});
+    if (nfull < nv) iteration(nfull, std::true_type{});
+    // the last n % 8 elements: one lane, one partial byte
+    if (w == 0 && l == 0 && n8 < n) {
         uint32_t byte = 0;
-        for (int64_t j = groups * 8; j < n; ++j) {
+        for (int64_t j = n8; j < n; ++j) {
             const Out o = step(g[j], e[j], m[j], beta1, c, clip);
             e[j] = o.e;
             m[j] = o.m;
@@ -95,11 +145,11 @@ __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, fl
             if (sgn) sgn[j] = static_cast<int8_t>(o.s);
             byte |= (o.s == 1 ? 1u : 0u) << (j & 7);
         }
-        if (bits) bits[groups] = static_cast<uint8_t>(byte);
+        if (bits) bits[n8 >> 3] = static_cast<uint8_t>(byte);
     }
     if (nonfinite) {
         nf = wave_sum(nf);
-        if (lane() == 0 && nf) atomicAdd(nonfinite, nf);
+        if (l == 0 && nf) atomicAdd(nonfinite, nf);
     }
 }
 
@@ -116,15 +166,15 @@ extern "C" int ef_sign_compress(const float* g, float* e, float* m, int64_t n, f
     if (n > 0 && (!g || !e || !m)) return fail(EF_EINVAL, "g, e and m must not be NULL");
     if (n > 0 && (!aligned16(g) || !aligned16(e) || !aligned16(m)))
         return fail(EF_EINVAL, "g, e and m must be 16-byte aligned");
-    if (sign_out && (reinterpret_cast<uintptr_t>(sign_out) & 7u))
-        return fail(EF_EINVAL, "sign_out must be 8-byte aligned");
+    if (sign_out && (reinterpret_cast<uintptr_t>(sign_out) & 3u))
+        return fail(EF_EINVAL, "sign_out must be 4-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (nonfinite) EF_TRY(launch("sign_zero", sign::k_zero_u32, dim3(1), dim3(1), s, nonfinite));
     if (n == 0) return EF_OK;
     const float c = 1.0f - beta1;
-    const int64_t groups = n >> 3;
-    int64_t grid = cdiv(groups > 0 ? groups : 1, sign::kBlock);
-    if (grid > sign::kMaxGrid) grid = sign::kMaxGrid;
+    const int64_t n8 = n & ~static_cast<int64_t>(7);
+    const int64_t waves = std::max<int64_t>(1, cdiv(n8, sign::kRegion));
+    const int64_t grid = cdiv(waves, sign::kWaves);
     return launch("sign_ef", sign::k_sign, dim3(static_cast<unsigned>(grid)), dim3(sign::kBlock), s, g, e, m, n,
                   beta1, c, clip, sign_out, bits, nonfinite);
 }

@@ -119,7 +119,7 @@ int ef_topk_compress_segmented(const float* g, float* e, int32_t nseg,
  *   sign_out[i] = q                        (int8, nullable)
  *   bits[i/8] bit (i%8) = (q == +1)        (uint8[ceil(n/8)], LSB first, pad 0, nullable)
  *   *nonfinite = count of non-finite new e plus non-finite new m (nullable)
- * 0 <= n <= 2^31 - 1; 0 <= beta1 <= 1; clip > 0.
+ * 0 <= n <= 2^31 - 1; 0 <= beta1 <= 1; clip > 0; sign_out 4-byte aligned.
  * ------------------------------------------------------------------------ */
 int ef_sign_compress(const float* g, float* e, float* m, int64_t n, float beta1,
                      float clip, int8_t* sign_out, uint8_t* bits, uint32_t* nonfinite,

@@ -128,7 +128,7 @@ def test_sign_argument_checks():
     assert ok(c=0.0) == efg.EF_EINVAL
     assert ok(m=None) == efg.EF_EINVAL
     assert ok(e=FAKE_ODD) == efg.EF_EINVAL
-    assert ok(s=FAKE + 4) == efg.EF_EINVAL
+    assert ok(s=FAKE + 2) == efg.EF_EINVAL
 
 
 def test_decode_and_sgd_argument_checks():
