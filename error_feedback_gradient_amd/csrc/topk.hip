@@ -66,8 +66,9 @@ constexpr int kGroup = 256;                        // regions per group (candida
 constexpr int kSampleChunk = 256;                  // contiguous elements per sample chunk
 constexpr int kSampleChunksMax = 4096;
 constexpr int kSampleChunksMin = 256;
+constexpr int kSampleBlock = 256;                  // threads of the sample kernel
 constexpr int kSampleChunksPerWave = 4;
-constexpr int kSampleBlockChunks = kSampleChunksPerWave * kWavesPerBlock;
+constexpr int kSampleBlockChunks = kSampleChunksPerWave * (kSampleBlock / kWave);
 constexpr int kSampleBins = 4096;
 constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
 constexpr int kChunk = 4096;                       // entries per block-unit in select and emit
@@ -89,7 +90,8 @@ struct alignas(16) SegPlan {
     int32_t mode;
     int32_t sample_chunks, sample_rank;
     int32_t sample_rank_hi, exhaustive, direct, raw_chunks;
-    int32_t pad[6];
+    int32_t compact_split;  // blocks per group in the compaction (1, 2, 4 or 8)
+    int32_t pad[5];
 };
 static_assert(sizeof(SegPlan) == 112, "SegPlan layout");
 
@@ -119,13 +121,14 @@ struct Plan {
     int64_t QR = 0;     // raw chunks (fallback units)
     int64_t QC = 0;     // bound on candidate chunks
     int64_t Ctot = 0;   // candidate slot entries
+    int64_t CB = 0;     // compaction blocks
     bool any_normal = false;
     std::vector<SegPlan> seg;
-    std::vector<int32_t> rb, gbb, sbb, rcb;  // prefix tables, nseg+1 each
+    std::vector<int32_t> rb, gbb, sbb, rcb, cbb;  // prefix tables, nseg+1 each
 };
 
 struct Layout {
-    size_t plan, rb, gbb, sbb, rcb, static_end;
+    size_t plan, rb, gbb, sbb, rcb, cbb, static_end;
     size_t header, state, shist, rhist, grp_cnt, zero_end;
     size_t ccb, grp_off, region_cnt, cval, cidx, dval, didx, cgt, ceq, rgt, req;
     size_t total;
@@ -141,6 +144,7 @@ static Layout make_layout(const Plan& p) {
     L.gbb = at; at += (ns + 1) * 4;
     L.sbb = at; at += (ns + 1) * 4;
     L.rcb = at; at += (ns + 1) * 4;
+    L.cbb = at; at += (ns + 1) * 4;
     at = round_up(at, 256);
     L.static_end = at;
     L.header = take(sizeof(Header));
@@ -179,6 +183,7 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
     p.gbb.assign(nseg + 1, 0);
     p.sbb.assign(nseg + 1, 0);
     p.rcb.assign(nseg + 1, 0);
+    p.cbb.assign(nseg + 1, 0);
     int64_t out = 0;
     for (int32_t s = 0; s < nseg; ++s) {
         const int64_t n = off[s + 1] - off[s];
@@ -232,6 +237,9 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
                 P.sample_rank = static_cast<int32_t>(m);
                 P.sample_rank_hi = static_cast<int32_t>(m_hi);
                 P.exhaustive = exhaustive ? 1 : 0;
+                // about 2048 expected candidates per compaction block
+                const double per_group = std::min<double>(P.nregions, kGroup) * std::min<double>(region_len, kRegion * rho);
+                P.compact_split = per_group > 8192 ? 8 : per_group > 4096 ? 4 : per_group > 2048 ? 2 : 1;
             }
             P.raw_chunks = static_cast<int32_t>(cdiv(n, kChunk));
             p.any_normal = true;
@@ -249,11 +257,14 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
         p.SB += cdiv(P.sample_chunks, kSampleBlockChunks);
         p.rcb[s] = static_cast<int32_t>(p.QR);
         p.QR += P.raw_chunks;
+        p.cbb[s] = static_cast<int32_t>(p.CB);
+        if (P.cap > 0) p.CB += static_cast<int64_t>(P.ngroups) * P.compact_split;
     }
     p.rb[nseg] = static_cast<int32_t>(p.R);
     p.gbb[nseg] = static_cast<int32_t>(p.G);
     p.sbb[nseg] = static_cast<int32_t>(p.SB);
     p.rcb[nseg] = static_cast<int32_t>(p.QR);
+    p.cbb[nseg] = static_cast<int32_t>(p.CB);
     p.QC += 1;
     return EF_OK;
 }
@@ -272,7 +283,7 @@ __global__ __launch_bounds__(kBlock) void k_init(uint4* zero, int64_t nvec, uint
 }
 
 // 1. sample histogram of x = g + e on the top 12 key bits
-__global__ __launch_bounds__(kBlock) void k_sample(const float* __restrict__ g, const float* __restrict__ e,
+__global__ __launch_bounds__(kSampleBlock) void k_sample(const float* __restrict__ g, const float* __restrict__ e,
                                                    const SegPlan* __restrict__ plan, int32_t nseg,
                                                    const int32_t* __restrict__ sbb, uint32_t* __restrict__ shist) {
     __shared__ uint32_t h[kSampleBins];
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(kBlock) void k_sample(const float* __restrict__ g, 
     const int64_t off = plan[s].off, n = plan[s].n;
     const int S = plan[s].sample_chunks;
     const bool exhaustive = plan[s].exhaustive != 0;
-    for (int i = threadIdx.x; i < kSampleBins; i += kBlock) h[i] = 0;
+    for (int i = threadIdx.x; i < kSampleBins; i += kSampleBlock) h[i] = 0;
     __syncthreads();
     const int w = threadIdx.x / kWave;
     const int l = lane();
@@ -308,7 +319,7 @@ __global__ __launch_bounds__(kBlock) void k_sample(const float* __restrict__ g, 
             if (ok[u][j]) atomicAdd(&h[key_of(xs[u][j]) >> kSampleShift], 1u);
     __syncthreads();
     uint32_t* gh = shist + static_cast<size_t>(s) * kSampleBins;
-    for (int i = threadIdx.x; i < kSampleBins; i += kBlock)
+    for (int i = threadIdx.x; i < kSampleBins; i += kSampleBlock)
         if (h[i]) atomicAdd(&gh[i], h[i]);
 }
 
@@ -611,10 +622,12 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_groups(const SegPlan* __res
 }
 
 // 4. per group of regions: candidate slots -> dense index-ordered list, and the
-//    first radix histogram (top 11 key bits) of the tensor
+//    first radix histogram (top 11 key bits) of the tensor.  A tensor with many
+//    candidates per group shares each group among compact_split blocks: every
+//    one scans the group's region counts and copies its own slice of regions.
 __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                    const int32_t* __restrict__ gbb, const int32_t* __restrict__ rb,
-                                                    const SegState* __restrict__ st,
+                                                    const int32_t* __restrict__ cbb, const int32_t* __restrict__ gbb,
+                                                    const int32_t* __restrict__ rb, const SegState* __restrict__ st,
                                                     const uint32_t* __restrict__ region_cnt,
                                                     const uint32_t* __restrict__ grp_off,
                                                     const float* __restrict__ cval, const int32_t* __restrict__ cidx,
@@ -623,12 +636,19 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     __shared__ uint32_t loff[kGroup];
     __shared__ uint32_t h[kRadixBins];
     __shared__ uint32_t lds[kWavesPerBlock + 1];
-    const int gi = blockIdx.x;
-    const int s = upper_index(gbb, nseg, gi);
+    const int b = blockIdx.x;
+    const int s = upper_index(cbb, nseg, b);
     if (plan[s].mode != MODE_NORMAL || st[s].fallback) return;
-    const int gl = gi - gbb[s];
+    const int split = plan[s].compact_split;
+    const int lb = b - cbb[s];
+    const int gl = lb / split, part = lb % split;
+    const int gi = gbb[s] + gl;
     const int64_t r0 = rb[s] + static_cast<int64_t>(gl) * kGroup;  // first region (global)
     const int nr = min(kGroup, plan[s].nregions - gl * kGroup);
+    const int slice = kGroup / split;
+    const int rs = part * slice;                                    // this block's regions [rs, re)
+    const int re = min(nr, rs + slice);
+    if (rs >= re) return;
     const int t = threadIdx.x;
     const uint32_t c = t < nr ? region_cnt[r0 + t] : 0u;
     uint32_t total;
@@ -636,11 +656,12 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     loff[t] = ex;
     for (int i = t; i < kRadixBins; i += kBlock) h[i] = 0;
     __syncthreads();
+    const uint32_t q0 = loff[rs], q1 = re < nr ? loff[re] : total;
     const uint32_t dbase = grp_off[gi];
     const int64_t slot0 = plan[s].cand_base + (r0 - rb[s]) * plan[s].cap;
     const int64_t cap = plan[s].cap;
-    for (uint32_t q = t; q < total; q += kBlock) {
-        const int r = upper_index(loff, nr, q);
+    for (uint32_t q = q0 + t; q < q1; q += kBlock) {
+        const int r = rs + upper_index(loff + rs, re - rs, q);
         const int64_t src = slot0 + r * cap + (q - loff[r]);
         const float v = cval[src];
         dval[dbase + q] = v;
@@ -648,9 +669,11 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
         atomicAdd(&h[key_of(v) >> 20], 1u);
     }
     __syncthreads();
-    uint32_t* gh = rhist + static_cast<size_t>(s) * kRadixBins;
-    for (int i = t; i < kRadixBins; i += kBlock)
-        if (h[i]) atomicAdd(&gh[i], h[i]);
+    if (q1 > q0) {
+        uint32_t* gh = rhist + static_cast<size_t>(s) * kRadixBins;
+        for (int i = t; i < kRadixBins; i += kBlock)
+            if (h[i]) atomicAdd(&gh[i], h[i]);
+    }
 }
 
 // 4b. fallback tensors only: put back x where the stream already wrote e = 0
@@ -948,7 +971,7 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     uint8_t* W = static_cast<uint8_t*>(ws);
     auto at = [&](size_t o) { return W + o; };
 
-    // static tables: plan and prefix tables; the first chunk rides on k_init
+    // static tables: plan and prefix tables
     std::vector<uint32_t> words(L.static_end / 4, 0u);
     {
         uint8_t* h = reinterpret_cast<uint8_t*>(words.data());
@@ -957,12 +980,18 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
         memcpy(h + L.gbb, P.gbb.data(), P.gbb.size() * 4);
         memcpy(h + L.sbb, P.sbb.data(), P.sbb.size() * 4);
         memcpy(h + L.rcb, P.rcb.data(), P.rcb.size() * 4);
+        memcpy(h + L.cbb, P.cbb.data(), P.cbb.size() * 4);
     }
+    // small plans (one tensor) ride on k_init's arguments; larger ones take one
+    // copy through the pinned staging ring
     WordChunk first;
-    first.n = static_cast<uint32_t>(std::min<size_t>(words.size(), kWordChunk));
-    memcpy(first.w, words.data(), first.n * 4);
-    if (words.size() > first.n)
-        EF_TRY(upload_words(W + first.n * 4, words.data() + first.n, words.size() - first.n, s));
+    first.n = 0;
+    if (words.size() <= kWordChunk) {
+        first.n = static_cast<uint32_t>(words.size());
+        memcpy(first.w, words.data(), first.n * 4);
+    } else {
+        EF_TRY(upload_bytes(W, words.data(), words.size() * 4, s));
+    }
     const int64_t nzero = static_cast<int64_t>((L.zero_end - L.header) / 16);
     const unsigned zgrid = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, cdiv(nzero, kBlock))));
     EF_TRY(launch("topk_init", k_init, dim3(zgrid), dim3(kBlock), s, reinterpret_cast<uint4*>(at(L.header)), nzero,
@@ -992,7 +1021,7 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     const int32_t nseg = P.nseg;
 
     if (P.any_normal && P.SB > 0) {
-        EF_TRY(launch("topk_sample_hist", k_sample, dim3(static_cast<unsigned>(P.SB)), dim3(kBlock), s, g,
+        EF_TRY(launch("topk_sample_hist", k_sample, dim3(static_cast<unsigned>(P.SB)), dim3(kSampleBlock), s, g,
                       static_cast<const float*>(e), plan, nseg, sbb, shist));
         EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
                       static_cast<const uint32_t*>(shist), st));
@@ -1004,7 +1033,8 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     EF_TRY(launch("topk_scan_groups", k_scan_groups, dim3(1), dim3(kScanBlock), s, plan, nseg, gbb, P.G,
                   static_cast<const uint32_t*>(grp_cnt), grp_off, st, ccb, hdr,
                   static_cast<uint32_t>((flags & EF_FLAG_FORCE_FALLBACK) ? 1u : 0u)));
-    EF_TRY(launch("topk_compact", k_compact, dim3(static_cast<unsigned>(P.G)), dim3(kBlock), s, plan, nseg, gbb, rb,
+    EF_TRY(launch("topk_compact", k_compact, dim3(static_cast<unsigned>(P.CB)), dim3(kBlock), s, plan, nseg,
+                  static_cast<const int32_t*>(reinterpret_cast<int32_t*>(at(L.cbb))), gbb, rb,
                   static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
                   static_cast<const uint32_t*>(grp_off), static_cast<const float*>(cval),
                   static_cast<const int32_t*>(cidx), dval, didx, rhist));

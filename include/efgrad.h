@@ -94,7 +94,10 @@ int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals
  *   K_s = seg_k[0] + ... + seg_k[s-1]; indices are positions in the packed
  *   buffer (seg_off[s] + local index), so idx is ascending overall.
  * *nonfinite counts over all tensors.  The host tables are read during the
- * call only.
+ * call only: the per-tensor plan built from them reaches the device through a
+ * small ring of pinned host staging buffers owned by the library (8 slots of
+ * at least 64 KB, kept for the life of the process; a slot is reused only once
+ * its previous copy has completed).
  * ------------------------------------------------------------------------ */
 size_t ef_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* seg_off,
                                          const int64_t* seg_k);
