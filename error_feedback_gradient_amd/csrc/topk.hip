@@ -130,7 +130,7 @@ struct Plan {
 struct Layout {
     size_t plan, rb, gbb, sbb, rcb, cbb, static_end;
     size_t header, state, shist, rhist, grp_cnt, zero_end;
-    size_t ccb, grp_off, region_cnt, cval, cidx, dval, didx, cgt, ceq, rgt, req;
+    size_t ccb, grp_off, region_cnt, cpair, dval, didx, cgt, ceq, rgt, req;
     size_t total;
 };
 
@@ -156,8 +156,7 @@ static Layout make_layout(const Plan& p) {
     L.ccb = take((ns + 1) * 4);
     L.grp_off = take(static_cast<size_t>(p.G) * 4);
     L.region_cnt = take(static_cast<size_t>(p.R) * 4);
-    L.cval = take(static_cast<size_t>(p.Ctot) * 4);
-    L.cidx = take(static_cast<size_t>(p.Ctot) * 4);
+    L.cpair = take(static_cast<size_t>(p.Ctot) * 8);
     L.dval = take(static_cast<size_t>(p.Ctot) * 4);
     L.didx = take(static_cast<size_t>(p.Ctot) * 4);
     L.cgt = take(static_cast<size_t>(p.QC) * 4);
@@ -390,8 +389,8 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // element j went into the slot (false once the slot is full).
 template <int NV>
 __device__ __forceinline__ void append_hits(const float (&x)[NV], const bool (&hit)[NV], int64_t gidx0,
-                                            uint32_t& cnt, uint32_t cap, float* __restrict__ cv,
-                                            int32_t* __restrict__ ci, bool (&stored)[NV]) {
+                                            uint32_t& cnt, uint32_t cap, uint2* __restrict__ cp,
+                                            bool (&stored)[NV]) {
     uint64_t bal[NV];
     uint64_t any = 0;
 #pragma unroll
@@ -412,8 +411,7 @@ __device__ __forceinline__ void append_hits(const float (&x)[NV], const bool (&h
     for (int j = 0; j < NV; ++j) {
         if (hit[j]) {
             if (pos < cap) {
-                cv[pos] = x[j];
-                ci[pos] = static_cast<int32_t>(gidx0 + j);
+                cp[pos] = make_uint2(__float_as_uint(x[j]), static_cast<uint32_t>(gidx0 + j));
                 stored[j] = true;
             }
             ++pos;
@@ -433,8 +431,8 @@ __device__ __forceinline__ float stream_e(float x, uint32_t key, bool stored, ui
 template <int MODE>
 __device__ __forceinline__ void stream_region(const float* __restrict__ g, float* __restrict__ e, int64_t gbeg,
                                               int64_t gend, uint32_t tlo, uint32_t thi, uint32_t cap,
-                                              float* __restrict__ cv, int32_t* __restrict__ ci,
-                                              float* __restrict__ vals, int32_t* __restrict__ idx,
+                                              uint2* __restrict__ cp, float* __restrict__ vals,
+                                              int32_t* __restrict__ idx,
                                               int64_t out_base, uint32_t& cnt, uint32_t& nf) {
     const int l = lane();
     // body [a, bnd) is 16-byte aligned (g and e are 16-byte aligned)
@@ -455,7 +453,7 @@ __device__ __forceinline__ void stream_region(const float* __restrict__ g, float
             hit[0] = (MODE == MODE_NORMAL) && key >= tlo;
         }
         bool stored[1] = {false};
-        if (MODE == MODE_NORMAL) append_hits<1>(xv, hit, from + l, cnt, cap, cv, ci, stored);
+        if (MODE == MODE_NORMAL) append_hits<1>(xv, hit, from + l, cnt, cap, cp, stored);
         if (ok) {
             e[i] = stream_e<MODE>(xv[0], key, stored[0], thi);
             if (MODE == MODE_ALL) {
@@ -491,20 +489,29 @@ __device__ __forceinline__ void stream_region(const float* __restrict__ g, float
             const f4 x = gv[u] + ev[u];
             float xs[4] = {x.x, x.y, x.z, x.w};
             uint32_t key[4];
-            bool hit[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                key[t] = key_of(xs[t]);
-                nf += (ok && key[t] >= 0x7f800000u) ? 1u : 0u;
-                hit[t] = (MODE == MODE_NORMAL) && ok && key[t] >= tlo;
+            for (int t = 0; t < 4; ++t) key[t] = key_of(xs[t]);
+            // common case in one compare: no candidate and no Inf/NaN among the four
+            const uint32_t kmax = max(max(key[0], key[1]), max(key[2], key[3]));
+            const uint32_t lim = MODE == MODE_NORMAL ? min(tlo, 0x7f800000u) : 0x7f800000u;
+            f4 eo = MODE == MODE_ALL ? f4{0.f, 0.f, 0.f, 0.f} : x;
+            if (__ballot(ok && kmax >= lim)) {
+                bool hit[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    nf += (ok && key[t] >= 0x7f800000u) ? 1u : 0u;
+                    hit[t] = (MODE == MODE_NORMAL) && ok && key[t] >= tlo;
+                }
+                if (MODE == MODE_NORMAL) {
+                    bool stored[4];
+                    append_hits<4>(xs, hit, a + 4 * j, cnt, cap, cp, stored);
+                    eo = f4{stream_e<MODE>(xs[0], key[0], stored[0], thi),
+                            stream_e<MODE>(xs[1], key[1], stored[1], thi),
+                            stream_e<MODE>(xs[2], key[2], stored[2], thi),
+                            stream_e<MODE>(xs[3], key[3], stored[3], thi)};
+                }
             }
-            bool stored[4] = {false, false, false, false};
-            if (MODE == MODE_NORMAL) append_hits<4>(xs, hit, a + 4 * j, cnt, cap, cv, ci, stored);
             if (ok) {
-                const f4 eo = {stream_e<MODE>(xs[0], key[0], stored[0], thi),
-                               stream_e<MODE>(xs[1], key[1], stored[1], thi),
-                               stream_e<MODE>(xs[2], key[2], stored[2], thi),
-                               stream_e<MODE>(xs[3], key[3], stored[3], thi)};
                 __builtin_nontemporal_store(eo, e4 + j);
                 if (MODE == MODE_ALL) {
                     const int64_t i0 = a + 4 * j;
@@ -530,8 +537,8 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
                                                          const int32_t* __restrict__ rb, int64_t R,
                                                          SegState* __restrict__ st,
                                                          uint32_t* __restrict__ region_cnt,
-                                                         uint32_t* __restrict__ grp_cnt, float* __restrict__ cval,
-                                                         int32_t* __restrict__ cidx, float* __restrict__ vals,
+                                                         uint32_t* __restrict__ grp_cnt, uint2* __restrict__ cpair,
+                                                         float* __restrict__ vals,
                                                          int32_t* __restrict__ idx, uint32_t* __restrict__ nonfinite) {
     const int64_t w = static_cast<int64_t>(blockIdx.x) * kStreamWaves + threadIdx.x / kWave;
     if (w >= R) return;
@@ -544,17 +551,16 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
     const int mode = P.mode;
     uint32_t cnt = 0, nf = 0;
     const uint32_t cap = static_cast<uint32_t>(P.cap);
-    float* cv = cval + P.cand_base + rl * P.cap;
-    int32_t* ci = cidx + P.cand_base + rl * P.cap;
+    uint2* cp = cpair + P.cand_base + rl * P.cap;
     if (mode == MODE_NORMAL) {
         // a direct (dense) selection collects nothing
         const uint32_t tlo = P.direct ? kNoKey : st[s].tlo;
         const uint32_t thi = P.direct ? kNoKey : st[s].thi;
-        stream_region<MODE_NORMAL>(g, e, gbeg, gend, tlo, thi, cap, cv, ci, vals, idx, 0, cnt, nf);
+        stream_region<MODE_NORMAL>(g, e, gbeg, gend, tlo, thi, cap, cp, vals, idx, 0, cnt, nf);
     } else if (mode == MODE_ALL) {
-        stream_region<MODE_ALL>(g, e, gbeg, gend, 0, 0, 0, cv, ci, vals, idx, P.out_off + lbeg, cnt, nf);
+        stream_region<MODE_ALL>(g, e, gbeg, gend, 0, 0, 0, cp, vals, idx, P.out_off + lbeg, cnt, nf);
     } else {
-        stream_region<MODE_NONE>(g, e, gbeg, gend, 0, 0, 0, cv, ci, vals, idx, 0, cnt, nf);
+        stream_region<MODE_NONE>(g, e, gbeg, gend, 0, 0, 0, cp, vals, idx, 0, cnt, nf);
     }
     nf = wave_sum(nf);
     if (lane() == 0) {
@@ -630,9 +636,8 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
                                                     const int32_t* __restrict__ rb, const SegState* __restrict__ st,
                                                     const uint32_t* __restrict__ region_cnt,
                                                     const uint32_t* __restrict__ grp_off,
-                                                    const float* __restrict__ cval, const int32_t* __restrict__ cidx,
-                                                    float* __restrict__ dval, int32_t* __restrict__ didx,
-                                                    uint32_t* __restrict__ rhist) {
+                                                    const uint2* __restrict__ cpair, float* __restrict__ dval,
+                                                    int32_t* __restrict__ didx, uint32_t* __restrict__ rhist) {
     __shared__ uint32_t loff[kGroup];
     __shared__ uint32_t h[kRadixBins];
     __shared__ uint32_t lds[kWavesPerBlock + 1];
@@ -663,9 +668,10 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     for (uint32_t q = q0 + t; q < q1; q += kBlock) {
         const int r = rs + upper_index(loff + rs, re - rs, q);
         const int64_t src = slot0 + r * cap + (q - loff[r]);
-        const float v = cval[src];
+        const uint2 pr = cpair[src];
+        const float v = __uint_as_float(pr.x);
         dval[dbase + q] = v;
-        didx[dbase + q] = cidx[src];
+        didx[dbase + q] = static_cast<int32_t>(pr.y);
         atomicAdd(&h[key_of(v) >> 20], 1u);
     }
     __syncthreads();
@@ -681,8 +687,7 @@ __global__ __launch_bounds__(kBlock) void k_restore(const SegPlan* __restrict__ 
                                                     const int32_t* __restrict__ rb, int64_t R,
                                                     const SegState* __restrict__ st, const Header* __restrict__ hdr,
                                                     const uint32_t* __restrict__ region_cnt,
-                                                    const float* __restrict__ cval,
-                                                    const int32_t* __restrict__ cidx, float* __restrict__ e) {
+                                                    const uint2* __restrict__ cpair, float* __restrict__ e) {
     if (!hdr->any_fallback) return;
     const int64_t nw = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
     for (int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; w < R; w += nw) {
@@ -691,9 +696,13 @@ __global__ __launch_bounds__(kBlock) void k_restore(const SegPlan* __restrict__ 
         const uint32_t thi = st[s].thi;
         const uint32_t cnt = region_cnt[w];
         const int64_t slot = plan[s].cand_base + (w - rb[s]) * plan[s].cap;
+        const int64_t lo = plan[s].off, hi = plan[s].off + plan[s].n;
         for (uint32_t j = lane(); j < cnt; j += kWave) {
-            const float v = cval[slot + j];
-            if (key_of(v) >= thi) e[cidx[slot + j]] = v;
+            const uint2 pr = cpair[slot + j];
+            const float v = __uint_as_float(pr.x);
+            // indices were written by the stream of this call; the range check
+            // keeps a workspace overwritten meanwhile from becoming a stray write
+            if (key_of(v) >= thi && pr.y >= lo && pr.y < hi) e[pr.y] = v;
         }
     }
 }
@@ -912,6 +921,7 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
         const uint32_t thi = u.raw ? kNoKey : st[u.s].thi;
         const uint32_t G0 = (u.raw ? rgt : cgt)[u.slot], E0 = (u.raw ? req : ceq)[u.slot];
         const int64_t out_off = plan[u.s].out_off, kseg = plan[u.s].k;
+        const int64_t seg_lo = plan[u.s].off, seg_hi = plan[u.s].off + plan[u.s].n;
         const uint32_t j0 = threadIdx.x * kPerThread;
         float v[kPerThread];
         uint32_t ngt = 0, neq = 0;
@@ -940,6 +950,7 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
                 ++eqb;
             }
             const int64_t id = u.raw ? u.idx_base + j0 + i : static_cast<int64_t>(u.id[j0 + i]);
+            if (id < seg_lo || id >= seg_hi) continue;  // only if the workspace was overwritten meanwhile
             if (pos >= 0 && pos < kseg) {
                 vals[out_off + pos] = v[i];
                 idx[out_off + pos] = static_cast<int32_t>(id);
@@ -1010,8 +1021,7 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     uint32_t* ccb = reinterpret_cast<uint32_t*>(at(L.ccb));
     uint32_t* grp_off = reinterpret_cast<uint32_t*>(at(L.grp_off));
     uint32_t* region_cnt = reinterpret_cast<uint32_t*>(at(L.region_cnt));
-    float* cval = reinterpret_cast<float*>(at(L.cval));
-    int32_t* cidx = reinterpret_cast<int32_t*>(at(L.cidx));
+    uint2* cpair = reinterpret_cast<uint2*>(at(L.cpair));
     float* dval = reinterpret_cast<float*>(at(L.dval));
     int32_t* didx = reinterpret_cast<int32_t*>(at(L.didx));
     uint32_t* cgt = reinterpret_cast<uint32_t*>(at(L.cgt));
@@ -1027,7 +1037,7 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
                       static_cast<const uint32_t*>(shist), st));
     }
     EF_TRY(launch("topk_stream", k_stream, dim3(static_cast<unsigned>(cdiv(P.R, kStreamWaves))), dim3(kStreamBlock),
-                  s, g, e, plan, nseg, rb, P.R, st, region_cnt, grp_cnt, cval, cidx, vals, idx, nonfinite));
+                  s, g, e, plan, nseg, rb, P.R, st, region_cnt, grp_cnt, cpair, vals, idx, nonfinite));
     if (!P.any_normal) return EF_OK;
 
     EF_TRY(launch("topk_scan_groups", k_scan_groups, dim3(1), dim3(kScanBlock), s, plan, nseg, gbb, P.G,
@@ -1036,13 +1046,11 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     EF_TRY(launch("topk_compact", k_compact, dim3(static_cast<unsigned>(P.CB)), dim3(kBlock), s, plan, nseg,
                   static_cast<const int32_t*>(reinterpret_cast<int32_t*>(at(L.cbb))), gbb, rb,
                   static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
-                  static_cast<const uint32_t*>(grp_off), static_cast<const float*>(cval),
-                  static_cast<const int32_t*>(cidx), dval, didx, rhist));
+                  static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair), dval, didx, rhist));
     const unsigned gres = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, cdiv(P.R, kWavesPerBlock))));
     EF_TRY(launch("topk_restore", k_restore, dim3(gres), dim3(kBlock), s, plan, nseg, rb, P.R,
                   static_cast<const SegState*>(st), static_cast<const Header*>(hdr),
-                  static_cast<const uint32_t*>(region_cnt), static_cast<const float*>(cval),
-                  static_cast<const int32_t*>(cidx), e));
+                  static_cast<const uint32_t*>(region_cnt), static_cast<const uint2*>(cpair), e));
     const unsigned gu = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, P.QC + P.QR)));
     for (int pass = 0; pass < 3; ++pass) {
         EF_TRY(launch("topk_hist", k_hist, dim3(gu), dim3(kBlock), s, pass, plan, nseg,
