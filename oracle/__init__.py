@@ -50,6 +50,7 @@ def lib():
             "orc_delta_decode": [p, i64, i64, p],
             "orc_blocks_encode": [p, i64, i64, p, p, p, p],
             "orc_blocks_decode": [p, p, p, i64, p, i64, p],
+            "orc_quantize_int8": [p, p, i64, p, p, p],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -186,3 +187,14 @@ def blocks_decode(mask, counts_m1, offs, n, k_cap=None):
                                    _ptr(offs if offs.size else np.zeros(1, np.uint8)), n, _ptr(idx),
                                    k_cap, _ptr(k)), "blocks_decode")
     return idx[:min(int(k[0]), k_cap)], int(k[0])
+
+
+def quantize_int8(vals, idx, e):
+    """Returns (q int8, scale, e_new); e is not modified."""
+    vals = _f32(vals)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    e2 = _f32(e).copy()
+    q = np.empty(max(1, vals.size), np.int8)
+    sc = np.zeros(1, np.float32)
+    _check(lib().orc_quantize_int8(_ptr(vals), _ptr(idx), vals.size, _ptr(e2), _ptr(q), _ptr(sc)), "quantize_int8")
+    return q[:vals.size], float(sc[0]), e2

@@ -352,3 +352,44 @@ int orc_blocks_decode(const uint8_t* mask, const uint8_t* counts_m1, const uint8
     *k_out = k;
     return ORC_OK;
 }
+
+/*
+ * 8-bit quantisation of a sent packet, with the quantisation error kept in the
+ * residual.  [SPARSE] "与其他压缩技术的比较" (comparison with other compression):
+ * systems combine top-k with 8-bit quantisation of the kept values.
+ * READINGS: one symmetric scale per packet; amax = largest finite |v|;
+ *   inv   = 127 / amax            (float32 division, correctly rounded)
+ *   scale = amax / 127            (float32 division, correctly rounded)
+ *   q     = rint(v * inv)         (float32 product, round half to even), clamped to [-127, 127]
+ *   e[idx] = v - q * scale        (float32 product, then float32 difference)
+ * A non-finite v, and every v when amax is 0 (all kept values are +-0) or when
+ * no value is finite, gets q = 0 and keeps all of v in the residual.
+ * *scale_out receives scale (0 when amax is 0 or absent).
+ */
+int orc_quantize_int8(const float* vals, const int32_t* idx, int64_t k, float* e, int8_t* q,
+                      float* scale_out) {
+    if (k < 0) return ORC_EINVAL;
+    float amax = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+        float a = fabsf(vals[j]);
+        if (!is_nonfinite(vals[j]) && a > amax) amax = a;
+    }
+    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    const float scale = amax > 0.0f ? amax / 127.0f : 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+        float v = vals[j];
+        int qi = 0;
+        if (amax > 0.0f && !is_nonfinite(v)) {
+            float t = v * inv;
+            float r = rintf(t);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            qi = (int)r;
+        }
+        float deq = (float)qi * scale;
+        q[j] = (int8_t)qi;
+        e[idx[j]] = v - deq;
+    }
+    *scale_out = scale;
+    return ORC_OK;
+}
