@@ -96,7 +96,7 @@ def main():
     ap.add_argument("--k", type=int, default=None, help="override k (testing only)")
     ap.add_argument("--cpu-sample", type=int, default=40_000_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="large", choices=["large", "flat", "bert", "sign", "decode"],
+    ap.add_argument("--workload", default="large", choices=["large", "flat", "bert", "sign", "decode", "quant"],
                     help="large (default, the headline) or one of the other workloads")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -253,7 +253,8 @@ def time_steps(step, W, K, kernel_label):
     torch.cuda.synchronize()
     kms, launches = efg.profile_read(kernel_label)
     efg.profile_enable(False)
-    return start.elapsed_time(stop) / K, kms / max(1, launches), launches
+    # time of the labelled kernels per step (equal to the mean launch when one kernel matches)
+    return start.elapsed_time(stop) / K, kms / K, launches
 
 
 def other_workload(args):
@@ -321,6 +322,25 @@ def other_workload(args):
             t0 = time.perf_counter()
             oracle.sign(g0, z, z, gen.SIGN_BETA1, gen.SIGN_CLIP)
             cpu = (ns, time.perf_counter() - t0, f"first {ns:,} elements of the step-0 gradient")
+    elif wl == "quant":
+        n, k = gen.LARGE_N, gen.LARGE_K
+        idx_h = gen.sorted_unique_indices(n, k, 405)
+        v_h = gen.large_gradient(11, n=k)
+        vals = torch.from_numpy(v_h).to(dev)
+        idx = torch.from_numpy(idx_h).to(dev)
+        e = torch.zeros(n, device=dev)
+        q = torch.empty(k, dtype=torch.int8, device=dev)
+        sc = torch.empty(1, device=dev)
+        wsq = efg.workspace(efg.lib().ef_quantize_workspace_bytes(k), dev)
+        step = lambda t: efg.ef_quantize_int8(vals, idx, e, q=q, scale=sc, ws=wsq)
+        # read v twice and idx once, write q and one residual word per entry
+        label, bpe, units, unit = "quant_", 17, k, "entries/s"
+        metric = "8-bit packet quantisation entries/s, k=1.3e6 of N=1.3e9"
+        desc = "8-bit quantisation of a 1.3e6-entry packet (values of the large workload's law) into int8 with one scale, error kept in the residual"
+        if not args.no_cpu_baseline:
+            t0 = time.perf_counter()
+            oracle.quantize_int8(v_h, np.arange(k, dtype=np.int32), np.zeros(k, np.float32))
+            cpu = (k, time.perf_counter() - t0, f"one full packet, k = {k:,}")
     else:
         n, P, kp = gen.DECODE_N, gen.DECODE_PACKETS, gen.DECODE_K
         idx_l, val_l = [], []
@@ -362,8 +382,8 @@ def other_workload(args):
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": {"workload": desc, "n": units},
         "roofline": {"kernel": label, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "avg_ms": kms, "launches": launches,
-                     "bytes_per_elem": bpe},
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "kernel_ms_per_step": kms,
+                     "launches": launches, "bytes_per_elem": bpe},
     }
     res.update(extra)
     if cpu is not None:

@@ -32,6 +32,8 @@ SIGNATURES = {
     "ef_topk_segmented_workspace_bytes": (_sz, [_i32, _p, _p]),
     "ef_topk_compress_segmented": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _sz, _p, _u32, _p]),
     "ef_sign_compress": (C.c_int, [_p, _p, _p, _i64, _f, _f, _p, _p, _p, _p]),
+    "ef_quantize_workspace_bytes": (_sz, [_i64]),
+    "ef_quantize_int8": (C.c_int, [_p, _p, _i64, _p, _i64, _p, _p, _p, _sz, _p]),
     "sparse_decode_accumulate": (C.c_int, [_p, _i64, _i32, _p, _p, _p, _p, _p]),
     "sgd_apply": (C.c_int, [_p, _p, _i64, _f, _p]),
     "encode_bitmap": (C.c_int, [_p, _i64, _i64, _p, _p]),
@@ -197,6 +199,25 @@ def ef_sign_compress(g, e, m, beta1=0.9, clip=5.0, sign_out=None, bits=None, non
     _check(lib().ef_sign_compress(_ptr(g), _ptr(e), _ptr(m), n, beta1, clip, _ptr(sign_out), _ptr(bits),
                                   _ptr(nonfinite), _stream(dev)), "ef_sign_compress")
     return sign_out, bits
+
+
+# ---------------------------------------------------------------- 8-bit packet values
+def ef_quantize_int8(vals, idx, e, q=None, scale=None, ws=None):
+    """q = rint(vals * 127/amax), e[idx] = vals - q*scale; returns (q int8, scale float32[1])."""
+    dev = _gpu(vals, "vals")
+    k = vals.numel()
+    _need(vals, torch.float32, dev, "vals")
+    _need(idx, torch.int32, dev, "idx", k)
+    _need(e, torch.float32, dev, "e")
+    if q is None:
+        q = torch.empty(max(k, 1), dtype=torch.int8, device=dev)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(lib().ef_quantize_workspace_bytes(k), dev)
+    _check(lib().ef_quantize_int8(_ptr(vals), _ptr(idx), k, _ptr(e), e.numel(), _ptr(q), _ptr(scale), _ptr(ws),
+                                  ws.numel(), _stream(dev)), "ef_quantize_int8")
+    return q[:k], scale
 
 
 # ---------------------------------------------------------------- decode / sgd

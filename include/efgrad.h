@@ -129,6 +129,26 @@ int ef_sign_compress(const float* g, float* e, float* m, int64_t n, float beta1,
                      void* stream);
 
 /* ------------------------------------------------------------------------
+ * 8-bit quantisation of a sent packet, the quantisation error kept in the
+ * residual.  [SPARSE] "与其他压缩技术的比较" (comparison with other compression
+ * techniques): top-k followed by 8-bit quantisation of the kept values.
+ *
+ * Applied after ef_topk_compress to its (vals, idx) and the residual e[n]:
+ *   amax  = largest finite |vals[j]|           (0 if none)
+ *   inv   = 127 / amax,  scale = amax / 127     (float32, correctly rounded)
+ *   q[j]  = rint(vals[j] * inv) clamped to [-127, 127]   (round half to even;
+ *           0 for a non-finite value, when amax = 0, or for a NaN product)
+ *   e[idx[j]] = vals[j] - q[j] * scale         (float32; the receiver gets
+ *           q[j] * scale, and q*scale + e' equals vals[j] exactly)
+ *   *scale_out = scale                          (device float)
+ * Entries whose idx lies outside [0, n) update no residual.  ws: at least
+ * ef_quantize_workspace_bytes(k) bytes, 4-byte aligned.
+ * ------------------------------------------------------------------------ */
+size_t ef_quantize_workspace_bytes(int64_t k);
+int ef_quantize_int8(const float* vals, const int32_t* idx, int64_t k, float* e, int64_t n,
+                     int8_t* q, float* scale_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Receiver-side aggregation of sparse packets.  [SPARSE] "梯度稀疏化的基本原理"
  * (values sharing an index are summed) and "详细算法流程" step 6.
  *

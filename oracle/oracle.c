@@ -363,7 +363,8 @@ int orc_blocks_decode(const uint8_t* mask, const uint8_t* counts_m1, const uint8
  *   q     = rint(v * inv)         (float32 product, round half to even), clamped to [-127, 127]
  *   e[idx] = v - q * scale        (float32 product, then float32 difference)
  * A non-finite v, and every v when amax is 0 (all kept values are +-0) or when
- * no value is finite, gets q = 0 and keeps all of v in the residual.
+ * no value is finite, gets q = 0 and keeps all of v in the residual.  A NaN
+ * product (0 * inf, only when amax is below 127 / FLT_MAX) also gives q = 0.
  * *scale_out receives scale (0 when amax is 0 or absent).
  */
 int orc_quantize_int8(const float* vals, const int32_t* idx, int64_t k, float* e, int8_t* q,
@@ -382,6 +383,7 @@ int orc_quantize_int8(const float* vals, const int32_t* idx, int64_t k, float* e
         if (amax > 0.0f && !is_nonfinite(v)) {
             float t = v * inv;
             float r = rintf(t);
+            if (r != r) r = 0.0f;  /* 0 * inf when amax is below 127 / FLT_MAX */
             if (r > 127.0f) r = 127.0f;
             if (r < -127.0f) r = -127.0f;
             qi = (int)r;
