@@ -96,6 +96,7 @@ def main():
     ap.add_argument("--k", type=int, default=None, help="override k (testing only)")
     ap.add_argument("--cpu-sample", type=int, default=40_000_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stats", action="store_true", help="also compute the fused monitoring statistics")
     ap.add_argument("--workload", default="large", choices=["large", "flat", "bert", "sign", "decode", "quant"],
                     help="large (default, the headline) or one of the other workloads")
     args = ap.parse_args()
@@ -131,8 +132,10 @@ def main():
     wsb = efg.workspace(efg.lib().blocks_workspace_bytes(k, n), dev)
     nonfinite = torch.zeros(1, dtype=torch.int32, device=dev)
 
+    stats = torch.zeros(2, dtype=torch.float64, device=dev) if args.stats else None
+
     def step(t):
-        efg.ef_topk_compress(grads[t], e, k, vals=vals, idx=idx, ws=ws, nonfinite=nonfinite)
+        efg.ef_topk_compress(grads[t], e, k, vals=vals, idx=idx, ws=ws, nonfinite=nonfinite, stats=stats)
         efg.encode_blocks(idx, n, mask=mask, counts_m1=counts, offs=offs, nblk_out=nblk, ws=wsb)
 
     for t in range(W):
@@ -204,7 +207,7 @@ def main():
             if args.n is None else f"reduced test size N={n}",
             "n": n,
             "k": k,
-            "step": "ef_topk_compress + encode_blocks",
+            "step": "ef_topk_compress + encode_blocks" + (" (with monitoring statistics)" if args.stats else ""),
             "parallelism": "single GPU",
         },
         "hbm_GBps_step": STREAM_BYTES_PER_ELEM * n / (ms_per_step * 1e-3) / 1e9,

@@ -28,10 +28,11 @@ SIGNATURES = {
     "ef_last_error": (C.c_char_p, []),
     "ef_version": (C.c_char_p, []),
     "ef_topk_workspace_bytes": (_sz, [_i64, _i64]),
-    "ef_topk_compress": (C.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _sz, _p, _u32, _p]),
+    "ef_topk_compress": (C.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _sz, _p, _p, _u32, _p]),
     "ef_topk_segmented_workspace_bytes": (_sz, [_i32, _p, _p]),
-    "ef_topk_compress_segmented": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _sz, _p, _u32, _p]),
-    "ef_sign_compress": (C.c_int, [_p, _p, _p, _i64, _f, _f, _p, _p, _p, _p]),
+    "ef_topk_compress_segmented": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _sz, _p, _p, _u32, _p]),
+    "ef_sign_workspace_bytes": (_sz, [_i64]),
+    "ef_sign_compress": (C.c_int, [_p, _p, _p, _i64, _f, _f, _p, _p, _p, _p, _p, _sz, _p]),
     "ef_quantize_workspace_bytes": (_sz, [_i64]),
     "ef_quantize_int8": (C.c_int, [_p, _p, _i64, _p, _i64, _p, _p, _p, _sz, _p]),
     "sparse_decode_accumulate": (C.c_int, [_p, _i64, _i32, _p, _p, _p, _p, _p]),
@@ -118,9 +119,10 @@ def ef_topk_workspace_bytes(n: int, k: int) -> int:
     return int(lib().ef_topk_workspace_bytes(n, k))
 
 
-def ef_topk_compress(g, e, k, vals=None, idx=None, ws=None, nonfinite=None, flags=0):
+def ef_topk_compress(g, e, k, vals=None, idx=None, ws=None, nonfinite=None, flags=0, stats=None):
     """x = g + e; keep the k largest |x| (ties: lower index); returns (vals, idx);
-    e is updated in place."""
+    e is updated in place.  stats (float64 GPU tensor of 2) receives
+    {sum vals^2, sum new e^2}."""
     dev = _gpu(g, "g")
     n = g.numel()
     _need(g, torch.float32, dev, "g")
@@ -135,8 +137,10 @@ def ef_topk_compress(g, e, k, vals=None, idx=None, ws=None, nonfinite=None, flag
         ws = workspace(ef_topk_workspace_bytes(n, k), dev)
     if nonfinite is not None:
         _need(nonfinite, torch.int32, dev, "nonfinite", 1)
+    if stats is not None:
+        _need(stats, torch.float64, dev, "stats", 2)
     _check(lib().ef_topk_compress(_ptr(g), _ptr(e), n, k, _ptr(vals), _ptr(idx), _ptr(ws), ws.numel(),
-                                  _ptr(nonfinite), flags, _stream(dev)), "ef_topk_compress")
+                                  _ptr(nonfinite), _ptr(stats), flags, _stream(dev)), "ef_topk_compress")
     return vals, idx
 
 
@@ -152,9 +156,11 @@ def ef_topk_segmented_workspace_bytes(seg_off, seg_k) -> int:
     return int(lib().ef_topk_segmented_workspace_bytes(len(ks), po, pk))
 
 
-def ef_topk_compress_segmented(g, e, seg_off, seg_k, vals=None, idx=None, ws=None, nonfinite=None, flags=0):
+def ef_topk_compress_segmented(g, e, seg_off, seg_k, vals=None, idx=None, ws=None, nonfinite=None, flags=0,
+                               stats=None):
     """Top-k EF of every tensor [seg_off[s], seg_off[s+1]) with its own seg_k[s]
-    (host integer sequences); returns (vals, idx) concatenated in tensor order."""
+    (host integer sequences); returns (vals, idx) concatenated in tensor order.
+    stats (float64 GPU tensor of 2*nseg) receives per tensor {sum vals^2, sum new e^2}."""
     dev = _gpu(g, "g")
     off, po = _i64_host(seg_off)
     ks, pk = _i64_host(seg_k)
@@ -171,16 +177,19 @@ def ef_topk_compress_segmented(g, e, seg_off, seg_k, vals=None, idx=None, ws=Non
         ws = workspace(lib().ef_topk_segmented_workspace_bytes(len(ks), po, pk), dev)
     if nonfinite is not None:
         _need(nonfinite, torch.int32, dev, "nonfinite", 1)
+    if stats is not None:
+        _need(stats, torch.float64, dev, "stats", 2 * len(ks))
     _check(lib().ef_topk_compress_segmented(_ptr(g), _ptr(e), len(ks), po, pk, _ptr(vals), _ptr(idx), _ptr(ws),
-                                            ws.numel(), _ptr(nonfinite), flags, _stream(dev)),
+                                            ws.numel(), _ptr(nonfinite), _ptr(stats), flags, _stream(dev)),
            "ef_topk_compress_segmented")
     return vals, idx
 
 
 # ---------------------------------------------------------------- sign
 def ef_sign_compress(g, e, m, beta1=0.9, clip=5.0, sign_out=None, bits=None, nonfinite=None,
-                     want_sign=True, want_bits=True):
-    """1-bit sign EF with momentum; e and m updated in place.  Returns (sign int8, bits uint8)."""
+                     want_sign=True, want_bits=True, stats=None, ws=None):
+    """1-bit sign EF with momentum; e and m updated in place.  Returns (sign int8, bits uint8).
+    stats (float64 GPU tensor of 4) receives {sum e'^2, sum m'^2, #(+1), #(-1)}."""
     dev = _gpu(g, "g")
     n = g.numel()
     _need(g, torch.float32, dev, "g")
@@ -196,8 +205,13 @@ def ef_sign_compress(g, e, m, beta1=0.9, clip=5.0, sign_out=None, bits=None, non
         _need(bits, torch.uint8, dev, "bits", (n + 7) // 8)
     if nonfinite is not None:
         _need(nonfinite, torch.int32, dev, "nonfinite", 1)
+    if stats is not None:
+        _need(stats, torch.float64, dev, "stats", 4)
+        if ws is None:
+            ws = workspace(lib().ef_sign_workspace_bytes(n), dev)
     _check(lib().ef_sign_compress(_ptr(g), _ptr(e), _ptr(m), n, beta1, clip, _ptr(sign_out), _ptr(bits),
-                                  _ptr(nonfinite), _stream(dev)), "ef_sign_compress")
+                                  _ptr(nonfinite), _ptr(stats), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(dev)), "ef_sign_compress")
     return sign_out, bits
 
 

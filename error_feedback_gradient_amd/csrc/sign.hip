@@ -72,10 +72,13 @@ __global__ void k_zero_u32(uint32_t* p) { *p = 0; }
 // lane l of unroll step u holds float4 j = base + 64u + l, i.e. elements
 // 4j..4j+3; lanes 2i and 2i+1 together hold one whole output byte of bits.
 // The last n - n8 elements are done by the first lane of wave 0.
+// With STATS, wave w also writes part[w] = {sum e'^2, sum m'^2, #(+1), #(-1)}
+// (float64, finite values only) for k_sign_stats.
+template <bool STATS>
 __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, float* __restrict__ e,
                                                  float* __restrict__ m, int64_t n, float beta1, float c,
                                                  float clip, int8_t* __restrict__ sgn, uint8_t* __restrict__ bits,
-                                                 uint32_t* __restrict__ nonfinite) {
+                                                 uint32_t* __restrict__ nonfinite, double4* __restrict__ part) {
     const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
     const int64_t n8 = n & ~static_cast<int64_t>(7);
     const int64_t beg = w * kRegion;
@@ -83,6 +86,16 @@ __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, fl
     const int64_t end = min(beg + static_cast<int64_t>(kRegion), n8);
     const int l = lane();
     uint32_t nf = 0;
+    double se = 0.0, sm = 0.0;
+    uint32_t cp = 0, cn = 0;
+    auto account = [&](const Out& o) {
+        if (STATS) {
+            if ((__float_as_uint(o.e) & 0x7f800000u) != 0x7f800000u) se += static_cast<double>(o.e) * o.e;
+            if ((__float_as_uint(o.m) & 0x7f800000u) != 0x7f800000u) sm += static_cast<double>(o.m) * o.m;
+            cp += o.s == 1;
+            cn += o.s == -1;
+        }
+    };
     const int64_t nv = beg < end ? (end - beg) >> 2 : 0;  // even
     const f4* g4 = reinterpret_cast<const f4*>(g + beg);
     f4* e4 = reinterpret_cast<f4*>(e + beg);
@@ -118,6 +131,7 @@ __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, fl
                 eo[t] = o.e;
                 mo[t] = o.m;
                 nf += ok ? nonfinite2(o.e, o.m) : 0u;
+                if (ok) account(o);
                 s4v |= static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(o.s))) << (8 * t);
                 nib |= (o.s == 1 ? 1u : 0u) << t;
             }
@@ -142,6 +156,7 @@ __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, fl
             e[j] = o.e;
             m[j] = o.m;
             nf += nonfinite2(o.e, o.m);
+            account(o);
             if (sgn) sgn[j] = static_cast<int8_t>(o.s);
             byte |= (o.s == 1 ? 1u : 0u) << (j & 7);
         }
@@ -151,15 +166,63 @@ __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, fl
         nf = wave_sum(nf);
         if (l == 0 && nf) atomicAdd(nonfinite, nf);
     }
+    if (STATS) {
+        se = wave_sum(se);
+        sm = wave_sum(sm);
+        cp = wave_sum(cp);
+        cn = wave_sum(cn);
+        if (l == 0) part[w] = make_double4(se, sm, static_cast<double>(cp), static_cast<double>(cn));
+    }
 }
+
+// Sums the per-wave statistics in a fixed order: stats = {sum e'^2, sum m'^2, #(+1), #(-1)}.
+constexpr int kStatsBlock = 1024;
+__global__ __launch_bounds__(kStatsBlock) void k_sign_stats(const double4* __restrict__ part, int64_t nw,
+                                                            double* __restrict__ stats) {
+    __shared__ double4 lsum[kStatsBlock / kWave];
+    double4 a = make_double4(0.0, 0.0, 0.0, 0.0);
+    for (int64_t w = threadIdx.x; w < nw; w += kStatsBlock) {
+        a.x += part[w].x;
+        a.y += part[w].y;
+        a.z += part[w].z;
+        a.w += part[w].w;
+    }
+    a.x = wave_sum(a.x);
+    a.y = wave_sum(a.y);
+    a.z = wave_sum(a.z);
+    a.w = wave_sum(a.w);
+    if (lane() == 0) lsum[threadIdx.x / kWave] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double4 t = make_double4(0.0, 0.0, 0.0, 0.0);
+        for (int i = 0; i < kStatsBlock / kWave; ++i) {
+            t.x += lsum[i].x;
+            t.y += lsum[i].y;
+            t.z += lsum[i].z;
+            t.w += lsum[i].w;
+        }
+        stats[0] = t.x;
+        stats[1] = t.y;
+        stats[2] = t.z;
+        stats[3] = t.w;
+    }
+}
+
+inline int64_t waves_for(int64_t n) { return std::max<int64_t>(1, cdiv(n & ~static_cast<int64_t>(7), kRegion)); }
 
 }  // namespace sign
 }  // namespace efg
 
 using namespace efg;
 
+extern "C" size_t ef_sign_workspace_bytes(int64_t n) {
+    if (n < 0) return 0;
+    return static_cast<size_t>(sign::waves_for(n)) * sizeof(double4);
+}
+
 extern "C" int ef_sign_compress(const float* g, float* e, float* m, int64_t n, float beta1, float clip,
-                                int8_t* sign_out, uint8_t* bits, uint32_t* nonfinite, void* stream) {
+                                int8_t* sign_out, uint8_t* bits, uint32_t* nonfinite, double* stats, void* ws,
+                                size_t ws_bytes, void* stream) {
     if (n < 0 || n > kMaxElems) return fail(EF_EINVAL, "n=%lld outside [0, 2^31-1]", (long long)n);
     if (!(beta1 >= 0.0f && beta1 <= 1.0f)) return fail(EF_EINVAL, "beta1 must lie in [0, 1]");
     if (!(clip > 0.0f)) return fail(EF_EINVAL, "clip must be > 0 (+inf disables clipping)");
@@ -168,13 +231,26 @@ extern "C" int ef_sign_compress(const float* g, float* e, float* m, int64_t n, f
         return fail(EF_EINVAL, "g, e and m must be 16-byte aligned");
     if (sign_out && (reinterpret_cast<uintptr_t>(sign_out) & 3u))
         return fail(EF_EINVAL, "sign_out must be 4-byte aligned");
+    if (stats) {
+        const size_t need = ef_sign_workspace_bytes(n);
+        if (!ws || ws_bytes < need) return fail(EF_EWS, "ef_sign_compress: statistics need %zu bytes of workspace", need);
+        if (reinterpret_cast<uintptr_t>(ws) & 31u) return fail(EF_EINVAL, "workspace must be 32-byte aligned");
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (nonfinite) EF_TRY(launch("sign_zero", sign::k_zero_u32, dim3(1), dim3(1), s, nonfinite));
-    if (n == 0) return EF_OK;
     const float c = 1.0f - beta1;
-    const int64_t n8 = n & ~static_cast<int64_t>(7);
-    const int64_t waves = std::max<int64_t>(1, cdiv(n8, sign::kRegion));
+    const int64_t waves = sign::waves_for(n);
     const int64_t grid = cdiv(waves, sign::kWaves);
-    return launch("sign_ef", sign::k_sign, dim3(static_cast<unsigned>(grid)), dim3(sign::kBlock), s, g, e, m, n,
-                  beta1, c, clip, sign_out, bits, nonfinite);
+    double4* part = static_cast<double4*>(ws);
+    if (n > 0) {
+        if (stats)
+            EF_TRY(launch("sign_ef", sign::k_sign<true>, dim3(static_cast<unsigned>(grid)), dim3(sign::kBlock), s, g,
+                          e, m, n, beta1, c, clip, sign_out, bits, nonfinite, part));
+        else
+            EF_TRY(launch("sign_ef", sign::k_sign<false>, dim3(static_cast<unsigned>(grid)), dim3(sign::kBlock), s, g,
+                          e, m, n, beta1, c, clip, sign_out, bits, nonfinite, static_cast<double4*>(nullptr)));
+    }
+    if (!stats) return EF_OK;
+    return launch("sign_stats", sign::k_sign_stats, dim3(1), dim3(sign::kStatsBlock), s,
+                  static_cast<const double4*>(part), n > 0 ? waves : static_cast<int64_t>(0), stats);
 }

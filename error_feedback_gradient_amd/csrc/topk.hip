@@ -130,7 +130,7 @@ struct Plan {
 struct Layout {
     size_t plan, rb, gbb, sbb, rcb, cbb, static_end;
     size_t header, state, shist, rhist, grp_cnt, zero_end;
-    size_t ccb, grp_off, region_cnt, cpair, dval, didx, cgt, ceq, rgt, req;
+    size_t ccb, grp_off, region_cnt, cpair, dval, didx, cgt, ceq, rgt, req, spart, gpart, cpart, rpart;
     size_t total;
 };
 
@@ -163,6 +163,11 @@ static Layout make_layout(const Plan& p) {
     L.ceq = take(static_cast<size_t>(p.QC) * 4);
     L.rgt = take(static_cast<size_t>(p.QR) * 4);
     L.req = take(static_cast<size_t>(p.QR) * 4);
+    // monitoring partials (sent, dropped energy): per region, per candidate unit, per raw unit
+    L.spart = take(static_cast<size_t>(p.R) * 16);
+    L.gpart = take(static_cast<size_t>(p.G) * 16);
+    L.cpart = take(static_cast<size_t>(p.QC) * 16);
+    L.rpart = take(static_cast<size_t>(p.QR) * 16);
     L.total = at;
     return L;
 }
@@ -428,12 +433,18 @@ __device__ __forceinline__ float stream_e(float x, uint32_t key, bool stored, ui
     return x;
 }
 
-template <int MODE>
+// Square of a finite value in float64 (exact), 0 for Inf / NaN.
+__device__ __forceinline__ double sq_finite(float x, uint32_t key) {
+    const double d = static_cast<double>(x);
+    return key < 0x7f800000u ? d * d : 0.0;
+}
+
+template <int MODE, bool STATS>
 __device__ __forceinline__ void stream_region(const float* __restrict__ g, float* __restrict__ e, int64_t gbeg,
                                               int64_t gend, uint32_t tlo, uint32_t thi, uint32_t cap,
                                               uint2* __restrict__ cp, float* __restrict__ vals,
                                               int32_t* __restrict__ idx,
-                                              int64_t out_base, uint32_t& cnt, uint32_t& nf) {
+                                              int64_t out_base, uint32_t& cnt, uint32_t& nf, double& acc) {
     const int l = lane();
     // body [a, bnd) is 16-byte aligned (g and e are 16-byte aligned)
     int64_t a = (gbeg + 3) & ~static_cast<int64_t>(3);
@@ -451,6 +462,7 @@ __device__ __forceinline__ void stream_region(const float* __restrict__ g, float
             key = key_of(xv[0]);
             nf += key >= 0x7f800000u;
             hit[0] = (MODE == MODE_NORMAL) && key >= tlo;
+            if (STATS && !hit[0]) acc += sq_finite(xv[0], key);
         }
         bool stored[1] = {false};
         if (MODE == MODE_NORMAL) append_hits<1>(xv, hit, from + l, cnt, cap, cp, stored);
@@ -495,12 +507,17 @@ __device__ __forceinline__ void stream_region(const float* __restrict__ g, float
             const uint32_t kmax = max(max(key[0], key[1]), max(key[2], key[3]));
             const uint32_t lim = MODE == MODE_NORMAL ? min(tlo, 0x7f800000u) : 0x7f800000u;
             f4 eo = MODE == MODE_ALL ? f4{0.f, 0.f, 0.f, 0.f} : x;
-            if (__ballot(ok && kmax >= lim)) {
+            const bool rare = ok && kmax >= lim;
+            if (STATS && ok && !rare)
+                acc += (sq_finite(xs[0], key[0]) + sq_finite(xs[1], key[1])) +
+                       (sq_finite(xs[2], key[2]) + sq_finite(xs[3], key[3]));
+            if (__ballot(rare)) {
                 bool hit[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     nf += (ok && key[t] >= 0x7f800000u) ? 1u : 0u;
                     hit[t] = (MODE == MODE_NORMAL) && ok && key[t] >= tlo;
+                    if (STATS && rare && !hit[t]) acc += sq_finite(xs[t], key[t]);
                 }
                 if (MODE == MODE_NORMAL) {
                     bool stored[4];
@@ -531,7 +548,10 @@ __device__ __forceinline__ void stream_region(const float* __restrict__ g, float
     if (bnd < gend) scalar_part(bnd, gend);
 }
 
-// 2. the streaming pass; one wave per region of kRegion elements
+// 2. the streaming pass; one wave per region of kRegion elements.  With STATS
+// each region also records the float64 energy of the elements it already knows
+// the fate of (all of them unless they are candidates): spart[w] = {sent, dropped}.
+template <bool STATS>
 __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict__ g, float* __restrict__ e,
                                                          const SegPlan* __restrict__ plan, int32_t nseg,
                                                          const int32_t* __restrict__ rb, int64_t R,
@@ -539,7 +559,8 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
                                                          uint32_t* __restrict__ region_cnt,
                                                          uint32_t* __restrict__ grp_cnt, uint2* __restrict__ cpair,
                                                          float* __restrict__ vals,
-                                                         int32_t* __restrict__ idx, uint32_t* __restrict__ nonfinite) {
+                                                         int32_t* __restrict__ idx, uint32_t* __restrict__ nonfinite,
+                                                         double2* __restrict__ spart) {
     const int64_t w = static_cast<int64_t>(blockIdx.x) * kStreamWaves + threadIdx.x / kWave;
     if (w >= R) return;
     const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
@@ -550,17 +571,22 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
     const int64_t gbeg = P.off + lbeg, gend = P.off + lend;
     const int mode = P.mode;
     uint32_t cnt = 0, nf = 0;
+    double acc = 0.0;
     const uint32_t cap = static_cast<uint32_t>(P.cap);
     uint2* cp = cpair + P.cand_base + rl * P.cap;
     if (mode == MODE_NORMAL) {
         // a direct (dense) selection collects nothing
         const uint32_t tlo = P.direct ? kNoKey : st[s].tlo;
         const uint32_t thi = P.direct ? kNoKey : st[s].thi;
-        stream_region<MODE_NORMAL>(g, e, gbeg, gend, tlo, thi, cap, cp, vals, idx, 0, cnt, nf);
+        stream_region<MODE_NORMAL, STATS>(g, e, gbeg, gend, tlo, thi, cap, cp, vals, idx, 0, cnt, nf, acc);
     } else if (mode == MODE_ALL) {
-        stream_region<MODE_ALL>(g, e, gbeg, gend, 0, 0, 0, cp, vals, idx, P.out_off + lbeg, cnt, nf);
+        stream_region<MODE_ALL, STATS>(g, e, gbeg, gend, 0, 0, 0, cp, vals, idx, P.out_off + lbeg, cnt, nf, acc);
     } else {
-        stream_region<MODE_NONE>(g, e, gbeg, gend, 0, 0, 0, cp, vals, idx, 0, cnt, nf);
+        stream_region<MODE_NONE, STATS>(g, e, gbeg, gend, 0, 0, 0, cp, vals, idx, 0, cnt, nf, acc);
+    }
+    if (STATS) {
+        acc = wave_sum(acc);
+        if (lane() == 0) spart[w] = mode == MODE_ALL ? make_double2(acc, 0.0) : make_double2(0.0, acc);
     }
     nf = wave_sum(nf);
     if (lane() == 0) {
@@ -910,8 +936,10 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
                                                   const int32_t* __restrict__ didx, const uint32_t* __restrict__ cgt,
                                                   const uint32_t* __restrict__ ceq, const uint32_t* __restrict__ rgt,
                                                   const uint32_t* __restrict__ req, float* __restrict__ e,
-                                                  float* __restrict__ vals, int32_t* __restrict__ idx) {
+                                                  float* __restrict__ vals, int32_t* __restrict__ idx,
+                                                  double2* __restrict__ cpart, double2* __restrict__ rpart) {
     __shared__ uint64_t lds[kWavesPerBlock + 1];
+    __shared__ double2 lsum[kWavesPerBlock];
     const int64_t Qc = hdr->total_cchunks;
     const int64_t Q = Qc + (hdr->any_fallback ? QR : 0);
     for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
@@ -937,6 +965,7 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
         const uint64_t before = block_excl_scan<kBlock>((static_cast<uint64_t>(ngt) << 32) | neq, lds, &tot);
         uint32_t gtb = G0 + static_cast<uint32_t>(before >> 32);
         uint32_t eqb = E0 + static_cast<uint32_t>(before);
+        double sent = 0.0, drop = 0.0;
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i) {
             if (j0 + i >= u.cnt) continue;
@@ -949,6 +978,8 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
                 if (eqb < r) pos = static_cast<int64_t>(gtb) + eqb;
                 ++eqb;
             }
+            if (pos >= 0) sent += sq_finite(v[i], key);
+            else drop += sq_finite(v[i], key);
             const int64_t id = u.raw ? u.idx_base + j0 + i : static_cast<int64_t>(u.id[j0 + i]);
             if (id < seg_lo || id >= seg_hi) continue;  // only if the workspace was overwritten meanwhile
             if (pos >= 0 && pos < kseg) {
@@ -959,21 +990,107 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
                 e[id] = v[i];
             }
         }
+        if (cpart) {
+            // fixed-order block sum of the unit's sent and dropped energy
+            sent = wave_sum(sent);
+            drop = wave_sum(drop);
+            if (lane() == 0) lsum[threadIdx.x / kWave] = make_double2(sent, drop);
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                double2 t = make_double2(0.0, 0.0);
+                for (int i = 0; i < kWavesPerBlock; ++i) {
+                    t.x += lsum[i].x;
+                    t.y += lsum[i].y;
+                }
+                (u.raw ? rpart : cpart)[u.slot] = t;
+            }
+        }
         __syncthreads();
     }
 }
 
+// 7. per-tensor monitoring statistics {sent energy, residual energy} from the
+// stream's and the emit's partials, summed in a fixed order.
+__device__ __forceinline__ double2 block_sum2(double2 v, double2* lsum) {
+    v.x = wave_sum(v.x);
+    v.y = wave_sum(v.y);
+    if (lane() == 0) lsum[threadIdx.x / kWave] = v;
+    __syncthreads();
+    double2 t = make_double2(0.0, 0.0);
+    for (int i = 0; i < kWavesPerBlock; ++i) {
+        t.x += lsum[i].x;
+        t.y += lsum[i].y;
+    }
+    __syncthreads();
+    return t;
+}
+
+// 7a. one block per group of kGroup regions: the group's stream partials
+__global__ __launch_bounds__(kGroup) void k_stats_groups(const SegPlan* __restrict__ plan, int32_t nseg,
+                                                         const int32_t* __restrict__ gbb,
+                                                         const int32_t* __restrict__ rb,
+                                                         const double2* __restrict__ spart,
+                                                         double2* __restrict__ gpart) {
+    __shared__ double2 lsum[kWavesPerBlock];
+    const int gi = blockIdx.x;
+    const int s = upper_index(gbb, nseg, gi);
+    const int gl = gi - gbb[s];
+    const int64_t r = rb[s] + static_cast<int64_t>(gl) * kGroup + threadIdx.x;
+    const bool ok = static_cast<int>(threadIdx.x) < plan[s].nregions - gl * kGroup;
+    const double2 t = block_sum2(ok ? spart[r] : make_double2(0.0, 0.0), lsum);
+    if (threadIdx.x == 0) gpart[gi] = t;
+}
+
+// 7b. per tensor
+__global__ __launch_bounds__(kBlock) void k_stats(const SegPlan* __restrict__ plan, const SegState* __restrict__ st,
+                                                  const int32_t* __restrict__ gbb, const int32_t* __restrict__ rcb,
+                                                  const double2* __restrict__ gpart, const double2* __restrict__ cpart,
+                                                  const double2* __restrict__ rpart, double* __restrict__ stats) {
+    __shared__ double2 lsum[kWavesPerBlock];
+    const int s = blockIdx.x;
+    const int mode = plan[s].mode;
+    const bool fb = mode == MODE_NORMAL && st[s].fallback;
+    double2 a = make_double2(0.0, 0.0);
+    if (!fb) {
+        // the stream's groups (every element of a k = 0 or k = n tensor, the
+        // non-candidates of a candidate-path tensor)
+        for (int64_t gi = gbb[s] + threadIdx.x; gi < gbb[s + 1]; gi += kBlock) {
+            a.x += gpart[gi].x;
+            a.y += gpart[gi].y;
+        }
+    }
+    if (mode == MODE_NORMAL) {
+        const double2* p = fb ? rpart + rcb[s] : cpart + st[s].cchunk_begin;
+        const int64_t nu = fb ? plan[s].raw_chunks : st[s].cchunks;
+        for (int64_t q = threadIdx.x; q < nu; q += kBlock) {
+            a.x += p[q].x;
+            a.y += p[q].y;
+        }
+    }
+    const double2 t = block_sum2(a, lsum);
+    if (threadIdx.x == 0) {
+        stats[2 * s] = t.x;
+        stats[2 * s + 1] = t.y;
+    }
+}
+
+__global__ void k_stats_zero(double* __restrict__ stats, int32_t n) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) stats[i] = 0.0;
+}
+
 // ------------------------------------------------------------------ host driver
 static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* idx, void* ws, size_t ws_bytes,
-               uint32_t* nonfinite, uint32_t flags, hipStream_t s) {
+               uint32_t* nonfinite, double* stats, uint32_t flags, hipStream_t s) {
     const Layout L = make_layout(P);
     WordChunk none;
     none.n = 0;
     if (P.R == 0) {
-        // nothing to stream: only the counter needs clearing
+        // nothing to stream: only the counter and the statistics need clearing
         if (nonfinite)
             EF_TRY(launch("topk_init", k_init, dim3(1), dim3(kBlock), s, static_cast<uint4*>(nullptr),
                           static_cast<int64_t>(0), nonfinite, static_cast<uint32_t*>(nullptr), none));
+        if (stats && P.nseg > 0)
+            EF_TRY(launch("topk_stats", k_stats_zero, dim3(1), dim3(kBlock), s, stats, 2 * P.nseg));
         return EF_OK;
     }
     if (!ws) return fail(EF_EWS, "workspace is NULL (%zu bytes needed)", L.total);
@@ -1028,7 +1145,20 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     uint32_t* ceq = reinterpret_cast<uint32_t*>(at(L.ceq));
     uint32_t* rgt = reinterpret_cast<uint32_t*>(at(L.rgt));
     uint32_t* req = reinterpret_cast<uint32_t*>(at(L.req));
+    double2* spart = reinterpret_cast<double2*>(at(L.spart));
+    double2* cpart = stats ? reinterpret_cast<double2*>(at(L.cpart)) : nullptr;
+    double2* rpart = stats ? reinterpret_cast<double2*>(at(L.rpart)) : nullptr;
     const int32_t nseg = P.nseg;
+    double2* gpart = reinterpret_cast<double2*>(at(L.gpart));
+    auto finish_stats = [&]() -> int {
+        if (!stats) return EF_OK;
+        EF_TRY(launch("topk_stats_groups", k_stats_groups, dim3(static_cast<unsigned>(P.G)), dim3(kGroup), s, plan,
+                      nseg, gbb, rb, static_cast<const double2*>(spart), gpart));
+        return launch("topk_stats", k_stats, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
+                      static_cast<const SegState*>(st), gbb, rcb, static_cast<const double2*>(gpart),
+                      static_cast<const double2*>(reinterpret_cast<double2*>(at(L.cpart))),
+                      static_cast<const double2*>(reinterpret_cast<double2*>(at(L.rpart))), stats);
+    };
 
     if (P.any_normal && P.SB > 0) {
         EF_TRY(launch("topk_sample_hist", k_sample, dim3(static_cast<unsigned>(P.SB)), dim3(kSampleBlock), s, g,
@@ -1036,9 +1166,14 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
         EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
                       static_cast<const uint32_t*>(shist), st));
     }
-    EF_TRY(launch("topk_stream", k_stream, dim3(static_cast<unsigned>(cdiv(P.R, kStreamWaves))), dim3(kStreamBlock),
-                  s, g, e, plan, nseg, rb, P.R, st, region_cnt, grp_cnt, cpair, vals, idx, nonfinite));
-    if (!P.any_normal) return EF_OK;
+    const dim3 sgrid(static_cast<unsigned>(cdiv(P.R, kStreamWaves)));
+    if (stats)
+        EF_TRY(launch("topk_stream", k_stream<true>, sgrid, dim3(kStreamBlock), s, g, e, plan, nseg, rb, P.R, st,
+                      region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart));
+    else
+        EF_TRY(launch("topk_stream", k_stream<false>, sgrid, dim3(kStreamBlock), s, g, e, plan, nseg, rb, P.R, st,
+                      region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart));
+    if (!P.any_normal) return finish_stats();
 
     EF_TRY(launch("topk_scan_groups", k_scan_groups, dim3(1), dim3(kScanBlock), s, plan, nseg, gbb, P.G,
                   static_cast<const uint32_t*>(grp_cnt), grp_off, st, ccb, hdr,
@@ -1069,8 +1204,8 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
                   static_cast<const uint32_t*>(ccb), rcb, P.QR, static_cast<const Header*>(hdr),
                   static_cast<const float*>(dval), static_cast<const int32_t*>(didx),
                   static_cast<const uint32_t*>(cgt), static_cast<const uint32_t*>(ceq),
-                  static_cast<const uint32_t*>(rgt), static_cast<const uint32_t*>(req), e, vals, idx));
-    return EF_OK;
+                  static_cast<const uint32_t*>(rgt), static_cast<const uint32_t*>(req), e, vals, idx, cpart, rpart));
+    return finish_stats();
 }
 
 static int check_common(const float* g, const float* e, int64_t total, int64_t ksum, const float* vals,
@@ -1098,14 +1233,14 @@ size_t ef_topk_workspace_bytes(int64_t n, int64_t k) {
 }
 
 int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals, int32_t* idx, void* ws,
-                     size_t ws_bytes, uint32_t* nonfinite, uint32_t flags, void* stream) {
+                     size_t ws_bytes, uint32_t* nonfinite, double* stats, uint32_t flags, void* stream) {
     if (n < 0 || n > kMaxElems) return fail(EF_EINVAL, "n=%lld outside [0, 2^31-1]", (long long)n);
     if (k < 0 || k > n) return fail(EF_EINVAL, "k=%lld outside [0, n=%lld]", (long long)k, (long long)n);
     EF_TRY(topk::check_common(g, e, n, k, vals, idx, flags));
     int64_t off[2] = {0, n}, ks[1] = {k};
     topk::Plan p;
     EF_TRY(topk::make_plan(1, off, ks, p));
-    return topk::run(g, e, p, vals, idx, ws, ws_bytes, nonfinite, flags, static_cast<hipStream_t>(stream));
+    return topk::run(g, e, p, vals, idx, ws, ws_bytes, nonfinite, stats, flags, static_cast<hipStream_t>(stream));
 }
 
 size_t ef_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* seg_off, const int64_t* seg_k) {
@@ -1116,13 +1251,13 @@ size_t ef_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* seg_off, c
 
 int ef_topk_compress_segmented(const float* g, float* e, int32_t nseg, const int64_t* seg_off,
                                const int64_t* seg_k, float* vals, int32_t* idx, void* ws, size_t ws_bytes,
-                               uint32_t* nonfinite, uint32_t flags, void* stream) {
+                               uint32_t* nonfinite, double* stats, uint32_t flags, void* stream) {
     topk::Plan p;
     EF_TRY(topk::make_plan(nseg, seg_off, seg_k, p));
     int64_t ksum = 0;
     for (int32_t s = 0; s < nseg; ++s) ksum += seg_k[s];
     EF_TRY(topk::check_common(g, e, nseg > 0 ? seg_off[nseg] : 0, ksum, vals, idx, flags));
-    return topk::run(g, e, p, vals, idx, ws, ws_bytes, nonfinite, flags, static_cast<hipStream_t>(stream));
+    return topk::run(g, e, p, vals, idx, ws, ws_bytes, nonfinite, stats, flags, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -70,6 +70,10 @@ const char* ef_version(void);
  *   vals[0..k) = x at those indices, bit for bit          (float32, output)
  *   e_i        = +0.0 for i in S, x_i otherwise           (in place)
  *   *nonfinite = number of i with x_i = +-Inf or NaN      (nullable)
+ *   stats[0] = sum of vals^2, stats[1] = sum of new e^2   (device double[2],
+ *              nullable; finite values only, float64; the monitoring signals of
+ *              [ONEBIT] 6.2 and 8 item 3, computed in the same passes; the sums
+ *              are reduced in a fixed order, so they repeat bit for bit)
  * g is read only.  0 <= k <= n <= 2^31 - 1.  vals/idx may be NULL when k = 0.
  * ws: device workspace of at least ef_topk_workspace_bytes(n, k) bytes, 256-byte
  * aligned; its contents on entry do not matter.
@@ -78,7 +82,7 @@ const char* ef_version(void);
 size_t ef_topk_workspace_bytes(int64_t n, int64_t k);
 int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals,
                      int32_t* idx, void* ws, size_t ws_bytes, uint32_t* nonfinite,
-                     uint32_t flags, void* stream);
+                     double* stats, uint32_t flags, void* stream);
 
 /* ------------------------------------------------------------------------
  * Layer-wise top-k over many tensors packed in one buffer: the operation of
@@ -93,7 +97,8 @@ int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals
  * Output: tensor s's kept entries go to vals/idx[K_s, K_s + seg_k[s]) with
  *   K_s = seg_k[0] + ... + seg_k[s-1]; indices are positions in the packed
  *   buffer (seg_off[s] + local index), so idx is ascending overall.
- * *nonfinite counts over all tensors.  The host tables are read during the
+ * *nonfinite counts over all tensors; stats (nullable) gets two doubles per
+ * tensor, stats[2s] and stats[2s+1], as above.  The host tables are read during the
  * call only: the per-tensor plan built from them reaches the device through a
  * small ring of pinned host staging buffers owned by the library (8 slots of
  * at least 64 KB, kept for the life of the process; a slot is reused only once
@@ -104,7 +109,7 @@ size_t ef_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* seg_off,
 int ef_topk_compress_segmented(const float* g, float* e, int32_t nseg,
                                const int64_t* seg_off, const int64_t* seg_k,
                                float* vals, int32_t* idx, void* ws, size_t ws_bytes,
-                               uint32_t* nonfinite, uint32_t flags, void* stream);
+                               uint32_t* nonfinite, double* stats, uint32_t flags, void* stream);
 
 /* ------------------------------------------------------------------------
  * 1-bit sign compression with averaged error feedback and momentum.
@@ -122,11 +127,16 @@ int ef_topk_compress_segmented(const float* g, float* e, int32_t nseg,
  *   sign_out[i] = q                        (int8, nullable)
  *   bits[i/8] bit (i%8) = (q == +1)        (uint8[ceil(n/8)], LSB first, pad 0, nullable)
  *   *nonfinite = count of non-finite new e plus non-finite new m (nullable)
+ *   stats = {sum e'^2, sum m'^2, #(q = +1), #(q = -1)}  (device double[4],
+ *           nullable; finite values only, float64, fixed-order sums; needs
+ *           ws of ef_sign_workspace_bytes(n) bytes, 32-byte aligned; ws may be
+ *           NULL when stats is NULL)
  * 0 <= n <= 2^31 - 1; 0 <= beta1 <= 1; clip > 0; sign_out 4-byte aligned.
  * ------------------------------------------------------------------------ */
+size_t ef_sign_workspace_bytes(int64_t n);
 int ef_sign_compress(const float* g, float* e, float* m, int64_t n, float beta1,
                      float clip, int8_t* sign_out, uint8_t* bits, uint32_t* nonfinite,
-                     void* stream);
+                     double* stats, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * 8-bit quantisation of a sent packet, the quantisation error kept in the

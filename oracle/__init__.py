@@ -56,6 +56,8 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = C.c_int
+        L.orc_sumsq.argtypes = [p, i64]
+        L.orc_sumsq.restype = C.c_double
         _lib = L
     return _lib
 
@@ -198,3 +200,9 @@ def quantize_int8(vals, idx, e):
     sc = np.zeros(1, np.float32)
     _check(lib().orc_quantize_int8(_ptr(vals), _ptr(idx), vals.size, _ptr(e2), _ptr(q), _ptr(sc)), "quantize_int8")
     return q[:vals.size], float(sc[0]), e2
+
+
+def sumsq(a):
+    """Sum of squares of the finite entries, float64, in index order."""
+    a = _f32(a)
+    return float(lib().orc_sumsq(_ptr(a), a.size))

@@ -395,3 +395,17 @@ int orc_quantize_int8(const float* vals, const int32_t* idx, int64_t k, float* e
     *scale_out = scale;
     return ORC_OK;
 }
+
+/*
+ * Monitoring statistic: sum of squares of the finite entries of a float32
+ * array, accumulated in float64 in index order.  [ONEBIT] "6.2" (a vanishing
+ * L2 norm of the error buffer signals trouble) and "8" item 3 (watch the
+ * error buffer's L2 norm).  Squares of float32 values are exact in float64;
+ * only the summation rounds.
+ */
+double orc_sumsq(const float* a, int64_t n) {
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        if (!is_nonfinite(a[i])) s += (double)a[i] * (double)a[i];
+    return s;
+}

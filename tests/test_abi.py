@@ -64,7 +64,7 @@ def test_topk_argument_checks():
     assert efg.ef_topk_workspace_bytes(10, 11) == 0
     assert efg.ef_topk_workspace_bytes(-1, 0) == 0
     assert efg.ef_topk_workspace_bytes(2**31, 1) == 0
-    call = lambda g, e, n, k, v, i, w, wb, flags=0: L.ef_topk_compress(g, e, n, k, v, i, w, wb, None, flags, None)
+    call = lambda g, e, n, k, v, i, w, wb, flags=0: L.ef_topk_compress(g, e, n, k, v, i, w, wb, None, None, flags, None)
     assert call(FAKE, FAKE, -1, 0, FAKE, FAKE, FAKE, ws) == efg.EF_EINVAL
     assert call(FAKE, FAKE, 10, 11, FAKE, FAKE, FAKE, ws) == efg.EF_EINVAL
     assert call(FAKE, FAKE, 2**31, 1, FAKE, FAKE, FAKE, ws) == efg.EF_EINVAL
@@ -94,19 +94,19 @@ def test_segmented_argument_checks():
     ks = np.array([1, 1], np.int64)
     p = lambda a: a.ctypes.data_as(C.c_void_p)
     assert L.ef_topk_segmented_workspace_bytes(2, p(off), p(ks)) == 0
-    rc = L.ef_topk_compress_segmented(FAKE, FAKE, 2, p(off), p(ks), FAKE, FAKE, FAKE, 1 << 30, None, 0, None)
+    rc = L.ef_topk_compress_segmented(FAKE, FAKE, 2, p(off), p(ks), FAKE, FAKE, FAKE, 1 << 30, None, None, 0, None)
     assert rc == efg.EF_EINVAL and "non-decreasing" in efg.last_error()
     off = np.array([0, 10, 20], np.int64)
     ks = np.array([1, 11], np.int64)
-    rc = L.ef_topk_compress_segmented(FAKE, FAKE, 2, p(off), p(ks), FAKE, FAKE, FAKE, 1 << 30, None, 0, None)
+    rc = L.ef_topk_compress_segmented(FAKE, FAKE, 2, p(off), p(ks), FAKE, FAKE, FAKE, 1 << 30, None, None, 0, None)
     assert rc == efg.EF_EINVAL and "segment 1" in efg.last_error()
     off = np.array([0, 10, 20], np.int64)
     ks = np.array([1, 2], np.int64)
     need = L.ef_topk_segmented_workspace_bytes(2, p(off), p(ks))
     assert need > 0
-    rc = L.ef_topk_compress_segmented(FAKE, FAKE, 2, p(off), p(ks), FAKE, FAKE, FAKE, need - 1, None, 0, None)
+    rc = L.ef_topk_compress_segmented(FAKE, FAKE, 2, p(off), p(ks), FAKE, FAKE, FAKE, need - 1, None, None, 0, None)
     assert rc == efg.EF_EWS
-    assert L.ef_topk_compress_segmented(FAKE, FAKE, -1, None, None, FAKE, FAKE, FAKE, 0, None, 0, None) == efg.EF_EINVAL
+    assert L.ef_topk_compress_segmented(FAKE, FAKE, -1, None, None, FAKE, FAKE, FAKE, 0, None, None, 0, None) == efg.EF_EINVAL
 
 
 def test_bert_layout_workspace():
@@ -121,7 +121,7 @@ def test_sign_argument_checks():
     L = efg.lib()
     ok = lambda **kw: L.ef_sign_compress(kw.get("g", FAKE), kw.get("e", FAKE), kw.get("m", FAKE), kw.get("n", 64),
                                          kw.get("b", 0.9), kw.get("c", 5.0), kw.get("s", FAKE), kw.get("bits", FAKE),
-                                         None, None)
+                                         None, kw.get("stats", None), kw.get("ws", None), kw.get("wsb", 0), None)
     assert ok(n=-1) == efg.EF_EINVAL
     assert ok(b=1.5) == efg.EF_EINVAL
     assert ok(b=float("nan")) == efg.EF_EINVAL
@@ -129,6 +129,9 @@ def test_sign_argument_checks():
     assert ok(m=None) == efg.EF_EINVAL
     assert ok(e=FAKE_ODD) == efg.EF_EINVAL
     assert ok(s=FAKE + 2) == efg.EF_EINVAL
+    assert ok(stats=FAKE) == efg.EF_EWS
+    assert ok(stats=FAKE, ws=FAKE, wsb=efg.lib().ef_sign_workspace_bytes(64) - 1) == efg.EF_EWS
+    assert ok(stats=FAKE, ws=FAKE + 16, wsb=1 << 20) == efg.EF_EINVAL
 
 
 def test_decode_and_sgd_argument_checks():

@@ -189,10 +189,11 @@ def test_large_invariants_two_steps():
     ed = torch.zeros(n, dtype=torch.float32, device=dev)
     e_prev = np.zeros(n, np.float32)
     ws = efg.workspace(efg.ef_topk_workspace_bytes(n, k), dev)
+    st = torch.zeros(2, dtype=torch.float64, device=dev)
     for t in range(2):
         gd = gen.large_gradient_device(t, n, dev)
         g = host(gd)
-        v, i = efg.ef_topk_compress(gd, ed, k, ws=ws)
+        v, i = efg.ef_topk_compress(gd, ed, k, ws=ws, stats=st if t == 1 else None)
         vh, ih, eh = host(v), host(i), host(ed)
         del gd
         say(f"large step {t}: checking invariants")
@@ -213,4 +214,15 @@ def test_large_invariants_two_steps():
         assert_bits_equal(eh, x, f"large e step {t}")
         e_prev = x  # host-computed state, equal to the GPU's bit for bit
         del eh
+        if t == 1:
+            # monitoring statistics against float64 sums of the host copies
+            sh = host(st)
+            v64 = vh.astype(np.float64)
+            sent = float(np.dot(v64, v64))
+            resid = 0.0
+            for lo in range(0, n, 1 << 26):
+                c = x[lo:lo + (1 << 26)].astype(np.float64)
+                resid += float(np.dot(c, c))
+            assert abs(sh[0] - sent) <= 2 * k * 2.0 ** -53 * sent
+            assert abs(sh[1] - resid) <= 2 * n * 2.0 ** -53 * resid
         say(f"large step {t}: ok")
