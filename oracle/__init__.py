@@ -58,6 +58,16 @@ def lib():
             fn.restype = C.c_int
         L.orc_sumsq.argtypes = [p, i64]
         L.orc_sumsq.restype = C.c_double
+        L.orc_philox4x32_10.argtypes = [p, p, p]
+        L.orc_philox4x32_10.restype = None
+        L.orc_sum_abs_exact.argtypes = [p, i64]
+        L.orc_sum_abs_exact.restype = C.c_double
+        L.orc_uniform.argtypes = [C.c_uint64, C.c_uint64, i64]
+        L.orc_uniform.restype = C.c_float
+        L.orc_keep_probability.argtypes = [f, i64, f]
+        L.orc_keep_probability.restype = C.c_float
+        L.orc_random_sparsify.argtypes = [p, p, i64, i64, C.c_uint64, C.c_uint64, i64, p, p, p, p, u32p]
+        L.orc_random_sparsify.restype = C.c_int
         _lib = L
     return _lib
 
@@ -206,3 +216,44 @@ def sumsq(a):
     """Sum of squares of the finite entries, float64, in index order."""
     a = _f32(a)
     return float(lib().orc_sumsq(_ptr(a), a.size))
+
+
+def philox4x32_10(ctr, key):
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().orc_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return [int(v) for v in out]
+
+
+def sum_abs_exact(x):
+    """Sum of |x| over the finite entries, exact, rounded once to float64."""
+    x = _f32(x)
+    return float(lib().orc_sum_abs_exact(_ptr(x), x.size))
+
+
+def uniform(seed, step, i):
+    return float(lib().orc_uniform(seed, step, i))
+
+
+def keep_probability(x, k, s32):
+    return float(lib().orc_keep_probability(x, k, s32))
+
+
+def random_sparsify(g, e, k, seed, step, cap=None):
+    """Returns (vals, idx, e_new, count, S32, nonfinite); vals/idx hold min(count, cap) entries."""
+    g = _f32(g)
+    e2 = _f32(e).copy()
+    n = g.size
+    if cap is None:
+        cap = n
+    vals = np.empty(max(cap, 1), np.float32)
+    idx = np.empty(max(cap, 1), np.int32)
+    cnt = np.zeros(1, np.int64)
+    s32 = np.zeros(1, np.float32)
+    bad = np.zeros(1, np.uint32)
+    _check(lib().orc_random_sparsify(_ptr(g), _ptr(e2), n, k, seed, step, cap, _ptr(vals), _ptr(idx), _ptr(cnt),
+                                     _ptr(s32), _ptr(bad)), "random_sparsify")
+    c = int(cnt[0])
+    w = min(c, cap)
+    return vals[:w].copy(), idx[:w].copy(), e2, c, float(s32[0]), int(bad[0])

@@ -409,3 +409,150 @@ double orc_sumsq(const float* a, int64_t n) {
         if (!is_nonfinite(a[i])) s += (double)a[i] * (double)a[i];
     return s;
 }
+
+/*
+ * Sum of |x_i| over the finite x_i, correctly rounded to float64.
+ * READING: the pages normalise by the total magnitude without fixing how it
+ * is summed; the exact sum rounded once is the one result that every
+ * summation order can agree on.  Every finite float32 magnitude is an integer
+ * multiple of 2^-149 below 2^128, so the exact sum of up to 2^31 of them is an
+ * integer multiple of 2^-149 below 2^159: it is accumulated exactly in a
+ * 320-bit fixed-point integer (ten 32-bit limbs, limb 0 holding 2^-149..2^-118)
+ * and rounded to the nearest float64, ties to even, at the end.
+ */
+double orc_sum_abs_exact(const float* x, int64_t n) {
+    uint64_t limb[11] = {0};
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u = f2u(x[i]) & 0x7fffffffu;
+        uint32_t ex = u >> 23;
+        if (ex == 0xffu) continue;
+        uint64_t mant = u & 0x7fffffu;
+        int shift = 0;
+        if (ex > 0) { mant |= 0x800000u; shift = (int)ex - 1; }
+        /* |x| = mant * 2^(shift - 149) */
+        int q = shift / 32, r = shift % 32;
+        uint64_t v = mant << r; /* < 2^55 */
+        limb[q] += v & 0xffffffffu;
+        limb[q + 1] += v >> 32;
+        for (int j = q; j < 10; ++j) { /* keep every limb below 2^32 */
+            if (limb[j] >> 32) { limb[j + 1] += limb[j] >> 32; limb[j] &= 0xffffffffu; }
+        }
+    }
+    /* Highest set bit of the 320-bit integer. */
+    int top = -1;
+    for (int j = 9; j >= 0 && top < 0; --j)
+        if (limb[j]) for (int b = 31; b >= 0; --b) if ((limb[j] >> b) & 1u) { top = 32 * j + b; break; }
+    if (top < 0) return 0.0;
+    /* Take the 53 bits below and including 'top', then round on the rest. */
+    uint64_t mant = 0;
+    int sticky = 0, guard = 0;
+    for (int b = top; b >= 0; --b) {
+        int bit = (int)((limb[b / 32] >> (b % 32)) & 1u);
+        if (b > top - 53) mant = (mant << 1) | (uint64_t)bit;
+        else if (b == top - 53) guard = bit;
+        else sticky |= bit;
+    }
+    int lsb_pos = top - 52; /* position of the last kept bit */
+    if (lsb_pos < 0) lsb_pos = 0; /* 53 bits or fewer: mant holds every bit, exactly */
+    if (guard && (sticky || (mant & 1u))) mant += 1; /* may carry to 2^53: ldexp still exact */
+    return ldexp((double)mant, lsb_pos - 149);
+}
+
+/*
+ * Philox4x32-10 counter-based generator, from its published definition
+ * (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2,
+ * 3", SC 2011): ten rounds of two 32x32->64 multiplications mixed with the
+ * counter and a key bumped by two Weyl constants between rounds.
+ */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* READING: the uniform draw u_i in [0, 1) for element i.  Philox is keyed by
+ * the 64-bit seed (low word first) and run on the counter
+ * {i div 4, 0, step low word, step high word}; element i takes output word
+ * (i mod 4), keeps its top 24 bits and scales them by 2^-24, which is exact in
+ * float32. */
+float orc_uniform(uint64_t seed, uint64_t step, int64_t i) {
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    const uint32_t ctr[4] = {(uint32_t)(i / 4), 0u, (uint32_t)step, (uint32_t)(step >> 32)};
+    uint32_t r[4];
+    orc_philox4x32_10(ctr, key, r);
+    return (float)(r[i % 4] >> 8) * 0x1p-24f;
+}
+
+/* READING: the keep probability of one element, in float32:
+ * p = (float(k) * |x|) / S32, lowered to 1 when above it (IEEE comparisons, so
+ * a NaN quotient is left alone and keeps nothing), and 0 for a non-finite x. */
+float orc_keep_probability(float x, int64_t k, float S32) {
+    if (is_nonfinite(x)) return 0.0f;
+    float t = (float)k * fabsf(x);
+    float p = t / S32;
+    if (p > 1.0f) p = 1.0f;
+    return p;
+}
+
+/*
+ * Random sparsification with error feedback.  [SPARSE] "随机稀疏化" (random
+ * sparsification): every element survives with a probability proportional to
+ * its magnitude, scaled so that k elements survive on average; the error
+ * compensation around it is the page's generic loop (add the residual, sparsify,
+ * keep what was not sent).
+ * READINGS:
+ *   x_i = g_i + e_i (float32); S64 = orc_sum_abs_exact(x), S32 = float(S64);
+ *   p_i = orc_keep_probability(x_i, k, S32); u_i = orc_uniform(seed, step, i);
+ *   x_i is kept iff u_i < p_i (so p = 0 keeps nothing and p = 1 keeps always).
+ *   Probabilities above 1 are clipped, so the expected count is k less what
+ *   the clipped elements lose.  A kept element is sent as x_i, unscaled: the
+ *   sparse tensor holds x on the kept positions and zero elsewhere, and its
+ *   residual becomes +0; every other element keeps e' = x.  Kept elements are
+ *   sent in index order; only the first cap of them are written, and kept
+ *   elements beyond cap stay whole in the residual (they were not sent).
+ * *count_out = number kept (may exceed cap); *sum_out = S32.
+ */
+int orc_random_sparsify(const float* g, float* e, int64_t n, int64_t k, uint64_t seed, uint64_t step,
+                        int64_t cap, float* vals, int32_t* idx, int64_t* count_out, float* sum_out,
+                        uint32_t* nonfinite) {
+    if (n < 0 || k < 0 || cap < 0 || n > 0x7fffffffLL) return ORC_EINVAL;
+    float* x = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    if (!x) return ORC_ENOMEM;
+    uint32_t bad = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        x[i] = g[i] + e[i];
+        bad += (uint32_t)is_nonfinite(x[i]);
+    }
+    const float S32 = (float)orc_sum_abs_exact(x, n);
+    int64_t count = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const int keep = orc_uniform(seed, step, i) < orc_keep_probability(x[i], k, S32);
+        if (keep && count < cap) {
+            vals[count] = x[i];
+            idx[count] = (int32_t)i;
+            e[i] = 0.0f;
+        } else {
+            e[i] = x[i];
+        }
+        count += keep;
+    }
+    free(x);
+    *count_out = count;
+    *sum_out = S32;
+    if (nonfinite) *nonfinite = bad;
+    return ORC_OK;
+}
