@@ -35,6 +35,9 @@ SIGNATURES = {
     "ef_sign_compress": (C.c_int, [_p, _p, _p, _i64, _f, _f, _p, _p, _p, _p, _p, _sz, _p]),
     "ef_quantize_workspace_bytes": (_sz, [_i64]),
     "ef_quantize_int8": (C.c_int, [_p, _p, _i64, _p, _i64, _p, _p, _p, _sz, _p]),
+    "ef_random_sparsify_workspace_bytes": (_sz, [_i64]),
+    "ef_random_sparsify": (C.c_int, [_p, _p, _i64, _i64, C.c_uint64, C.c_uint64, _p, _p, _i64, _p, _p, _p, _p, _sz,
+                                     _u32, _p]),
     "sparse_decode_accumulate": (C.c_int, [_p, _i64, _i32, _p, _p, _p, _p, _p]),
     "sgd_apply": (C.c_int, [_p, _p, _i64, _f, _p]),
     "encode_bitmap": (C.c_int, [_p, _i64, _i64, _p, _p]),
@@ -232,6 +235,42 @@ def ef_quantize_int8(vals, idx, e, q=None, scale=None, ws=None):
     _check(lib().ef_quantize_int8(_ptr(vals), _ptr(idx), k, _ptr(e), e.numel(), _ptr(q), _ptr(scale), _ptr(ws),
                                   ws.numel(), _stream(dev)), "ef_quantize_int8")
     return q[:k], scale
+
+
+# ---------------------------------------------------------------- random sparsification
+def ef_random_sparsify(g, e, k, seed, step, cap=None, vals=None, idx=None, count=None, sum_out=None,
+                       nonfinite=None, ws=None, flags=0):
+    """Keep x = g + e with probability min(1, k|x|/S) (Philox draws keyed by
+    seed and step); e <- residual in place.  Returns (vals, idx, count) where
+    vals/idx hold cap slots of which the first min(count, cap) are written and
+    count is a device int64[1]."""
+    dev = _gpu(g, "g")
+    n = g.numel()
+    _need(g, torch.float32, dev, "g")
+    _need(e, torch.float32, dev, "e", n)
+    if cap is None:
+        cap = max(1, 2 * k + 64)
+    if vals is None:
+        vals = torch.empty(max(cap, 1), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    _need(vals, torch.float32, dev, "vals")
+    _need(idx, torch.int32, dev, "idx")
+    if vals.numel() < cap or idx.numel() < cap:
+        raise ValueError("vals and idx need at least cap slots")
+    if count is None:
+        count = torch.empty(1, dtype=torch.int64, device=dev)
+    _need(count, torch.int64, dev, "count", 1)
+    if sum_out is not None:
+        _need(sum_out, torch.float32, dev, "sum_out", 1)
+    if nonfinite is not None:
+        _need(nonfinite, torch.int32, dev, "nonfinite", 1)
+    if ws is None:
+        ws = workspace(lib().ef_random_sparsify_workspace_bytes(n), dev)
+    _check(lib().ef_random_sparsify(_ptr(g), _ptr(e), n, k, seed, step, _ptr(vals), _ptr(idx), cap, _ptr(count),
+                                    _ptr(sum_out), _ptr(nonfinite), _ptr(ws), ws.numel(), flags, _stream(dev)),
+           "ef_random_sparsify")
+    return vals, idx, count
 
 
 # ---------------------------------------------------------------- decode / sgd

@@ -146,4 +146,30 @@ __device__ __forceinline__ int upper_index(const T* a, int n, T v) {
     return lo;
 }
 
+// Exclusive scan in place of a[0..m) (uint32 or uint64) by one block of
+// kScanThreads threads, each summing a contiguous slice; total -> *tot (if
+// set) and, converted, -> *tot64 (if set).
+constexpr int kScanThreads = 1024;
+template <typename T>
+__global__ __launch_bounds__(kScanThreads) void k_excl_scan(T* __restrict__ a, int64_t m, T* __restrict__ tot,
+                                                            int64_t* __restrict__ tot64) {
+    __shared__ T lds[kScanThreads / kWave + 1];
+    const int64_t per = (m + kScanThreads - 1) / kScanThreads;
+    const int64_t i0 = per * threadIdx.x < m ? per * threadIdx.x : m;
+    const int64_t i1 = i0 + per < m ? i0 + per : m;
+    T sum = 0;
+    for (int64_t i = i0; i < i1; ++i) sum += a[i];
+    T total;
+    T run = block_excl_scan<kScanThreads>(sum, lds, &total);
+    for (int64_t i = i0; i < i1; ++i) {
+        const T t = a[i];
+        a[i] = run;
+        run += t;
+    }
+    if (threadIdx.x == 0) {
+        if (tot) *tot = total;
+        if (tot64) *tot64 = static_cast<int64_t>(total);
+    }
+}
+
 }  // namespace efg

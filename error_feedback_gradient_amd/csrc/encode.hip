@@ -20,7 +20,6 @@ constexpr int kBlock = 256;
 constexpr int kPer = 16;
 constexpr int kChunk = kBlock * kPer;  // items per block-unit
 constexpr int kMaxGrid = 4096;
-constexpr int kScanBlock = 1024;
 
 inline unsigned grid_for(int64_t items, int64_t per_block) {
     int64_t g = cdiv(std::max<int64_t>(items, 1), per_block);
@@ -40,29 +39,6 @@ __global__ __launch_bounds__(kBlock) void k_fill_bytes(uint8_t* __restrict__ p, 
     if (blockIdx.x == 0) {
         if (threadIdx.x < head) p[threadIdx.x] = v;
         for (int64_t i = head + nv * 16 + threadIdx.x; i < n; i += kBlock) p[i] = v;
-    }
-}
-
-// Exclusive scan in place of a[0..m) (uint32 or uint64); total -> *tot (if set)
-// and, converted, -> *tot64 (if set).
-template <typename T>
-__global__ __launch_bounds__(kScanBlock) void k_scan(T* __restrict__ a, int64_t m, T* __restrict__ tot,
-                                                     int64_t* __restrict__ tot64) {
-    __shared__ T lds[kScanBlock / kWave + 1];
-    const int64_t per = (m + kScanBlock - 1) / kScanBlock;
-    const int64_t i0 = std::min<int64_t>(m, per * threadIdx.x), i1 = std::min<int64_t>(m, i0 + per);
-    T sum = 0;
-    for (int64_t i = i0; i < i1; ++i) sum += a[i];
-    T total;
-    T run = block_excl_scan<kScanBlock>(sum, lds, &total);
-    for (int64_t i = i0; i < i1; ++i) {
-        const T t = a[i];
-        a[i] = run;
-        run += t;
-    }
-    if (threadIdx.x == 0) {
-        if (tot) *tot = total;
-        if (tot64) *tot64 = static_cast<int64_t>(total);
     }
 }
 
@@ -408,7 +384,7 @@ static int bitmap_decode_into(const uint8_t* bits, int64_t nbits, int32_t* out, 
     const int64_t nbytes = (nbits + 7) / 8;
     const int64_t nchunks = std::max<int64_t>(1, cdiv(nbytes, kChunk));
     EF_TRY(launch("bitmap_count", k_bm_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, bits, nbits, nchunks, cnt));
-    EF_TRY(launch("bitmap_scan", k_scan<uint32_t>, dim3(1), dim3(kScanBlock), s, cnt, nchunks, k_out32, k_out));
+    EF_TRY(launch("bitmap_scan", k_excl_scan<uint32_t>, dim3(1), dim3(kScanThreads), s, cnt, nchunks, k_out32, k_out));
     return launch("bitmap_write", k_bm_write, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, bits, nbits, nchunks,
                   static_cast<const uint32_t*>(cnt), out, cap);
 }
@@ -446,7 +422,7 @@ int encode_delta(const int32_t* idx, int64_t k, uint8_t* out, int64_t* nbytes_ou
     uint32_t* cnt = static_cast<uint32_t*>(ws);
     const int64_t nchunks = std::max<int64_t>(1, cdiv(k, kChunk));
     EF_TRY(launch("delta_count", k_de_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, idx, k, nchunks, cnt));
-    EF_TRY(launch("delta_scan", k_scan<uint32_t>, dim3(1), dim3(kScanBlock), s, cnt, nchunks,
+    EF_TRY(launch("delta_scan", k_excl_scan<uint32_t>, dim3(1), dim3(kScanThreads), s, cnt, nchunks,
                   static_cast<uint32_t*>(nullptr), nbytes_out));
     if (k == 0) return EF_OK;
     return launch("delta_write", k_de_write, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, idx, k, nchunks,
@@ -469,9 +445,9 @@ int decode_delta(const uint8_t* in, int64_t nbytes, int64_t k, int32_t* idx, uin
     if (status) EF_TRY(launch("delta_zero", k_zero_u32, dim3(1), dim3(1), s, status));
     EF_TRY(launch("delta_dcount", k_dd_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, in, nbytes, nchunks, tcnt,
                   dsum, status));
-    EF_TRY(launch("delta_dscan32", k_scan<uint32_t>, dim3(1), dim3(kScanBlock), s, tcnt, nchunks, ttot,
+    EF_TRY(launch("delta_dscan32", k_excl_scan<uint32_t>, dim3(1), dim3(kScanThreads), s, tcnt, nchunks, ttot,
                   static_cast<int64_t*>(nullptr)));
-    EF_TRY(launch("delta_dscan64", k_scan<uint64_t>, dim3(1), dim3(kScanBlock), s, dsum, nchunks,
+    EF_TRY(launch("delta_dscan64", k_excl_scan<uint64_t>, dim3(1), dim3(kScanThreads), s, dsum, nchunks,
                   static_cast<uint64_t*>(nullptr), static_cast<int64_t*>(nullptr)));
     if (status)
         EF_TRY(launch("delta_check", k_dd_check, dim3(1), dim3(1), s, in, nbytes, k,
@@ -510,7 +486,7 @@ int encode_blocks(const int32_t* idx, int64_t k, int64_t n, uint8_t* mask, uint8
                       static_cast<uint8_t>(0)));
     EF_TRY(launch("blocks_count", k_be_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, idx, k, n, nchunks, offs,
                   flags, cnt));
-    EF_TRY(launch("blocks_scan", k_scan<uint32_t>, dim3(1), dim3(kScanBlock), s, cnt, nchunks,
+    EF_TRY(launch("blocks_scan", k_excl_scan<uint32_t>, dim3(1), dim3(kScanThreads), s, cnt, nchunks,
                   static_cast<uint32_t*>(nullptr), nblk_out));
     if (k > 0)
         EF_TRY(launch("blocks_write", k_be_write, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, idx, k, n, nchunks,
@@ -545,7 +521,7 @@ int decode_blocks(const uint8_t* mask, const uint8_t* counts_m1, const uint8_t* 
     const int64_t mcap = std::min(k, nb);
     EF_TRY(launch("blocks_dcount", k_bd_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, counts_m1,
                   static_cast<const uint32_t*>(nblk), mcap, nchunks, cnt));
-    EF_TRY(launch("blocks_dscan", k_scan<uint32_t>, dim3(1), dim3(kScanBlock), s, cnt, nchunks,
+    EF_TRY(launch("blocks_dscan", k_excl_scan<uint32_t>, dim3(1), dim3(kScanThreads), s, cnt, nchunks,
                   static_cast<uint32_t*>(nullptr), static_cast<int64_t*>(nullptr)));
     return launch("blocks_dwrite", k_bd_write, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, counts_m1, offs,
                   static_cast<const int32_t*>(blk), static_cast<const uint32_t*>(nblk), mcap, nchunks,

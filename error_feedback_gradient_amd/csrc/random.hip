@@ -1,0 +1,539 @@
+// Random magnitude-proportional sparsification with error feedback, gfx950.
+//
+// "梯度稀疏化" page, section "随机稀疏化" (random sparsification): each element
+// survives with a probability proportional to its magnitude, normalised so
+// that k survive on average; it sits inside the page's generic error
+// compensation loop (section "误差补偿": add the residual, sparsify, keep in
+// the residual what was not sent).
+//
+// Per call, with x = g + e, S = sum of |x| over the finite x (exact, rounded
+// to float64 and then to float32: S32):
+//   p_i = min(1, (float(k) * |x_i|) / S32)  (float32; 0 for non-finite x_i)
+//   u_i = word (i mod 4) of Philox4x32-10(counter {i/4, 0, step lo, step hi},
+//         key {seed lo, seed hi}), top 24 bits times 2^-24
+//   kept iff u_i < p_i; kept elements are sent unscaled in index order (the
+//   first cap of them), their residual becomes +0; all others keep e = x.
+//
+// Passes (one wave per region of kRegion elements in the streaming ones):
+//   k_rs_accum   x = g + e written into e; per-lane float64 sums of |x|
+//                (12 B per element)
+//   k_rs_total   sums the wave partials and certifies float32(S) from a
+//                rigorous error bound; only when the bound straddles a
+//                float32 rounding boundary (or on EF_FLAG_FORCE_FALLBACK)
+//                do k_rs_exact / k_rs_exact_total re-read x and sum it
+//                exactly with integer accumulators (4 B per element, rare)
+//   k_rs_mark    reads x, draws u with one Philox call per 4 elements, writes
+//                the keep bitmap and per-region counts (4 B + 1 bit per element)
+//   k_excl_scan  region counts -> output offsets, the kept count
+//   k_rs_write   per region, the set bits of the bitmap -> (x, i) at their
+//                index-ordered place, e[i] = +0 (reads 1 bit per element plus
+//                the kept elements)
+// Every product, quotient and sum is rounded on its own (-ffp-contract=off,
+// IEEE division, denormals kept).
+#include <algorithm>
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace efg {
+namespace rs {
+
+#ifndef EFG_RS_BLOCK
+#define EFG_RS_BLOCK 512
+#endif
+#ifndef EFG_RS_REGION
+#define EFG_RS_REGION 8192
+#endif
+#ifndef EFG_RS_UNROLL
+#define EFG_RS_UNROLL 16
+#endif
+#ifndef EFG_RS_MARK_UNROLL
+#define EFG_RS_MARK_UNROLL 8
+#endif
+constexpr int kBlock = EFG_RS_BLOCK;
+constexpr int kWaves = kBlock / kWave;
+constexpr int kRegion = EFG_RS_REGION;
+constexpr int kUnroll = EFG_RS_UNROLL;
+constexpr int kMarkUnroll = EFG_RS_MARK_UNROLL;
+constexpr int kRegionWords = kRegion / 32;  // bitmap words per region
+static_assert(kRegion % 1024 == 0 && kRegion <= 8192,
+              "a region is whole 32-bit words of 4-element lanes, and at most 4 words per lane in k_rs_write");
+// The float64 error bound below assumes at most 8192 elements per region:
+// with n < 2^31 there are then at most 2^18 region partials.
+constexpr int kTotalBlock = 1024;
+constexpr int kExactWaves = 2048;  // grid of the exact-sum pass (grid-stride over regions)
+constexpr int kExactBlock = 256;
+constexpr int kBands = 8;  // exponent bands of 32 binades each
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+struct State {
+    double approx;      // float64 sum of the wave partials
+    float s32;          // S32
+    uint32_t uncertain; // 1: the exact pass decides S32
+    uint32_t nonfinite; // non-finite x seen by k_rs_accum
+    uint32_t kept;      // number kept (scan total)
+    uint32_t pad[10];
+};
+static_assert(sizeof(State) == 64, "State is one 64-byte slot");
+
+__device__ __forceinline__ bool finite(float x) { return (__float_as_uint(x) & 0x7f800000u) != 0x7f800000u; }
+
+__global__ void k_rs_init(State* st) {
+    st->approx = 0.0;
+    st->s32 = 0.0f;
+    st->uncertain = 0;
+    st->nonfinite = 0;
+    st->kept = 0;
+}
+
+// Wave w owns elements [w*kRegion, min((w+1)*kRegion, n)).  Lane l of unroll
+// step u holds float4 j = base + 64u + l of the region; a final partial float4
+// (only in the last region) is handled component by component.
+__global__ __launch_bounds__(kBlock) void k_rs_accum(const float* __restrict__ g, float* __restrict__ e, int64_t n,
+                                                     double* __restrict__ part, State* __restrict__ st) {
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
+    const int64_t beg = w * kRegion;
+    if (beg >= n) return;
+    const int64_t len = min(static_cast<int64_t>(kRegion), n - beg);
+    const int64_t nfull = len >> 2;
+    const int64_t nv = (len + 3) >> 2;
+    const int l = lane();
+    const f4* g4 = reinterpret_cast<const f4*>(g + beg);
+    f4* e4 = reinterpret_cast<f4*>(e + beg);
+    // four sequential float64 accumulators per lane: at most 32 additions each
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    uint32_t nf = 0;
+    auto account = [&](double& a, float x) {
+        if (finite(x)) a += static_cast<double>(fabsf(x));
+        else ++nf;
+    };
+    auto iteration = [&](int64_t base, auto guard) {
+        constexpr bool GUARD = decltype(guard)::value;
+        f4 gv[kUnroll], ev[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = base + u * kWave + l;
+            if (!GUARD || j < nfull) {
+                gv[u] = __builtin_nontemporal_load(g4 + j);
+                ev[u] = __builtin_nontemporal_load(e4 + j);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = base + u * kWave + l;
+            if (!GUARD || j < nfull) {
+                const f4 x = gv[u] + ev[u];
+                __builtin_nontemporal_store(x, e4 + j);
+                account(a0, x.x);
+                account(a1, x.y);
+                account(a2, x.z);
+                account(a3, x.w);
+            } else if (GUARD && j == nfull && nfull < nv) {
+                const int64_t i = beg + 4 * nfull;
+                const int64_t rem = len - 4 * nfull;  // 1..3
+                float x = g[i] + e[i];
+                e[i] = x;
+                account(a0, x);
+                if (rem > 1) {
+                    x = g[i + 1] + e[i + 1];
+                    e[i + 1] = x;
+                    account(a1, x);
+                }
+                if (rem > 2) {
+                    x = g[i + 2] + e[i + 2];
+                    e[i + 2] = x;
+                    account(a2, x);
+                }
+            }
+        }
+    };
+    constexpr int64_t kStep = kWave * kUnroll;
+    int64_t base = 0;
+    for (; base + kStep <= nfull; base += kStep) iteration(base, std::false_type{});
+    if (base < nv) iteration(base, std::true_type{});
+    double a = (a0 + a1) + (a2 + a3);
+    a = wave_sum(a);
+    nf = wave_sum(nf);
+    if (l == 0) {
+        part[w] = a;
+        if (nf) atomicAdd(&st->nonfinite, nf);
+    }
+}
+
+// Sum of the wave partials and the certified float32 rounding of the exact sum.
+// Every partial and sum is a sum of non-negative float64 values; along any
+// path of the summation tree there are at most 32 + 2 (lane) + 6 (wave)
+// + 256 (thread's share of <= 2^18 partials) + 6 + 16 (block) = 318 additions,
+// so the computed total t is within a relative 330 * 2^-53 < 2^-44 of the exact
+// sum S (Higham, Accuracy and Stability of Numerical Algorithms, section 4.2).
+// lo = t(1 - 2^-40) and hi = t(1 + 2^-40), each rounded once, then bracket S,
+// and rounding to float64 then float32 is monotone: when lo and hi give the
+// same float32 so does S.  Otherwise the exact pass decides.
+__global__ __launch_bounds__(kTotalBlock) void k_rs_total(const double* __restrict__ part, int64_t nw,
+                                                          uint32_t force_exact, State* __restrict__ st,
+                                                          float* __restrict__ sum_out,
+                                                          uint32_t* __restrict__ nonfinite) {
+    __shared__ double lsum[kTotalBlock / kWave];
+    double a = 0.0;
+    for (int64_t w = threadIdx.x; w < nw; w += kTotalBlock) a += part[w];
+    a = wave_sum(a);
+    if (lane() == 0) lsum[threadIdx.x / kWave] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        for (int i = 0; i < kTotalBlock / kWave; ++i) t += lsum[i];
+        const double lo = t * (1.0 - 0x1p-40);
+        const double hi = t * (1.0 + 0x1p-40);
+        const float flo = static_cast<float>(lo), fhi = static_cast<float>(hi);
+        const uint32_t unc = force_exact || __float_as_uint(flo) != __float_as_uint(fhi);
+        st->approx = t;
+        st->s32 = flo;
+        st->uncertain = unc;
+        if (sum_out) *sum_out = flo;
+        if (nonfinite) *nonfinite = st->nonfinite;
+    }
+}
+
+// Exact sum of |x| over the finite x, used when k_rs_total could not certify
+// float32(S).  A finite float32 magnitude is M * 2^s * 2^-149 with an integer
+// M < 2^24 and s = max(biased exponent, 1) - 1 in [0, 253]; band b = s / 32
+// gathers M << (s mod 32) (< 2^55) in one uint64 per lane and band.  After
+// each region (<= 131 elements per lane, so no band exceeds 2^63) the bands
+// are folded into 32-bit halves summed in uint64.  Wave w writes 16 uint64
+// (band b: low-half sum, high-half sum) to xpart[16 w ..].
+__global__ __launch_bounds__(kExactBlock) void k_rs_exact(const float* __restrict__ x, int64_t n, int64_t nw,
+                                                          const State* __restrict__ st,
+                                                          uint64_t* __restrict__ xpart) {
+    if (!st->uncertain) return;
+    const int64_t w0 = static_cast<int64_t>(blockIdx.x) * (kExactBlock / kWave) + threadIdx.x / kWave;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * (kExactBlock / kWave);
+    const int l = lane();
+    uint64_t wlo[kBands], whi[kBands];
+#pragma unroll
+    for (int b = 0; b < kBands; ++b) wlo[b] = whi[b] = 0;
+    for (int64_t r = w0; r < nw; r += stride) {
+        const int64_t beg = r * kRegion;
+        const int64_t end = min(beg + static_cast<int64_t>(kRegion), n);
+        uint64_t acc[kBands];
+#pragma unroll
+        for (int b = 0; b < kBands; ++b) acc[b] = 0;
+        for (int64_t i = beg + l; i < end; i += kWave) {
+            const uint32_t u = __float_as_uint(x[i]) & 0x7fffffffu;
+            const uint32_t ex = u >> 23;
+            if (ex == 0xffu) continue;
+            const uint32_t s = ex ? ex - 1 : 0;
+            const uint64_t m = static_cast<uint64_t>((u & 0x7fffffu) | (ex ? 0x800000u : 0u)) << (s & 31u);
+            const uint32_t band = s >> 5;
+#pragma unroll
+            for (int b = 0; b < kBands; ++b) acc[b] += band == static_cast<uint32_t>(b) ? m : 0ull;
+        }
+#pragma unroll
+        for (int b = 0; b < kBands; ++b) {
+            wlo[b] += acc[b] & 0xffffffffull;
+            whi[b] += acc[b] >> 32;
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < kBands; ++b) {
+        wlo[b] = wave_sum(wlo[b]);
+        whi[b] = wave_sum(whi[b]);
+    }
+    if (l == 0) {
+        const int64_t w = w0;
+#pragma unroll
+        for (int b = 0; b < kBands; ++b) {
+            xpart[16 * w + 2 * b] = wlo[b];
+            xpart[16 * w + 2 * b + 1] = whi[b];
+        }
+    }
+}
+
+// Bits [p, p + 64) of the integer held in 32-bit limbs L[0..nl) (bits below
+// 0 read as zero); *below gets whether any bit under p is set.
+__device__ uint64_t window64(const uint64_t* L, int nl, int p, bool* below) {
+    uint64_t r = 0;
+    bool any = false;
+    for (int j = 0; j < nl; ++j) {
+        const int sh = 32 * j - p;  // where limb bit 0 lands in the window
+        if (sh <= -32) {
+            any |= L[j] != 0;
+        } else if (sh < 0) {
+            r |= L[j] >> (-sh);
+            any |= (L[j] & ((1ull << (-sh)) - 1)) != 0;
+        } else if (sh < 64) {
+            r |= L[j] << sh;
+        }
+    }
+    *below = any;
+    return r;
+}
+
+// Totals the exact band sums and rounds them to float64 (nearest, ties to
+// even), then to float32.
+constexpr int kLimbs = 12;
+__global__ __launch_bounds__(kExactBlock) void k_rs_exact_total(const uint64_t* __restrict__ xpart, int64_t nwx,
+                                                                State* __restrict__ st, float* __restrict__ sum_out) {
+    if (!st->uncertain) return;
+    __shared__ uint64_t tot[16];
+    if (threadIdx.x < 16) {
+        uint64_t a = 0;
+        for (int64_t w = 0; w < nwx; ++w) a += xpart[16 * w + threadIdx.x];
+        tot[threadIdx.x] = a;
+    }
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    // band b is (lo + hi * 2^32) * 2^(32 b) in units of 2^-149
+    uint64_t L[kLimbs];
+    for (int j = 0; j < kLimbs; ++j) L[j] = 0;
+    for (int b = 0; b < kBands; ++b) {
+        L[b] += tot[2 * b];
+        L[b + 1] += tot[2 * b + 1];
+    }
+    for (int j = 0; j + 1 < kLimbs; ++j) {
+        L[j + 1] += L[j] >> 32;
+        L[j] &= 0xffffffffull;
+    }
+    int top = -1;
+    for (int j = kLimbs - 1; j >= 0; --j) {
+        if (L[j]) {
+            top = 32 * j + 63 - __clzll(L[j]);
+            break;
+        }
+    }
+    double S = 0.0;
+    if (top >= 0) {
+        bool below = false;
+        const uint64_t W = window64(L, kLimbs, top - 63, &below);  // bit 63 of W is the leading bit
+        if (top < 53) {
+            S = ldexp(static_cast<double>(W >> (63 - top)), -149);  // every bit fits: exact
+        } else {
+            uint64_t mant = W >> 11;
+            const bool guard = (W >> 10) & 1u;
+            const bool sticky = below || (W & 0x3ffull) != 0;
+            if (guard && (sticky || (mant & 1u))) ++mant;
+            S = ldexp(static_cast<double>(mant), top - 52 - 149);
+        }
+    }
+    st->approx = S;
+    st->s32 = static_cast<float>(S);
+    if (sum_out) *sum_out = st->s32;
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011) on counter c with key
+// {k0, k1}; the key advances by the two Weyl constants after every round.
+__device__ __forceinline__ void philox(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3, uint32_t k0,
+                                       uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        // one 32x32->64 product per multiplier (v_mad_u64_u32 gives both halves)
+        const uint64_t p0 = static_cast<uint64_t>(c0) * 0xD2511F53u;
+        const uint64_t p1 = static_cast<uint64_t>(c2) * 0xCD9E8D57u;
+        const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+        c0 = n0;
+        c1 = static_cast<uint32_t>(p1);
+        c2 = n2;
+        c3 = static_cast<uint32_t>(p0);
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+}
+
+__device__ __forceinline__ uint32_t keep_bit(float x, uint32_t word, float kf, float S) {
+    if (!finite(x)) return 0u;
+    const float t = kf * fabsf(x);
+    float p = t / S;
+    if (p > 1.0f) p = 1.0f;
+    const float u = static_cast<float>(word >> 8) * 0x1p-24f;
+    return u < p ? 1u : 0u;
+}
+
+// Decisions for the region of wave w.  Lane l of unroll step u holds float4 j
+// (elements 4j..4j+3 of the region, one Philox call); eight neighbouring lanes
+// OR their nibbles into one 32-bit bitmap word (bit i mod 32 of word i / 32).
+__global__ __launch_bounds__(kBlock) void k_rs_mark(const float* __restrict__ x, int64_t n, float kf, uint32_t key0,
+                                                    uint32_t key1, uint32_t step0, uint32_t step1,
+                                                    const State* __restrict__ st, uint32_t* __restrict__ bm,
+                                                    uint32_t* __restrict__ cnt) {
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
+    const int64_t beg = w * kRegion;
+    if (beg >= n) return;
+    const int64_t len = min(static_cast<int64_t>(kRegion), n - beg);
+    const int64_t nfull = len >> 2;
+    const int64_t nv = (len + 3) >> 2;
+    const int l = lane();
+    const float S = st->s32;
+    const f4* x4 = reinterpret_cast<const f4*>(x + beg);
+    uint32_t* bw = bm + (beg >> 5);
+    const uint32_t q0 = static_cast<uint32_t>(beg >> 2);
+    uint32_t count = 0;
+    auto iteration = [&](int64_t base, auto guard) {
+        constexpr bool GUARD = decltype(guard)::value;
+        f4 xv[kMarkUnroll];
+#pragma unroll
+        for (int u = 0; u < kMarkUnroll; ++u) {
+            const int64_t j = base + u * kWave + l;
+            if (!GUARD || j < nfull) {
+                xv[u] = __builtin_nontemporal_load(x4 + j);
+            } else {
+                xv[u] = f4{0.f, 0.f, 0.f, 0.f};
+                if (j == nfull) {
+                    const int64_t rem = len - 4 * nfull;  // 0..3 valid components
+                    if (rem > 0) xv[u].x = x[beg + 4 * nfull];
+                    if (rem > 1) xv[u].y = x[beg + 4 * nfull + 1];
+                    if (rem > 2) xv[u].z = x[beg + 4 * nfull + 2];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kMarkUnroll; ++u) {
+            const int64_t j = base + u * kWave + l;
+            uint32_t c0 = q0 + static_cast<uint32_t>(j), c1 = 0u, c2 = step0, c3 = step1;
+            philox(c0, c1, c2, c3, key0, key1);
+            uint32_t nib = keep_bit(xv[u].x, c0, kf, S) | keep_bit(xv[u].y, c1, kf, S) << 1 |
+                           keep_bit(xv[u].z, c2, kf, S) << 2 | keep_bit(xv[u].w, c3, kf, S) << 3;
+            if (GUARD && j >= nv) nib = 0;  // zero-filled components of a partial float4 have p = 0 anyway
+            count += __popc(nib);
+            uint32_t word = nib << (4 * (l & 7));
+            word |= __shfl_xor(word, 1, kWave);
+            word |= __shfl_xor(word, 2, kWave);
+            word |= __shfl_xor(word, 4, kWave);
+            const int64_t j8 = base + u * kWave + (l & ~7);  // first float4 of this word
+            if ((l & 7) == 0 && (!GUARD || j8 < nv)) bw[j8 >> 3] = word;
+        }
+    };
+    constexpr int64_t kStep = kWave * kMarkUnroll;
+    int64_t base = 0;
+    for (; base + kStep <= nfull; base += kStep) iteration(base, std::false_type{});
+    if (base < nv) iteration(base, std::true_type{});
+    count = wave_sum(count);
+    if (l == 0) cnt[w] = count;
+}
+
+// Region w: its bitmap words (4 per lane) in order, each set bit -> output
+// slot off[w] + rank; slots below cap get (x, i) and e[i] = +0.
+__global__ __launch_bounds__(kBlock) void k_rs_write(float* __restrict__ e, int64_t n, int64_t nw,
+                                                     const uint32_t* __restrict__ bm,
+                                                     const uint32_t* __restrict__ off,
+                                                     const State* __restrict__ st, float* __restrict__ vals,
+                                                     int32_t* __restrict__ idx, int64_t cap) {
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
+    const int64_t beg = w * kRegion;
+    if (beg >= n) return;
+    const uint32_t o = off[w];
+    const uint32_t o_next = w + 1 < nw ? off[w + 1] : st->kept;
+    if (o_next == o || static_cast<int64_t>(o) >= cap) return;
+    const int64_t len = min(static_cast<int64_t>(kRegion), n - beg);
+    const int64_t nwords = (len + 31) >> 5;
+    const int l = lane();
+    const uint32_t* bw = bm + (beg >> 5);
+    uint32_t wd[4];
+    uint32_t c = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t wi = 4 * l + q;
+        wd[q] = wi < nwords ? bw[wi] : 0u;
+        c += __popc(wd[q]);
+    }
+    int64_t pos = static_cast<int64_t>(o) + (wave_incl_scan(c) - c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t v = wd[q];
+        while (v) {
+            const int b = __ffs(v) - 1;
+            v &= v - 1;
+            if (pos < cap) {
+                const int64_t i = beg + 32 * (4 * l + q) + b;
+                vals[pos] = e[i];
+                idx[pos] = static_cast<int32_t>(i);
+                e[i] = 0.0f;
+            }
+            ++pos;
+        }
+    }
+}
+
+__global__ void k_rs_empty(int64_t* count_out, float* sum_out, uint32_t* nonfinite) {
+    *count_out = 0;
+    if (sum_out) *sum_out = 0.0f;
+    if (nonfinite) *nonfinite = 0;
+}
+
+struct Layout {
+    int64_t nw;
+    size_t state, part, cnt, xpart, bm, total;
+};
+
+inline Layout layout_for(int64_t n) {
+    Layout L{};
+    L.nw = std::max<int64_t>(1, cdiv(n, kRegion));
+    size_t o = 0;
+    L.state = o;
+    o += 256;
+    L.part = o;
+    o = round_up(o + static_cast<size_t>(L.nw) * sizeof(double), 256);
+    L.cnt = o;
+    o = round_up(o + static_cast<size_t>(L.nw) * sizeof(uint32_t), 256);
+    L.xpart = o;
+    o = round_up(o + static_cast<size_t>(kExactWaves) * 16 * sizeof(uint64_t), 256);
+    L.bm = o;
+    o = round_up(o + static_cast<size_t>(L.nw) * kRegionWords * sizeof(uint32_t), 256);
+    L.total = o;
+    return L;
+}
+
+}  // namespace rs
+}  // namespace efg
+
+using namespace efg;
+
+extern "C" size_t ef_random_sparsify_workspace_bytes(int64_t n) {
+    if (n < 0 || n > kMaxElems) return 0;
+    return rs::layout_for(n).total;
+}
+
+extern "C" int ef_random_sparsify(const float* g, float* e, int64_t n, int64_t k, uint64_t seed, uint64_t step,
+                                  float* vals, int32_t* idx, int64_t cap, int64_t* count_out, float* sum_out,
+                                  uint32_t* nonfinite, void* ws, size_t ws_bytes, uint32_t flags, void* stream) {
+    if (n < 0 || n > kMaxElems) return fail(EF_EINVAL, "n=%lld outside [0, 2^31-1]", (long long)n);
+    if (k < 0 || k > kMaxElems) return fail(EF_EINVAL, "k=%lld outside [0, 2^31-1]", (long long)k);
+    if (cap < 0) return fail(EF_EINVAL, "cap must be >= 0");
+    if (flags & ~EF_FLAG_FORCE_FALLBACK) return fail(EF_EINVAL, "unknown flags 0x%x", flags);
+    if (!count_out) return fail(EF_EINVAL, "count_out must not be NULL");
+    if (n > 0 && (!g || !e)) return fail(EF_EINVAL, "g and e must not be NULL");
+    if (n > 0 && (!aligned16(g) || !aligned16(e))) return fail(EF_EINVAL, "g and e must be 16-byte aligned");
+    if (cap > 0 && (!vals || !idx)) return fail(EF_EINVAL, "vals and idx must not be NULL when cap > 0");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n == 0) return launch("rs_empty", rs::k_rs_empty, dim3(1), dim3(1), s, count_out, sum_out, nonfinite);
+    const rs::Layout L = rs::layout_for(n);
+    if (!ws || ws_bytes < L.total)
+        return fail(EF_EWS, "ef_random_sparsify: needs %zu bytes of workspace", L.total);
+    if (!aligned256(ws)) return fail(EF_EINVAL, "workspace must be 256-byte aligned");
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    rs::State* st = reinterpret_cast<rs::State*>(base + L.state);
+    double* part = reinterpret_cast<double*>(base + L.part);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(base + L.cnt);
+    uint64_t* xpart = reinterpret_cast<uint64_t*>(base + L.xpart);
+    uint32_t* bm = reinterpret_cast<uint32_t*>(base + L.bm);
+    const unsigned grid = static_cast<unsigned>(cdiv(L.nw, rs::kWaves));
+    const unsigned xgrid =
+        static_cast<unsigned>(cdiv(std::min<int64_t>(rs::kExactWaves, L.nw), rs::kExactBlock / kWave));
+    const int64_t nwx = static_cast<int64_t>(xgrid) * (rs::kExactBlock / kWave);
+    EF_TRY(launch("rs_init", rs::k_rs_init, dim3(1), dim3(1), s, st));
+    EF_TRY(launch("rs_accum", rs::k_rs_accum, dim3(grid), dim3(rs::kBlock), s, g, e, n, part, st));
+    EF_TRY(launch("rs_total", rs::k_rs_total, dim3(1), dim3(rs::kTotalBlock), s, static_cast<const double*>(part),
+                  L.nw, static_cast<uint32_t>(flags & EF_FLAG_FORCE_FALLBACK), st, sum_out, nonfinite));
+    EF_TRY(launch("rs_exact", rs::k_rs_exact, dim3(xgrid), dim3(rs::kExactBlock), s, static_cast<const float*>(e), n,
+                  L.nw, static_cast<const rs::State*>(st), xpart));
+    EF_TRY(launch("rs_exact_total", rs::k_rs_exact_total, dim3(1), dim3(rs::kExactBlock), s,
+                  static_cast<const uint64_t*>(xpart), nwx, st, sum_out));
+    EF_TRY(launch("rs_mark", rs::k_rs_mark, dim3(grid), dim3(rs::kBlock), s, static_cast<const float*>(e), n,
+                  static_cast<float>(k), static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32),
+                  static_cast<uint32_t>(step), static_cast<uint32_t>(step >> 32), static_cast<const rs::State*>(st),
+                  bm, cnt));
+    EF_TRY(launch("rs_scan", k_excl_scan<uint32_t>, dim3(1), dim3(kScanThreads), s, cnt, L.nw, &st->kept, count_out));
+    return launch("rs_write", rs::k_rs_write, dim3(grid), dim3(rs::kBlock), s, e, n, L.nw,
+                  static_cast<const uint32_t*>(bm), static_cast<const uint32_t*>(cnt),
+                  static_cast<const rs::State*>(st), vals, idx, cap);
+}

@@ -21,6 +21,9 @@ Workloads (sizes are exact):
              N(0,1) starting weights.
 * ``large``  N = 1,300,000,000 magnitudes exp(-7 + 2 z), z ~ N(0,1), with random
              signs from a separate bit stream, k = 1,300,000, 5 chained steps.
+* ``random`` the large workload's gradients and sizes with k = 1,300,000 the
+             expected count of random sparsification; its draws are keyed by
+             RANDOM_SEED and the step number.
 
 Nothing in this module computes any part of the compression method.
 """
@@ -41,6 +44,7 @@ SIGN_N, SIGN_STEPS, SIGN_BETA1, SIGN_CLIP = 340_000_000, 50, 0.9, 5.0
 DECODE_N, DECODE_PACKETS, DECODE_K, DECODE_LR = 25_600_000, 16, 25_600, 0.1
 LARGE_N, LARGE_K, LARGE_STEPS, LARGE_BLOCK = 1_300_000_000, 1_300_000, 5, 256
 BERT_STEPS = 20
+RANDOM_SEED = 0x5EED_0001
 
 
 def rng(*key: int) -> np.random.Generator:

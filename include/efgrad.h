@@ -159,6 +159,39 @@ int ef_quantize_int8(const float* vals, const int32_t* idx, int64_t k, float* e,
                      int8_t* q, float* scale_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Random magnitude-proportional sparsification with error feedback.
+ * [SPARSE] "随机稀疏化" (random sparsification: each element survives with a
+ * probability proportional to its magnitude, normalised so that about k
+ * survive) inside the page's error-compensation loop ("误差补偿").
+ *
+ * Per element i, float32, each product and quotient rounded on its own:
+ *   x  = g + e
+ *   S  = sum of |x| over the finite x, exact, rounded to float64 and then to
+ *        float32 (S32; *sum_out, device float, nullable)
+ *   p  = min(1, (float(k) * |x|) / S32)      0 for a non-finite x; a NaN
+ *        quotient (S32 = 0 or inf/inf) keeps nothing
+ *   u  = word (i mod 4) of Philox4x32-10 on counter {i/4, 0, step low 32,
+ *        step high 32} with key {seed low 32, seed high 32}, top 24 bits
+ *        times 2^-24
+ *   kept iff u < p
+ * Kept elements are written in increasing index order: the first cap of them
+ * as vals[j] = x, idx[j] = i, and their residual becomes +0.  Every other
+ * element, a kept one beyond cap included, keeps e = x.
+ *   *count_out = number kept (device int64, required; may exceed cap)
+ *   *nonfinite = number of non-finite x (device uint32, nullable)
+ * 0 <= n, k <= 2^31 - 1; cap >= 0 (vals/idx may be NULL when cap = 0);
+ * g and e 16-byte aligned; ws: ef_random_sparsify_workspace_bytes(n) bytes,
+ * 256-byte aligned (unused when n = 0).
+ * flags: 0 or EF_FLAG_FORCE_FALLBACK (always take the exact integer sum
+ * instead of the certified float64 one; the result is the same).
+ * ------------------------------------------------------------------------ */
+size_t ef_random_sparsify_workspace_bytes(int64_t n);
+int ef_random_sparsify(const float* g, float* e, int64_t n, int64_t k, uint64_t seed,
+                       uint64_t step, float* vals, int32_t* idx, int64_t cap,
+                       int64_t* count_out, float* sum_out, uint32_t* nonfinite, void* ws,
+                       size_t ws_bytes, uint32_t flags, void* stream);
+
+/* ------------------------------------------------------------------------
  * Receiver-side aggregation of sparse packets.  [SPARSE] "梯度稀疏化的基本原理"
  * (values sharing an index are summed) and "详细算法流程" step 6.
  *

@@ -51,6 +51,7 @@ def lib():
             "orc_blocks_encode": [p, i64, i64, p, p, p, p],
             "orc_blocks_decode": [p, p, p, i64, p, i64, p],
             "orc_quantize_int8": [p, p, i64, p, p, p],
+            "orc_random_keep_at": [p, p, i64, i64, f, C.c_uint64, C.c_uint64, p],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -257,3 +258,13 @@ def random_sparsify(g, e, k, seed, step, cap=None):
     c = int(cnt[0])
     w = min(c, cap)
     return vals[:w].copy(), idx[:w].copy(), e2, c, float(s32[0]), int(bad[0])
+
+
+def random_keep_at(x_at, pos, k, s32, seed, step):
+    """Keep decisions (bool array) for elements pos whose x values are x_at."""
+    x_at = _f32(x_at)
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    keep = np.zeros(max(pos.size, 1), np.uint8)
+    _check(lib().orc_random_keep_at(_ptr(x_at), _ptr(pos), pos.size, k, s32, seed, step, _ptr(keep)),
+           "random_keep_at")
+    return keep[:pos.size].astype(bool)

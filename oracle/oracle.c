@@ -556,3 +556,16 @@ int orc_random_sparsify(const float* g, float* e, int64_t n, int64_t k, uint64_t
     if (nonfinite) *nonfinite = bad;
     return ORC_OK;
 }
+
+/* The keep decision of orc_random_sparsify at chosen positions: keep[j] for
+ * element pos[j], whose x = g + e is x[j], given S32.  Lets large inputs be
+ * checked one sampled element at a time. */
+int orc_random_keep_at(const float* x, const int64_t* pos, int64_t m, int64_t k, float S32, uint64_t seed,
+                       uint64_t step, uint8_t* keep) {
+    if (m < 0 || k < 0) return ORC_EINVAL;
+    for (int64_t j = 0; j < m; ++j) {
+        if (pos[j] < 0 || pos[j] > 0x7fffffffLL) return ORC_EINVAL;
+        keep[j] = (uint8_t)(orc_uniform(seed, step, pos[j]) < orc_keep_probability(x[j], k, S32));
+    }
+    return ORC_OK;
+}

@@ -167,3 +167,29 @@ def test_binding_never_uses_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def test_random_sparsify_argument_checks():
+    L = efg.lib()
+    ws = L.ef_random_sparsify_workspace_bytes(100_000)
+    assert ws > 100_000 // 8
+    assert L.ef_random_sparsify_workspace_bytes(-1) == 0
+    assert L.ef_random_sparsify_workspace_bytes(2**31) == 0
+    call = lambda **kw: L.ef_random_sparsify(
+        kw.get("g", FAKE), kw.get("e", FAKE), kw.get("n", 100_000), kw.get("k", 100), 1, 2, kw.get("v", FAKE),
+        kw.get("i", FAKE), kw.get("cap", 300), kw.get("cnt", FAKE), None, None, kw.get("ws", FAKE),
+        kw.get("wsb", ws), kw.get("flags", 0), None)
+    assert call(n=-1) == efg.EF_EINVAL
+    assert call(n=2**31) == efg.EF_EINVAL
+    assert call(k=-1) == efg.EF_EINVAL
+    assert call(cap=-1) == efg.EF_EINVAL
+    assert call(flags=2) == efg.EF_EINVAL
+    assert call(cnt=None) == efg.EF_EINVAL
+    assert call(g=None) == efg.EF_EINVAL
+    assert call(e=FAKE_ODD) == efg.EF_EINVAL and "aligned" in efg.last_error()
+    assert call(v=None) == efg.EF_EINVAL
+    assert call(ws=None) == efg.EF_EWS
+    assert call(wsb=ws - 1) == efg.EF_EWS
+    assert call(ws=FAKE + 16) == efg.EF_EINVAL
+    # the bitmap dominates the workspace: about n/8 bytes
+    assert L.ef_random_sparsify_workspace_bytes(1_300_000_000) < 1_300_000_000 // 8 + (8 << 20)

@@ -282,3 +282,14 @@ def test_lognormal_workload_expected_count():
     _, idx, _, c, _, _ = oracle.random_sparsify(g, np.zeros(n, np.float32), k, 123, 0)
     mu, sd = p.sum(), math.sqrt(np.sum(p * (1 - p)))
     assert mu <= k and abs(c - mu) < 6 * sd
+
+
+def test_keep_at_matches_full_run():
+    g, e = draw(20_000, 8)
+    x = (g + e).astype(np.float32)
+    _, idx, _, c, s32, _ = oracle.random_sparsify(g, e, 700, 9, 3)
+    pos = np.arange(x.size)
+    keep = oracle.random_keep_at(x, pos, 700, np.float32(s32), 9, 3)
+    assert np.nonzero(keep)[0].tolist() == idx.tolist()
+    sub = np.array([19_999, 0, 5, 4, 12_345], np.int64)
+    assert oracle.random_keep_at(x[sub], sub, 700, np.float32(s32), 9, 3).tolist() == keep[sub].tolist()
