@@ -15,8 +15,8 @@
 //   first cap of them), their residual becomes +0; all others keep e = x.
 //
 // Passes (one wave per region of kRegion elements in the streaming ones):
-//   k_rs_accum   x = g + e written into e; per-lane float64 sums of |x|
-//                (12 B per element)
+//   k_rs_accum   x = g + e written into e; float64 sums of |x| per lane,
+//                folded per block (12 B per element)
 //   k_rs_total   sums the wave partials and certifies float32(S) from a
 //                rigorous error bound; only when the bound straddles a
 //                float32 rounding boundary (or on EF_FLAG_FORCE_FALLBACK)
@@ -24,7 +24,7 @@
 //                exactly with integer accumulators (4 B per element, rare)
 //   k_rs_mark    reads x, draws u with one Philox call per 4 elements, writes
 //                the keep bitmap and per-region counts (4 B + 1 bit per element)
-//   k_excl_scan  region counts -> output offsets, the kept count
+//   k_rs_scan_tiles, k_excl_scan  region counts -> output offsets, the kept count
 //   k_rs_write   per region, the set bits of the bitmap -> (x, i) at their
 //                index-ordered place, e[i] = +0 (reads 1 bit per element plus
 //                the kept elements)
@@ -38,32 +38,44 @@
 namespace efg {
 namespace rs {
 
+// Shapes measured on MI355X (sweep over blocks 256-1024, regions 2048-8192,
+// unrolls 4-16): k_rs_accum streams regions of EFG_RS_ACC_REGION elements per
+// wave with all EFG_RS_ACC_UNROLL float4 loads of g and e issued at once;
+// k_rs_mark and k_rs_write work on regions of EFG_RS_REGION elements (one
+// bitmap slice and one output count each).
 #ifndef EFG_RS_BLOCK
 #define EFG_RS_BLOCK 512
+#endif
+#ifndef EFG_RS_ACC_REGION
+#define EFG_RS_ACC_REGION 4096
+#endif
+#ifndef EFG_RS_ACC_UNROLL
+#define EFG_RS_ACC_UNROLL 16
 #endif
 #ifndef EFG_RS_REGION
 #define EFG_RS_REGION 8192
 #endif
-#ifndef EFG_RS_UNROLL
-#define EFG_RS_UNROLL 16
-#endif
 #ifndef EFG_RS_MARK_UNROLL
-#define EFG_RS_MARK_UNROLL 8
+#define EFG_RS_MARK_UNROLL 4
 #endif
 constexpr int kBlock = EFG_RS_BLOCK;
 constexpr int kWaves = kBlock / kWave;
+constexpr int kAccRegion = EFG_RS_ACC_REGION;
+constexpr int kUnroll = EFG_RS_ACC_UNROLL;
 constexpr int kRegion = EFG_RS_REGION;
-constexpr int kUnroll = EFG_RS_UNROLL;
 constexpr int kMarkUnroll = EFG_RS_MARK_UNROLL;
 constexpr int kRegionWords = kRegion / 32;  // bitmap words per region
 static_assert(kRegion % 1024 == 0 && kRegion <= 8192,
               "a region is whole 32-bit words of 4-element lanes, and at most 4 words per lane in k_rs_write");
-// The float64 error bound below assumes at most 8192 elements per region:
-// with n < 2^31 there are then at most 2^18 region partials.
+static_assert(kAccRegion % 256 == 0 && static_cast<long long>(kAccRegion) * kWaves >= 8192 && kWaves <= 16 &&
+                  kAccRegion / kWave / 4 <= 32,
+              "the float64 error bound of k_rs_total counts at most 32 additions per lane accumulator, "
+              "16 waves per block and 2^18 block partials");
 constexpr int kTotalBlock = 1024;
 constexpr int kExactWaves = 2048;  // grid of the exact-sum pass (grid-stride over regions)
 constexpr int kExactBlock = 256;
 constexpr int kBands = 8;  // exponent bands of 32 binades each
+constexpr int kScanTile = 4 * kScanThreads;  // region counts per first-level scan block
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
@@ -87,96 +99,121 @@ __global__ void k_rs_init(State* st) {
     st->kept = 0;
 }
 
-// Wave w owns elements [w*kRegion, min((w+1)*kRegion, n)).  Lane l of unroll
-// step u holds float4 j = base + 64u + l of the region; a final partial float4
-// (only in the last region) is handled component by component.
+// Wave w owns elements [w*kAccRegion, min((w+1)*kAccRegion, n)).  Lane l of
+// unroll step u holds float4 j = base + 64u + l of the region; a final partial
+// float4 (only in the last region) is handled component by component.  Block
+// b writes part[b], the sum of its waves' partials in wave order.
 __global__ __launch_bounds__(kBlock) void k_rs_accum(const float* __restrict__ g, float* __restrict__ e, int64_t n,
                                                      double* __restrict__ part, State* __restrict__ st) {
+    __shared__ double lsum[kWaves];
+    __shared__ uint32_t lnf[kWaves];
     const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
-    const int64_t beg = w * kRegion;
-    if (beg >= n) return;
-    const int64_t len = min(static_cast<int64_t>(kRegion), n - beg);
-    const int64_t nfull = len >> 2;
-    const int64_t nv = (len + 3) >> 2;
+    const int64_t beg = w * kAccRegion;
     const int l = lane();
-    const f4* g4 = reinterpret_cast<const f4*>(g + beg);
-    f4* e4 = reinterpret_cast<f4*>(e + beg);
     // four sequential float64 accumulators per lane: at most 32 additions each
     double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
     uint32_t nf = 0;
-    auto account = [&](double& a, float x) {
-        if (finite(x)) a += static_cast<double>(fabsf(x));
-        else ++nf;
-    };
-    auto iteration = [&](int64_t base, auto guard) {
-        constexpr bool GUARD = decltype(guard)::value;
-        f4 gv[kUnroll], ev[kUnroll];
+    if (beg < n) {
+        const int64_t len = min(static_cast<int64_t>(kAccRegion), n - beg);
+        const int64_t nfull = len >> 2;
+        const int64_t nv = (len + 3) >> 2;
+        const f4* g4 = reinterpret_cast<const f4*>(g + beg);
+        f4* e4 = reinterpret_cast<f4*>(e + beg);
+        auto account = [&](double& a, float x) {
+            if (finite(x)) a += static_cast<double>(fabsf(x));
+            else ++nf;
+        };
+        auto iteration = [&](int64_t base, auto guard) {
+            constexpr bool GUARD = decltype(guard)::value;
+            f4 gv[kUnroll], ev[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t j = base + u * kWave + l;
-            if (!GUARD || j < nfull) {
-                gv[u] = __builtin_nontemporal_load(g4 + j);
-                ev[u] = __builtin_nontemporal_load(e4 + j);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t j = base + u * kWave + l;
-            if (!GUARD || j < nfull) {
-                const f4 x = gv[u] + ev[u];
-                __builtin_nontemporal_store(x, e4 + j);
-                account(a0, x.x);
-                account(a1, x.y);
-                account(a2, x.z);
-                account(a3, x.w);
-            } else if (GUARD && j == nfull && nfull < nv) {
-                const int64_t i = beg + 4 * nfull;
-                const int64_t rem = len - 4 * nfull;  // 1..3
-                float x = g[i] + e[i];
-                e[i] = x;
-                account(a0, x);
-                if (rem > 1) {
-                    x = g[i + 1] + e[i + 1];
-                    e[i + 1] = x;
-                    account(a1, x);
-                }
-                if (rem > 2) {
-                    x = g[i + 2] + e[i + 2];
-                    e[i + 2] = x;
-                    account(a2, x);
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t j = base + u * kWave + l;
+                if (!GUARD || j < nfull) {
+                    gv[u] = __builtin_nontemporal_load(g4 + j);
+                    ev[u] = __builtin_nontemporal_load(e4 + j);
                 }
             }
-        }
-    };
-    constexpr int64_t kStep = kWave * kUnroll;
-    int64_t base = 0;
-    for (; base + kStep <= nfull; base += kStep) iteration(base, std::false_type{});
-    if (base < nv) iteration(base, std::true_type{});
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t j = base + u * kWave + l;
+                if (!GUARD || j < nfull) {
+                    const f4 x = gv[u] + ev[u];
+                    __builtin_nontemporal_store(x, e4 + j);
+                    account(a0, x.x);
+                    account(a1, x.y);
+                    account(a2, x.z);
+                    account(a3, x.w);
+                } else if (GUARD && j == nfull && nfull < nv) {
+                    const int64_t i = beg + 4 * nfull;
+                    const int64_t rem = len - 4 * nfull;  // 1..3
+                    float x = g[i] + e[i];
+                    e[i] = x;
+                    account(a0, x);
+                    if (rem > 1) {
+                        x = g[i + 1] + e[i + 1];
+                        e[i + 1] = x;
+                        account(a1, x);
+                    }
+                    if (rem > 2) {
+                        x = g[i + 2] + e[i + 2];
+                        e[i + 2] = x;
+                        account(a2, x);
+                    }
+                }
+            }
+        };
+        constexpr int64_t kStep = kWave * kUnroll;
+        int64_t base = 0;
+        for (; base + kStep <= nfull; base += kStep) iteration(base, std::false_type{});
+        if (base < nv) iteration(base, std::true_type{});
+    }
     double a = (a0 + a1) + (a2 + a3);
     a = wave_sum(a);
     nf = wave_sum(nf);
     if (l == 0) {
-        part[w] = a;
-        if (nf) atomicAdd(&st->nonfinite, nf);
+        lsum[threadIdx.x / kWave] = a;
+        lnf[threadIdx.x / kWave] = nf;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        uint32_t c = 0;
+        for (int i = 0; i < kWaves; ++i) {
+            t += lsum[i];
+            c += lnf[i];
+        }
+        part[blockIdx.x] = t;
+        if (c) atomicAdd(&st->nonfinite, c);
     }
 }
 
-// Sum of the wave partials and the certified float32 rounding of the exact sum.
-// Every partial and sum is a sum of non-negative float64 values; along any
-// path of the summation tree there are at most 32 + 2 (lane) + 6 (wave)
-// + 256 (thread's share of <= 2^18 partials) + 6 + 16 (block) = 318 additions,
-// so the computed total t is within a relative 330 * 2^-53 < 2^-44 of the exact
+// Sum of the block partials and the certified float32 rounding of the exact
+// sum.  Every partial and sum is a sum of non-negative float64 values; along
+// any path of the summation tree there are at most 32 + 2 (lane) + 6 (wave)
+// + 16 (block of <= 16 waves) + 256 (thread's share of <= 2^18 partials) + 2
+// + 6 + 16 (final block) = 336 additions,
+// so the computed total t is within a relative 340 * 2^-53 < 2^-44 of the exact
 // sum S (Higham, Accuracy and Stability of Numerical Algorithms, section 4.2).
 // lo = t(1 - 2^-40) and hi = t(1 + 2^-40), each rounded once, then bracket S,
 // and rounding to float64 then float32 is monotone: when lo and hi give the
 // same float32 so does S.  Otherwise the exact pass decides.
-__global__ __launch_bounds__(kTotalBlock) void k_rs_total(const double* __restrict__ part, int64_t nw,
+__global__ __launch_bounds__(kTotalBlock) void k_rs_total(const double* __restrict__ part, int64_t np,
                                                           uint32_t force_exact, State* __restrict__ st,
                                                           float* __restrict__ sum_out,
                                                           uint32_t* __restrict__ nonfinite) {
     __shared__ double lsum[kTotalBlock / kWave];
-    double a = 0.0;
-    for (int64_t w = threadIdx.x; w < nw; w += kTotalBlock) a += part[w];
+    // four independent chains per thread keep four loads in flight
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    int64_t w = threadIdx.x;
+    for (; w + 3 * kTotalBlock < np; w += 4 * kTotalBlock) {
+        a0 += part[w];
+        a1 += part[w + kTotalBlock];
+        a2 += part[w + 2 * kTotalBlock];
+        a3 += part[w + 3 * kTotalBlock];
+    }
+    for (; w < np; w += kTotalBlock) a0 += part[w];
+    double a = (a0 + a1) + (a2 + a3);
     a = wave_sum(a);
     if (lane() == 0) lsum[threadIdx.x / kWave] = a;
     __syncthreads();
@@ -340,13 +377,41 @@ __device__ __forceinline__ void philox(uint32_t& c0, uint32_t& c1, uint32_t& c2,
     }
 }
 
-__device__ __forceinline__ uint32_t keep_bit(float x, uint32_t word, float kf, float S) {
-    if (!finite(x)) return 0u;
-    const float t = kf * fabsf(x);
-    float p = t / S;
-    if (p > 1.0f) p = 1.0f;
-    const float u = static_cast<float>(word >> 8) * 0x1p-24f;
-    return u < p ? 1u : 0u;
+// The decision u < min(1, fl(t / S)) with t = fl(k |x|), for the four
+// elements of one float4.  When rS = fl(1/S) is a normal float (fast),
+// pa = fl(t * rS) is within a relative 2^-22 of the correctly rounded quotient
+// whenever u is a positive draw (u >= 2^-24, so only quotients in the normal
+// range matter): u < pa (1 - 2^-20) proves u < quotient and u >= pa (1 + 2^-20)
+// proves the opposite, each product rounded once.  Draws within that margin,
+// u = 0 and every element of a non-fast call take the correctly rounded
+// division (rare: the branch is skipped when no lane of the wave needs it).
+// The clip at 1 never changes the outcome (u < 1).
+__device__ __forceinline__ uint32_t keep_nibble(const float (&x)[4], const uint32_t (&word)[4], float kf, float S,
+                                                float rS, bool fast) {
+    uint32_t nib = 0, unsure = 0;
+    float t[4], u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        t[i] = kf * fabsf(x[i]);
+        u[i] = static_cast<float>(word[i] >> 8) * 0x1p-24f;
+        const float pa = t[i] * rS;
+        const bool ok = finite(x[i]);
+        const bool yes = fast && u[i] > 0.0f && u[i] < pa * (1.0f - 0x1p-20f);
+        const bool no = fast && u[i] > 0.0f && u[i] >= pa * (1.0f + 0x1p-20f);
+        nib |= (ok && yes ? 1u : 0u) << i;
+        unsure |= (ok && !yes && !no ? 1u : 0u) << i;
+    }
+    if (unsure) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if ((unsure >> i) & 1u) {
+                float p = t[i] / S;
+                if (p > 1.0f) p = 1.0f;
+                nib |= (u[i] < p ? 1u : 0u) << i;
+            }
+        }
+    }
+    return nib;
 }
 
 // Decisions for the region of wave w.  Lane l of unroll step u holds float4 j
@@ -364,6 +429,9 @@ __global__ __launch_bounds__(kBlock) void k_rs_mark(const float* __restrict__ x,
     const int64_t nv = (len + 3) >> 2;
     const int l = lane();
     const float S = st->s32;
+    const float rS = 1.0f / S;
+    // 1/S normal: S in [2^-126, 2^126]
+    const bool fast = S >= 0x1p-126f && S <= 0x1p126f;
     const f4* x4 = reinterpret_cast<const f4*>(x + beg);
     uint32_t* bw = bm + (beg >> 5);
     const uint32_t q0 = static_cast<uint32_t>(beg >> 2);
@@ -391,8 +459,9 @@ __global__ __launch_bounds__(kBlock) void k_rs_mark(const float* __restrict__ x,
             const int64_t j = base + u * kWave + l;
             uint32_t c0 = q0 + static_cast<uint32_t>(j), c1 = 0u, c2 = step0, c3 = step1;
             philox(c0, c1, c2, c3, key0, key1);
-            uint32_t nib = keep_bit(xv[u].x, c0, kf, S) | keep_bit(xv[u].y, c1, kf, S) << 1 |
-                           keep_bit(xv[u].z, c2, kf, S) << 2 | keep_bit(xv[u].w, c3, kf, S) << 3;
+            const float xs[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+            const uint32_t ws[4] = {c0, c1, c2, c3};
+            uint32_t nib = keep_nibble(xs, ws, kf, S, rS, fast);
             if (GUARD && j >= nv) nib = 0;  // zero-filled components of a partial float4 have p = 0 anyway
             count += __popc(nib);
             uint32_t word = nib << (4 * (l & 7));
@@ -412,17 +481,18 @@ __global__ __launch_bounds__(kBlock) void k_rs_mark(const float* __restrict__ x,
 }
 
 // Region w: its bitmap words (4 per lane) in order, each set bit -> output
-// slot off[w] + rank; slots below cap get (x, i) and e[i] = +0.
+// slot (region start) + rank; slots below cap get (x, i) and e[i] = +0.
 __global__ __launch_bounds__(kBlock) void k_rs_write(float* __restrict__ e, int64_t n, int64_t nw,
                                                      const uint32_t* __restrict__ bm,
                                                      const uint32_t* __restrict__ off,
+                                                     const uint32_t* __restrict__ tsum,
                                                      const State* __restrict__ st, float* __restrict__ vals,
                                                      int32_t* __restrict__ idx, int64_t cap) {
     const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + threadIdx.x / kWave;
     const int64_t beg = w * kRegion;
     if (beg >= n) return;
-    const uint32_t o = off[w];
-    const uint32_t o_next = w + 1 < nw ? off[w + 1] : st->kept;
+    const uint32_t o = off[w] + tsum[w / kScanTile];
+    const uint32_t o_next = w + 1 < nw ? off[w + 1] + tsum[(w + 1) / kScanTile] : st->kept;
     if (o_next == o || static_cast<int64_t>(o) >= cap) return;
     const int64_t len = min(static_cast<int64_t>(kRegion), n - beg);
     const int64_t nwords = (len + 31) >> 5;
@@ -454,6 +524,27 @@ __global__ __launch_bounds__(kBlock) void k_rs_write(float* __restrict__ e, int6
     }
 }
 
+// First level of the region-count scan: block t scans counts
+// [t*kScanTile, (t+1)*kScanTile) in place (exclusive) and writes its total to
+// tsum[t]; k_excl_scan then scans tsum, and region w starts at
+// cnt[w] + tsum[w / kScanTile].
+__global__ __launch_bounds__(kScanThreads) void k_rs_scan_tiles(uint32_t* __restrict__ cnt, int64_t nw,
+                                                                uint32_t* __restrict__ tsum) {
+    __shared__ uint32_t lds[kScanThreads / kWave + 1];
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kScanTile + 4 * threadIdx.x;
+    uint32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = t0 + q < nw ? cnt[t0 + q] : 0u;
+    uint32_t total;
+    uint32_t run = block_excl_scan<kScanThreads>(v[0] + v[1] + v[2] + v[3], lds, &total);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (t0 + q < nw) cnt[t0 + q] = run;
+        run += v[q];
+    }
+    if (threadIdx.x == 0) tsum[blockIdx.x] = total;
+}
+
 __global__ void k_rs_empty(int64_t* count_out, float* sum_out, uint32_t* nonfinite) {
     *count_out = 0;
     if (sum_out) *sum_out = 0.0f;
@@ -461,20 +552,24 @@ __global__ void k_rs_empty(int64_t* count_out, float* sum_out, uint32_t* nonfini
 }
 
 struct Layout {
-    int64_t nw;
-    size_t state, part, cnt, xpart, bm, total;
+    int64_t nw, nb, ntiles;  // mark/write regions, accumulation blocks, scan tiles
+    size_t state, part, cnt, tsum, xpart, bm, total;
 };
 
 inline Layout layout_for(int64_t n) {
     Layout L{};
     L.nw = std::max<int64_t>(1, cdiv(n, kRegion));
+    L.nb = std::max<int64_t>(1, cdiv(n, static_cast<int64_t>(kAccRegion) * kWaves));
+    L.ntiles = cdiv(L.nw, kScanTile);
     size_t o = 0;
     L.state = o;
     o += 256;
     L.part = o;
-    o = round_up(o + static_cast<size_t>(L.nw) * sizeof(double), 256);
+    o = round_up(o + static_cast<size_t>(L.nb) * sizeof(double), 256);
     L.cnt = o;
     o = round_up(o + static_cast<size_t>(L.nw) * sizeof(uint32_t), 256);
+    L.tsum = o;
+    o = round_up(o + static_cast<size_t>(L.ntiles) * sizeof(uint32_t), 256);
     L.xpart = o;
     o = round_up(o + static_cast<size_t>(kExactWaves) * 16 * sizeof(uint64_t), 256);
     L.bm = o;
@@ -514,16 +609,18 @@ extern "C" int ef_random_sparsify(const float* g, float* e, int64_t n, int64_t k
     rs::State* st = reinterpret_cast<rs::State*>(base + L.state);
     double* part = reinterpret_cast<double*>(base + L.part);
     uint32_t* cnt = reinterpret_cast<uint32_t*>(base + L.cnt);
+    uint32_t* tsum = reinterpret_cast<uint32_t*>(base + L.tsum);
     uint64_t* xpart = reinterpret_cast<uint64_t*>(base + L.xpart);
     uint32_t* bm = reinterpret_cast<uint32_t*>(base + L.bm);
     const unsigned grid = static_cast<unsigned>(cdiv(L.nw, rs::kWaves));
+    const unsigned agrid = static_cast<unsigned>(L.nb);
     const unsigned xgrid =
         static_cast<unsigned>(cdiv(std::min<int64_t>(rs::kExactWaves, L.nw), rs::kExactBlock / kWave));
     const int64_t nwx = static_cast<int64_t>(xgrid) * (rs::kExactBlock / kWave);
     EF_TRY(launch("rs_init", rs::k_rs_init, dim3(1), dim3(1), s, st));
-    EF_TRY(launch("rs_accum", rs::k_rs_accum, dim3(grid), dim3(rs::kBlock), s, g, e, n, part, st));
+    EF_TRY(launch("rs_accum", rs::k_rs_accum, dim3(agrid), dim3(rs::kBlock), s, g, e, n, part, st));
     EF_TRY(launch("rs_total", rs::k_rs_total, dim3(1), dim3(rs::kTotalBlock), s, static_cast<const double*>(part),
-                  L.nw, static_cast<uint32_t>(flags & EF_FLAG_FORCE_FALLBACK), st, sum_out, nonfinite));
+                  L.nb, static_cast<uint32_t>(flags & EF_FLAG_FORCE_FALLBACK), st, sum_out, nonfinite));
     EF_TRY(launch("rs_exact", rs::k_rs_exact, dim3(xgrid), dim3(rs::kExactBlock), s, static_cast<const float*>(e), n,
                   L.nw, static_cast<const rs::State*>(st), xpart));
     EF_TRY(launch("rs_exact_total", rs::k_rs_exact_total, dim3(1), dim3(rs::kExactBlock), s,
@@ -532,8 +629,11 @@ extern "C" int ef_random_sparsify(const float* g, float* e, int64_t n, int64_t k
                   static_cast<float>(k), static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32),
                   static_cast<uint32_t>(step), static_cast<uint32_t>(step >> 32), static_cast<const rs::State*>(st),
                   bm, cnt));
-    EF_TRY(launch("rs_scan", k_excl_scan<uint32_t>, dim3(1), dim3(kScanThreads), s, cnt, L.nw, &st->kept, count_out));
+    EF_TRY(launch("rs_scan_tiles", rs::k_rs_scan_tiles, dim3(static_cast<unsigned>(L.ntiles)), dim3(kScanThreads), s,
+                  cnt, L.nw, tsum));
+    EF_TRY(launch("rs_scan", k_excl_scan<uint32_t>, dim3(1), dim3(kScanThreads), s, tsum, L.ntiles, &st->kept,
+                  count_out));
     return launch("rs_write", rs::k_rs_write, dim3(grid), dim3(rs::kBlock), s, e, n, L.nw,
                   static_cast<const uint32_t*>(bm), static_cast<const uint32_t*>(cnt),
-                  static_cast<const rs::State*>(st), vals, idx, cap);
+                  static_cast<const uint32_t*>(tsum), static_cast<const rs::State*>(st), vals, idx, cap);
 }

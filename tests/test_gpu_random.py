@@ -211,3 +211,34 @@ def test_large_workload_full_size(flags):
         assert abs(c - mu) < 6 * sd and mu <= k * (1 + 1e-6), (c, mu, sd)
         say(f"random full size flags={flags} step={step}: ok (kept {c}, S={S})")
         del g, x, p, xh
+
+
+def boundary_case(k, delta_ulps, seed=31, step=4, n=4096):
+    """Probabilities that sit on top of their draws: x_j = u_j for j >= 1 and
+    x_0 chosen so that S32 = k (+- a few ulps); every p_j is then u_j up to
+    the last bits, so each decision is settled by rounding alone."""
+    u = np.array([oracle.uniform(seed, step, j) for j in range(n)], np.float32)
+    g = u.copy()
+    rest = float(np.sum(u[1:].astype(np.float64)))
+    ulp = float(np.spacing(np.float32(k)))
+    g[0] = np.float32(k + delta_ulps * ulp - rest)
+    return g, np.zeros(n, np.float32), seed, step
+
+
+@pytest.mark.parametrize("k,d", [(8192, -3), (8192, -1), (8192, 0), (8192, 1), (8191, -1), (8191, 0), (8191, 1),
+                                 (6000, 0), (6001, 2)])
+def test_probabilities_on_their_draws(k, d):
+    g, e, seed, step = boundary_case(k, d)
+    for flags in (0, efg.EF_FLAG_FORCE_FALLBACK):
+        check(g, e, k, seed, step, flags=flags, what=f"boundary k={k} d={d} flags={flags}")
+
+
+def test_sum_above_reciprocal_range():
+    """S between 2^126 and the float32 maximum: 1/S is subnormal, every
+    decision takes the division."""
+    n = 1000
+    g = np.full(n, np.float32(2.0 ** 117), np.float32) * gen.normal_small(n, 710).astype(np.float32)
+    e = np.zeros(n, np.float32)
+    S = oracle.sum_abs_exact(g)
+    assert 2.0 ** 126 < S < float(np.finfo(np.float32).max)
+    check(g, e, 100, 5, 5, what="S > 2^126")
