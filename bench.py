@@ -33,12 +33,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic():
-    """HBM bytes per launch of the streaming kernel from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE passes, or None if the kernel sources changed since."""
+# committed rocprofv3 traffic summaries of the roofline kernel of other workloads
+TRAFFIC_PROFILES = {"random": "rs_accum_large_1p3e9_traffic"}
+
+
+def measured_traffic(name="topk_stream_large_1p3e9_traffic"):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (profiles/<name>.json), or None if the kernel sources
+    changed since."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "topk_stream_large_1p3e9_traffic.json")
+    path = os.path.join(ROOT, "profiles", name + ".json")
     try:
         rec = json.load(open(path))
         src = b"".join(open(os.path.join(ROOT, p), "rb").read() for p in rec["sources"])
@@ -97,7 +102,7 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=40_000_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stats", action="store_true", help="also compute the fused monitoring statistics")
-    ap.add_argument("--workload", default="large", choices=["large", "flat", "bert", "sign", "decode", "quant"],
+    ap.add_argument("--workload", default="large", choices=["large", "flat", "bert", "sign", "decode", "quant", "random"],
                     help="large (default, the headline) or one of the other workloads")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -174,19 +179,7 @@ def main():
             breakdown[lab] = round(ms, 4)
     efg.profile_enable(False)
 
-    # plain device copy of 2 GiB as the practical bandwidth ceiling (read + write)
-    a = torch.empty(1 << 29, dtype=torch.float32, device=dev)
-    b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        b.copy_(a)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * a.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del a, b
+    copy_gbps = copy_ceiling(dev)
 
     result = {
         "metric": METRIC,
@@ -234,6 +227,28 @@ def main():
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def copy_ceiling(dev):
+    """Plain device copy of 2 GiB, ten times (read + write GB/s): the practical
+    bandwidth ceiling, and the known-size kernel that calibrates rocprofv3's
+    FETCH_SIZE / WRITE_SIZE counters in the same process."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    a = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        b.copy_(a)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    gbps = 2 * a.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del a, b
+    return gbps
 
 
 def time_steps(step, W, K, kernel_label):
@@ -344,6 +359,28 @@ def other_workload(args):
             t0 = time.perf_counter()
             oracle.quantize_int8(v_h, np.arange(k, dtype=np.int32), np.zeros(k, np.float32))
             cpu = (k, time.perf_counter() - t0, f"one full packet, k = {k:,}")
+    elif wl == "random":
+        n, k, seed = gen.LARGE_N, gen.LARGE_K, gen.RANDOM_SEED
+        grads = [gen.large_gradient_device(t, n, dev) for t in range(W + K)]
+        e = torch.zeros(n, device=dev)
+        cap = 2 * k + 64
+        vals = torch.empty(cap, device=dev)
+        idx = torch.empty(cap, dtype=torch.int32, device=dev)
+        cnt = torch.empty(1, dtype=torch.int64, device=dev)
+        wsr = efg.workspace(efg.lib().ef_random_sparsify_workspace_bytes(n), dev)
+        step = lambda t: efg.ef_random_sparsify(grads[t], e, k, seed, t, cap=cap, vals=vals, idx=idx, count=cnt,
+                                                ws=wsr)
+        # rs_accum reads g and e and writes e back (x = g + e)
+        label, bpe, units, unit = "rs_accum", 12, n, "elems/s"
+        metric = "EF random sparsification elems/s, N=1.3e9 fp32, expected k=1.3e6"
+        desc = ("random magnitude-proportional sparsification of the large workload's gradient law, N=1.3e9, "
+                "expected k=1.3e6, Philox draws, index-ordered output, residual carried")
+        if not args.no_cpu_baseline:
+            ns = 10_000_000
+            g0 = gen.large_gradient(0, n=ns)
+            t0 = time.perf_counter()
+            oracle.random_sparsify(g0, np.zeros(ns, np.float32), ns // 1000, seed, 0)
+            cpu = (ns, time.perf_counter() - t0, f"first {ns:,} elements of the step-0 gradient, k = {ns // 1000:,}")
     else:
         n, P, kp = gen.DECODE_N, gen.DECODE_PACKETS, gen.DECODE_K
         idx_l, val_l = [], []
@@ -379,13 +416,25 @@ def other_workload(args):
         _, dms, dl = time_steps(step, 1, K, "decode_scatter")
         extra["decode_scatter_ms"] = dms
         extra["decode_entries_per_s"] = P * kp / (dms * 1e-3)
+    if wl == "random":
+        # every kernel of the path, one at a time; whole-path algorithmic bytes:
+        # accum 12 B, mark 4 B + 1 bit, write 1 bit + 16 B per kept element
+        for kl in ("rs_mark", "rs_write", "rs_total", "rs_exact", "rs_scan", "rs_"):
+            _, kms_l, nl = time_steps(step, 1, K, kl)
+            extra[f"{kl}_ms"] = kms_l
+        path_bytes = n * (12 + 4 + 0.25) + 16 * k
+        extra["path_GBps"] = path_bytes / (extra["rs__ms"] * 1e-3) / 1e9
+        extra["mark_elems_per_s"] = n / (extra["rs_mark_ms"] * 1e-3)
+        extra["copy_ceiling_GBps"] = copy_ceiling(dev)
     achieved = bpe * units / (kms * 1e-3) / 1e9
     res = {
         "metric": metric, "value": units / (ms * 1e-3), "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic", "config": {"workload": desc, "n": units},
         "roofline": {"kernel": label, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "kernel_ms_per_step": kms,
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": measured_traffic(TRAFFIC_PROFILES[wl]) if wl in TRAFFIC_PROFILES else None,
+                     "kernel_ms_per_step": kms,
                      "launches": launches, "bytes_per_elem": bpe},
     }
     res.update(extra)
