@@ -52,6 +52,8 @@ def lib():
             "orc_blocks_decode": [p, p, p, i64, p, i64, p],
             "orc_quantize_int8": [p, p, i64, p, p, p],
             "orc_random_keep_at": [p, p, i64, i64, f, C.c_uint64, C.c_uint64, p],
+            "orc_adam_step": [p, p, p, p, i64, f, f, f, f, f, u32p],
+            "orc_onebit_adam_update": [p, i32, p, p, p, i64, f, f, f, f, u32p],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -113,16 +115,17 @@ def topk_segmented(g, e, seg_off, seg_k):
 
 
 def sign(g, e, m, beta1=0.9, clip=5.0):
-    """Returns (e_new, m_new, sign int8, bits uint8, nonfinite)."""
+    """Returns (e_new, m_new, sign int8, bits uint8, nonfinite); m may be None
+    (compress only: m_new is then None)."""
     g = _f32(g)
     e2 = _f32(e).copy()
-    m2 = _f32(m).copy()
+    m2 = None if m is None else _f32(m).copy()
     n = g.size
     s = np.empty(n, np.int8)
     bits = np.empty((n + 7) // 8, np.uint8)
     bad = np.zeros(1, np.uint32)
-    _check(lib().orc_sign(_ptr(g), _ptr(e2), _ptr(m2), n, beta1, clip, _ptr(s), _ptr(bits),
-                          _ptr(bad)), "sign")
+    _check(lib().orc_sign(_ptr(g), _ptr(e2), None if m2 is None else _ptr(m2), n, beta1, clip, _ptr(s),
+                          _ptr(bits), _ptr(bad)), "sign")
     return e2, m2, s, bits, int(bad[0])
 
 
@@ -268,3 +271,33 @@ def random_keep_at(x_at, pos, k, s32, seed, step):
     _check(lib().orc_random_keep_at(_ptr(x_at), _ptr(pos), pos.size, k, s32, seed, step, _ptr(keep)),
            "random_keep_at")
     return keep[:pos.size].astype(bool)
+
+
+def adam_scalars(lr, beta1, beta2, t, t_v=None):
+    """(step_size, sqrt_bc2) of step t (1-based): lr / (1 - beta1^t) and
+    sqrt(1 - beta2^t_v), t_v = t unless v is frozen, evaluated in float64 with
+    the float32 betas the EMAs use, then rounded to float32."""
+    t_v = t if t_v is None else t_v
+    b1, b2 = float(np.float32(beta1)), float(np.float32(beta2))
+    return float(np.float32(lr / (1.0 - b1 ** t))), float(np.float32(np.sqrt(1.0 - b2 ** t_v)))
+
+
+def adam_step(g, m, v, w, beta1, beta2, step_size, sqrt_bc2, eps):
+    """Returns (m_new, v_new, w_new, nonfinite)."""
+    g = _f32(g)
+    m2, v2, w2 = _f32(m).copy(), _f32(v).copy(), _f32(w).copy()
+    bad = np.zeros(1, np.uint32)
+    _check(lib().orc_adam_step(_ptr(g), _ptr(m2), _ptr(v2), _ptr(w2), g.size, beta1, beta2, step_size, sqrt_bc2,
+                               eps, _ptr(bad)), "adam_step")
+    return m2, v2, w2, int(bad[0])
+
+
+def onebit_adam_update(qsum, nworkers, m, v, w, beta1, step_size, sqrt_bc2, eps):
+    """Returns (m_new, w_new, nonfinite); v is read only."""
+    q = np.ascontiguousarray(qsum, dtype=np.int8)
+    m2, w2 = _f32(m).copy(), _f32(w).copy()
+    v = _f32(v)
+    bad = np.zeros(1, np.uint32)
+    _check(lib().orc_onebit_adam_update(_ptr(q), nworkers, _ptr(m2), _ptr(v), _ptr(w2), q.size, beta1, step_size,
+                                        sqrt_bc2, eps, _ptr(bad)), "onebit_adam_update")
+    return m2, w2, int(bad[0])

@@ -149,7 +149,8 @@ int orc_topk_segmented(const float* g, float* e, int32_t nseg,
  * own (no fused multiply-add); (1 - beta1) is itself a float32 value; the
  * packed bit is 1 exactly when q = +1, least significant bit first, pad bits
  * zero; non-finite e' and m' are counted, not trapped.
- * sign_out and bits may be NULL.
+ * sign_out and bits may be NULL.  m may be NULL: the momentum is then left to
+ * the step that follows the exchange of the signs (orc_onebit_adam_update).
  */
 int orc_sign(const float* g, float* e, float* m, int64_t n, float beta1, float clip,
              int8_t* sign_out, uint8_t* bits, uint32_t* nonfinite) {
@@ -168,12 +169,15 @@ int orc_sign(const float* g, float* e, float* m, int64_t n, float beta1, float c
         float ea = beta1 * e[i];
         float eb = c * delta;
         float en = ea + eb;
-        float ma = beta1 * m[i];
-        float mb = c * q;
-        float mn = ma + mb;
         e[i] = en;
-        m[i] = mn;
-        bad += (uint32_t)is_nonfinite(en) + (uint32_t)is_nonfinite(mn);
+        bad += (uint32_t)is_nonfinite(en);
+        if (m) {
+            float ma = beta1 * m[i];
+            float mb = c * q;
+            float mn = ma + mb;
+            m[i] = mn;
+            bad += (uint32_t)is_nonfinite(mn);
+        }
         if (sign_out) sign_out[i] = (int8_t)s;
         if (bits && s == 1) bits[i >> 3] |= (uint8_t)(1u << (i & 7));
     }
@@ -567,5 +571,91 @@ int orc_random_keep_at(const float* x, const int64_t* pos, int64_t m, int64_t k,
         if (pos[j] < 0 || pos[j] > 0x7fffffffLL) return ORC_EINVAL;
         keep[j] = (uint8_t)(orc_uniform(seed, step, pos[j]) < orc_keep_probability(x[j], k, S32));
     }
+    return ORC_OK;
+}
+
+/*
+ * The parameter update shared by both Adam phases, per element:
+ *   d = sqrt(v) / sqrt_bc2 + eps
+ *   w' = w - step_size * (m / d)
+ * READING: textbook Adam (Kingma and Ba, ICLR 2015, Algorithm 1: theta -=
+ * alpha * mhat / (sqrt(vhat) + eps), mhat = m / (1 - beta1^t), vhat = v / (1 -
+ * beta2^t)) with the two bias corrections folded into host scalars:
+ * step_size = lr / (1 - beta1^t) and sqrt_bc2 = sqrt(1 - beta2^t_v), where t_v
+ * is the step at which v was last updated.  Square root and divisions
+ * correctly rounded float32, every operation rounded on its own.
+ */
+static float adam_param(float w, float m, float v, float step_size, float sqrt_bc2, float eps) {
+    float r = sqrtf(v);
+    float q = r / sqrt_bc2;
+    float d = q + eps;
+    float u = m / d;
+    float s = step_size * u;
+    return w - s;
+}
+
+/*
+ * One full-precision Adam step (the warm-up phase).  [ONEBIT] "6.1 收敛不稳定问题"
+ * trains its first steps at full precision before switching to 1-bit
+ * compression; "3.1 关键数据结构设计" keeps momentum, variance, beta1, beta2,
+ * eps and the step count.  READING: textbook Adam on the (averaged) gradient g:
+ *   m' = beta1 * m + (1 - beta1) * g
+ *   v' = beta2 * v + (1 - beta2) * (g * g)
+ *   w' = adam_param(w, m', v', ...)
+ * (1 - beta1) and (1 - beta2) are float32 values; no fused multiply-add.
+ * Non-finite m', v', w' are counted.
+ */
+int orc_adam_step(const float* g, float* m, float* v, float* w, int64_t n, float beta1, float beta2,
+                  float step_size, float sqrt_bc2, float eps, uint32_t* nonfinite) {
+    if (n < 0) return ORC_EINVAL;
+    const float c1 = 1.0f - beta1, c2 = 1.0f - beta2;
+    uint32_t bad = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        float ma = beta1 * m[i];
+        float mb = c1 * g[i];
+        float mn = ma + mb;
+        float g2 = g[i] * g[i];
+        float va = beta2 * v[i];
+        float vb = c2 * g2;
+        float vn = va + vb;
+        float wn = adam_param(w[i], mn, vn, step_size, sqrt_bc2, eps);
+        m[i] = mn;
+        v[i] = vn;
+        w[i] = wn;
+        bad += (uint32_t)is_nonfinite(mn) + (uint32_t)is_nonfinite(vn) + (uint32_t)is_nonfinite(wn);
+    }
+    if (nonfinite) *nonfinite = bad;
+    return ORC_OK;
+}
+
+/*
+ * One compression-phase step of 1-bit Adam after the signs were exchanged.
+ * qsum[i] is the sum over the nworkers workers of their int8 signs q
+ * (orc_sign with m = NULL), so the averaged compressed gradient is
+ *   ghat = qsum / nworkers                      (float32 division)
+ * [ONEBIT] "2.2 动量修正策略": m' = beta1 * m + (1 - beta1) * ghat.
+ * READING: the variance is frozen during compression (only the signs are
+ * exchanged, so no worker holds the averaged full-precision gradient that a
+ * shared v would need); v is read, never written.  w' = adam_param(w, m', v).
+ * With one worker ghat = q and m' is exactly orc_sign's momentum.
+ * 1 <= nworkers <= 127 (the sum fits int8).
+ */
+int orc_onebit_adam_update(const int8_t* qsum, int32_t nworkers, float* m, const float* v, float* w, int64_t n,
+                           float beta1, float step_size, float sqrt_bc2, float eps, uint32_t* nonfinite) {
+    if (n < 0 || nworkers < 1 || nworkers > 127) return ORC_EINVAL;
+    const float c1 = 1.0f - beta1;
+    const float nw = (float)nworkers;
+    uint32_t bad = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        float ghat = (float)qsum[i] / nw;
+        float ma = beta1 * m[i];
+        float mb = c1 * ghat;
+        float mn = ma + mb;
+        float wn = adam_param(w[i], mn, v[i], step_size, sqrt_bc2, eps);
+        m[i] = mn;
+        w[i] = wn;
+        bad += (uint32_t)is_nonfinite(mn) + (uint32_t)is_nonfinite(wn);
+    }
+    if (nonfinite) *nonfinite = bad;
     return ORC_OK;
 }
