@@ -33,6 +33,8 @@ SIGNATURES = {
     "ef_topk_compress_segmented": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _sz, _p, _p, _u32, _p]),
     "ef_sign_workspace_bytes": (_sz, [_i64]),
     "ef_sign_compress": (C.c_int, [_p, _p, _p, _i64, _f, _f, _p, _p, _p, _p, _p, _sz, _p]),
+    "ef_adam_step": (C.c_int, [_p, _p, _p, _p, _i64, _f, _f, _f, _f, _f, _p, _p]),
+    "ef_onebit_adam_update": (C.c_int, [_p, _i32, _p, _p, _p, _i64, _f, _f, _f, _f, _p, _p]),
     "ef_quantize_workspace_bytes": (_sz, [_i64]),
     "ef_quantize_int8": (C.c_int, [_p, _p, _i64, _p, _i64, _p, _p, _p, _sz, _p]),
     "ef_random_sparsify_workspace_bytes": (_sz, [_i64]),
@@ -192,12 +194,14 @@ def ef_topk_compress_segmented(g, e, seg_off, seg_k, vals=None, idx=None, ws=Non
 def ef_sign_compress(g, e, m, beta1=0.9, clip=5.0, sign_out=None, bits=None, nonfinite=None,
                      want_sign=True, want_bits=True, stats=None, ws=None):
     """1-bit sign EF with momentum; e and m updated in place.  Returns (sign int8, bits uint8).
-    stats (float64 GPU tensor of 4) receives {sum e'^2, sum m'^2, #(+1), #(-1)}."""
+    m may be None (compress only).  stats (float64 GPU tensor of 4) receives
+    {sum e'^2, sum m'^2, #(+1), #(-1)}."""
     dev = _gpu(g, "g")
     n = g.numel()
     _need(g, torch.float32, dev, "g")
     _need(e, torch.float32, dev, "e", n)
-    _need(m, torch.float32, dev, "m", n)
+    if m is not None:
+        _need(m, torch.float32, dev, "m", n)
     if sign_out is None and want_sign:
         sign_out = torch.empty(n, dtype=torch.int8, device=dev)
     if bits is None and want_bits:
@@ -216,6 +220,44 @@ def ef_sign_compress(g, e, m, beta1=0.9, clip=5.0, sign_out=None, bits=None, non
                                   _ptr(nonfinite), _ptr(stats), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(dev)), "ef_sign_compress")
     return sign_out, bits
+
+
+# ---------------------------------------------------------------- Adam around 1-bit compression
+def adam_scalars(lr, beta1, beta2, t, t_v=None):
+    """(step_size, sqrt_bc2) of step t (1-based): lr / (1 - beta1^t) and
+    sqrt(1 - beta2^t_v) (t_v = t unless the variance is frozen), in float64
+    from the float32 betas the kernels use, rounded to float32."""
+    import struct
+
+    f32 = lambda x: struct.unpack("f", struct.pack("f", x))[0]
+    t_v = t if t_v is None else t_v
+    b1, b2 = f32(beta1), f32(beta2)
+    return f32(lr / (1.0 - b1 ** t)), f32((1.0 - b2 ** t_v) ** 0.5)
+
+
+def ef_adam_step(g, m, v, w, beta1, beta2, step_size, sqrt_bc2, eps, nonfinite=None):
+    """One full-precision Adam step in place on m, v, w."""
+    dev = _gpu(g, "g")
+    n = g.numel()
+    for t, name in ((g, "g"), (m, "m"), (v, "v"), (w, "w")):
+        _need(t, torch.float32, dev, name, n)
+    if nonfinite is not None:
+        _need(nonfinite, torch.int32, dev, "nonfinite", 1)
+    _check(lib().ef_adam_step(_ptr(g), _ptr(m), _ptr(v), _ptr(w), n, beta1, beta2, step_size, sqrt_bc2, eps,
+                              _ptr(nonfinite), _stream(dev)), "ef_adam_step")
+
+
+def ef_onebit_adam_update(qsum, nworkers, m, v, w, beta1, step_size, sqrt_bc2, eps, nonfinite=None):
+    """One 1-bit Adam compression-phase update in place on m, w (v read only)."""
+    dev = _gpu(m, "m")
+    n = m.numel()
+    _need(qsum, torch.int8, dev, "qsum", n)
+    for t, name in ((m, "m"), (v, "v"), (w, "w")):
+        _need(t, torch.float32, dev, name, n)
+    if nonfinite is not None:
+        _need(nonfinite, torch.int32, dev, "nonfinite", 1)
+    _check(lib().ef_onebit_adam_update(_ptr(qsum), nworkers, _ptr(m), _ptr(v), _ptr(w), n, beta1, step_size,
+                                       sqrt_bc2, eps, _ptr(nonfinite), _stream(dev)), "ef_onebit_adam_update")
 
 
 # ---------------------------------------------------------------- 8-bit packet values

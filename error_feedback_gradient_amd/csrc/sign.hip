@@ -9,7 +9,8 @@
 // float4 of g, e and m per unroll step (128-bit non-temporal loads and
 // stores), writes its four int8 signs as one 32-bit store, and pairs with its
 // neighbour lane to form one byte of packed bits.  21.125 bytes move per
-// element with both optional outputs (read g, e, m; write e, m, int8, 1 bit).
+// element with both optional outputs (read g, e, m; write e, m, int8, 1 bit);
+// 13.125 when m is NULL (compress only, the momentum follows the exchange).
 // Every product and sum is rounded on its own: the library is compiled with
 // -ffp-contract=off.
 #include <algorithm>
@@ -73,8 +74,9 @@ __global__ void k_zero_u32(uint32_t* p) { *p = 0; }
 // 4j..4j+3; lanes 2i and 2i+1 together hold one whole output byte of bits.
 // The last n - n8 elements are done by the first lane of wave 0.
 // With STATS, wave w also writes part[w] = {sum e'^2, sum m'^2, #(+1), #(-1)}
-// (float64, finite values only) for k_sign_stats.
-template <bool STATS>
+// (float64, finite values only) for k_sign_stats.  Without MOM, m is neither
+// read nor written (compress only; its terms count as zero).
+template <bool STATS, bool MOM>
 __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, float* __restrict__ e,
                                                  float* __restrict__ m, int64_t n, float beta1, float c,
                                                  float clip, int8_t* __restrict__ sgn, uint8_t* __restrict__ bits,
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, fl
     auto account = [&](const Out& o) {
         if (STATS) {
             if ((__float_as_uint(o.e) & 0x7f800000u) != 0x7f800000u) se += static_cast<double>(o.e) * o.e;
-            if ((__float_as_uint(o.m) & 0x7f800000u) != 0x7f800000u) sm += static_cast<double>(o.m) * o.m;
+            if (MOM && (__float_as_uint(o.m) & 0x7f800000u) != 0x7f800000u) sm += static_cast<double>(o.m) * o.m;
             cp += o.s == 1;
             cn += o.s == -1;
         }
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, fl
     const int64_t nv = beg < end ? (end - beg) >> 2 : 0;  // even
     const f4* g4 = reinterpret_cast<const f4*>(g + beg);
     f4* e4 = reinterpret_cast<f4*>(e + beg);
-    f4* m4 = reinterpret_cast<f4*>(m + beg);
+    f4* m4 = MOM ? reinterpret_cast<f4*>(m + beg) : nullptr;
     uint32_t* s4 = sgn ? reinterpret_cast<uint32_t*>(sgn + beg) : nullptr;
     uint8_t* b8 = bits ? bits + (beg >> 3) : nullptr;
     auto iteration = [&](int64_t base, auto guard) {
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, fl
             if (!GUARD || j < nv) {
                 gv[u] = __builtin_nontemporal_load(g4 + j);
                 ev[u] = __builtin_nontemporal_load(e4 + j);
-                mv[u] = __builtin_nontemporal_load(m4 + j);
+                mv[u] = MOM ? __builtin_nontemporal_load(m4 + j) : f4{0.f, 0.f, 0.f, 0.f};
             } else {
                 gv[u] = ev[u] = mv[u] = f4{0.f, 0.f, 0.f, 0.f};
             }
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, fl
                 const Out o = step(ga[t], ea[t], ma[t], beta1, c, clip);
                 eo[t] = o.e;
                 mo[t] = o.m;
-                nf += ok ? nonfinite2(o.e, o.m) : 0u;
+                nf += ok ? nonfinite2(o.e, MOM ? o.m : 0.0f) : 0u;
                 if (ok) account(o);
                 s4v |= static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(o.s))) << (8 * t);
                 nib |= (o.s == 1 ? 1u : 0u) << t;
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, fl
             const uint32_t hi = __shfl_xor(nib, 1, kWave);  // the odd lane's nibble
             if (ok) {
                 __builtin_nontemporal_store(f4{eo[0], eo[1], eo[2], eo[3]}, e4 + j);
-                __builtin_nontemporal_store(f4{mo[0], mo[1], mo[2], mo[3]}, m4 + j);
+                if (MOM) __builtin_nontemporal_store(f4{mo[0], mo[1], mo[2], mo[3]}, m4 + j);
                 if (s4) s4[j] = s4v;
                 if (b8 && !(l & 1)) b8[j >> 1] = static_cast<uint8_t>(nib | (hi << 4));
             }
@@ -152,10 +154,10 @@ __global__ __launch_bounds__(kBlock) void k_sign(const float* __restrict__ g, fl
     if (w == 0 && l == 0 && n8 < n) {
         uint32_t byte = 0;
         for (int64_t j = n8; j < n; ++j) {
-            const Out o = step(g[j], e[j], m[j], beta1, c, clip);
+            const Out o = step(g[j], e[j], MOM ? m[j] : 0.0f, beta1, c, clip);
             e[j] = o.e;
-            m[j] = o.m;
-            nf += nonfinite2(o.e, o.m);
+            if (MOM) m[j] = o.m;
+            nf += nonfinite2(o.e, MOM ? o.m : 0.0f);
             account(o);
             if (sgn) sgn[j] = static_cast<int8_t>(o.s);
             byte |= (o.s == 1 ? 1u : 0u) << (j & 7);
@@ -226,8 +228,8 @@ extern "C" int ef_sign_compress(const float* g, float* e, float* m, int64_t n, f
     if (n < 0 || n > kMaxElems) return fail(EF_EINVAL, "n=%lld outside [0, 2^31-1]", (long long)n);
     if (!(beta1 >= 0.0f && beta1 <= 1.0f)) return fail(EF_EINVAL, "beta1 must lie in [0, 1]");
     if (!(clip > 0.0f)) return fail(EF_EINVAL, "clip must be > 0 (+inf disables clipping)");
-    if (n > 0 && (!g || !e || !m)) return fail(EF_EINVAL, "g, e and m must not be NULL");
-    if (n > 0 && (!aligned16(g) || !aligned16(e) || !aligned16(m)))
+    if (n > 0 && (!g || !e)) return fail(EF_EINVAL, "g and e must not be NULL");
+    if (n > 0 && (!aligned16(g) || !aligned16(e) || (m && !aligned16(m))))
         return fail(EF_EINVAL, "g, e and m must be 16-byte aligned");
     if (sign_out && (reinterpret_cast<uintptr_t>(sign_out) & 3u))
         return fail(EF_EINVAL, "sign_out must be 4-byte aligned");
@@ -243,12 +245,20 @@ extern "C" int ef_sign_compress(const float* g, float* e, float* m, int64_t n, f
     const int64_t grid = cdiv(waves, sign::kWaves);
     double4* part = static_cast<double4*>(ws);
     if (n > 0) {
-        if (stats)
-            EF_TRY(launch("sign_ef", sign::k_sign<true>, dim3(static_cast<unsigned>(grid)), dim3(sign::kBlock), s, g,
-                          e, m, n, beta1, c, clip, sign_out, bits, nonfinite, part));
+        const dim3 gd(static_cast<unsigned>(grid)), bd(sign::kBlock);
+        double4* p = stats ? part : nullptr;
+        if (stats && m)
+            EF_TRY(launch("sign_ef", sign::k_sign<true, true>, gd, bd, s, g, e, m, n, beta1, c, clip, sign_out, bits,
+                          nonfinite, p));
+        else if (stats)
+            EF_TRY(launch("sign_ef", sign::k_sign<true, false>, gd, bd, s, g, e, m, n, beta1, c, clip, sign_out, bits,
+                          nonfinite, p));
+        else if (m)
+            EF_TRY(launch("sign_ef", sign::k_sign<false, true>, gd, bd, s, g, e, m, n, beta1, c, clip, sign_out, bits,
+                          nonfinite, p));
         else
-            EF_TRY(launch("sign_ef", sign::k_sign<false>, dim3(static_cast<unsigned>(grid)), dim3(sign::kBlock), s, g,
-                          e, m, n, beta1, c, clip, sign_out, bits, nonfinite, static_cast<double4*>(nullptr)));
+            EF_TRY(launch("sign_ef", sign::k_sign<false, false>, gd, bd, s, g, e, m, n, beta1, c, clip, sign_out,
+                          bits, nonfinite, p));
     }
     if (!stats) return EF_OK;
     return launch("sign_stats", sign::k_sign_stats, dim3(1), dim3(sign::kStatsBlock), s,

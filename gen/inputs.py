@@ -21,6 +21,10 @@ Workloads (sizes are exact):
              N(0,1) starting weights.
 * ``large``  N = 1,300,000,000 magnitudes exp(-7 + 2 z), z ~ N(0,1), with random
              signs from a separate bit stream, k = 1,300,000, 5 chained steps.
+* ``adam``   the sign workload's size and gradient law (N = 340,000,000, the
+             parameter count of BERT-large) for a full 1-bit Adam run: weights
+             0.02 N(0,1), lr = 2e-5, beta1 = 0.9, beta2 = 0.999, eps = 1e-8, clip 5,
+             3 full-precision warm-up steps, then 1-bit compression steps.
 * ``random`` the large workload's gradients and sizes with k = 1,300,000 the
              expected count of random sparsification; its draws are keyed by
              RANDOM_SEED and the step number.
@@ -45,6 +49,8 @@ DECODE_N, DECODE_PACKETS, DECODE_K, DECODE_LR = 25_600_000, 16, 25_600, 0.1
 LARGE_N, LARGE_K, LARGE_STEPS, LARGE_BLOCK = 1_300_000_000, 1_300_000, 5, 256
 BERT_STEPS = 20
 RANDOM_SEED = 0x5EED_0001
+ADAM_N, ADAM_LR, ADAM_BETA1, ADAM_BETA2, ADAM_EPS, ADAM_WARMUP, ADAM_STEPS = 340_000_000, 2e-5, 0.9, 0.999, 1e-8, 3, 8
+ADAM = 6
 
 
 def rng(*key: int) -> np.random.Generator:
@@ -223,6 +229,22 @@ def large_gradient_device(step: int, n: int, device, chunk: int = 1 << 27):
         neg = torch.randint(0, 2, (m,), generator=gz, device=device, dtype=torch.uint8).bool()
         out[lo:lo + m] = torch.where(neg, -mag, mag)
     return out
+
+
+def adam_weights(n: int = ADAM_N) -> np.ndarray:
+    """Initial weights of the adam workload: 0.02 * N(0, 1)."""
+    def fill(c, m):
+        return (0.02 * rng(ADAM, 0, c, 0).standard_normal(m)).astype(np.float32)
+    return _chunked(n, fill)
+
+
+def adam_weights_device(n: int, device):
+    """The same law drawn on the device (values differ from the numpy stream)."""
+    import torch
+
+    gz = torch.Generator(device=device)
+    gz.manual_seed(ADAM * 1_000_003)
+    return torch.randn(n, generator=gz, device=device, dtype=torch.float32).mul_(0.02)
 
 
 def sign_gradient_device(step: int, n: int, device):

@@ -123,10 +123,14 @@ int ef_topk_compress_segmented(const float* g, float* e, int32_t nseg,
  *   q  = sign(x) in {-1, 0, +1}            sign(+-0) = sign(NaN) = 0
  *   c  = 1 - beta1                         (a float32 value)
  *   e  = beta1*e + c*(x - q)               (in place)
- *   m  = beta1*m + c*q                     (in place)
+ *   m  = beta1*m + c*q                     (in place; m may be NULL: compress
+ *                                           only, for data-parallel 1-bit Adam
+ *                                           where the momentum follows the
+ *                                           exchange of the signs)
  *   sign_out[i] = q                        (int8, nullable)
  *   bits[i/8] bit (i%8) = (q == +1)        (uint8[ceil(n/8)], LSB first, pad 0, nullable)
  *   *nonfinite = count of non-finite new e plus non-finite new m (nullable)
+ *                (stats: sum m'^2 is 0 when m is NULL)
  *   stats = {sum e'^2, sum m'^2, #(q = +1), #(q = -1)}  (device double[4],
  *           nullable; finite values only, float64, fixed-order sums; needs
  *           ws of ef_sign_workspace_bytes(n) bytes, 32-byte aligned; ws may be
@@ -137,6 +141,37 @@ size_t ef_sign_workspace_bytes(int64_t n);
 int ef_sign_compress(const float* g, float* e, float* m, int64_t n, float beta1,
                      float clip, int8_t* sign_out, uint8_t* bits, uint32_t* nonfinite,
                      double* stats, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Adam around the 1-bit compression.  [ONEBIT] "3.1 关键数据结构设计" (the state
+ * holds momentum, variance, beta1, beta2, eps and the step count), "2.2
+ * 动量修正策略" (momentum on the compressed gradient) and "6.1 收敛不稳定问题" (full
+ * precision for the first steps, then 1-bit compression).  The variance and
+ * parameter rules are textbook Adam (Kingma and Ba, Algorithm 1), with the
+ * bias corrections as host scalars:
+ *   step_size = lr / (1 - beta1^t),   sqrt_bc2 = sqrt(1 - beta2^t_v)
+ *   w = w - step_size * (m / (sqrt(v) / sqrt_bc2 + eps))
+ * float32; square root and divisions correctly rounded, every other product
+ * and sum rounded on its own; (1 - beta) is the float32 complement of beta.
+ *
+ * ef_adam_step: one full-precision (warm-up) step on the averaged gradient g:
+ *   m = beta1*m + (1-beta1)*g;  v = beta2*v + (1-beta2)*(g*g);  w as above.
+ * ef_onebit_adam_update: one compression-phase step once every worker's int8
+ * signs (ef_sign_compress with m = NULL) were summed into qsum (exact integer
+ * sum, 1 <= nworkers <= 127):
+ *   ghat = qsum / nworkers;  m = beta1*m + (1-beta1)*ghat;  v unchanged
+ *   (frozen after warm-up: only the signs are exchanged);  w as above.
+ *   With nworkers = 1, m matches ef_sign_compress's fused momentum bit for bit.
+ * *nonfinite (device uint32, nullable, overwritten) counts non-finite new m,
+ * v (warm-up only) and w.  g, m, v, w 16-byte aligned; qsum 4-byte aligned;
+ * 0 <= n <= 2^31 - 1; 0 <= beta <= 1; sqrt_bc2 > 0; eps >= 0.
+ * ------------------------------------------------------------------------ */
+int ef_adam_step(const float* g, float* m, float* v, float* w, int64_t n, float beta1,
+                 float beta2, float step_size, float sqrt_bc2, float eps, uint32_t* nonfinite,
+                 void* stream);
+int ef_onebit_adam_update(const int8_t* qsum, int32_t nworkers, float* m, const float* v,
+                          float* w, int64_t n, float beta1, float step_size, float sqrt_bc2,
+                          float eps, uint32_t* nonfinite, void* stream);
 
 /* ------------------------------------------------------------------------
  * 8-bit quantisation of a sent packet, the quantisation error kept in the

@@ -126,7 +126,8 @@ def test_sign_argument_checks():
     assert ok(b=1.5) == efg.EF_EINVAL
     assert ok(b=float("nan")) == efg.EF_EINVAL
     assert ok(c=0.0) == efg.EF_EINVAL
-    assert ok(m=None) == efg.EF_EINVAL
+    assert ok(m=None, e=None) == efg.EF_EINVAL  # m may be NULL (compress only), e may not
+    assert ok(m=FAKE_ODD) == efg.EF_EINVAL
     assert ok(e=FAKE_ODD) == efg.EF_EINVAL
     assert ok(s=FAKE + 2) == efg.EF_EINVAL
     assert ok(stats=FAKE) == efg.EF_EWS
@@ -193,3 +194,30 @@ def test_random_sparsify_argument_checks():
     assert call(ws=FAKE + 16) == efg.EF_EINVAL
     # the bitmap dominates the workspace: about n/8 bytes
     assert L.ef_random_sparsify_workspace_bytes(1_300_000_000) < 1_300_000_000 // 8 + (8 << 20)
+
+
+def test_adam_argument_checks():
+    L = efg.lib()
+    step = lambda **kw: L.ef_adam_step(kw.get("g", FAKE), kw.get("m", FAKE), kw.get("v", FAKE), kw.get("w", FAKE),
+                                       kw.get("n", 64), kw.get("b1", 0.9), kw.get("b2", 0.999), 1e-3,
+                                       kw.get("sb", 0.1), kw.get("eps", 1e-8), None, None)
+    assert step(n=-1) == efg.EF_EINVAL
+    assert step(b1=1.5) == efg.EF_EINVAL
+    assert step(b2=float("nan")) == efg.EF_EINVAL
+    assert step(sb=0.0) == efg.EF_EINVAL
+    assert step(eps=-1.0) == efg.EF_EINVAL
+    assert step(g=None) == efg.EF_EINVAL
+    assert step(v=FAKE_ODD) == efg.EF_EINVAL
+    upd = lambda **kw: L.ef_onebit_adam_update(kw.get("q", FAKE), kw.get("nw", 1), kw.get("m", FAKE), FAKE, FAKE,
+                                               64, 0.9, 1e-3, 0.1, 1e-8, None, None)
+    assert upd(nw=0) == efg.EF_EINVAL
+    assert upd(nw=128) == efg.EF_EINVAL
+    assert upd(q=None) == efg.EF_EINVAL
+    assert upd(q=FAKE + 2) == efg.EF_EINVAL
+    assert upd(m=None) == efg.EF_EINVAL
+
+
+def test_adam_scalars_match_the_oracle_helper():
+    import oracle
+    for args in [(2e-5, 0.9, 0.999, 1), (1e-3, 0.9, 0.999, 100, 10), (0.1, 0.5, 0.9, 7, 7)]:
+        assert efg.adam_scalars(*args) == oracle.adam_scalars(*args)
