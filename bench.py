@@ -102,7 +102,7 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=40_000_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stats", action="store_true", help="also compute the fused monitoring statistics")
-    ap.add_argument("--workload", default="large", choices=["large", "flat", "bert", "sign", "decode", "quant", "random"],
+    ap.add_argument("--workload", default="large", choices=["large", "flat", "bert", "sign", "decode", "quant", "random", "adam"],
                     help="large (default, the headline) or one of the other workloads")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -359,6 +359,40 @@ def other_workload(args):
             t0 = time.perf_counter()
             oracle.quantize_int8(v_h, np.arange(k, dtype=np.int32), np.zeros(k, np.float32))
             cpu = (k, time.perf_counter() - t0, f"one full packet, k = {k:,}")
+    elif wl == "adam":
+        n = gen.ADAM_N
+        b1, b2, eps, lr = gen.ADAM_BETA1, gen.ADAM_BETA2, gen.ADAM_EPS, gen.ADAM_LR
+        grads = [gen.sign_gradient_device(t, n, dev) for t in range(W + K)]
+        w = gen.adam_weights_device(n, dev)
+        m, v, e = torch.zeros(n, device=dev), torch.zeros(n, device=dev), torch.zeros(n, device=dev)
+        q = torch.empty(n, dtype=torch.int8, device=dev)
+        bits = torch.empty((n + 7) // 8, dtype=torch.uint8, device=dev)
+        # the state after the warm-up phase: full-precision steps first (untimed)
+        for t in range(1, gen.ADAM_WARMUP + 1):
+            ss, sb = efg.adam_scalars(lr, b1, b2, t)
+            efg.ef_adam_step(grads[0], m, v, w, b1, b2, ss, sb, eps)
+
+        def step(t):
+            # one compression-phase step on one worker: signs (int8 for the local
+            # sum, packed bits for the wire), then momentum and update
+            ss, sb = efg.adam_scalars(lr, b1, b2, gen.ADAM_WARMUP + 1 + t, gen.ADAM_WARMUP)
+            efg.ef_sign_compress(grads[t], e, None, b1, gen.SIGN_CLIP, sign_out=q, bits=bits)
+            efg.ef_onebit_adam_update(q, 1, m, v, w, b1, ss, sb, eps)
+        label, bpe, units, unit = "onebit_update", 21, n, "elems/s"
+        metric = "1-bit Adam compression-phase step elems/s, N=340M fp32"
+        desc = ("1-bit Adam step on one worker, N=340M: compress-only sign EF (int8 + packed bits), then momentum "
+                "on the signs, frozen variance and the Adam parameter update; lr 2e-5, betas 0.9/0.999")
+        if not args.no_cpu_baseline:
+            ns = 20_000_000
+            g0 = gen.sign_gradient(0, n=ns)
+            z = np.zeros(ns, np.float32)
+            w0 = gen.adam_weights(ns)
+            vv = np.full(ns, 1e-6, np.float32)
+            ss, sb = efg.adam_scalars(lr, b1, b2, 4, 3)
+            t0 = time.perf_counter()
+            _, _, q0, _, _ = oracle.sign(g0, z, None, b1, gen.SIGN_CLIP)
+            oracle.onebit_adam_update(q0, 1, z, vv, w0, b1, ss, sb, eps)
+            cpu = (ns, time.perf_counter() - t0, f"first {ns:,} elements of one compression-phase step")
     elif wl == "random":
         n, k, seed = gen.LARGE_N, gen.LARGE_K, gen.RANDOM_SEED
         grads = [gen.large_gradient_device(t, n, dev) for t in range(W + K)]
@@ -416,6 +450,18 @@ def other_workload(args):
         _, dms, dl = time_steps(step, 1, K, "decode_scatter")
         extra["decode_scatter_ms"] = dms
         extra["decode_entries_per_s"] = P * kp / (dms * 1e-3)
+    if wl == "adam":
+        _, cms, _ = time_steps(step, 1, K, "sign_ef")
+        extra["sign_compress_ms"] = cms
+        extra["sign_compress_GBps"] = 13.125 * n / (cms * 1e-3) / 1e9
+        extra["path_GBps"] = 34.125 * n / ((cms + kms) * 1e-3) / 1e9
+
+        def warm(t):
+            ss, sb = efg.adam_scalars(lr, b1, b2, 1 + t)
+            efg.ef_adam_step(grads[t], m, v, w, b1, b2, ss, sb, eps)
+        _, ams, _ = time_steps(warm, 1, K, "adam_step")
+        extra["adam_step_ms"] = ams
+        extra["adam_step_GBps"] = 28 * n / (ams * 1e-3) / 1e9
     if wl == "random":
         # every kernel of the path, one at a time; whole-path algorithmic bytes:
         # accum 12 B, mark 4 B + 1 bit, write 1 bit + 16 B per kept element

@@ -84,8 +84,10 @@ __device__ __forceinline__ void element(float gin, float& m, float& v, float& w,
 // Wave w owns elements [w*kRegion, min((w+1)*kRegion, n)); lane l of unroll
 // step u holds float4 j = base + 64u + l of its region; a final partial float4
 // (only in the last region) goes element by element.  ONEBIT reads the four
-// int8 sums of a float4 as one 32-bit word (qsum is 4-byte aligned).
-template <bool ONEBIT>
+// int8 sums of a float4 as one 32-bit word (qsum is 4-byte aligned).  Without
+// DIV the worker count is a power of two: qs * (1/N) is then exact and equals
+// the correctly rounded qs / N.
+template <bool ONEBIT, bool DIV>
 __global__ __launch_bounds__(kBlock) void k_adam(const float* __restrict__ g, const int8_t* __restrict__ qsum,
                                                  float nworkers, float* __restrict__ m, float* __restrict__ v,
                                                  float* __restrict__ w, int64_t n, Hyper h,
@@ -103,11 +105,10 @@ __global__ __launch_bounds__(kBlock) void k_adam(const float* __restrict__ g, co
     f4* v4 = reinterpret_cast<f4*>(v + beg);
     f4* w4 = reinterpret_cast<f4*>(w + beg);
     uint32_t nf = 0;
+    const float recip = 1.0f / nworkers;
+    auto ghat = [&](float qs) -> float { return DIV ? qs / nworkers : qs * recip; };
     auto gin_of = [&](f4 gv, uint32_t qw, int t) -> float {
-        if (ONEBIT) {
-            const float qs = static_cast<float>(static_cast<int8_t>(qw >> (8 * t)));
-            return qs / nworkers;
-        }
+        if (ONEBIT) return ghat(static_cast<float>(static_cast<int8_t>(qw >> (8 * t))));
         return t == 0 ? gv.x : t == 1 ? gv.y : t == 2 ? gv.z : gv.w;
     };
     auto iteration = [&](int64_t base, auto guard) {
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(kBlock) void k_adam(const float* __restrict__ g, co
                 __builtin_nontemporal_store(f4{wa[0], wa[1], wa[2], wa[3]}, w4 + j);
             } else if (GUARD && j == nfull && nfull < nv) {
                 for (int64_t i = beg + 4 * nfull; i < beg + len; ++i) {
-                    const float gin = ONEBIT ? static_cast<float>(qsum[i]) / nworkers : g[i];
+                    const float gin = ONEBIT ? ghat(static_cast<float>(qsum[i])) : g[i];
                     float mi = m[i], vi = v[i], wi = w[i];
                     element<ONEBIT>(gin, mi, vi, wi, h, nf);
                     m[i] = mi;
@@ -190,7 +191,7 @@ extern "C" int ef_adam_step(const float* g, float* m, float* v, float* w, int64_
     if (nonfinite) EF_TRY(launch("adam_zero", adam::k_zero_u32, dim3(1), dim3(1), s, nonfinite));
     if (n == 0) return EF_OK;
     const adam::Hyper h{beta1, 1.0f - beta1, beta2, 1.0f - beta2, step_size, sqrt_bc2, eps, 0.0f};
-    return launch("adam_step", adam::k_adam<false>, dim3(static_cast<unsigned>(adam::blocks_for(n))),
+    return launch("adam_step", adam::k_adam<false, false>, dim3(static_cast<unsigned>(adam::blocks_for(n))),
                   dim3(adam::kBlock), s, g, static_cast<const int8_t*>(nullptr), 1.0f, m, v, w, n, h, nonfinite);
 }
 
@@ -205,7 +206,9 @@ extern "C" int ef_onebit_adam_update(const int8_t* qsum, int32_t nworkers, float
     if (nonfinite) EF_TRY(launch("onebit_zero", adam::k_zero_u32, dim3(1), dim3(1), s, nonfinite));
     if (n == 0) return EF_OK;
     const adam::Hyper h{beta1, 1.0f - beta1, 1.0f, 0.0f, step_size, sqrt_bc2, eps, 0.0f};
-    return launch("onebit_update", adam::k_adam<true>, dim3(static_cast<unsigned>(adam::blocks_for(n))),
-                  dim3(adam::kBlock), s, static_cast<const float*>(nullptr), qsum, static_cast<float>(nworkers), m,
-                  const_cast<float*>(v), w, n, h, nonfinite);
+    const bool pow2 = (nworkers & (nworkers - 1)) == 0;
+    return launch("onebit_update", pow2 ? adam::k_adam<true, false> : adam::k_adam<true, true>,
+                  dim3(static_cast<unsigned>(adam::blocks_for(n))), dim3(adam::kBlock), s,
+                  static_cast<const float*>(nullptr), qsum, static_cast<float>(nworkers), m, const_cast<float*>(v), w,
+                  n, h, nonfinite);
 }

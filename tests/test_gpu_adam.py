@@ -56,7 +56,7 @@ def test_adam_step(n, kind):
 
 
 @pytest.mark.parametrize("n", SIZES)
-@pytest.mark.parametrize("nworkers", [1, 3, 127])
+@pytest.mark.parametrize("nworkers", [1, 2, 3, 64, 127])
 def test_onebit_update(n, nworkers):
     dev = device()
     _, m, v, w = state(n, n % 991)
