@@ -34,7 +34,7 @@ def log(*a):
 
 
 # committed rocprofv3 traffic summaries of the roofline kernel of other workloads
-TRAFFIC_PROFILES = {"random": "rs_accum_large_1p3e9_traffic"}
+TRAFFIC_PROFILES = {"random": "rs_accum_large_1p3e9_traffic", "adam": "onebit_update_adam_340m_traffic"}
 
 
 def measured_traffic(name="topk_stream_large_1p3e9_traffic"):
@@ -471,7 +471,8 @@ def other_workload(args):
         path_bytes = n * (12 + 4 + 0.25) + 16 * k
         extra["path_GBps"] = path_bytes / (extra["rs__ms"] * 1e-3) / 1e9
         extra["mark_elems_per_s"] = n / (extra["rs_mark_ms"] * 1e-3)
-        extra["copy_ceiling_GBps"] = copy_ceiling(dev)
+    # the practical ceiling, and the known-size kernel for the traffic counters
+    extra["copy_ceiling_GBps"] = copy_ceiling(dev)
     achieved = bpe * units / (kms * 1e-3) / 1e9
     res = {
         "metric": metric, "value": units / (ms * 1e-3), "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
