@@ -179,6 +179,22 @@ def main():
             breakdown[lab] = round(ms, 4)
     efg.profile_enable(False)
 
+    # per-step spread of the whole step and of the compression alone
+    steps_ms = per_step_ms(step, range(W, W + K), dev)
+    compress_ms = per_step_ms(
+        lambda t: efg.ef_topk_compress(grads[t], e, k, vals=vals, idx=idx, ws=ws, nonfinite=nonfinite, stats=stats),
+        range(W, W + K), dev)
+    # the last packet is well formed: k ascending in-range indices, finite values,
+    # no non-finite input, and the block mask counts its distinct 256-element blocks
+    step(W + K - 1)
+    torch.cuda.synchronize()
+    il = idx.long()
+    blocks = torch.unique(il >> 8).numel()
+    ok = (bool((il[1:] > il[:-1]).all()) and int(il[0]) >= 0 and int(il[-1]) < n
+          and bool(torch.isfinite(vals).all()) and int(nonfinite.item()) == 0 and int(nblk.item()) == blocks)
+    if not ok:
+        raise SystemExit("bench: the packet of the last step is malformed")
+
     copy_gbps = copy_ceiling(dev)
 
     result = {
@@ -219,6 +235,9 @@ def main():
         },
         "copy_ceiling_GBps": copy_gbps,
         "kernel_ms_one_step": breakdown,
+        "step_ms": steps_ms,
+        "compress_only_ms": compress_ms,
+        "verified": ok,
     }
     if not args.no_cpu_baseline:
         del grads
@@ -273,6 +292,29 @@ def time_steps(step, W, K, kernel_label):
     efg.profile_enable(False)
     # time of the labelled kernels per step (equal to the mean launch when one kernel matches)
     return start.elapsed_time(stop) / K, kms / K, launches
+
+
+def per_step_ms(step, steps, dev, flush_bytes=0):
+    """Each step bracketed by its own HIP events (outside the contract's timed
+    region): {"median", "min"} in ms.  With flush_bytes, a scratch buffer of
+    that size is written before every step so that the step starts with a cold
+    256 MB Infinity Cache."""
+    import statistics
+
+    import torch
+
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev) if flush_bytes else None
+    times = []
+    for t in steps:
+        if scratch is not None:
+            scratch.fill_(float(t))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step(t)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    return {"median": statistics.median(times), "min": min(times), "steps": len(times)}
 
 
 def other_workload(args):
@@ -445,7 +487,10 @@ def other_workload(args):
             oracle.sgd(w0, Gr, gen.DECODE_LR)
             cpu = (n, time.perf_counter() - t0, "one full decode + SGD step")
     ms, kms, launches = time_steps(step, W, K, label)
-    extra = {}
+    extra = {"step_ms": per_step_ms(step, range(W, W + K), dev)}
+    if wl in ("flat", "decode"):
+        # inputs fit the 256 MB Infinity Cache: also time each step after a 1 GiB write
+        extra["cold_step_ms"] = per_step_ms(step, range(W, W + K), dev, flush_bytes=1 << 30)
     if wl == "decode":
         _, dms, dl = time_steps(step, 1, K, "decode_scatter")
         extra["decode_scatter_ms"] = dms
