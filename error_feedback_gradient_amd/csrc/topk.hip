@@ -48,15 +48,16 @@ namespace topk {
 constexpr int kBlock = 256;                        // threads of the select / emit kernels
 constexpr int kWavesPerBlock = kBlock / kWave;
 // Streaming-pass shape, measured on MI355X: 4096-element regions per wave,
-// 8 x 128-bit loads in flight per lane and array, 1024-thread blocks.
+// all 16 x 128-bit loads of a region issued per lane and array before the
+// first use (176 VGPRs, no spills), 512-thread blocks.
 #ifndef EFG_STREAM_BLOCK
-#define EFG_STREAM_BLOCK 1024
+#define EFG_STREAM_BLOCK 512
 #endif
 #ifndef EFG_STREAM_REGION
 #define EFG_STREAM_REGION 4096
 #endif
 #ifndef EFG_STREAM_UNROLL
-#define EFG_STREAM_UNROLL 8
+#define EFG_STREAM_UNROLL 16
 #endif
 constexpr int kStreamBlock = EFG_STREAM_BLOCK;     // threads of the streaming kernel
 constexpr int kStreamWaves = kStreamBlock / kWave;
