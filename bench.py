@@ -170,7 +170,7 @@ def main():
     step(0)
     torch.cuda.synchronize()
     labels = ["upload", "topk_init", "topk_sample_hist", "topk_sample_select", "topk_stream", "topk_scan_groups",
-              "topk_compact", "topk_restore", "topk_hist", "topk_digit", "topk_count", "topk_emit_scan", "topk_write",
+              "topk_compact", "topk_hist", "topk_digit", "topk_count", "topk_emit_scan", "topk_write",
               "blocks_clear", "blocks_count", "blocks_scan", "blocks_write", "blocks_mask"]
     breakdown = {}
     for lab in labels:
@@ -495,6 +495,33 @@ def other_workload(args):
         _, dms, dl = time_steps(step, 1, K, "decode_scatter")
         extra["decode_scatter_ms"] = dms
         extra["decode_entries_per_s"] = P * kp / (dms * 1e-3)
+        # index encodings of every packet, encoded and decoded (16 packets per timed call)
+        pk = [idx[p * kp:(p + 1) * kp] for p in range(P)]
+        bm = [torch.empty((n + 7) // 8, dtype=torch.uint8, device=dev) for _ in range(P)]
+        bidx = [torch.empty(kp, dtype=torch.int32, device=dev) for _ in range(P)]
+        bk = torch.empty(1, dtype=torch.int64, device=dev)
+        wsb = efg.workspace(efg.lib().decode_bitmap_workspace_bytes(n), dev)
+        ds = [efg.encode_delta(pk[p]) for p in range(P)]
+        torch.cuda.synchronize()
+        dn = [int(ds[p][1].item()) for p in range(P)]
+        didx = [torch.empty(kp, dtype=torch.int32, device=dev) for _ in range(P)]
+        dst = torch.empty(1, dtype=torch.int32, device=dev)
+        wsd = efg.workspace(max(efg.lib().delta_workspace_bytes(kp), efg.lib().delta_workspace_bytes(max(dn))), dev)
+        enc = {
+            "bitmap_encode": lambda t: [efg.encode_bitmap(pk[p], n, bits=bm[p]) for p in range(P)],
+            "bitmap_decode": lambda t: [efg.decode_bitmap(bm[p], n, kp, idx=bidx[p], k_out=bk, ws=wsb) for p in range(P)],
+            "delta_encode": lambda t: [efg.encode_delta(pk[p], out=ds[p][0], nbytes_out=ds[p][1], ws=wsd) for p in range(P)],
+            "delta_decode": lambda t: [efg.decode_delta(ds[p][0], dn[p], kp, idx=didx[p], status=dst, ws=wsd)
+                                       for p in range(P)],
+        }
+        for name, fn in enc.items():
+            fn(0)
+            r = per_step_ms(fn, range(K), dev)
+            extra[name + "_ms"] = r["median"]
+        torch.cuda.synchronize()
+        extra["encodings_round_trip"] = all(torch.equal(bidx[p], pk[p]) and torch.equal(didx[p], pk[p])
+                                            for p in range(P))
+        extra["delta_bytes_per_index"] = sum(dn) / (P * kp)
     if wl == "adam":
         _, cms, _ = time_steps(step, 1, K, "sign_ef")
         extra["sign_compress_ms"] = cms

@@ -245,30 +245,94 @@ __global__ __launch_bounds__(kBlock) void k_dd_write(const uint8_t* __restrict__
 }
 
 // ------------------------------------------------------------------ blocks
-__device__ __forceinline__ bool blk_leader(const int32_t* idx, int64_t j, int64_t n, int64_t* blk) {
-    const int64_t i = idx[j];
-    if (i < 0 || i >= n) return false;
-    *blk = i >> 8;
-    if (j == 0) return true;
-    const int64_t ip = idx[j - 1];
-    return !(ip >= 0 && ip < n && (ip >> 8) == (i >> 8));
+// Encoder, for ascending indices in [0, n) (others are skipped and never cause a
+// write outside the outputs).  One block per chunk of kChunk list entries;
+// thread t holds entries [j0, j0 + kPer) of its chunk in registers (four
+// 128-bit loads when idx is 16-byte aligned).  A "leader" is the first entry
+// of a 256-element block; a "byte leader" the first entry of a mask byte
+// (8 blocks, 2048 elements), which writes that whole byte.
+template <bool VEC>
+__device__ __forceinline__ void load_entries(const int32_t* __restrict__ idx, int64_t j0, int64_t k,
+                                             int32_t (&v)[kPer], int32_t* prev) {
+    if (VEC && j0 + kPer <= k) {
+        const int4* p = reinterpret_cast<const int4*>(idx + j0);
+#pragma unroll
+        for (int q = 0; q < kPer / 4; ++q) {
+            const int4 w = p[q];
+            v[4 * q] = w.x;
+            v[4 * q + 1] = w.y;
+            v[4 * q + 2] = w.z;
+            v[4 * q + 3] = w.w;
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) v[t] = j0 + t < k ? idx[j0 + t] : -1;
+    }
+    *prev = j0 > 0 && j0 - 1 < k ? idx[j0 - 1] : -1;
 }
 
+__device__ __forceinline__ bool in_range(int64_t i, int64_t n) { return i >= 0 && i < n; }
+
+// Runs of equal (entry >> shift) are walked backwards over the thread's
+// entries; the run of its last entry may continue into the next thread's
+// range, so that part is read from global memory first (at most `limit`
+// entries).  An entry outside [0, n) ends a run.
+__device__ __forceinline__ int64_t tail_run(const int32_t* __restrict__ idx, int64_t from, int64_t k, int64_t n,
+                                            int64_t key, int shift, int64_t limit, uint32_t* bits) {
+    int64_t len = 0;
+    for (int64_t j = from; j < k && len < limit; ++j) {
+        const int64_t ij = idx[j];
+        if (!in_range(ij, n) || (ij >> shift) != key) break;
+        ++len;
+        if (bits) *bits |= 1u << ((ij >> 8) & 7);
+    }
+    return len;
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kBlock) void k_be_count(const int32_t* __restrict__ idx, int64_t k, int64_t n,
                                                      int64_t nchunks, uint8_t* __restrict__ offs,
-                                                     uint8_t* __restrict__ flags, uint32_t* __restrict__ cnt) {
+                                                     uint8_t* __restrict__ mask, uint32_t* __restrict__ cnt) {
     __shared__ uint32_t lds[kBlock / kWave + 1];
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        int32_t v[kPer];
+        int32_t prev;
+        load_entries<VEC>(idx, j0, k, v, &prev);
+        // mask byte of the run that ends this thread's entries, continued past them
+        int64_t run_m = -1;
+        uint32_t acc = 0;
+        if (in_range(v[kPer - 1], n)) {
+            run_m = v[kPer - 1] >> 11;
+            tail_run(idx, j0 + kPer, k, n, run_m, 11, 2048, &acc);
+        }
         uint32_t s = 0;
-        for (int t = 0; t < kPer && j0 + t < k; ++t) {
-            const int64_t i = idx[j0 + t];
-            offs[j0 + t] = static_cast<uint8_t>(i & 255);
-            int64_t b;
-            if (blk_leader(idx, j0 + t, n, &b)) {
-                ++s;
-                flags[b] = 1;
+        uint32_t ob[kPer / 4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int t = kPer - 1; t >= 0; --t) {
+            const int64_t i = v[t];
+            ob[t / 4] |= static_cast<uint32_t>(i & 255) << (8 * (t & 3));
+            if (!in_range(i, n)) {
+                run_m = -1;
+                acc = 0;
+                continue;
             }
+            const int64_t m = i >> 11;
+            if (m != run_m) {
+                run_m = m;
+                acc = 0;
+            }
+            acc |= 1u << ((i >> 8) & 7);
+            const int64_t ip = t == 0 ? prev : v[t - 1];
+            const bool ok_prev = in_range(ip, n);
+            if (!ok_prev || (ip >> 8) != (i >> 8)) ++s;
+            // the first entry of a mask byte writes the whole byte
+            if (!ok_prev || (ip >> 11) != m) mask[m] = static_cast<uint8_t>(acc);
+        }
+        if (VEC && j0 + kPer <= k) {
+            *reinterpret_cast<uint4*>(offs + j0) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+        } else {
+            for (int t = 0; t < kPer && j0 + t < k; ++t) offs[j0 + t] = static_cast<uint8_t>(v[t] & 255);
         }
         uint32_t total;
         block_excl_scan<kBlock>(s, lds, &total);
@@ -276,39 +340,51 @@ __global__ __launch_bounds__(kBlock) void k_be_count(const int32_t* __restrict__
     }
 }
 
+template <bool VEC>
 __global__ __launch_bounds__(kBlock) void k_be_write(const int32_t* __restrict__ idx, int64_t k, int64_t n,
                                                      int64_t nchunks, const uint32_t* __restrict__ cnt,
                                                      uint8_t* __restrict__ counts_m1, int64_t cap) {
     __shared__ uint32_t lds[kBlock / kWave + 1];
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
-        uint32_t s = 0;
-        for (int t = 0; t < kPer && j0 + t < k; ++t) {
-            int64_t b;
-            s += blk_leader(idx, j0 + t, n, &b) ? 1u : 0u;
+        int32_t v[kPer];
+        int32_t prev;
+        load_entries<VEC>(idx, j0, k, v, &prev);
+        // length of each entry's run of equal blocks from that entry on
+        int64_t run_b = -1, run_len = 0;
+        if (in_range(v[kPer - 1], n)) {
+            run_b = v[kPer - 1] >> 8;
+            run_len = tail_run(idx, j0 + kPer, k, n, run_b, 8, 256, nullptr);
+        }
+        uint32_t len_at[kPer];
+        uint32_t lead = 0;
+#pragma unroll
+        for (int t = kPer - 1; t >= 0; --t) {
+            const int64_t i = v[t];
+            len_at[t] = 0;
+            if (!in_range(i, n)) {
+                run_b = -1;
+                run_len = 0;
+                continue;
+            }
+            const int64_t b = i >> 8;
+            if (b != run_b) {
+                run_b = b;
+                run_len = 0;
+            }
+            ++run_len;
+            len_at[t] = static_cast<uint32_t>(run_len < 256 ? run_len : 256);
+            const int64_t ip = t == 0 ? prev : v[t - 1];
+            if (!in_range(ip, n) || (ip >> 8) != b) lead |= 1u << t;
         }
         uint32_t total;
-        int64_t ord = static_cast<int64_t>(cnt[c]) + block_excl_scan<kBlock>(s, lds, &total);
-        for (int t = 0; t < kPer && j0 + t < k; ++t) {
-            int64_t b;
-            if (!blk_leader(idx, j0 + t, n, &b)) continue;
-            int64_t e = j0 + t + 1;
-            while (e < k && e - (j0 + t) < 256 && idx[e] >= 0 && idx[e] < n && (idx[e] >> 8) == b) ++e;
-            if (ord < cap) counts_m1[ord] = static_cast<uint8_t>(e - (j0 + t) - 1);
+        int64_t ord = static_cast<int64_t>(cnt[c]) + block_excl_scan<kBlock>(__popc(lead), lds, &total);
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            if (!((lead >> t) & 1u)) continue;
+            if (ord < cap) counts_m1[ord] = static_cast<uint8_t>(len_at[t] - 1);
             ++ord;
         }
-    }
-}
-
-__global__ __launch_bounds__(kBlock) void k_be_mask(const uint8_t* __restrict__ flags, int64_t nb,
-                                                    uint8_t* __restrict__ mask) {
-    const int64_t nm = (nb + 7) / 8;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nm; i += stride) {
-        uint32_t v = 0;
-        for (int t = 0; t < 8; ++t)
-            if (i * 8 + t < nb && flags[i * 8 + t]) v |= 1u << t;
-        mask[i] = static_cast<uint8_t>(v);
     }
 }
 
@@ -478,22 +554,21 @@ int encode_blocks(const int32_t* idx, int64_t k, int64_t n, uint8_t* mask, uint8
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t nb = cdiv(n, 256);
     uint8_t* W = static_cast<uint8_t*>(ws);
-    uint8_t* flags = W;
     uint32_t* cnt = reinterpret_cast<uint32_t*>(W + round_up(static_cast<size_t>(nb) + 16, 256));
     const int64_t nchunks = std::max<int64_t>(1, cdiv(k, kChunk));
+    // mask bytes without any listed block stay zero; the others are written by their byte leader
     if (nb > 0)
-        EF_TRY(launch("blocks_clear", k_fill_bytes, dim3(grid_for(nb, kBlock * 16)), dim3(kBlock), s, flags, nb,
-                      static_cast<uint8_t>(0)));
-    EF_TRY(launch("blocks_count", k_be_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, idx, k, n, nchunks, offs,
-                  flags, cnt));
+        EF_TRY(launch("blocks_clear", k_fill_bytes, dim3(grid_for((nb + 7) / 8, kBlock * 16)), dim3(kBlock), s, mask,
+                      (nb + 7) / 8, static_cast<uint8_t>(0)));
+    const bool vec = aligned16(idx) && aligned16(offs);
+    EF_TRY(launch("blocks_count", vec ? k_be_count<true> : k_be_count<false>, dim3(grid_for(nchunks, 1)),
+                  dim3(kBlock), s, idx, k, n, nchunks, offs, mask, cnt));
     EF_TRY(launch("blocks_scan", k_excl_scan<uint32_t>, dim3(1), dim3(kScanThreads), s, cnt, nchunks,
                   static_cast<uint32_t*>(nullptr), nblk_out));
-    if (k > 0)
-        EF_TRY(launch("blocks_write", k_be_write, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, idx, k, n, nchunks,
-                      static_cast<const uint32_t*>(cnt), counts_m1, std::min(k, nb)));
-    if (nb == 0) return EF_OK;
-    return launch("blocks_mask", k_be_mask, dim3(grid_for((nb + 7) / 8, kBlock)), dim3(kBlock), s,
-                  static_cast<const uint8_t*>(flags), nb, mask);
+    if (k == 0) return EF_OK;
+    return launch("blocks_write", vec ? k_be_write<true> : k_be_write<false>, dim3(grid_for(nchunks, 1)),
+                  dim3(kBlock), s, idx, k, n, nchunks, static_cast<const uint32_t*>(cnt), counts_m1,
+                  std::min(k, nb));
 }
 
 int decode_blocks(const uint8_t* mask, const uint8_t* counts_m1, const uint8_t* offs, int64_t n, int64_t k,

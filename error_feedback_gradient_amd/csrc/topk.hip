@@ -72,7 +72,11 @@ constexpr int kSampleChunksPerWave = 4;
 constexpr int kSampleBlockChunks = kSampleChunksPerWave * (kSampleBlock / kWave);
 constexpr int kSampleBins = 4096;
 constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
-constexpr int kChunk = 4096;                       // entries per block-unit in select and emit
+#ifndef EFG_CHUNK
+#define EFG_CHUNK 4096
+#endif
+constexpr int kChunk = EFG_CHUNK;                  // entries per block-unit in select and emit
+static_assert(kChunk % kBlock == 0, "whole entries per thread");
 constexpr int kPerThread = kChunk / kBlock;
 constexpr int kRadixBins = 2048;
 constexpr int kMaxGrid = 2048;
@@ -658,19 +662,22 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_groups(const SegPlan* __res
 //    first radix histogram (top 11 key bits) of the tensor.  A tensor with many
 //    candidates per group shares each group among compact_split blocks: every
 //    one scans the group's region counts and copies its own slice of regions.
+//    For a tensor that takes the exact fallback, the same blocks instead put
+//    back x where the stream already wrote e = 0, so that e holds x whole.
 __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ plan, int32_t nseg,
                                                     const int32_t* __restrict__ cbb, const int32_t* __restrict__ gbb,
                                                     const int32_t* __restrict__ rb, const SegState* __restrict__ st,
                                                     const uint32_t* __restrict__ region_cnt,
                                                     const uint32_t* __restrict__ grp_off,
                                                     const uint2* __restrict__ cpair, float* __restrict__ dval,
-                                                    int32_t* __restrict__ didx, uint32_t* __restrict__ rhist) {
+                                                    int32_t* __restrict__ didx, uint32_t* __restrict__ rhist,
+                                                    float* __restrict__ e) {
     __shared__ uint32_t loff[kGroup];
     __shared__ uint32_t h[kRadixBins];
     __shared__ uint32_t lds[kWavesPerBlock + 1];
     const int b = blockIdx.x;
     const int s = upper_index(cbb, nseg, b);
-    if (plan[s].mode != MODE_NORMAL || st[s].fallback) return;
+    if (plan[s].mode != MODE_NORMAL) return;
     const int split = plan[s].compact_split;
     const int lb = b - cbb[s];
     const int gl = lb / split, part = lb % split;
@@ -682,6 +689,25 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     const int re = min(nr, rs + slice);
     if (rs >= re) return;
     const int t = threadIdx.x;
+    if (st[s].fallback) {
+        // the exact selection runs over x held in e: put back the stored
+        // candidates the stream cleared (key >= thi), one wave per region
+        const uint32_t thi = st[s].thi;
+        const int64_t lo = plan[s].off, hi = plan[s].off + plan[s].n;
+        const int64_t cap = plan[s].cap;
+        for (int r = rs + t / kWave; r < re; r += kWavesPerBlock) {
+            const uint32_t cnt = region_cnt[r0 + r];
+            const int64_t slot = plan[s].cand_base + (r0 + r - rb[s]) * cap;
+            for (uint32_t j = lane(); j < cnt; j += kWave) {
+                const uint2 pr = cpair[slot + j];
+                const float v = __uint_as_float(pr.x);
+                // indices were written by the stream of this call; the range check
+                // keeps a workspace overwritten meanwhile from becoming a stray write
+                if (key_of(v) >= thi && pr.y >= lo && pr.y < hi) e[pr.y] = v;
+            }
+        }
+        return;
+    }
     const uint32_t c = t < nr ? region_cnt[r0 + t] : 0u;
     uint32_t total;
     const uint32_t ex = block_excl_scan<kBlock>(c, lds, &total);
@@ -706,31 +732,6 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
         uint32_t* gh = rhist + static_cast<size_t>(s) * kRadixBins;
         for (int i = t; i < kRadixBins; i += kBlock)
             if (h[i]) atomicAdd(&gh[i], h[i]);
-    }
-}
-
-// 4b. fallback tensors only: put back x where the stream already wrote e = 0
-__global__ __launch_bounds__(kBlock) void k_restore(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                    const int32_t* __restrict__ rb, int64_t R,
-                                                    const SegState* __restrict__ st, const Header* __restrict__ hdr,
-                                                    const uint32_t* __restrict__ region_cnt,
-                                                    const uint2* __restrict__ cpair, float* __restrict__ e) {
-    if (!hdr->any_fallback) return;
-    const int64_t nw = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-    for (int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; w < R; w += nw) {
-        const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
-        if (plan[s].mode != MODE_NORMAL || !st[s].fallback) continue;
-        const uint32_t thi = st[s].thi;
-        const uint32_t cnt = region_cnt[w];
-        const int64_t slot = plan[s].cand_base + (w - rb[s]) * plan[s].cap;
-        const int64_t lo = plan[s].off, hi = plan[s].off + plan[s].n;
-        for (uint32_t j = lane(); j < cnt; j += kWave) {
-            const uint2 pr = cpair[slot + j];
-            const float v = __uint_as_float(pr.x);
-            // indices were written by the stream of this call; the range check
-            // keeps a workspace overwritten meanwhile from becoming a stray write
-            if (key_of(v) >= thi && pr.y >= lo && pr.y < hi) e[pr.y] = v;
-        }
     }
 }
 
@@ -1182,11 +1183,7 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     EF_TRY(launch("topk_compact", k_compact, dim3(static_cast<unsigned>(P.CB)), dim3(kBlock), s, plan, nseg,
                   static_cast<const int32_t*>(reinterpret_cast<int32_t*>(at(L.cbb))), gbb, rb,
                   static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
-                  static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair), dval, didx, rhist));
-    const unsigned gres = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, cdiv(P.R, kWavesPerBlock))));
-    EF_TRY(launch("topk_restore", k_restore, dim3(gres), dim3(kBlock), s, plan, nseg, rb, P.R,
-                  static_cast<const SegState*>(st), static_cast<const Header*>(hdr),
-                  static_cast<const uint32_t*>(region_cnt), static_cast<const uint2*>(cpair), e));
+                  static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair), dval, didx, rhist, e));
     const unsigned gu = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, P.QC + P.QR)));
     for (int pass = 0; pass < 3; ++pass) {
         EF_TRY(launch("topk_hist", k_hist, dim3(gu), dim3(kBlock), s, pass, plan, nseg,
