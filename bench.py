@@ -34,7 +34,8 @@ def log(*a):
 
 
 # committed rocprofv3 traffic summaries of the roofline kernel of other workloads
-TRAFFIC_PROFILES = {"random": "rs_accum_large_1p3e9_traffic", "adam": "onebit_update_adam_340m_traffic"}
+TRAFFIC_PROFILES = {"random": "rs_accum_large_1p3e9_traffic", "adam": "onebit_update_adam_340m_traffic",
+                    "sign": "sign_ef_340m_traffic"}
 
 
 def measured_traffic(name="topk_stream_large_1p3e9_traffic"):
