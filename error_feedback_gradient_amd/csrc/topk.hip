@@ -66,10 +66,19 @@ constexpr int kUnroll = EFG_STREAM_UNROLL;         // 128-bit loads in flight pe
 constexpr int kGroup = 256;                        // regions per group (candidate totals, compaction)
 constexpr int kSampleChunk = 256;                  // contiguous elements per sample chunk
 constexpr int kSampleChunksMax = 4096;
-constexpr int kSampleChunksMin = 256;
+#ifndef EFG_SAMPLE_DIV
+#define EFG_SAMPLE_DIV 16
+#endif
+#ifndef EFG_SAMPLE_MIN
+#define EFG_SAMPLE_MIN 256
+#endif
+constexpr int kSampleChunksMin = EFG_SAMPLE_MIN;  // fewest sample chunks of a sampled tensor
+constexpr int kSampleDiv = EFG_SAMPLE_DIV;         // sample one chunk in kSampleDiv (up to the maximum)
 constexpr int kSampleBlock = 256;                  // threads of the sample kernel
 constexpr int kSampleChunksPerWave = 4;
 constexpr int kSampleBlockChunks = kSampleChunksPerWave * (kSampleBlock / kWave);
+constexpr int kSampleBlocksTarget = 1024;            // enough sample blocks to fill the chip
+constexpr int kSampleRoundsMax = 8;
 constexpr int kSampleBins = 4096;
 constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
 #ifndef EFG_CHUNK
@@ -123,6 +132,7 @@ struct Plan {
     int64_t R = 0;      // regions (waves of the streaming pass)
     int64_t G = 0;      // region groups
     int64_t SB = 0;     // sample blocks
+    int32_t sample_rounds = 1;  // groups of kSampleBlockChunks chunks per sample block
     int64_t QR = 0;     // raw chunks (fallback units)
     int64_t QC = 0;     // bound on candidate chunks
     int64_t Ctot = 0;   // candidate slot entries
@@ -209,10 +219,12 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
         P.nregions = static_cast<int32_t>(cdiv(n, kRegion));
         P.ngroups = static_cast<int32_t>(cdiv(P.nregions, kGroup));
         if (P.mode == MODE_NORMAL) {
-            // Sample: every element of small tensors, else 1/8 of the 256-element
-            // chunks (at least 256 and at most 4096 chunks), evenly spaced.
+            // Sample: every element of small tensors, else 1/16 of the 256-element
+            // chunks (at least 256 and at most 4096 chunks), evenly spaced.  On the
+            // layer-wise BERT-base layout 1/16 reads 6 % of the data instead of
+            // 12.5 % and is 3 % faster per step than 1/8; 1/32 gained nothing more.
             const int64_t chunks = cdiv(n, kSampleChunk);
-            int64_t S = std::min<int64_t>(kSampleChunksMax, chunks / 8);
+            int64_t S = std::min<int64_t>(kSampleChunksMax, chunks / kSampleDiv);
             S = std::min<int64_t>(chunks, std::max<int64_t>(kSampleChunksMin, S));
             const bool exhaustive = (S == chunks);
             const int64_t S_el = exhaustive ? n : S * kSampleChunk;
@@ -262,12 +274,21 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
         p.gbb[s] = static_cast<int32_t>(p.G);
         p.R += P.nregions;
         p.G += P.ngroups;
-        p.sbb[s] = static_cast<int32_t>(p.SB);
-        p.SB += cdiv(P.sample_chunks, kSampleBlockChunks);
+        p.SB += P.sample_chunks;  // total sample chunks for now; blocks below
         p.rcb[s] = static_cast<int32_t>(p.QR);
         p.QR += P.raw_chunks;
         p.cbb[s] = static_cast<int32_t>(p.CB);
         if (P.cap > 0) p.CB += static_cast<int64_t>(P.ngroups) * P.compact_split;
+    }
+    // Sample blocks: many small tensors would otherwise give thousands of blocks,
+    // each clearing and flushing a whole 4096-bin histogram; beyond about
+    // kSampleBlocksTarget blocks every block takes several chunk groups.
+    p.sample_rounds = static_cast<int32_t>(std::min<int64_t>(
+        kSampleRoundsMax, std::max<int64_t>(1, cdiv(p.SB, static_cast<int64_t>(kSampleBlockChunks) * kSampleBlocksTarget))));
+    p.SB = 0;
+    for (int32_t s = 0; s < nseg; ++s) {
+        p.sbb[s] = static_cast<int32_t>(p.SB);
+        p.SB += cdiv(p.seg[s].sample_chunks, static_cast<int64_t>(kSampleBlockChunks) * p.sample_rounds);
     }
     p.rb[nseg] = static_cast<int32_t>(p.R);
     p.gbb[nseg] = static_cast<int32_t>(p.G);
@@ -291,10 +312,12 @@ __global__ __launch_bounds__(kBlock) void k_init(uint4* zero, int64_t nvec, uint
     }
 }
 
-// 1. sample histogram of x = g + e on the top 12 key bits
+// 1. sample histogram of x = g + e on the top 12 key bits; each block takes
+//    `rounds` consecutive groups of kSampleBlockChunks chunks of its tensor
 __global__ __launch_bounds__(kSampleBlock) void k_sample(const float* __restrict__ g, const float* __restrict__ e,
                                                    const SegPlan* __restrict__ plan, int32_t nseg,
-                                                   const int32_t* __restrict__ sbb, uint32_t* __restrict__ shist) {
+                                                   const int32_t* __restrict__ sbb, int32_t rounds,
+                                                   uint32_t* __restrict__ shist) {
     __shared__ uint32_t h[kSampleBins];
     const int b = blockIdx.x;
     const int s = upper_index(sbb, nseg, b);
@@ -305,27 +328,30 @@ __global__ __launch_bounds__(kSampleBlock) void k_sample(const float* __restrict
     __syncthreads();
     const int w = threadIdx.x / kWave;
     const int l = lane();
-    const int c0 = (b - sbb[s]) * kSampleBlockChunks + w * kSampleChunksPerWave;
-    float xs[kSampleChunksPerWave][4];
-    bool ok[kSampleChunksPerWave][4];
+    for (int rd = 0; rd < rounds; ++rd) {
+        const int c0 = ((b - sbb[s]) * rounds + rd) * kSampleBlockChunks + w * kSampleChunksPerWave;
+        if (c0 >= S) break;  // wave-uniform: the rest of this block's chunks lie past the sample
+        float xs[kSampleChunksPerWave][4];
+        bool ok[kSampleChunksPerWave][4];
 #pragma unroll
-    for (int u = 0; u < kSampleChunksPerWave; ++u) {
-        const int c = c0 + u;
-        int64_t start = 0;
-        if (exhaustive) start = static_cast<int64_t>(c) * kSampleChunk;
-        else if (S > 1) start = static_cast<int64_t>(c) * (n - kSampleChunk) / (S - 1);
+        for (int u = 0; u < kSampleChunksPerWave; ++u) {
+            const int c = c0 + u;
+            int64_t start = 0;
+            if (exhaustive) start = static_cast<int64_t>(c) * kSampleChunk;
+            else if (S > 1) start = static_cast<int64_t>(c) * (n - kSampleChunk) / (S - 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t loc = start + j * kWave + l;
-            ok[u][j] = (c < S) && (loc < n);
-            xs[u][j] = ok[u][j] ? (g[off + loc] + e[off + loc]) : 0.0f;
+            for (int j = 0; j < 4; ++j) {
+                const int64_t loc = start + j * kWave + l;
+                ok[u][j] = (c < S) && (loc < n);
+                xs[u][j] = ok[u][j] ? (g[off + loc] + e[off + loc]) : 0.0f;
+            }
         }
+#pragma unroll
+        for (int u = 0; u < kSampleChunksPerWave; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (ok[u][j]) atomicAdd(&h[key_of(xs[u][j]) >> kSampleShift], 1u);
     }
-#pragma unroll
-    for (int u = 0; u < kSampleChunksPerWave; ++u)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (ok[u][j]) atomicAdd(&h[key_of(xs[u][j]) >> kSampleShift], 1u);
     __syncthreads();
     uint32_t* gh = shist + static_cast<size_t>(s) * kSampleBins;
     for (int i = threadIdx.x; i < kSampleBins; i += kSampleBlock)
@@ -1164,7 +1190,7 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
 
     if (P.any_normal && P.SB > 0) {
         EF_TRY(launch("topk_sample_hist", k_sample, dim3(static_cast<unsigned>(P.SB)), dim3(kSampleBlock), s, g,
-                      static_cast<const float*>(e), plan, nseg, sbb, shist));
+                      static_cast<const float*>(e), plan, nseg, sbb, P.sample_rounds, shist));
         EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
                       static_cast<const uint32_t*>(shist), st));
     }
