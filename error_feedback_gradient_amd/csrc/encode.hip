@@ -204,11 +204,38 @@ __global__ __launch_bounds__(kBlock) void k_dd_count(const uint8_t* __restrict__
     }
 }
 
-__global__ void k_dd_check(const uint8_t* __restrict__ in, int64_t nbytes, int64_t k,
-                           const uint32_t* __restrict__ ttot, uint32_t* __restrict__ status) {
-    bool bad = static_cast<int64_t>(*ttot) != k;
-    if (nbytes > 0 && (in[nbytes - 1] & 0x80u)) bad = true;  // unterminated last varint
-    if (bad) atomicOr(status, 1u);
+// Both chunk scans of the decoder (varint counts and delta sums) in one launch,
+// then the stream checks: as many varints as k, and a terminated last varint.
+__global__ __launch_bounds__(kScanThreads) void k_dd_scan(const uint8_t* __restrict__ in, int64_t nbytes, int64_t k,
+                                                         int64_t nchunks, uint32_t* __restrict__ tcnt,
+                                                         uint64_t* __restrict__ dsum,
+                                                         uint32_t* __restrict__ status) {
+    __shared__ uint32_t lds[kScanThreads / kWave + 1];
+    __shared__ uint64_t lds64[kScanThreads / kWave + 1];
+    const int64_t per = (nchunks + kScanThreads - 1) / kScanThreads;
+    const int64_t i0 = min(nchunks, per * threadIdx.x), i1 = min(nchunks, i0 + per);
+    uint32_t a = 0;
+    uint64_t b = 0;
+    for (int64_t i = i0; i < i1; ++i) {
+        a += tcnt[i];
+        b += dsum[i];
+    }
+    uint32_t ta;
+    uint64_t tb;
+    uint32_t ra = block_excl_scan<kScanThreads>(a, lds, &ta);
+    uint64_t rb = block_excl_scan<kScanThreads>(b, lds64, &tb);
+    for (int64_t i = i0; i < i1; ++i) {
+        const uint32_t x = tcnt[i];
+        const uint64_t y = dsum[i];
+        tcnt[i] = ra;
+        dsum[i] = rb;
+        ra += x;
+        rb += y;
+    }
+    if (threadIdx.x == 0 && status) {
+        const bool bad = static_cast<int64_t>(ta) != k || (nbytes > 0 && (in[nbytes - 1] & 0x80u));
+        if (bad) atomicOr(status, 1u);
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void k_dd_write(const uint8_t* __restrict__ in, int64_t nbytes,
@@ -517,17 +544,11 @@ int decode_delta(const uint8_t* in, int64_t nbytes, int64_t k, int32_t* idx, uin
     uint8_t* W = static_cast<uint8_t*>(ws);
     uint32_t* tcnt = reinterpret_cast<uint32_t*>(W);
     uint64_t* dsum = reinterpret_cast<uint64_t*>(W + round_up(static_cast<size_t>(nchunks + 1) * 4, 256));
-    uint32_t* ttot = reinterpret_cast<uint32_t*>(W + need - 256);
     if (status) EF_TRY(launch("delta_zero", k_zero_u32, dim3(1), dim3(1), s, status));
     EF_TRY(launch("delta_dcount", k_dd_count, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, in, nbytes, nchunks, tcnt,
                   dsum, status));
-    EF_TRY(launch("delta_dscan32", k_excl_scan<uint32_t>, dim3(1), dim3(kScanThreads), s, tcnt, nchunks, ttot,
-                  static_cast<int64_t*>(nullptr)));
-    EF_TRY(launch("delta_dscan64", k_excl_scan<uint64_t>, dim3(1), dim3(kScanThreads), s, dsum, nchunks,
-                  static_cast<uint64_t*>(nullptr), static_cast<int64_t*>(nullptr)));
-    if (status)
-        EF_TRY(launch("delta_check", k_dd_check, dim3(1), dim3(1), s, in, nbytes, k,
-                      static_cast<const uint32_t*>(ttot), status));
+    EF_TRY(launch("delta_dscan", k_dd_scan, dim3(1), dim3(kScanThreads), s, in, nbytes, k, nchunks, tcnt, dsum,
+                  status));
     if (nbytes == 0) return EF_OK;
     return launch("delta_dwrite", k_dd_write, dim3(grid_for(nchunks, 1)), dim3(kBlock), s, in, nbytes, nchunks,
                   static_cast<const uint32_t*>(tcnt), static_cast<const uint64_t*>(dsum), k, idx, status);
