@@ -238,8 +238,10 @@ int ef_random_sparsify(const float* g, float* e, int64_t n, int64_t k, uint64_t 
  * emits).  An entry outside [0, n), or not above the entry before it in its
  * packet, is skipped and counted in *invalid (device uint32, nullable,
  * overwritten); with unordered packets other entries may be missed too, but no
- * write ever lands outside G.  pk_off must be non-decreasing with pk_off[0] >= 0;
- * it is read on the device.
+ * write ever lands outside G.  pk_off must be non-decreasing with pk_off[0] >= 0
+ * and pk_off[npk] at most the number of entries vals and idx hold (the library
+ * cannot see their length and reads every entry the table names); it is read on
+ * the device.
  * ------------------------------------------------------------------------ */
 int sparse_decode_accumulate(float* G, int64_t n, int32_t npk, const float* vals,
                              const int32_t* idx, const int64_t* pk_off,
