@@ -25,6 +25,12 @@
  *  - Floating-point data problems (Inf/NaN) are not call errors: the calls that
  *    can meet them count them into an optional device uint32 `nonfinite`
  *    (overwritten by each call).
+ *  - HIP graph capture: with ef_profile_enable off, every call only launches
+ *    kernels (no memset, no host wait), so a captured call replays exactly
+ *    like the eager one.  The exception is ef_topk_compress_segmented with more
+ *    than 13 tensors: its per-call plan no longer fits kernel arguments and is
+ *    copied from a pinned host buffer that the library reuses, so such calls
+ *    must not be captured.
  *
  * Sources cited below ("pages"):
  *   [SPARSE] "梯度稀疏化：只传输重要的梯度元素" — gradient sparsification.
