@@ -536,14 +536,24 @@ def other_workload(args):
         extra["adam_step_ms"] = ams
         extra["adam_step_GBps"] = 28 * n / (ams * 1e-3) / 1e9
     if wl == "random":
+        # which way the last call decided, from the call state at the start of
+        # the workspace (float32 S32 at byte 8, S_lo at 24, overflow flag at 28)
+        b = wsr[:64].cpu().numpy().tobytes()
+        s32_, slo_ = np.frombuffer(b, np.float32, 1, 8)[0], np.frombuffer(b, np.float32, 1, 24)[0]
+        slots = slo_ > 0 and np.frombuffer(b, np.uint32, 1, 28)[0] == 0 and s32_ >= slo_
+        extra["decided_by"] = "candidate slots" if slots else "second pass"
         # every kernel of the path, one at a time; whole-path algorithmic bytes:
-        # accum 12 B, mark 4 B + 1 bit, write 1 bit + 16 B per kept element
-        for kl in ("rs_mark", "rs_write", "rs_total", "rs_exact", "rs_scan", "rs_"):
+        # accum 12 B, then 16 B per kept element (the candidates and the sample
+        # are below 0.1 %), plus mark 4 B + 2 bits when the second pass runs
+        for kl in ("rs_sample", "rs_mark", "rs_filter", "rs_write", "rs_total", "rs_exact", "rs_scan", "rs_"):
             _, kms_l, nl = time_steps(step, 1, K, kl)
             extra[f"{kl}_ms"] = kms_l
-        path_bytes = n * (12 + 4 + 0.25) + 16 * k
+        path_bytes = n * 12 + 16 * k if slots else n * (12 + 4 + 0.25) + 16 * k
         extra["path_GBps"] = path_bytes / (extra["rs__ms"] * 1e-3) / 1e9
-        extra["mark_elems_per_s"] = n / (extra["rs_mark_ms"] * 1e-3)
+        # the same step made to take the exact integer sum and the second pass
+        forced = lambda t: efg.ef_random_sparsify(grads[t], e, k, seed, t, cap=cap, vals=vals, idx=idx, count=cnt,
+                                                  ws=wsr, flags=efg.EF_FLAG_FORCE_FALLBACK)
+        extra["forced_two_pass_step_ms"] = time_steps(forced, 1, K, "rs_")[0]
     # the practical ceiling, and the known-size kernel for the traffic counters
     extra["copy_ceiling_GBps"] = copy_ceiling(dev)
     achieved = bpe * units / (kms * 1e-3) / 1e9

@@ -224,7 +224,8 @@ int ef_quantize_int8(const float* vals, const int32_t* idx, int64_t k, float* e,
  * g and e 16-byte aligned; ws: ef_random_sparsify_workspace_bytes(n) bytes,
  * 256-byte aligned (unused when n = 0).
  * flags: 0 or EF_FLAG_FORCE_FALLBACK (always take the exact integer sum
- * instead of the certified float64 one; the result is the same).
+ * instead of the certified float64 one, and the second pass over x instead of
+ * the candidates collected while summing; the result is the same).
  * ------------------------------------------------------------------------ */
 size_t ef_random_sparsify_workspace_bytes(int64_t n);
 int ef_random_sparsify(const float* g, float* e, int64_t n, int64_t k, uint64_t seed,

@@ -2,7 +2,12 @@
 oracle: bit for bit on vals, idx, the count, S32, the non-finite count and the
 whole residual, at sizes that span many regions and ragged tails; at the large
 workload's full size, S32 against a certified float64 sum, every decision in
-sampled windows and at every kept position, and the bookkeeping everywhere."""
+sampled windows and at every kept position, and the bookkeeping everywhere.
+
+Both ways a call can decide are covered: the candidate slots filled by the
+accumulation pass (calls with n >= 65536 and k <= n / 512, when the sampled
+guess S_lo is at most S32 and no slot overflows) and the second marking pass;
+call_path reads which one a call took from the library's call state."""
 import math
 
 import numpy as np
@@ -16,7 +21,18 @@ from gpu_util import assert_bits_equal, device, host, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
-REGION = 8192
+REGION = 4096
+
+
+def call_path(ws):
+    """'slots' or 'two-pass', from the call state the library keeps at the
+    start of its workspace (float32 S32 at byte 8, float32 S_lo at byte 24,
+    uint32 slot-overflow flag at byte 28)."""
+    b = host(ws[:64]).tobytes()
+    s32 = np.frombuffer(b, np.float32, 1, 8)[0]
+    slo = np.frombuffer(b, np.float32, 1, 24)[0]
+    ovf = np.frombuffer(b, np.uint32, 1, 28)[0]
+    return "slots" if slo > 0 and ovf == 0 and s32 >= slo else "two-pass"
 
 
 def inputs(kind, n, key):
@@ -41,17 +57,21 @@ def run_gpu(g, e, k, seed, step, cap, flags=0):
     gd, ed = to_dev(g, dev), to_dev(e, dev)
     s32 = torch.empty(1, dtype=torch.float32, device=dev)
     nf = torch.zeros(1, dtype=torch.int32, device=dev)
-    vals, idx, cnt = efg.ef_random_sparsify(gd, ed, k, seed, step, cap=cap, sum_out=s32, nonfinite=nf, flags=flags)
+    ws = efg.workspace(efg.lib().ef_random_sparsify_workspace_bytes(g.size), dev)
+    vals, idx, cnt = efg.ef_random_sparsify(gd, ed, k, seed, step, cap=cap, sum_out=s32, nonfinite=nf, ws=ws,
+                                            flags=flags)
     c = int(host(cnt)[0])
     w = min(c, cap)
-    return host(vals)[:w], host(idx)[:w], host(ed), c, np.float32(host(s32)[0]), int(host(nf)[0])
+    return host(vals)[:w], host(idx)[:w], host(ed), c, np.float32(host(s32)[0]), int(host(nf)[0]), call_path(ws)
 
 
-def check(g, e, k, seed, step, cap=None, flags=0, what=""):
+def check(g, e, k, seed, step, cap=None, flags=0, what="", path=None):
     n = g.size
     if cap is None:
         cap = max(1, 2 * k + 64)
-    v, i, e2, c, s32, nf = run_gpu(g, e, k, seed, step, cap, flags)
+    v, i, e2, c, s32, nf, took = run_gpu(g, e, k, seed, step, cap, flags)
+    if path is not None:
+        assert took == path, (what, took, path)
     ov, oi, oe, oc, os32, onf = oracle.random_sparsify(g, e, k, seed, step, cap)
     assert c == oc, (what, c, oc)
     assert np.float32(s32).view(np.uint32) == np.float32(os32).view(np.uint32), (what, s32, os32)
@@ -62,7 +82,8 @@ def check(g, e, k, seed, step, cap=None, flags=0, what=""):
     return c
 
 
-SIZES = [1, 3, 4, 5, 63, 1000, REGION - 1, REGION, REGION + 1, 3 * REGION + 7, 100_003, (1 << 20) + 3]
+SIZES = [1, 3, 4, 5, 63, 1000, REGION - 1, REGION, REGION + 1, 2 * REGION + 1, 3 * REGION + 7, 100_003,
+         (1 << 20) + 3]
 
 
 @pytest.mark.parametrize("n", SIZES)
@@ -71,6 +92,70 @@ def test_sizes_and_kinds(n, kind):
     g, e = inputs(kind, n, n % 1000)
     for k in sorted({0, 1, max(1, n // 100), n}):
         check(g, e, k, 12345, 7, what=f"{kind} n={n} k={k}")
+
+
+@pytest.mark.parametrize("n", [65536, 65536 + 5, 16 * REGION * 3 + 7, (1 << 20) + 3, 3_000_017])
+@pytest.mark.parametrize("kind", ["normal", "lognormal", "ties"])
+def test_candidate_slots(n, kind):
+    """Few kept per region: the accumulation pass's candidates decide."""
+    g, e = inputs(kind, n, n % 997)
+    for k in sorted({1, n // 4096, n // 512}):
+        check(g, e, k, 4242, 3, what=f"slots {kind} n={n} k={k}", path="slots")
+        check(g, e, k, 4242, 3, flags=efg.EF_FLAG_FORCE_FALLBACK, what=f"forced {kind} n={n} k={k}",
+              path="two-pass")
+
+
+def test_slots_given_up_on_a_high_guess():
+    """n = 2^22: the sample reads chunks 4j of 256 elements.  Mass only there
+    makes the guess S_lo = 7/8 n * 1 three and a half times S: the second pass
+    decides."""
+    n = 1 << 22
+    x = np.repeat((np.arange(n // 256) % 4 == 0).astype(np.float32), 256)
+    check(x, np.zeros(n, np.float32), 4096, 5, 6, what="high guess", path="two-pass")
+
+
+def test_slots_given_up_on_overflow():
+    """One region holding most of S has far more than 64 candidates."""
+    n = 1 << 20
+    g, e = inputs("normal", n, 11)
+    g[7 * REGION:8 * REGION] = np.float32(1000.0)
+    dev = device()
+    ws = efg.workspace(efg.lib().ef_random_sparsify_workspace_bytes(n), dev)
+    efg.ef_random_sparsify(to_dev(g, dev), to_dev(e, dev), n // 512, 5, 6, ws=ws)
+    assert np.frombuffer(host(ws[:64]).tobytes(), np.uint32, 1, 28)[0] == 1
+    check(g, e, n // 512, 5, 6, what="overflow", path="two-pass")
+
+
+def guess_equals_sum_case(delta, seed=77, step=5):
+    """n = 2^22, k = 4096.  Ones fill the sampled chunks (chunks 4j of 256), so
+    S_lo = 0.875 * 2^22 = 3670016 exactly; the other chunks hold 200 elements
+    whose probabilities k v / S32 = v / 896 sit within two ulps of their draws,
+    then ones and one fraction so that S32 = S_lo + delta ulps (ulp 0.25)."""
+    n, k = 1 << 22, 4096
+    smask = np.repeat(np.arange(n // 256) % 4 == 0, 256)
+    x = smask.astype(np.float32)
+    free = np.nonzero(~smask)[0]
+    bpos = free[::15000][:200]
+    u = np.array([oracle.uniform(seed, step, int(j)) for j in bpos], np.float32)
+    v = (np.float32(896.0) * u).astype(np.float32)
+    v = (v.view(np.int32) + (np.arange(bpos.size, dtype=np.int32) % 5 - 2)).view(np.float32)
+    v[v <= 0] = np.float32(1.0)
+    x[bpos] = v
+    rest = 3670016.0 + 0.25 * delta - float(np.sum(x.astype(np.float64)))
+    ones = int(math.floor(rest))
+    fill = np.setdiff1d(free, bpos)[:ones + 1]
+    x[fill[:ones]] = 1.0
+    x[fill[ones]] = np.float32(rest - ones)
+    assert np.float32(oracle.sum_abs_exact(x)) == np.float32(3670016.0 + 0.25 * delta)
+    return x, k, seed, step
+
+
+@pytest.mark.parametrize("delta,path", [(-1, "two-pass"), (0, "slots"), (1, "slots")])
+def test_guess_at_the_sum(delta, path):
+    """S_lo against S32 at equality and one ulp either side, with decisions
+    settled by the last bits of the probability."""
+    x, k, seed, step = guess_equals_sum_case(delta)
+    check(x, np.zeros_like(x), k, seed, step, what=f"S32 = S_lo + {delta} ulp", path=path)
 
 
 @pytest.mark.parametrize("n", [5, REGION + 1, 100_003, (1 << 20) + 3])
@@ -118,9 +203,11 @@ def test_seed_and_step_words():
         check(g, e, 1000, seed, step, what=f"seed={seed} step={step}")
 
 
-def test_chained_steps():
-    """Ten steps with a fresh gradient each: the residual carries between calls."""
-    n, k = 1_000_003, 10_000
+@pytest.mark.parametrize("k", [10_000, 1_000])
+def test_chained_steps(k):
+    """Ten steps with a fresh gradient each: the residual carries between calls
+    (k = 1000 decides from the candidate slots, k = 10000 by the second pass)."""
+    n = 1_000_003
     dev = device()
     e_o = np.zeros(n, np.float32)
     ed = torch.zeros(n, dtype=torch.float32, device=dev)
@@ -179,6 +266,7 @@ def test_large_workload_full_size(flags):
         vals, idx, cnt = efg.ef_random_sparsify(g, e, k, seed, step, cap=cap, sum_out=s32, nonfinite=nf, ws=ws,
                                                 flags=flags)
         torch.cuda.synchronize()
+        assert call_path(ws) == ("two-pass" if flags else "slots")
         c = int(host(cnt)[0])
         S = np.float32(host(s32)[0])
         assert 0 < c <= cap and int(host(nf)[0]) == 0
