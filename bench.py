@@ -55,6 +55,33 @@ def measured_traffic(name="topk_stream_large_1p3e9_traffic"):
     return rec["traffic_bytes"]
 
 
+def pin_one_core():
+    """Pins the calling thread to its first allowed core (the oracle is
+    single-threaded); returns the previous affinity set, or None if pinning is
+    not available."""
+    try:
+        prev = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {sorted(prev)[0]})
+        return prev
+    except (AttributeError, OSError):
+        return None
+
+
+def unpin(prev):
+    if prev:
+        os.sched_setaffinity(0, prev)
+
+
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "the host CPU"
+
+
 def cpu_baseline(n_sample: int, k_sample: int):
     """The oracle as it stands, single-threaded, on the first n_sample elements
     of the step-0 gradient (numpy stream), e = 0."""
@@ -63,31 +90,22 @@ def cpu_baseline(n_sample: int, k_sample: int):
     import gen
     import oracle
 
-    cores = 1
-    try:
-        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
-    except (AttributeError, OSError):
-        cores = os.cpu_count() or 1
     g = gen.large_gradient(0, n=n_sample)
     e = np.zeros(n_sample, np.float32)
+    prev = pin_one_core()
+    cores = 1  # the oracle runs on one thread
     t0 = time.perf_counter()
     oracle.topk(g, e, k_sample)
     dt = time.perf_counter() - t0
-    model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
+    unpin(prev)
+    model = host_cpu_model()
     return {
         "value": n_sample / dt,
         "unit": "elems/s",
         "cores": cores,
         "kind": "oracle",
         "sample": f"first {n_sample:,} elements of the step-0 log-normal gradient, k = {k_sample:,}, e = 0; "
-                  f"{dt:.2f} s on one core of {model or 'the host CPU'} ({os.cpu_count()} logical CPUs)",
+                  f"{dt:.2f} s on one core of {model} ({os.cpu_count()} logical CPUs)",
         "seconds": dt,
         "GBps_algorithmic": STREAM_BYTES_PER_ELEM * n_sample / dt / 1e9,
     }
@@ -331,6 +349,9 @@ def other_workload(args):
     W, K = args.warmup, args.steps
     wl = args.workload
     cpu = None
+    # the oracle timings below run on one pinned core (the thread is unpinned
+    # before the GPU is timed)
+    pinned = None if args.no_cpu_baseline else pin_one_core()
     if wl == "flat":
         n, k = gen.FLAT_N, gen.FLAT_K
         grads = [torch.from_numpy(gen.flat_gradient(t)).to(dev) for t in range(W + K)]
@@ -487,6 +508,7 @@ def other_workload(args):
             Gr = oracle.decode(Gh, np.concatenate(val_l), np.concatenate(idx_l), offs)
             oracle.sgd(w0, Gr, gen.DECODE_LR)
             cpu = (n, time.perf_counter() - t0, "one full decode + SGD step")
+    unpin(pinned)
     ms, kms, launches = time_steps(step, W, K, label)
     extra = {"step_ms": per_step_ms(step, range(W, W + K), dev)}
     if wl in ("flat", "decode"):
@@ -569,9 +591,9 @@ def other_workload(args):
     }
     res.update(extra)
     if cpu is not None:
-        cores = 1
+        cores = 1  # the oracle runs on one thread
         res["cpu_baseline"] = {"value": cpu[0] / cpu[1], "unit": unit, "cores": cores, "kind": "oracle",
-                               "sample": cpu[2] + f"; {cpu[1]:.2f} s"}
+                               "sample": cpu[2] + f"; {cpu[1]:.2f} s on one core of {host_cpu_model()}"}
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
