@@ -203,16 +203,19 @@ def main():
     compress_ms = per_step_ms(
         lambda t: efg.ef_topk_compress(grads[t], e, k, vals=vals, idx=idx, ws=ws, nonfinite=nonfinite, stats=stats),
         range(W, W + K), dev)
-    # the last packet is well formed: k ascending in-range indices, finite values,
-    # no non-finite input, and the block mask counts its distinct 256-element blocks
-    step(W + K - 1)
+    # one more step, verified: the packet and the residual are the top-k of
+    # x = g + e by the invariants that fix it, and the block encoding decodes
+    # back to the packet
+    t_last = W + K - 1
+    x = grads[t_last] + e
+    step(t_last)
     torch.cuda.synchronize()
-    il = idx.long()
-    blocks = torch.unique(il >> 8).numel()
-    ok = (bool((il[1:] > il[:-1]).all()) and int(il[0]) >= 0 and int(il[-1]) < n
-          and bool(torch.isfinite(vals).all()) and int(nonfinite.item()) == 0 and int(nblk.item()) == blocks)
+    ok = topk_invariants(x, vals, idx, k, e) and int(nonfinite.item()) == 0
+    del x
+    back = efg.decode_blocks(mask, counts, offs, n, k)
+    ok = ok and torch.equal(back, idx)
     if not ok:
-        raise SystemExit("bench: the packet of the last step is malformed")
+        raise SystemExit("bench: the last step's packet is not the top-k of its input")
 
     copy_gbps = copy_ceiling(dev)
 
@@ -287,6 +290,53 @@ def copy_ceiling(dev):
     gbps = 2 * a.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del a, b
     return gbps
+
+
+def topk_invariants(x, vals, idx, k, e_after):
+    """True when (vals, idx, e_after) is the top-k of x: k strictly increasing
+    in-range indices, vals = x[idx] bit for bit, every kept key (|x| bits) >=
+    every dropped key with ties kept by lower index, and e_after = x except
+    +0 at idx.  These properties fix the result uniquely, so the check needs
+    no second implementation of the selection.  Device tensors."""
+    import torch
+
+    n = x.numel()
+    ik = idx.long()
+    if idx.numel() != k:
+        return False
+    if k == 0:
+        return torch.equal(e_after.view(torch.int32), x.view(torch.int32))
+    ok = bool((ik[1:] > ik[:-1]).all()) and int(ik[0]) >= 0 and int(ik[-1]) < n
+    ok = ok and torch.equal(vals.view(torch.int32), x[ik].view(torch.int32))
+    if ok and k < n:
+        key = x.view(torch.int32) & 0x7FFFFFFF
+        kept = torch.zeros(n, dtype=torch.bool, device=x.device)
+        kept[ik] = True
+        T = int(key[ik].min())
+        dmax = int(key.masked_fill(kept, -1).max())
+        ok = T >= dmax
+        if ok and T == dmax:
+            ok = int(ik[key[ik] == T].max()) < int(torch.nonzero((key == T) & ~kept)[0, 0])
+        del key, kept
+    if ok:
+        want = x.clone()
+        want[ik] = 0.0
+        ok = torch.equal(e_after.view(torch.int32), want.view(torch.int32))
+    return ok
+
+
+def sign_bits_agree(sgn, bits):
+    """int8 signs in {-1, 0, +1} and the packed bits equal (sign == +1), LSB
+    first, zero padding.  Device tensors."""
+    import torch
+
+    n = sgn.numel()
+    if not bool(((sgn >= -1) & (sgn <= 1)).all()):
+        return False
+    pos = torch.zeros(((n + 7) // 8) * 8, dtype=torch.int32, device=sgn.device)
+    pos[:n] = (sgn == 1).int()
+    w = torch.tensor([1, 2, 4, 8, 16, 32, 64, 128], dtype=torch.int32, device=sgn.device)
+    return torch.equal((pos.view(-1, 8) * w).sum(1).to(torch.uint8), bits)
 
 
 def time_steps(step, W, K, kernel_label):
@@ -576,6 +626,54 @@ def other_workload(args):
         forced = lambda t: efg.ef_random_sparsify(grads[t], e, k, seed, t, cap=cap, vals=vals, idx=idx, count=cnt,
                                                   ws=wsr, flags=efg.EF_FLAG_FORCE_FALLBACK)
         extra["forced_two_pass_step_ms"] = time_steps(forced, 1, K, "rs_")[0]
+    # one more step, verified by properties that need no second implementation
+    t_last = W + K - 1
+    if wl in ("flat", "bert", "random"):
+        x = grads[t_last] + e
+    if wl == "adam":
+        step(t_last)  # the int8 signs and their packed bits of this step agree
+        ok = sign_bits_agree(q, bits) and bool(torch.isfinite(w).all()) and bool(torch.isfinite(m).all())
+    elif wl == "sign":
+        step(t_last)
+        ok = sign_bits_agree(sgn, bits) and bool(torch.isfinite(e).all()) and bool(torch.isfinite(m).all())
+    elif wl == "flat":
+        step(t_last)
+        ok = topk_invariants(x, vals, idx, k, e)
+    elif wl == "bert":
+        step(t_last)
+        ok, o = True, 0
+        for s_, kk in enumerate(ks):  # each tensor is the top-k_s of its slice
+            a, b = int(off[s_]), int(off[s_ + 1])
+            ok = ok and topk_invariants(x[a:b], vals[o:o + kk], idx[o:o + kk] - a, int(kk), e[a:b])
+            o += int(kk)
+    elif wl == "random":
+        step(t_last)  # bookkeeping: vals = x[idx] in increasing index order, e = x except +0 there
+        c = int(cnt.item())
+        ik = idx[:min(c, cap)].long()
+        want = x.clone()
+        want[ik] = 0.0
+        ok = (0 < c <= cap and bool((ik[1:] > ik[:-1]).all()) and int(ik[0]) >= 0 and int(ik[-1]) < n
+              and torch.equal(vals[:c].view(torch.int32), x[ik].view(torch.int32))
+              and torch.equal(e.view(torch.int32), want.view(torch.int32)))
+        del want
+    elif wl == "quant":
+        step(t_last)  # codes within +-127, a finite positive scale, zero values coded 0
+        scale = float(sc.item())
+        ok = (bool((q >= -127).all()) and 0.0 < scale < float("inf")
+              and bool((q[vals == 0] == 0).all()))
+    else:
+        w_before = w.clone()
+        step(t_last)  # G is zero wherever no packet entry lands, and there w is untouched
+        touched = torch.zeros(n, dtype=torch.bool, device=dev)
+        touched[idx.long()] = True
+        ok = bool((G[~touched] == 0).all()) and torch.equal(w[G == 0], w_before[G == 0])
+        del w_before, touched
+    torch.cuda.synchronize()
+    if wl in ("flat", "bert", "random"):
+        del x
+    if not ok:
+        raise SystemExit(f"bench: the {wl} workload's last step failed its check")
+    extra["verified"] = ok
     # the practical ceiling, and the known-size kernel for the traffic counters
     extra["copy_ceiling_GBps"] = copy_ceiling(dev)
     achieved = bpe * units / (kms * 1e-3) / 1e9
