@@ -18,12 +18,20 @@
 //                 index order, with wave ballots.  Candidates with key >= T_hi
 //                 are almost surely kept, so the stream already writes e = 0
 //                 for them.  This is the only full pass: 12 bytes/element.
-//   3. scan       per-tensor candidate totals from per-group counts; a tensor
-//                 drops to the exact fallback when a slot overflowed or fewer
-//                 than k candidates were found (decided on the device; later
-//                 kernels skip the path not taken).
+//   3. scan       per-tensor candidate totals from per-group counts (true
+//                 counts: a region may have more candidates than its slot
+//                 holds); a tensor drops to the exact fallback when its
+//                 candidates exceed its slot capacity or fewer than k were
+//                 found (decided on the device; later kernels skip the path
+//                 not taken).
 //   4. compact    per group of 256 regions: candidate slots -> one dense,
 //                 index-ordered list, plus the first radix histogram.
+//      recollect  a region whose slot overflowed (its first `cap` candidates
+//                 are in the slot, the rest are untouched in e) is read again
+//                 past its last stored index by one wave, which appends the
+//                 rest at their places in the dense list.  Clustered
+//                 magnitudes thus cost one extra read of the crowded regions
+//                 instead of the exact pass over the whole tensor.
 //   5. radix      exact k-th largest key T over the candidates: digit passes
 //                 of 11, 10 and 10 bits with LDS-privatised histograms.
 //   6. emit       entries with key > T, plus the first r entries with key == T
@@ -115,14 +123,16 @@ struct alignas(16) SegState {
     uint32_t overflow, fallback;
     uint32_t ncand, dense_off, cchunk_begin, cchunks;
     uint32_t prefix, want, T, r;
-    uint32_t pad[4];
+    uint32_t group_base;  // the tensor's first group offset (dense list position = dense_off + grp_off - group_base)
+    uint32_t pad[3];
 };
 static_assert(sizeof(SegState) == 64, "SegState layout");
 
 struct alignas(16) Header {
     uint32_t any_fallback;
     uint32_t total_cchunks;
-    uint32_t pad[62];
+    uint32_t n_overflow;  // entries of the overflowed-region list
+    uint32_t pad[61];
 };
 static_assert(sizeof(Header) == 256, "Header layout");
 
@@ -145,7 +155,7 @@ struct Plan {
 struct Layout {
     size_t plan, rb, gbb, sbb, rcb, cbb, static_end;
     size_t header, state, shist, rhist, grp_cnt, zero_end;
-    size_t ccb, grp_off, region_cnt, cpair, dval, didx, cgt, ceq, rgt, req, spart, gpart, cpart, rpart;
+    size_t ccb, grp_off, region_cnt, ovf, cpair, dval, didx, cgt, ceq, rgt, req, spart, gpart, cpart, rpart;
     size_t total;
 };
 
@@ -171,6 +181,7 @@ static Layout make_layout(const Plan& p) {
     L.ccb = take((ns + 1) * 4);
     L.grp_off = take(static_cast<size_t>(p.G) * 4);
     L.region_cnt = take(static_cast<size_t>(p.R) * 4);
+    L.ovf = take(static_cast<size_t>(p.R) * 4);
     L.cpair = take(static_cast<size_t>(p.Ctot) * 8);
     L.dval = take(static_cast<size_t>(p.Ctot) * 4);
     L.didx = take(static_cast<size_t>(p.Ctot) * 4);
@@ -591,7 +602,8 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
                                                          uint32_t* __restrict__ grp_cnt, uint2* __restrict__ cpair,
                                                          float* __restrict__ vals,
                                                          int32_t* __restrict__ idx, uint32_t* __restrict__ nonfinite,
-                                                         double2* __restrict__ spart) {
+                                                         double2* __restrict__ spart, Header* __restrict__ hdr,
+                                                         uint32_t* __restrict__ ovf) {
     const int64_t w = static_cast<int64_t>(blockIdx.x) * kStreamWaves + threadIdx.x / kWave;
     if (w >= R) return;
     const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
@@ -621,10 +633,13 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
     }
     nf = wave_sum(nf);
     if (lane() == 0) {
-        const uint32_t kept = cnt < cap ? cnt : cap;
-        region_cnt[w] = kept;
-        if (cnt > cap) atomicOr(&st[s].overflow, 1u);
-        if (kept) atomicAdd(&grp_cnt[P.group_begin + rl / kGroup], kept);
+        // the true count: the slot holds the first min(cnt, cap) candidates
+        region_cnt[w] = cnt;
+        if (cnt > cap) {
+            atomicOr(&st[s].overflow, 1u);
+            ovf[atomicAdd(&hdr->n_overflow, 1u)] = static_cast<uint32_t>(w);
+        }
+        if (cnt) atomicAdd(&grp_cnt[P.group_begin + rl / kGroup], cnt);
         if (nf && nonfinite) atomicAdd(nonfinite, nf);
     }
 }
@@ -658,11 +673,14 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_groups(const SegPlan* __res
             const uint32_t d0 = b < G ? grp_off[b] : total;
             const uint32_t d1 = en < G ? grp_off[en] : total;
             const uint32_t nc = d1 - d0;
-            const bool fb = force_fallback || plan[s].direct || st[s].overflow ||
+            // the dense list of a tensor reuses its own slot area's extent
+            const int64_t capacity = static_cast<int64_t>(plan[s].nregions) * plan[s].cap;
+            const bool fb = force_fallback || plan[s].direct || static_cast<int64_t>(nc) > capacity ||
                             static_cast<int64_t>(nc) < plan[s].k;
             st[s].fallback = fb ? 1u : 0u;
             st[s].ncand = nc;
-            st[s].dense_off = d0;
+            st[s].dense_off = static_cast<uint32_t>(plan[s].cand_base);
+            st[s].group_base = d0;
             st[s].want = static_cast<uint32_t>(plan[s].k);
             st[s].prefix = 0;
             cchunks = fb ? 0u : (nc + kChunk - 1) / kChunk;
@@ -722,7 +740,7 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
         const int64_t lo = plan[s].off, hi = plan[s].off + plan[s].n;
         const int64_t cap = plan[s].cap;
         for (int r = rs + t / kWave; r < re; r += kWavesPerBlock) {
-            const uint32_t cnt = region_cnt[r0 + r];
+            const uint32_t cnt = min(region_cnt[r0 + r], static_cast<uint32_t>(cap));
             const int64_t slot = plan[s].cand_base + (r0 + r - rb[s]) * cap;
             for (uint32_t j = lane(); j < cnt; j += kWave) {
                 const uint2 pr = cpair[slot + j];
@@ -741,11 +759,12 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     for (int i = t; i < kRadixBins; i += kBlock) h[i] = 0;
     __syncthreads();
     const uint32_t q0 = loff[rs], q1 = re < nr ? loff[re] : total;
-    const uint32_t dbase = grp_off[gi];
+    const uint32_t dbase = st[s].dense_off + (grp_off[gi] - st[s].group_base);
     const int64_t slot0 = plan[s].cand_base + (r0 - rb[s]) * plan[s].cap;
     const int64_t cap = plan[s].cap;
     for (uint32_t q = q0 + t; q < q1; q += kBlock) {
         const int r = rs + upper_index(loff + rs, re - rs, q);
+        if (q - loff[r] >= cap) continue;  // past the slot: k_recollect writes it
         const int64_t src = slot0 + r * cap + (q - loff[r]);
         const uint2 pr = cpair[src];
         const float v = __uint_as_float(pr.x);
@@ -757,6 +776,84 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     if (q1 > q0) {
         uint32_t* gh = rhist + static_cast<size_t>(s) * kRadixBins;
         for (int i = t; i < kRadixBins; i += kBlock)
+            if (h[i]) atomicAdd(&gh[i], h[i]);
+    }
+}
+
+// 4b. one wave per overflowed region of a tensor on the fast path.  Its slot
+//     holds the region's first `cap` candidates in index order; the rest were
+//     not stored, so the stream left e = x for them.  They are read again from
+//     e past the last stored index (eight 64-element rows in flight per lane)
+//     and appended in index order after the stored ones, at the dense
+//     positions k_compact left free; their top digits join the first radix
+//     histogram (counted in a per-wave LDS histogram and added to the global
+//     one per region: the crowded candidates share a few bins, and one global
+//     atomic each would serialise on them).  Like the stream for stored ones,
+//     it clears e where the key is >= thi, so that every candidate of the
+//     dense list obeys the rule k_write relies on.  Grid-stride over the
+//     overflow list; empty in the common case.
+constexpr int kRecollectBlocks = 512;
+constexpr int kRecollectRows = 8;
+__global__ __launch_bounds__(kBlock) void k_recollect(const SegPlan* __restrict__ plan, int32_t nseg,
+                                                      const int32_t* __restrict__ rb, const int32_t* __restrict__ gbb,
+                                                      const SegState* __restrict__ st,
+                                                      const uint32_t* __restrict__ region_cnt,
+                                                      const uint32_t* __restrict__ grp_off,
+                                                      const uint2* __restrict__ cpair, const Header* __restrict__ hdr,
+                                                      const uint32_t* __restrict__ ovf, float* __restrict__ e,
+                                                      float* __restrict__ dval, int32_t* __restrict__ didx,
+                                                      uint32_t* __restrict__ rhist) {
+    __shared__ uint32_t lh[kWavesPerBlock][kRadixBins];
+    const uint32_t nov = hdr->n_overflow;
+    const int l = lane();
+    uint32_t* h = lh[threadIdx.x / kWave];
+    const uint32_t stride = gridDim.x * kWavesPerBlock;
+    for (uint32_t j = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; j < nov; j += stride) {
+        const int32_t w = static_cast<int32_t>(ovf[j]);
+        const int s = upper_index(rb, nseg, w);
+        const SegPlan& P = plan[s];
+        const uint32_t cap = static_cast<uint32_t>(P.cap);
+        if (P.mode != MODE_NORMAL || st[s].fallback || cap == 0) continue;
+        const int64_t rl = w - rb[s];
+        const int64_t gend = P.off + min(rl * kRegion + kRegion, P.n);
+        const uint32_t cnt = region_cnt[w];
+        const int64_t last = cpair[P.cand_base + rl * cap + cap - 1].y;  // index of the last stored candidate
+        // dense position of the region's first candidate: its group's offset plus
+        // the true counts of the group's earlier regions
+        const int64_t g0 = rb[s] + rl / kGroup * kGroup;
+        uint32_t before = 0;
+        for (int64_t r = g0 + l; r < w; r += kWave) before += region_cnt[r];
+        before = wave_sum(before);
+        const uint32_t gi = static_cast<uint32_t>(gbb[s] + rl / kGroup);
+        const uint32_t base = st[s].dense_off + (grp_off[gi] - st[s].group_base) + before;
+        const uint32_t tlo = st[s].tlo, thi = st[s].thi;
+        for (int i = l; i < kRadixBins; i += kWave) h[i] = 0;
+        uint32_t pos = cap;  // next entry of this region
+        for (int64_t i0 = last + 1; i0 < gend && pos < cnt; i0 += kWave * kRecollectRows) {
+            float x[kRecollectRows];
+#pragma unroll
+            for (int u = 0; u < kRecollectRows; ++u) {
+                const int64_t i = i0 + u * kWave + l;
+                x[u] = i < gend ? e[i] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kRecollectRows; ++u) {
+                const int64_t i = i0 + u * kWave + l;
+                const uint32_t key = key_of(x[u]);
+                const bool hit = i < gend && key >= tlo;
+                const uint64_t bal = __ballot(hit);
+                const uint32_t p = pos + count_below(bal);
+                if (hit && p < cnt) {
+                    dval[base + p] = x[u];
+                    didx[base + p] = static_cast<int32_t>(i);
+                    atomicAdd(&h[key >> 20], 1u);
+                    if (key >= thi) e[i] = 0.0f;
+                }
+                pos += popc64(bal);
+            }
+        }
+        uint32_t* gh = rhist + static_cast<size_t>(s) * kRadixBins;
+        for (int i = l; i < kRadixBins; i += kWave)
             if (h[i]) atomicAdd(&gh[i], h[i]);
     }
 }
@@ -1166,6 +1263,7 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     uint32_t* ccb = reinterpret_cast<uint32_t*>(at(L.ccb));
     uint32_t* grp_off = reinterpret_cast<uint32_t*>(at(L.grp_off));
     uint32_t* region_cnt = reinterpret_cast<uint32_t*>(at(L.region_cnt));
+    uint32_t* ovf = reinterpret_cast<uint32_t*>(at(L.ovf));
     uint2* cpair = reinterpret_cast<uint2*>(at(L.cpair));
     float* dval = reinterpret_cast<float*>(at(L.dval));
     int32_t* didx = reinterpret_cast<int32_t*>(at(L.didx));
@@ -1197,10 +1295,10 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     const dim3 sgrid(static_cast<unsigned>(cdiv(P.R, kStreamWaves)));
     if (stats)
         EF_TRY(launch("topk_stream", k_stream<true>, sgrid, dim3(kStreamBlock), s, g, e, plan, nseg, rb, P.R, st,
-                      region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart));
+                      region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart, hdr, ovf));
     else
         EF_TRY(launch("topk_stream", k_stream<false>, sgrid, dim3(kStreamBlock), s, g, e, plan, nseg, rb, P.R, st,
-                      region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart));
+                      region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart, hdr, ovf));
     if (!P.any_normal) return finish_stats();
 
     EF_TRY(launch("topk_scan_groups", k_scan_groups, dim3(1), dim3(kScanBlock), s, plan, nseg, gbb, P.G,
@@ -1210,6 +1308,10 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
                   static_cast<const int32_t*>(reinterpret_cast<int32_t*>(at(L.cbb))), gbb, rb,
                   static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
                   static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair), dval, didx, rhist, e));
+    EF_TRY(launch("topk_recollect", k_recollect, dim3(kRecollectBlocks), dim3(kBlock), s, plan, nseg, rb, gbb,
+                  static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
+                  static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair),
+                  static_cast<const Header*>(hdr), static_cast<const uint32_t*>(ovf), e, dval, didx, rhist));
     const unsigned gu = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, P.QC + P.QR)));
     for (int pass = 0; pass < 3; ++pass) {
         EF_TRY(launch("topk_hist", k_hist, dim3(gu), dim3(kBlock), s, pass, plan, nseg,

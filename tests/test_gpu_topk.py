@@ -62,13 +62,72 @@ def test_forced_fallback(n, k, kind):
     check(g, e, k, flags=efg.EF_FLAG_FORCE_FALLBACK, what=f"fallback n={n} k={k} {kind}")
 
 
-def test_clustered_magnitudes_overflow_to_fallback():
-    # all large values sit in one region: per-region candidate slots overflow
+def test_clustered_magnitudes_overflow():
+    # all large values sit in a few regions: their candidate slots overflow and
+    # the rest of their candidates are read again from e
     n, k = 2_000_000, 20_000
     g = gen.normal_small(n, 110, 0, scale=1e-3)
     g[500_000:540_000] = gen.normal_small(40_000, 111, 0, scale=10.0)
     e = np.zeros(n, np.float32)
     check(g, e, k, what="clustered")
+
+
+@pytest.mark.parametrize("where", ["start", "end", "two", "ties", "residual"])
+def test_clustered_regions_recollected(where):
+    """Crowded regions at the tensor's start, at its ragged end, in two places,
+    full of equal keys, or carried in the residual; several k."""
+    n = 3_000_017
+    g = gen.normal_small(n, 112, 1, scale=1e-3)
+    e = np.zeros(n, np.float32)
+    if where == "start":
+        g[:30_000] = gen.normal_small(30_000, 113, 1, scale=5.0)
+    elif where == "end":
+        g[-30_001:] = gen.normal_small(30_001, 114, 1, scale=5.0)
+    elif where == "two":
+        g[100_003:112_003] = gen.normal_small(12_000, 115, 1, scale=5.0)
+        g[2_000_000:2_020_000] = gen.normal_small(20_000, 116, 1, scale=3.0)
+    elif where == "ties":
+        g[700_000:740_000] = np.float32(2.5)
+    else:
+        e[1_234_567:1_264_567] = gen.normal_small(30_000, 117, 1, scale=5.0)
+    for k in (3000, 10_000, 25_000):
+        check(g, e, k, what=f"clustered {where} k={k}")
+
+
+def test_clustered_flat_layers():
+    """A flat call over tensors of very different scales (the usual way a whole
+    model's gradient is compressed at once): the top entries crowd into the
+    large-scale tensors."""
+    r = gen.rng(118)
+    sizes = [768] * 20 + [3072] * 4 + [589_824] * 4 + [393_216]
+    parts = [gen.normal_small(m, 119, i, scale=float(10.0 ** r.uniform(-4, -1))) for i, m in enumerate(sizes)]
+    g = np.concatenate(parts).astype(np.float32)
+    e = gen.normal_small(g.size, 120, scale=1e-5)
+    for k in (g.size // 1000, g.size // 300):
+        check(g, e, k, what=f"flat layers k={k}")
+
+
+def sampled_chunk_mask(n):
+    """Elements the top-k sample reads for a tensor of n elements (chunks of 256
+    starting at c * (n - 256) / (S - 1), S = max(256, min(4096, chunks / 16)))."""
+    chunks = -(-n // 256)
+    S = min(chunks, max(256, min(4096, chunks // 16)))
+    m = np.zeros(n, bool)
+    for c in range(S):
+        st = c * (n - 256) // (S - 1)
+        m[st:st + 256] = True
+    return m
+
+
+def test_candidates_beyond_capacity_fall_back():
+    """The sample sees only small values, so the threshold it gives lets most
+    of the tensor through: more candidates than the slots hold in total, and
+    the exact fallback decides."""
+    n, k = 2_000_000, 2000
+    m = sampled_chunk_mask(n)
+    g = np.where(m, gen.normal_small(n, 121, scale=1e-3), np.float32(1.0)).astype(np.float32)
+    g[::7] = np.float32(0.5)
+    check(g, np.zeros(n, np.float32), k, what="beyond capacity")
 
 
 def test_flat_chain_ten_steps():
