@@ -604,43 +604,71 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
                                                          int32_t* __restrict__ idx, uint32_t* __restrict__ nonfinite,
                                                          double2* __restrict__ spart, Header* __restrict__ hdr,
                                                          uint32_t* __restrict__ ovf) {
+    __shared__ uint32_t lcnt[kStreamWaves];
+    __shared__ int32_t lgrp[kStreamWaves];
     const int64_t w = static_cast<int64_t>(blockIdx.x) * kStreamWaves + threadIdx.x / kWave;
-    if (w >= R) return;
-    const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
-    const SegPlan& P = plan[s];
-    const int64_t rl = w - rb[s];
-    const int64_t lbeg = rl * kRegion;
-    const int64_t lend = min(lbeg + static_cast<int64_t>(kRegion), P.n);
-    const int64_t gbeg = P.off + lbeg, gend = P.off + lend;
-    const int mode = P.mode;
-    uint32_t cnt = 0, nf = 0;
-    double acc = 0.0;
-    const uint32_t cap = static_cast<uint32_t>(P.cap);
-    uint2* cp = cpair + P.cand_base + rl * P.cap;
-    if (mode == MODE_NORMAL) {
-        // a direct (dense) selection collects nothing
-        const uint32_t tlo = P.direct ? kNoKey : st[s].tlo;
-        const uint32_t thi = P.direct ? kNoKey : st[s].thi;
-        stream_region<MODE_NORMAL, STATS>(g, e, gbeg, gend, tlo, thi, cap, cp, vals, idx, 0, cnt, nf, acc);
-    } else if (mode == MODE_ALL) {
-        stream_region<MODE_ALL, STATS>(g, e, gbeg, gend, 0, 0, 0, cp, vals, idx, P.out_off + lbeg, cnt, nf, acc);
-    } else {
-        stream_region<MODE_NONE, STATS>(g, e, gbeg, gend, 0, 0, 0, cp, vals, idx, 0, cnt, nf, acc);
-    }
-    if (STATS) {
-        acc = wave_sum(acc);
-        if (lane() == 0) spart[w] = mode == MODE_ALL ? make_double2(acc, 0.0) : make_double2(0.0, acc);
-    }
-    nf = wave_sum(nf);
-    if (lane() == 0) {
-        // the true count: the slot holds the first min(cnt, cap) candidates
-        region_cnt[w] = cnt;
-        if (cnt > cap) {
-            atomicOr(&st[s].overflow, 1u);
-            ovf[atomicAdd(&hdr->n_overflow, 1u)] = static_cast<uint32_t>(w);
+    uint32_t cnt = 0;
+    int32_t grp = -1;
+    if (w < R) {
+        const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
+        const SegPlan& P = plan[s];
+        const int64_t rl = w - rb[s];
+        const int64_t lbeg = rl * kRegion;
+        const int64_t lend = min(lbeg + static_cast<int64_t>(kRegion), P.n);
+        const int64_t gbeg = P.off + lbeg, gend = P.off + lend;
+        const int mode = P.mode;
+        uint32_t nf = 0;
+        double acc = 0.0;
+        const uint32_t cap = static_cast<uint32_t>(P.cap);
+        uint2* cp = cpair + P.cand_base + rl * P.cap;
+        if (mode == MODE_NORMAL) {
+            // a direct (dense) selection collects nothing
+            const uint32_t tlo = P.direct ? kNoKey : st[s].tlo;
+            const uint32_t thi = P.direct ? kNoKey : st[s].thi;
+            stream_region<MODE_NORMAL, STATS>(g, e, gbeg, gend, tlo, thi, cap, cp, vals, idx, 0, cnt, nf, acc);
+        } else if (mode == MODE_ALL) {
+            stream_region<MODE_ALL, STATS>(g, e, gbeg, gend, 0, 0, 0, cp, vals, idx, P.out_off + lbeg, cnt, nf, acc);
+        } else {
+            stream_region<MODE_NONE, STATS>(g, e, gbeg, gend, 0, 0, 0, cp, vals, idx, 0, cnt, nf, acc);
         }
-        if (cnt) atomicAdd(&grp_cnt[P.group_begin + rl / kGroup], cnt);
-        if (nf && nonfinite) atomicAdd(nonfinite, nf);
+        if (STATS) {
+            acc = wave_sum(acc);
+            if (lane() == 0) spart[w] = mode == MODE_ALL ? make_double2(acc, 0.0) : make_double2(0.0, acc);
+        }
+        nf = wave_sum(nf);
+        if (lane() == 0) {
+            // the true count: the slot holds the first min(cnt, cap) candidates
+            region_cnt[w] = cnt;
+            if (cnt > cap) {
+                atomicOr(&st[s].overflow, 1u);
+                ovf[atomicAdd(&hdr->n_overflow, 1u)] = static_cast<uint32_t>(w);
+            }
+            if (nf && nonfinite) atomicAdd(nonfinite, nf);
+        }
+        grp = P.group_begin + static_cast<int32_t>(rl / kGroup);
+    }
+    // Group totals: one global atomic per group and block instead of one per
+    // region.  The 256 regions of a group run on blocks of every XCD, so their
+    // atomics meet at one address outside the L2s and are applied one after
+    // another; per region, that queue outlasted the stream by ~50 us.
+    if (lane() == 0) {
+        lcnt[threadIdx.x / kWave] = cnt;
+        lgrp[threadIdx.x / kWave] = cnt ? grp : -1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t g0 = -1;
+        uint32_t sum = 0;
+        for (int i = 0; i < kStreamWaves; ++i) {
+            if (lgrp[i] < 0) continue;
+            if (lgrp[i] != g0) {
+                if (sum) atomicAdd(&grp_cnt[g0], sum);
+                g0 = lgrp[i];
+                sum = 0;
+            }
+            sum += lcnt[i];
+        }
+        if (sum) atomicAdd(&grp_cnt[g0], sum);
     }
 }
 
