@@ -52,8 +52,9 @@ extern "C" {
 #define EF_EHIP 3     /* the HIP runtime rejected a launch                        */
 #define EF_ENOTIMPL 4 /* entry point not available in this build                  */
 
-/* Debug flag for the top-k calls: take the exact full-pass selection path for
- * every tensor even when the sampled candidate path would have succeeded. */
+/* Debug flag: take each call's exact fallback path even when its faster path
+ * would have succeeded (top-k: the full-pass selection for every tensor;
+ * random sparsification: see ef_random_sparsify).  Results do not change. */
 #define EF_FLAG_FORCE_FALLBACK 1u
 
 /* Message describing the last error returned on the calling thread. */
