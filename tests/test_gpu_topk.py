@@ -207,6 +207,40 @@ def test_segmented_ragged(kind):
     seg_check(sizes, ks, 4, kind, flags=efg.EF_FLAG_FORCE_FALLBACK)
 
 
+def seg_check_arrays(g, e, sizes, ks, what):
+    dev = device()
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    ed = to_dev(e, dev)
+    v, i = efg.ef_topk_compress_segmented(to_dev(g, dev), ed, off, ks)
+    ov, oi, oe, _ = oracle.topk_segmented(g, e, off, ks)
+    assert_bits_equal(host(i), oi, f"seg idx {what}")
+    assert_bits_equal(host(v), ov, f"seg vals {what}")
+    assert_bits_equal(host(ed), oe, f"seg e {what}")
+
+
+def test_segmented_crowded_regions():
+    """Several tensors, some with crowded regions (their slots overflow and are
+    read again), one whose sample sees only small values (more candidates than
+    its slots: the exact fallback), and plain ones, in one call: each tensor's
+    dense list sits at its own base."""
+    sizes = [100_003, 2_000_000, 50_000, 3_000_017, 2_000_000, 700_001]
+    parts, es = [], []
+    for t, m in enumerate(sizes):
+        x = gen.normal_small(m, 130, t, scale=1e-3)
+        if t == 1:
+            x[400_000:440_000] = gen.normal_small(40_000, 131, t, scale=5.0)
+        if t == 3:
+            x[5:20_005] = gen.normal_small(20_000, 132, t, scale=5.0)
+            x[-30_000:] = np.float32(3.0)
+        if t == 4:
+            x = np.where(sampled_chunk_mask(m), x, np.float32(1.0)).astype(np.float32)
+        parts.append(x)
+        es.append(gen.normal_small(m, 133, t, scale=1e-4))
+    g, e = np.concatenate(parts), np.concatenate(es)
+    for ks in ([1000, 20_000, 500, 30_000, 2000, 7000], [100, 5000, 1, 25_000, 20_000, 70_000]):
+        seg_check_arrays(g, e, sizes, np.array(ks, np.int64), f"ks={ks}")
+
+
 def test_segmented_many_small():
     r = gen.rng(130)
     sizes = r.integers(1, 3000, size=700).tolist()
