@@ -143,6 +143,7 @@ struct Plan {
     int64_t G = 0;      // region groups
     int64_t SB = 0;     // sample blocks
     int32_t sample_rounds = 1;  // groups of kSampleBlockChunks chunks per sample block
+    int32_t hcopies = 1;        // copies of each radix histogram (blocks add to copy blockIdx % hcopies)
     int64_t QR = 0;     // raw chunks (fallback units)
     int64_t QC = 0;     // bound on candidate chunks
     int64_t Ctot = 0;   // candidate slot entries
@@ -175,7 +176,7 @@ static Layout make_layout(const Plan& p) {
     L.header = take(sizeof(Header));
     L.state = take(ns * sizeof(SegState));
     L.shist = take(ns * kSampleBins * 4);
-    L.rhist = take(ns * kRadixBins * 4);
+    L.rhist = take(3 * ns * static_cast<size_t>(p.hcopies) * kRadixBins * 4);
     L.grp_cnt = take(static_cast<size_t>(p.G) * 4);
     L.zero_end = at;
     L.ccb = take((ns + 1) * 4);
@@ -294,6 +295,11 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
     // Sample blocks: many small tensors would otherwise give thousands of blocks,
     // each clearing and flushing a whole 4096-bin histogram; beyond about
     // kSampleBlocksTarget blocks every block takes several chunk groups.
+    // A tensor's compaction and histogram blocks run on every XCD; their
+    // atomics on one histogram meet beyond the L2s and are applied in turn.
+    // With few tensors (few histograms, many blocks each) every histogram gets
+    // eight copies; with many, the blocks per tensor are few anyway.
+    p.hcopies = nseg <= 8 ? 8 : 1;
     p.sample_rounds = static_cast<int32_t>(std::min<int64_t>(
         kSampleRoundsMax, std::max<int64_t>(1, cdiv(p.SB, static_cast<int64_t>(kSampleBlockChunks) * kSampleBlocksTarget))));
     p.SB = 0;
@@ -730,6 +736,13 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_groups(const SegPlan* __res
     }
 }
 
+// Radix histogram of pass p (0..2) of tensor s, copy c: each pass has its own
+// histograms, cleared by k_init, so no kernel has to clear one after use.
+__device__ __forceinline__ uint32_t* radix_hist(uint32_t* rhist, int pass, int s, int c, int32_t nseg,
+                                                int32_t hcopies) {
+    return rhist + ((static_cast<size_t>(pass) * nseg + s) * hcopies + c) * kRadixBins;
+}
+
 // 4. per group of regions: candidate slots -> dense index-ordered list, and the
 //    first radix histogram (top 11 key bits) of the tensor.  A tensor with many
 //    candidates per group shares each group among compact_split blocks: every
@@ -743,7 +756,7 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
                                                     const uint32_t* __restrict__ grp_off,
                                                     const uint2* __restrict__ cpair, float* __restrict__ dval,
                                                     int32_t* __restrict__ didx, uint32_t* __restrict__ rhist,
-                                                    float* __restrict__ e) {
+                                                    int32_t hcopies, float* __restrict__ e) {
     __shared__ uint32_t loff[kGroup];
     __shared__ uint32_t h[kRadixBins];
     __shared__ uint32_t lds[kWavesPerBlock + 1];
@@ -802,7 +815,7 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     }
     __syncthreads();
     if (q1 > q0) {
-        uint32_t* gh = rhist + static_cast<size_t>(s) * kRadixBins;
+        uint32_t* gh = radix_hist(rhist, 0, s, b % hcopies, nseg, hcopies);
         for (int i = t; i < kRadixBins; i += kBlock)
             if (h[i]) atomicAdd(&gh[i], h[i]);
     }
@@ -830,7 +843,7 @@ __global__ __launch_bounds__(kBlock) void k_recollect(const SegPlan* __restrict_
                                                       const uint2* __restrict__ cpair, const Header* __restrict__ hdr,
                                                       const uint32_t* __restrict__ ovf, float* __restrict__ e,
                                                       float* __restrict__ dval, int32_t* __restrict__ didx,
-                                                      uint32_t* __restrict__ rhist) {
+                                                      uint32_t* __restrict__ rhist, int32_t hcopies) {
     __shared__ uint32_t lh[kWavesPerBlock][kRadixBins];
     const uint32_t nov = hdr->n_overflow;
     const int l = lane();
@@ -880,7 +893,7 @@ __global__ __launch_bounds__(kBlock) void k_recollect(const SegPlan* __restrict_
                 pos += popc64(bal);
             }
         }
-        uint32_t* gh = rhist + static_cast<size_t>(s) * kRadixBins;
+        uint32_t* gh = radix_hist(rhist, 0, s, blockIdx.x % hcopies, nseg, hcopies);
         for (int i = l; i < kRadixBins; i += kWave)
             if (h[i]) atomicAdd(&gh[i], h[i]);
     }
@@ -951,7 +964,8 @@ __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __rest
                                                  const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
                                                  const int32_t* __restrict__ rcb, int64_t QR,
                                                  const Header* __restrict__ hdr, const float* __restrict__ dval,
-                                                 const float* __restrict__ e, uint32_t* __restrict__ rhist) {
+                                                 const float* __restrict__ e, uint32_t* __restrict__ rhist,
+                                                 int32_t hcopies) {
     __shared__ uint32_t h[kRadixBins];
     const int64_t Qc = pass > 0 ? hdr->total_cchunks : 0;
     const int64_t Q = Qc + (hdr->any_fallback ? QR : 0);
@@ -968,7 +982,7 @@ __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __rest
             if (radix_digit(pass, key_of(u.v[j]), prefix, &d)) atomicAdd(&h[d], 1u);
         }
         __syncthreads();
-        uint32_t* gh = rhist + static_cast<size_t>(u.s) * kRadixBins;
+        uint32_t* gh = radix_hist(rhist, pass, u.s, blockIdx.x % hcopies, nseg, hcopies);
         for (int i = threadIdx.x; i < nb; i += kBlock) {
             if (h[i]) atomicAdd(&gh[i], h[i]);
             h[i] = 0;
@@ -978,21 +992,35 @@ __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __rest
 }
 
 // 5b. fix one digit per tensor
-__global__ __launch_bounds__(kBlock) void k_digit(int pass, const SegPlan* __restrict__ plan,
-                                                  SegState* __restrict__ st, uint32_t* __restrict__ rhist) {
+__global__ __launch_bounds__(kBlock) void k_digit(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
+                                                  SegState* __restrict__ st, const uint32_t* __restrict__ rhist,
+                                                  int32_t hcopies) {
     __shared__ uint32_t lds[kWavesPerBlock + 1];
+    __shared__ uint4 hsum[kRadixBins / 4];
     const int s = blockIdx.x;
     if (plan[s].mode != MODE_NORMAL) return;
     const int nb = pass == 0 ? 2048 : 1024;
-    uint32_t* gh = rhist + static_cast<size_t>(s) * kRadixBins;
+    // the tensor's histogram of this pass is the sum of its copies
+    const uint4* gh = reinterpret_cast<const uint4*>(radix_hist(const_cast<uint32_t*>(rhist), pass, s, 0, nseg, hcopies));
+    for (int i = threadIdx.x; i < nb / 4; i += kBlock) {
+        uint4 v = gh[i];
+        for (int c = 1; c < hcopies; ++c) {
+            const uint4 w = gh[c * (kRadixBins / 4) + i];
+            v.x += w.x;
+            v.y += w.y;
+            v.z += w.z;
+            v.w += w.w;
+        }
+        hsum[i] = v;
+    }
+    __syncthreads();
+    const uint32_t* hs = reinterpret_cast<const uint32_t*>(hsum);
     const uint32_t want = st[s].want;
     const uint32_t prefix = st[s].prefix;
     int d;
     uint32_t above;
-    const bool f = pass == 0 ? find_rank_bin<2048 / kBlock>(gh, want, &d, &above, lds)
-                             : find_rank_bin<1024 / kBlock>(gh, want, &d, &above, lds);
-    __syncthreads();
-    for (int i = threadIdx.x; i < nb; i += kBlock) gh[i] = 0;
+    const bool f = pass == 0 ? find_rank_bin<2048 / kBlock>(hs, want, &d, &above, lds)
+                             : find_rank_bin<1024 / kBlock>(hs, want, &d, &above, lds);
     if (f) {
         const uint32_t np = pass == 0 ? static_cast<uint32_t>(d) : ((prefix << 10) | static_cast<uint32_t>(d));
         st[s].prefix = np;
@@ -1335,19 +1363,21 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     EF_TRY(launch("topk_compact", k_compact, dim3(static_cast<unsigned>(P.CB)), dim3(kBlock), s, plan, nseg,
                   static_cast<const int32_t*>(reinterpret_cast<int32_t*>(at(L.cbb))), gbb, rb,
                   static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
-                  static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair), dval, didx, rhist, e));
+                  static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair), dval, didx, rhist,
+                  P.hcopies, e));
     EF_TRY(launch("topk_recollect", k_recollect, dim3(kRecollectBlocks), dim3(kBlock), s, plan, nseg, rb, gbb,
                   static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
                   static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair),
-                  static_cast<const Header*>(hdr), static_cast<const uint32_t*>(ovf), e, dval, didx, rhist));
+                  static_cast<const Header*>(hdr), static_cast<const uint32_t*>(ovf), e, dval, didx, rhist,
+                  P.hcopies));
     const unsigned gu = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, P.QC + P.QR)));
     for (int pass = 0; pass < 3; ++pass) {
         EF_TRY(launch("topk_hist", k_hist, dim3(gu), dim3(kBlock), s, pass, plan, nseg,
                       static_cast<const SegState*>(st), static_cast<const uint32_t*>(ccb), rcb, P.QR,
                       static_cast<const Header*>(hdr), static_cast<const float*>(dval),
-                      static_cast<const float*>(e), rhist));
-        EF_TRY(launch("topk_digit", k_digit, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, pass, plan, st,
-                      rhist));
+                      static_cast<const float*>(e), rhist, P.hcopies));
+        EF_TRY(launch("topk_digit", k_digit, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, pass, plan, nseg,
+                      st, static_cast<const uint32_t*>(rhist), P.hcopies));
     }
     EF_TRY(launch("topk_count", k_count, dim3(gu), dim3(kBlock), s, plan, nseg, static_cast<const SegState*>(st),
                   static_cast<const uint32_t*>(ccb), rcb, P.QR, static_cast<const Header*>(hdr),
