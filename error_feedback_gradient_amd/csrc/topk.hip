@@ -1107,9 +1107,14 @@ __global__ __launch_bounds__(kBlock) void k_emit_scan(const SegPlan* __restrict_
     }
 }
 
-// 6c. ordered write of the kept entries.  Candidate units also settle the
-// residual of entries the stream cleared early (key >= thi): a kept one keeps
-// e = 0, a dropped one gets x back.
+// 6c. the kept entries at their index-ordered places.  Wave w of a block takes
+//     entries [1024 w, 1024 w + 1024) of the unit, lane l entry 1024 w + 64 i + l
+//     of row i, so loads and (mostly kept-together) stores coalesce.  An entry's
+//     place is (entries with key > T before it) + min(r, entries with key == T
+//     before it): the unit's counts before it (from k_emit_scan), those of the
+//     block's earlier waves, of the wave's earlier rows, and of the row's lower
+//     lanes (ballots).  Kept entries get e = +0 unless the stream cleared them
+//     (key >= thi); dropped ones the stream cleared get x back.
 __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ plan, int32_t nseg,
                                                   const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
                                                   const int32_t* __restrict__ rcb, int64_t QR,
@@ -1119,49 +1124,60 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
                                                   const uint32_t* __restrict__ req, float* __restrict__ e,
                                                   float* __restrict__ vals, int32_t* __restrict__ idx,
                                                   double2* __restrict__ cpart, double2* __restrict__ rpart) {
-    __shared__ uint64_t lds[kWavesPerBlock + 1];
+    constexpr int kRows = kChunk / kBlock;  // rows of 64 entries per wave
+    __shared__ uint32_t wgt[kWavesPerBlock], weq[kWavesPerBlock];
     __shared__ double2 lsum[kWavesPerBlock];
     const int64_t Qc = hdr->total_cchunks;
     const int64_t Q = Qc + (hdr->any_fallback ? QR : 0);
+    const int wv = threadIdx.x / kWave;
+    const int l = lane();
     for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
         const Unit u = unit_of(q, Qc, plan, nseg, st, ccb, rcb, dval, didx, e);
         if (u.skip) continue;
         const uint32_t T = st[u.s].T, r = st[u.s].r;
         const uint32_t thi = u.raw ? kNoKey : st[u.s].thi;
-        const uint32_t G0 = (u.raw ? rgt : cgt)[u.slot], E0 = (u.raw ? req : ceq)[u.slot];
         const int64_t out_off = plan[u.s].out_off, kseg = plan[u.s].k;
         const int64_t seg_lo = plan[u.s].off, seg_hi = plan[u.s].off + plan[u.s].n;
-        const uint32_t j0 = threadIdx.x * kPerThread;
-        float v[kPerThread];
-        uint32_t ngt = 0, neq = 0;
+        const uint32_t w0 = static_cast<uint32_t>(wv) * (kRows * kWave);
+        float v[kRows];
+        uint32_t ngt = 0, neq = 0;  // this wave's counts (wave-uniform)
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            const bool ok = j0 + i < u.cnt;
-            v[i] = ok ? u.v[j0 + i] : 0.0f;
+        for (int i = 0; i < kRows; ++i) {
+            const uint32_t j = w0 + i * kWave + l;
+            const bool ok = j < u.cnt;
+            v[i] = ok ? u.v[j] : 0.0f;
             const uint32_t key = key_of(v[i]);
-            ngt += ok && key > T;
-            neq += ok && key == T;
+            ngt += popc64(__ballot(ok && key > T));
+            neq += popc64(__ballot(ok && key == T));
         }
-        uint64_t tot;
-        const uint64_t before = block_excl_scan<kBlock>((static_cast<uint64_t>(ngt) << 32) | neq, lds, &tot);
-        uint32_t gtb = G0 + static_cast<uint32_t>(before >> 32);
-        uint32_t eqb = E0 + static_cast<uint32_t>(before);
+        if (l == 0) {
+            wgt[wv] = ngt;
+            weq[wv] = neq;
+        }
+        __syncthreads();
+        uint32_t gtb = (u.raw ? rgt : cgt)[u.slot], eqb = (u.raw ? req : ceq)[u.slot];
+        for (int i = 0; i < wv; ++i) {
+            gtb += wgt[i];
+            eqb += weq[i];
+        }
         double sent = 0.0, drop = 0.0;
 #pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            if (j0 + i >= u.cnt) continue;
+        for (int i = 0; i < kRows; ++i) {
+            const uint32_t j = w0 + i * kWave + l;
+            const bool ok = j < u.cnt;
             const uint32_t key = key_of(v[i]);
+            const bool gt = ok && key > T, eq = ok && key == T;
+            const uint64_t bg = __ballot(gt), be = __ballot(eq);
+            const uint32_t g_before = gtb + count_below(bg), e_before = eqb + count_below(be);
+            gtb += popc64(bg);
+            eqb += popc64(be);
+            if (!ok) continue;
             int64_t pos = -1;
-            if (key > T) {
-                pos = static_cast<int64_t>(gtb) + min(r, eqb);
-                ++gtb;
-            } else if (key == T) {
-                if (eqb < r) pos = static_cast<int64_t>(gtb) + eqb;
-                ++eqb;
-            }
+            if (gt) pos = static_cast<int64_t>(g_before) + min(r, e_before);
+            else if (eq && e_before < r) pos = static_cast<int64_t>(g_before) + e_before;
             if (pos >= 0) sent += sq_finite(v[i], key);
             else drop += sq_finite(v[i], key);
-            const int64_t id = u.raw ? u.idx_base + j0 + i : static_cast<int64_t>(u.id[j0 + i]);
+            const int64_t id = u.raw ? u.idx_base + j : static_cast<int64_t>(u.id[j]);
             if (id < seg_lo || id >= seg_hi) continue;  // only if the workspace was overwritten meanwhile
             if (pos >= 0 && pos < kseg) {
                 vals[out_off + pos] = v[i];
@@ -1175,7 +1191,7 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
             // fixed-order block sum of the unit's sent and dropped energy
             sent = wave_sum(sent);
             drop = wave_sum(drop);
-            if (lane() == 0) lsum[threadIdx.x / kWave] = make_double2(sent, drop);
+            if (l == 0) lsum[wv] = make_double2(sent, drop);
             __syncthreads();
             if (threadIdx.x == 0) {
                 double2 t = make_double2(0.0, 0.0);
