@@ -12,12 +12,14 @@
 //                 elements of the tensor above it, and T_hi, with (very
 //                 likely) fewer than k above it.
 //   2. stream     ONE pass over the tensor, one wave per 4096 elements: read
-//                 g and e (128-bit non-temporal loads, 8 in flight per lane
-//                 and array), write e (128-bit stores), and append every
-//                 element with key >= T_lo to the wave's candidate slot, in
-//                 index order, with wave ballots.  Candidates with key >= T_hi
-//                 are almost surely kept, so the stream already writes e = 0
-//                 for them.  This is the only full pass: 12 bytes/element.
+//                 g and e (128-bit non-temporal loads, all 16 of the region in
+//                 flight per lane and array), write e (128-bit stores), and
+//                 append every element with key >= T_lo to the wave's
+//                 candidate slot, in index order, with wave ballots.
+//                 Candidates with key >= T_hi are almost surely kept, so the
+//                 stream already writes e = 0 for them.  Each block adds its
+//                 regions' candidate counts to their group totals with one
+//                 atomic per group.  This is the only full pass: 12 B/element.
 //   3. scan       per-tensor candidate totals from per-group counts (true
 //                 counts: a region may have more candidates than its slot
 //                 holds); a tensor drops to the exact fallback when its
