@@ -1309,15 +1309,23 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
         memcpy(h + L.rcb, P.rcb.data(), P.rcb.size() * 4);
         memcpy(h + L.cbb, P.cbb.data(), P.cbb.size() * 4);
     }
-    // small plans (one tensor) ride on k_init's arguments; larger ones take one
-    // copy through the pinned staging ring
+    // Small plans (up to 11 tensors) ride on k_init's arguments.  Larger ones
+    // take one copy through the pinned staging ring, except under HIP graph
+    // capture: a captured copy would read the ring slot again at every replay,
+    // after later calls reused it, so there the plan goes in kernel-argument
+    // chunks of kWordChunk words, which the graph keeps by value.
     WordChunk first;
     first.n = 0;
     if (words.size() <= kWordChunk) {
         first.n = static_cast<uint32_t>(words.size());
         memcpy(first.w, words.data(), first.n * 4);
     } else {
-        EF_TRY(upload_bytes(W, words.data(), words.size() * 4, s));
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess) return fail(EF_EHIP, "stream capture query failed");
+        if (cs == hipStreamCaptureStatusActive)
+            EF_TRY(upload_words(W, words.data(), words.size(), s));
+        else
+            EF_TRY(upload_bytes(W, words.data(), words.size() * 4, s));
     }
     const int64_t nzero = static_cast<int64_t>((L.zero_end - L.header) / 16);
     const unsigned zgrid = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, cdiv(nzero, kBlock))));

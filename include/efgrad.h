@@ -27,10 +27,10 @@
  *    (overwritten by each call).
  *  - HIP graph capture: with ef_profile_enable off, every call only launches
  *    kernels (no memset, no host wait), so a captured call replays exactly
- *    like the eager one.  The exception is ef_topk_compress_segmented with more
- *    than 13 tensors: its per-call plan no longer fits kernel arguments and is
- *    copied from a pinned host buffer that the library reuses, so such calls
- *    must not be captured.
+ *    like the eager one.  ef_topk_compress_segmented with more than 11 tensors
+ *    copies its per-call plan from a pinned host buffer when called eagerly;
+ *    under capture it passes the plan in kernel arguments instead (one small
+ *    launch per 500 words, about 17 tensors), so captured calls are safe too.
  *
  * Sources cited below ("pages"):
  *   [SPARSE] "梯度稀疏化：只传输重要的梯度元素" — gradient sparsification.

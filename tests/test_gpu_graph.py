@@ -1,6 +1,8 @@
 """Steps of the library captured in HIP graphs (torch.cuda.graph) replay bit
 for bit like the same calls made eagerly: single-tensor top-k with block
-encoding, sign compression, random sparsification and the 1-bit Adam update.
+encoding, layer-wise top-k calls over 12 and 60 tensors (whose plans go in
+kernel-argument chunks under capture), sign compression, random
+sparsification and the 1-bit Adam update.
 Every call launches kernels only (no memset or host-staged copies for these
 shapes), so capture records the whole step.  Each replay is followed by some
 eager work and a synchronisation before it is checked."""
@@ -78,6 +80,29 @@ def test_topk_and_blocks_in_a_graph():
 
     state = [torch.zeros(n, device=dev)]
     assert run_chain(step, state, lambda: [vals, idx, mask, counts[:int(nblk.item())], offs, nblk], dev)
+
+
+@pytest.mark.parametrize("layout", ["12 tensors", "60 tensors"])
+def test_layerwise_topk_in_a_graph(layout):
+    """Plans of 512 words and of about 2,700 words (six kernel-argument chunks
+    under capture)."""
+    dev = device()
+    if layout == "12 tensors":
+        sizes = [768, 3072, 100_003, 768, 250_000, 4096, 77, 590_000, 768, 3072, 200_001, 33]
+    else:
+        sizes = [int(m) for m in gen.rng(141).integers(1, 60_000, size=60)]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    ks = np.array([max(1, m // 100) for m in sizes], np.int64)
+    n, K = int(off[-1]), int(ks.sum())
+    grads = [torch.from_numpy(gen.normal_small(n, 140, t)).to(dev) for t in range(T)]
+    ws = efg.workspace(efg.ef_topk_segmented_workspace_bytes(off, ks), dev)
+    vals = torch.empty(K, device=dev)
+    idx = torch.empty(K, dtype=torch.int32, device=dev)
+
+    def step(t, st):
+        efg.ef_topk_compress_segmented(grads[t], st[0], off, ks, vals=vals, idx=idx, ws=ws)
+
+    assert run_chain(step, [torch.zeros(n, device=dev)], lambda: [vals, idx], dev)
 
 
 def test_sign_random_and_onebit_in_graphs():
