@@ -56,11 +56,15 @@ namespace rs {
 
 // Shapes measured on MI355X (sweep over blocks 256-1024, regions 2048-8192,
 // unrolls 4-16): the streaming passes work on regions of EFG_RS_REGION
-// elements per wave; k_rs_accum issues all EFG_RS_ACC_UNROLL float4 loads of
-// g and e of a region at once.  With the draws, k_rs_accum is about 60% busy
-// on the vector ALU (Philox: 20 64-bit multiply-adds per 4 elements); halving
-// the unroll (4 waves per SIMD instead of 2) or capping registers for 3 waves
-// measured no faster.
+// elements per wave; k_rs_accum issues EFG_RS_ACC_UNROLL float4 loads of g
+// and of e at once, then draws their Philox words while the loads are in
+// flight (the draws depend on the index only), then uses both.  Philox is 20
+// 64-bit multiply-adds per 4 elements; hidden under the loads' latency that
+// way, with 8 loads per array (150 VGPRs, 3 waves per SIMD), the pass costs
+// 2.57 ms at N = 1.3e9 against 2.75 ms when each float4's draw followed its
+// data (16 loads per array, 2 waves per SIMD; 16 with the draws first spills).
+// Without the draws (calls that take the second pass) 16 loads per array stay
+// best: EFG_RS_PLAIN_UNROLL.
 #ifndef EFG_RS_BLOCK
 #define EFG_RS_BLOCK 512
 #endif
@@ -68,7 +72,10 @@ namespace rs {
 #define EFG_RS_REGION 4096
 #endif
 #ifndef EFG_RS_ACC_UNROLL
-#define EFG_RS_ACC_UNROLL 16
+#define EFG_RS_ACC_UNROLL 8
+#endif
+#ifndef EFG_RS_PLAIN_UNROLL
+#define EFG_RS_PLAIN_UNROLL 16
 #endif
 #ifndef EFG_RS_MARK_UNROLL
 #define EFG_RS_MARK_UNROLL 4
@@ -76,14 +83,16 @@ namespace rs {
 constexpr int kBlock = EFG_RS_BLOCK;
 constexpr int kWaves = kBlock / kWave;
 constexpr int kRegion = EFG_RS_REGION;
-constexpr int kUnroll = EFG_RS_ACC_UNROLL;
+constexpr int kUnroll = EFG_RS_ACC_UNROLL;         // k_rs_accum with the draws
+constexpr int kPlainUnroll = EFG_RS_PLAIN_UNROLL;  // k_rs_accum without them
 constexpr int kMarkUnroll = EFG_RS_MARK_UNROLL;
 constexpr int kRegionWords = kRegion / 32;  // bitmap words per region
 constexpr int kWordsPerLane = kRegionWords / kWave;
 constexpr int kSlot = kWave;                // candidate entries per region: one per lane in k_rs_filter
 static_assert(kRegion % 2048 == 0 && kRegion <= 8192,
               "a region is whole 32-bit words of 4-element lanes, 1 to 4 words per lane in k_rs_write");
-static_assert(kRegion % (4 * kWave * kUnroll) == 0 && kWaves <= 16 && kRegion / kWave / 4 <= 32,
+static_assert(kRegion % (4 * kWave * kUnroll) == 0 && kRegion % (4 * kWave * kPlainUnroll) == 0 && kWaves <= 16 &&
+                  kRegion / kWave / 4 <= 32,
               "the float64 error bound of k_rs_total counts at most 32 additions per lane accumulator, "
               "16 waves per block and 2^18 block partials");
 static_assert(kRegionWords * 4 >= kSlot * 8, "a region's candidate slot fits in its bitmap slice");
@@ -249,17 +258,31 @@ __global__ __launch_bounds__(kBlock) void k_rs_accum(const float* __restrict__ g
         };
         auto iteration = [&](int64_t base, auto guard) {
             constexpr bool GUARD = decltype(guard)::value;
-            f4 gv[kUnroll], ev[kUnroll];
+            constexpr int kU = SPEC ? kUnroll : kPlainUnroll;
+            f4 gv[kU], ev[kU];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+            for (int u = 0; u < kU; ++u) {
                 const int64_t j = base + u * kWave + l;
                 if (!GUARD || j < nfull) {
                     gv[u] = __builtin_nontemporal_load(g4 + j);
                     ev[u] = __builtin_nontemporal_load(e4 + j);
                 }
             }
+            // the draws depend on the index only: computed while the loads are in flight
+            uint32_t pw[kU][4];
+            if (spec) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
+                for (int u = 0; u < kU; ++u) {
+                    uint32_t c0 = q0 + static_cast<uint32_t>(base + u * kWave + l), c1 = 0u, c2 = step0, c3 = step1;
+                    philox(c0, c1, c2, c3, key0, key1);
+                    pw[u][0] = c0;
+                    pw[u][1] = c1;
+                    pw[u][2] = c2;
+                    pw[u][3] = c3;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
                 const int64_t j = base + u * kWave + l;
                 f4 x = f4{0.f, 0.f, 0.f, 0.f};
                 int valid = 4;  // components of this float4 inside the tensor
@@ -290,10 +313,8 @@ __global__ __launch_bounds__(kBlock) void k_rs_accum(const float* __restrict__ g
                     valid = 0;
                 }
                 if (spec) {
-                    uint32_t c0 = q0 + static_cast<uint32_t>(j), c1 = 0u, c2 = step0, c3 = step1;
-                    philox(c0, c1, c2, c3, key0, key1);
                     const float xs[4] = {x.x, x.y, x.z, x.w};
-                    const uint32_t ws[4] = {c0, c1, c2, c3};
+                    const uint32_t ws[4] = {pw[u][0], pw[u][1], pw[u][2], pw[u][3]};
                     bool hit[4];
                     uint64_t bal[4], any = 0;
 #pragma unroll
@@ -324,7 +345,7 @@ __global__ __launch_bounds__(kBlock) void k_rs_accum(const float* __restrict__ g
                 }
             }
         };
-        constexpr int64_t kStep = kWave * kUnroll;
+        constexpr int64_t kStep = kWave * (SPEC ? kUnroll : kPlainUnroll);
         int64_t base = 0;
         for (; base + kStep <= nfull; base += kStep) iteration(base, std::false_type{});
         if (base < nv) iteration(base, std::true_type{});
