@@ -122,7 +122,7 @@ static_assert(sizeof(SegPlan) == 112, "SegPlan layout");
 struct alignas(16) SegState {
     uint32_t tlo;       // keys >= tlo become candidates
     uint32_t thi;       // stored candidates with key >= thi get e = 0 in the stream
-    uint32_t overflow, fallback;
+    uint32_t spare, fallback;
     uint32_t ncand, dense_off, cchunk_begin, cchunks;
     uint32_t prefix, want, T, r;
     uint32_t group_base;  // the tensor's first group offset (dense list position = dense_off + grp_off - group_base)
@@ -612,11 +612,12 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
                                                          int32_t* __restrict__ idx, uint32_t* __restrict__ nonfinite,
                                                          double2* __restrict__ spart, Header* __restrict__ hdr,
                                                          uint32_t* __restrict__ ovf) {
-    __shared__ uint32_t lcnt[kStreamWaves];
+    __shared__ uint32_t lcnt[kStreamWaves], lovf[kStreamWaves];
     __shared__ int32_t lgrp[kStreamWaves];
     const int64_t w = static_cast<int64_t>(blockIdx.x) * kStreamWaves + threadIdx.x / kWave;
     uint32_t cnt = 0;
     int32_t grp = -1;
+    bool ovfl = false;
     if (w < R) {
         const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
         const SegPlan& P = plan[s];
@@ -647,27 +648,26 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
         if (lane() == 0) {
             // the true count: the slot holds the first min(cnt, cap) candidates
             region_cnt[w] = cnt;
-            if (cnt > cap) {
-                atomicOr(&st[s].overflow, 1u);
-                ovf[atomicAdd(&hdr->n_overflow, 1u)] = static_cast<uint32_t>(w);
-            }
             if (nf && nonfinite) atomicAdd(nonfinite, nf);
         }
         grp = P.group_begin + static_cast<int32_t>(rl / kGroup);
+        ovfl = cnt > cap;
     }
-    // Group totals: one global atomic per group and block instead of one per
-    // region.  The 256 regions of a group run on blocks of every XCD, so their
-    // atomics meet at one address outside the L2s and are applied one after
-    // another; per region, that queue outlasted the stream by ~50 us.
+    // Group totals and the overflow list: global atomics per block instead of
+    // per region.  The 256 regions of a group run on blocks of every XCD, so
+    // their atomics meet at one address outside the L2s and are applied one
+    // after another; per region, that queue outlasted the stream by ~50 us.
     if (lane() == 0) {
         lcnt[threadIdx.x / kWave] = cnt;
         lgrp[threadIdx.x / kWave] = cnt ? grp : -1;
+        lovf[threadIdx.x / kWave] = ovfl ? 1u : 0u;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         int32_t g0 = -1;
-        uint32_t sum = 0;
+        uint32_t sum = 0, nov = 0;
         for (int i = 0; i < kStreamWaves; ++i) {
+            nov += lovf[i];
             if (lgrp[i] < 0) continue;
             if (lgrp[i] != g0) {
                 if (sum) atomicAdd(&grp_cnt[g0], sum);
@@ -677,6 +677,13 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
             sum += lcnt[i];
         }
         if (sum) atomicAdd(&grp_cnt[g0], sum);
+        if (nov) {
+            // overflowed regions of this block (in any order: each is read again on its own)
+            uint32_t at = atomicAdd(&hdr->n_overflow, nov);
+            const int64_t w0 = w - threadIdx.x / kWave;  // this block's first region
+            for (int i = 0; i < kStreamWaves; ++i)
+                if (lovf[i]) ovf[at++] = static_cast<uint32_t>(w0 + i);
+        }
     }
 }
 
