@@ -95,7 +95,7 @@ constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
 #define EFG_CHUNK 4096
 #endif
 constexpr int kChunk = EFG_CHUNK;                  // entries per block-unit in select and emit
-static_assert(kChunk % (kBlock * kWave) == 0, "whole rows of 64 entries per wave in k_write");
+static_assert(kChunk % kBlock == 0, "k_write: each wave takes kChunk / kBlock rows of 64 entries");
 constexpr int kRadixBins = 2048;
 constexpr int kMaxGrid = 2048;
 constexpr uint32_t kNoKey = 0xffffffffu;           // above every 31-bit key
