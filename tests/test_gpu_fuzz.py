@@ -1,0 +1,193 @@
+"""Seeded randomized parity: many small random configurations of every call,
+each compared bit for bit with the CPU oracle.  Sizes, k, value laws (normal,
+log-normal, few distinct magnitudes, all equal, salted with Inf/NaN/±0/
+subnormals, crowded into one stretch), residuals, segment layouts and seeds are
+drawn from one seeded generator, so a failure names a reproducible case.  The
+hand-picked cases elsewhere cover the known edges; this sweep covers the
+combinations between them (ragged tails at odd sizes, k near the ends, short
+tensors inside long layouts)."""
+import numpy as np
+import pytest
+import torch
+
+import error_feedback_gradient_amd as efg
+import gen
+import oracle
+from gpu_util import assert_bits_equal, device, host, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def values(r, n, kind):
+    if kind == "normal":
+        return r.standard_normal(n, dtype=np.float32)
+    if kind == "lognormal":
+        x = np.exp(r.standard_normal(n) * 2.0 - 3.0).astype(np.float32)
+        return np.where(r.integers(0, 2, n) == 1, x, -x).astype(np.float32)
+    if kind == "levels":
+        return (r.integers(-4, 5, n).astype(np.float32) * np.float32(0.5))
+    if kind == "equal":
+        return np.full(n, np.float32(1.25))
+    if kind == "specials":
+        x = r.standard_normal(n, dtype=np.float32)
+        pool = np.array([0.0, -0.0, 1e-45, -1e-40, np.inf, -np.inf, np.nan, 3.4e38], np.float32)
+        pick = r.random(n) < 0.02
+        x[pick] = pool[r.integers(0, pool.size, int(pick.sum()))]
+        return x
+    if kind == "crowded":
+        x = (r.standard_normal(n) * 1e-3).astype(np.float32)
+        if n > 8:
+            a = int(r.integers(0, n))
+            b = min(n, a + int(r.integers(1, max(2, n // 4))))
+            x[a:b] = (r.standard_normal(b - a) * 10).astype(np.float32)
+        return x
+    raise ValueError(kind)
+
+
+KINDS = ["normal", "lognormal", "levels", "equal", "specials", "crowded"]
+
+
+def draw_n(r):
+    # mostly small, some across many regions, a few with odd tails
+    c = r.random()
+    if c < 0.4:
+        return int(r.integers(1, 5000))
+    if c < 0.8:
+        return int(r.integers(5000, 300_000))
+    return int(r.integers(300_000, 2_500_000))
+
+
+def draw_k(r, n):
+    c = r.random()
+    if c < 0.1:
+        return 0
+    if c < 0.2:
+        return n
+    if c < 0.3:
+        return max(0, n - int(r.integers(0, 3)))
+    if c < 0.45:
+        return int(r.integers(1, 4))
+    return max(1, int(n * 10 ** r.uniform(-3.5, -0.5)))
+
+
+@pytest.mark.parametrize("case", range(400))
+def test_topk_random_cases(case):
+    r = np.random.default_rng([2024, 1, case])
+    n = draw_n(r)
+    k = min(n, draw_k(r, n))
+    kind = KINDS[int(r.integers(0, len(KINDS)))]
+    g = values(r, n, kind)
+    e = values(r, n, "normal") * np.float32(r.choice([0.0, 1e-3, 1.0]))
+    flags = efg.EF_FLAG_FORCE_FALLBACK if r.random() < 0.15 else 0
+    what = f"case {case}: n={n} k={k} {kind} flags={flags}"
+    say(what)
+    dev = device()
+    ed = to_dev(e, dev)
+    nf = torch.zeros(1, dtype=torch.int32, device=dev)
+    v, i = efg.ef_topk_compress(to_dev(g, dev), ed, k, nonfinite=nf, flags=flags)
+    ov, oi, oe, onf = oracle.topk(g, e, k)
+    assert_bits_equal(host(i)[:k], oi, f"idx {what}")
+    assert_bits_equal(host(v)[:k], ov, f"vals {what}")
+    assert_bits_equal(host(ed), oe, f"e {what}")
+    assert int(host(nf)[0]) == onf, what
+
+
+@pytest.mark.parametrize("case", range(200))
+def test_segmented_random_cases(case):
+    r = np.random.default_rng([2024, 2, case])
+    nseg = int(r.integers(1, 40))
+    sizes = [int(r.choice([0, 1, 3, int(r.integers(1, 3000)), int(r.integers(3000, 150_000))])) for _ in range(nseg)]
+    ks = [min(m, draw_k(r, m)) if m > 0 else 0 for m in sizes]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(off[-1])
+    kind = KINDS[int(r.integers(0, len(KINDS)))]
+    g = values(r, n, kind)
+    e = values(r, n, "normal") * np.float32(r.choice([0.0, 1e-3]))
+    what = f"case {case}: {nseg} tensors, n={n}, K={sum(ks)} {kind}"
+    say(what)
+    dev = device()
+    ed = to_dev(e, dev)
+    v, i = efg.ef_topk_compress_segmented(to_dev(g, dev), ed, off, np.array(ks, np.int64))
+    ov, oi, oe, _ = oracle.topk_segmented(g, e, off, np.array(ks, np.int64))
+    K = int(sum(ks))
+    assert_bits_equal(host(i)[:K], oi, f"idx {what}")
+    assert_bits_equal(host(v)[:K], ov, f"vals {what}")
+    assert_bits_equal(host(ed), oe, f"e {what}")
+
+
+@pytest.mark.parametrize("case", range(300))
+def test_random_sparsify_random_cases(case):
+    r = np.random.default_rng([2024, 3, case])
+    n = draw_n(r)
+    k = int(r.choice([0, 1, max(1, n // 5000), max(1, n // 600), max(1, n // 50), n, 2 * n]))
+    kind = KINDS[int(r.integers(0, len(KINDS)))]
+    g = values(r, n, kind)
+    e = values(r, n, "normal") * np.float32(r.choice([0.0, 1e-3]))
+    seed, step = int(r.integers(0, 2**63)), int(r.integers(0, 2**40))
+    cap = int(r.choice([2 * k + 64, max(0, k // 2), 0]))
+    flags = efg.EF_FLAG_FORCE_FALLBACK if r.random() < 0.2 else 0
+    what = f"case {case}: n={n} k={k} {kind} cap={cap} flags={flags}"
+    say(what)
+    dev = device()
+    ed = to_dev(e, dev)
+    s32 = torch.empty(1, dtype=torch.float32, device=dev)
+    nf = torch.zeros(1, dtype=torch.int32, device=dev)
+    vals, idx, cnt = efg.ef_random_sparsify(to_dev(g, dev), ed, k, seed, step, cap=cap, sum_out=s32, nonfinite=nf,
+                                            flags=flags)
+    ov, oi, oe, oc, os32, onf = oracle.random_sparsify(g, e, k, seed, step, cap)
+    c = int(host(cnt)[0])
+    assert c == oc, (what, c, oc)
+    w = min(c, cap)
+    assert_bits_equal(host(idx)[:w], oi, f"idx {what}")
+    assert_bits_equal(host(vals)[:w], ov, f"vals {what}")
+    assert_bits_equal(host(ed), oe, f"e {what}")
+    assert np.float32(host(s32)[0]).view(np.uint32) == np.float32(os32).view(np.uint32), what
+    assert int(host(nf)[0]) == onf, what
+
+
+@pytest.mark.parametrize("case", range(200))
+def test_sign_quant_and_encodings_random_cases(case):
+    r = np.random.default_rng([2024, 4, case])
+    n = draw_n(r)
+    kind = KINDS[int(r.integers(0, len(KINDS)))]
+    dev = device()
+    # sign EF with and without momentum
+    g = values(r, n, kind)
+    e = values(r, n, "normal") * np.float32(1e-3)
+    m = values(r, n, "normal") * np.float32(1e-2) if r.random() < 0.7 else None
+    beta1 = float(r.choice([0.0, 0.5, 0.9, 0.999]))
+    clip = float(r.choice([5.0, 0.5, np.inf]))
+    what = f"case {case}: n={n} {kind} beta1={beta1} clip={clip} m={'yes' if m is not None else 'no'}"
+    say(what)
+    ed = to_dev(e, dev)
+    md = to_dev(m, dev) if m is not None else None
+    s, b = efg.ef_sign_compress(to_dev(g, dev), ed, md, beta1, clip)
+    oe, om, osg, ob, _ = oracle.sign(g, e, m, beta1, clip)
+    assert_bits_equal(host(ed), oe, f"sign e {what}")
+    if m is not None:
+        assert_bits_equal(host(md), om, f"sign m {what}")
+    assert_bits_equal(host(s), osg, f"sign q {what}")
+    assert_bits_equal(host(b), ob, f"sign bits {what}")
+    # a sorted index set of this size, its encodings, and 8-bit values on it
+    k = min(n, max(1, int(n * 10 ** r.uniform(-3, -0.3))))
+    idx = np.sort(r.choice(n, size=k, replace=False)).astype(np.int32)
+    idd = to_dev(idx, dev)
+    assert_bits_equal(host(efg.encode_bitmap(idd, n)), oracle.bitmap_encode(idx, n), f"bitmap {what}")
+    st, nb = efg.encode_delta(idd)
+    ost = oracle.delta_encode(idx)
+    assert int(host(nb)[0]) == ost.size
+    assert_bits_equal(host(st)[:ost.size], ost, f"delta {what}")
+    mask, cm1, offs, nblk = efg.encode_blocks(idd, n)
+    omask, ocm1, ooffs = oracle.blocks_encode(idx, n)
+    assert int(host(nblk)[0]) == ocm1.size
+    assert_bits_equal(host(mask), omask, f"blocks mask {what}")
+    assert_bits_equal(host(cm1)[:ocm1.size], ocm1, f"blocks counts {what}")
+    assert_bits_equal(host(offs)[:k], ooffs, f"blocks offsets {what}")
+    v = values(r, k, kind)
+    e2 = values(r, n, "normal") * np.float32(1e-3)
+    e2d = to_dev(e2, dev)
+    q, sc = efg.ef_quantize_int8(to_dev(v, dev), idd, e2d)
+    oq, osc, oe2 = oracle.quantize_int8(v, idx, e2)
+    assert_bits_equal(host(q)[:k], oq, f"quant q {what}")
+    assert np.float32(host(sc)[0]).view(np.uint32) == np.float32(osc).view(np.uint32), what
+    assert_bits_equal(host(e2d), oe2, f"quant e {what}")
