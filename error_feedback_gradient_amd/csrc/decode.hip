@@ -5,13 +5,19 @@
 // (aggregate, then w = w - lr * G).
 //
 // Decode without float atomics and in packet order: each block owns one tile
-// of 8192 consecutive positions of G (fastest of 1024-16384 on MI355X).  For
-// every packet, 16 lanes search the packet's (ascending) index list together
-// for the entries that land in the tile,
-// stages them in LDS, loads G once for every touched position, adds the
+// of 4096 consecutive positions of G.  For every packet, 16 lanes search the
+// packet's (ascending) index list together for the entries that land in the
+// tile, stage them in LDS, load G once for every touched position, add the
 // packets one after another in LDS (a barrier between packets keeps the
-// order), and writes every touched position back once.  The sum at each index
+// order), and write every touched position back once.  The sum at each index
 // is therefore ((G + v_p0) + v_p1) + ... in packet order, bit for bit.
+// The block's time is a chain of dependent loads (packet bounds, search,
+// entries, G), so what counts is how many blocks a CU holds at once: a 4096
+// tile and 512 staged entries (20 KB of LDS, up to eight blocks per CU) took
+// 48 us on the 16-packet 25.6M workload, against 62 us for 8192 and 2048
+// (45 KB, three per CU); tiles of 2048 to 8192 and stages of 256 to 2048
+// were tried.  A tile whose packets hold more than 512 entries in it takes
+// the slower path that adds them from global memory.
 #include "common.hpp"
 
 namespace efg {
@@ -19,10 +25,13 @@ namespace decode {
 
 constexpr int kBlock = 256;
 #ifndef EFG_DECODE_TILE
-#define EFG_DECODE_TILE 8192
+#define EFG_DECODE_TILE 4096
 #endif
 constexpr int kTile = EFG_DECODE_TILE;               // positions of G per block
-constexpr int kStage = 2048;
+#ifndef EFG_DECODE_STAGE
+#define EFG_DECODE_STAGE 512
+#endif
+constexpr int kStage = EFG_DECODE_STAGE;             // staged entries per packet group (more: the global path)
 constexpr int kSearchLanes = 16;                     // lanes that search one packet together
 constexpr int kPkGroup = kBlock / kSearchLanes;      // packets searched at once per block
 
@@ -44,31 +53,66 @@ __global__ __launch_bounds__(kBlock) void k_validate(int64_t n, const int32_t* _
     if (lane() == 0 && bad) atomicAdd(invalid, bad);
 }
 
-// lower_bound(a[0..len), v) computed by the 16 lanes of one aligned lane group
-// (gl = lane within the group): each round probes the last element of 16
-// equal sub-ranges and keeps the first one that reaches v, so a search takes
-// about log16(len) dependent loads instead of log2(len).  Every lane of the
-// wave must call it (it ballots); inactive groups pass len = 0.  For an
-// unsorted list the result is still some position in [0, len].
-__device__ __forceinline__ int64_t group_lower_bound(const int32_t* a, int64_t len, int64_t v, int gl) {
-    const int shift = threadIdx.x & 48;  // this group's 16 bits of the wave's ballot
-    int64_t L = 0, R = len;
-    while (__any(R - L > kSearchLanes)) {
-        const bool more = R - L > kSearchLanes;
-        const int64_t step = more ? (R - L + kSearchLanes - 1) / kSearchLanes : 0;
-        const int64_t pos = L + static_cast<int64_t>(gl + 1) * step - 1;
-        const bool below = more && pos < R && static_cast<int64_t>(a[pos]) < v;
-        const uint32_t m = static_cast<uint32_t>(__ballot(below) >> shift) & 0xffffu;
-        if (more) {
-            const int64_t c = __popc(m);
-            const int64_t nl = min(L + c * step, R);
-            R = min(L + (c + 1) * step, R);
-            L = nl;
-        }
+// lower_bound(a[0..len), v) for two values at once, computed by the 16 lanes
+// of one aligned lane group (gl = lane within the group).  A first round
+// probes 16 positions 16 apart around the guess len * v / n (where the bound
+// lies when the indices are spread evenly over [0, n)); each later round
+// probes the last element of 16 equal sub-ranges of what is left.  Every
+// round keeps the range between the last probe below v and the first one that
+// is not, so a search takes two dependent loads when the guess is within 128
+// entries and about log16(len) more when it is not; the two searches share
+// their rounds.  Every lane of the wave must call it (it ballots); inactive
+// groups pass len = 0.  For an unsorted list each result is still some
+// position in [0, len].
+struct Search {
+    int64_t L, R, v;
+};
+
+__device__ __forceinline__ void search_round(const int32_t* a, Search& s, int gl, int shift, bool first,
+                                             int64_t guess, int64_t len) {
+    int64_t pos = 0;
+    bool act = false;
+    if (first) {
+        act = len > 0;
+        pos = min(max(guess + static_cast<int64_t>(gl - 8) * kSearchLanes, static_cast<int64_t>(0)), len - 1);
+    } else if (s.R - s.L > kSearchLanes) {
+        act = true;
+        const int64_t step = (s.R - s.L + kSearchLanes - 1) / kSearchLanes;
+        pos = min(s.L + static_cast<int64_t>(gl + 1) * step - 1, s.R - 1);
     }
-    const int64_t pos = L + gl;
-    const bool below = pos < R && static_cast<int64_t>(a[pos]) < v;
-    return L + __popc(static_cast<uint32_t>(__ballot(below) >> shift) & 0xffffu);
+    const bool below = act && static_cast<int64_t>(a[pos]) < s.v;
+    const uint32_t m = static_cast<uint32_t>(__ballot(below) >> shift) & 0xffffu;
+    if (!act) return;
+    // probe positions are non-decreasing in the lane index: the range left
+    // lies after the last probe below v (c of them) and up to the next one
+    // (the group's lanes are all active here: act is the same for all 16)
+    const int c = __popc(m);
+    const int g0 = static_cast<int>(lane()) & ~(kSearchLanes - 1);
+    const int64_t pl = __shfl(pos, g0 + max(c - 1, 0), kWave);
+    const int64_t pr = __shfl(pos, g0 + min(c, kSearchLanes - 1), kWave);
+    const int64_t nl = c > 0 ? pl + 1 : s.L;
+    const int64_t nr = c < kSearchLanes ? pr : s.R;
+    s.L = min(nl, s.R);
+    s.R = max(nr, s.L);
+}
+
+__device__ __forceinline__ void group_lower_bound2(const int32_t* a, int64_t len, int64_t n, int64_t v0,
+                                                   int64_t v1, int gl, int64_t* r0, int64_t* r1) {
+    const int shift = threadIdx.x & 48;  // this group's 16 bits of the wave's ballot
+    Search s0{0, len, v0}, s1{0, len, v1};
+    const int64_t g0 = n > 0 ? len * v0 / n : 0, g1 = n > 0 ? len * v1 / n : 0;
+    search_round(a, s0, gl, shift, true, g0, len);
+    search_round(a, s1, gl, shift, true, g1, len);
+    while (__any(s0.R - s0.L > kSearchLanes || s1.R - s1.L > kSearchLanes)) {
+        search_round(a, s0, gl, shift, false, 0, len);
+        search_round(a, s1, gl, shift, false, 0, len);
+    }
+    // at most 16 entries left: one probe each
+    const int64_t p0 = s0.L + gl, p1 = s1.L + gl;
+    const bool b0 = p0 < s0.R && static_cast<int64_t>(a[p0]) < v0;
+    const bool b1 = p1 < s1.R && static_cast<int64_t>(a[p1]) < v1;
+    *r0 = s0.L + __popc(static_cast<uint32_t>(__ballot(b0) >> shift) & 0xffffu);
+    *r1 = s1.L + __popc(static_cast<uint32_t>(__ballot(b1) >> shift) & 0xffffu);
 }
 
 __global__ __launch_bounds__(kBlock) void k_decode(float* __restrict__ G, int64_t n, int32_t npk,
@@ -112,8 +156,8 @@ __global__ __launch_bounds__(kBlock) void k_decode(float* __restrict__ G, int64_
                 const int64_t pe = pk_off[pg + grp + 1];
                 len = pe > pb ? pe - pb : 0;
             }
-            const int64_t a = group_lower_bound(idx + pb, len, lo, gl);
-            const int64_t b = group_lower_bound(idx + pb, len, hi, gl);
+            int64_t a, b;
+            group_lower_bound2(idx + pb, len, n, lo, hi, gl, &a, &b);
             if (grp < np && gl == 0) {
                 p_lo[grp] = pb + a;
                 p_cnt[grp] = static_cast<uint32_t>(b > a ? b - a : 0);

@@ -64,23 +64,34 @@ __global__ __launch_bounds__(kBlock) void k_bitmap_set(const int32_t* __restrict
     }
 }
 
-// per-chunk popcount of bytes [c*kChunk, ...) limited to nbits bits
-__device__ __forceinline__ uint32_t byte_bits(const uint8_t* bits, int64_t nbits, int64_t byte) {
-    if (byte * 8 >= nbits) return 0;
-    uint32_t v = bits[byte];
-    const int64_t valid = nbits - byte * 8;
-    if (valid < 8) v &= (1u << valid) - 1u;
-    return v;
+// The thread's kPer bitmap bytes from byte b0, limited to nbits bits (bytes
+// past the end count as 0).  All loads are issued before any is used: a byte
+// past the end reads the last byte instead (nbits >= 1).
+__device__ __forceinline__ void load_bits(const uint8_t* bits, int64_t nbits, int64_t b0, uint32_t (&v)[kPer]) {
+    const int64_t nbytes = (nbits + 7) / 8;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) v[t] = bits[min(b0 + t, nbytes - 1)];
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+        const int64_t valid = nbits - (b0 + t) * 8;
+        v[t] = valid <= 0 ? 0u : valid < 8 ? v[t] & ((1u << valid) - 1u) : v[t];
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void k_bm_count(const uint8_t* __restrict__ bits, int64_t nbits,
                                                      int64_t nchunks, uint32_t* __restrict__ cnt) {
     __shared__ uint32_t lds[kBlock / kWave + 1];
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        if (nbits == 0) {
+            if (threadIdx.x == 0) cnt[c] = 0;
+            continue;
+        }
         uint32_t s = 0;
         const int64_t b0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t v[kPer];
+        load_bits(bits, nbits, b0, v);
 #pragma unroll
-        for (int t = 0; t < kPer; ++t) s += __popc(byte_bits(bits, nbits, b0 + t));
+        for (int t = 0; t < kPer; ++t) s += __popc(v[t]);
         uint32_t total;
         block_excl_scan<kBlock>(s, lds, &total);
         if (threadIdx.x == 0) cnt[c] = total;
@@ -93,15 +104,14 @@ __global__ __launch_bounds__(kBlock) void k_bm_write(const uint8_t* __restrict__
                                                      int64_t nchunks, const uint32_t* __restrict__ cnt,
                                                      int32_t* __restrict__ out, int64_t cap) {
     __shared__ uint32_t lds[kBlock / kWave + 1];
+    if (nbits == 0) return;
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const int64_t b0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
         uint32_t v[kPer];
+        load_bits(bits, nbits, b0, v);
         uint32_t s = 0;
 #pragma unroll
-        for (int t = 0; t < kPer; ++t) {
-            v[t] = byte_bits(bits, nbits, b0 + t);
-            s += __popc(v[t]);
-        }
+        for (int t = 0; t < kPer; ++t) s += __popc(v[t]);
         uint32_t total;
         int64_t pos = static_cast<int64_t>(cnt[c]) + block_excl_scan<kBlock>(s, lds, &total);
 #pragma unroll
@@ -122,18 +132,33 @@ __device__ __forceinline__ uint32_t leb_len(uint32_t d) {
     return d < (1u << 7) ? 1u : d < (1u << 14) ? 2u : d < (1u << 21) ? 3u : d < (1u << 28) ? 4u : 5u;
 }
 
-__device__ __forceinline__ uint32_t delta_at(const int32_t* idx, int64_t j) {
-    const int64_t prev = j > 0 ? static_cast<int64_t>(idx[j - 1]) : 0;
-    return static_cast<uint32_t>(static_cast<int64_t>(idx[j]) - prev);
+// Differences idx[j] - idx[j - 1] (idx[-1] = 0) of the thread's kPer entries
+// from j0; entries past k get 0 and are not used.  All loads are issued
+// before any is used: a position outside [0, k) reads entry k - 1 (k >= 1).
+__device__ __forceinline__ void load_deltas(const int32_t* idx, int64_t k, int64_t j0, uint32_t (&d)[kPer]) {
+    int32_t v[kPer + 1];
+#pragma unroll
+    for (int t = 0; t <= kPer; ++t) v[t] = idx[min(max(j0 + t - 1, static_cast<int64_t>(0)), k - 1)];
+    if (j0 == 0) v[0] = 0;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t)
+        d[t] = static_cast<uint32_t>(static_cast<int64_t>(v[t + 1]) - static_cast<int64_t>(v[t]));
 }
 
 __global__ __launch_bounds__(kBlock) void k_de_count(const int32_t* __restrict__ idx, int64_t k, int64_t nchunks,
                                                      uint32_t* __restrict__ cnt) {
     __shared__ uint32_t lds[kBlock / kWave + 1];
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        if (k == 0) {
+            if (threadIdx.x == 0) cnt[c] = 0;
+            continue;
+        }
         const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t d[kPer];
+        load_deltas(idx, k, j0, d);
         uint32_t s = 0;
-        for (int t = 0; t < kPer && j0 + t < k; ++t) s += leb_len(delta_at(idx, j0 + t));
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) s += j0 + t < k ? leb_len(d[t]) : 0u;
         uint32_t total;
         block_excl_scan<kBlock>(s, lds, &total);
         if (threadIdx.x == 0) cnt[c] = total;
@@ -143,14 +168,18 @@ __global__ __launch_bounds__(kBlock) void k_de_count(const int32_t* __restrict__
 __global__ __launch_bounds__(kBlock) void k_de_write(const int32_t* __restrict__ idx, int64_t k, int64_t nchunks,
                                                      const uint32_t* __restrict__ cnt, uint8_t* __restrict__ out) {
     __shared__ uint32_t lds[kBlock / kWave + 1];
+    if (k == 0) return;
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t dl[kPer];
+        load_deltas(idx, k, j0, dl);
         uint32_t s = 0;
-        for (int t = 0; t < kPer && j0 + t < k; ++t) s += leb_len(delta_at(idx, j0 + t));
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) s += j0 + t < k ? leb_len(dl[t]) : 0u;
         uint32_t total;
         int64_t pos = static_cast<int64_t>(cnt[c]) + block_excl_scan<kBlock>(s, lds, &total);
         for (int t = 0; t < kPer && j0 + t < k; ++t) {
-            uint32_t d = delta_at(idx, j0 + t);
+            uint32_t d = dl[t];
             for (;;) {
                 const uint32_t low = d & 0x7fu;
                 d >>= 7;
@@ -165,14 +194,33 @@ __global__ __launch_bounds__(kBlock) void k_de_write(const int32_t* __restrict__
     }
 }
 
-// value of the varint that ends at terminator byte p (walks back over at most 4
-// continuation bytes); sets *bad when the varint is longer than 5 bytes
-__device__ __forceinline__ uint64_t varint_ending_at(const uint8_t* in, int64_t p, bool* bad) {
-    int64_t q = p;
-    while (q > 0 && (in[q - 1] & 0x80u) && p - q < 4) --q;
-    if (q > 0 && (in[q - 1] & 0x80u)) *bad = true;  // more than 5 bytes
-    uint64_t v = 0;
-    for (int64_t t = p; t >= q; --t) v = (v << 7) | (in[t] & 0x7fu);
+// The thread's kPer stream bytes from b0 and the 5 before them (a varint that
+// ends in the thread's range starts at most 4 bytes before it; one more byte
+// tells whether it is longer than 5 bytes).  w[5 + t] is byte b0 + t; bytes
+// before the stream read as 0 (no continuation bit), bytes past its end are
+// not used.  All loads are issued before any is used: a position outside
+// [0, nbytes) reads byte nbytes - 1 (nbytes >= 1).
+constexpr int kWin = kPer + 5;
+__device__ __forceinline__ void load_window(const uint8_t* in, int64_t nbytes, int64_t b0, uint32_t (&w)[kWin]) {
+#pragma unroll
+    for (int i = 0; i < kWin; ++i) w[i] = in[min(max(b0 - 5 + i, static_cast<int64_t>(0)), nbytes - 1)];
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+        if (b0 - 5 + i < 0) w[i] = 0;
+}
+
+// value of the varint that ends at terminator byte w[p] (p >= 5): back over at
+// most 4 continuation bytes, the first byte the least significant; sets *bad
+// when the byte before those 4 continues it too (longer than 5 bytes)
+__device__ __forceinline__ uint64_t varint_ending_at(const uint32_t (&w)[kWin], int p, bool* bad) {
+    uint64_t v = w[p] & 0x7fu;
+    bool cont = true;
+#pragma unroll
+    for (int j = 1; j <= 4; ++j) {
+        cont = cont && (w[p - j] & 0x80u);
+        if (cont) v = (v << 7) | (w[p - j] & 0x7fu);
+    }
+    if (cont && (w[p - 5] & 0x80u)) *bad = true;
     return v;
 }
 
@@ -182,14 +230,24 @@ __global__ __launch_bounds__(kBlock) void k_dd_count(const uint8_t* __restrict__
     __shared__ uint32_t lds[kBlock / kWave + 1];
     __shared__ uint64_t lds64[kBlock / kWave + 1];
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        if (nbytes == 0) {
+            if (threadIdx.x == 0) {
+                tcnt[c] = 0;
+                dsum[c] = 0;
+            }
+            continue;
+        }
         const int64_t b0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t w[kWin];
+        load_window(in, nbytes, b0, w);
         uint32_t s = 0;
         uint64_t d = 0;
         bool bad = false;
-        for (int t = 0; t < kPer && b0 + t < nbytes; ++t) {
-            if (!(in[b0 + t] & 0x80u)) {
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            if (b0 + t < nbytes && !(w[5 + t] & 0x80u)) {
                 ++s;
-                d += varint_ending_at(in, b0 + t, &bad);
+                d += varint_ending_at(w, 5 + t, &bad);
             }
         }
         if (bad && status) atomicOr(status, 1u);
@@ -244,24 +302,29 @@ __global__ __launch_bounds__(kBlock) void k_dd_write(const uint8_t* __restrict__
                                                      int32_t* __restrict__ idx, uint32_t* __restrict__ status) {
     __shared__ uint32_t lds[kBlock / kWave + 1];
     __shared__ uint64_t lds64[kBlock / kWave + 1];
+    if (nbytes == 0) return;
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const int64_t b0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t w[kWin];
+        load_window(in, nbytes, b0, w);
         uint32_t s = 0;
         uint64_t d = 0;
         bool bad = false;
-        for (int t = 0; t < kPer && b0 + t < nbytes; ++t) {
-            if (!(in[b0 + t] & 0x80u)) {
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            if (b0 + t < nbytes && !(w[5 + t] & 0x80u)) {
                 ++s;
-                d += varint_ending_at(in, b0 + t, &bad);
+                d += varint_ending_at(w, 5 + t, &bad);
             }
         }
         uint32_t total;
         uint64_t total64;
         int64_t ord = static_cast<int64_t>(tcnt[c]) + block_excl_scan<kBlock>(s, lds, &total);
         uint64_t acc = dsum[c] + block_excl_scan<kBlock>(d, lds64, &total64);
-        for (int t = 0; t < kPer && b0 + t < nbytes; ++t) {
-            if (!(in[b0 + t] & 0x80u)) {
-                acc += varint_ending_at(in, b0 + t, &bad);
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            if (b0 + t < nbytes && !(w[5 + t] & 0x80u)) {
+                acc += varint_ending_at(w, 5 + t, &bad);
                 if (acc > 0x7fffffffull) bad = true;
                 if (ord < k) idx[ord] = static_cast<int32_t>(acc);
                 ++ord;
@@ -415,6 +478,22 @@ __global__ __launch_bounds__(kBlock) void k_be_write(const int32_t* __restrict__
     }
 }
 
+// Entries per non-empty block (count_m1 + 1) of the thread's kPer blocks from
+// j0; 0 past the m blocks.  All loads are issued before any is used: a
+// position past the end reads block m - 1 (none when m = 0).
+__device__ __forceinline__ void load_counts(const uint8_t* counts_m1, int64_t m, int64_t j0, uint32_t (&cn)[kPer]) {
+    if (m <= 0) {
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) cn[t] = 0;
+        return;
+    }
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) cn[t] = counts_m1[min(j0 + t, m - 1)] + 1u;
+#pragma unroll
+    for (int t = 0; t < kPer; ++t)
+        if (j0 + t >= m) cn[t] = 0;
+}
+
 // per chunk of non-empty blocks: sum of (count_m1 + 1), limited to the device-side block count
 __global__ __launch_bounds__(kBlock) void k_bd_count(const uint8_t* __restrict__ counts_m1,
                                                      const uint32_t* __restrict__ nblk, int64_t mcap,
@@ -423,8 +502,11 @@ __global__ __launch_bounds__(kBlock) void k_bd_count(const uint8_t* __restrict__
     const int64_t m = std::min<int64_t>(*nblk, mcap);
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t cn[kPer];
+        load_counts(counts_m1, m, j0, cn);
         uint32_t s = 0;
-        for (int t = 0; t < kPer && j0 + t < m; ++t) s += counts_m1[j0 + t] + 1u;
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) s += cn[t];
         uint32_t total;
         block_excl_scan<kBlock>(s, lds, &total);
         if (threadIdx.x == 0) csum[c] = total;
@@ -441,13 +523,19 @@ __global__ __launch_bounds__(kBlock) void k_bd_write(const uint8_t* __restrict__
     const int64_t m = std::min<int64_t>(*nblk, mcap);
     for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const int64_t j0 = c * kChunk + static_cast<int64_t>(threadIdx.x) * kPer;
+        uint32_t cn[kPer];
+        load_counts(counts_m1, m, j0, cn);
+        int32_t bl[kPer];
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) bl[t] = m > 0 ? blk[min(j0 + t, m - 1)] : 0;
         uint32_t s = 0;
-        for (int t = 0; t < kPer && j0 + t < m; ++t) s += counts_m1[j0 + t] + 1u;
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) s += cn[t];
         uint32_t total;
         int64_t pos = static_cast<int64_t>(csum[c]) + block_excl_scan<kBlock>(s, lds, &total);
         for (int t = 0; t < kPer && j0 + t < m; ++t) {
-            const int64_t base = static_cast<int64_t>(blk[j0 + t]) * 256;
-            const uint32_t cntb = counts_m1[j0 + t] + 1u;
+            const int64_t base = static_cast<int64_t>(bl[t]) * 256;
+            const uint32_t cntb = cn[t];
             for (uint32_t u = 0; u < cntb; ++u, ++pos)
                 if (pos < k) idx[pos] = static_cast<int32_t>(base + offs[pos]);
         }

@@ -92,7 +92,7 @@ constexpr int kSampleRoundsMax = 8;
 constexpr int kSampleBins = 4096;
 constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
 #ifndef EFG_CHUNK
-#define EFG_CHUNK 4096
+#define EFG_CHUNK 2048
 #endif
 constexpr int kChunk = EFG_CHUNK;                  // entries per block-unit in select and emit
 static_assert(kChunk % kBlock == 0, "k_write: each wave takes kChunk / kBlock rows of 64 entries");
@@ -130,7 +130,7 @@ struct alignas(16) SegState {
 static_assert(sizeof(SegState) == 64, "SegState layout");
 
 struct alignas(16) Header {
-    uint32_t any_fallback;
+    uint32_t total_rchunks;  // raw chunks of the tensors that take the exact fallback
     uint32_t total_cchunks;
     uint32_t n_overflow;  // entries of the overflowed-region list
     uint32_t pad[61];
@@ -145,19 +145,19 @@ struct Plan {
     int64_t SB = 0;     // sample blocks
     int32_t sample_rounds = 1;  // groups of kSampleBlockChunks chunks per sample block
     int32_t hcopies = 1;        // copies of each radix histogram (blocks add to copy blockIdx % hcopies)
-    int64_t QR = 0;     // raw chunks (fallback units)
+    int64_t QR = 0;     // bound on raw chunks (fallback units): those of every tensor
     int64_t QC = 0;     // bound on candidate chunks
     int64_t Ctot = 0;   // candidate slot entries
     int64_t CB = 0;     // compaction blocks
     bool any_normal = false;
     std::vector<SegPlan> seg;
-    std::vector<int32_t> rb, gbb, sbb, rcb, cbb;  // prefix tables, nseg+1 each
+    std::vector<int32_t> rb, gbb, sbb, cbb;  // prefix tables, nseg+1 each
 };
 
 struct Layout {
-    size_t plan, rb, gbb, sbb, rcb, cbb, static_end;
+    size_t plan, rb, gbb, sbb, cbb, static_end;
     size_t header, state, shist, rhist, grp_cnt, zero_end;
-    size_t ccb, grp_off, region_cnt, ovf, cpair, dval, didx, cgt, ceq, rgt, req, spart, gpart, cpart, rpart;
+    size_t ccb, rcb, grp_off, region_cnt, ovf, cpair, dval, didx, cgt, ceq, rgt, req, spart, gpart, cpart, rpart;
     size_t total;
 };
 
@@ -170,7 +170,6 @@ static Layout make_layout(const Plan& p) {
     L.rb = at; at += (ns + 1) * 4;
     L.gbb = at; at += (ns + 1) * 4;
     L.sbb = at; at += (ns + 1) * 4;
-    L.rcb = at; at += (ns + 1) * 4;
     L.cbb = at; at += (ns + 1) * 4;
     at = round_up(at, 256);
     L.static_end = at;
@@ -181,6 +180,7 @@ static Layout make_layout(const Plan& p) {
     L.grp_cnt = take(static_cast<size_t>(p.G) * 4);
     L.zero_end = at;
     L.ccb = take((ns + 1) * 4);
+    L.rcb = take((ns + 1) * 4);
     L.grp_off = take(static_cast<size_t>(p.G) * 4);
     L.region_cnt = take(static_cast<size_t>(p.R) * 4);
     L.ovf = take(static_cast<size_t>(p.R) * 4);
@@ -214,7 +214,6 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
     p.rb.assign(nseg + 1, 0);
     p.gbb.assign(nseg + 1, 0);
     p.sbb.assign(nseg + 1, 0);
-    p.rcb.assign(nseg + 1, 0);
     p.cbb.assign(nseg + 1, 0);
     int64_t out = 0;
     for (int32_t s = 0; s < nseg; ++s) {
@@ -288,7 +287,6 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
         p.R += P.nregions;
         p.G += P.ngroups;
         p.SB += P.sample_chunks;  // total sample chunks for now; blocks below
-        p.rcb[s] = static_cast<int32_t>(p.QR);
         p.QR += P.raw_chunks;
         p.cbb[s] = static_cast<int32_t>(p.CB);
         if (P.cap > 0) p.CB += static_cast<int64_t>(P.ngroups) * P.compact_split;
@@ -311,7 +309,6 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
     p.rb[nseg] = static_cast<int32_t>(p.R);
     p.gbb[nseg] = static_cast<int32_t>(p.G);
     p.sbb[nseg] = static_cast<int32_t>(p.SB);
-    p.rcb[nseg] = static_cast<int32_t>(p.QR);
     p.cbb[nseg] = static_cast<int32_t>(p.CB);
     p.QC += 1;
     return EF_OK;
@@ -359,9 +356,13 @@ __global__ __launch_bounds__(kSampleBlock) void k_sample(const float* __restrict
             else if (S > 1) start = static_cast<int64_t>(c) * (n - kSampleChunk) / (S - 1);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                // every load is issued before any is used: a position past the
+                // sample or the tensor reads the tensor's last element (n >= 1)
                 const int64_t loc = start + j * kWave + l;
                 ok[u][j] = (c < S) && (loc < n);
-                xs[u][j] = ok[u][j] ? (g[off + loc] + e[off + loc]) : 0.0f;
+                const int64_t at = off + min(loc, n - 1);
+                const float x = g[at] + e[at];
+                xs[u][j] = ok[u][j] ? x : 0.0f;
             }
         }
 #pragma unroll
@@ -693,7 +694,8 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_groups(const SegPlan* __res
                                                             const uint32_t* __restrict__ grp_cnt,
                                                             uint32_t* __restrict__ grp_off,
                                                             SegState* __restrict__ st, uint32_t* __restrict__ ccb,
-                                                            Header* __restrict__ hdr, uint32_t force_fallback) {
+                                                            uint32_t* __restrict__ rcb, Header* __restrict__ hdr,
+                                                            uint32_t force_fallback) {
     __shared__ uint32_t lds[kScanBlock / kWave + 1];
     uint32_t carry = 0;
     for (int64_t t0 = 0; t0 < G; t0 += kScanBlock) {
@@ -706,10 +708,10 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_groups(const SegPlan* __res
     }
     const uint32_t total = carry;
     __syncthreads();
-    uint32_t cc = 0, anyfb = 0;
+    uint32_t cc = 0, rc = 0;
     for (int32_t t0 = 0; t0 < nseg; t0 += kScanBlock) {
         const int32_t s = t0 + threadIdx.x;
-        uint32_t cchunks = 0;
+        uint32_t cchunks = 0, rchunks = 0;
         if (s < nseg && plan[s].mode == MODE_NORMAL) {
             const int64_t b = gbb[s], en = gbb[s + 1];
             const uint32_t d0 = b < G ? grp_off[b] : total;
@@ -726,21 +728,25 @@ __global__ __launch_bounds__(kScanBlock) void k_scan_groups(const SegPlan* __res
             st[s].want = static_cast<uint32_t>(plan[s].k);
             st[s].prefix = 0;
             cchunks = fb ? 0u : (nc + kChunk - 1) / kChunk;
+            rchunks = fb ? static_cast<uint32_t>(plan[s].raw_chunks) : 0u;
             st[s].cchunks = cchunks;
-            anyfb |= fb ? 1u : 0u;
         }
-        uint32_t tt;
+        uint32_t tt, tr;
         const uint32_t ex = block_excl_scan<kScanBlock>(cchunks, lds, &tt);
+        const uint32_t exr = block_excl_scan<kScanBlock>(rchunks, lds, &tr);
         if (s < nseg) {
             ccb[s] = cc + ex;
             st[s].cchunk_begin = cc + ex;
+            rcb[s] = rc + exr;
         }
         cc += tt;
+        rc += tr;
     }
-    if (anyfb) atomicOr(&hdr->any_fallback, 1u);
     if (threadIdx.x == 0) {
         ccb[nseg] = cc;
+        rcb[nseg] = rc;
         hdr->total_cchunks = cc;
+        hdr->total_rchunks = rc;
     }
 }
 
@@ -757,6 +763,7 @@ __device__ __forceinline__ uint32_t* radix_hist(uint32_t* rhist, int pass, int s
 //    one scans the group's region counts and copies its own slice of regions.
 //    For a tensor that takes the exact fallback, the same blocks instead put
 //    back x where the stream already wrote e = 0, so that e holds x whole.
+constexpr int kCompactItems = 8;
 __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ plan, int32_t nseg,
                                                     const int32_t* __restrict__ cbb, const int32_t* __restrict__ gbb,
                                                     const int32_t* __restrict__ rb, const SegState* __restrict__ st,
@@ -811,15 +818,33 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     const uint32_t dbase = st[s].dense_off + (grp_off[gi] - st[s].group_base);
     const int64_t slot0 = plan[s].cand_base + (r0 - rb[s]) * plan[s].cap;
     const int64_t cap = plan[s].cap;
-    for (uint32_t q = q0 + t; q < q1; q += kBlock) {
-        const int r = rs + upper_index(loff + rs, re - rs, q);
-        if (q - loff[r] >= cap) continue;  // past the slot: k_recollect writes it
-        const int64_t src = slot0 + r * cap + (q - loff[r]);
-        const uint2 pr = cpair[src];
-        const float v = __uint_as_float(pr.x);
-        dval[dbase + q] = v;
-        didx[dbase + q] = static_cast<int32_t>(pr.y);
-        atomicAdd(&h[key_of(v) >> 20], 1u);
+    // kCompactItems entries per thread in flight: an entry past the block's
+    // range or past its region's slot (k_recollect writes those) reads the
+    // group's first slot instead and is not used
+    for (uint32_t qb = q0; qb < q1; qb += kBlock * kCompactItems) {
+        uint2 pr[kCompactItems];
+        bool ok[kCompactItems];
+#pragma unroll
+        for (int u = 0; u < kCompactItems; ++u) {
+            const uint32_t q = qb + u * kBlock + t;
+            int64_t src = slot0;
+            ok[u] = q < q1;
+            if (ok[u]) {
+                const int r = rs + upper_index(loff + rs, re - rs, q);
+                ok[u] = q - loff[r] < cap;
+                if (ok[u]) src = slot0 + r * cap + (q - loff[r]);
+            }
+            pr[u] = cpair[src];
+        }
+#pragma unroll
+        for (int u = 0; u < kCompactItems; ++u) {
+            if (!ok[u]) continue;
+            const uint32_t q = qb + u * kBlock + t;
+            const float v = __uint_as_float(pr[u].x);
+            dval[dbase + q] = v;
+            didx[dbase + q] = static_cast<int32_t>(pr[u].y);
+            atomicAdd(&h[key_of(v) >> 20], 1u);
+        }
     }
     __syncthreads();
     if (q1 > q0) {
@@ -924,11 +949,11 @@ __device__ __forceinline__ bool radix_digit(int pass, uint32_t key, uint32_t pre
 
 // Work units of the select / emit kernels: candidate chunks of fast tensors
 // (kChunk entries of the dense list) followed by raw chunks of fallback
-// tensors (kChunk elements of x, which sits in e).
+// tensors (kChunk elements of x, which sits in e).  Both lists hold only the
+// tensors that take that path in this call (ccb, rcb: their prefix tables).
 struct Unit {
     int s;
     bool raw;
-    bool skip;
     const float* v;        // values
     const int32_t* id;     // indices (candidate units)
     int64_t idx_base;      // first index (raw units)
@@ -937,7 +962,7 @@ struct Unit {
 };
 
 __device__ __forceinline__ Unit unit_of(int64_t q, int64_t Qc, const SegPlan* plan, int32_t nseg,
-                                        const SegState* st, const uint32_t* ccb, const int32_t* rcb,
+                                        const SegState* st, const uint32_t* ccb, const uint32_t* rcb,
                                         const float* dval, const int32_t* didx, const float* e) {
     Unit u;
     if (q < Qc) {
@@ -946,57 +971,81 @@ __device__ __forceinline__ Unit unit_of(int64_t q, int64_t Qc, const SegPlan* pl
         const uint32_t lq = qq - ccb[u.s];
         const uint32_t base = st[u.s].dense_off + lq * kChunk;
         u.raw = false;
-        u.skip = false;
         u.v = dval + base;
         u.id = didx + base;
         u.idx_base = 0;
         u.cnt = min(static_cast<uint32_t>(kChunk), st[u.s].ncand - lq * kChunk);
         u.slot = qq;
     } else {
-        const int32_t qq = static_cast<int32_t>(q - Qc);
+        const uint32_t qq = static_cast<uint32_t>(q - Qc);
         u.s = upper_index(rcb, nseg, qq);
         const int64_t lbeg = static_cast<int64_t>(qq - rcb[u.s]) * kChunk;
         u.raw = true;
-        u.skip = !st[u.s].fallback;
         u.idx_base = plan[u.s].off + lbeg;
         u.v = e + u.idx_base;
         u.id = nullptr;
         u.cnt = static_cast<uint32_t>(min(static_cast<int64_t>(kChunk), plan[u.s].n - lbeg));
-        u.slot = static_cast<uint32_t>(qq);
+        u.slot = qq;
     }
     return u;
+}
+
+// A unit's entries as the select and emit kernels read them: wave w of the
+// block takes entries [w R 64, (w + 1) R 64), R = kChunk / kBlock rows of 64,
+// lane l entry w R 64 + 64 i + l in row i, so every row is one coalesced load.
+// All R loads are issued before any is used: an entry past the unit's end
+// (cnt >= 1) reads the unit's last entry instead and is marked absent.
+constexpr int kRows = kChunk / kBlock;
+__device__ __forceinline__ uint32_t load_rows(const Unit& u, float (&v)[kRows]) {
+    const uint32_t j0 = static_cast<uint32_t>(threadIdx.x / kWave) * (kRows * kWave) + lane();
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) v[i] = u.v[min(j0 + i * kWave, u.cnt - 1)];
+    return j0;
 }
 
 // 5a. radix histograms (pass 0 only for fallback tensors: the compaction did it for the others)
 __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
                                                  const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
-                                                 const int32_t* __restrict__ rcb, int64_t QR,
+                                                 const uint32_t* __restrict__ rcb,
                                                  const Header* __restrict__ hdr, const float* __restrict__ dval,
                                                  const float* __restrict__ e, uint32_t* __restrict__ rhist,
                                                  int32_t hcopies) {
     __shared__ uint32_t h[kRadixBins];
     const int64_t Qc = pass > 0 ? hdr->total_cchunks : 0;
-    const int64_t Q = Qc + (hdr->any_fallback ? QR : 0);
+    const int64_t Q = Qc + hdr->total_rchunks;
     if (Q == 0) return;
     const int nb = pass == 0 ? 2048 : 1024;
     for (int i = threadIdx.x; i < kRadixBins; i += kBlock) h[i] = 0;
-    __syncthreads();
-    for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
-        const Unit u = unit_of(q, Qc, plan, nseg, st, ccb, rcb, dval, nullptr, e);
-        if (u.skip) continue;
-        const uint32_t prefix = st[u.s].prefix;
-        for (uint32_t j = threadIdx.x; j < u.cnt; j += kBlock) {
-            uint32_t d;
-            if (radix_digit(pass, key_of(u.v[j]), prefix, &d)) atomicAdd(&h[d], 1u);
-        }
+    // h holds the counts of tensor `cur`; they go out when the block's next
+    // unit is another tensor's, and at the end (once for a tensor that
+    // spans many of the block's units)
+    auto flush = [&](int s) {
         __syncthreads();
-        uint32_t* gh = radix_hist(rhist, pass, u.s, blockIdx.x % hcopies, nseg, hcopies);
+        uint32_t* gh = radix_hist(rhist, pass, s, blockIdx.x % hcopies, nseg, hcopies);
         for (int i = threadIdx.x; i < nb; i += kBlock) {
             if (h[i]) atomicAdd(&gh[i], h[i]);
             h[i] = 0;
         }
         __syncthreads();
+    };
+    __syncthreads();
+    int cur = -1;
+    for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
+        const Unit u = unit_of(q, Qc, plan, nseg, st, ccb, rcb, dval, nullptr, e);
+        if (u.s != cur) {
+            if (cur >= 0) flush(cur);
+            cur = u.s;
+        }
+        const uint32_t prefix = st[u.s].prefix;
+        float v[kRows];
+        const uint32_t j0 = load_rows(u, v);
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            uint32_t d;
+            if (j0 + i * kWave < u.cnt && radix_digit(pass, key_of(v[i]), prefix, &d)) atomicAdd(&h[d], 1u);
+        }
     }
+    if (cur >= 0) flush(cur);
 }
 
 // 5b. fix one digit per tensor
@@ -1043,23 +1092,26 @@ __global__ __launch_bounds__(kBlock) void k_digit(int pass, const SegPlan* __res
 // 6a. per-unit counts of keys above T and equal to T
 __global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ plan, int32_t nseg,
                                                   const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
-                                                  const int32_t* __restrict__ rcb, int64_t QR,
+                                                  const uint32_t* __restrict__ rcb,
                                                   const Header* __restrict__ hdr, const float* __restrict__ dval,
                                                   const float* __restrict__ e, uint32_t* __restrict__ cgt,
                                                   uint32_t* __restrict__ ceq, uint32_t* __restrict__ rgt,
                                                   uint32_t* __restrict__ req) {
     __shared__ uint32_t sa[kWavesPerBlock], sb[kWavesPerBlock];
     const int64_t Qc = hdr->total_cchunks;
-    const int64_t Q = Qc + (hdr->any_fallback ? QR : 0);
+    const int64_t Q = Qc + hdr->total_rchunks;
     for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
         const Unit u = unit_of(q, Qc, plan, nseg, st, ccb, rcb, dval, nullptr, e);
-        if (u.skip) continue;
         const uint32_t T = st[u.s].T;
+        float v[kRows];
+        const uint32_t j0 = load_rows(u, v);
         uint32_t a = 0, b = 0;
-        for (uint32_t j = threadIdx.x; j < u.cnt; j += kBlock) {
-            const uint32_t key = key_of(u.v[j]);
-            a += key > T;
-            b += key == T;
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const bool ok = j0 + i * kWave < u.cnt;
+            const uint32_t key = key_of(v[i]);
+            a += ok && key > T;
+            b += ok && key == T;
         }
         a = wave_sum(a);
         b = wave_sum(b);
@@ -1081,13 +1133,18 @@ __global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ pl
     }
 }
 
-// 6b. exclusive scan of the unit counts of each tensor (packed gt:eq in 64 bits)
-__global__ __launch_bounds__(kBlock) void k_emit_scan(const SegPlan* __restrict__ plan,
-                                                      const SegState* __restrict__ st,
-                                                      const int32_t* __restrict__ rcb, uint32_t* __restrict__ cgt,
-                                                      uint32_t* __restrict__ ceq, uint32_t* __restrict__ rgt,
-                                                      uint32_t* __restrict__ req) {
-    __shared__ uint64_t lds[kWavesPerBlock + 1];
+// 6b. exclusive scan of the unit counts of each tensor (packed gt:eq in 64
+//     bits): one block per tensor, each thread taking kEmitItems consecutive
+//     units of every tile, so that a fallback tensor's hundreds of thousands
+//     of raw units take a few dozen block scans
+constexpr int kEmitScanBlock = 1024;
+constexpr int kEmitItems = 8;
+__global__ __launch_bounds__(kEmitScanBlock) void k_emit_scan(const SegPlan* __restrict__ plan,
+                                                              const SegState* __restrict__ st,
+                                                              const uint32_t* __restrict__ rcb,
+                                                              uint32_t* __restrict__ cgt, uint32_t* __restrict__ ceq,
+                                                              uint32_t* __restrict__ rgt, uint32_t* __restrict__ req) {
+    __shared__ uint64_t lds[kEmitScanBlock / kWave + 1];
     const int s = blockIdx.x;
     if (plan[s].mode != MODE_NORMAL) return;
     uint32_t *a, *b;
@@ -1102,22 +1159,36 @@ __global__ __launch_bounds__(kBlock) void k_emit_scan(const SegPlan* __restrict_
         n = st[s].cchunks;
     }
     uint64_t carry = 0;
-    for (int64_t t0 = 0; t0 < n; t0 += kBlock) {
-        const int64_t i = t0 + threadIdx.x;
-        const uint64_t v = i < n ? ((static_cast<uint64_t>(a[i]) << 32) | b[i]) : 0;
+    for (int64_t t0 = 0; t0 < n; t0 += static_cast<int64_t>(kEmitScanBlock) * kEmitItems) {
+        const int64_t i0 = t0 + static_cast<int64_t>(threadIdx.x) * kEmitItems;
+        uint64_t v[kEmitItems];
+        uint64_t sum = 0;
+#pragma unroll
+        for (int j = 0; j < kEmitItems; ++j) {
+            // all loads issued before any is used: past the end reads entry n - 1
+            const int64_t i = min(i0 + j, n - 1);
+            const uint64_t w = (static_cast<uint64_t>(a[i]) << 32) | b[i];
+            v[j] = i0 + j < n ? w : 0;
+            sum += v[j];
+        }
         uint64_t tot;
-        const uint64_t ex = block_excl_scan<kBlock>(v, lds, &tot) + carry;
-        if (i < n) {
-            a[i] = static_cast<uint32_t>(ex >> 32);
-            b[i] = static_cast<uint32_t>(ex);
+        uint64_t ex = block_excl_scan<kEmitScanBlock>(sum, lds, &tot) + carry;
+#pragma unroll
+        for (int j = 0; j < kEmitItems; ++j) {
+            const int64_t i = i0 + j;
+            if (i < n) {
+                a[i] = static_cast<uint32_t>(ex >> 32);
+                b[i] = static_cast<uint32_t>(ex);
+            }
+            ex += v[j];
         }
         carry += tot;
     }
 }
 
-// 6c. the kept entries at their index-ordered places.  Wave w of a block takes
-//     entries [1024 w, 1024 w + 1024) of the unit, lane l entry 1024 w + 64 i + l
-//     of row i, so loads and (mostly kept-together) stores coalesce.  An entry's
+// 6c. the kept entries at their index-ordered places, the unit read in rows as
+//     load_rows lays them out, so loads and (mostly kept-together) stores
+//     coalesce.  An entry's
 //     place is (entries with key > T before it) + min(r, entries with key == T
 //     before it): the unit's counts before it (from k_emit_scan), those of the
 //     block's earlier waves, of the wave's earlier rows, and of the row's lower
@@ -1125,35 +1196,37 @@ __global__ __launch_bounds__(kBlock) void k_emit_scan(const SegPlan* __restrict_
 //     (key >= thi); dropped ones the stream cleared get x back.
 __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ plan, int32_t nseg,
                                                   const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
-                                                  const int32_t* __restrict__ rcb, int64_t QR,
+                                                  const uint32_t* __restrict__ rcb,
                                                   const Header* __restrict__ hdr, const float* __restrict__ dval,
                                                   const int32_t* __restrict__ didx, const uint32_t* __restrict__ cgt,
                                                   const uint32_t* __restrict__ ceq, const uint32_t* __restrict__ rgt,
                                                   const uint32_t* __restrict__ req, float* __restrict__ e,
                                                   float* __restrict__ vals, int32_t* __restrict__ idx,
                                                   double2* __restrict__ cpart, double2* __restrict__ rpart) {
-    constexpr int kRows = kChunk / kBlock;  // rows of 64 entries per wave
     __shared__ uint32_t wgt[kWavesPerBlock], weq[kWavesPerBlock];
     __shared__ double2 lsum[kWavesPerBlock];
     const int64_t Qc = hdr->total_cchunks;
-    const int64_t Q = Qc + (hdr->any_fallback ? QR : 0);
+    const int64_t Q = Qc + hdr->total_rchunks;
     const int wv = threadIdx.x / kWave;
     const int l = lane();
     for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
         const Unit u = unit_of(q, Qc, plan, nseg, st, ccb, rcb, dval, didx, e);
-        if (u.skip) continue;
         const uint32_t T = st[u.s].T, r = st[u.s].r;
         const uint32_t thi = u.raw ? kNoKey : st[u.s].thi;
         const int64_t out_off = plan[u.s].out_off, kseg = plan[u.s].k;
         const int64_t seg_lo = plan[u.s].off, seg_hi = plan[u.s].off + plan[u.s].n;
-        const uint32_t w0 = static_cast<uint32_t>(wv) * (kRows * kWave);
+        uint32_t gtb = (u.raw ? rgt : cgt)[u.slot], eqb = (u.raw ? req : ceq)[u.slot];  // counts before the unit
         float v[kRows];
+        const uint32_t j0 = load_rows(u, v);
+        int32_t ids[kRows];  // the entries' indices (candidate units), loaded with the values
+        if (!u.raw) {
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) ids[i] = u.id[min(j0 + i * kWave, u.cnt - 1)];
+        }
         uint32_t ngt = 0, neq = 0;  // this wave's counts (wave-uniform)
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {
-            const uint32_t j = w0 + i * kWave + l;
-            const bool ok = j < u.cnt;
-            v[i] = ok ? u.v[j] : 0.0f;
+            const bool ok = j0 + i * kWave < u.cnt;
             const uint32_t key = key_of(v[i]);
             ngt += popc64(__ballot(ok && key > T));
             neq += popc64(__ballot(ok && key == T));
@@ -1163,7 +1236,6 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
             weq[wv] = neq;
         }
         __syncthreads();
-        uint32_t gtb = (u.raw ? rgt : cgt)[u.slot], eqb = (u.raw ? req : ceq)[u.slot];
         for (int i = 0; i < wv; ++i) {
             gtb += wgt[i];
             eqb += weq[i];
@@ -1171,7 +1243,7 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
         double sent = 0.0, drop = 0.0;
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {
-            const uint32_t j = w0 + i * kWave + l;
+            const uint32_t j = j0 + i * kWave;
             const bool ok = j < u.cnt;
             const uint32_t key = key_of(v[i]);
             const bool gt = ok && key > T, eq = ok && key == T;
@@ -1185,7 +1257,7 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
             else if (eq && e_before < r) pos = static_cast<int64_t>(g_before) + e_before;
             if (pos >= 0) sent += sq_finite(v[i], key);
             else drop += sq_finite(v[i], key);
-            const int64_t id = u.raw ? u.idx_base + j : static_cast<int64_t>(u.id[j]);
+            const int64_t id = u.raw ? u.idx_base + j : static_cast<int64_t>(ids[i]);
             if (id < seg_lo || id >= seg_hi) continue;  // only if the workspace was overwritten meanwhile
             if (pos >= 0 && pos < kseg) {
                 vals[out_off + pos] = v[i];
@@ -1248,7 +1320,7 @@ __global__ __launch_bounds__(kGroup) void k_stats_groups(const SegPlan* __restri
 
 // 7b. per tensor
 __global__ __launch_bounds__(kBlock) void k_stats(const SegPlan* __restrict__ plan, const SegState* __restrict__ st,
-                                                  const int32_t* __restrict__ gbb, const int32_t* __restrict__ rcb,
+                                                  const int32_t* __restrict__ gbb, const uint32_t* __restrict__ rcb,
                                                   const double2* __restrict__ gpart, const double2* __restrict__ cpart,
                                                   const double2* __restrict__ rpart, double* __restrict__ stats) {
     __shared__ double2 lsum[kWavesPerBlock];
@@ -1312,7 +1384,6 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
         memcpy(h + L.rb, P.rb.data(), P.rb.size() * 4);
         memcpy(h + L.gbb, P.gbb.data(), P.gbb.size() * 4);
         memcpy(h + L.sbb, P.sbb.data(), P.sbb.size() * 4);
-        memcpy(h + L.rcb, P.rcb.data(), P.rcb.size() * 4);
         memcpy(h + L.cbb, P.cbb.data(), P.cbb.size() * 4);
     }
     // Small plans (up to 11 tensors) ride on k_init's arguments.  Larger ones
@@ -1342,7 +1413,7 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     const int32_t* rb = reinterpret_cast<const int32_t*>(at(L.rb));
     const int32_t* gbb = reinterpret_cast<const int32_t*>(at(L.gbb));
     const int32_t* sbb = reinterpret_cast<const int32_t*>(at(L.sbb));
-    const int32_t* rcb = reinterpret_cast<const int32_t*>(at(L.rcb));
+    uint32_t* rcb = reinterpret_cast<uint32_t*>(at(L.rcb));
     Header* hdr = reinterpret_cast<Header*>(at(L.header));
     SegState* st = reinterpret_cast<SegState*>(at(L.state));
     uint32_t* shist = reinterpret_cast<uint32_t*>(at(L.shist));
@@ -1369,7 +1440,8 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
         EF_TRY(launch("topk_stats_groups", k_stats_groups, dim3(static_cast<unsigned>(P.G)), dim3(kGroup), s, plan,
                       nseg, gbb, rb, static_cast<const double2*>(spart), gpart));
         return launch("topk_stats", k_stats, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
-                      static_cast<const SegState*>(st), gbb, rcb, static_cast<const double2*>(gpart),
+                      static_cast<const SegState*>(st), gbb, static_cast<const uint32_t*>(rcb),
+                      static_cast<const double2*>(gpart),
                       static_cast<const double2*>(reinterpret_cast<double2*>(at(L.cpart))),
                       static_cast<const double2*>(reinterpret_cast<double2*>(at(L.rpart))), stats);
     };
@@ -1390,7 +1462,7 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     if (!P.any_normal) return finish_stats();
 
     EF_TRY(launch("topk_scan_groups", k_scan_groups, dim3(1), dim3(kScanBlock), s, plan, nseg, gbb, P.G,
-                  static_cast<const uint32_t*>(grp_cnt), grp_off, st, ccb, hdr,
+                  static_cast<const uint32_t*>(grp_cnt), grp_off, st, ccb, rcb, hdr,
                   static_cast<uint32_t>((flags & EF_FLAG_FORCE_FALLBACK) ? 1u : 0u)));
     EF_TRY(launch("topk_compact", k_compact, dim3(static_cast<unsigned>(P.CB)), dim3(kBlock), s, plan, nseg,
                   static_cast<const int32_t*>(reinterpret_cast<int32_t*>(at(L.cbb))), gbb, rb,
@@ -1405,19 +1477,19 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     const unsigned gu = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, P.QC + P.QR)));
     for (int pass = 0; pass < 3; ++pass) {
         EF_TRY(launch("topk_hist", k_hist, dim3(gu), dim3(kBlock), s, pass, plan, nseg,
-                      static_cast<const SegState*>(st), static_cast<const uint32_t*>(ccb), rcb, P.QR,
+                      static_cast<const SegState*>(st), static_cast<const uint32_t*>(ccb), static_cast<const uint32_t*>(rcb),
                       static_cast<const Header*>(hdr), static_cast<const float*>(dval),
                       static_cast<const float*>(e), rhist, P.hcopies));
         EF_TRY(launch("topk_digit", k_digit, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, pass, plan, nseg,
                       st, static_cast<const uint32_t*>(rhist), P.hcopies));
     }
     EF_TRY(launch("topk_count", k_count, dim3(gu), dim3(kBlock), s, plan, nseg, static_cast<const SegState*>(st),
-                  static_cast<const uint32_t*>(ccb), rcb, P.QR, static_cast<const Header*>(hdr),
+                  static_cast<const uint32_t*>(ccb), static_cast<const uint32_t*>(rcb), static_cast<const Header*>(hdr),
                   static_cast<const float*>(dval), static_cast<const float*>(e), cgt, ceq, rgt, req));
-    EF_TRY(launch("topk_emit_scan", k_emit_scan, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
-                  static_cast<const SegState*>(st), rcb, cgt, ceq, rgt, req));
+    EF_TRY(launch("topk_emit_scan", k_emit_scan, dim3(static_cast<unsigned>(nseg)), dim3(kEmitScanBlock), s, plan,
+                  static_cast<const SegState*>(st), static_cast<const uint32_t*>(rcb), cgt, ceq, rgt, req));
     EF_TRY(launch("topk_write", k_write, dim3(gu), dim3(kBlock), s, plan, nseg, static_cast<const SegState*>(st),
-                  static_cast<const uint32_t*>(ccb), rcb, P.QR, static_cast<const Header*>(hdr),
+                  static_cast<const uint32_t*>(ccb), static_cast<const uint32_t*>(rcb), static_cast<const Header*>(hdr),
                   static_cast<const float*>(dval), static_cast<const int32_t*>(didx),
                   static_cast<const uint32_t*>(cgt), static_cast<const uint32_t*>(ceq),
                   static_cast<const uint32_t*>(rgt), static_cast<const uint32_t*>(req), e, vals, idx, cpart, rpart));

@@ -50,7 +50,7 @@ extern "C" {
 #define EF_EINVAL 1   /* bad argument (null pointer, size, alignment, k > n, ...) */
 #define EF_EWS 2      /* workspace missing or smaller than the size query says   */
 #define EF_EHIP 3     /* the HIP runtime rejected a launch                        */
-#define EF_ENOTIMPL 4 /* entry point not available in this build                  */
+#define EF_ENOTIMPL 4 /* reserved: an operation the library does not provide      */
 
 /* Debug flag: take each call's exact fallback path even when its faster path
  * would have succeeded (top-k: the full-pass selection for every tensor;
