@@ -103,11 +103,12 @@ def test_segmented_random_cases(case):
     kind = KINDS[int(r.integers(0, len(KINDS)))]
     g = values(r, n, kind)
     e = values(r, n, "normal") * np.float32(r.choice([0.0, 1e-3]))
-    what = f"case {case}: {nseg} tensors, n={n}, K={sum(ks)} {kind}"
+    flags = efg.EF_FLAG_FORCE_FALLBACK if r.random() < 0.15 else 0
+    what = f"case {case}: {nseg} tensors, n={n}, K={sum(ks)} {kind} flags={flags}"
     say(what)
     dev = device()
     ed = to_dev(e, dev)
-    v, i = efg.ef_topk_compress_segmented(to_dev(g, dev), ed, off, np.array(ks, np.int64))
+    v, i = efg.ef_topk_compress_segmented(to_dev(g, dev), ed, off, np.array(ks, np.int64), flags=flags)
     ov, oi, oe, _ = oracle.topk_segmented(g, e, off, np.array(ks, np.int64))
     K = int(sum(ks))
     assert_bits_equal(host(i)[:K], oi, f"idx {what}")

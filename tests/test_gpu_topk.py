@@ -62,6 +62,16 @@ def test_forced_fallback(n, k, kind):
     check(g, e, k, flags=efg.EF_FLAG_FORCE_FALLBACK, what=f"fallback n={n} k={k} {kind}")
 
 
+def test_forced_fallback_many_units():
+    """The exact path over 20,000,003 elements: about 9,800 units of the select
+    kernels, so the per-tensor scan of their counts spans more than one
+    8192-unit tile, and the last unit is ragged."""
+    n, k = 20_000_003, 20_000
+    g, e = inputs(n, "lognormal", 7)
+    say(f"forced fallback n={n} k={k}")
+    check(g, e, k, flags=efg.EF_FLAG_FORCE_FALLBACK, what=f"fallback n={n} k={k}")
+
+
 def test_clustered_magnitudes_overflow():
     # all large values sit in a few regions: their candidate slots overflow and
     # the rest of their candidates are read again from e
