@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kSampleBlock) void k_sample(const float* __restrict
                                                    uint32_t* __restrict__ shist) {
     __shared__ uint32_t h[kSampleBins];
     const int b = blockIdx.x;
-    const int s = upper_index(sbb, nseg, b);
+    const int s = upper_index_wave(sbb, nseg, b);
     const int64_t off = plan[s].off, n = plan[s].n;
     const int S = plan[s].sample_chunks;
     const bool exhaustive = plan[s].exhaustive != 0;
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
     int32_t grp = -1;
     bool ovfl = false;
     if (w < R) {
-        const int s = upper_index(rb, nseg, static_cast<int32_t>(w));
+        const int s = upper_index_wave(rb, nseg, static_cast<int32_t>(w));
         const SegPlan& P = plan[s];
         const int64_t rl = w - rb[s];
         const int64_t lbeg = rl * kRegion;
@@ -776,7 +776,7 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     __shared__ uint32_t h[kRadixBins];
     __shared__ uint32_t lds[kWavesPerBlock + 1];
     const int b = blockIdx.x;
-    const int s = upper_index(cbb, nseg, b);
+    const int s = upper_index_wave(cbb, nseg, b);
     if (plan[s].mode != MODE_NORMAL) return;
     const int split = plan[s].compact_split;
     const int lb = b - cbb[s];
@@ -884,7 +884,7 @@ __global__ __launch_bounds__(kBlock) void k_recollect(const SegPlan* __restrict_
     const uint32_t stride = gridDim.x * kWavesPerBlock;
     for (uint32_t j = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; j < nov; j += stride) {
         const int32_t w = static_cast<int32_t>(ovf[j]);
-        const int s = upper_index(rb, nseg, w);
+        const int s = upper_index_wave(rb, nseg, w);
         const SegPlan& P = plan[s];
         const uint32_t cap = static_cast<uint32_t>(P.cap);
         if (P.mode != MODE_NORMAL || st[s].fallback || cap == 0) continue;
@@ -967,7 +967,7 @@ __device__ __forceinline__ Unit unit_of(int64_t q, int64_t Qc, const SegPlan* pl
     Unit u;
     if (q < Qc) {
         const uint32_t qq = static_cast<uint32_t>(q);
-        u.s = upper_index(ccb, nseg, qq);
+        u.s = upper_index_wave(ccb, nseg, qq);
         const uint32_t lq = qq - ccb[u.s];
         const uint32_t base = st[u.s].dense_off + lq * kChunk;
         u.raw = false;
@@ -978,7 +978,7 @@ __device__ __forceinline__ Unit unit_of(int64_t q, int64_t Qc, const SegPlan* pl
         u.slot = qq;
     } else {
         const uint32_t qq = static_cast<uint32_t>(q - Qc);
-        u.s = upper_index(rcb, nseg, qq);
+        u.s = upper_index_wave(rcb, nseg, qq);
         const int64_t lbeg = static_cast<int64_t>(qq - rcb[u.s]) * kChunk;
         u.raw = true;
         u.idx_base = plan[u.s].off + lbeg;
@@ -1310,7 +1310,7 @@ __global__ __launch_bounds__(kGroup) void k_stats_groups(const SegPlan* __restri
                                                          double2* __restrict__ gpart) {
     __shared__ double2 lsum[kWavesPerBlock];
     const int gi = blockIdx.x;
-    const int s = upper_index(gbb, nseg, gi);
+    const int s = upper_index_wave(gbb, nseg, gi);
     const int gl = gi - gbb[s];
     const int64_t r = rb[s] + static_cast<int64_t>(gl) * kGroup + threadIdx.x;
     const bool ok = static_cast<int>(threadIdx.x) < plan[s].nregions - gl * kGroup;
