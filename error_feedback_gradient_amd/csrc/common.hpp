@@ -146,24 +146,6 @@ __device__ __forceinline__ int upper_index(const T* a, int n, T v) {
     return lo;
 }
 
-// The same for a v that every lane of the wave holds, all 64 lanes active:
-// each round splits what is left into 64 sub-ranges and probes the first
-// element of every sub-range but the first, one per lane, so a table of up to
-// 4096 entries takes two dependent loads instead of about twelve.
-template <typename T>
-__device__ __forceinline__ int upper_index_wave(const T* a, int n, T v) {
-    int lo = 0, hi = n;  // the answer lies in [lo, hi)
-    while (hi - lo > 1) {
-        const int step = (hi - lo + kWave - 1) / kWave;
-        const int p = lo + (static_cast<int>(lane()) + 1) * step;
-        const bool le = p < hi && a[p] <= v;
-        // a is non-decreasing, so the lanes with le set are the lowest ones
-        lo += static_cast<int>(popc64(__ballot(le))) * step;
-        hi = min(lo + step, hi);
-    }
-    return lo;
-}
-
 // Exclusive scan in place of a[0..m) (uint32 or uint64) by one block of
 // kScanThreads threads, each summing a contiguous slice; total -> *tot (if
 // set) and, converted, -> *tot64 (if set).

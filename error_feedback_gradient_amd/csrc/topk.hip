@@ -102,6 +102,25 @@ constexpr uint32_t kNoKey = 0xffffffffu;           // above every 31-bit key
 
 enum : int32_t { MODE_NORMAL = 0, MODE_NONE = 1, MODE_ALL = 2 };
 
+// upper_index (largest i in [0, n) with a[i] <= v, a non-decreasing, a[0] <= v)
+// for a v that every lane of the wave holds, all 64 lanes active:
+// each round splits what is left into 64 sub-ranges and probes the first
+// element of every sub-range but the first, one per lane, so a table of up to
+// 4096 entries takes two dependent loads instead of about twelve.
+template <typename T>
+__device__ __forceinline__ int upper_index_wave(const T* a, int n, T v) {
+    int lo = 0, hi = n;  // the answer lies in [lo, hi)
+    while (hi - lo > 1) {
+        const int step = (hi - lo + kWave - 1) / kWave;
+        const int p = lo + (static_cast<int>(lane()) + 1) * step;
+        const bool le = p < hi && a[p] <= v;
+        // a is non-decreasing, so the lanes with le set are the lowest ones
+        lo += static_cast<int>(popc64(__ballot(le))) * step;
+        hi = min(lo + step, hi);
+    }
+    return lo;
+}
+
 struct alignas(16) SegPlan {
     int64_t off;        // first element in the packed buffer
     int64_t n;          // elements
