@@ -8,7 +8,10 @@
  *  - Pointers are DEVICE pointers unless the comment says "host".  All device
  *    buffers belong to the caller; the library never allocates or frees them.
  *    Scratch memory comes from a caller-provided device workspace whose size
- *    the matching *_workspace_bytes() host query returns.
+ *    the matching *_workspace_bytes() host query returns.  A workspace holds
+ *    one call's scratch until that call's work on its stream has finished:
+ *    calls in order on one stream may share a workspace; calls that can run
+ *    at the same time (on different streams) need one each.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only ENQUEUES work on that stream and returns; results are
  *    valid once the caller synchronises the stream.  No call waits for the
