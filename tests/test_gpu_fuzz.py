@@ -11,7 +11,6 @@ import pytest
 import torch
 
 import error_feedback_gradient_amd as efg
-import gen
 import oracle
 from gpu_util import assert_bits_equal, device, host, say, to_dev
 
