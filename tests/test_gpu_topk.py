@@ -258,6 +258,19 @@ def test_segmented_many_small():
     seg_check(sizes, ks, 5)
 
 
+def test_segmented_five_thousand_tensors():
+    """5,000 tensors of 1 to 400 elements (plus two long ones): the kernels'
+    64-way search for a block's tensor takes three rounds over these tables,
+    and the plan (about 560 KB) goes through the staging ring."""
+    r = gen.rng(131)
+    sizes = r.integers(1, 400, size=5000).tolist()
+    sizes[1234] = 300_007
+    sizes[4321] = 150_001
+    ks = [int(r.integers(0, s + 1)) if s < 1000 else s // 100 for s in sizes]
+    seg_check(sizes, ks, 6)
+    seg_check(sizes, ks, 7, "ties")
+
+
 def test_segmented_bert_two_steps():
     """The BERT-base layout (194 tensors, 108,888,576 elements), two chained steps."""
     dev = device()
