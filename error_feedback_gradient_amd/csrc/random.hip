@@ -681,6 +681,7 @@ __global__ __launch_bounds__(kBlock) void k_rs_mark(const float* __restrict__ x,
 
 // One lane per region r: the exact decision for each of its ccnt[r]
 // candidates; kmask[r] gets the kept slot entries, cnt[r] their number.
+constexpr int kFilterBatch = 8;  // candidates of a region whose slot entries are read at once
 __global__ __launch_bounds__(kLaneBlock) void k_rs_filter(const uint2* __restrict__ slots,
                                                           const uint32_t* __restrict__ ccnt, int64_t nw, float kf,
                                                           uint32_t key0, uint32_t key1, uint32_t step0,
@@ -693,12 +694,13 @@ __global__ __launch_bounds__(kLaneBlock) void k_rs_filter(const uint2* __restric
     const uint32_t c = ccnt[r];
     const uint2* sl = slots + r * kSlot;
     uint64_t m = 0;
-    for (uint32_t j0 = 0; j0 < c; j0 += 4) {
-        uint2 v[4];
+    for (uint32_t j0 = 0; j0 < c; j0 += kFilterBatch) {
+        // all loads issued before any is used: past the count reads the last candidate
+        uint2 v[kFilterBatch];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = j0 + t < c ? sl[j0 + t] : make_uint2(0u, 0u);
+        for (int t = 0; t < kFilterBatch; ++t) v[t] = sl[min(j0 + t, c - 1)];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < kFilterBatch; ++t) {
             if (j0 + t < c) {
                 const uint32_t i = v[t].y;
                 uint32_t c0 = i >> 2, c1 = 0u, c2 = step0, c3 = step1;
@@ -719,6 +721,7 @@ __global__ __launch_bounds__(kLaneBlock) void k_rs_filter(const uint2* __restric
 // (x, i) and e[i] = +0.  When the candidate slots decide, one lane per region
 // walks its keep mask; otherwise one wave per region reads its bitmap words
 // (kWordsPerLane per lane, in order).  Both grid-stride.
+constexpr int kWriteBatch = 4;  // kept entries of a region whose slot entries are read at once
 __global__ __launch_bounds__(kBlock) void k_rs_write(float* __restrict__ e, int64_t n, int64_t nw,
                                                      const uint32_t* __restrict__ bm, const uint2* __restrict__ slots,
                                                      const uint64_t* __restrict__ kmask,
@@ -733,11 +736,27 @@ __global__ __launch_bounds__(kBlock) void k_rs_write(float* __restrict__ e, int6
             if (!m) continue;
             int64_t pos = off[r] + tsum[r / kScanTile];
             const uint2* sl = slots + r * kSlot;
-            for (; m && pos < cap; m &= m - 1, ++pos) {
-                const uint2 c = sl[__ffsll(static_cast<unsigned long long>(m)) - 1];
-                vals[pos] = __uint_as_float(c.x);
-                idx[pos] = static_cast<int32_t>(c.y);
-                e[c.y] = 0.0f;
+            while (m && pos < cap) {
+                // the next kWriteBatch kept entries' slot reads go out together;
+                // past the last kept one, the first is read again and not used
+                uint2 c[kWriteBatch];
+                uint64_t mm = m;
+                const int first = __ffsll(static_cast<unsigned long long>(m)) - 1;
+#pragma unroll
+                for (int t = 0; t < kWriteBatch; ++t) {
+                    c[t] = sl[mm ? __ffsll(static_cast<unsigned long long>(mm)) - 1 : first];
+                    mm &= mm - 1;
+                }
+#pragma unroll
+                for (int t = 0; t < kWriteBatch; ++t) {
+                    if (m && pos < cap) {
+                        vals[pos] = __uint_as_float(c[t].x);
+                        idx[pos] = static_cast<int32_t>(c[t].y);
+                        e[c[t].y] = 0.0f;
+                        m &= m - 1;
+                        ++pos;
+                    }
+                }
             }
         }
         return;
