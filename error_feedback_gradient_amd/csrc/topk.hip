@@ -97,6 +97,7 @@ constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
 constexpr int kChunk = EFG_CHUNK;                  // entries per block-unit in select and emit
 static_assert(kChunk % kBlock == 0, "k_write: each wave takes kChunk / kBlock rows of 64 entries");
 constexpr int kRadixBins = 2048;
+constexpr int kHistCopies = 8;                     // copies of a histogram when a call has few tensors (1 or this)
 constexpr int kMaxGrid = 2048;
 constexpr uint32_t kNoKey = 0xffffffffu;           // above every 31-bit key
 
@@ -194,7 +195,7 @@ static Layout make_layout(const Plan& p) {
     L.static_end = at;
     L.header = take(sizeof(Header));
     L.state = take(ns * sizeof(SegState));
-    L.shist = take(ns * kSampleBins * 4);
+    L.shist = take(ns * static_cast<size_t>(p.hcopies) * kSampleBins * 4);
     L.rhist = take(3 * ns * static_cast<size_t>(p.hcopies) * kRadixBins * 4);
     L.grp_cnt = take(static_cast<size_t>(p.G) * 4);
     L.zero_end = at;
@@ -313,11 +314,13 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
     // Sample blocks: many small tensors would otherwise give thousands of blocks,
     // each clearing and flushing a whole 4096-bin histogram; beyond about
     // kSampleBlocksTarget blocks every block takes several chunk groups.
-    // A tensor's compaction and histogram blocks run on every XCD; their
-    // atomics on one histogram meet beyond the L2s and are applied in turn.
-    // With few tensors (few histograms, many blocks each) every histogram gets
-    // eight copies; with many, the blocks per tensor are few anyway.
-    p.hcopies = nseg <= 8 ? 8 : 1;
+    // A tensor's sampling, compaction and histogram blocks run on every XCD;
+    // their atomics on one histogram meet beyond the L2s and are applied in
+    // turn.  With few tensors (few histograms, many blocks each) every sample
+    // and radix histogram gets eight copies, one per XCD (blocks are handed to
+    // the XCDs in turn, so block b adds to copy b % 8); with many tensors the
+    // blocks per tensor are few anyway.
+    p.hcopies = nseg <= 8 ? kHistCopies : 1;
     p.sample_rounds = static_cast<int32_t>(std::min<int64_t>(
         kSampleRoundsMax, std::max<int64_t>(1, cdiv(p.SB, static_cast<int64_t>(kSampleBlockChunks) * kSampleBlocksTarget))));
     p.SB = 0;
@@ -351,7 +354,7 @@ __global__ __launch_bounds__(kBlock) void k_init(uint4* zero, int64_t nvec, uint
 __global__ __launch_bounds__(kSampleBlock) void k_sample(const float* __restrict__ g, const float* __restrict__ e,
                                                    const SegPlan* __restrict__ plan, int32_t nseg,
                                                    const int32_t* __restrict__ sbb, int32_t rounds,
-                                                   uint32_t* __restrict__ shist) {
+                                                   uint32_t* __restrict__ shist, int32_t hcopies) {
     __shared__ uint32_t h[kSampleBins];
     const int b = blockIdx.x;
     const int s = upper_index_wave(sbb, nseg, b);
@@ -391,9 +394,32 @@ __global__ __launch_bounds__(kSampleBlock) void k_sample(const float* __restrict
                 if (ok[u][j]) atomicAdd(&h[key_of(xs[u][j]) >> kSampleShift], 1u);
     }
     __syncthreads();
-    uint32_t* gh = shist + static_cast<size_t>(s) * kSampleBins;
+    uint32_t* gh = shist + (static_cast<size_t>(s) * hcopies + blockIdx.x % hcopies) * kSampleBins;
     for (int i = threadIdx.x; i < kSampleBins; i += kSampleBlock)
         if (h[i]) atomicAdd(&gh[i], h[i]);
+}
+
+// hsum[i] = sum over the kHistCopies copies (each `stride` uint4 apart) of
+// g4[i], for the PER * kBlock uint4 of a histogram; all of a thread's loads
+// are issued before any is used
+template <int PER>
+__device__ __forceinline__ void sum_copies(const uint4* g4, int stride, uint4* hsum) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const int i = threadIdx.x + r * kBlock;
+        uint4 w[kHistCopies];
+#pragma unroll
+        for (int c = 0; c < kHistCopies; ++c) w[c] = g4[c * stride + i];
+        uint4 v = w[0];
+#pragma unroll
+        for (int c = 1; c < kHistCopies; ++c) {
+            v.x += w[c].x;
+            v.y += w[c].y;
+            v.z += w[c].z;
+            v.w += w[c].w;
+        }
+        hsum[i] = v;
+    }
 }
 
 // Finds, in a histogram of PER*kBlock bins, the bin d such that the count
@@ -427,18 +453,24 @@ __device__ __forceinline__ bool find_rank_bin(const uint32_t* hist, uint32_t wan
 }
 
 __global__ __launch_bounds__(kBlock) void k_sample_select(const SegPlan* __restrict__ plan,
-                                                          const uint32_t* __restrict__ shist,
+                                                          const uint32_t* __restrict__ shist, int32_t hcopies,
                                                           SegState* __restrict__ st) {
     __shared__ uint32_t lds[kWavesPerBlock + 1];
     __shared__ uint32_t s_tlo, s_thi;
+    __shared__ uint4 hsum[kSampleBins / 4];
     const int s = blockIdx.x;
     if (plan[s].mode != MODE_NORMAL || plan[s].direct) return;
     if (threadIdx.x == 0) {
         s_tlo = 0;        // nothing found: every element is a candidate
         s_thi = kNoKey;   // nothing found: no element is cleared in the stream
     }
+    // the tensor's sample histogram is the sum of its copies
+    const uint32_t* h = shist + static_cast<size_t>(s) * hcopies * kSampleBins;
+    if (hcopies > 1) {
+        sum_copies<kSampleBins / 4 / kBlock>(reinterpret_cast<const uint4*>(h), kSampleBins / 4, hsum);
+        h = reinterpret_cast<const uint32_t*>(hsum);
+    }
     __syncthreads();
-    const uint32_t* h = shist + static_cast<size_t>(s) * kSampleBins;
     int d;
     uint32_t above;
     if (find_rank_bin<kSampleBins / kBlock>(h, static_cast<uint32_t>(plan[s].sample_rank), &d, &above, lds))
@@ -1078,16 +1110,13 @@ __global__ __launch_bounds__(kBlock) void k_digit(int pass, const SegPlan* __res
     const int nb = pass == 0 ? 2048 : 1024;
     // the tensor's histogram of this pass is the sum of its copies
     const uint4* gh = reinterpret_cast<const uint4*>(radix_hist(const_cast<uint32_t*>(rhist), pass, s, 0, nseg, hcopies));
-    for (int i = threadIdx.x; i < nb / 4; i += kBlock) {
-        uint4 v = gh[i];
-        for (int c = 1; c < hcopies; ++c) {
-            const uint4 w = gh[c * (kRadixBins / 4) + i];
-            v.x += w.x;
-            v.y += w.y;
-            v.z += w.z;
-            v.w += w.w;
-        }
-        hsum[i] = v;
+    if (hcopies > 1) {
+        if (pass == 0)
+            sum_copies<2048 / 4 / kBlock>(gh, kRadixBins / 4, hsum);
+        else
+            sum_copies<1024 / 4 / kBlock>(gh, kRadixBins / 4, hsum);
+    } else {
+        for (int i = threadIdx.x; i < nb / 4; i += kBlock) hsum[i] = gh[i];
     }
     __syncthreads();
     const uint32_t* hs = reinterpret_cast<const uint32_t*>(hsum);
@@ -1467,9 +1496,9 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
 
     if (P.any_normal && P.SB > 0) {
         EF_TRY(launch("topk_sample_hist", k_sample, dim3(static_cast<unsigned>(P.SB)), dim3(kSampleBlock), s, g,
-                      static_cast<const float*>(e), plan, nseg, sbb, P.sample_rounds, shist));
+                      static_cast<const float*>(e), plan, nseg, sbb, P.sample_rounds, shist, P.hcopies));
         EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
-                      static_cast<const uint32_t*>(shist), st));
+                      static_cast<const uint32_t*>(shist), P.hcopies, st));
     }
     const dim3 sgrid(static_cast<unsigned>(cdiv(P.R, kStreamWaves)));
     if (stats)
