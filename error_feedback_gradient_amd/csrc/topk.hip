@@ -1246,6 +1246,7 @@ __global__ __launch_bounds__(kEmitScanBlock) void k_emit_scan(const SegPlan* __r
 //     block's earlier waves, of the wave's earlier rows, and of the row's lower
 //     lanes (ballots).  Kept entries get e = +0 unless the stream cleared them
 //     (key >= thi); dropped ones the stream cleared get x back.
+template <bool STATS>
 __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ plan, int32_t nseg,
                                                   const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
                                                   const uint32_t* __restrict__ rcb,
@@ -1275,13 +1276,20 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
 #pragma unroll
             for (int i = 0; i < kRows; ++i) ids[i] = u.id[min(j0 + i * kWave, u.cnt - 1)];
         }
+        // per row: the entries above T, equal to T, and with a key >= thi (a
+        // dropped one of those gets x back); wave-uniform, kept for the placing
+        // loop, which skips rows where all three are empty
+        uint64_t bgs[kRows], bes[kRows], bhs[kRows];
         uint32_t ngt = 0, neq = 0;  // this wave's counts (wave-uniform)
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {
             const bool ok = j0 + i * kWave < u.cnt;
             const uint32_t key = key_of(v[i]);
-            ngt += popc64(__ballot(ok && key > T));
-            neq += popc64(__ballot(ok && key == T));
+            bgs[i] = __ballot(ok && key > T);
+            bes[i] = __ballot(ok && key == T);
+            bhs[i] = __ballot(ok && key >= thi);
+            ngt += popc64(bgs[i]);
+            neq += popc64(bes[i]);
         }
         if (l == 0) {
             wgt[wv] = ngt;
@@ -1298,8 +1306,9 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
             const uint32_t j = j0 + i * kWave;
             const bool ok = j < u.cnt;
             const uint32_t key = key_of(v[i]);
+            const uint64_t bg = bgs[i], be = bes[i];
+            if (!STATS && (bg | be | bhs[i]) == 0) continue;  // nothing to place or restore in this row
             const bool gt = ok && key > T, eq = ok && key == T;
-            const uint64_t bg = __ballot(gt), be = __ballot(eq);
             const uint32_t g_before = gtb + count_below(bg), e_before = eqb + count_below(be);
             gtb += popc64(bg);
             eqb += popc64(be);
@@ -1307,8 +1316,10 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
             int64_t pos = -1;
             if (gt) pos = static_cast<int64_t>(g_before) + min(r, e_before);
             else if (eq && e_before < r) pos = static_cast<int64_t>(g_before) + e_before;
-            if (pos >= 0) sent += sq_finite(v[i], key);
-            else drop += sq_finite(v[i], key);
+            if (STATS) {
+                if (pos >= 0) sent += sq_finite(v[i], key);
+                else drop += sq_finite(v[i], key);
+            }
             const int64_t id = u.raw ? u.idx_base + j : static_cast<int64_t>(ids[i]);
             if (id < seg_lo || id >= seg_hi) continue;  // only if the workspace was overwritten meanwhile
             if (pos >= 0 && pos < kseg) {
@@ -1319,7 +1330,7 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
                 e[id] = v[i];
             }
         }
-        if (cpart) {
+        if (STATS) {
             // fixed-order block sum of the unit's sent and dropped energy
             sent = wave_sum(sent);
             drop = wave_sum(drop);
@@ -1540,8 +1551,9 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
                   static_cast<const float*>(dval), static_cast<const float*>(e), cgt, ceq, rgt, req));
     EF_TRY(launch("topk_emit_scan", k_emit_scan, dim3(static_cast<unsigned>(nseg)), dim3(kEmitScanBlock), s, plan,
                   static_cast<const SegState*>(st), static_cast<const uint32_t*>(rcb), cgt, ceq, rgt, req));
-    EF_TRY(launch("topk_write", k_write, dim3(gu), dim3(kBlock), s, plan, nseg, static_cast<const SegState*>(st),
-                  static_cast<const uint32_t*>(ccb), static_cast<const uint32_t*>(rcb), static_cast<const Header*>(hdr),
+    EF_TRY(launch("topk_write", stats ? k_write<true> : k_write<false>, dim3(gu), dim3(kBlock), s, plan, nseg,
+                  static_cast<const SegState*>(st), static_cast<const uint32_t*>(ccb),
+                  static_cast<const uint32_t*>(rcb), static_cast<const Header*>(hdr),
                   static_cast<const float*>(dval), static_cast<const int32_t*>(didx),
                   static_cast<const uint32_t*>(cgt), static_cast<const uint32_t*>(ceq),
                   static_cast<const uint32_t*>(rgt), static_cast<const uint32_t*>(req), e, vals, idx, cpart, rpart));
