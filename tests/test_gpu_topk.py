@@ -129,6 +129,22 @@ def sampled_chunk_mask(n):
     return m
 
 
+def test_upper_edge_below_threshold_gives_x_back():
+    """The sample sees N(0,1) values only, while k large values sit in chunks it
+    does not read: its upper edge T_hi lies below the true threshold, so the
+    stream clears e for N(0,1) tail values that are not kept, and the emit must
+    give each of them x back (the fast path, not the fallback: the candidates
+    fit their slots).  Spread so that no region holds more than a few."""
+    n, k = 1_000_000, 1000
+    m = sampled_chunk_mask(n)
+    g = gen.normal_small(n, 122)
+    free = np.flatnonzero(~m)
+    big = free[np.linspace(0, free.size - 1, k).astype(np.int64)]
+    g[big] = gen.normal_small(k, 123, scale=1.0) + np.float32(20.0)
+    check(g, gen.normal_small(n, 124, scale=1e-3), k, what="T_hi below T")
+    check(g, gen.normal_small(n, 124, scale=1e-3), k + 300, what="T_hi below T, k beyond the planted values")
+
+
 def test_candidates_beyond_capacity_fall_back():
     """The sample sees only small values, so the threshold it gives lets most
     of the tensor through: more candidates than the slots hold in total, and
