@@ -111,10 +111,15 @@ def cpu_baseline(n_sample: int, k_sample: int):
     }
 
 
+# chained steps of each workload's recipe; the default number of timed steps
+CHAIN_STEPS = {"flat": 10, "bert": 20, "sign": 50, "large": 5}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: the workload's chained steps: 10 flat, 20 bert, 50 sign, else 5)")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--n", type=int, default=None, help="override N (testing only)")
     ap.add_argument("--k", type=int, default=None, help="override k (testing only)")
@@ -124,6 +129,8 @@ def main():
     ap.add_argument("--workload", default="large", choices=["large", "flat", "bert", "sign", "decode", "quant", "random", "adam"],
                     help="large (default, the headline) or one of the other workloads")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = CHAIN_STEPS.get(args.workload, 5)
     if args.gpus != 1:
         print(f"bench.py: this library measures one GPU's share of the gradient; --gpus {args.gpus} is not "
               "supported (run with --gpus 1).", file=sys.stderr, flush=True)
