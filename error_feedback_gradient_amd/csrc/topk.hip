@@ -98,6 +98,7 @@ constexpr int kChunk = EFG_CHUNK;                  // entries per block-unit in 
 static_assert(kChunk % kBlock == 0, "k_write: each wave takes kChunk / kBlock rows of 64 entries");
 constexpr int kRadixBins = 2048;
 constexpr int kHistCopies = 8;                     // copies of a histogram when a call has few tensors (1 or this)
+constexpr int64_t kCompactBlocksMax = 2048;        // compaction blocks the GPU holds at once (8 per CU)
 constexpr int kMaxGrid = 2048;
 constexpr uint32_t kNoKey = 0xffffffffu;           // above every 31-bit key
 
@@ -331,6 +332,23 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
     for (int32_t s = 0; s < nseg; ++s) {
         p.sbb[s] = static_cast<int32_t>(p.SB);
         p.SB += cdiv(p.seg[s].sample_chunks, static_cast<int64_t>(kSampleBlockChunks) * p.sample_rounds);
+    }
+    // Compaction blocks: splitting a group pays while the grid fits on the
+    // GPU at once; beyond kCompactBlocksMax blocks a second round would start,
+    // so the splits are halved until the grid fits or every split is 1.
+    while (p.CB > kCompactBlocksMax) {
+        bool any = false;
+        for (auto& P : p.seg)
+            if (P.compact_split > 1) {
+                P.compact_split /= 2;
+                any = true;
+            }
+        if (!any) break;
+        p.CB = 0;
+        for (int32_t s = 0; s < nseg; ++s) {
+            p.cbb[s] = static_cast<int32_t>(p.CB);
+            if (p.seg[s].cap > 0) p.CB += static_cast<int64_t>(p.seg[s].ngroups) * p.seg[s].compact_split;
+        }
     }
     p.rb[nseg] = static_cast<int32_t>(p.R);
     p.gbb[nseg] = static_cast<int32_t>(p.G);
