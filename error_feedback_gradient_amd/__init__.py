@@ -42,6 +42,7 @@ SIGNATURES = {
                                      _u32, _p]),
     "sparse_decode_accumulate": (C.c_int, [_p, _i64, _i32, _p, _p, _p, _p, _p]),
     "sgd_apply": (C.c_int, [_p, _p, _i64, _f, _p]),
+    "sparse_decode_sgd": (C.c_int, [_p, _p, _i64, _i32, _p, _p, _p, _f, _p, _p]),
     "encode_bitmap": (C.c_int, [_p, _i64, _i64, _p, _p]),
     "decode_bitmap_workspace_bytes": (_sz, [_i64]),
     "decode_bitmap": (C.c_int, [_p, _i64, _p, _i64, _p, _p, _sz, _p]),
@@ -335,6 +336,24 @@ def sgd_apply(w, G, lr):
     _need(w, torch.float32, dev, "w")
     _need(G, torch.float32, dev, "G", w.numel())
     _check(lib().sgd_apply(_ptr(w), _ptr(G), w.numel(), lr, _stream(dev)), "sgd_apply")
+    return w
+
+
+def sparse_decode_sgd(w, vals, idx, pk_off, lr, G=None, invalid=None):
+    """The receiver's step in one pass: G = the packets summed from zero (as
+    sparse_decode_accumulate on a zeroed G), then w -= lr * G (as sgd_apply).
+    G (optional float32 GPU tensor of w's size) receives the sum.  Returns w."""
+    dev = _gpu(w, "w")
+    _need(w, torch.float32, dev, "w")
+    if G is not None:
+        _need(G, torch.float32, dev, "G", w.numel())
+    _need(vals, torch.float32, dev, "vals")
+    _need(idx, torch.int32, dev, "idx")
+    _need(pk_off, torch.int64, dev, "pk_off")
+    if invalid is not None:
+        _need(invalid, torch.int32, dev, "invalid", 1)
+    _check(lib().sparse_decode_sgd(_ptr(w), _ptr(G), w.numel(), pk_off.numel() - 1, _ptr(vals), _ptr(idx),
+                                   _ptr(pk_off), lr, _ptr(invalid), _stream(dev)), "sparse_decode_sgd")
     return w
 
 

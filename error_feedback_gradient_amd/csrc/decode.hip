@@ -35,6 +35,8 @@ constexpr int kStage = EFG_DECODE_STAGE;             // staged entries per packe
 constexpr int kSearchLanes = 16;                     // lanes that search one packet together
 constexpr int kPkGroup = kBlock / kSearchLanes;      // packets searched at once per block
 
+typedef float f4 __attribute__((ext_vector_type(4)));
+
 __global__ void k_zero_u32(uint32_t* p) { *p = 0; }
 
 // entries that break the packet contract: index outside [0, n), or not above
@@ -115,9 +117,16 @@ __device__ __forceinline__ void group_lower_bound2(const int32_t* a, int64_t len
     *r1 = s1.L + __popc(static_cast<uint32_t>(__ballot(b1) >> shift) & 0xffffu);
 }
 
+// FUSED: the receiver's whole step on a G that starts at zero.  Every
+// position of the tile starts at +0 in LDS (no G load), the packets are added
+// as above, and the tile is written out whole: G (if given) = the sum, and
+// w = w - fl(lr * G), the same two roundings as sgd_apply.  One pass over w and
+// G instead of a zero fill, the scatter-add and the update.
+template <bool FUSED>
 __global__ __launch_bounds__(kBlock) void k_decode(float* __restrict__ G, int64_t n, int32_t npk,
                                                    const float* __restrict__ vals, const int32_t* __restrict__ idx,
-                                                   const int64_t* __restrict__ pk_off) {
+                                                   const int64_t* __restrict__ pk_off, float* __restrict__ w,
+                                                   float lr) {
     __shared__ float acc[kTile];
     __shared__ uint32_t touched[kTile / 32];
     __shared__ uint16_t st_loc[kStage];
@@ -128,11 +137,16 @@ __global__ __launch_bounds__(kBlock) void k_decode(float* __restrict__ G, int64_
 
     const int64_t lo = static_cast<int64_t>(blockIdx.x) * kTile;
     const int64_t hi = min(lo + kTile, n);
-    for (int i = threadIdx.x; i < kTile / 32; i += kBlock) touched[i] = 0;
+    if (FUSED) {
+        for (int i = threadIdx.x; i < kTile; i += kBlock) acc[i] = 0.0f;
+    } else {
+        for (int i = threadIdx.x; i < kTile / 32; i += kBlock) touched[i] = 0;
+    }
     __syncthreads();
 
     // first touch of a position loads G; later touches add in LDS
     auto touch = [&](uint32_t loc) {
+        if (FUSED) return;
         const uint32_t bit = 1u << (loc & 31);
         const uint32_t old = atomicOr(&touched[loc >> 5], bit);
         if (!(old & bit)) acc[loc] = G[lo + loc];
@@ -206,11 +220,32 @@ __global__ __launch_bounds__(kBlock) void k_decode(float* __restrict__ G, int64_
         }
         __syncthreads();
     }
-    for (int t = threadIdx.x; t < kTile; t += kBlock)
-        if (touched[t >> 5] & (1u << (t & 31))) G[lo + t] = acc[t];
+    if (!FUSED) {
+        for (int t = threadIdx.x; t < kTile; t += kBlock)
+            if (touched[t >> 5] & (1u << (t & 31))) G[lo + t] = acc[t];
+        return;
+    }
+    // the whole tile, four positions per thread at a time (w, G 16-byte aligned,
+    // lo a multiple of 4).  Reading w at the block's start instead, under the
+    // packet search, measured slower (its registers cost a wave per SIMD).
+    const int64_t len = hi - lo;
+    for (int t = 4 * static_cast<int>(threadIdx.x); t < len; t += 4 * kBlock) {
+        if (t + 4 <= len) {
+            const f4 a = {acc[t], acc[t + 1], acc[t + 2], acc[t + 3]};
+            f4* w4 = reinterpret_cast<f4*>(w + lo + t);
+            const f4 wv = __builtin_nontemporal_load(w4);
+            const f4 st = lr * a;
+            __builtin_nontemporal_store(wv - st, w4);
+            if (G) __builtin_nontemporal_store(a, reinterpret_cast<f4*>(G + lo + t));
+        } else {
+            for (int c = 0; c < 4 && t + c < len; ++c) {
+                const float st = lr * acc[t + c];
+                w[lo + t + c] = w[lo + t + c] - st;
+                if (G) G[lo + t + c] = acc[t + c];
+            }
+        }
+    }
 }
-
-typedef float f4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kBlock) void k_sgd(float* __restrict__ w, const float* __restrict__ G, int64_t n,
                                                 float lr) {
@@ -250,8 +285,27 @@ extern "C" int sparse_decode_accumulate(float* G, int64_t n, int32_t npk, const 
                           s, n, idx, pk_off, invalid));
     }
     if (n == 0 || npk == 0) return EF_OK;
-    return launch("decode_scatter", decode::k_decode, dim3(static_cast<unsigned>(cdiv(n, decode::kTile))),
-                  dim3(decode::kBlock), s, G, n, npk, vals, idx, pk_off);
+    return launch("decode_scatter", decode::k_decode<false>, dim3(static_cast<unsigned>(cdiv(n, decode::kTile))),
+                  dim3(decode::kBlock), s, G, n, npk, vals, idx, pk_off, static_cast<float*>(nullptr), 0.0f);
+}
+
+extern "C" int sparse_decode_sgd(float* w, float* G, int64_t n, int32_t npk, const float* vals, const int32_t* idx,
+                                 const int64_t* pk_off, float lr, uint32_t* invalid, void* stream) {
+    if (n < 0 || n > kMaxElems) return fail(EF_EINVAL, "n=%lld outside [0, 2^31-1]", (long long)n);
+    if (npk < 0) return fail(EF_EINVAL, "npk must be >= 0");
+    if (npk > 0 && (!vals || !idx || !pk_off)) return fail(EF_EINVAL, "vals, idx and pk_off must not be NULL");
+    if (n > 0 && !w) return fail(EF_EINVAL, "w must not be NULL");
+    if (n > 0 && (!aligned16(w) || (G && !aligned16(G)))) return fail(EF_EINVAL, "w and G must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (invalid) {
+        EF_TRY(launch("decode_zero", decode::k_zero_u32, dim3(1), dim3(1), s, invalid));
+        if (npk > 0)
+            EF_TRY(launch("decode_validate", decode::k_validate, dim3(static_cast<unsigned>(npk)), dim3(decode::kBlock),
+                          s, n, idx, pk_off, invalid));
+    }
+    if (n == 0) return EF_OK;
+    return launch("decode_sgd", decode::k_decode<true>, dim3(static_cast<unsigned>(cdiv(n, decode::kTile))),
+                  dim3(decode::kBlock), s, G, n, npk, vals, idx, pk_off, w, lr);
 }
 
 extern "C" int sgd_apply(float* w, const float* G, int64_t n, float lr, void* stream) {

@@ -262,6 +262,18 @@ int sparse_decode_accumulate(float* G, int64_t n, int32_t npk, const float* vals
  *   w_i = w_i - (lr * G_i)     (product rounded to float32, then the subtraction) */
 int sgd_apply(float* w, const float* G, int64_t n, float lr, void* stream);
 
+/* The receiver's step in one pass, [SPARSE] "详细算法流程" steps 6-7: G starts
+ * at +0 everywhere, the packets are added exactly as sparse_decode_accumulate
+ * adds them, and w_i = w_i - (lr * G_i) as sgd_apply computes it.  Bit for bit
+ * the same w (and G) as zeroing G, sparse_decode_accumulate, then sgd_apply,
+ * with one read and one write of w and one write of G instead of three passes.
+ * G (nullable) receives the sum; w and G are n floats, 16-byte aligned, and
+ * must not overlap.  Packets, pk_off and *invalid as for
+ * sparse_decode_accumulate. */
+int sparse_decode_sgd(float* w, float* G, int64_t n, int32_t npk, const float* vals,
+                      const int32_t* idx, const int64_t* pk_off, float lr,
+                      uint32_t* invalid, void* stream);
+
 /* ------------------------------------------------------------------------
  * Index encodings, [SPARSE] "索引编码压缩" (index encoding).  Inputs are index
  * lists as top-k emits them: strictly increasing, in [0, n).

@@ -143,6 +143,13 @@ def test_decode_and_sgd_argument_checks():
     assert L.sgd_apply(FAKE, FAKE, -1, 0.1, None) == efg.EF_EINVAL
     assert L.sgd_apply(FAKE_ODD, FAKE, 16, 0.1, None) == efg.EF_EINVAL
     assert L.sgd_apply(None, FAKE, 16, 0.1, None) == efg.EF_EINVAL
+    # the fused receiver step: sizes, missing packets, missing or misaligned w and G
+    assert L.sparse_decode_sgd(FAKE, FAKE, -1, 1, FAKE, FAKE, FAKE, 0.1, None, None) == efg.EF_EINVAL
+    assert L.sparse_decode_sgd(FAKE, FAKE, 10, -1, FAKE, FAKE, FAKE, 0.1, None, None) == efg.EF_EINVAL
+    assert L.sparse_decode_sgd(FAKE, FAKE, 10, 2, FAKE, None, FAKE, 0.1, None, None) == efg.EF_EINVAL
+    assert L.sparse_decode_sgd(None, FAKE, 10, 0, None, None, None, 0.1, None, None) == efg.EF_EINVAL
+    assert L.sparse_decode_sgd(FAKE_ODD, FAKE, 16, 0, None, None, None, 0.1, None, None) == efg.EF_EINVAL
+    assert L.sparse_decode_sgd(FAKE, FAKE_ODD, 16, 0, None, None, None, 0.1, None, None) == efg.EF_EINVAL
 
 
 def test_encoding_argument_checks():

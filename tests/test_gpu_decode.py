@@ -109,6 +109,80 @@ def test_decode_full_size_sixteen_packets_then_sgd():
         assert_bits_equal(host(back), ip, f"delta round trip packet {p}")
 
 
+def fused(w0, vals, idx, off, lr, with_G=True):
+    """sparse_decode_sgd on the GPU: (w, G or None, invalid count)."""
+    dev = device()
+    wd = to_dev(w0, dev)
+    Gd = torch.full((w0.size,), 7.0, dtype=torch.float32, device=dev) if with_G else None
+    inv = torch.zeros(1, dtype=torch.int32, device=dev)
+    efg.sparse_decode_sgd(wd, to_dev(vals, dev), to_dev(idx, dev), to_dev(off, dev), lr, G=Gd, invalid=inv)
+    return host(wd), (host(Gd) if with_G else None), int(host(inv)[0])
+
+
+def fused_ref(w0, vals, idx, off, lr):
+    """The oracle's two steps: decode onto a zero G, then the SGD update."""
+    G = oracle.decode(np.zeros(w0.size, np.float32), vals, idx, off)
+    return oracle.sgd(w0, G, lr), G
+
+
+@pytest.mark.parametrize("n,P,k", [(1, 1, 1), (5, 2, 3), (5000, 16, 100), (100_003, 16, 5000), (4096, 3, 4096),
+                                   (4097, 2, 4097), (1_000_000, 1, 3), (777, 40, 700), (300_000, 300, 2000)])
+@pytest.mark.parametrize("lr", [0.1, 1.0])
+def test_decode_sgd_fused(n, P, k, lr):
+    """The one-pass receiver step equals zeroing G, the decode and the SGD
+    update, bit for bit, for w and G (ragged last tiles, empty tiles, tiles
+    fuller than the staging area)."""
+    vals, idx, off = packets_from(n, P, min(k, n), 310)
+    w0 = gen.normal_small(n, 311)
+    w, G, inv = fused(w0, vals, idx, off, lr)
+    w_ref, G_ref = fused_ref(w0, vals, idx, off, lr)
+    assert_bits_equal(G, G_ref, f"fused G n={n} P={P} k={k}")
+    assert_bits_equal(w, w_ref, f"fused w n={n} P={P} k={k}")
+    assert inv == 0
+
+
+def test_decode_sgd_fused_edges():
+    dev = device()
+    n = 10_001
+    w0 = gen.normal_small(n, 312)
+    w0[:6] = np.array([0.0, -0.0, np.inf, -np.inf, 1e-45, -3.4e38], np.float32)
+    # no packets: G = +0 everywhere and w unchanged (w - 0.1 * +0 keeps -0)
+    empty = np.zeros(1, np.int64)
+    w, G, _ = fused(w0, np.zeros(0, np.float32), np.zeros(0, np.int32), empty, 0.1)
+    assert_bits_equal(w, w0, "no packets: w")
+    assert_bits_equal(G, np.zeros(n, np.float32), "no packets: G")
+    # without G, and with out-of-range / out-of-order entries (skipped and counted)
+    vals, idx, off = packets_from(n, 6, 0, 313, sizes=[0, 50, 0, 3000, 70, 1])
+    w, _, inv = fused(w0, vals, idx, off, 0.5, with_G=False)
+    assert_bits_equal(w, fused_ref(w0, vals, idx, off, 0.5)[0], "no G output")
+    assert inv == 0
+    bad = idx.copy()
+    bad[off[1]] = n + 5
+    bad[off[3] + 3] = bad[off[3] + 2]
+    w, G, inv = fused(w0, vals, bad, off, 0.5)
+    assert inv >= 2
+    assert np.all(np.isfinite(G))
+
+
+def test_decode_sgd_fused_full_size():
+    """The decode workload's 16 packets at N = 25.6M in one pass: w and G equal
+    the oracle's decode onto zero followed by its SGD update."""
+    n, P, k = gen.DECODE_N, gen.DECODE_PACKETS, gen.DECODE_K
+    vals, idx = [], []
+    for p in range(P):
+        g = gen.decode_packet_gradient(p)
+        sel = np.sort(np.argpartition(-np.abs(g), k - 1)[:k]).astype(np.int32)
+        idx.append(sel)
+        vals.append(g[sel])
+    off = np.concatenate([[0], np.cumsum([k] * P)]).astype(np.int64)
+    vals, idx = np.concatenate(vals), np.concatenate(idx)
+    w0 = gen.decode_weights()
+    w, G, _ = fused(w0, vals, idx, off, gen.DECODE_LR)
+    w_ref, G_ref = fused_ref(w0, vals, idx, off, gen.DECODE_LR)
+    assert_bits_equal(G, G_ref, "fused G full size")
+    assert_bits_equal(w, w_ref, "fused w full size")
+
+
 @pytest.mark.parametrize("n", [1, 3, 4, 5, 1000, 4099, 1_000_003])
 @pytest.mark.parametrize("lr", [0.1, 1.0, 0.0])
 def test_sgd_small(n, lr):
