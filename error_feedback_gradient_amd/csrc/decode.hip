@@ -228,16 +228,25 @@ __global__ __launch_bounds__(kBlock) void k_decode(float* __restrict__ G, int64_
     // the whole tile, four positions per thread at a time (w, G 16-byte aligned,
     // lo a multiple of 4).  Reading w at the block's start instead, under the
     // packet search, measured slower (its registers cost a wave per SIMD).
+    // All of a thread's w loads go out together.
+    constexpr int kQuads = kTile / (4 * kBlock);
+    static_assert(kTile % (4 * kBlock) == 0, "a tile is whole quads of every thread");
     const int64_t len = hi - lo;
-    for (int t = 4 * static_cast<int>(threadIdx.x); t < len; t += 4 * kBlock) {
+    f4 wv[kQuads];
+#pragma unroll
+    for (int r = 0; r < kQuads; ++r) {
+        const int t = 4 * (static_cast<int>(threadIdx.x) + r * kBlock);
+        if (t + 4 <= len) wv[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(w + lo + t));
+    }
+#pragma unroll
+    for (int r = 0; r < kQuads; ++r) {
+        const int t = 4 * (static_cast<int>(threadIdx.x) + r * kBlock);
         if (t + 4 <= len) {
             const f4 a = {acc[t], acc[t + 1], acc[t + 2], acc[t + 3]};
-            f4* w4 = reinterpret_cast<f4*>(w + lo + t);
-            const f4 wv = __builtin_nontemporal_load(w4);
             const f4 st = lr * a;
-            __builtin_nontemporal_store(wv - st, w4);
+            __builtin_nontemporal_store(wv[r] - st, reinterpret_cast<f4*>(w + lo + t));
             if (G) __builtin_nontemporal_store(a, reinterpret_cast<f4*>(G + lo + t));
-        } else {
+        } else if (t < len) {
             for (int c = 0; c < 4 && t + c < len; ++c) {
                 const float st = lr * acc[t + c];
                 w[lo + t + c] = w[lo + t + c] - st;
