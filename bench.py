@@ -224,6 +224,8 @@ def main():
     if not ok:
         raise SystemExit("bench: the last step's packet is not the top-k of its input")
 
+    del grads
+    add_gbps = add_ceiling(dev)  # before the copies: those calibrate the counters
     copy_gbps = copy_ceiling(dev)
 
     result = {
@@ -263,18 +265,40 @@ def main():
             "launches": launches,
         },
         "copy_ceiling_GBps": copy_gbps,
+        "torch_add_GBps": add_gbps,
         "kernel_ms_one_step": breakdown,
         "step_ms": steps_ms,
         "compress_only_ms": compress_ms,
         "verified": ok,
     }
     if not args.no_cpu_baseline:
-        del grads
         log(f"bench: CPU oracle on {args.cpu_sample:,} elements")
         result["cpu_baseline"] = cpu_baseline(args.cpu_sample, max(1, args.cpu_sample // 1000))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def add_ceiling(dev):
+    """torch's own elementwise a += b over 2^29 float32, ten times: read a, read
+    b, write a, the streaming pass's 12 B/element with no selection work.  GB/s
+    on that traffic, beside the streaming kernel's."""
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    a = torch.zeros(1 << 29, dtype=torch.float32, device=dev)
+    b = torch.ones_like(a)
+    a.add_(b)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        a.add_(b)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    gbps = 12 * a.numel() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del a, b
+    return gbps
 
 
 def copy_ceiling(dev):
