@@ -317,6 +317,14 @@ def ef_random_sparsify(g, e, k, seed, step, cap=None, vals=None, idx=None, count
 
 
 # ---------------------------------------------------------------- decode / sgd
+def _packets(vals, idx, pk_off):
+    """Packet count passed to the library.  Packets without a single entry
+    between them come as empty (NULL) vals/idx, which the library refuses for
+    npk > 0; pk_off must then describe only empty packets, which add nothing,
+    so they are passed as none."""
+    return 0 if vals.numel() == 0 or idx.numel() == 0 else pk_off.numel() - 1
+
+
 def sparse_decode_accumulate(G, vals, idx, pk_off, invalid=None):
     """G[idx] += vals packet by packet, in packet order.  pk_off: int64 GPU tensor [npk+1]."""
     dev = _gpu(G, "G")
@@ -326,7 +334,7 @@ def sparse_decode_accumulate(G, vals, idx, pk_off, invalid=None):
     _need(pk_off, torch.int64, dev, "pk_off")
     if invalid is not None:
         _need(invalid, torch.int32, dev, "invalid", 1)
-    _check(lib().sparse_decode_accumulate(_ptr(G), G.numel(), pk_off.numel() - 1, _ptr(vals), _ptr(idx),
+    _check(lib().sparse_decode_accumulate(_ptr(G), G.numel(), _packets(vals, idx, pk_off), _ptr(vals), _ptr(idx),
                                           _ptr(pk_off), _ptr(invalid), _stream(dev)), "sparse_decode_accumulate")
     return G
 
@@ -352,7 +360,7 @@ def sparse_decode_sgd(w, vals, idx, pk_off, lr, G=None, invalid=None):
     _need(pk_off, torch.int64, dev, "pk_off")
     if invalid is not None:
         _need(invalid, torch.int32, dev, "invalid", 1)
-    _check(lib().sparse_decode_sgd(_ptr(w), _ptr(G), w.numel(), pk_off.numel() - 1, _ptr(vals), _ptr(idx),
+    _check(lib().sparse_decode_sgd(_ptr(w), _ptr(G), w.numel(), _packets(vals, idx, pk_off), _ptr(vals), _ptr(idx),
                                    _ptr(pk_off), lr, _ptr(invalid), _stream(dev)), "sparse_decode_sgd")
     return w
 
