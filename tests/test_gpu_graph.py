@@ -2,7 +2,7 @@
 for bit like the same calls made eagerly: single-tensor top-k with block
 encoding, layer-wise top-k calls over 12 and 60 tensors (whose plans go in
 kernel-argument chunks under capture), sign compression, random
-sparsification and the 1-bit Adam update.
+sparsification, the 1-bit Adam update and the one-pass decode + SGD.
 Every call launches kernels only (no memset or host-staged copies for these
 shapes), so capture records the whole step.  Each replay is followed by some
 eager work and a synchronisation before it is checked."""
@@ -135,3 +135,22 @@ def test_sign_random_and_onebit_in_graphs():
 
     assert run_chain(onebit, [torch.zeros(n, device=dev), torch.zeros(n, device=dev),
                               torch.from_numpy(gen.normal_small(n, 812)).to(dev)], lambda: [sgn], dev)
+
+
+def test_decode_sgd_in_a_graph():
+    """The one-pass receiver step (sparse_decode_sgd) with its invalid-entry
+    count: the weights carry from step to step, G and the count are outputs."""
+    dev = device()
+    n, P, kp = 300_007, 6, 3000
+    r = gen.rng(150)
+    idx = np.concatenate([np.sort(r.choice(n, size=kp, replace=False)) for _ in range(P)]).astype(np.int32)
+    vals = [torch.from_numpy(gen.normal_small(P * kp, 151, t)).to(dev) for t in range(T)]
+    idd = torch.from_numpy(idx).to(dev)
+    off = torch.arange(0, (P + 1) * kp, kp, dtype=torch.int64, device=dev)
+    G = torch.empty(n, device=dev)
+    inv = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def step(t, st):
+        efg.sparse_decode_sgd(st[0], vals[t], idd, off, 0.1, G=G, invalid=inv)
+
+    assert run_chain(step, [torch.from_numpy(gen.normal_small(n, 152)).to(dev)], lambda: [G, inv], dev)
