@@ -1,7 +1,8 @@
 """The largest tensor the library accepts, n = 2^31 - 1: an odd length, so
 every pass ends on a ragged tail, and kept indices reach 2^31 - 2.  Top-k
 (with the block encoding round trip of its packet), random sparsification on
-both of its decision paths, sign compression and the two Adam updates, each
+both of its decision paths, sign compression, the two Adam updates and the
+decode (onto a zero G, and in one pass with the SGD update), each
 checked by the properties that pin its result at any size and, for the
 elementwise and random paths, against the oracle at sampled positions that
 include the first and last elements."""
@@ -12,7 +13,7 @@ import torch
 import error_feedback_gradient_amd as efg
 import gen
 import oracle
-from gpu_util import assert_bits_equal, device, host, say
+from gpu_util import assert_bits_equal, device, host, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -187,4 +188,47 @@ def test_adam_max_size():
     assert_bits_equal(host(w[pd]), ow2, "w 1-bit")
     assert_bits_equal(host(v[pd]), ov, "v frozen")
     del g, e, q, m, v, w
+    torch.cuda.empty_cache()
+
+
+def test_decode_and_sgd_max_size():
+    """Four packets over n = 2^31 - 1 (entries at 0 and n - 1, a crowd in the
+    last, ragged tile), added onto a zero G and, in one pass, applied to w:
+    G and w at every packet position and at sampled others against the oracle
+    (run on the positions the packets name, which is where G can be nonzero)."""
+    dev = device()
+    n, P, kp = NMAX, 4, 20_000
+    need(dev, 10 * n)
+    r = np.random.default_rng(61)
+    idx_l = []
+    for p in range(P):
+        core = r.choice(n - 3000, size=kp - 1002, replace=False)
+        tail = np.arange(n - 1000, n) if p % 2 == 0 else r.choice(np.arange(n - 3000, n), size=1000, replace=False)
+        idx_l.append(np.unique(np.concatenate([core, tail, [0, n - 1]]))[:kp].astype(np.int64))
+    idx = np.concatenate(idx_l)
+    off = np.concatenate([[0], np.cumsum([a.size for a in idx_l])]).astype(np.int64)
+    vals = gen.normal_small(idx.size, 62)
+    # the oracle on the union of the named positions (G is zero everywhere else)
+    uni = np.unique(idx)
+    G_u = oracle.decode(np.zeros(uni.size, np.float32), vals, np.searchsorted(uni, idx).astype(np.int32), off)
+    pos = np.unique(np.concatenate([positions(63, 50_000), uni]))
+    G_exp = np.zeros(pos.size, np.float32)
+    G_exp[np.searchsorted(pos, uni)] = G_u
+    pd = torch.from_numpy(pos).to(dev)
+    vd, idd, offd = to_dev(vals, dev), torch.from_numpy(idx.astype(np.int32)).to(dev), torch.from_numpy(off).to(dev)
+    say("decode n=2^31-1: accumulate onto zero")
+    G = torch.zeros(n, device=dev)
+    inv = torch.zeros(1, dtype=torch.int32, device=dev)
+    efg.sparse_decode_accumulate(G, vd, idd, offd, invalid=inv)
+    torch.cuda.synchronize()
+    assert int(host(inv)[0]) == 0
+    assert_bits_equal(host(G[pd]), G_exp, "G accumulate")
+    say("decode n=2^31-1: one pass with the SGD update")
+    w = torch.full((n,), 0.5, dtype=torch.float32, device=dev)
+    G.fill_(7.0)
+    efg.sparse_decode_sgd(w, vd, idd, offd, 0.1, G=G)
+    torch.cuda.synchronize()
+    assert_bits_equal(host(G[pd]), G_exp, "G one pass")
+    assert_bits_equal(host(w[pd]), oracle.sgd(np.full(pos.size, 0.5, np.float32), G_exp, 0.1), "w one pass")
+    del G, w
     torch.cuda.empty_cache()
