@@ -513,6 +513,7 @@ __global__ __launch_bounds__(kBlock) void k_bd_count(const uint8_t* __restrict__
     }
 }
 
+constexpr int kBdBatch = 8;  // outputs of a thread whose offsets are read at once
 __global__ __launch_bounds__(kBlock) void k_bd_write(const uint8_t* __restrict__ counts_m1,
                                                      const uint8_t* __restrict__ offs,
                                                      const int32_t* __restrict__ blk,
@@ -532,12 +533,32 @@ __global__ __launch_bounds__(kBlock) void k_bd_write(const uint8_t* __restrict__
 #pragma unroll
         for (int t = 0; t < kPer; ++t) s += cn[t];
         uint32_t total;
-        int64_t pos = static_cast<int64_t>(csum[c]) + block_excl_scan<kBlock>(s, lds, &total);
-        for (int t = 0; t < kPer && j0 + t < m; ++t) {
-            const int64_t base = static_cast<int64_t>(bl[t]) * 256;
-            const uint32_t cntb = cn[t];
-            for (uint32_t u = 0; u < cntb; ++u, ++pos)
-                if (pos < k) idx[pos] = static_cast<int32_t>(base + offs[pos]);
+        const int64_t pos = static_cast<int64_t>(csum[c]) + block_excl_scan<kBlock>(s, lds, &total);
+        // The thread's outputs [pos, pos + s) below k, kBdBatch at a time with
+        // every offset load of a batch issued before any is used.  Output q
+        // belongs to the last of the thread's blocks that starts at or before
+        // it (blocks past m hold nothing and come last).
+        uint32_t first[kPer];
+        uint32_t run = 0;
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            first[t] = run;
+            run += cn[t];
+        }
+        const int64_t lim = std::min<int64_t>(pos + s, k);
+        for (int64_t p0 = pos; p0 < lim; p0 += kBdBatch) {
+            uint32_t o[kBdBatch];
+#pragma unroll
+            for (int u = 0; u < kBdBatch; ++u) o[u] = offs[std::min<int64_t>(p0 + u, lim - 1)];
+#pragma unroll
+            for (int u = 0; u < kBdBatch; ++u) {
+                if (p0 + u >= lim) break;
+                const uint32_t q = static_cast<uint32_t>(p0 + u - pos);
+                int32_t b = bl[0];
+#pragma unroll
+                for (int t = 1; t < kPer; ++t) b = first[t] <= q ? bl[t] : b;
+                idx[p0 + u] = b * 256 + static_cast<int32_t>(o[u]);
+            }
         }
     }
 }
