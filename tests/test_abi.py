@@ -19,7 +19,8 @@ FAKE_ODD = 0x10004
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if n not in ("defined",)))
@@ -173,7 +174,8 @@ def test_binding_never_uses_the_oracle():
     for dirpath, _, files in os.walk(pkg):
         for f in files:
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
-                text = open(os.path.join(dirpath, f)).read()
+                with open(os.path.join(dirpath, f)) as fh:
+                    text = fh.read()
                 assert "oracle" not in text.lower(), f
 
 

@@ -1,6 +1,7 @@
 """Pins of the oracle's decode (scatter-add), SGD and index encodings (CPU only)."""
 import json
 import os
+import pathlib
 
 import numpy as np
 import pytest
@@ -12,7 +13,7 @@ GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def test_decode_hand_worked():
-    d = json.load(open(os.path.join(GOLD, "decode_worked.json")))
+    d = json.loads(pathlib.Path(os.path.join(GOLD, "decode_worked.json")).read_text())
     G = oracle.decode(np.zeros(d["n"], np.float32), d["vals"], d["idx"], d["pk_off"])
     assert G.tolist() == d["G"]
     w = oracle.sgd(d["w"], G, d["lr"])

@@ -7,6 +7,7 @@ forms of the recurrences (page "1-bit Adam gradient compression", sections
 """
 import json
 import os
+import pathlib
 
 import numpy as np
 import pytest
@@ -37,7 +38,7 @@ def bits_of(a):
 
 
 def test_hand_worked():
-    d = json.load(open(os.path.join(GOLD, "sign_worked.json")))
+    d = json.loads(pathlib.Path(os.path.join(GOLD, "sign_worked.json")).read_text())
     e2, m2, s, bits, bad = oracle.sign(d["g"], d["e"], d["m"], d["beta1"], d["clip"])
     assert s.tolist() == d["sign"]
     assert bits.tolist() == d["bits"]
@@ -81,7 +82,7 @@ def test_specials():
 
 
 def test_one_bit_ratio():
-    ratio = json.load(open(os.path.join(GOLD, "ratios.json")))["one_bit_reduction"]["value"]
+    ratio = json.loads(pathlib.Path(os.path.join(GOLD, "ratios.json")).read_text())["one_bit_reduction"]["value"]
     n = 8 * 12345
     _, _, _, bits, _ = oracle.sign(np.ones(n, np.float32), np.zeros(n, np.float32),
                                    np.zeros(n, np.float32), 0.9, 5.0)

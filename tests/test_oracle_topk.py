@@ -8,6 +8,7 @@ compensation and the step-by-step algorithm).
 """
 import json
 import os
+import pathlib
 import struct
 
 import numpy as np
@@ -43,7 +44,7 @@ def same_bits(a, b):
 
 @pytest.mark.parametrize("name", ["topk_worked.json", "topk_ties_worked.json"])
 def test_hand_worked(name):
-    d = json.load(open(os.path.join(GOLD, name)))
+    d = json.loads(pathlib.Path(os.path.join(GOLD, name)).read_text())
     vals, idx, e_new, bad = oracle.topk(d["g"], d["e"], d["k"])
     assert same_bits(vals, d["vals"])
     assert idx.tolist() == d["idx"]
@@ -209,6 +210,6 @@ def test_bert_layerwise_k_total():
     assert len(ks) == 194
     assert int(off[-1]) == 108_888_576
     assert int(ks.sum()) == 368_208
-    ratios = json.load(open(os.path.join(GOLD, "ratios.json")))["layerwise_ratios"]
+    ratios = json.loads(pathlib.Path(os.path.join(GOLD, "ratios.json")).read_text())["layerwise_ratios"]
     sizes = np.diff(off)
     assert np.all(ks[sizes > 1_000_000] == sizes[sizes > 1_000_000] * ratios["large_layer"] // 1)
