@@ -134,7 +134,7 @@ struct alignas(16) SegPlan {
     int32_t mode;
     int32_t sample_chunks, sample_rank;
     int32_t sample_rank_hi, exhaustive, direct, raw_chunks;
-    int32_t compact_split;  // blocks per group in the compaction (1, 2, 4 or 8)
+    int32_t compact_split;  // blocks per group in the compaction (a power of two, 1 to 32)
     int32_t pad[5];
 };
 static_assert(sizeof(SegPlan) == 112, "SegPlan layout");
@@ -291,13 +291,15 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
                 P.sample_rank = static_cast<int32_t>(m);
                 P.sample_rank_hi = static_cast<int32_t>(m_hi);
                 P.exhaustive = exhaustive ? 1 : 0;
-                // at most about 512 expected candidates per compaction block: the
+                // at most about 512 expected candidates per compaction block (up to
+                // 32 blocks per group of 256 regions, 8 regions each): the
                 // block's time is a chain of dependent steps, and where the large
                 // values crowd into a few groups, short blocks keep those groups
                 // from holding up the rest (a flat 108.9M-element call over the
                 // BERT-base tensors: compaction 51 us with 2048, 19 us with 512)
                 const double per_group = std::min<double>(P.nregions, kGroup) * std::min<double>(region_len, kRegion * rho);
-                P.compact_split = per_group > 2048 ? 8 : per_group > 1024 ? 4 : per_group > 512 ? 2 : 1;
+                P.compact_split = 1;
+                while (P.compact_split < 32 && per_group > 512.0 * P.compact_split) P.compact_split *= 2;
             }
             P.raw_chunks = static_cast<int32_t>(cdiv(n, kChunk));
             p.any_normal = true;
