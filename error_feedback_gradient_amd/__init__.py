@@ -29,10 +29,12 @@ SIGNATURES = {
     "ef_version": (C.c_char_p, []),
     "ef_topk_workspace_bytes": (_sz, [_i64, _i64]),
     "ef_topk_compress": (C.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _sz, _p, _p, _u32, _p]),
+    "ef_topk_workspace_status": (C.c_int, [_p, _p, _p]),
     "ef_topk_segmented_workspace_bytes": (_sz, [_i32, _p, _p]),
     "ef_topk_compress_segmented": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _sz, _p, _p, _u32, _p]),
     "ef_sign_workspace_bytes": (_sz, [_i64]),
     "ef_sign_compress": (C.c_int, [_p, _p, _p, _i64, _f, _f, _p, _p, _p, _p, _p, _sz, _p]),
+    "ef_adam_scalars": (C.c_int, [C.c_double, _f, _f, _i64, _i64, C.POINTER(_f), C.POINTER(_f)]),
     "ef_adam_step": (C.c_int, [_p, _p, _p, _p, _i64, _f, _f, _f, _f, _f, _p, _p]),
     "ef_onebit_adam_update": (C.c_int, [_p, _i32, _p, _p, _p, _i64, _f, _f, _f, _f, _p, _p]),
     "ef_quantize_workspace_bytes": (_sz, [_i64]),
@@ -150,15 +152,36 @@ def ef_topk_compress(g, e, k, vals=None, idx=None, ws=None, nonfinite=None, flag
     return vals, idx
 
 
+def ef_topk_workspace_status(ws, stray=None):
+    """Device uint32 (as int32[1]): indices the last top-k call on ws found
+    out of range in its own workspace entries (0 unless the workspace was
+    overwritten during the call)."""
+    dev = ws.device
+    if stray is None:
+        stray = torch.empty(1, dtype=torch.int32, device=dev)
+    _need(stray, torch.int32, dev, "stray", 1)
+    _check(lib().ef_topk_workspace_status(_ptr(ws), _ptr(stray), _stream(dev)), "ef_topk_workspace_status")
+    return stray
+
+
 def _i64_host(a):
     import numpy as np
     a = np.ascontiguousarray(a, dtype=np.int64)
     return a, a.ctypes.data_as(C.c_void_p)
 
 
-def ef_topk_segmented_workspace_bytes(seg_off, seg_k) -> int:
+def _segment_tables(seg_off, seg_k):
+    """Host int64 copies of the segment tables and their pointers; seg_off must
+    hold one entry more than seg_k (the library reads seg_off[nseg])."""
     off, po = _i64_host(seg_off)
     ks, pk = _i64_host(seg_k)
+    if off.ndim != 1 or ks.ndim != 1 or off.size != ks.size + 1:
+        raise ValueError(f"seg_off needs len(seg_k) + 1 = {ks.size + 1} entries, has {off.size}")
+    return off, po, ks, pk
+
+
+def ef_topk_segmented_workspace_bytes(seg_off, seg_k) -> int:
+    off, po, ks, pk = _segment_tables(seg_off, seg_k)
     return int(lib().ef_topk_segmented_workspace_bytes(len(ks), po, pk))
 
 
@@ -168,8 +191,7 @@ def ef_topk_compress_segmented(g, e, seg_off, seg_k, vals=None, idx=None, ws=Non
     (host integer sequences); returns (vals, idx) concatenated in tensor order.
     stats (float64 GPU tensor of 2*nseg) receives per tensor {sum vals^2, sum new e^2}."""
     dev = _gpu(g, "g")
-    off, po = _i64_host(seg_off)
-    ks, pk = _i64_host(seg_k)
+    off, po, ks, pk = _segment_tables(seg_off, seg_k)
     K = int(ks.sum())
     _need(g, torch.float32, dev, "g", int(off[-1]) if len(off) else 0)
     _need(e, torch.float32, dev, "e", int(off[-1]) if len(off) else 0)
@@ -225,15 +247,12 @@ def ef_sign_compress(g, e, m, beta1=0.9, clip=5.0, sign_out=None, bits=None, non
 
 # ---------------------------------------------------------------- Adam around 1-bit compression
 def adam_scalars(lr, beta1, beta2, t, t_v=None):
-    """(step_size, sqrt_bc2) of step t (1-based): lr / (1 - beta1^t) and
-    sqrt(1 - beta2^t_v) (t_v = t unless the variance is frozen), in float64
-    from the float32 betas the kernels use, rounded to float32."""
-    import struct
-
-    f32 = lambda x: struct.unpack("f", struct.pack("f", x))[0]
-    t_v = t if t_v is None else t_v
-    b1, b2 = f32(beta1), f32(beta2)
-    return f32(lr / (1.0 - b1 ** t)), f32((1.0 - b2 ** t_v) ** 0.5)
+    """(step_size, sqrt_bc2) of step t (1-based) from ef_adam_scalars: lr / (1 -
+    beta1^t) and sqrt(1 - beta2^t_v), t_v = t unless the variance is frozen."""
+    ss, sb = C.c_float(0.0), C.c_float(0.0)
+    _check(lib().ef_adam_scalars(lr, beta1, beta2, t, t if t_v is None else t_v, C.byref(ss), C.byref(sb)),
+           "ef_adam_scalars")
+    return ss.value, sb.value
 
 
 def ef_adam_step(g, m, v, w, beta1, beta2, step_size, sqrt_bc2, eps, nonfinite=None):
@@ -444,8 +463,15 @@ def encode_blocks(idx, n, mask=None, counts_m1=None, offs=None, nblk_out=None, w
 
 def decode_blocks(mask, counts_m1, offs, n, k, idx=None, ws=None):
     dev = _gpu(mask, "mask")
+    nb = (n + 255) // 256
+    _need(mask, torch.uint8, dev, "mask", (nb + 7) // 8)
+    _need(counts_m1, torch.uint8, dev, "counts_m1")
+    _need(offs, torch.uint8, dev, "offs", k)
     if idx is None:
         idx = torch.empty(max(k, 1), dtype=torch.int32, device=dev)
+    _need(idx, torch.int32, dev, "idx", k)
+    if ws is not None:
+        _need(ws, torch.uint8, dev, "ws")
     if ws is None:
         ws = workspace(lib().blocks_workspace_bytes(k, n), dev)
     _check(lib().decode_blocks(_ptr(mask), _ptr(counts_m1), _ptr(offs), n, k, _ptr(idx), _ptr(ws), ws.numel(),

@@ -19,6 +19,8 @@
 // One streaming pass each, one wave per region, 128-bit non-temporal loads
 // and stores.  Square root and divisions are correctly rounded; every other
 // product and sum is rounded on its own (-ffp-contract=off).
+#include <math.h>
+
 #include <algorithm>
 #include <type_traits>
 
@@ -181,6 +183,22 @@ inline int check_common(float* m, const float* v, float* w, int64_t n, float bet
 }  // namespace efg
 
 using namespace efg;
+
+// Bias corrections of step t as the two host scalars of the update, in
+// float64 from the float32 betas, each rounded once to float32.
+extern "C" int ef_adam_scalars(double lr, float beta1, float beta2, int64_t t, int64_t t_v, float* step_size,
+                               float* sqrt_bc2) {
+    if (!step_size || !sqrt_bc2) return fail(EF_EINVAL, "ef_adam_scalars: outputs must not be NULL");
+    if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+        return fail(EF_EINVAL, "ef_adam_scalars: betas must lie in [0, 1)");
+    if (t < 1 || t_v < 1) return fail(EF_EINVAL, "ef_adam_scalars: steps count from 1");
+    if (!isfinite(lr)) return fail(EF_EINVAL, "ef_adam_scalars: lr must be finite");
+    const double bc1 = 1.0 - pow(static_cast<double>(beta1), static_cast<double>(t));
+    const double bc2 = 1.0 - pow(static_cast<double>(beta2), static_cast<double>(t_v));
+    *step_size = static_cast<float>(lr / bc1);
+    *sqrt_bc2 = static_cast<float>(sqrt(bc2));
+    return EF_OK;
+}
 
 extern "C" int ef_adam_step(const float* g, float* m, float* v, float* w, int64_t n, float beta1, float beta2,
                             float step_size, float sqrt_bc2, float eps, uint32_t* nonfinite, void* stream) {

@@ -55,9 +55,6 @@ struct WordChunk {
 // arguments (copied by the runtime at launch, so the host buffer is free as
 // soon as the call returns and no pinned staging or host wait is needed).
 int upload_words(void* dst, const uint32_t* src, size_t nwords, hipStream_t s);
-// Upload host bytes through a pinned staging ring with one asynchronous copy;
-// the host buffer is free on return.
-int upload_bytes(void* dst, const void* src, size_t bytes, hipStream_t s);
 // Fill n bytes of device memory with zero using a kernel (no memset node).
 int zero_bytes(void* dst, size_t n, hipStream_t s);
 

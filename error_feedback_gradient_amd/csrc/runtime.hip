@@ -3,6 +3,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -36,6 +37,9 @@ struct ProfRec {
     hipEvent_t start, stop;
 };
 std::mutex g_prof_mu;
+// read first by every launch, without the lock: launches do not serialise on
+// the mutex while profiling is off
+std::atomic<bool> g_prof_armed{false};
 bool g_prof_on = false;
 std::string g_prof_only;
 std::vector<ProfRec> g_prof;
@@ -48,9 +52,10 @@ void prof_clear_locked() {
 }  // namespace
 
 ProfScope::ProfScope(const char* label, hipStream_t s) : stream(s) {
+    if (!g_prof_armed.load(std::memory_order_acquire)) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof_on) return;
-    if (!g_prof_only.empty() && std::string(label).find(g_prof_only) == std::string::npos) return;
+    if (!g_prof_only.empty() && !strstr(label, g_prof_only.c_str())) return;
     ProfRec r;
     r.label = label;
     if (!g_prof_pool.empty()) {
@@ -88,51 +93,6 @@ int upload_words(void* dst, const uint32_t* src, size_t nwords, hipStream_t s) {
     return EF_OK;
 }
 
-// Ring of pinned host staging buffers for host -> device uploads of a few KB to
-// a few MB.  A slot is reused only after the copy that last used it has
-// finished (its event), so the caller's host data is free when the call
-// returns and the host waits only when it runs kStageSlots calls ahead.
-namespace {
-constexpr int kStageSlots = 8;
-struct StageSlot {
-    void* buf = nullptr;
-    size_t cap = 0;
-    hipEvent_t done = nullptr;
-    bool pending = false;
-};
-std::mutex g_stage_mu;
-StageSlot g_stage[kStageSlots];
-int g_stage_next = 0;
-}  // namespace
-
-int upload_bytes(void* dst, const void* src, size_t bytes, hipStream_t s) {
-    if (bytes == 0) return EF_OK;
-    std::lock_guard<std::mutex> lk(g_stage_mu);
-    StageSlot& sl = g_stage[g_stage_next];
-    g_stage_next = (g_stage_next + 1) % kStageSlots;
-    if (sl.pending) {
-        if (hipEventSynchronize(sl.done) != hipSuccess) return fail(EF_EHIP, "upload: wait for staging slot failed");
-        sl.pending = false;
-    }
-    if (!sl.done && hipEventCreateWithFlags(&sl.done, hipEventDisableTiming) != hipSuccess)
-        return fail(EF_EHIP, "upload: event creation failed");
-    if (sl.cap < bytes) {
-        if (sl.buf) (void)hipHostFree(sl.buf);
-        sl.buf = nullptr;
-        sl.cap = 0;
-        size_t want = bytes < (64u << 10) ? (64u << 10) : bytes;
-        if (hipHostMalloc(&sl.buf, want, hipHostMallocDefault) != hipSuccess)
-            return fail(EF_EHIP, "upload: pinned staging allocation of %zu bytes failed", want);
-        sl.cap = want;
-    }
-    memcpy(sl.buf, src, bytes);
-    hipError_t err = hipMemcpyAsync(dst, sl.buf, bytes, hipMemcpyHostToDevice, s);
-    if (err != hipSuccess) return fail(EF_EHIP, "upload: copy failed: %s", hipGetErrorString(err));
-    if (hipEventRecord(sl.done, s) != hipSuccess) return fail(EF_EHIP, "upload: event record failed");
-    sl.pending = true;
-    return EF_OK;
-}
-
 __global__ void k_zero(uint8_t* dst, size_t n) {
     size_t nv = n / 16;
     uint4* d4 = reinterpret_cast<uint4*>(dst);
@@ -165,6 +125,7 @@ int ef_profile_enable(int on, const char* only) {
     efg::prof_clear_locked();
     efg::g_prof_on = on != 0;
     efg::g_prof_only = (on && only) ? only : "";
+    efg::g_prof_armed.store(efg::g_prof_on, std::memory_order_release);
     return EF_OK;
 }
 

@@ -47,6 +47,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -159,6 +160,31 @@ struct alignas(16) Header {
 static_assert(sizeof(Header) == 256, "Header layout");
 
 // ------------------------------------------------------------------ host plan
+// A vector with inline room for N elements: a call over one tensor builds its
+// plan without touching the host heap (the allocation-free entry point relies
+// on it); longer plans spill to a std::vector.
+template <typename T, size_t N>
+class SmallVec {
+public:
+    size_t size() const { return n_; }
+    T* data() { return n_ <= N ? inl_ : heap_.data(); }
+    const T* data() const { return n_ <= N ? inl_ : heap_.data(); }
+    T& operator[](size_t i) { return data()[i]; }
+    const T& operator[](size_t i) const { return data()[i]; }
+    T* begin() { return data(); }
+    T* end() { return data() + n_; }
+    void assign(size_t n, const T& v) {
+        n_ = n;
+        if (n > N) heap_.assign(n, v);
+        else for (size_t i = 0; i < n; ++i) inl_[i] = v;
+    }
+
+private:
+    size_t n_ = 0;
+    T inl_[N];
+    std::vector<T> heap_;
+};
+
 struct Plan {
     int32_t nseg = 0;
     int64_t R = 0;      // regions (waves of the streaming pass)
@@ -171,12 +197,12 @@ struct Plan {
     int64_t Ctot = 0;   // candidate slot entries
     int64_t CB = 0;     // compaction blocks
     bool any_normal = false;
-    std::vector<SegPlan> seg;
-    std::vector<int32_t> rb, gbb, sbb, cbb;  // prefix tables, nseg+1 each
+    SmallVec<SegPlan, 1> seg;
+    SmallVec<int32_t, 2> rb, gbb, sbb, cbb;  // prefix tables, nseg+1 each
 };
 
 struct Layout {
-    size_t plan, rb, gbb, sbb, cbb, static_end;
+    size_t status, plan, rb, gbb, sbb, cbb, static_end;
     size_t header, state, shist, rhist, grp_cnt, zero_end;
     size_t ccb, rcb, grp_off, region_cnt, ovf, cpair, dval, didx, cgt, ceq, rgt, req, spart, gpart, cpart, rpart;
     size_t total;
@@ -187,6 +213,9 @@ static Layout make_layout(const Plan& p) {
     size_t at = 0;
     auto take = [&](size_t bytes) { size_t o = at; at = round_up(at + bytes, 256); return o; };
     const size_t ns = static_cast<size_t>(p.nseg);
+    // word 0: indices the call found out of their tensor's range in its own
+    // workspace entries (written as part of the tables, so it starts at 0)
+    L.status = take(256);
     L.plan = take(ns * sizeof(SegPlan));
     L.rb = at; at += (ns + 1) * 4;
     L.gbb = at; at += (ns + 1) * 4;
@@ -231,7 +260,7 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
     if (nseg > 0 && off[nseg] > kMaxElems) return fail(EF_EINVAL, "packed buffer exceeds 2^31-1 elements");
     p = Plan{};
     p.nseg = nseg;
-    p.seg.resize(nseg);
+    p.seg.assign(nseg, SegPlan{});
     p.rb.assign(nseg + 1, 0);
     p.gbb.assign(nseg + 1, 0);
     p.sbb.assign(nseg + 1, 0);
@@ -361,12 +390,17 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
 }
 
 // ------------------------------------------------------------------ kernels
-// Clears the per-call state and writes the first chunk of the plan tables.
+// Clears the per-call state and writes the plan tables into the workspace:
+// a small plan from the kernel arguments (chunk c), a cached one from pinned
+// host memory (tsrc, tvec 16-byte words; every block copies a slice).
 __global__ __launch_bounds__(kBlock) void k_init(uint4* zero, int64_t nvec, uint32_t* nonfinite, uint32_t* dst,
-                                                 WordChunk c) {
+                                                 WordChunk c, const uint4* __restrict__ tsrc, int64_t tvec) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nvec; i += stride)
         zero[i] = make_uint4(0, 0, 0, 0);
+    uint4* tdst = reinterpret_cast<uint4*>(dst);
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < tvec; i += stride)
+        tdst[i] = tsrc[i];
     if (blockIdx.x == 0) {
         for (uint32_t i = threadIdx.x; i < c.n; i += kBlock) dst[i] = c.w[i];
         if (nonfinite && threadIdx.x == 0) *nonfinite = 0;
@@ -846,7 +880,8 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
                                                     const uint32_t* __restrict__ grp_off,
                                                     const uint2* __restrict__ cpair, float* __restrict__ dval,
                                                     int32_t* __restrict__ didx, uint32_t* __restrict__ rhist,
-                                                    int32_t hcopies, float* __restrict__ e) {
+                                                    int32_t hcopies, float* __restrict__ e,
+                                                    uint32_t* __restrict__ stray) {
     __shared__ uint32_t loff[kGroup];
     __shared__ uint32_t h[kRadixBins];
     __shared__ uint32_t lds[kWavesPerBlock + 1];
@@ -877,8 +912,12 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
                 const uint2 pr = cpair[slot + j];
                 const float v = __uint_as_float(pr.x);
                 // indices were written by the stream of this call; the range check
-                // keeps a workspace overwritten meanwhile from becoming a stray write
-                if (key_of(v) >= thi && pr.y >= lo && pr.y < hi) e[pr.y] = v;
+                // keeps a workspace overwritten meanwhile from becoming a stray
+                // write, and counts it
+                if (key_of(v) >= thi) {
+                    if (pr.y >= lo && pr.y < hi) e[pr.y] = v;
+                    else atomicAdd(stray, 1u);
+                }
             }
         }
         return;
@@ -1275,7 +1314,8 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
                                                   const uint32_t* __restrict__ ceq, const uint32_t* __restrict__ rgt,
                                                   const uint32_t* __restrict__ req, float* __restrict__ e,
                                                   float* __restrict__ vals, int32_t* __restrict__ idx,
-                                                  double2* __restrict__ cpart, double2* __restrict__ rpart) {
+                                                  double2* __restrict__ cpart, double2* __restrict__ rpart,
+                                                  uint32_t* __restrict__ stray) {
     __shared__ uint32_t wgt[kWavesPerBlock], weq[kWavesPerBlock];
     __shared__ double2 lsum[kWavesPerBlock];
     const int64_t Qc = hdr->total_cchunks;
@@ -1341,7 +1381,10 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
                 else drop += sq_finite(v[i], key);
             }
             const int64_t id = u.raw ? u.idx_base + j : static_cast<int64_t>(ids[i]);
-            if (id < seg_lo || id >= seg_hi) continue;  // only if the workspace was overwritten meanwhile
+            if (id < seg_lo || id >= seg_hi) {  // only if the workspace was overwritten meanwhile
+                atomicAdd(stray, 1u);
+                continue;
+            }
             if (pos >= 0 && pos < kseg) {
                 vals[out_off + pos] = v[i];
                 idx[out_off + pos] = static_cast<int32_t>(id);
@@ -1439,58 +1482,82 @@ __global__ void k_stats_zero(double* __restrict__ stats, int32_t n) {
 }
 
 // ------------------------------------------------------------------ host driver
-static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* idx, void* ws, size_t ws_bytes,
-               uint32_t* nonfinite, double* stats, uint32_t flags, hipStream_t s) {
-    const Layout L = make_layout(P);
+// The plan and prefix tables as the kernels read them at the start of the
+// workspace (L.static_end bytes).
+static void fill_words(const Plan& P, const Layout& L, uint32_t* words) {
+    uint8_t* h = reinterpret_cast<uint8_t*>(words);
+    memset(h, 0, L.static_end);
+    memcpy(h + L.plan, P.seg.data(), P.seg.size() * sizeof(SegPlan));
+    memcpy(h + L.rb, P.rb.data(), P.rb.size() * 4);
+    memcpy(h + L.gbb, P.gbb.data(), P.gbb.size() * 4);
+    memcpy(h + L.sbb, P.sbb.data(), P.sbb.size() * 4);
+    memcpy(h + L.cbb, P.cbb.data(), P.cbb.size() * 4);
+}
+
+static int check_ws(const Layout& L, const void* ws, size_t ws_bytes) {
+    if (!ws) return fail(EF_EWS, "workspace is NULL (%zu bytes needed)", L.total);
+    if (ws_bytes < L.total) return fail(EF_EWS, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+    if (!aligned256(ws)) return fail(EF_EINVAL, "workspace must be 256-byte aligned");
+    return EF_OK;
+}
+
+// A plan's tables on the host (words) and, when they sit in pinned host
+// memory, the address the device reads them at (words_dev).
+struct Tables {
+    const uint32_t* words;
+    const uint4* words_dev;
+};
+
+static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables tb, float* vals, int32_t* idx,
+               void* ws, size_t ws_bytes, uint32_t* nonfinite, double* stats, uint32_t flags, hipStream_t s,
+               bool* read_pinned = nullptr) {
+    if (read_pinned) *read_pinned = false;
     WordChunk none;
     none.n = 0;
     if (P.R == 0) {
         // nothing to stream: only the counter and the statistics need clearing
         if (nonfinite)
             EF_TRY(launch("topk_init", k_init, dim3(1), dim3(kBlock), s, static_cast<uint4*>(nullptr),
-                          static_cast<int64_t>(0), nonfinite, static_cast<uint32_t*>(nullptr), none));
+                          static_cast<int64_t>(0), nonfinite, static_cast<uint32_t*>(nullptr), none,
+                          static_cast<const uint4*>(nullptr), static_cast<int64_t>(0)));
         if (stats && P.nseg > 0)
             EF_TRY(launch("topk_stats", k_stats_zero, dim3(1), dim3(kBlock), s, stats, 2 * P.nseg));
         return EF_OK;
     }
-    if (!ws) return fail(EF_EWS, "workspace is NULL (%zu bytes needed)", L.total);
-    if (ws_bytes < L.total) return fail(EF_EWS, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
-    if (!aligned256(ws)) return fail(EF_EINVAL, "workspace must be 256-byte aligned");
+    EF_TRY(check_ws(L, ws, ws_bytes));
     uint8_t* W = static_cast<uint8_t*>(ws);
     auto at = [&](size_t o) { return W + o; };
 
-    // static tables: plan and prefix tables
-    std::vector<uint32_t> words(L.static_end / 4, 0u);
-    {
-        uint8_t* h = reinterpret_cast<uint8_t*>(words.data());
-        memcpy(h + L.plan, P.seg.data(), P.seg.size() * sizeof(SegPlan));
-        memcpy(h + L.rb, P.rb.data(), P.rb.size() * 4);
-        memcpy(h + L.gbb, P.gbb.data(), P.gbb.size() * 4);
-        memcpy(h + L.sbb, P.sbb.data(), P.sbb.size() * 4);
-        memcpy(h + L.cbb, P.cbb.data(), P.cbb.size() * 4);
-    }
-    // Small plans (up to 11 tensors) ride on k_init's arguments.  Larger ones
-    // take one copy through the pinned staging ring, except under HIP graph
-    // capture: a captured copy would read the ring slot again at every replay,
-    // after later calls reused it, so there the plan goes in kernel-argument
-    // chunks of kWordChunk words, which the graph keeps by value.
+    // The plan tables reach the workspace in k_init: a small plan (up to 11
+    // tensors) in its kernel arguments, a larger one read by its blocks from
+    // the plan cache's pinned host copy.  Under HIP graph capture a larger
+    // plan goes in kernel-argument chunks of kWordChunk words instead, which
+    // the graph keeps by value: a replay must not depend on a host buffer the
+    // cache may reuse later.
+    const size_t nwords = L.static_end / 4;
     WordChunk first;
     first.n = 0;
-    if (words.size() <= kWordChunk) {
-        first.n = static_cast<uint32_t>(words.size());
-        memcpy(first.w, words.data(), first.n * 4);
+    const uint4* tsrc = nullptr;
+    int64_t tvec = 0;
+    if (nwords <= kWordChunk) {
+        first.n = static_cast<uint32_t>(nwords);
+        memcpy(first.w, tb.words, first.n * 4);
     } else {
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(s, &cs) != hipSuccess) return fail(EF_EHIP, "stream capture query failed");
-        if (cs == hipStreamCaptureStatusActive)
-            EF_TRY(upload_words(W, words.data(), words.size(), s));
-        else
-            EF_TRY(upload_bytes(W, words.data(), words.size() * 4, s));
+        if (cs == hipStreamCaptureStatusActive || !tb.words_dev) {
+            EF_TRY(upload_words(W, tb.words, nwords, s));
+        } else {
+            tsrc = tb.words_dev;
+            tvec = static_cast<int64_t>(L.static_end / 16);
+            if (read_pinned) *read_pinned = true;
+        }
     }
     const int64_t nzero = static_cast<int64_t>((L.zero_end - L.header) / 16);
-    const unsigned zgrid = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, cdiv(nzero, kBlock))));
+    const unsigned zgrid = static_cast<unsigned>(
+        std::min<int64_t>(kMaxGrid, std::max<int64_t>({1, cdiv(nzero, kBlock), cdiv(tvec, kBlock)})));
     EF_TRY(launch("topk_init", k_init, dim3(zgrid), dim3(kBlock), s, reinterpret_cast<uint4*>(at(L.header)), nzero,
-                  nonfinite, reinterpret_cast<uint32_t*>(W), first));
+                  nonfinite, reinterpret_cast<uint32_t*>(W), first, tsrc, tvec));
 
     const SegPlan* plan = reinterpret_cast<const SegPlan*>(at(L.plan));
     const int32_t* rb = reinterpret_cast<const int32_t*>(at(L.rb));
@@ -1498,6 +1565,7 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
     const int32_t* sbb = reinterpret_cast<const int32_t*>(at(L.sbb));
     uint32_t* rcb = reinterpret_cast<uint32_t*>(at(L.rcb));
     Header* hdr = reinterpret_cast<Header*>(at(L.header));
+    uint32_t* stray = reinterpret_cast<uint32_t*>(at(L.status));
     SegState* st = reinterpret_cast<SegState*>(at(L.state));
     uint32_t* shist = reinterpret_cast<uint32_t*>(at(L.shist));
     uint32_t* rhist = reinterpret_cast<uint32_t*>(at(L.rhist));
@@ -1551,7 +1619,7 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
                   static_cast<const int32_t*>(reinterpret_cast<int32_t*>(at(L.cbb))), gbb, rb,
                   static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
                   static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair), dval, didx, rhist,
-                  P.hcopies, e));
+                  P.hcopies, e, stray));
     EF_TRY(launch("topk_recollect", k_recollect, dim3(kRecollectBlocks), dim3(kBlock), s, plan, nseg, rb, gbb,
                   static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
                   static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair),
@@ -1576,7 +1644,8 @@ static int run(const float* g, float* e, const Plan& P, float* vals, int32_t* id
                   static_cast<const uint32_t*>(rcb), static_cast<const Header*>(hdr),
                   static_cast<const float*>(dval), static_cast<const int32_t*>(didx),
                   static_cast<const uint32_t*>(cgt), static_cast<const uint32_t*>(ceq),
-                  static_cast<const uint32_t*>(rgt), static_cast<const uint32_t*>(req), e, vals, idx, cpart, rpart));
+                  static_cast<const uint32_t*>(rgt), static_cast<const uint32_t*>(req), e, vals, idx, cpart, rpart,
+                  stray));
     return finish_stats();
 }
 
@@ -1586,6 +1655,120 @@ static int check_common(const float* g, const float* e, int64_t total, int64_t k
     if (total > 0 && (!g || !e)) return fail(EF_EINVAL, "g and e must not be NULL");
     if (total > 0 && (!aligned16(g) || !aligned16(e))) return fail(EF_EINVAL, "g and e must be 16-byte aligned");
     if (ksum > 0 && (!vals || !idx)) return fail(EF_EINVAL, "vals and idx must not be NULL when k > 0");
+    return EF_OK;
+}
+
+// ------------------------------------------------------------------ plan cache
+// A layer-wise call usually repeats the same tables step after step.  Its
+// plan is built and checked once and kept, with its tables in pinned host
+// memory that k_init reads straight into the workspace: a repeated call
+// neither rebuilds the plan nor launches a separate copy, and the contents of
+// the workspace on entry still do not matter.  A full cache reuses its least
+// recently used entry, waiting first (the only host wait of a call) until
+// the last call that read that entry's pinned tables has passed its k_init.
+constexpr int kPlanCacheSize = 16;
+struct CachedPlan {
+    int32_t nseg = -1;  // -1: empty
+    uint64_t hash = 0;
+    std::vector<int64_t> off, ks;
+    Plan plan;
+    Layout L{};
+    uint32_t* host = nullptr;  // pinned, L.static_end bytes used
+    const uint4* dev = nullptr;  // the same memory as the device addresses it
+    size_t cap = 0;
+    hipEvent_t read_done = nullptr;  // recorded after the last k_init that read `host`
+    bool filled = false;             // host holds this entry's tables
+    bool pending = false;
+    uint64_t stamp = 0;
+};
+
+namespace {
+std::mutex g_cache_mu;
+CachedPlan g_cache[kPlanCacheSize];
+uint64_t g_cache_clock = 0;
+}  // namespace
+
+static uint64_t table_hash(int32_t nseg, const int64_t* off, const int64_t* ks) {
+    uint64_t h = 1469598103934665603ull ^ static_cast<uint64_t>(static_cast<uint32_t>(nseg));
+    auto mix = [&](int64_t v) {
+        h ^= static_cast<uint64_t>(v);
+        h *= 1099511628211ull;
+    };
+    for (int32_t i = 0; i <= nseg; ++i) mix(off[i]);
+    for (int32_t i = 0; i < nseg; ++i) mix(ks[i]);
+    return h;
+}
+
+// The cache entry for these tables, built on a miss (which also checks them).
+// Called with g_cache_mu held; the entry stays valid while it is held.
+static int cached_plan(int32_t nseg, const int64_t* off, const int64_t* ks, CachedPlan** out) {
+    if (nseg < 0) return fail(EF_EINVAL, "nseg must be >= 0 (got %d)", nseg);
+    if (nseg > 0 && (!off || !ks)) return fail(EF_EINVAL, "segment tables must not be NULL");
+    const int64_t zero_off[1] = {0};
+    if (nseg == 0 && !off) off = zero_off;
+    const uint64_t h = table_hash(nseg, off, ks);
+    CachedPlan* victim = nullptr;  // the first empty entry, else the least recently used one
+    for (CachedPlan& c : g_cache) {
+        if (c.nseg == nseg && c.hash == h && std::equal(c.off.begin(), c.off.end(), off) &&
+            std::equal(c.ks.begin(), c.ks.end(), ks)) {
+            c.stamp = ++g_cache_clock;
+            *out = &c;
+            return EF_OK;
+        }
+        if (c.nseg < 0) {
+            if (!victim || victim->nseg >= 0) victim = &c;
+        } else if (!victim || (victim->nseg >= 0 && c.stamp < victim->stamp)) {
+            victim = &c;
+        }
+    }
+    Plan p;
+    EF_TRY(make_plan(nseg, off, ks, p));
+    CachedPlan& c = *victim;
+    if (c.pending) {
+        // its pinned tables may still be read by a queued k_init
+        if (hipEventSynchronize(c.read_done) != hipSuccess)
+            return fail(EF_EHIP, "plan cache: wait for an evicted entry failed");
+        c.pending = false;
+    }
+    c.nseg = -1;
+    c.filled = false;
+    c.L = make_layout(p);
+    c.plan = std::move(p);
+    c.off.assign(off, off + nseg + 1);
+    c.ks.assign(ks, ks + nseg);
+    c.hash = h;
+    c.nseg = nseg;
+    c.stamp = ++g_cache_clock;
+    *out = &c;
+    return EF_OK;
+}
+
+// The entry's tables in pinned host memory, written on its first use by a
+// call (the size query needs no device and never gets here).
+static int pinned_tables(CachedPlan& c) {
+    if (c.filled) return EF_OK;
+    const size_t bytes = c.L.static_end;
+    if (c.cap < bytes) {
+        if (c.host) (void)hipHostFree(c.host);
+        c.host = nullptr;
+        c.dev = nullptr;
+        c.cap = 0;
+        void* hp = nullptr;
+        if (hipHostMalloc(&hp, bytes, hipHostMallocPortable | hipHostMallocMapped) != hipSuccess)
+            return fail(EF_EHIP, "plan cache: pinned allocation of %zu bytes failed", bytes);
+        void* dp = nullptr;
+        if (hipHostGetDevicePointer(&dp, hp, 0) != hipSuccess) {
+            (void)hipHostFree(hp);
+            return fail(EF_EHIP, "plan cache: no device address for the pinned tables");
+        }
+        c.host = static_cast<uint32_t*>(hp);
+        c.dev = static_cast<const uint4*>(dp);
+        c.cap = bytes;
+    }
+    if (!c.read_done && hipEventCreateWithFlags(&c.read_done, hipEventDisableTiming) != hipSuccess)
+        return fail(EF_EHIP, "plan cache: event creation failed");
+    fill_words(c.plan, c.L, c.host);
+    c.filled = true;
     return EF_OK;
 }
 
@@ -1604,32 +1787,70 @@ size_t ef_topk_workspace_bytes(int64_t n, int64_t k) {
     return topk::make_layout(p).total;
 }
 
-int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals, int32_t* idx, void* ws,
-                     size_t ws_bytes, uint32_t* nonfinite, double* stats, uint32_t flags, void* stream) {
+// One flat tensor: a plan of one segment, built on the stack, whose tables
+// always fit k_init's kernel arguments.
+static int topk_flat(const float* g, float* e, int64_t n, int64_t k, float* vals, int32_t* idx, void* ws,
+                     size_t ws_bytes, uint32_t* nonfinite, double* stats, uint32_t flags, hipStream_t s) {
     if (n < 0 || n > kMaxElems) return fail(EF_EINVAL, "n=%lld outside [0, 2^31-1]", (long long)n);
     if (k < 0 || k > n) return fail(EF_EINVAL, "k=%lld outside [0, n=%lld]", (long long)k, (long long)n);
     EF_TRY(topk::check_common(g, e, n, k, vals, idx, flags));
     int64_t off[2] = {0, n}, ks[1] = {k};
     topk::Plan p;
     EF_TRY(topk::make_plan(1, off, ks, p));
-    return topk::run(g, e, p, vals, idx, ws, ws_bytes, nonfinite, stats, flags, static_cast<hipStream_t>(stream));
+    const topk::Layout L = topk::make_layout(p);
+    uint32_t words[kWordChunk];
+    static_assert(sizeof(words) >= 512, "a one-segment plan's tables fit the kernel arguments");
+    topk::fill_words(p, L, words);
+    return topk::run(g, e, p, L, topk::Tables{words, nullptr}, vals, idx, ws, ws_bytes, nonfinite, stats, flags, s);
+}
+
+int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals, int32_t* idx, void* ws,
+                     size_t ws_bytes, uint32_t* nonfinite, double* stats, uint32_t flags, void* stream) {
+    return topk_flat(g, e, n, k, vals, idx, ws, ws_bytes, nonfinite, stats, flags,
+                     static_cast<hipStream_t>(stream));
+}
+
+__global__ void k_copy_status(const uint32_t* __restrict__ status, uint32_t* __restrict__ out) { *out = *status; }
+
+int ef_topk_workspace_status(const void* ws, uint32_t* stray, void* stream) {
+    if (!stray) return fail(EF_EINVAL, "ef_topk_workspace_status: stray must not be NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* w = const_cast<void*>(ws);
+    if (!w) return fail(EF_EINVAL, "ef_topk_workspace_status: ws must not be NULL");
+    if (!aligned256(w)) return fail(EF_EINVAL, "ef_topk_workspace_status: workspace must be 256-byte aligned");
+    return launch("topk_status", k_copy_status, dim3(1), dim3(1), s, static_cast<const uint32_t*>(w), stray);
 }
 
 size_t ef_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* seg_off, const int64_t* seg_k) {
-    topk::Plan p;
-    if (topk::make_plan(nseg, seg_off, seg_k, p) != EF_OK) return 0;
-    return topk::make_layout(p).total;
+    std::lock_guard<std::mutex> lk(topk::g_cache_mu);
+    topk::CachedPlan* c = nullptr;
+    if (topk::cached_plan(nseg, seg_off, seg_k, &c) != EF_OK) return 0;
+    return c->L.total;
 }
 
 int ef_topk_compress_segmented(const float* g, float* e, int32_t nseg, const int64_t* seg_off,
                                const int64_t* seg_k, float* vals, int32_t* idx, void* ws, size_t ws_bytes,
                                uint32_t* nonfinite, double* stats, uint32_t flags, void* stream) {
-    topk::Plan p;
-    EF_TRY(topk::make_plan(nseg, seg_off, seg_k, p));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lk(topk::g_cache_mu);
+    topk::CachedPlan* c = nullptr;
+    EF_TRY(topk::cached_plan(nseg, seg_off, seg_k, &c));
     int64_t ksum = 0;
-    for (int32_t s = 0; s < nseg; ++s) ksum += seg_k[s];
+    for (int32_t i = 0; i < nseg; ++i) ksum += seg_k[i];
     EF_TRY(topk::check_common(g, e, nseg > 0 ? seg_off[nseg] : 0, ksum, vals, idx, flags));
-    return topk::run(g, e, p, vals, idx, ws, ws_bytes, nonfinite, stats, flags, static_cast<hipStream_t>(stream));
+    if (c->plan.R > 0) {
+        EF_TRY(topk::check_ws(c->L, ws, ws_bytes));
+        EF_TRY(topk::pinned_tables(*c));
+    }
+    bool read_pinned = false;
+    const int rc = topk::run(g, e, c->plan, c->L, topk::Tables{c->host, c->dev}, vals, idx, ws, ws_bytes, nonfinite,
+                             stats, flags, s, &read_pinned);
+    if (read_pinned) {
+        // this call's k_init reads the entry's pinned tables when it runs
+        if (hipEventRecord(c->read_done, s) != hipSuccess) return fail(EF_EHIP, "plan cache: event record failed");
+        c->pending = true;
+    }
+    return rc;
 }
 
 }  // extern "C"

@@ -14,8 +14,9 @@
  *    at the same time (on different streams) need one each.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only ENQUEUES work on that stream and returns; results are
- *    valid once the caller synchronises the stream.  No call waits for the
- *    device and none copies data device -> host.
+ *    valid once the caller synchronises the stream.  No call copies data
+ *    device -> host, and none waits for the device, with one exception named
+ *    at ef_topk_compress_segmented (its plan cache, beyond 16 table sets).
  *  - Sizes are int64_t.  Element indices are int32_t, so arrays that are
  *    indexed hold at most 2^31 - 1 elements.
  *  - float arrays read or written element-wise in bulk (g, e, m, w, G) must be
@@ -31,9 +32,9 @@
  *  - HIP graph capture: with ef_profile_enable off, every call only launches
  *    kernels (no memset, no host wait), so a captured call replays exactly
  *    like the eager one.  ef_topk_compress_segmented with more than 11 tensors
- *    copies its per-call plan from a pinned host buffer when called eagerly;
- *    under capture it passes the plan in kernel arguments instead (one small
- *    launch per 500 words, about 17 tensors), so captured calls are safe too.
+ *    reads its cached plan from pinned host memory when called eagerly; under
+ *    capture it passes the plan in kernel arguments instead (one small launch
+ *    per 500 words, about 17 tensors), so a replay never depends on the cache.
  *
  * Sources cited below ("pages"):
  *   [SPARSE] "梯度稀疏化：只传输重要的梯度元素" — gradient sparsification.
@@ -94,6 +95,13 @@ int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals
                      int32_t* idx, void* ws, size_t ws_bytes, uint32_t* nonfinite,
                      double* stats, uint32_t flags, void* stream);
 
+/* Defensive count of the last top-k call on a workspace (ws): the
+ * number of indices that call found outside their tensor's range in its own
+ * workspace entries and therefore did not write through.  0 unless something
+ * else wrote to the workspace during the call.  *stray is a device uint32;
+ * the copy is enqueued on `stream` after the calls before it. */
+int ef_topk_workspace_status(const void* ws, uint32_t* stray, void* stream);
+
 /* ------------------------------------------------------------------------
  * Layer-wise top-k over many tensors packed in one buffer: the operation of
  * ef_topk_compress applied to every tensor on its own, all in one launch
@@ -109,10 +117,14 @@ int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals
  *   buffer (seg_off[s] + local index), so idx is ascending overall.
  * *nonfinite counts over all tensors; stats (nullable) gets two doubles per
  * tensor, stats[2s] and stats[2s+1], as above.  The host tables are read during the
- * call only: the per-tensor plan built from them reaches the device through a
- * small ring of pinned host staging buffers owned by the library (8 slots of
- * at least 64 KB, kept for the life of the process; a slot is reused only once
- * its previous copy has completed).
+ * call only.  The per-tensor plan built from them is cached by the library
+ * (16 distinct table sets, in pinned host memory it keeps for the life of the
+ * process) and copied into the workspace by the call's first kernel, so
+ * repeated calls with the same tables skip rebuilding it; the workspace
+ * contents on entry still do not matter.  A call with a table set not in a
+ * full cache reuses the least recently used entry and, if a queued call may
+ * still read that entry, waits for that call's first kernel: the only case in
+ * which a call waits for the device.
  * ------------------------------------------------------------------------ */
 size_t ef_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* seg_off,
                                          const int64_t* seg_k);
@@ -176,6 +188,13 @@ int ef_sign_compress(const float* g, float* e, float* m, int64_t n, float beta1,
  * v (warm-up only) and w.  g, m, v, w 16-byte aligned; qsum 4-byte aligned;
  * 0 <= n <= 2^31 - 1; 0 <= beta <= 1; sqrt_bc2 > 0; eps >= 0.
  * ------------------------------------------------------------------------ */
+/* The two host scalars of step t (1-based):
+ *   *step_size = lr / (1 - beta1^t),  *sqrt_bc2 = sqrt(1 - beta2^t_v)
+ * in float64 from the float32 betas (powers by pow, correctly rounded square
+ * root), each rounded once to float32.  t_v = t while the variance is updated; once it is frozen, the last
+ * warm-up step.  Host outputs.  0 <= beta < 1, t >= 1, t_v >= 1, lr finite. */
+int ef_adam_scalars(double lr, float beta1, float beta2, int64_t t, int64_t t_v,
+                    float* step_size, float* sqrt_bc2);
 int ef_adam_step(const float* g, float* m, float* v, float* w, int64_t n, float beta1,
                  float beta2, float step_size, float sqrt_bc2, float eps, uint32_t* nonfinite,
                  void* stream);

@@ -39,3 +39,29 @@ def assert_bits_equal(got, want, what):
 
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def check_topk_invariants_device(x, vals, idx, e_after, k):
+    """Asserts that (vals, idx, e_after) is the top-k of x (device tensors, any
+    size): k strictly increasing in-range indices; vals = x[idx] bit for bit;
+    every kept key (|x| bits) >= every dropped key, equal keys kept by lower
+    index; e_after = x except +0 at idx.  These fix the result uniquely.
+    Overwrites x."""
+    n = x.numel()
+    ik = idx.long()
+    assert idx.numel() == k
+    if k > 0:
+        assert bool((ik[1:] > ik[:-1]).all()) and int(ik[0]) >= 0 and int(ik[-1]) < n
+        assert torch.equal(vals.view(torch.int32), x[ik].view(torch.int32))
+    if 0 < k < n:
+        key = x.view(torch.int32) & 0x7FFFFFFF
+        kept = torch.zeros(n, dtype=torch.bool, device=x.device)
+        kept[ik] = True
+        T = int(key[ik].min())
+        drop_max = int(key.masked_fill(kept, -1).max())
+        assert T >= drop_max
+        if T == drop_max:  # ties at the threshold: the lower indices are kept
+            assert int(ik[key[ik] == T].max()) < int(torch.nonzero((key == T) & ~kept)[0, 0])
+        del key, kept
+    x[ik] = 0.0
+    assert torch.equal(e_after.view(torch.int32), x.view(torch.int32))

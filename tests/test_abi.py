@@ -227,6 +227,22 @@ def test_adam_argument_checks():
 
 
 def test_adam_scalars_match_the_oracle_helper():
+    """ef_adam_scalars (the library's host arithmetic) gives the oracle's
+    scalars, which test_oracle_adam pins through torch.optim.Adam."""
     import oracle
     for args in [(2e-5, 0.9, 0.999, 1), (1e-3, 0.9, 0.999, 100, 10), (0.1, 0.5, 0.9, 7, 7)]:
         assert efg.adam_scalars(*args) == oracle.adam_scalars(*args)
+    r = np.random.default_rng(77)
+    for _ in range(2000):
+        lr = float(10.0 ** r.uniform(-7, 0))
+        b1, b2 = float(r.choice([0.0, 0.5, 0.9, 0.95, r.uniform(0, 1)])), float(r.choice([0.9, 0.99, 0.999, 0.9999]))
+        t = int(r.integers(1, 100_000))
+        tv = int(r.integers(1, t + 1))
+        assert efg.adam_scalars(lr, b1, b2, t, tv) == oracle.adam_scalars(lr, b1, b2, t, tv), (lr, b1, b2, t, tv)
+    L = efg.lib()
+    a, b = C.c_float(), C.c_float()
+    assert L.ef_adam_scalars(1e-3, 1.0, 0.999, 1, 1, C.byref(a), C.byref(b)) == efg.EF_EINVAL
+    assert L.ef_adam_scalars(1e-3, 0.9, 0.999, 0, 1, C.byref(a), C.byref(b)) == efg.EF_EINVAL
+    assert L.ef_adam_scalars(1e-3, 0.9, 0.999, 1, 0, C.byref(a), C.byref(b)) == efg.EF_EINVAL
+    assert L.ef_adam_scalars(float("inf"), 0.9, 0.999, 1, 1, C.byref(a), C.byref(b)) == efg.EF_EINVAL
+    assert L.ef_adam_scalars(1e-3, 0.9, 0.999, 1, 1, None, C.byref(b)) == efg.EF_EINVAL

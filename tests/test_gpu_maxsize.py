@@ -77,6 +77,28 @@ def test_topk_max_size_two_steps():
     torch.cuda.empty_cache()
 
 
+def test_topk_max_size_forced_fallback():
+    """The exact fallback at n = 2^31 - 1 (raw units up to the last index,
+    kept indices up to 2^31 - 2), on a residual carried from a fast-path step."""
+    dev = device()
+    n, k = NMAX, NMAX // 1000
+    need(dev, 26 * n)
+    from gpu_util import check_topk_invariants_device
+    e = torch.zeros(n, device=dev)
+    ws = efg.workspace(efg.ef_topk_workspace_bytes(n, k), dev)
+    for t, flags in ((0, 0), (1, efg.EF_FLAG_FORCE_FALLBACK)):
+        say(f"top-k n=2^31-1 step {t} flags {flags}")
+        g = gen.large_gradient_device(10 + t, n, dev)
+        x = g + e
+        v, i = efg.ef_topk_compress(g, e, k, ws=ws, flags=flags)
+        torch.cuda.synchronize()
+        del g
+        check_topk_invariants_device(x, v, i, e, k)
+        del x
+    del e, ws, v, i
+    torch.cuda.empty_cache()
+
+
 def call_path(ws):
     """'slots' or 'two-pass', from the call state at the start of the workspace
     (float32 S32 at byte 8, float32 S_lo at byte 24, uint32 overflow flag at 28)."""

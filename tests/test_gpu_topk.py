@@ -8,7 +8,7 @@ import torch
 import error_feedback_gradient_amd as efg
 import gen
 import oracle
-from gpu_util import assert_bits_equal, device, host, say, to_dev
+from gpu_util import assert_bits_equal, check_topk_invariants_device, device, host, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -358,3 +358,94 @@ def test_large_invariants_two_steps():
             assert abs(sh[0] - sent) <= 2 * k * 2.0 ** -53 * sent
             assert abs(sh[1] - resid) <= 2 * n * 2.0 ** -53 * resid
         say(f"large step {t}: ok")
+
+
+def test_large_forced_fallback_two_steps():
+    """The exact fallback at the headline size, N = 1.3e9, k = 1.3e6, two
+    chained steps (the second on a residual the fallback wrote): its raw units
+    address e past 4 GiB and its per-tensor unit scan covers about 635,000
+    units.  Checked on the device by the invariants that fix the result."""
+    dev = device()
+    n, k = gen.LARGE_N, gen.LARGE_K
+    free, _ = torch.cuda.mem_get_info(dev)
+    if free < 24 * n + (1 << 30):
+        pytest.skip("not enough device memory")
+    e = torch.zeros(n, dtype=torch.float32, device=dev)
+    ws = efg.workspace(efg.ef_topk_workspace_bytes(n, k), dev)
+    nf = torch.zeros(1, dtype=torch.int32, device=dev)
+    for t in range(2):
+        say(f"large forced fallback step {t}")
+        g = gen.large_gradient_device(t, n, dev)
+        x = g + e  # float32 elementwise on the device, as the kernel adds
+        v, i = efg.ef_topk_compress(g, e, k, ws=ws, nonfinite=nf, flags=efg.EF_FLAG_FORCE_FALLBACK)
+        torch.cuda.synchronize()
+        del g
+        assert int(nf.item()) == 0
+        check_topk_invariants_device(x, v, i, e, k)
+        del x
+        say(f"large forced fallback step {t}: ok")
+    del e, ws
+    torch.cuda.empty_cache()
+
+
+def test_segmented_bert_forced_fallback():
+    """The BERT-base layout (194 tensors) with every tensor on the exact
+    fallback, bit for bit against the oracle, on a residual carried from a
+    fast-path step."""
+    dev = device()
+    off, ks = gen.bert_segments()
+    n = int(off[-1])
+    ed = torch.zeros(n, dtype=torch.float32, device=dev)
+    e_ref = np.zeros(n, np.float32)
+    ws = efg.workspace(efg.ef_topk_segmented_workspace_bytes(off, ks), dev)
+    for t, flags in ((0, 0), (1, efg.EF_FLAG_FORCE_FALLBACK)):
+        g = gen.bert_gradient(t)
+        v, i = efg.ef_topk_compress_segmented(to_dev(g, dev), ed, off, ks, ws=ws, flags=flags)
+        say(f"bert forced fallback step {t} (flags {flags}): oracle ...")
+        ov, oi, e_ref, _ = oracle.topk_segmented(g, e_ref, off, ks)
+        assert_bits_equal(host(i), oi, f"bert idx step {t}")
+        assert_bits_equal(host(v), ov, f"bert vals step {t}")
+        assert_bits_equal(host(ed), e_ref, f"bert e step {t}")
+
+
+def test_segmented_plan_cache_rotation():
+    """More distinct layouts than the plan cache holds (16), each of more than
+    11 tensors (so their tables go through the cache's pinned copy), called in
+    rotation twice with one workspace, interleaved with a flat call on the
+    same workspace: every call equals the oracle, and the workspace status
+    word stays 0."""
+    dev = device()
+    r = gen.rng(150)
+    layouts = []
+    for j in range(20):
+        sizes = r.integers(1, 5000, size=int(r.integers(12, 40))).tolist()
+        ks = [int(r.integers(0, s_ + 1)) for s_ in sizes]
+        layouts.append((sizes, ks))
+    big = max(efg.ef_topk_segmented_workspace_bytes(np.concatenate([[0], np.cumsum(sz)]), ks)
+              for sz, ks in layouts)
+    ws = efg.workspace(max(big, efg.ef_topk_workspace_bytes(100_000, 1000)), dev)
+    for rnd in range(2):
+        for j, (sizes, ks) in enumerate(layouts):
+            off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+            n = int(off[-1])
+            g, e = gen.normal_small(n, 151, rnd, j), gen.normal_small(n, 152, rnd, j, scale=0.1)
+            ed = to_dev(e, dev)
+            v, i = efg.ef_topk_compress_segmented(to_dev(g, dev), ed, off, ks, ws=ws)
+            ov, oi, oe, _ = oracle.topk_segmented(g, e, off, np.array(ks, np.int64))
+            assert_bits_equal(host(i), oi, f"idx round {rnd} layout {j}")
+            assert_bits_equal(host(v), ov, f"vals round {rnd} layout {j}")
+            assert_bits_equal(host(ed), oe, f"e round {rnd} layout {j}")
+            assert int(host(efg.ef_topk_workspace_status(ws))[0]) == 0
+            if j % 7 == 3:
+                gf = gen.normal_small(100_000, 153, rnd, j)
+                check(gf, np.zeros(100_000, np.float32), 1000, what="flat between layouts")
+
+
+def test_workspace_status_zero_after_calls():
+    dev = device()
+    n, k = 300_007, 3000
+    g, e = inputs(n, "normal", 11)
+    ws = efg.workspace(efg.ef_topk_workspace_bytes(n, k), dev)
+    for flags in (0, efg.EF_FLAG_FORCE_FALLBACK):
+        efg.ef_topk_compress(to_dev(g, dev), to_dev(e, dev), k, ws=ws, flags=flags)
+        assert int(host(efg.ef_topk_workspace_status(ws))[0]) == 0
