@@ -29,6 +29,7 @@ SIGNATURES = {
     "ef_version": (C.c_char_p, []),
     "ef_topk_workspace_bytes": (_sz, [_i64, _i64]),
     "ef_topk_compress": (C.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _sz, _p, _p, _u32, _p]),
+    "ef_topk_compress_noalloc": (C.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _p, _u32, _p]),
     "ef_topk_workspace_status": (C.c_int, [_p, _p, _p]),
     "ef_topk_segmented_workspace_bytes": (_sz, [_i32, _p, _p]),
     "ef_topk_compress_segmented": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _sz, _p, _p, _u32, _p]),
@@ -152,16 +153,43 @@ def ef_topk_compress(g, e, k, vals=None, idx=None, ws=None, nonfinite=None, flag
     return vals, idx
 
 
-def ef_topk_workspace_status(ws, stray=None):
+def ef_topk_workspace_status(ws, stray=None, device=None):
     """Device uint32 (as int32[1]): indices the last top-k call on ws found
     out of range in its own workspace entries (0 unless the workspace was
-    overwritten during the call)."""
-    dev = ws.device
+    overwritten during the call).  ws=None: the allocation-free call's static
+    scratch on `device`."""
+    dev = ws.device if ws is not None else torch.device(device if device is not None else "cuda")
     if stray is None:
         stray = torch.empty(1, dtype=torch.int32, device=dev)
     _need(stray, torch.int32, dev, "stray", 1)
     _check(lib().ef_topk_workspace_status(_ptr(ws), _ptr(stray), _stream(dev)), "ef_topk_workspace_status")
     return stray
+
+
+EF_TOPK_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def ef_topk_compress_noalloc(g, e, k, vals=None, idx=None, nonfinite=None, flags=0, stats=None):
+    """ef_topk_compress with the library's static scratch instead of a workspace
+    (the C call allocates nothing; vals and idx are allocated here only when
+    the caller does not pass them).  Returns (vals, idx)."""
+    dev = _gpu(g, "g")
+    n = g.numel()
+    _need(g, torch.float32, dev, "g")
+    _need(e, torch.float32, dev, "e", n)
+    if vals is None:
+        vals = torch.empty(k, dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty(k, dtype=torch.int32, device=dev)
+    _need(vals, torch.float32, dev, "vals", k)
+    _need(idx, torch.int32, dev, "idx", k)
+    if nonfinite is not None:
+        _need(nonfinite, torch.int32, dev, "nonfinite", 1)
+    if stats is not None:
+        _need(stats, torch.float64, dev, "stats", 2)
+    _check(lib().ef_topk_compress_noalloc(_ptr(g), _ptr(e), n, k, _ptr(vals), _ptr(idx), _ptr(nonfinite),
+                                          _ptr(stats), flags, _stream(dev)), "ef_topk_compress_noalloc")
+    return vals, idx
 
 
 def _i64_host(a):

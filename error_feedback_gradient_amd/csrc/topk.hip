@@ -1772,6 +1772,45 @@ static int pinned_tables(CachedPlan& c) {
     return EF_OK;
 }
 
+// ------------------------------------------------------------------ allocation-free entry point
+// The scratch of ef_topk_compress_noalloc: one array per GPU the library runs
+// on, kept until the process ends and shared by every such call on that GPU.
+// In host code `scratch` names a host-side stand-in, not device memory: only
+// the device address looked up below (once per device, with that device
+// current) is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[EF_TOPK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+}  // namespace
+
+// Device address of this library's scratch array on the device that runs
+// stream s (the current device for the NULL stream).
+static int scratch_address(hipStream_t s, void** out) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(EF_EHIP, "ef_topk_compress_noalloc: no current device");
+    int dev = cur;
+    if (s && hipStreamGetDevice(s, &dev) != hipSuccess)
+        return fail(EF_EHIP, "ef_topk_compress_noalloc: cannot tell the stream's device");
+    if (dev < 0 || dev >= kMaxDevices) return fail(EF_EINVAL, "ef_topk_compress_noalloc: device %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess)
+            return fail(EF_EHIP, "ef_topk_compress_noalloc: cannot select device %d", dev);
+        void* ptr = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (err != hipSuccess || !ptr)
+            return fail(EF_EHIP, "ef_topk_compress_noalloc: scratch address lookup failed: %s",
+                        hipGetErrorString(err));
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return EF_OK;
+}
+
 }  // namespace topk
 }  // namespace efg
 
@@ -1790,7 +1829,8 @@ size_t ef_topk_workspace_bytes(int64_t n, int64_t k) {
 // One flat tensor: a plan of one segment, built on the stack, whose tables
 // always fit k_init's kernel arguments.
 static int topk_flat(const float* g, float* e, int64_t n, int64_t k, float* vals, int32_t* idx, void* ws,
-                     size_t ws_bytes, uint32_t* nonfinite, double* stats, uint32_t flags, hipStream_t s) {
+                     size_t ws_bytes, bool static_scratch, uint32_t* nonfinite, double* stats, uint32_t flags,
+                     hipStream_t s) {
     if (n < 0 || n > kMaxElems) return fail(EF_EINVAL, "n=%lld outside [0, 2^31-1]", (long long)n);
     if (k < 0 || k > n) return fail(EF_EINVAL, "k=%lld outside [0, n=%lld]", (long long)k, (long long)n);
     EF_TRY(topk::check_common(g, e, n, k, vals, idx, flags));
@@ -1798,6 +1838,15 @@ static int topk_flat(const float* g, float* e, int64_t n, int64_t k, float* vals
     topk::Plan p;
     EF_TRY(topk::make_plan(1, off, ks, p));
     const topk::Layout L = topk::make_layout(p);
+    if (static_scratch) {
+        if (L.total > EF_TOPK_NOALLOC_SCRATCH_BYTES)
+            return fail(EF_EWS, "ef_topk_compress_noalloc: n=%lld, k=%lld needs %zu bytes of scratch; the static "
+                        "scratch holds %zu (use ef_topk_compress with a workspace)",
+                        (long long)n, (long long)k, L.total, static_cast<size_t>(EF_TOPK_NOALLOC_SCRATCH_BYTES));
+        ws_bytes = EF_TOPK_NOALLOC_SCRATCH_BYTES;
+        ws = nullptr;
+        if (p.R > 0) EF_TRY(topk::scratch_address(s, &ws));
+    }
     uint32_t words[kWordChunk];
     static_assert(sizeof(words) >= 512, "a one-segment plan's tables fit the kernel arguments");
     topk::fill_words(p, L, words);
@@ -1806,7 +1855,13 @@ static int topk_flat(const float* g, float* e, int64_t n, int64_t k, float* vals
 
 int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals, int32_t* idx, void* ws,
                      size_t ws_bytes, uint32_t* nonfinite, double* stats, uint32_t flags, void* stream) {
-    return topk_flat(g, e, n, k, vals, idx, ws, ws_bytes, nonfinite, stats, flags,
+    return topk_flat(g, e, n, k, vals, idx, ws, ws_bytes, false, nonfinite, stats, flags,
+                     static_cast<hipStream_t>(stream));
+}
+
+int ef_topk_compress_noalloc(const float* g, float* e, int64_t n, int64_t k, float* vals, int32_t* idx,
+                             uint32_t* nonfinite, double* stats, uint32_t flags, void* stream) {
+    return topk_flat(g, e, n, k, vals, idx, nullptr, 0, true, nonfinite, stats, flags,
                      static_cast<hipStream_t>(stream));
 }
 
@@ -1816,7 +1871,7 @@ int ef_topk_workspace_status(const void* ws, uint32_t* stray, void* stream) {
     if (!stray) return fail(EF_EINVAL, "ef_topk_workspace_status: stray must not be NULL");
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* w = const_cast<void*>(ws);
-    if (!w) return fail(EF_EINVAL, "ef_topk_workspace_status: ws must not be NULL");
+    if (!w) EF_TRY(topk::scratch_address(s, &w));
     if (!aligned256(w)) return fail(EF_EINVAL, "ef_topk_workspace_status: workspace must be 256-byte aligned");
     return launch("topk_status", k_copy_status, dim3(1), dim3(1), s, static_cast<const uint32_t*>(w), stray);
 }

@@ -95,12 +95,35 @@ int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals
                      int32_t* idx, void* ws, size_t ws_bytes, uint32_t* nonfinite,
                      double* stats, uint32_t flags, void* stream);
 
-/* Defensive count of the last top-k call on a workspace (ws): the
+/* Defensive count of the last top-k call on a workspace (ws; NULL = the
+ * static scratch of ef_topk_compress_noalloc on the stream's device): the
  * number of indices that call found outside their tensor's range in its own
  * workspace entries and therefore did not write through.  0 unless something
  * else wrote to the workspace during the call.  *stray is a device uint32;
  * the copy is enqueued on `stream` after the calls before it. */
 int ef_topk_workspace_status(const void* ws, uint32_t* stray, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Allocation-free top-k, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): ef_topk_compress without a workspace argument.
+ *
+ * Arguments and results are those of ef_topk_compress.  The scratch is one
+ * static device array of EF_TOPK_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU the
+ * library runs on, held until the process ends; the first call on a device
+ * looks its address up (hipGetSymbolAddress).  A call whose scratch need,
+ * ef_topk_workspace_bytes(n, k), exceeds the array returns EF_EWS before
+ * enqueueing anything (n = 1e6, k = 1e4 needs 1.2 MB; n = 2^26, k = 2^16
+ * 14 MB).  The call makes no hipMalloc, hipFree or other allocating call; a
+ * one-tensor plan is built on the host stack.  Every call on one GPU uses
+ * that GPU's array and leaves its contents behind (each call clears what it
+ * needs cleared): calls that can overlap on one GPU (different streams) race
+ * on the array and give wrong results, so serialise them.
+ * ------------------------------------------------------------------------ */
+#define EF_TOPK_NOALLOC_SCRATCH_BYTES (32u << 20)
+int ef_topk_compress_noalloc(const float* g, float* e, int64_t n, int64_t k, float* vals,
+                             int32_t* idx, uint32_t* nonfinite, double* stats, uint32_t flags,
+                             void* stream);
 
 /* ------------------------------------------------------------------------
  * Layer-wise top-k over many tensors packed in one buffer: the operation of

@@ -79,6 +79,29 @@ def test_topk_argument_checks():
     assert call(FAKE, FAKE, 1000, 10, FAKE, FAKE, FAKE_ODD, ws) == efg.EF_EINVAL
 
 
+def test_topk_noalloc_argument_checks():
+    """The allocation-free call checks its arguments, and its scratch need
+    against the static array, on the host before it touches the GPU."""
+    L = efg.lib()
+    lim = efg.EF_TOPK_NOALLOC_SCRATCH_BYTES
+    call = lambda g, e, n, k, v, i, flags=0: L.ef_topk_compress_noalloc(g, e, n, k, v, i, None, None, flags, None)
+    assert call(FAKE, FAKE, -1, 0, FAKE, FAKE) == efg.EF_EINVAL
+    assert call(FAKE, FAKE, 10, 11, FAKE, FAKE) == efg.EF_EINVAL
+    assert call(FAKE, FAKE, 2**31, 1, FAKE, FAKE) == efg.EF_EINVAL
+    assert call(None, FAKE, 1000, 10, FAKE, FAKE) == efg.EF_EINVAL
+    assert call(FAKE_ODD, FAKE, 1000, 10, FAKE, FAKE) == efg.EF_EINVAL
+    assert call(FAKE, FAKE, 1000, 10, FAKE, None) == efg.EF_EINVAL
+    assert call(FAKE, FAKE, 1000, 10, FAKE, FAKE, flags=8) == efg.EF_EINVAL
+    # beyond the static scratch: a clear error, nothing enqueued
+    n, k = 1 << 24, (1 << 24) // 10
+    assert efg.ef_topk_workspace_bytes(n, k) > lim
+    assert call(FAKE, FAKE, n, k, FAKE, FAKE) == efg.EF_EWS
+    assert "static" in efg.last_error() and str(lim) in efg.last_error()
+    # the sizes the header promises fit
+    assert efg.ef_topk_workspace_bytes(1_000_000, 10_000) < lim
+    assert efg.ef_topk_workspace_bytes(1 << 26, 1 << 16) < lim
+
+
 def test_topk_workspace_sizes():
     # sample-based candidate capacity keeps the workspace far below the data
     n, k = 1_300_000_000, 1_300_000
