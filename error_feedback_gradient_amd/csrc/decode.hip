@@ -4,20 +4,25 @@
 // workers that share an index are added) and step-by-step algorithm steps 6-7
 // (aggregate, then w = w - lr * G).
 //
-// Decode without float atomics and in packet order: each block owns one tile
-// of 4096 consecutive positions of G.  For every packet, 16 lanes search the
-// packet's (ascending) index list together for the entries that land in the
-// tile, stage them in LDS, load G once for every touched position, add the
-// packets one after another in LDS (a barrier between packets keeps the
-// order), and write every touched position back once.  The sum at each index
-// is therefore ((G + v_p0) + v_p1) + ... in packet order, bit for bit.
-// The block's time is a chain of dependent loads (packet bounds, search,
-// entries, G), so what counts is how many blocks a CU holds at once: a 4096
-// tile and 512 staged entries (20 KB of LDS, up to eight blocks per CU) took
-// 48 us on the 16-packet 25.6M workload, against 62 us for 8192 and 2048
-// (45 KB, three per CU); tiles of 2048 to 8192 and stages of 256 to 2048
-// were tried.  A tile whose packets hold more than 512 entries in it takes
-// the slower path that adds them from global memory.
+// Decode without float atomics and in packet order: G is cut into tiles of
+// 4096 positions, each summed in LDS by one block, so the sum at each index is
+// ((G + v_p0) + v_p1) + ... in packet order, bit for bit.
+//
+// k_decode_tiles (up to 64 packets): a block owns a run of consecutive tiles
+// (as many blocks as the GPU holds at once).  A packet's position is searched
+// once per block and then carried from tile to tile, so a tile costs one
+// round of loads, issued a tile ahead: every packet's next 16 entries and,
+// fused with the SGD update, the tile's w.  Entries are applied in rounds
+// that an LDS atomic min orders by packet (see the kernel).  Fused, G is
+// written whole and w only where w - fl(lr * G) differs from w in its bits
+// (where the packets land), with plain stores: on the 16-packet 25.6M
+// workload, whose w and G (205 MB) fit the 256 MB last-level cache,
+// non-temporal stores took 72 us a step against 54, and writing every quad of
+// w 54 against 43.
+// k_decode (more packets): one block per tile, each searching every packet
+// for its entries (the design the multi-tile kernel replaced: 81 us fused).
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace efg {
@@ -36,6 +41,30 @@ constexpr int kSearchLanes = 16;                     // lanes that search one pa
 constexpr int kPkGroup = kBlock / kSearchLanes;      // packets searched at once per block
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+
+#ifndef EFG_DECODE_NT_LOAD
+#define EFG_DECODE_NT_LOAD 0
+#endif
+#ifndef EFG_DECODE_NT_STORE
+#define EFG_DECODE_NT_STORE 0
+#endif
+__device__ __forceinline__ f4 ld4(const f4* p) {
+    if (EFG_DECODE_NT_LOAD) return __builtin_nontemporal_load(p);
+    return *p;
+}
+__device__ __forceinline__ void st4(f4 v, f4* p) {
+    if (EFG_DECODE_NT_STORE) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+// w - fl(lr * G) stored only where its bits differ from w's: where G is +0 the
+// difference is w itself (a signalling NaN comes back quiet and is stored), so
+// a sparse G writes back only the quads its entries touch.  The result in
+// memory is the same as storing every quad.
+__device__ __forceinline__ void st4_changed(f4 wn, f4 wo, f4* p) {
+    const bool same = __float_as_uint(wn.x) == __float_as_uint(wo.x) && __float_as_uint(wn.y) == __float_as_uint(wo.y) &&
+                      __float_as_uint(wn.z) == __float_as_uint(wo.z) && __float_as_uint(wn.w) == __float_as_uint(wo.w);
+    if (!same) st4(wn, p);
+}
 
 __global__ void k_zero_u32(uint32_t* p) { *p = 0; }
 
@@ -236,7 +265,7 @@ __global__ __launch_bounds__(kBlock) void k_decode(float* __restrict__ G, int64_
 #pragma unroll
     for (int r = 0; r < kQuads; ++r) {
         const int t = 4 * (static_cast<int>(threadIdx.x) + r * kBlock);
-        if (t + 4 <= len) wv[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(w + lo + t));
+        if (t + 4 <= len) wv[r] = ld4(reinterpret_cast<const f4*>(w + lo + t));
     }
 #pragma unroll
     for (int r = 0; r < kQuads; ++r) {
@@ -244,13 +273,338 @@ __global__ __launch_bounds__(kBlock) void k_decode(float* __restrict__ G, int64_
         if (t + 4 <= len) {
             const f4 a = {acc[t], acc[t + 1], acc[t + 2], acc[t + 3]};
             const f4 st = lr * a;
-            __builtin_nontemporal_store(wv[r] - st, reinterpret_cast<f4*>(w + lo + t));
-            if (G) __builtin_nontemporal_store(a, reinterpret_cast<f4*>(G + lo + t));
+            st4_changed(wv[r] - st, wv[r], reinterpret_cast<f4*>(w + lo + t));
+            if (G) st4(a, reinterpret_cast<f4*>(G + lo + t));
         } else if (t < len) {
             for (int c = 0; c < 4 && t + c < len; ++c) {
                 const float st = lr * acc[t + c];
                 w[lo + t + c] = w[lo + t + c] - st;
                 if (G) G[lo + t + c] = acc[t + c];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ multi-tile decode
+// Each block owns a run of consecutive tiles.  Every packet's position is
+// searched once, for the block's first tile, and then carried from tile to
+// tile in the registers of the packet's 16 lanes, so that a tile costs one
+// round of loads: every packet's next 16 entries (index, the index before it,
+// value), read together with the tile's w.  The entries below the tile's end
+// (their count is the run of leading lanes found by a ballot) are applied to
+// the tile's LDS sums in packet order without a barrier per packet: in each
+// round every pending entry offers (round tag, packet-major slot) to its
+// position with an LDS atomic min, and the entry holding the minimum adds; the
+// tag of a later round is smaller, so older tags never win.  A position that
+// several packets hit takes one round per packet, in packet order; the others
+// all add in the first round.  A packet with 16 or more entries in one tile
+// sends the whole tile down the dense path, which stages every entry from
+// global memory in packet-major chunks and applies each chunk the same way.
+constexpr int kMaxPk = 64;                        // packets whose cursors a block carries
+constexpr int kDenseStage = 1024;                 // entries per staged chunk of a dense tile
+constexpr int kWin = kSearchLanes;                // entries of a packet read per tile and round
+
+// lower_bound(a[0..len), v) by the 16 lanes of a group (every lane of the wave
+// must call it; inactive groups pass len = 0)
+__device__ __forceinline__ int64_t group_lower_bound1(const int32_t* a, int64_t len, int64_t v, int gl) {
+    const int shift = threadIdx.x & 48;
+    Search s{0, len, v};
+    while (__any(s.R - s.L > kSearchLanes)) search_round(a, s, gl, shift, false, 0, len);
+    const int64_t p = s.L + gl;
+    const bool b = p < s.R && static_cast<int64_t>(a[p]) < v;
+    return s.L + __popc(static_cast<uint32_t>(__ballot(b) >> shift) & 0xffffu);
+}
+
+// Round tag of an LDS atomic-min key: later rounds get smaller tags.
+__device__ __forceinline__ uint32_t round_key(uint32_t epoch, uint32_t slot) {
+    return ((0xffffu - epoch) << 16) | slot;
+}
+
+// One entry's addition to the tile: the fused form sums from +0; the other
+// loads G at a position's first touch in the tile (touched bit).
+template <bool FUSED>
+__device__ __forceinline__ bool apply_entry(float* acc, uint32_t* touched, const float* G, int64_t lo, uint32_t loc,
+                                            float v) {
+    if (FUSED) {
+        acc[loc] = acc[loc] + v;
+        return false;
+    }
+    const uint32_t bit = 1u << (loc & 31);
+    const uint32_t old = atomicOr(&touched[loc >> 5], bit);
+    const bool first = !(old & bit);
+    const float base = first ? G[lo + loc] : acc[loc];
+    acc[loc] = base + v;
+    return first;  // this entry writes the position back once the tile is summed
+}
+
+#ifndef EFG_DECODE_WAVES
+#define EFG_DECODE_WAVES 1
+#endif
+template <bool FUSED, int SLOTS>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(EFG_DECODE_WAVES))) void k_decode_tiles(float* __restrict__ G, int64_t n, int32_t npk,
+                                                         const float* __restrict__ vals,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int64_t* __restrict__ pk_off, float* __restrict__ w,
+                                                         float lr, int64_t ntiles) {
+    __shared__ float acc[kTile];
+    __shared__ uint32_t own[kTile];
+    __shared__ uint32_t touched[kTile / 32];
+    __shared__ uint16_t st_loc[kDenseStage];
+    __shared__ float st_val[kDenseStage];
+    __shared__ uint32_t p_cnt[kMaxPk], p_sof[kMaxPk + 1];
+    __shared__ int64_t p_beg[kMaxPk];
+    __shared__ uint32_t lds[kBlock / kWave + 1];
+
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * ntiles / gridDim.x;
+    const int64_t t1 = static_cast<int64_t>(blockIdx.x + 1) * ntiles / gridDim.x;
+    const int tid = threadIdx.x, grp = tid / kSearchLanes, gl = tid % kSearchLanes;
+    const int g0 = static_cast<int>(lane()) & ~(kSearchLanes - 1);  // the group's first lane in the wave
+    for (int i = tid; i < kTile; i += kBlock) {
+        own[i] = 0xffffffffu;
+        if (FUSED) acc[i] = 0.0f;
+    }
+    if (!FUSED)
+        for (int i = tid; i < kTile / 32; i += kBlock) touched[i] = 0;
+
+    // packet grp + 16 u of lane group grp: entries [pb, pe), next entry cur,
+    // index of the entry before cur (last; -1 if none: indices are >= 0)
+    int64_t pb[SLOTS], pe[SLOTS], cur[SLOTS];
+    int64_t last[SLOTS];
+    {
+        const int64_t lo0 = t0 * kTile;
+#pragma unroll
+        for (int u = 0; u < SLOTS; ++u) {
+            const int p = grp + kPkGroup * u;
+            pb[u] = pe[u] = 0;
+            if (p < npk) {
+                pb[u] = pk_off[p];
+                pe[u] = max(pk_off[p + 1], pb[u]);
+            }
+            int64_t a, b;
+            group_lower_bound2(idx + pb[u], pe[u] - pb[u], n, lo0, lo0, gl, &a, &b);
+            cur[u] = pb[u] + a;
+            last[u] = -1;
+            if (cur[u] > pb[u]) last[u] = idx[cur[u] - 1];
+        }
+    }
+    __syncthreads();
+
+    constexpr int kQuads = kTile / (4 * kBlock);
+    static_assert(kTile % (4 * kBlock) == 0, "a tile is whole quads of every thread");
+    uint32_t epoch = 0;
+    // after each round (every thread, uniformly): the next tag; when the 16-bit
+    // tags run out, every position's key goes back above all tags
+    auto next_round = [&]() {
+        if (++epoch == 0x10000u) {
+            __syncthreads();
+            for (int i = tid; i < kTile; i += kBlock) own[i] = 0xffffffffu;
+            epoch = 0;
+            __syncthreads();
+        }
+    };
+    // Loads of a tile, issued as early as their inputs allow: w needs only the
+    // tile, the entry window of a packet its cursor after the tile before.
+    auto load_w = [&](int64_t t, f4 (&wv)[kQuads]) {
+        const int64_t lo = t * kTile, len = min(lo + kTile, n) - lo;
+#pragma unroll
+        for (int r = 0; r < kQuads; ++r) {
+            const int q = 4 * (tid + r * kBlock);
+            if (q + 4 <= len) wv[r] = ld4(reinterpret_cast<const f4*>(w + lo + q));
+        }
+    };
+    auto load_window = [&](int32_t (&x)[SLOTS], float (&v)[SLOTS], bool (&in)[SLOTS]) {
+#pragma unroll
+        for (int u = 0; u < SLOTS; ++u) {
+            const int64_t j = cur[u] + gl;
+            in[u] = j < pe[u];
+            x[u] = 0x7fffffff;
+            v[u] = 0.0f;
+            if (in[u]) {
+                x[u] = idx[j];
+                v[u] = vals[j];
+            }
+        }
+    };
+    f4 wA[kQuads];
+    int32_t xA[SLOTS];
+    float vA[SLOTS];
+    bool inA[SLOTS];
+    if (FUSED) load_w(t0, wA);
+    load_window(xA, vA, inA);
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t lo = t * kTile, hi = min(lo + kTile, n);
+        const int64_t len = hi - lo;
+        const bool more = t + 1 < t1;
+        // the next tile's w, in flight while this tile is summed and written
+        f4 wB[kQuads];
+        if (FUSED && more) load_w(t + 1, wB);
+        uint32_t lead[SLOTS];
+        bool full = false;
+#pragma unroll
+        for (int u = 0; u < SLOTS; ++u) {
+            const bool lt = inA[u] && xA[u] < hi;
+            const uint32_t m = static_cast<uint32_t>(__ballot(lt) >> (tid & 48)) & 0xffffu;
+            lead[u] = __ffs(~m | 0x10000u) - 1;  // leading lanes below hi (16: window full)
+            full |= lead[u] == kWin;
+        }
+        const bool dense = __syncthreads_or(full);
+        int32_t xB[SLOTS];
+        float vB[SLOTS];
+        bool inB[SLOTS];
+        uint32_t back[SLOTS];  // positions this lane writes back (accumulate only; 0xffffffff: none)
+#pragma unroll
+        for (int u = 0; u < SLOTS; ++u) back[u] = 0xffffffffu;
+        if (!dense) {
+            // each lane applies its own entry: valid when in [lo, hi) (so in [0, n))
+            // and above the entry before it in its packet
+            bool pend[SLOTS];
+            uint32_t loc[SLOTS];
+            float val[SLOTS];
+            bool anyp = false;
+#pragma unroll
+            for (int u = 0; u < SLOTS; ++u) {
+                const int64_t prev = __shfl_up(xA[u], 1, kSearchLanes);
+                const int64_t before = gl == 0 ? last[u] : prev;
+                pend[u] = static_cast<uint32_t>(gl) < lead[u] && xA[u] >= lo && xA[u] > before;
+                loc[u] = pend[u] ? static_cast<uint32_t>(xA[u] - lo) : 0u;
+                val[u] = vA[u];
+                anyp |= pend[u];
+                const int32_t lx = __shfl(xA[u], g0 + static_cast<int>(lead[u] > 0 ? lead[u] - 1 : 0), kWave);
+                if (lead[u] > 0) last[u] = lx;
+                cur[u] += lead[u];
+            }
+            // the next tile's windows go out before this tile's sums and stores
+            if (more) load_window(xB, vB, inB);
+            while (__syncthreads_or(anyp)) {
+#pragma unroll
+                for (int u = 0; u < SLOTS; ++u)
+                    if (pend[u]) atomicMin(&own[loc[u]], round_key(epoch, static_cast<uint32_t>((grp + kPkGroup * u) * kWin + gl)));
+                __syncthreads();
+                anyp = false;
+#pragma unroll
+                for (int u = 0; u < SLOTS; ++u) {
+                    if (pend[u] && own[loc[u]] == round_key(epoch, static_cast<uint32_t>((grp + kPkGroup * u) * kWin + gl))) {
+                        if (apply_entry<FUSED>(acc, touched, G, lo, loc[u], val[u])) back[u] = loc[u];
+                        pend[u] = false;
+                    }
+                    anyp |= pend[u];
+                }
+                next_round();
+            }
+        } else {
+            // dense tile: every packet's entries below hi, staged from global
+            // memory in packet-major chunks
+            uint32_t cnt[SLOTS];
+#pragma unroll
+            for (int u = 0; u < SLOTS; ++u) {
+                const bool f = lead[u] == kWin;
+                const int64_t from = cur[u] + (f ? kWin : 0);
+                const int64_t e = group_lower_bound1(idx + from, f ? pe[u] - from : 0, hi, gl);
+                cnt[u] = lead[u] + static_cast<uint32_t>(f ? e : 0);
+                const int p = grp + kPkGroup * u;
+                if (gl == 0 && p < npk) {
+                    p_cnt[p] = cnt[u];
+                    p_beg[p] = cur[u];
+                }
+            }
+            __syncthreads();
+            const uint32_t c = tid < npk ? p_cnt[tid] : 0u;
+            uint32_t total;
+            const uint32_t ex = block_excl_scan<kBlock>(c, lds, &total);
+            if (tid < npk) p_sof[tid] = ex;
+            if (tid == 0) p_sof[npk] = total;
+            __syncthreads();
+            for (uint32_t cb = 0; cb < total; cb += kDenseStage) {
+                const uint32_t ce = min(total, cb + kDenseStage);
+                for (uint32_t q = cb + tid; q < ce; q += kBlock) {
+                    const int p = upper_index(p_sof, npk, q);
+                    const int64_t j = p_beg[p] + (q - p_sof[p]);
+                    const int64_t xi = idx[j];
+                    const int64_t before = j > pk_off[p] ? static_cast<int64_t>(idx[j - 1]) : -1;
+                    const bool ok = xi >= lo && xi < hi && xi > before;
+                    st_loc[q - cb] = ok ? static_cast<uint16_t>(xi - lo) : 0xffffu;
+                    st_val[q - cb] = vals[j];
+                }
+                __syncthreads();
+                constexpr int kPer = kDenseStage / kBlock;
+                bool pend[kPer];
+                bool anyp = false;
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    const uint32_t q = tid + i * kBlock;
+                    pend[i] = cb + q < ce && st_loc[q] != 0xffffu;
+                    anyp |= pend[i];
+                }
+                while (__syncthreads_or(anyp)) {
+#pragma unroll
+                    for (int i = 0; i < kPer; ++i)
+                        if (pend[i]) atomicMin(&own[st_loc[tid + i * kBlock]], round_key(epoch, tid + i * kBlock));
+                    __syncthreads();
+                    anyp = false;
+#pragma unroll
+                    for (int i = 0; i < kPer; ++i) {
+                        const uint32_t q = tid + i * kBlock;
+                        if (pend[i] && own[st_loc[q]] == round_key(epoch, q)) {
+                            apply_entry<FUSED>(acc, touched, G, lo, st_loc[q], st_val[q]);
+                            pend[i] = false;
+                        }
+                        anyp |= pend[i];
+                    }
+                    next_round();
+                }
+                __syncthreads();  // the chunk's staging area is reused by the next chunk
+            }
+#pragma unroll
+            for (int u = 0; u < SLOTS; ++u) {
+                if (cnt[u] > 0) last[u] = idx[cur[u] + cnt[u] - 1];
+                cur[u] += cnt[u];
+            }
+            if (more) load_window(xB, vB, inB);
+        }
+        __syncthreads();
+        if (FUSED) {
+            // the whole tile: G (if given) = the sum, w -= fl(lr * G); the sums go
+            // back to +0 for the next tile
+#pragma unroll
+            for (int r = 0; r < kQuads; ++r) {
+                const int q = 4 * (tid + r * kBlock);
+                if (q + 4 <= len) {
+                    const f4 a = *reinterpret_cast<const f4*>(&acc[q]);
+                    *reinterpret_cast<f4*>(&acc[q]) = f4{0.f, 0.f, 0.f, 0.f};
+                    const f4 st = lr * a;
+                    st4_changed(wA[r] - st, wA[r], reinterpret_cast<f4*>(w + lo + q));
+                    if (G) st4(a, reinterpret_cast<f4*>(G + lo + q));
+                } else if (q < len) {
+                    for (int c = 0; c < 4 && q + c < len; ++c) {
+                        const float st = lr * acc[q + c];
+                        w[lo + q + c] = w[lo + q + c] - st;
+                        if (G) G[lo + q + c] = acc[q + c];
+                        acc[q + c] = 0.0f;
+                    }
+                }
+            }
+        } else {
+            if (dense) {
+                for (int i = tid; i < kTile; i += kBlock)
+                    if (touched[i >> 5] & (1u << (i & 31))) G[lo + i] = acc[i];
+                __syncthreads();
+            } else {
+                // each position by the entry that touched it first
+#pragma unroll
+                for (int u = 0; u < SLOTS; ++u)
+                    if (back[u] != 0xffffffffu) G[lo + back[u]] = acc[back[u]];
+            }
+            for (int i = tid; i < kTile / 32; i += kBlock) touched[i] = 0;
+        }
+        __syncthreads();
+        if (more) {
+#pragma unroll
+            for (int r = 0; r < kQuads; ++r) wA[r] = wB[r];
+#pragma unroll
+            for (int u = 0; u < SLOTS; ++u) {
+                xA[u] = xB[u];
+                vA[u] = vB[u];
+                inA[u] = inB[u];
             }
         }
     }
@@ -263,16 +617,57 @@ __global__ __launch_bounds__(kBlock) void k_sgd(float* __restrict__ w, const flo
     f4* w4 = reinterpret_cast<f4*>(w);
     const f4* g4 = reinterpret_cast<const f4*>(G);
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < nv; i += stride) {
-        const f4 gv = __builtin_nontemporal_load(g4 + i);
-        const f4 wv = __builtin_nontemporal_load(w4 + i);
+        const f4 gv = ld4(g4 + i);
+        const f4 wv = ld4(w4 + i);
         const f4 st = lr * gv;
-        __builtin_nontemporal_store(wv - st, w4 + i);
+        st4_changed(wv - st, wv, w4 + i);
     }
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
         const int64_t j = nv * 4 + threadIdx.x;
         const float st = lr * G[j];
         w[j] = w[j] - st;
     }
+}
+
+// Blocks of the multi-tile kernel that the GPU holds at once (its LDS use
+// sets that), asked once per kernel and device.
+template <bool FUSED, int SLOTS>
+static int resident_blocks(int64_t* out) {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(EF_EHIP, "decode: no current device");
+    if (!cached[dev]) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_tiles<FUSED, SLOTS>, kBlock, 0) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return fail(EF_EHIP, "decode: occupancy query failed");
+        cached[dev] = std::max(1, per_cu) * std::max(1, cus);
+    }
+    *out = cached[dev];
+    return EF_OK;
+}
+
+// The tiles of G split among the blocks the GPU holds at once, each block a
+// run of consecutive tiles; more packets than one block carries take the
+// one-tile-per-block kernel.
+template <bool FUSED>
+static int launch_decode(const char* label, float* G, int64_t n, int32_t npk, const float* vals,
+                         const int32_t* idx, const int64_t* pk_off, float* w, float lr, hipStream_t s) {
+    const int64_t ntiles = cdiv(n, kTile);
+    if (npk > kMaxPk)
+        return launch(label, k_decode<FUSED>, dim3(static_cast<unsigned>(ntiles)), dim3(kBlock), s, G, n, npk,
+                      vals, idx, pk_off, w, lr);
+    int64_t res = 0;
+    if (npk <= kPkGroup) {
+        EF_TRY((resident_blocks<FUSED, 1>(&res)));
+        return launch(label, k_decode_tiles<FUSED, 1>, dim3(static_cast<unsigned>(std::min(ntiles, res))),
+                      dim3(kBlock), s, G, n, npk, vals, idx, pk_off, w, lr, ntiles);
+    }
+    EF_TRY((resident_blocks<FUSED, kMaxPk / kPkGroup>(&res)));
+    return launch(label, k_decode_tiles<FUSED, kMaxPk / kPkGroup>, dim3(static_cast<unsigned>(std::min(ntiles, res))),
+                  dim3(kBlock), s, G, n, npk, vals, idx, pk_off, w, lr, ntiles);
 }
 
 }  // namespace decode
@@ -294,8 +689,7 @@ extern "C" int sparse_decode_accumulate(float* G, int64_t n, int32_t npk, const 
                           s, n, idx, pk_off, invalid));
     }
     if (n == 0 || npk == 0) return EF_OK;
-    return launch("decode_scatter", decode::k_decode<false>, dim3(static_cast<unsigned>(cdiv(n, decode::kTile))),
-                  dim3(decode::kBlock), s, G, n, npk, vals, idx, pk_off, static_cast<float*>(nullptr), 0.0f);
+    return decode::launch_decode<false>("decode_scatter", G, n, npk, vals, idx, pk_off, nullptr, 0.0f, s);
 }
 
 extern "C" int sparse_decode_sgd(float* w, float* G, int64_t n, int32_t npk, const float* vals, const int32_t* idx,
@@ -313,8 +707,7 @@ extern "C" int sparse_decode_sgd(float* w, float* G, int64_t n, int32_t npk, con
                           s, n, idx, pk_off, invalid));
     }
     if (n == 0) return EF_OK;
-    return launch("decode_sgd", decode::k_decode<true>, dim3(static_cast<unsigned>(cdiv(n, decode::kTile))),
-                  dim3(decode::kBlock), s, G, n, npk, vals, idx, pk_off, w, lr);
+    return decode::launch_decode<true>("decode_sgd", G, n, npk, vals, idx, pk_off, w, lr, s);
 }
 
 extern "C" int sgd_apply(float* w, const float* G, int64_t n, float lr, void* stream) {

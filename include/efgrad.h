@@ -308,7 +308,8 @@ int sgd_apply(float* w, const float* G, int64_t n, float lr, void* stream);
  * at +0 everywhere, the packets are added exactly as sparse_decode_accumulate
  * adds them, and w_i = w_i - (lr * G_i) as sgd_apply computes it.  Bit for bit
  * the same w (and G) as zeroing G, sparse_decode_accumulate, then sgd_apply,
- * with one read and one write of w and one write of G instead of three passes.
+ * reading w and writing G once; w is written back only where its bits change
+ * (where the packets land), which gives the same memory contents.
  * G (nullable) receives the sum; w and G are n floats, 16-byte aligned, and
  * must not overlap.  Packets, pk_off and *invalid as for
  * sparse_decode_accumulate. */
