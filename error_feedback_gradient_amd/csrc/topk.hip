@@ -20,29 +20,27 @@
 //                 stream already writes e = 0 for them.  Each block adds its
 //                 regions' candidate counts to their group totals with one
 //                 atomic per group.  This is the only full pass: 12 B/element.
-//   3. scan       per-tensor candidate totals from per-group counts (true
-//                 counts: a region may have more candidates than its slot
-//                 holds); a tensor drops to the exact fallback when its
-//                 candidates exceed its slot capacity or fewer than k were
-//                 found (decided on the device; later kernels skip the path
-//                 not taken).
-//   4. compact    per group of 256 regions: candidate slots -> one dense,
-//                 index-ordered list, plus the first radix histogram.
+//   3. compact    per group of 256 regions: the tensor's group totals decide
+//                 its path (exact fallback when its candidates exceed its slot
+//                 capacity or fewer than k were found); candidate slots -> one
+//                 dense index-ordered list, plus the first radix histogram.
 //      recollect  a region whose slot overflowed (its first `cap` candidates
 //                 are in the slot, the rest are untouched in e) is read again
 //                 past its last stored index by one wave, which appends the
 //                 rest at their places in the dense list.  Clustered
 //                 magnitudes thus cost one extra read of the crowded regions
 //                 instead of the exact pass over the whole tensor.
-//   5. radix      exact k-th largest key T over the candidates: digit passes
-//                 of 11, 10 and 10 bits with LDS-privatised histograms.
-//   6. emit       entries with key > T, plus the first r entries with key == T
+//   4. radix      exact k-th largest key T over the candidates: digits of 11,
+//                 10 and 10 bits, each histogram (LDS-privatised) built by one
+//                 kernel and its digit found by the blocks of the next one.
+//   5. emit       entries with key > T, plus the first r entries with key == T
 //                 in index order, are written in index order.  Their residual
 //                 becomes +0 unless the stream already cleared it; a dropped
 //                 candidate that the stream cleared gets x back.
-// The fallback first puts x back wherever the stream cleared it, then runs
-// steps 5-6 over the whole tensor (x sits in e).  Only integer atomics are
-// used, so results do not depend on timing.
+// The exact fallback runs steps 4-5 over the whole tensor (x sits in e): its
+// compaction blocks histogram x for the first digit and put x back wherever
+// the stream cleared it.  Only integer atomics are used, so results do not
+// depend on timing.
 #include <math.h>
 #include <string.h>
 
@@ -98,6 +96,18 @@ constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
 constexpr int kChunk = EFG_CHUNK;                  // entries per block-unit in select and emit
 static_assert(kChunk % kBlock == 0, "k_write: each wave takes kChunk / kBlock rows of 64 entries");
 constexpr int kRadixBins = 2048;
+// Every radix histogram keeps, after its fine bins, coarse bins of 32 fine
+// ones each (64 for the 11-bit first digit, 32 for the 10-bit ones): the
+// kernel that needs a tensor's digit finds it from the coarse bins and one
+// slice of 32 fine bins, instead of a digit launch reading every bin.
+constexpr int kCoarse = 64;
+constexpr int kHistWords = kRadixBins + kCoarse;
+// A fallback tensor's elements are taken in units of kRawChunk (kRawSub
+// chunks of kChunk), so that its per-unit counts stay few enough for one
+// block to scan (79,346 units at 1.3e9 elements).
+constexpr int kRawSub = 8;
+constexpr int kRawChunk = kRawSub * kChunk;
+constexpr int kSelectBlocks = 2048;                // select / emit blocks shared out among the tensors
 constexpr int kHistCopies = 8;                     // copies of a histogram when a call has few tensors (1 or this)
 constexpr int64_t kCompactBlocksMax = 2048;        // compaction blocks the GPU holds at once (8 per CU)
 constexpr int kMaxGrid = 2048;
@@ -134,28 +144,31 @@ struct alignas(16) SegPlan {
     int32_t cap;        // candidate slots per region
     int32_t mode;
     int32_t sample_chunks, sample_rank;
-    int32_t sample_rank_hi, exhaustive, direct, raw_chunks;
+    int32_t sample_rank_hi, exhaustive, direct, raw_units;  // raw units: kRawChunk elements each
     int32_t compact_split;  // blocks per group in the compaction (a power of two, 1 to 32)
-    int32_t pad[5];
+    int32_t cunit_base;     // first entry of the tensor's candidate units in the per-unit count arrays
+    int32_t runit_base;     // first entry of its raw units
+    int32_t pad[3];
 };
 static_assert(sizeof(SegPlan) == 112, "SegPlan layout");
 
+// Per-call state of a tensor.  Each field is written by one kernel (the
+// tensor's first block in it) and read by later kernels only.
 struct alignas(16) SegState {
-    uint32_t tlo;       // keys >= tlo become candidates
+    uint32_t tlo;       // keys >= tlo become candidates (sample select)
     uint32_t thi;       // stored candidates with key >= thi get e = 0 in the stream
-    uint32_t spare, fallback;
-    uint32_t ncand, dense_off, cchunk_begin, cchunks;
-    uint32_t prefix, want, T, r;
-    uint32_t group_base;  // the tensor's first group offset (dense list position = dense_off + grp_off - group_base)
-    uint32_t pad[3];
+    uint32_t fallback;  // the exact full-pass selection (compaction)
+    uint32_t ncand;     // candidates found (compaction)
+    uint32_t p0, w0;    // top 11 key bits of T and the rank left below them (first select pass)
+    uint32_t p1, w1;    // top 21 bits and the rank left (second select pass)
+    uint32_t T, r;      // the k-th largest key and the ties kept (count pass)
+    uint32_t pad[6];
 };
 static_assert(sizeof(SegState) == 64, "SegState layout");
 
 struct alignas(16) Header {
-    uint32_t total_rchunks;  // raw chunks of the tensors that take the exact fallback
-    uint32_t total_cchunks;
     uint32_t n_overflow;  // entries of the overflowed-region list
-    uint32_t pad[61];
+    uint32_t pad[63];
 };
 static_assert(sizeof(Header) == 256, "Header layout");
 
@@ -192,19 +205,20 @@ struct Plan {
     int64_t SB = 0;     // sample blocks
     int32_t sample_rounds = 1;  // groups of kSampleBlockChunks chunks per sample block
     int32_t hcopies = 1;        // copies of each radix histogram (blocks add to copy blockIdx % hcopies)
-    int64_t QR = 0;     // bound on raw chunks (fallback units): those of every tensor
-    int64_t QC = 0;     // bound on candidate chunks
+    int64_t QR = 0;     // raw units (fallback units) of every tensor
+    int64_t QC = 0;     // bound on candidate units (kChunk entries each)
+    int64_t HB = 0;     // select / emit blocks (static share of each tensor: hb)
     int64_t Ctot = 0;   // candidate slot entries
     int64_t CB = 0;     // compaction blocks
     bool any_normal = false;
     SmallVec<SegPlan, 1> seg;
-    SmallVec<int32_t, 2> rb, gbb, sbb, cbb;  // prefix tables, nseg+1 each
+    SmallVec<int32_t, 2> rb, gbb, sbb, cbb, hb;  // prefix tables, nseg+1 each
 };
 
 struct Layout {
-    size_t status, plan, rb, gbb, sbb, cbb, static_end;
+    size_t status, plan, rb, gbb, sbb, cbb, hb, static_end;
     size_t header, state, shist, rhist, grp_cnt, zero_end;
-    size_t ccb, rcb, grp_off, region_cnt, ovf, cpair, dval, didx, cgt, ceq, rgt, req, spart, gpart, cpart, rpart;
+    size_t grp_off, region_cnt, ovf, cpair, dval, didx, cgt, ceq, rgt, req, spart, gpart, cpart, rpart;
     size_t total;
 };
 
@@ -221,16 +235,15 @@ static Layout make_layout(const Plan& p) {
     L.gbb = at; at += (ns + 1) * 4;
     L.sbb = at; at += (ns + 1) * 4;
     L.cbb = at; at += (ns + 1) * 4;
+    L.hb = at; at += (ns + 1) * 4;
     at = round_up(at, 256);
     L.static_end = at;
     L.header = take(sizeof(Header));
     L.state = take(ns * sizeof(SegState));
     L.shist = take(ns * static_cast<size_t>(p.hcopies) * kSampleBins * 4);
-    L.rhist = take(3 * ns * static_cast<size_t>(p.hcopies) * kRadixBins * 4);
+    L.rhist = take(3 * ns * static_cast<size_t>(p.hcopies) * kHistWords * 4);
     L.grp_cnt = take(static_cast<size_t>(p.G) * 4);
     L.zero_end = at;
-    L.ccb = take((ns + 1) * 4);
-    L.rcb = take((ns + 1) * 4);
     L.grp_off = take(static_cast<size_t>(p.G) * 4);
     L.region_cnt = take(static_cast<size_t>(p.R) * 4);
     L.ovf = take(static_cast<size_t>(p.R) * 4);
@@ -265,6 +278,7 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
     p.gbb.assign(nseg + 1, 0);
     p.sbb.assign(nseg + 1, 0);
     p.cbb.assign(nseg + 1, 0);
+    p.hb.assign(nseg + 1, 0);
     int64_t out = 0;
     for (int32_t s = 0; s < nseg; ++s) {
         const int64_t n = off[s + 1] - off[s];
@@ -312,6 +326,7 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
                 // exact full-pass path directly
                 P.direct = 1;
                 P.cap = 0;
+                P.compact_split = 1;
             } else {
                 int64_t cap = static_cast<int64_t>(ceil(kRegion * rho * 3.0)) + 32;
                 cap = static_cast<int64_t>(round_up(static_cast<size_t>(cap), 4));
@@ -330,10 +345,12 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
                 P.compact_split = 1;
                 while (P.compact_split < 32 && per_group > 512.0 * P.compact_split) P.compact_split *= 2;
             }
-            P.raw_chunks = static_cast<int32_t>(cdiv(n, kChunk));
+            P.raw_units = static_cast<int32_t>(cdiv(n, kRawChunk));
             p.any_normal = true;
         }
         P.cand_base = p.Ctot;
+        P.cunit_base = static_cast<int32_t>(p.QC);
+        P.runit_base = static_cast<int32_t>(p.QR);
         p.Ctot += static_cast<int64_t>(P.nregions) * P.cap;
         p.QC += cdiv(static_cast<int64_t>(P.nregions) * P.cap, kChunk);
         P.region_begin = static_cast<int32_t>(p.R);
@@ -343,9 +360,9 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
         p.R += P.nregions;
         p.G += P.ngroups;
         p.SB += P.sample_chunks;  // total sample chunks for now; blocks below
-        p.QR += P.raw_chunks;
+        p.QR += P.raw_units;
         p.cbb[s] = static_cast<int32_t>(p.CB);
-        if (P.cap > 0) p.CB += static_cast<int64_t>(P.ngroups) * P.compact_split;
+        if (P.mode == MODE_NORMAL) p.CB += static_cast<int64_t>(P.ngroups) * P.compact_split;
     }
     // Sample blocks: many small tensors would otherwise give thousands of blocks,
     // each clearing and flushing a whole 4096-bin histogram; beyond about
@@ -378,7 +395,7 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
         p.CB = 0;
         for (int32_t s = 0; s < nseg; ++s) {
             p.cbb[s] = static_cast<int32_t>(p.CB);
-            if (p.seg[s].cap > 0) p.CB += static_cast<int64_t>(p.seg[s].ngroups) * p.seg[s].compact_split;
+            if (p.seg[s].mode == MODE_NORMAL) p.CB += static_cast<int64_t>(p.seg[s].ngroups) * p.seg[s].compact_split;
         }
     }
     p.rb[nseg] = static_cast<int32_t>(p.R);
@@ -386,6 +403,22 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
     p.sbb[nseg] = static_cast<int32_t>(p.SB);
     p.cbb[nseg] = static_cast<int32_t>(p.CB);
     p.QC += 1;
+    // Select / emit blocks: each tensor that selects gets a fixed share of
+    // about kSelectBlocks blocks, in proportion to its size (at least one, at
+    // most one per raw unit), so that a block finds its tensor in a static
+    // table and strides over the tensor's units, whichever path it takes.
+    int64_t raw_total = 0;
+    for (int32_t s = 0; s < nseg; ++s)
+        if (p.seg[s].mode == MODE_NORMAL) raw_total += p.seg[s].raw_units;
+    p.HB = 0;
+    for (int32_t s = 0; s < nseg; ++s) {
+        p.hb[s] = static_cast<int32_t>(p.HB);
+        const SegPlan& P = p.seg[s];
+        if (P.mode != MODE_NORMAL) continue;
+        const int64_t share = raw_total > 0 ? kSelectBlocks * static_cast<int64_t>(P.raw_units) / raw_total : 0;
+        p.HB += std::max<int64_t>(1, std::min<int64_t>(P.raw_units, share));
+    }
+    p.hb[nseg] = static_cast<int32_t>(p.HB);
     return EF_OK;
 }
 
@@ -796,190 +829,243 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
     }
 }
 
-// 3. group offsets, per-tensor candidate totals and the path decision
-constexpr int kScanBlock = 1024;
-__global__ __launch_bounds__(kScanBlock) void k_scan_groups(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                            const int32_t* __restrict__ gbb, int64_t G,
-                                                            const uint32_t* __restrict__ grp_cnt,
-                                                            uint32_t* __restrict__ grp_off,
-                                                            SegState* __restrict__ st, uint32_t* __restrict__ ccb,
-                                                            uint32_t* __restrict__ rcb, Header* __restrict__ hdr,
-                                                            uint32_t force_fallback) {
-    __shared__ uint32_t lds[kScanBlock / kWave + 1];
-    uint32_t carry = 0;
-    for (int64_t t0 = 0; t0 < G; t0 += kScanBlock) {
-        const int64_t i = t0 + threadIdx.x;
-        const uint32_t v = i < G ? grp_cnt[i] : 0u;
-        uint32_t tt;
-        const uint32_t ex = block_excl_scan<kScanBlock>(v, lds, &tt);
-        if (i < G) grp_off[i] = carry + ex;
-        carry += tt;
-    }
-    const uint32_t total = carry;
-    __syncthreads();
-    uint32_t cc = 0, rc = 0;
-    for (int32_t t0 = 0; t0 < nseg; t0 += kScanBlock) {
-        const int32_t s = t0 + threadIdx.x;
-        uint32_t cchunks = 0, rchunks = 0;
-        if (s < nseg && plan[s].mode == MODE_NORMAL) {
-            const int64_t b = gbb[s], en = gbb[s + 1];
-            const uint32_t d0 = b < G ? grp_off[b] : total;
-            const uint32_t d1 = en < G ? grp_off[en] : total;
-            const uint32_t nc = d1 - d0;
-            // the dense list of a tensor reuses its own slot area's extent
-            const int64_t capacity = static_cast<int64_t>(plan[s].nregions) * plan[s].cap;
-            const bool fb = force_fallback || plan[s].direct || static_cast<int64_t>(nc) > capacity ||
-                            static_cast<int64_t>(nc) < plan[s].k;
-            st[s].fallback = fb ? 1u : 0u;
-            st[s].ncand = nc;
-            st[s].dense_off = static_cast<uint32_t>(plan[s].cand_base);
-            st[s].group_base = d0;
-            st[s].want = static_cast<uint32_t>(plan[s].k);
-            st[s].prefix = 0;
-            cchunks = fb ? 0u : (nc + kChunk - 1) / kChunk;
-            rchunks = fb ? static_cast<uint32_t>(plan[s].raw_chunks) : 0u;
-            st[s].cchunks = cchunks;
-        }
-        uint32_t tt, tr;
-        const uint32_t ex = block_excl_scan<kScanBlock>(cchunks, lds, &tt);
-        const uint32_t exr = block_excl_scan<kScanBlock>(rchunks, lds, &tr);
-        if (s < nseg) {
-            ccb[s] = cc + ex;
-            st[s].cchunk_begin = cc + ex;
-            rcb[s] = rc + exr;
-        }
-        cc += tt;
-        rc += tr;
-    }
-    if (threadIdx.x == 0) {
-        ccb[nseg] = cc;
-        rcb[nseg] = rc;
-        hdr->total_cchunks = cc;
-        hdr->total_rchunks = rc;
-    }
-}
-
-// Radix histogram of pass p (0..2) of tensor s, copy c: each pass has its own
-// histograms, cleared by k_init, so no kernel has to clear one after use.
+// Radix histogram of pass p (0..2) of tensor s, copy c: kRadixBins fine bins
+// then kCoarse coarse ones.  Each pass has its own histograms, cleared by
+// k_init, so no kernel has to clear one after use.
 __device__ __forceinline__ uint32_t* radix_hist(uint32_t* rhist, int pass, int s, int c, int32_t nseg,
                                                 int32_t hcopies) {
-    return rhist + ((static_cast<size_t>(pass) * nseg + s) * hcopies + c) * kRadixBins;
+    return rhist + ((static_cast<size_t>(pass) * nseg + s) * hcopies + c) * kHistWords;
 }
 
-// 4. per group of regions: candidate slots -> dense index-ordered list, and the
-//    first radix histogram (top 11 key bits) of the tensor.  A tensor with many
-//    candidates per group shares each group among compact_split blocks: every
-//    one scans the group's region counts and copies its own slice of regions.
-//    For a tensor that takes the exact fallback, the same blocks instead put
-//    back x where the stream already wrote e = 0, so that e holds x whole.
+// Sum of the 32 fine bins of coarse bin c of an LDS histogram, read with a
+// rotation so that the lanes of a wave hit different banks.
+__device__ __forceinline__ uint32_t coarse_sum(const uint32_t* h, int c) {
+    uint32_t t = 0;
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) t += h[c * 32 + ((i + c) & 31)];
+    return t;
+}
+
+// Adds a block's LDS histogram h (nb fine bins) to the global one gh: the
+// fine bins that are not zero, then the coarse sums.  Every thread of the
+// block calls it; h is not changed.
+__device__ __forceinline__ void flush_hist(const uint32_t* h, int nb, uint32_t* gh) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb; i += kBlock)
+        if (h[i]) atomicAdd(&gh[i], h[i]);
+    for (int c = threadIdx.x; c < nb / 32; c += kBlock) {
+        const uint32_t t = coarse_sum(h, c);
+        if (t) atomicAdd(&gh[kRadixBins + c], t);
+    }
+}
+
+// The same for one wave's own LDS histogram (the wave's lanes only).
+__device__ __forceinline__ void flush_hist_wave(const uint32_t* h, uint32_t* gh) {
+    for (int i = lane(); i < kRadixBins; i += kWave)
+        if (h[i]) atomicAdd(&gh[i], h[i]);
+    const uint32_t t = coarse_sum(h, lane());
+    if (t) atomicAdd(&gh[kRadixBins + lane()], t);
+}
+
+// The bin d of a tensor's histogram (nb = 2048 or 1024 fine bins, summed over
+// its hcopies copies) that holds the want-th largest key: fewer than `want`
+// keys lie above d and at least `want` from d up; *above = keys above d.
+// Called by a whole wave, every lane gets the result: one round of loads for
+// the coarse bins, one for the 32 fine bins of the coarse bin found (all of a
+// lane's copies loaded together).  Needs want >= 1 and at least want keys.
+__device__ __forceinline__ void wave_find_digit(const uint32_t* gh0, int32_t hcopies, int nb, uint32_t want,
+                                                uint32_t* d, uint32_t* above) {
+    const int l = static_cast<int>(lane());
+    const int nc = nb / 32;
+    uint32_t w[kHistCopies];
+    // lane l: coarse bin nc - 1 - l (the top one first)
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c)
+        w[c] = gh0[(c < hcopies ? c : 0) * kHistWords + kRadixBins + (l < nc ? nc - 1 - l : 0)];
+    uint32_t cv = 0;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) cv += (c < hcopies && l < nc) ? w[c] : 0u;
+    const uint32_t cum = wave_incl_scan(cv);  // keys in the top l + 1 coarse bins
+    const uint64_t hit = __ballot(l < nc && cum >= want);
+    const int L = hit ? static_cast<int>(__ffsll(static_cast<long long>(hit))) - 1 : nc - 1;
+    const int cb = nc - 1 - L;
+    const uint32_t above_c = __shfl(cum, L, kWave) - __shfl(cv, L, kWave);
+    // lane l < 32: fine bin 32 cb + 31 - l
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c)
+        w[c] = gh0[(c < hcopies ? c : 0) * kHistWords + 32 * cb + (l < 32 ? 31 - l : 0)];
+    uint32_t fv = 0;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) fv += (c < hcopies && l < 32) ? w[c] : 0u;
+    const uint32_t cum2 = wave_incl_scan(fv);
+    const uint64_t hit2 = __ballot(l < 32 && above_c + cum2 >= want);
+    const int L2 = hit2 ? static_cast<int>(__ffsll(static_cast<long long>(hit2))) - 1 : 31;
+    *d = static_cast<uint32_t>(32 * cb + 31 - L2);
+    *above = above_c + __shfl(cum2, L2, kWave) - __shfl(fv, L2, kWave);
+}
+
+// 3. compaction, one block per group of kGroup regions (compact_split blocks
+//    per group for tensors with many expected candidates, each taking a slice
+//    of the group's regions).  Every block first sums its tensor's group
+//    counts: the candidates before its group give its dense offset, their
+//    total decides the path (the tensor's first block records both).
+//    Candidate path: the group's slots -> the dense index-ordered list, plus
+//    the first radix histogram (top 11 key bits).  Exact fallback: the block's
+//    elements are read for the first radix histogram of the full pass, and
+//    then x is put back where the stream cleared it (those reads saw +0: the
+//    histogram moves each such element from bin 0 to its own bin).
 constexpr int kCompactItems = 8;
+constexpr int kRawRows = 16;
 __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ plan, int32_t nseg,
                                                     const int32_t* __restrict__ cbb, const int32_t* __restrict__ gbb,
-                                                    const int32_t* __restrict__ rb, const SegState* __restrict__ st,
+                                                    const int32_t* __restrict__ rb, SegState* __restrict__ st,
+                                                    const uint32_t* __restrict__ grp_cnt,
+                                                    uint32_t* __restrict__ grp_off,
                                                     const uint32_t* __restrict__ region_cnt,
-                                                    const uint32_t* __restrict__ grp_off,
                                                     const uint2* __restrict__ cpair, float* __restrict__ dval,
                                                     int32_t* __restrict__ didx, uint32_t* __restrict__ rhist,
                                                     int32_t hcopies, float* __restrict__ e,
-                                                    uint32_t* __restrict__ stray) {
+                                                    uint32_t* __restrict__ stray, uint32_t force_fallback) {
     __shared__ uint32_t loff[kGroup];
     __shared__ uint32_t h[kRadixBins];
     __shared__ uint32_t lds[kWavesPerBlock + 1];
+    __shared__ uint32_t red[2][kWavesPerBlock];
     const int b = blockIdx.x;
     const int s = upper_index_wave(cbb, nseg, b);
-    if (plan[s].mode != MODE_NORMAL) return;
-    const int split = plan[s].compact_split;
+    const SegPlan& P = plan[s];
+    const int split = P.compact_split;
     const int lb = b - cbb[s];
     const int gl = lb / split, part = lb % split;
     const int gi = gbb[s] + gl;
+    const int t = threadIdx.x;
+    // the tensor's candidates before this group, and in all
+    uint32_t before = 0, total = 0;
+    for (int g = t; g < P.ngroups; g += kBlock) {
+        const uint32_t c = grp_cnt[gbb[s] + g];
+        total += c;
+        before += g < gl ? c : 0u;
+    }
+    before = wave_sum(before);
+    total = wave_sum(total);
+    if (lane() == 0) {
+        red[0][t / kWave] = before;
+        red[1][t / kWave] = total;
+    }
+    for (int i = t; i < kRadixBins; i += kBlock) h[i] = 0;
+    __syncthreads();
+    before = 0;
+    total = 0;
+    for (int i = 0; i < kWavesPerBlock; ++i) {
+        before += red[0][i];
+        total += red[1][i];
+    }
+    const int64_t capacity = static_cast<int64_t>(P.nregions) * P.cap;
+    const bool fb = force_fallback || P.direct || static_cast<int64_t>(total) > capacity ||
+                    static_cast<int64_t>(total) < P.k;
+    if (t == 0) {
+        if (lb == 0) {
+            st[s].fallback = fb ? 1u : 0u;
+            st[s].ncand = total;
+        }
+        if (part == 0) grp_off[gi] = before;  // k_recollect places the group's overflowed regions
+    }
     const int64_t r0 = rb[s] + static_cast<int64_t>(gl) * kGroup;  // first region (global)
-    const int nr = min(kGroup, plan[s].nregions - gl * kGroup);
+    const int nr = min(kGroup, P.nregions - gl * kGroup);
     const int slice = kGroup / split;
-    const int rs = part * slice;                                    // this block's regions [rs, re)
+    const int rs = part * slice;  // this block's regions [rs, re)
     const int re = min(nr, rs + slice);
     if (rs >= re) return;
-    const int t = threadIdx.x;
-    if (st[s].fallback) {
-        // the exact selection runs over x held in e: put back the stored
-        // candidates the stream cleared (key >= thi), one wave per region
+    const int64_t cap = P.cap;
+    if (fb) {
+        // the first radix histogram of x over the block's elements [a, z); e
+        // reads +0 where the stream cleared a stored candidate
+        const int64_t a = P.off + (static_cast<int64_t>(gl) * kGroup + rs) * kRegion;
+        const int64_t z = P.off + min((static_cast<int64_t>(gl) * kGroup + re) * kRegion, P.n);
+        for (int64_t i0 = a + t; i0 < z; i0 += kBlock * kRawRows) {
+            float x[kRawRows];
+#pragma unroll
+            for (int u = 0; u < kRawRows; ++u) x[u] = e[min(i0 + u * kBlock, z - 1)];
+#pragma unroll
+            for (int u = 0; u < kRawRows; ++u)
+                if (i0 + u * kBlock < z) atomicAdd(&h[key_of(x[u]) >> 20], 1u);
+        }
+        __syncthreads();  // every read of e is done before x is put back
         const uint32_t thi = st[s].thi;
-        const int64_t lo = plan[s].off, hi = plan[s].off + plan[s].n;
-        const int64_t cap = plan[s].cap;
+        const int64_t lo = P.off, hi = P.off + P.n;
         for (int r = rs + t / kWave; r < re; r += kWavesPerBlock) {
             const uint32_t cnt = min(region_cnt[r0 + r], static_cast<uint32_t>(cap));
-            const int64_t slot = plan[s].cand_base + (r0 + r - rb[s]) * cap;
+            const int64_t slot = P.cand_base + (r0 + r - rb[s]) * cap;
             for (uint32_t j = lane(); j < cnt; j += kWave) {
                 const uint2 pr = cpair[slot + j];
                 const float v = __uint_as_float(pr.x);
+                const uint32_t key = key_of(v);
                 // indices were written by the stream of this call; the range check
                 // keeps a workspace overwritten meanwhile from becoming a stray
                 // write, and counts it
-                if (key_of(v) >= thi) {
-                    if (pr.y >= lo && pr.y < hi) e[pr.y] = v;
-                    else atomicAdd(stray, 1u);
+                if (key >= thi) {
+                    if (pr.y >= lo && pr.y < hi) {
+                        e[pr.y] = v;
+                        atomicSub(&h[0], 1u);
+                        atomicAdd(&h[key >> 20], 1u);
+                    } else {
+                        atomicAdd(stray, 1u);
+                    }
                 }
             }
         }
-        return;
-    }
-    const uint32_t c = t < nr ? region_cnt[r0 + t] : 0u;
-    uint32_t total;
-    const uint32_t ex = block_excl_scan<kBlock>(c, lds, &total);
-    loff[t] = ex;
-    for (int i = t; i < kRadixBins; i += kBlock) h[i] = 0;
-    __syncthreads();
-    const uint32_t q0 = loff[rs], q1 = re < nr ? loff[re] : total;
-    const uint32_t dbase = st[s].dense_off + (grp_off[gi] - st[s].group_base);
-    const int64_t slot0 = plan[s].cand_base + (r0 - rb[s]) * plan[s].cap;
-    const int64_t cap = plan[s].cap;
-    // kCompactItems entries per thread in flight: an entry past the block's
-    // range or past its region's slot (k_recollect writes those) reads the
-    // group's first slot instead and is not used
-    for (uint32_t qb = q0; qb < q1; qb += kBlock * kCompactItems) {
-        uint2 pr[kCompactItems];
-        bool ok[kCompactItems];
+    } else {
+        const uint32_t c = t < nr ? region_cnt[r0 + t] : 0u;
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan<kBlock>(c, lds, &tot);
+        loff[t] = ex;
+        __syncthreads();
+        const uint32_t q0 = loff[rs], q1 = re < nr ? loff[re] : tot;
+        const int64_t dbase = P.cand_base + before;
+        const int64_t slot0 = P.cand_base + (r0 - rb[s]) * cap;
+        // kCompactItems entries per thread in flight: an entry past the block's
+        // range or past its region's slot (k_recollect writes those) reads the
+        // group's first slot instead and is not used
+        for (uint32_t qb = q0; qb < q1; qb += kBlock * kCompactItems) {
+            uint2 pr[kCompactItems];
+            bool ok[kCompactItems];
 #pragma unroll
-        for (int u = 0; u < kCompactItems; ++u) {
-            const uint32_t q = qb + u * kBlock + t;
-            int64_t src = slot0;
-            ok[u] = q < q1;
-            if (ok[u]) {
-                const int r = rs + upper_index(loff + rs, re - rs, q);
-                ok[u] = q - loff[r] < cap;
-                if (ok[u]) src = slot0 + r * cap + (q - loff[r]);
+            for (int u = 0; u < kCompactItems; ++u) {
+                const uint32_t q = qb + u * kBlock + t;
+                int64_t src = slot0;
+                ok[u] = q < q1;
+                if (ok[u]) {
+                    const int r = rs + upper_index(loff + rs, re - rs, q);
+                    ok[u] = q - loff[r] < cap;
+                    if (ok[u]) src = slot0 + r * cap + (q - loff[r]);
+                }
+                pr[u] = cpair[src];
             }
-            pr[u] = cpair[src];
-        }
 #pragma unroll
-        for (int u = 0; u < kCompactItems; ++u) {
-            if (!ok[u]) continue;
-            const uint32_t q = qb + u * kBlock + t;
-            const float v = __uint_as_float(pr[u].x);
-            dval[dbase + q] = v;
-            didx[dbase + q] = static_cast<int32_t>(pr[u].y);
-            atomicAdd(&h[key_of(v) >> 20], 1u);
+            for (int u = 0; u < kCompactItems; ++u) {
+                if (!ok[u]) continue;
+                const uint32_t q = qb + u * kBlock + t;
+                const float v = __uint_as_float(pr[u].x);
+                dval[dbase + q] = v;
+                didx[dbase + q] = static_cast<int32_t>(pr[u].y);
+                atomicAdd(&h[key_of(v) >> 20], 1u);
+            }
         }
     }
-    __syncthreads();
-    if (q1 > q0) {
-        uint32_t* gh = radix_hist(rhist, 0, s, b % hcopies, nseg, hcopies);
-        for (int i = t; i < kRadixBins; i += kBlock)
-            if (h[i]) atomicAdd(&gh[i], h[i]);
-    }
+    flush_hist(h, kRadixBins, radix_hist(rhist, 0, s, b % hcopies, nseg, hcopies));
 }
 
-// 4b. one wave per overflowed region of a tensor on the fast path.  Its slot
-//     holds the region's first `cap` candidates in index order; the rest were
-//     not stored, so the stream left e = x for them.  They are read again from
-//     e past the last stored index (eight 64-element rows in flight per lane)
-//     and appended in index order after the stored ones, at the dense
-//     positions k_compact left free; their top digits join the first radix
-//     histogram (counted in a per-wave LDS histogram and added to the global
-//     one per region: the crowded candidates share a few bins, and one global
-//     atomic each would serialise on them).  Like the stream for stored ones,
-//     it clears e where the key is >= thi, so that every candidate of the
-//     dense list obeys the rule k_write relies on.  Grid-stride over the
-//     overflow list; empty in the common case.
+// 4. one wave per overflowed region of a tensor on the fast path.  Its slot
+//    holds the region's first `cap` candidates in index order; the rest were
+//    not stored, so the stream left e = x for them.  They are read again from
+//    e past the last stored index (eight 64-element rows in flight per lane)
+//    and appended in index order after the stored ones, at the dense
+//    positions k_compact left free; their top digits join the first radix
+//    histogram (counted in a per-wave LDS histogram and added to the global
+//    one per region: the crowded candidates share a few bins, and one global
+//    atomic each would serialise on them).  Like the stream for stored ones,
+//    it clears e where the key is >= thi, so that every candidate of the
+//    dense list obeys the rule k_write relies on.  Grid-stride over the
+//    overflow list; empty in the common case.
 constexpr int kRecollectBlocks = 512;
 constexpr int kRecollectRows = 8;
 __global__ __launch_bounds__(kBlock) void k_recollect(const SegPlan* __restrict__ plan, int32_t nseg,
@@ -1006,14 +1092,14 @@ __global__ __launch_bounds__(kBlock) void k_recollect(const SegPlan* __restrict_
         const int64_t gend = P.off + min(rl * kRegion + kRegion, P.n);
         const uint32_t cnt = region_cnt[w];
         const int64_t last = cpair[P.cand_base + rl * cap + cap - 1].y;  // index of the last stored candidate
-        // dense position of the region's first candidate: its group's offset plus
-        // the true counts of the group's earlier regions
+        // dense position of the region's first candidate: its group's offset in
+        // the tensor plus the true counts of the group's earlier regions
         const int64_t g0 = rb[s] + rl / kGroup * kGroup;
         uint32_t before = 0;
         for (int64_t r = g0 + l; r < w; r += kWave) before += region_cnt[r];
         before = wave_sum(before);
         const uint32_t gi = static_cast<uint32_t>(gbb[s] + rl / kGroup);
-        const uint32_t base = st[s].dense_off + (grp_off[gi] - st[s].group_base) + before;
+        const int64_t base = P.cand_base + grp_off[gi] + before;
         const uint32_t tlo = st[s].tlo, thi = st[s].thi;
         for (int i = l; i < kRadixBins; i += kWave) h[i] = 0;
         uint32_t pos = cap;  // next entry of this region
@@ -1040,9 +1126,7 @@ __global__ __launch_bounds__(kBlock) void k_recollect(const SegPlan* __restrict_
                 pos += popc64(bal);
             }
         }
-        uint32_t* gh = radix_hist(rhist, 0, s, blockIdx.x % hcopies, nseg, hcopies);
-        for (int i = l; i < kRadixBins; i += kWave)
-            if (h[i]) atomicAdd(&gh[i], h[i]);
+        flush_hist_wave(h, radix_hist(rhist, 0, s, blockIdx.x % hcopies, nseg, hcopies));
     }
 }
 
@@ -1061,184 +1145,191 @@ __device__ __forceinline__ bool radix_digit(int pass, uint32_t key, uint32_t pre
     return (key >> 10) == prefix;
 }
 
-// Work units of the select / emit kernels: candidate chunks of fast tensors
-// (kChunk entries of the dense list) followed by raw chunks of fallback
-// tensors (kChunk elements of x, which sits in e).  Both lists hold only the
-// tensors that take that path in this call (ccb, rcb: their prefix tables).
-struct Unit {
+// The select / emit blocks: each tensor that selects owns blocks
+// [hb[s], hb[s+1]) (static); they stride over the tensor's work units, which
+// depend on the path the compaction chose: the dense candidate list in units
+// of kChunk entries, or x itself (in e) in units of kRawChunk elements, each
+// taken as kRawSub chunks of kChunk.  Per-unit counts and statistics sit at
+// the tensor's static bases (cunit_base, runit_base).
+struct SelBlock {
     int s;
-    bool raw;
-    const float* v;        // values
-    const int32_t* id;     // indices (candidate units)
-    int64_t idx_base;      // first index (raw units)
-    uint32_t cnt;
-    uint32_t slot;         // index into cgt/ceq or rgt/req
+    int lb, nb;      // this block among the tensor's blocks
+    bool raw;        // exact fallback: units of x
+    uint32_t units;
 };
 
-__device__ __forceinline__ Unit unit_of(int64_t q, int64_t Qc, const SegPlan* plan, int32_t nseg,
-                                        const SegState* st, const uint32_t* ccb, const uint32_t* rcb,
-                                        const float* dval, const int32_t* didx, const float* e) {
-    Unit u;
-    if (q < Qc) {
-        const uint32_t qq = static_cast<uint32_t>(q);
-        u.s = upper_index_wave(ccb, nseg, qq);
-        const uint32_t lq = qq - ccb[u.s];
-        const uint32_t base = st[u.s].dense_off + lq * kChunk;
-        u.raw = false;
-        u.v = dval + base;
-        u.id = didx + base;
-        u.idx_base = 0;
-        u.cnt = min(static_cast<uint32_t>(kChunk), st[u.s].ncand - lq * kChunk);
-        u.slot = qq;
-    } else {
-        const uint32_t qq = static_cast<uint32_t>(q - Qc);
-        u.s = upper_index_wave(rcb, nseg, qq);
-        const int64_t lbeg = static_cast<int64_t>(qq - rcb[u.s]) * kChunk;
-        u.raw = true;
-        u.idx_base = plan[u.s].off + lbeg;
-        u.v = e + u.idx_base;
-        u.id = nullptr;
-        u.cnt = static_cast<uint32_t>(min(static_cast<int64_t>(kChunk), plan[u.s].n - lbeg));
-        u.slot = qq;
-    }
-    return u;
+__device__ __forceinline__ SelBlock sel_block(const SegPlan* plan, int32_t nseg, const int32_t* hb,
+                                              const SegState* st) {
+    SelBlock sb;
+    sb.s = upper_index_wave(hb, nseg, static_cast<int32_t>(blockIdx.x));
+    sb.lb = static_cast<int>(blockIdx.x) - hb[sb.s];
+    sb.nb = hb[sb.s + 1] - hb[sb.s];
+    sb.raw = st[sb.s].fallback != 0;
+    sb.units = sb.raw ? static_cast<uint32_t>(plan[sb.s].raw_units)
+                      : (st[sb.s].ncand + kChunk - 1) / kChunk;
+    return sb;
 }
 
-// A unit's entries as the select and emit kernels read them: wave w of the
+// One kChunk piece of a unit: chunk j (0 .. kRawSub - 1) of raw unit u, or
+// candidate unit u (j = 0).
+struct Chunk {
+    const float* v;      // values
+    const int32_t* id;   // indices (candidate units)
+    int64_t idx_base;    // first index (raw chunks)
+    uint32_t cnt;        // entries (0: nothing left in this raw unit)
+};
+
+__device__ __forceinline__ Chunk chunk_of(const SegPlan& P, const SegState& S, bool raw, uint32_t u, int j,
+                                          const float* dval, const int32_t* didx, const float* e) {
+    Chunk c;
+    if (!raw) {
+        const int64_t base = P.cand_base + static_cast<int64_t>(u) * kChunk;
+        c.v = dval + base;
+        c.id = didx + base;
+        c.idx_base = 0;
+        c.cnt = min(static_cast<uint32_t>(kChunk), S.ncand - u * kChunk);
+    } else {
+        const int64_t lbeg = static_cast<int64_t>(u) * kRawChunk + static_cast<int64_t>(j) * kChunk;
+        c.idx_base = P.off + lbeg;
+        c.v = e + c.idx_base;
+        c.id = nullptr;
+        c.cnt = lbeg < P.n ? static_cast<uint32_t>(min(static_cast<int64_t>(kChunk), P.n - lbeg)) : 0u;
+    }
+    return c;
+}
+
+// A chunk's entries as the select and emit kernels read them: wave w of the
 // block takes entries [w R 64, (w + 1) R 64), R = kChunk / kBlock rows of 64,
 // lane l entry w R 64 + 64 i + l in row i, so every row is one coalesced load.
-// All R loads are issued before any is used: an entry past the unit's end
-// (cnt >= 1) reads the unit's last entry instead and is marked absent.
+// All R loads are issued before any is used: an entry past the chunk's end
+// (cnt >= 1) reads the chunk's last entry instead and is marked absent.
 constexpr int kRows = kChunk / kBlock;
-__device__ __forceinline__ uint32_t load_rows(const Unit& u, float (&v)[kRows]) {
+__device__ __forceinline__ uint32_t load_rows(const Chunk& c, float (&v)[kRows]) {
     const uint32_t j0 = static_cast<uint32_t>(threadIdx.x / kWave) * (kRows * kWave) + lane();
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) v[i] = u.v[min(j0 + i * kWave, u.cnt - 1)];
+    for (int i = 0; i < kRows; ++i) v[i] = c.v[min(j0 + i * kWave, c.cnt - 1)];
     return j0;
 }
 
-// 5a. radix histograms (pass 0 only for fallback tensors: the compaction did it for the others)
-__global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
-                                                 const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
-                                                 const uint32_t* __restrict__ rcb,
-                                                 const Header* __restrict__ hdr, const float* __restrict__ dval,
-                                                 const float* __restrict__ e, uint32_t* __restrict__ rhist,
-                                                 int32_t hcopies) {
-    __shared__ uint32_t h[kRadixBins];
-    const int64_t Qc = pass > 0 ? hdr->total_cchunks : 0;
-    const int64_t Q = Qc + hdr->total_rchunks;
-    if (Q == 0) return;
-    const int nb = pass == 0 ? 2048 : 1024;
-    for (int i = threadIdx.x; i < kRadixBins; i += kBlock) h[i] = 0;
-    // h holds the counts of tensor `cur`; they go out when the block's next
-    // unit is another tensor's, and at the end (once for a tensor that
-    // spans many of the block's units)
-    auto flush = [&](int s) {
-        __syncthreads();
-        uint32_t* gh = radix_hist(rhist, pass, s, blockIdx.x % hcopies, nseg, hcopies);
-        for (int i = threadIdx.x; i < nb; i += kBlock) {
-            if (h[i]) atomicAdd(&gh[i], h[i]);
-            h[i] = 0;
+// The digits fixed before pass `pass` (1, 2 or 3 = the count) of tensor s, as
+// each select block finds them from the previous pass's histogram:
+// pass 1: p0, w0 from the first histogram; pass 2: p1, w1 from the second and
+// (p0, w0); pass 3: T, r from the third and (p1, w1).  The tensor's first
+// block records them for the later kernels.
+__device__ __forceinline__ void digits_before(int pass, int s, int lb, const SegPlan* plan, int32_t nseg,
+                                              SegState* st, const uint32_t* rhist, int32_t hcopies,
+                                              uint32_t* prefix, uint32_t* want) {
+    uint32_t d, above;
+    const uint32_t* gh = radix_hist(const_cast<uint32_t*>(rhist), pass - 1, s, 0, nseg, hcopies);
+    if (pass == 1) {
+        const uint32_t k = static_cast<uint32_t>(plan[s].k);
+        wave_find_digit(gh, hcopies, 2048, k, &d, &above);
+        *prefix = d;
+        *want = k - above;
+        if (lb == 0 && threadIdx.x == 0) {
+            st[s].p0 = *prefix;
+            st[s].w0 = *want;
         }
-        __syncthreads();
-    };
-    __syncthreads();
-    int cur = -1;
-    for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
-        const Unit u = unit_of(q, Qc, plan, nseg, st, ccb, rcb, dval, nullptr, e);
-        if (u.s != cur) {
-            if (cur >= 0) flush(cur);
-            cur = u.s;
+    } else if (pass == 2) {
+        const uint32_t p0 = st[s].p0, w0 = st[s].w0;
+        wave_find_digit(gh, hcopies, 1024, w0, &d, &above);
+        *prefix = (p0 << 10) | d;
+        *want = w0 - above;
+        if (lb == 0 && threadIdx.x == 0) {
+            st[s].p1 = *prefix;
+            st[s].w1 = *want;
         }
-        const uint32_t prefix = st[u.s].prefix;
-        float v[kRows];
-        const uint32_t j0 = load_rows(u, v);
-#pragma unroll
-        for (int i = 0; i < kRows; ++i) {
-            uint32_t d;
-            if (j0 + i * kWave < u.cnt && radix_digit(pass, key_of(v[i]), prefix, &d)) atomicAdd(&h[d], 1u);
+    } else {
+        const uint32_t p1 = st[s].p1, w1 = st[s].w1;
+        wave_find_digit(gh, hcopies, 1024, w1, &d, &above);
+        *prefix = (p1 << 10) | d;  // T
+        *want = w1 - above;        // r
+        if (lb == 0 && threadIdx.x == 0) {
+            st[s].T = *prefix;
+            st[s].r = *want;
         }
     }
-    if (cur >= 0) flush(cur);
 }
 
-// 5b. fix one digit per tensor
-__global__ __launch_bounds__(kBlock) void k_digit(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
-                                                  SegState* __restrict__ st, const uint32_t* __restrict__ rhist,
-                                                  int32_t hcopies) {
-    __shared__ uint32_t lds[kWavesPerBlock + 1];
-    __shared__ uint4 hsum[kRadixBins / 4];
-    const int s = blockIdx.x;
-    if (plan[s].mode != MODE_NORMAL) return;
-    const int nb = pass == 0 ? 2048 : 1024;
-    // the tensor's histogram of this pass is the sum of its copies
-    const uint4* gh = reinterpret_cast<const uint4*>(radix_hist(const_cast<uint32_t*>(rhist), pass, s, 0, nseg, hcopies));
-    if (hcopies > 1) {
-        if (pass == 0)
-            sum_copies<2048 / 4 / kBlock>(gh, kRadixBins / 4, hsum);
-        else
-            sum_copies<1024 / 4 / kBlock>(gh, kRadixBins / 4, hsum);
-    } else {
-        for (int i = threadIdx.x; i < nb / 4; i += kBlock) hsum[i] = gh[i];
-    }
+// 5. radix histograms of passes 1 and 2 (pass 0 came with the compaction)
+__global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
+                                                 const int32_t* __restrict__ hb, SegState* __restrict__ st,
+                                                 const float* __restrict__ dval, const float* __restrict__ e,
+                                                 uint32_t* __restrict__ rhist, int32_t hcopies) {
+    __shared__ uint32_t h[1024];
+    const SelBlock sb = sel_block(plan, nseg, hb, st);
+    if (sb.lb > 0 && static_cast<uint32_t>(sb.lb) >= sb.units) return;
+    uint32_t prefix, want;
+    digits_before(pass, sb.s, sb.lb, plan, nseg, st, rhist, hcopies, &prefix, &want);
+    if (static_cast<uint32_t>(sb.lb) >= sb.units) return;
+    for (int i = threadIdx.x; i < 1024; i += kBlock) h[i] = 0;
     __syncthreads();
-    const uint32_t* hs = reinterpret_cast<const uint32_t*>(hsum);
-    const uint32_t want = st[s].want;
-    const uint32_t prefix = st[s].prefix;
-    int d;
-    uint32_t above;
-    const bool f = pass == 0 ? find_rank_bin<2048 / kBlock>(hs, want, &d, &above, lds)
-                             : find_rank_bin<1024 / kBlock>(hs, want, &d, &above, lds);
-    if (f) {
-        const uint32_t np = pass == 0 ? static_cast<uint32_t>(d) : ((prefix << 10) | static_cast<uint32_t>(d));
-        st[s].prefix = np;
-        st[s].want = want - above;
-        if (pass == 2) {
-            st[s].T = np;
-            st[s].r = want - above;
+    const SegPlan& P = plan[sb.s];
+    const SegState& S = st[sb.s];
+    const int nsub = sb.raw ? kRawSub : 1;
+    for (uint32_t u = sb.lb; u < sb.units; u += sb.nb) {
+        for (int j = 0; j < nsub; ++j) {
+            const Chunk c = chunk_of(P, S, sb.raw, u, j, dval, nullptr, e);
+            if (c.cnt == 0) break;
+            float v[kRows];
+            const uint32_t j0 = load_rows(c, v);
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) {
+                uint32_t d;
+                if (j0 + i * kWave < c.cnt && radix_digit(pass, key_of(v[i]), prefix, &d)) atomicAdd(&h[d], 1u);
+            }
         }
     }
+    flush_hist(h, 1024, radix_hist(rhist, pass, sb.s, blockIdx.x % hcopies, nseg, hcopies));
 }
 
 // 6a. per-unit counts of keys above T and equal to T
 __global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                  const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
-                                                  const uint32_t* __restrict__ rcb,
-                                                  const Header* __restrict__ hdr, const float* __restrict__ dval,
-                                                  const float* __restrict__ e, uint32_t* __restrict__ cgt,
-                                                  uint32_t* __restrict__ ceq, uint32_t* __restrict__ rgt,
-                                                  uint32_t* __restrict__ req) {
-    __shared__ uint32_t sa[kWavesPerBlock], sb[kWavesPerBlock];
-    const int64_t Qc = hdr->total_cchunks;
-    const int64_t Q = Qc + hdr->total_rchunks;
-    for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
-        const Unit u = unit_of(q, Qc, plan, nseg, st, ccb, rcb, dval, nullptr, e);
-        const uint32_t T = st[u.s].T;
-        float v[kRows];
-        const uint32_t j0 = load_rows(u, v);
+                                                  const int32_t* __restrict__ hb, SegState* __restrict__ st,
+                                                  const uint32_t* __restrict__ rhist, int32_t hcopies,
+                                                  const float* __restrict__ dval, const float* __restrict__ e,
+                                                  uint32_t* __restrict__ cgt, uint32_t* __restrict__ ceq,
+                                                  uint32_t* __restrict__ rgt, uint32_t* __restrict__ req) {
+    __shared__ uint32_t sa[kWavesPerBlock], sbq[kWavesPerBlock];
+    const SelBlock sb = sel_block(plan, nseg, hb, st);
+    if (sb.lb > 0 && static_cast<uint32_t>(sb.lb) >= sb.units) return;
+    uint32_t T, r;
+    digits_before(3, sb.s, sb.lb, plan, nseg, st, rhist, hcopies, &T, &r);
+    const SegPlan& P = plan[sb.s];
+    const SegState& S = st[sb.s];
+    const int nsub = sb.raw ? kRawSub : 1;
+    uint32_t* gt = sb.raw ? rgt + P.runit_base : cgt + P.cunit_base;
+    uint32_t* eq = sb.raw ? req + P.runit_base : ceq + P.cunit_base;
+    for (uint32_t u = sb.lb; u < sb.units; u += sb.nb) {
         uint32_t a = 0, b = 0;
+        for (int j = 0; j < nsub; ++j) {
+            const Chunk c = chunk_of(P, S, sb.raw, u, j, dval, nullptr, e);
+            if (c.cnt == 0) break;
+            float v[kRows];
+            const uint32_t j0 = load_rows(c, v);
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) {
-            const bool ok = j0 + i * kWave < u.cnt;
-            const uint32_t key = key_of(v[i]);
-            a += ok && key > T;
-            b += ok && key == T;
+            for (int i = 0; i < kRows; ++i) {
+                const bool ok = j0 + i * kWave < c.cnt;
+                const uint32_t key = key_of(v[i]);
+                a += ok && key > T;
+                b += ok && key == T;
+            }
         }
         a = wave_sum(a);
         b = wave_sum(b);
         if (lane() == 0) {
             sa[threadIdx.x / kWave] = a;
-            sb[threadIdx.x / kWave] = b;
+            sbq[threadIdx.x / kWave] = b;
         }
         __syncthreads();
         if (threadIdx.x == 0) {
             uint32_t ta = 0, tb = 0;
             for (int i = 0; i < kWavesPerBlock; ++i) {
                 ta += sa[i];
-                tb += sb[i];
+                tb += sbq[i];
             }
-            (u.raw ? rgt : cgt)[u.slot] = ta;
-            (u.raw ? req : ceq)[u.slot] = tb;
+            gt[u] = ta;
+            eq[u] = tb;
         }
         __syncthreads();
     }
@@ -1246,28 +1337,27 @@ __global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ pl
 
 // 6b. exclusive scan of the unit counts of each tensor (packed gt:eq in 64
 //     bits): one block per tensor, each thread taking kEmitItems consecutive
-//     units of every tile, so that a fallback tensor's hundreds of thousands
-//     of raw units take a few dozen block scans
+//     units of every tile
 constexpr int kEmitScanBlock = 1024;
 constexpr int kEmitItems = 8;
 __global__ __launch_bounds__(kEmitScanBlock) void k_emit_scan(const SegPlan* __restrict__ plan,
                                                               const SegState* __restrict__ st,
-                                                              const uint32_t* __restrict__ rcb,
                                                               uint32_t* __restrict__ cgt, uint32_t* __restrict__ ceq,
                                                               uint32_t* __restrict__ rgt, uint32_t* __restrict__ req) {
     __shared__ uint64_t lds[kEmitScanBlock / kWave + 1];
     const int s = blockIdx.x;
-    if (plan[s].mode != MODE_NORMAL) return;
+    const SegPlan& P = plan[s];
+    if (P.mode != MODE_NORMAL) return;
     uint32_t *a, *b;
     int64_t n;
     if (st[s].fallback) {
-        a = rgt + rcb[s];
-        b = req + rcb[s];
-        n = plan[s].raw_chunks;
+        a = rgt + P.runit_base;
+        b = req + P.runit_base;
+        n = P.raw_units;
     } else {
-        a = cgt + st[s].cchunk_begin;
-        b = ceq + st[s].cchunk_begin;
-        n = st[s].cchunks;
+        a = cgt + P.cunit_base;
+        b = ceq + P.cunit_base;
+        n = (st[s].ncand + kChunk - 1) / kChunk;
     }
     uint64_t carry = 0;
     for (int64_t t0 = 0; t0 < n; t0 += static_cast<int64_t>(kEmitScanBlock) * kEmitItems) {
@@ -1297,100 +1387,113 @@ __global__ __launch_bounds__(kEmitScanBlock) void k_emit_scan(const SegPlan* __r
     }
 }
 
-// 6c. the kept entries at their index-ordered places, the unit read in rows as
-//     load_rows lays them out, so loads and (mostly kept-together) stores
-//     coalesce.  An entry's
-//     place is (entries with key > T before it) + min(r, entries with key == T
-//     before it): the unit's counts before it (from k_emit_scan), those of the
-//     block's earlier waves, of the wave's earlier rows, and of the row's lower
-//     lanes (ballots).  Kept entries get e = +0 unless the stream cleared them
-//     (key >= thi); dropped ones the stream cleared get x back.
+// 6c. the kept entries at their index-ordered places, each chunk read in rows
+//     as load_rows lays them out, so loads and (mostly kept-together) stores
+//     coalesce.  An entry's place is (entries with key > T before it) +
+//     min(r, entries with key == T before it): the unit's counts before it
+//     (from k_emit_scan), those of the unit's earlier chunks, of the block's
+//     earlier waves, of the wave's earlier rows, and of the row's lower lanes
+//     (ballots).  Kept entries get e = +0 unless the stream cleared them (key
+//     >= thi); dropped ones the stream cleared get x back.
 template <bool STATS>
 __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                  const SegState* __restrict__ st, const uint32_t* __restrict__ ccb,
-                                                  const uint32_t* __restrict__ rcb,
-                                                  const Header* __restrict__ hdr, const float* __restrict__ dval,
-                                                  const int32_t* __restrict__ didx, const uint32_t* __restrict__ cgt,
-                                                  const uint32_t* __restrict__ ceq, const uint32_t* __restrict__ rgt,
-                                                  const uint32_t* __restrict__ req, float* __restrict__ e,
-                                                  float* __restrict__ vals, int32_t* __restrict__ idx,
-                                                  double2* __restrict__ cpart, double2* __restrict__ rpart,
-                                                  uint32_t* __restrict__ stray) {
+                                                  const int32_t* __restrict__ hb, const SegState* __restrict__ st,
+                                                  const float* __restrict__ dval, const int32_t* __restrict__ didx,
+                                                  const uint32_t* __restrict__ cgt, const uint32_t* __restrict__ ceq,
+                                                  const uint32_t* __restrict__ rgt, const uint32_t* __restrict__ req,
+                                                  float* __restrict__ e, float* __restrict__ vals,
+                                                  int32_t* __restrict__ idx, double2* __restrict__ cpart,
+                                                  double2* __restrict__ rpart, uint32_t* __restrict__ stray) {
     __shared__ uint32_t wgt[kWavesPerBlock], weq[kWavesPerBlock];
     __shared__ double2 lsum[kWavesPerBlock];
-    const int64_t Qc = hdr->total_cchunks;
-    const int64_t Q = Qc + hdr->total_rchunks;
+    const SelBlock sb = sel_block(plan, nseg, hb, st);
+    if (static_cast<uint32_t>(sb.lb) >= sb.units) return;
     const int wv = threadIdx.x / kWave;
     const int l = lane();
-    for (int64_t q = blockIdx.x; q < Q; q += gridDim.x) {
-        const Unit u = unit_of(q, Qc, plan, nseg, st, ccb, rcb, dval, didx, e);
-        const uint32_t T = st[u.s].T, r = st[u.s].r;
-        const uint32_t thi = u.raw ? kNoKey : st[u.s].thi;
-        const int64_t out_off = plan[u.s].out_off, kseg = plan[u.s].k;
-        const int64_t seg_lo = plan[u.s].off, seg_hi = plan[u.s].off + plan[u.s].n;
-        uint32_t gtb = (u.raw ? rgt : cgt)[u.slot], eqb = (u.raw ? req : ceq)[u.slot];  // counts before the unit
-        float v[kRows];
-        const uint32_t j0 = load_rows(u, v);
-        int32_t ids[kRows];  // the entries' indices (candidate units), loaded with the values
-        if (!u.raw) {
-#pragma unroll
-            for (int i = 0; i < kRows; ++i) ids[i] = u.id[min(j0 + i * kWave, u.cnt - 1)];
-        }
-        // per row: the entries above T, equal to T, and with a key >= thi (a
-        // dropped one of those gets x back); wave-uniform, kept for the placing
-        // loop, which skips rows where all three are empty
-        uint64_t bgs[kRows], bes[kRows], bhs[kRows];
-        uint32_t ngt = 0, neq = 0;  // this wave's counts (wave-uniform)
-#pragma unroll
-        for (int i = 0; i < kRows; ++i) {
-            const bool ok = j0 + i * kWave < u.cnt;
-            const uint32_t key = key_of(v[i]);
-            bgs[i] = __ballot(ok && key > T);
-            bes[i] = __ballot(ok && key == T);
-            bhs[i] = __ballot(ok && key >= thi);
-            ngt += popc64(bgs[i]);
-            neq += popc64(bes[i]);
-        }
-        if (l == 0) {
-            wgt[wv] = ngt;
-            weq[wv] = neq;
-        }
-        __syncthreads();
-        for (int i = 0; i < wv; ++i) {
-            gtb += wgt[i];
-            eqb += weq[i];
-        }
+    const SegPlan& P = plan[sb.s];
+    const SegState& S = st[sb.s];
+    const uint32_t T = S.T, r = S.r;
+    const uint32_t thi = sb.raw ? kNoKey : S.thi;
+    const int64_t out_off = P.out_off, kseg = P.k;
+    const int64_t seg_lo = P.off, seg_hi = P.off + P.n;
+    const int nsub = sb.raw ? kRawSub : 1;
+    const uint32_t* gtp = sb.raw ? rgt + P.runit_base : cgt + P.cunit_base;
+    const uint32_t* eqp = sb.raw ? req + P.runit_base : ceq + P.cunit_base;
+    double2* part = sb.raw ? (rpart ? rpart + P.runit_base : nullptr) : (cpart ? cpart + P.cunit_base : nullptr);
+    for (uint32_t u = sb.lb; u < sb.units; u += sb.nb) {
+        uint32_t gtu = gtp[u], equ = eqp[u];  // counts before the unit's next chunk
         double sent = 0.0, drop = 0.0;
+        for (int j = 0; j < nsub; ++j) {
+            const Chunk c = chunk_of(P, S, sb.raw, u, j, dval, didx, e);
+            if (c.cnt == 0) break;
+            float v[kRows];
+            const uint32_t j0 = load_rows(c, v);
+            int32_t ids[kRows];  // the entries' indices (candidate units), loaded with the values
+            if (!sb.raw) {
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) {
-            const uint32_t j = j0 + i * kWave;
-            const bool ok = j < u.cnt;
-            const uint32_t key = key_of(v[i]);
-            const uint64_t bg = bgs[i], be = bes[i];
-            if (!STATS && (bg | be | bhs[i]) == 0) continue;  // nothing to place or restore in this row
-            const bool gt = ok && key > T, eq = ok && key == T;
-            const uint32_t g_before = gtb + count_below(bg), e_before = eqb + count_below(be);
-            gtb += popc64(bg);
-            eqb += popc64(be);
-            if (!ok) continue;
-            int64_t pos = -1;
-            if (gt) pos = static_cast<int64_t>(g_before) + min(r, e_before);
-            else if (eq && e_before < r) pos = static_cast<int64_t>(g_before) + e_before;
-            if (STATS) {
-                if (pos >= 0) sent += sq_finite(v[i], key);
-                else drop += sq_finite(v[i], key);
+                for (int i = 0; i < kRows; ++i) ids[i] = c.id[min(j0 + i * kWave, c.cnt - 1)];
             }
-            const int64_t id = u.raw ? u.idx_base + j : static_cast<int64_t>(ids[i]);
-            if (id < seg_lo || id >= seg_hi) {  // only if the workspace was overwritten meanwhile
-                atomicAdd(stray, 1u);
-                continue;
+            // per row: the entries above T, equal to T, and with a key >= thi (a
+            // dropped one of those gets x back); wave-uniform, kept for the
+            // placing loop, which skips rows where all three are empty
+            uint64_t bgs[kRows], bes[kRows], bhs[kRows];
+            uint32_t ngt = 0, neq = 0;  // this wave's counts (wave-uniform)
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) {
+                const bool ok = j0 + i * kWave < c.cnt;
+                const uint32_t key = key_of(v[i]);
+                bgs[i] = __ballot(ok && key > T);
+                bes[i] = __ballot(ok && key == T);
+                bhs[i] = __ballot(ok && key >= thi);
+                ngt += popc64(bgs[i]);
+                neq += popc64(bes[i]);
             }
-            if (pos >= 0 && pos < kseg) {
-                vals[out_off + pos] = v[i];
-                idx[out_off + pos] = static_cast<int32_t>(id);
-                if (key < thi) e[id] = 0.0f;
-            } else if (pos < 0 && key >= thi) {
-                e[id] = v[i];
+            if (l == 0) {
+                wgt[wv] = ngt;
+                weq[wv] = neq;
+            }
+            __syncthreads();
+            uint32_t gtb = gtu, eqb = equ;
+            for (int i = 0; i < kWavesPerBlock; ++i) {
+                if (i < wv) {
+                    gtb += wgt[i];
+                    eqb += weq[i];
+                }
+                gtu += wgt[i];
+                equ += weq[i];
+            }
+            __syncthreads();  // wgt / weq are rewritten by the next chunk
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) {
+                const uint32_t jj = j0 + i * kWave;
+                const bool ok = jj < c.cnt;
+                const uint32_t key = key_of(v[i]);
+                const uint64_t bg = bgs[i], be = bes[i];
+                if (!STATS && (bg | be | bhs[i]) == 0) continue;  // nothing to place or restore in this row
+                const bool gt = ok && key > T, eq = ok && key == T;
+                const uint32_t g_before = gtb + count_below(bg), e_before = eqb + count_below(be);
+                gtb += popc64(bg);
+                eqb += popc64(be);
+                if (!ok) continue;
+                int64_t pos = -1;
+                if (gt) pos = static_cast<int64_t>(g_before) + min(r, e_before);
+                else if (eq && e_before < r) pos = static_cast<int64_t>(g_before) + e_before;
+                if (STATS) {
+                    if (pos >= 0) sent += sq_finite(v[i], key);
+                    else drop += sq_finite(v[i], key);
+                }
+                const int64_t id = sb.raw ? c.idx_base + jj : static_cast<int64_t>(ids[i]);
+                if (id < seg_lo || id >= seg_hi) {  // only if the workspace was overwritten meanwhile
+                    atomicAdd(stray, 1u);
+                    continue;
+                }
+                if (pos >= 0 && pos < kseg) {
+                    vals[out_off + pos] = v[i];
+                    idx[out_off + pos] = static_cast<int32_t>(id);
+                    if (key < thi) e[id] = 0.0f;
+                } else if (pos < 0 && key >= thi) {
+                    e[id] = v[i];
+                }
             }
         }
         if (STATS) {
@@ -1405,10 +1508,10 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
                     t.x += lsum[i].x;
                     t.y += lsum[i].y;
                 }
-                (u.raw ? rpart : cpart)[u.slot] = t;
+                part[u] = t;
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
@@ -1446,7 +1549,7 @@ __global__ __launch_bounds__(kGroup) void k_stats_groups(const SegPlan* __restri
 
 // 7b. per tensor
 __global__ __launch_bounds__(kBlock) void k_stats(const SegPlan* __restrict__ plan, const SegState* __restrict__ st,
-                                                  const int32_t* __restrict__ gbb, const uint32_t* __restrict__ rcb,
+                                                  const int32_t* __restrict__ gbb,
                                                   const double2* __restrict__ gpart, const double2* __restrict__ cpart,
                                                   const double2* __restrict__ rpart, double* __restrict__ stats) {
     __shared__ double2 lsum[kWavesPerBlock];
@@ -1463,8 +1566,8 @@ __global__ __launch_bounds__(kBlock) void k_stats(const SegPlan* __restrict__ pl
         }
     }
     if (mode == MODE_NORMAL) {
-        const double2* p = fb ? rpart + rcb[s] : cpart + st[s].cchunk_begin;
-        const int64_t nu = fb ? plan[s].raw_chunks : st[s].cchunks;
+        const double2* p = fb ? rpart + plan[s].runit_base : cpart + plan[s].cunit_base;
+        const int64_t nu = fb ? plan[s].raw_units : (st[s].ncand + kChunk - 1) / kChunk;
         for (int64_t q = threadIdx.x; q < nu; q += kBlock) {
             a.x += p[q].x;
             a.y += p[q].y;
@@ -1492,6 +1595,7 @@ static void fill_words(const Plan& P, const Layout& L, uint32_t* words) {
     memcpy(h + L.gbb, P.gbb.data(), P.gbb.size() * 4);
     memcpy(h + L.sbb, P.sbb.data(), P.sbb.size() * 4);
     memcpy(h + L.cbb, P.cbb.data(), P.cbb.size() * 4);
+    memcpy(h + L.hb, P.hb.data(), P.hb.size() * 4);
 }
 
 static int check_ws(const Layout& L, const void* ws, size_t ws_bytes) {
@@ -1563,14 +1667,13 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
     const int32_t* rb = reinterpret_cast<const int32_t*>(at(L.rb));
     const int32_t* gbb = reinterpret_cast<const int32_t*>(at(L.gbb));
     const int32_t* sbb = reinterpret_cast<const int32_t*>(at(L.sbb));
-    uint32_t* rcb = reinterpret_cast<uint32_t*>(at(L.rcb));
+    const int32_t* hb = reinterpret_cast<const int32_t*>(at(L.hb));
     Header* hdr = reinterpret_cast<Header*>(at(L.header));
     uint32_t* stray = reinterpret_cast<uint32_t*>(at(L.status));
     SegState* st = reinterpret_cast<SegState*>(at(L.state));
     uint32_t* shist = reinterpret_cast<uint32_t*>(at(L.shist));
     uint32_t* rhist = reinterpret_cast<uint32_t*>(at(L.rhist));
     uint32_t* grp_cnt = reinterpret_cast<uint32_t*>(at(L.grp_cnt));
-    uint32_t* ccb = reinterpret_cast<uint32_t*>(at(L.ccb));
     uint32_t* grp_off = reinterpret_cast<uint32_t*>(at(L.grp_off));
     uint32_t* region_cnt = reinterpret_cast<uint32_t*>(at(L.region_cnt));
     uint32_t* ovf = reinterpret_cast<uint32_t*>(at(L.ovf));
@@ -1591,8 +1694,7 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
         EF_TRY(launch("topk_stats_groups", k_stats_groups, dim3(static_cast<unsigned>(P.G)), dim3(kGroup), s, plan,
                       nseg, gbb, rb, static_cast<const double2*>(spart), gpart));
         return launch("topk_stats", k_stats, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
-                      static_cast<const SegState*>(st), gbb, static_cast<const uint32_t*>(rcb),
-                      static_cast<const double2*>(gpart),
+                      static_cast<const SegState*>(st), gbb, static_cast<const double2*>(gpart),
                       static_cast<const double2*>(reinterpret_cast<double2*>(at(L.cpart))),
                       static_cast<const double2*>(reinterpret_cast<double2*>(at(L.rpart))), stats);
     };
@@ -1612,40 +1714,30 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
                       region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart, hdr, ovf));
     if (!P.any_normal) return finish_stats();
 
-    EF_TRY(launch("topk_scan_groups", k_scan_groups, dim3(1), dim3(kScanBlock), s, plan, nseg, gbb, P.G,
-                  static_cast<const uint32_t*>(grp_cnt), grp_off, st, ccb, rcb, hdr,
-                  static_cast<uint32_t>((flags & EF_FLAG_FORCE_FALLBACK) ? 1u : 0u)));
     EF_TRY(launch("topk_compact", k_compact, dim3(static_cast<unsigned>(P.CB)), dim3(kBlock), s, plan, nseg,
-                  static_cast<const int32_t*>(reinterpret_cast<int32_t*>(at(L.cbb))), gbb, rb,
-                  static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
-                  static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair), dval, didx, rhist,
-                  P.hcopies, e, stray));
+                  static_cast<const int32_t*>(reinterpret_cast<int32_t*>(at(L.cbb))), gbb, rb, st,
+                  static_cast<const uint32_t*>(grp_cnt), grp_off, static_cast<const uint32_t*>(region_cnt),
+                  static_cast<const uint2*>(cpair), dval, didx, rhist, P.hcopies, e, stray,
+                  static_cast<uint32_t>((flags & EF_FLAG_FORCE_FALLBACK) ? 1u : 0u)));
     EF_TRY(launch("topk_recollect", k_recollect, dim3(kRecollectBlocks), dim3(kBlock), s, plan, nseg, rb, gbb,
                   static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
                   static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair),
                   static_cast<const Header*>(hdr), static_cast<const uint32_t*>(ovf), e, dval, didx, rhist,
                   P.hcopies));
-    const unsigned gu = static_cast<unsigned>(std::min<int64_t>(kMaxGrid, std::max<int64_t>(1, P.QC + P.QR)));
-    for (int pass = 0; pass < 3; ++pass) {
-        EF_TRY(launch("topk_hist", k_hist, dim3(gu), dim3(kBlock), s, pass, plan, nseg,
-                      static_cast<const SegState*>(st), static_cast<const uint32_t*>(ccb), static_cast<const uint32_t*>(rcb),
-                      static_cast<const Header*>(hdr), static_cast<const float*>(dval),
-                      static_cast<const float*>(e), rhist, P.hcopies));
-        EF_TRY(launch("topk_digit", k_digit, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, pass, plan, nseg,
-                      st, static_cast<const uint32_t*>(rhist), P.hcopies));
-    }
-    EF_TRY(launch("topk_count", k_count, dim3(gu), dim3(kBlock), s, plan, nseg, static_cast<const SegState*>(st),
-                  static_cast<const uint32_t*>(ccb), static_cast<const uint32_t*>(rcb), static_cast<const Header*>(hdr),
-                  static_cast<const float*>(dval), static_cast<const float*>(e), cgt, ceq, rgt, req));
+    const dim3 hgrid(static_cast<unsigned>(P.HB));
+    for (int pass = 1; pass < 3; ++pass)
+        EF_TRY(launch("topk_hist", k_hist, hgrid, dim3(kBlock), s, pass, plan, nseg, hb, st,
+                      static_cast<const float*>(dval), static_cast<const float*>(e), rhist, P.hcopies));
+    EF_TRY(launch("topk_count", k_count, hgrid, dim3(kBlock), s, plan, nseg, hb, st,
+                  static_cast<const uint32_t*>(rhist), P.hcopies, static_cast<const float*>(dval),
+                  static_cast<const float*>(e), cgt, ceq, rgt, req));
     EF_TRY(launch("topk_emit_scan", k_emit_scan, dim3(static_cast<unsigned>(nseg)), dim3(kEmitScanBlock), s, plan,
-                  static_cast<const SegState*>(st), static_cast<const uint32_t*>(rcb), cgt, ceq, rgt, req));
-    EF_TRY(launch("topk_write", stats ? k_write<true> : k_write<false>, dim3(gu), dim3(kBlock), s, plan, nseg,
-                  static_cast<const SegState*>(st), static_cast<const uint32_t*>(ccb),
-                  static_cast<const uint32_t*>(rcb), static_cast<const Header*>(hdr),
-                  static_cast<const float*>(dval), static_cast<const int32_t*>(didx),
-                  static_cast<const uint32_t*>(cgt), static_cast<const uint32_t*>(ceq),
-                  static_cast<const uint32_t*>(rgt), static_cast<const uint32_t*>(req), e, vals, idx, cpart, rpart,
-                  stray));
+                  static_cast<const SegState*>(st), cgt, ceq, rgt, req));
+    EF_TRY(launch("topk_write", stats ? k_write<true> : k_write<false>, hgrid, dim3(kBlock), s, plan, nseg, hb,
+                  static_cast<const SegState*>(st), static_cast<const float*>(dval),
+                  static_cast<const int32_t*>(didx), static_cast<const uint32_t*>(cgt),
+                  static_cast<const uint32_t*>(ceq), static_cast<const uint32_t*>(rgt),
+                  static_cast<const uint32_t*>(req), e, vals, idx, cpart, rpart, stray));
     return finish_stats();
 }
 
