@@ -38,6 +38,7 @@ SIGNATURES = {
     "ef_adam_scalars": (C.c_int, [C.c_double, _f, _f, _i64, _i64, C.POINTER(_f), C.POINTER(_f)]),
     "ef_adam_step": (C.c_int, [_p, _p, _p, _p, _i64, _f, _f, _f, _f, _f, _p, _p]),
     "ef_onebit_adam_update": (C.c_int, [_p, _i32, _p, _p, _p, _i64, _f, _f, _f, _f, _p, _p]),
+    "ef_onebit_adam_update_var": (C.c_int, [_p, _i32, _p, _p, _p, _i64, _f, _f, _f, _f, _f, _p, _p]),
     "ef_quantize_workspace_bytes": (_sz, [_i64]),
     "ef_quantize_int8": (C.c_int, [_p, _p, _i64, _p, _i64, _p, _p, _p, _sz, _p]),
     "ef_random_sparsify_workspace_bytes": (_sz, [_i64]),
@@ -306,6 +307,21 @@ def ef_onebit_adam_update(qsum, nworkers, m, v, w, beta1, step_size, sqrt_bc2, e
         _need(nonfinite, torch.int32, dev, "nonfinite", 1)
     _check(lib().ef_onebit_adam_update(_ptr(qsum), nworkers, _ptr(m), _ptr(v), _ptr(w), n, beta1, step_size,
                                        sqrt_bc2, eps, _ptr(nonfinite), _stream(dev)), "ef_onebit_adam_update")
+
+
+def ef_onebit_adam_update_var(qsum, nworkers, m, v, w, beta1, beta2, step_size, sqrt_bc2, eps, nonfinite=None):
+    """One 1-bit Adam compression-phase update with the variance still updated
+    from ghat = qsum / nworkers; in place on m, v, w."""
+    dev = _gpu(m, "m")
+    n = m.numel()
+    _need(qsum, torch.int8, dev, "qsum", n)
+    for t, name in ((m, "m"), (v, "v"), (w, "w")):
+        _need(t, torch.float32, dev, name, n)
+    if nonfinite is not None:
+        _need(nonfinite, torch.int32, dev, "nonfinite", 1)
+    _check(lib().ef_onebit_adam_update_var(_ptr(qsum), nworkers, _ptr(m), _ptr(v), _ptr(w), n, beta1, beta2,
+                                           step_size, sqrt_bc2, eps, _ptr(nonfinite), _stream(dev)),
+           "ef_onebit_adam_update_var")
 
 
 # ---------------------------------------------------------------- 8-bit packet values

@@ -16,6 +16,8 @@
 // were summed into qsum): ghat = qsum / nworkers;
 //   m' = beta1 m + (1 - beta1) ghat;  v frozen (read only);  w' as above
 //   reads qsum (1 B), m, v, w and writes m, w: 21 B per element.
+// ef_onebit_adam_update_var: the same with v' = beta2 v + (1 - beta2) ghat^2
+//   (every replica holds the same ghat, so this v stays shared too): 25 B.
 // One streaming pass each, one wave per region, 128-bit non-temporal loads
 // and stores.  Square root and divisions are correctly rounded; every other
 // product and sum is rounded on its own (-ffp-contract=off).
@@ -63,21 +65,22 @@ struct Hyper {
     float beta1, c1, beta2, c2, step_size, sqrt_bc2, eps, inv_unused;
 };
 
-// One element of either phase.  ONEBIT: gin is ghat and v is kept.
-template <bool ONEBIT>
+// One element.  VUPD: v takes gin^2 (warm-up, and the 1-bit step that keeps
+// updating the variance with ghat^2); otherwise v is kept.
+template <bool VUPD>
 __device__ __forceinline__ void element(float gin, float& m, float& v, float& w, const Hyper& h, uint32_t& nf) {
     const float ma = h.beta1 * m;
     const float mb = h.c1 * gin;
     const float mn = ma + mb;
     float vn = v;
-    if (!ONEBIT) {
+    if (VUPD) {
         const float g2 = gin * gin;
         const float va = h.beta2 * v;
         const float vb = h.c2 * g2;
         vn = va + vb;
     }
     const float wn = param(w, mn, vn, h.step_size, h.sqrt_bc2, h.eps);
-    nf += nonfinite(mn) + nonfinite(wn) + (ONEBIT ? 0u : nonfinite(vn));
+    nf += nonfinite(mn) + nonfinite(wn) + (VUPD ? nonfinite(vn) : 0u);
     m = mn;
     v = vn;
     w = wn;
@@ -89,7 +92,7 @@ __device__ __forceinline__ void element(float gin, float& m, float& v, float& w,
 // int8 sums of a float4 as one 32-bit word (qsum is 4-byte aligned).  Without
 // DIV the worker count is a power of two: qs * (1/N) is then exact and equals
 // the correctly rounded qs / N.
-template <bool ONEBIT, bool DIV>
+template <bool ONEBIT, bool DIV, bool VUPD>
 __global__ __launch_bounds__(kBlock) void k_adam(const float* __restrict__ g, const int8_t* __restrict__ qsum,
                                                  float nworkers, float* __restrict__ m, float* __restrict__ v,
                                                  float* __restrict__ w, int64_t n, Hyper h,
@@ -137,17 +140,17 @@ __global__ __launch_bounds__(kBlock) void k_adam(const float* __restrict__ g, co
                 float wa[4] = {wv4[u].x, wv4[u].y, wv4[u].z, wv4[u].w};
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    element<ONEBIT>(gin_of(ONEBIT ? f4{} : gv[u], ONEBIT ? qv[u] : 0u, t), ma[t], va[t], wa[t], h, nf);
+                    element<VUPD>(gin_of(ONEBIT ? f4{} : gv[u], ONEBIT ? qv[u] : 0u, t), ma[t], va[t], wa[t], h, nf);
                 __builtin_nontemporal_store(f4{ma[0], ma[1], ma[2], ma[3]}, m4 + j);
-                if (!ONEBIT) __builtin_nontemporal_store(f4{va[0], va[1], va[2], va[3]}, v4 + j);
+                if (VUPD) __builtin_nontemporal_store(f4{va[0], va[1], va[2], va[3]}, v4 + j);
                 __builtin_nontemporal_store(f4{wa[0], wa[1], wa[2], wa[3]}, w4 + j);
             } else if (GUARD && j == nfull && nfull < nv) {
                 for (int64_t i = beg + 4 * nfull; i < beg + len; ++i) {
                     const float gin = ONEBIT ? ghat(static_cast<float>(qsum[i])) : g[i];
                     float mi = m[i], vi = v[i], wi = w[i];
-                    element<ONEBIT>(gin, mi, vi, wi, h, nf);
+                    element<VUPD>(gin, mi, vi, wi, h, nf);
                     m[i] = mi;
-                    if (!ONEBIT) v[i] = vi;
+                    if (VUPD) v[i] = vi;
                     w[i] = wi;
                 }
             }
@@ -209,7 +212,7 @@ extern "C" int ef_adam_step(const float* g, float* m, float* v, float* w, int64_
     if (nonfinite) EF_TRY(launch("adam_zero", adam::k_zero_u32, dim3(1), dim3(1), s, nonfinite));
     if (n == 0) return EF_OK;
     const adam::Hyper h{beta1, 1.0f - beta1, beta2, 1.0f - beta2, step_size, sqrt_bc2, eps, 0.0f};
-    return launch("adam_step", adam::k_adam<false, false>, dim3(static_cast<unsigned>(adam::blocks_for(n))),
+    return launch("adam_step", adam::k_adam<false, false, true>, dim3(static_cast<unsigned>(adam::blocks_for(n))),
                   dim3(adam::kBlock), s, g, static_cast<const int8_t*>(nullptr), 1.0f, m, v, w, n, h, nonfinite);
 }
 
@@ -225,8 +228,26 @@ extern "C" int ef_onebit_adam_update(const int8_t* qsum, int32_t nworkers, float
     if (n == 0) return EF_OK;
     const adam::Hyper h{beta1, 1.0f - beta1, 1.0f, 0.0f, step_size, sqrt_bc2, eps, 0.0f};
     const bool pow2 = (nworkers & (nworkers - 1)) == 0;
-    return launch("onebit_update", pow2 ? adam::k_adam<true, false> : adam::k_adam<true, true>,
+    return launch("onebit_update", pow2 ? adam::k_adam<true, false, false> : adam::k_adam<true, true, false>,
                   dim3(static_cast<unsigned>(adam::blocks_for(n))), dim3(adam::kBlock), s,
                   static_cast<const float*>(nullptr), qsum, static_cast<float>(nworkers), m, const_cast<float*>(v), w,
                   n, h, nonfinite);
+}
+
+extern "C" int ef_onebit_adam_update_var(const int8_t* qsum, int32_t nworkers, float* m, float* v, float* w,
+                                         int64_t n, float beta1, float beta2, float step_size, float sqrt_bc2,
+                                         float eps, uint32_t* nonfinite, void* stream) {
+    EF_TRY(adam::check_common(m, v, w, n, beta1, step_size, sqrt_bc2, eps));
+    if (!(beta2 >= 0.0f && beta2 <= 1.0f)) return fail(EF_EINVAL, "beta2 must lie in [0, 1]");
+    if (nworkers < 1 || nworkers > 127) return fail(EF_EINVAL, "nworkers must lie in [1, 127]");
+    if (n > 0 && (!qsum || (reinterpret_cast<uintptr_t>(qsum) & 3u)))
+        return fail(EF_EINVAL, "qsum must be a 4-byte aligned pointer");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (nonfinite) EF_TRY(launch("onebit_zero", adam::k_zero_u32, dim3(1), dim3(1), s, nonfinite));
+    if (n == 0) return EF_OK;
+    const adam::Hyper h{beta1, 1.0f - beta1, beta2, 1.0f - beta2, step_size, sqrt_bc2, eps, 0.0f};
+    const bool pow2 = (nworkers & (nworkers - 1)) == 0;
+    return launch("onebit_update_var", pow2 ? adam::k_adam<true, false, true> : adam::k_adam<true, true, true>,
+                  dim3(static_cast<unsigned>(adam::blocks_for(n))), dim3(adam::kBlock), s,
+                  static_cast<const float*>(nullptr), qsum, static_cast<float>(nworkers), m, v, w, n, h, nonfinite);
 }

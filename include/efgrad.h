@@ -224,6 +224,16 @@ int ef_adam_step(const float* g, float* m, float* v, float* w, int64_t n, float 
 int ef_onebit_adam_update(const int8_t* qsum, int32_t nworkers, float* m, const float* v,
                           float* w, int64_t n, float beta1, float step_size, float sqrt_bc2,
                           float eps, uint32_t* nonfinite, void* stream);
+/* ef_onebit_adam_update_var: the compression-phase step with the variance
+ * still updated, from the averaged compressed gradient (the pages list v in
+ * the state but give no rule for it; this is textbook Adam fed ghat):
+ *   ghat = qsum / nworkers;  m = beta1*m + (1-beta1)*ghat;
+ *   v = beta2*v + (1-beta2)*(ghat*ghat);  w as above (t_v = t).
+ * Every replica holds the same ghat, so v stays identical on all of them.
+ * Same rounding, alignment and *nonfinite (m, v, w) rules as ef_adam_step. */
+int ef_onebit_adam_update_var(const int8_t* qsum, int32_t nworkers, float* m, float* v,
+                              float* w, int64_t n, float beta1, float beta2, float step_size,
+                              float sqrt_bc2, float eps, uint32_t* nonfinite, void* stream);
 
 /* ------------------------------------------------------------------------
  * 8-bit quantisation of a sent packet, the quantisation error kept in the

@@ -17,7 +17,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# EFG_ORACLE_LIB names another build of oracle.c (the sanitizer test's)
+_LIB = os.environ.get("EFG_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fno-builtin",
@@ -290,6 +291,14 @@ def adam_step(g, m, v, w, beta1, beta2, step_size, sqrt_bc2, eps):
     _check(lib().orc_adam_step(_ptr(g), _ptr(m2), _ptr(v2), _ptr(w2), g.size, beta1, beta2, step_size, sqrt_bc2,
                                eps, _ptr(bad)), "adam_step")
     return m2, v2, w2, int(bad[0])
+
+
+def onebit_adam_update_var(qsum, nworkers, m, v, w, beta1, beta2, step_size, sqrt_bc2, eps):
+    """The compression-phase step with the variance still updated: the Adam
+    step (adam_step) fed ghat = qsum / nworkers, a correctly rounded float32
+    division.  Returns (m_new, v_new, w_new, nonfinite)."""
+    ghat = np.ascontiguousarray(qsum, dtype=np.int8).astype(np.float32) / np.float32(nworkers)
+    return adam_step(ghat, m, v, w, beta1, beta2, step_size, sqrt_bc2, eps)
 
 
 def onebit_adam_update(qsum, nworkers, m, v, w, beta1, step_size, sqrt_bc2, eps):

@@ -247,6 +247,10 @@ def test_adam_argument_checks():
     assert upd(q=None) == efg.EF_EINVAL
     assert upd(q=FAKE + 2) == efg.EF_EINVAL
     assert upd(m=None) == efg.EF_EINVAL
+    var = lambda **kw: L.ef_onebit_adam_update_var(FAKE, kw.get("nw", 1), FAKE, FAKE, FAKE, 64, 0.9,
+                                                   kw.get("b2", 0.999), 1e-3, 0.1, 1e-8, None, None)
+    assert var(nw=0) == efg.EF_EINVAL
+    assert var(b2=1.5) == efg.EF_EINVAL
 
 
 def test_adam_scalars_match_the_oracle_helper():

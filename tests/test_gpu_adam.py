@@ -76,6 +76,28 @@ def test_onebit_update(n, nworkers):
     assert int(host(nf)[0]) == onf
 
 
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("nworkers", [1, 3, 64, 127])
+def test_onebit_update_var(n, nworkers):
+    """The 1-bit step with the variance updated from ghat, against the oracle."""
+    dev = device()
+    _, m, v, w = state(n, n % 983)
+    r = np.random.default_rng(n + 7 * nworkers)
+    qsum = np.zeros(n, np.int64)
+    for _ in range(nworkers):
+        qsum += r.integers(-1, 2, n)
+    qsum = qsum.astype(np.int8)
+    ss, sb = efg.adam_scalars(2e-5, B1, B2, 40)
+    md, vd, wd = to_dev(m, dev), to_dev(v, dev), to_dev(w, dev)
+    nf = torch.zeros(1, dtype=torch.int32, device=dev)
+    efg.ef_onebit_adam_update_var(to_dev(qsum, dev), nworkers, md, vd, wd, B1, B2, ss, sb, EPS, nonfinite=nf)
+    om, ov, ow, onf = oracle.onebit_adam_update_var(qsum, nworkers, m, v, w, B1, B2, ss, sb, EPS)
+    assert_bits_equal(host(md), om, f"m n={n} N={nworkers}")
+    assert_bits_equal(host(vd), ov, f"v n={n} N={nworkers}")
+    assert_bits_equal(host(wd), ow, f"w n={n} N={nworkers}")
+    assert int(host(nf)[0]) == onf
+
+
 @pytest.mark.parametrize("n", [1, 7, 8, 9, 8191, 8192, 8193, 100_003])
 def test_compress_only_sign(n):
     dev = device()

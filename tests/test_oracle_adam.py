@@ -142,3 +142,35 @@ def test_scalars():
     assert ss == float(np.float32(2e-5 / (1 - b1))) and sb == float(np.float32(math.sqrt(1 - b2)))
     ss, sb = oracle.adam_scalars(2e-5, 0.9, 0.999, 100, 10)
     assert sb == float(np.float32(math.sqrt(1 - b2 ** 10)))
+
+
+@pytest.mark.parametrize("nworkers", [1, 3, 8])
+def test_onebit_update_var_is_torch_adam_fed_the_averaged_signs(nworkers):
+    """The 1-bit step that keeps updating the variance is textbook Adam (here
+    torch.optim.Adam) fed ghat = qsum / nworkers, ghat formed by torch."""
+    n, T = 20_000, 10
+    r = np.random.default_rng(40 + nworkers)
+    w0 = r.standard_normal(n).astype(np.float32)
+    qs = []
+    for _ in range(T):
+        q = np.zeros(n, np.int64)
+        for _ in range(nworkers):
+            q += r.integers(-1, 2, n)
+        qs.append(q.astype(np.int8))
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    w = w0.copy()
+    for t, q in enumerate(qs, start=1):
+        ss, sb = oracle.adam_scalars(1e-3, B1, B2, t)
+        m, v, w, _ = oracle.onebit_adam_update_var(q, nworkers, m, v, w, B1, B2, ss, sb, EPS)
+    p = torch.nn.Parameter(torch.from_numpy(w0.copy()))
+    b1, b2 = float(np.float32(B1)), float(np.float32(B2))
+    opt = torch.optim.Adam([p], lr=1e-3, betas=(b1, b2), eps=EPS, foreach=False)
+    for q in qs:
+        p.grad = torch.from_numpy(q).to(torch.float32) / nworkers
+        opt.step()
+    st = opt.state[p]
+    assert np.all(np.abs(m - st["exp_avg"].numpy()) <= 1e-6 + 2e-6 * np.abs(m))
+    assert np.all(np.abs(v - st["exp_avg_sq"].numpy()) <= 1e-6 * (1 - B2) + 2e-6 * np.abs(v))
+    wt = p.detach().numpy()
+    assert np.all(np.abs(w - wt) <= T * np.spacing(np.abs(wt)) + 1e-4 * np.abs(wt - w0))

@@ -214,3 +214,25 @@ def test_bert_layerwise_k_total():
     ratios = json.loads(pathlib.Path(os.path.join(GOLD, "ratios.json")).read_text())["layerwise_ratios"]
     sizes = np.diff(off)
     assert np.all(ks[sizes > 1_000_000] == sizes[sizes > 1_000_000] * ratios["large_layer"] // 1)
+
+
+def test_oracle_chain_split_and_resumed(tmp_path):
+    """The residual is the whole state of the top-k chain: the oracle's chain
+    split at step 5, e written with np.save and read back, gives the same
+    packets and final e as the unsplit chain."""
+    n, k, T, split = 20_000, 200, 10, 5
+    grads = [gen.normal_small(n, 160, t) for t in range(T)]
+    e_full = np.zeros(n, np.float32)
+    full = []
+    for g in grads:
+        v, i, e_full, _ = oracle.topk(g, e_full, k)
+        full.append((v, i))
+    e = np.zeros(n, np.float32)
+    for g in grads[:split]:
+        _, _, e, _ = oracle.topk(g, e, k)
+    np.save(tmp_path / "e.npy", e)
+    e = np.load(tmp_path / "e.npy")
+    for t in range(split, T):
+        v, i, e, _ = oracle.topk(grads[t], e, k)
+        assert np.array_equal(i, full[t][1]) and np.array_equal(v.view(np.uint32), full[t][0].view(np.uint32))
+    assert np.array_equal(e.view(np.uint32), e_full.view(np.uint32))
