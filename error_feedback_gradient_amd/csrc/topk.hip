@@ -70,6 +70,7 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 #endif
 constexpr int kStreamBlock = EFG_STREAM_BLOCK;     // threads of the streaming kernel
 constexpr int kStreamWaves = kStreamBlock / kWave;
+constexpr int64_t kFewRegions = 4096;             // below: one-wave stream blocks, one copy of each histogram
 constexpr int kRegion = EFG_STREAM_REGION;         // elements per wave in the streaming pass
 constexpr int kUnroll = EFG_STREAM_UNROLL;         // 128-bit loads in flight per lane and array
 constexpr int kGroup = 256;                        // regions per group (candidate totals, compaction)
@@ -371,9 +372,10 @@ static int make_plan(int32_t nseg, const int64_t* off, const int64_t* ks, Plan& 
     // their atomics on one histogram meet beyond the L2s and are applied in
     // turn.  With few tensors (few histograms, many blocks each) every sample
     // and radix histogram gets eight copies, one per XCD (blocks are handed to
-    // the XCDs in turn, so block b adds to copy b % 8); with many tensors the
-    // blocks per tensor are few anyway.
-    p.hcopies = nseg <= 8 ? kHistCopies : 1;
+    // the XCDs in turn, so block b adds to copy b % 8); with many tensors, or
+    // a small call, the blocks per histogram are few anyway, and one copy
+    // spares the clearing and the reading of the others.
+    p.hcopies = (nseg <= 8 && p.R >= kFewRegions) ? kHistCopies : 1;
     p.sample_rounds = static_cast<int32_t>(std::min<int64_t>(
         kSampleRoundsMax, std::max<int64_t>(1, cdiv(p.SB, static_cast<int64_t>(kSampleBlockChunks) * kSampleBlocksTarget))));
     p.SB = 0;
@@ -743,8 +745,8 @@ __device__ __forceinline__ void stream_region(const float* __restrict__ g, float
 // 2. the streaming pass; one wave per region of kRegion elements.  With STATS
 // each region also records the float64 energy of the elements it already knows
 // the fate of (all of them unless they are candidates): spart[w] = {sent, dropped}.
-template <bool STATS>
-__global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict__ g, float* __restrict__ e,
+template <bool STATS, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void k_stream(const float* __restrict__ g, float* __restrict__ e,
                                                          const SegPlan* __restrict__ plan, int32_t nseg,
                                                          const int32_t* __restrict__ rb, int64_t R,
                                                          SegState* __restrict__ st,
@@ -754,9 +756,9 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
                                                          int32_t* __restrict__ idx, uint32_t* __restrict__ nonfinite,
                                                          double2* __restrict__ spart, Header* __restrict__ hdr,
                                                          uint32_t* __restrict__ ovf) {
-    __shared__ uint32_t lcnt[kStreamWaves], lovf[kStreamWaves];
-    __shared__ int32_t lgrp[kStreamWaves];
-    const int64_t w = static_cast<int64_t>(blockIdx.x) * kStreamWaves + threadIdx.x / kWave;
+    __shared__ uint32_t lcnt[WAVES], lovf[WAVES];
+    __shared__ int32_t lgrp[WAVES];
+    const int64_t w = static_cast<int64_t>(blockIdx.x) * WAVES + threadIdx.x / kWave;
     uint32_t cnt = 0;
     int32_t grp = -1;
     bool ovfl = false;
@@ -808,7 +810,7 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
     if (threadIdx.x == 0) {
         int32_t g0 = -1;
         uint32_t sum = 0, nov = 0;
-        for (int i = 0; i < kStreamWaves; ++i) {
+        for (int i = 0; i < WAVES; ++i) {
             nov += lovf[i];
             if (lgrp[i] < 0) continue;
             if (lgrp[i] != g0) {
@@ -823,7 +825,7 @@ __global__ __launch_bounds__(kStreamBlock) void k_stream(const float* __restrict
             // overflowed regions of this block (in any order: each is read again on its own)
             uint32_t at = atomicAdd(&hdr->n_overflow, nov);
             const int64_t w0 = w - threadIdx.x / kWave;  // this block's first region
-            for (int i = 0; i < kStreamWaves; ++i)
+            for (int i = 0; i < WAVES; ++i)
                 if (lovf[i]) ovf[at++] = static_cast<uint32_t>(w0 + i);
         }
     }
@@ -1705,13 +1707,22 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
         EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
                       static_cast<const uint32_t*>(shist), P.hcopies, st));
     }
-    const dim3 sgrid(static_cast<unsigned>(cdiv(P.R, kStreamWaves)));
+    // A call with few regions streams them with one-wave blocks, so that they
+    // spread over every CU (the flat N = 1e6 call has 245 regions).
+    auto stream = [&](auto waves, auto stats_on) -> int {
+        constexpr int W = decltype(waves)::value;
+        constexpr bool ST = decltype(stats_on)::value;
+        return launch("topk_stream", k_stream<ST, W>, dim3(static_cast<unsigned>(cdiv(P.R, W))), dim3(W * kWave), s,
+                      g, e, plan, nseg, rb, P.R, st, region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart, hdr,
+                      ovf);
+    };
+    using Few = std::integral_constant<int, 1>;
+    using Many = std::integral_constant<int, kStreamWaves>;
+    const bool few = P.R < kFewRegions;
     if (stats)
-        EF_TRY(launch("topk_stream", k_stream<true>, sgrid, dim3(kStreamBlock), s, g, e, plan, nseg, rb, P.R, st,
-                      region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart, hdr, ovf));
+        EF_TRY(few ? stream(Few{}, std::true_type{}) : stream(Many{}, std::true_type{}));
     else
-        EF_TRY(launch("topk_stream", k_stream<false>, sgrid, dim3(kStreamBlock), s, g, e, plan, nseg, rb, P.R, st,
-                      region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart, hdr, ovf));
+        EF_TRY(few ? stream(Few{}, std::false_type{}) : stream(Many{}, std::false_type{}));
     if (!P.any_normal) return finish_stats();
 
     EF_TRY(launch("topk_compact", k_compact, dim3(static_cast<unsigned>(P.CB)), dim3(kBlock), s, plan, nseg,
