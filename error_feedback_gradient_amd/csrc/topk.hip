@@ -24,19 +24,21 @@
 //                 its path (exact fallback when its candidates exceed its slot
 //                 capacity or fewer than k were found); candidate slots -> one
 //                 dense index-ordered list, plus the first radix histogram.
-//      recollect  a region whose slot overflowed (its first `cap` candidates
+//                 A region whose slot overflowed (its first `cap` candidates
 //                 are in the slot, the rest are untouched in e) is read again
-//                 past its last stored index by one wave, which appends the
-//                 rest at their places in the dense list.  Clustered
-//                 magnitudes thus cost one extra read of the crowded regions
-//                 instead of the exact pass over the whole tensor.
+//                 past its last stored index by one wave of the same block,
+//                 which appends the rest at their places in the dense list.
+//                 Clustered magnitudes thus cost one extra read of the crowded
+//                 regions instead of the exact pass over the whole tensor.
 //   4. radix      exact k-th largest key T over the candidates: digits of 11,
 //                 10 and 10 bits, each histogram (LDS-privatised) built by one
 //                 kernel and its digit found by the blocks of the next one.
 //   5. emit       entries with key > T, plus the first r entries with key == T
-//                 in index order, are written in index order.  Their residual
-//                 becomes +0 unless the stream already cleared it; a dropped
-//                 candidate that the stream cleared gets x back.
+//                 in index order, are written in index order: a count kernel
+//                 totals each block's contiguous range of the list, and every
+//                 write block starts after the totals of the blocks before it.
+//                 Their residual becomes +0 unless the stream already cleared
+//                 it; a dropped candidate that the stream cleared gets x back.
 // The exact fallback runs steps 4-5 over the whole tensor (x sits in e): its
 // compaction blocks histogram x for the first digit and put x back wherever
 // the stream cleared it.  Only integer atomics are used, so results do not
@@ -104,8 +106,8 @@ constexpr int kRadixBins = 2048;
 constexpr int kCoarse = 64;
 constexpr int kHistWords = kRadixBins + kCoarse;
 // A fallback tensor's elements are taken in units of kRawChunk (kRawSub
-// chunks of kChunk), so that its per-unit counts stay few enough for one
-// block to scan (79,346 units at 1.3e9 elements).
+// chunks of kChunk), so that its per-unit monitoring partials stay few
+// (79,346 units at 1.3e9 elements).
 constexpr int kRawSub = 8;
 constexpr int kRawChunk = kRawSub * kChunk;
 constexpr int kSelectBlocks = 2048;                // select / emit blocks shared out among the tensors
@@ -167,12 +169,6 @@ struct alignas(16) SegState {
 };
 static_assert(sizeof(SegState) == 64, "SegState layout");
 
-struct alignas(16) Header {
-    uint32_t n_overflow;  // entries of the overflowed-region list
-    uint32_t pad[63];
-};
-static_assert(sizeof(Header) == 256, "Header layout");
-
 // ------------------------------------------------------------------ host plan
 // A vector with inline room for N elements: a call over one tensor builds its
 // plan without touching the host heap (the allocation-free entry point relies
@@ -218,8 +214,8 @@ struct Plan {
 
 struct Layout {
     size_t status, plan, rb, gbb, sbb, cbb, hb, static_end;
-    size_t header, state, shist, rhist, grp_cnt, zero_end;
-    size_t grp_off, region_cnt, ovf, cpair, dval, didx, cgt, ceq, rgt, req, spart, gpart, cpart, rpart;
+    size_t state, shist, rhist, grp_cnt, zero_end;
+    size_t region_cnt, cpair, dval, didx, btot, spart, gpart, cpart, rpart;
     size_t total;
 };
 
@@ -239,22 +235,17 @@ static Layout make_layout(const Plan& p) {
     L.hb = at; at += (ns + 1) * 4;
     at = round_up(at, 256);
     L.static_end = at;
-    L.header = take(sizeof(Header));
     L.state = take(ns * sizeof(SegState));
     L.shist = take(ns * static_cast<size_t>(p.hcopies) * kSampleBins * 4);
     L.rhist = take(3 * ns * static_cast<size_t>(p.hcopies) * kHistWords * 4);
     L.grp_cnt = take(static_cast<size_t>(p.G) * 4);
     L.zero_end = at;
-    L.grp_off = take(static_cast<size_t>(p.G) * 4);
     L.region_cnt = take(static_cast<size_t>(p.R) * 4);
-    L.ovf = take(static_cast<size_t>(p.R) * 4);
     L.cpair = take(static_cast<size_t>(p.Ctot) * 8);
     L.dval = take(static_cast<size_t>(p.Ctot) * 4);
     L.didx = take(static_cast<size_t>(p.Ctot) * 4);
-    L.cgt = take(static_cast<size_t>(p.QC) * 4);
-    L.ceq = take(static_cast<size_t>(p.QC) * 4);
-    L.rgt = take(static_cast<size_t>(p.QR) * 4);
-    L.req = take(static_cast<size_t>(p.QR) * 4);
+    // per select block: its range's counts of keys above T and equal to T
+    L.btot = take(static_cast<size_t>(p.HB) * 8);
     // monitoring partials (sent, dropped energy): per region, per candidate unit, per raw unit
     L.spart = take(static_cast<size_t>(p.R) * 16);
     L.gpart = take(static_cast<size_t>(p.G) * 16);
@@ -754,14 +745,12 @@ __global__ __launch_bounds__(WAVES * kWave) void k_stream(const float* __restric
                                                          uint32_t* __restrict__ grp_cnt, uint2* __restrict__ cpair,
                                                          float* __restrict__ vals,
                                                          int32_t* __restrict__ idx, uint32_t* __restrict__ nonfinite,
-                                                         double2* __restrict__ spart, Header* __restrict__ hdr,
-                                                         uint32_t* __restrict__ ovf) {
-    __shared__ uint32_t lcnt[WAVES], lovf[WAVES];
+                                                         double2* __restrict__ spart) {
+    __shared__ uint32_t lcnt[WAVES];
     __shared__ int32_t lgrp[WAVES];
     const int64_t w = static_cast<int64_t>(blockIdx.x) * WAVES + threadIdx.x / kWave;
     uint32_t cnt = 0;
     int32_t grp = -1;
-    bool ovfl = false;
     if (w < R) {
         const int s = upper_index_wave(rb, nseg, static_cast<int32_t>(w));
         const SegPlan& P = plan[s];
@@ -795,23 +784,19 @@ __global__ __launch_bounds__(WAVES * kWave) void k_stream(const float* __restric
             if (nf && nonfinite) atomicAdd(nonfinite, nf);
         }
         grp = P.group_begin + static_cast<int32_t>(rl / kGroup);
-        ovfl = cnt > cap;
     }
-    // Group totals and the overflow list: global atomics per block instead of
-    // per region.  The 256 regions of a group run on blocks of every XCD, so
+    // Group totals: global atomics per block instead of per region.  The 256 regions of a group run on blocks of every XCD, so
     // their atomics meet at one address outside the L2s and are applied one
     // after another; per region, that queue outlasted the stream by ~50 us.
     if (lane() == 0) {
         lcnt[threadIdx.x / kWave] = cnt;
         lgrp[threadIdx.x / kWave] = cnt ? grp : -1;
-        lovf[threadIdx.x / kWave] = ovfl ? 1u : 0u;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         int32_t g0 = -1;
-        uint32_t sum = 0, nov = 0;
+        uint32_t sum = 0;
         for (int i = 0; i < WAVES; ++i) {
-            nov += lovf[i];
             if (lgrp[i] < 0) continue;
             if (lgrp[i] != g0) {
                 if (sum) atomicAdd(&grp_cnt[g0], sum);
@@ -821,13 +806,6 @@ __global__ __launch_bounds__(WAVES * kWave) void k_stream(const float* __restric
             sum += lcnt[i];
         }
         if (sum) atomicAdd(&grp_cnt[g0], sum);
-        if (nov) {
-            // overflowed regions of this block (in any order: each is read again on its own)
-            uint32_t at = atomicAdd(&hdr->n_overflow, nov);
-            const int64_t w0 = w - threadIdx.x / kWave;  // this block's first region
-            for (int i = 0; i < WAVES; ++i)
-                if (lovf[i]) ovf[at++] = static_cast<uint32_t>(w0 + i);
-        }
     }
 }
 
@@ -912,17 +890,23 @@ __device__ __forceinline__ void wave_find_digit(const uint32_t* gh0, int32_t hco
 //    counts: the candidates before its group give its dense offset, their
 //    total decides the path (the tensor's first block records both).
 //    Candidate path: the group's slots -> the dense index-ordered list, plus
-//    the first radix histogram (top 11 key bits).  Exact fallback: the block's
-//    elements are read for the first radix histogram of the full pass, and
-//    then x is put back where the stream cleared it (those reads saw +0: the
-//    histogram moves each such element from bin 0 to its own bin).
+//    the first radix histogram (top 11 key bits).  An overflowed region then
+//    gets one wave of the block, which reads e again past the region's last
+//    stored index (eight 64-element rows in flight per lane) and appends the
+//    rest of its candidates in index order at the dense places the copy left
+//    free; like the stream for stored ones, it clears e where the key is >=
+//    thi, so that every entry of the dense list obeys the rule k_write relies
+//    on.  Exact fallback: the block's elements are read for the first radix
+//    histogram of the full pass, and then x is put back where the stream
+//    cleared it (those reads saw +0: the histogram moves each such element
+//    from bin 0 to its own bin).
 constexpr int kCompactItems = 8;
 constexpr int kRawRows = 16;
+constexpr int kRecollectRows = 8;
 __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ plan, int32_t nseg,
                                                     const int32_t* __restrict__ cbb, const int32_t* __restrict__ gbb,
                                                     const int32_t* __restrict__ rb, SegState* __restrict__ st,
                                                     const uint32_t* __restrict__ grp_cnt,
-                                                    uint32_t* __restrict__ grp_off,
                                                     const uint32_t* __restrict__ region_cnt,
                                                     const uint2* __restrict__ cpair, float* __restrict__ dval,
                                                     int32_t* __restrict__ didx, uint32_t* __restrict__ rhist,
@@ -938,7 +922,6 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     const int split = P.compact_split;
     const int lb = b - cbb[s];
     const int gl = lb / split, part = lb % split;
-    const int gi = gbb[s] + gl;
     const int t = threadIdx.x;
     // the tensor's candidates before this group, and in all
     uint32_t before = 0, total = 0;
@@ -964,12 +947,9 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     const int64_t capacity = static_cast<int64_t>(P.nregions) * P.cap;
     const bool fb = force_fallback || P.direct || static_cast<int64_t>(total) > capacity ||
                     static_cast<int64_t>(total) < P.k;
-    if (t == 0) {
-        if (lb == 0) {
-            st[s].fallback = fb ? 1u : 0u;
-            st[s].ncand = total;
-        }
-        if (part == 0) grp_off[gi] = before;  // k_recollect places the group's overflowed regions
+    if (t == 0 && lb == 0) {
+        st[s].fallback = fb ? 1u : 0u;
+        st[s].ncand = total;
     }
     const int64_t r0 = rb[s] + static_cast<int64_t>(gl) * kGroup;  // first region (global)
     const int nr = min(kGroup, P.nregions - gl * kGroup);
@@ -1025,8 +1005,8 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
         const int64_t dbase = P.cand_base + before;
         const int64_t slot0 = P.cand_base + (r0 - rb[s]) * cap;
         // kCompactItems entries per thread in flight: an entry past the block's
-        // range or past its region's slot (k_recollect writes those) reads the
-        // group's first slot instead and is not used
+        // range or past its region's slot (written below) reads the group's
+        // first slot instead and is not used
         for (uint32_t qb = q0; qb < q1; qb += kBlock * kCompactItems) {
             uint2 pr[kCompactItems];
             bool ok[kCompactItems];
@@ -1052,84 +1032,43 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
                 atomicAdd(&h[key_of(v) >> 20], 1u);
             }
         }
-    }
-    flush_hist(h, kRadixBins, radix_hist(rhist, 0, s, b % hcopies, nseg, hcopies));
-}
-
-// 4. one wave per overflowed region of a tensor on the fast path.  Its slot
-//    holds the region's first `cap` candidates in index order; the rest were
-//    not stored, so the stream left e = x for them.  They are read again from
-//    e past the last stored index (eight 64-element rows in flight per lane)
-//    and appended in index order after the stored ones, at the dense
-//    positions k_compact left free; their top digits join the first radix
-//    histogram (counted in a per-wave LDS histogram and added to the global
-//    one per region: the crowded candidates share a few bins, and one global
-//    atomic each would serialise on them).  Like the stream for stored ones,
-//    it clears e where the key is >= thi, so that every candidate of the
-//    dense list obeys the rule k_write relies on.  Grid-stride over the
-//    overflow list; empty in the common case.
-constexpr int kRecollectBlocks = 512;
-constexpr int kRecollectRows = 8;
-__global__ __launch_bounds__(kBlock) void k_recollect(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                      const int32_t* __restrict__ rb, const int32_t* __restrict__ gbb,
-                                                      const SegState* __restrict__ st,
-                                                      const uint32_t* __restrict__ region_cnt,
-                                                      const uint32_t* __restrict__ grp_off,
-                                                      const uint2* __restrict__ cpair, const Header* __restrict__ hdr,
-                                                      const uint32_t* __restrict__ ovf, float* __restrict__ e,
-                                                      float* __restrict__ dval, int32_t* __restrict__ didx,
-                                                      uint32_t* __restrict__ rhist, int32_t hcopies) {
-    __shared__ uint32_t lh[kWavesPerBlock][kRadixBins];
-    const uint32_t nov = hdr->n_overflow;
-    const int l = lane();
-    uint32_t* h = lh[threadIdx.x / kWave];
-    const uint32_t stride = gridDim.x * kWavesPerBlock;
-    for (uint32_t j = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; j < nov; j += stride) {
-        const int32_t w = static_cast<int32_t>(ovf[j]);
-        const int s = upper_index_wave(rb, nseg, w);
-        const SegPlan& P = plan[s];
-        const uint32_t cap = static_cast<uint32_t>(P.cap);
-        if (P.mode != MODE_NORMAL || st[s].fallback || cap == 0) continue;
-        const int64_t rl = w - rb[s];
-        const int64_t gend = P.off + min(rl * kRegion + kRegion, P.n);
-        const uint32_t cnt = region_cnt[w];
-        const int64_t last = cpair[P.cand_base + rl * cap + cap - 1].y;  // index of the last stored candidate
-        // dense position of the region's first candidate: its group's offset in
-        // the tensor plus the true counts of the group's earlier regions
-        const int64_t g0 = rb[s] + rl / kGroup * kGroup;
-        uint32_t before = 0;
-        for (int64_t r = g0 + l; r < w; r += kWave) before += region_cnt[r];
-        before = wave_sum(before);
-        const uint32_t gi = static_cast<uint32_t>(gbb[s] + rl / kGroup);
-        const int64_t base = P.cand_base + grp_off[gi] + before;
+        // overflowed regions, one wave each (none in the common case)
         const uint32_t tlo = st[s].tlo, thi = st[s].thi;
-        for (int i = l; i < kRadixBins; i += kWave) h[i] = 0;
-        uint32_t pos = cap;  // next entry of this region
-        for (int64_t i0 = last + 1; i0 < gend && pos < cnt; i0 += kWave * kRecollectRows) {
-            float x[kRecollectRows];
+        const int l = lane();
+        for (int r = rs + t / kWave; r < re; r += kWavesPerBlock) {
+            const uint32_t cnt = region_cnt[r0 + r];
+            if (cnt <= cap) continue;
+            const int64_t rl = static_cast<int64_t>(gl) * kGroup + r;  // region within the tensor
+            const int64_t gend = P.off + min(rl * kRegion + kRegion, P.n);
+            const int64_t last = cpair[slot0 + r * cap + cap - 1].y;  // index of the last stored candidate
+            const int64_t base = dbase + loff[r];
+            uint32_t pos = static_cast<uint32_t>(cap);  // next entry of this region
+            for (int64_t i0 = last + 1; i0 < gend && pos < cnt; i0 += kWave * kRecollectRows) {
+                float x[kRecollectRows];
 #pragma unroll
-            for (int u = 0; u < kRecollectRows; ++u) {
-                const int64_t i = i0 + u * kWave + l;
-                x[u] = i < gend ? e[i] : 0.0f;
-            }
-#pragma unroll
-            for (int u = 0; u < kRecollectRows; ++u) {
-                const int64_t i = i0 + u * kWave + l;
-                const uint32_t key = key_of(x[u]);
-                const bool hit = i < gend && key >= tlo;
-                const uint64_t bal = __ballot(hit);
-                const uint32_t p = pos + count_below(bal);
-                if (hit && p < cnt) {
-                    dval[base + p] = x[u];
-                    didx[base + p] = static_cast<int32_t>(i);
-                    atomicAdd(&h[key >> 20], 1u);
-                    if (key >= thi) e[i] = 0.0f;
+                for (int u = 0; u < kRecollectRows; ++u) {
+                    const int64_t i = i0 + u * kWave + l;
+                    x[u] = i < gend ? e[i] : 0.0f;
                 }
-                pos += popc64(bal);
+#pragma unroll
+                for (int u = 0; u < kRecollectRows; ++u) {
+                    const int64_t i = i0 + u * kWave + l;
+                    const uint32_t key = key_of(x[u]);
+                    const bool hit = i < gend && key >= tlo;
+                    const uint64_t bal = __ballot(hit);
+                    const uint32_t p = pos + count_below(bal);
+                    if (hit && p < cnt) {
+                        dval[base + p] = x[u];
+                        didx[base + p] = static_cast<int32_t>(i);
+                        atomicAdd(&h[key >> 20], 1u);
+                        if (key >= thi) e[i] = 0.0f;
+                    }
+                    pos += popc64(bal);
+                }
             }
         }
-        flush_hist_wave(h, radix_hist(rhist, 0, s, blockIdx.x % hcopies, nseg, hcopies));
     }
+    flush_hist(h, kRadixBins, radix_hist(rhist, 0, s, b % hcopies, nseg, hcopies));
 }
 
 // Radix digit of `key` in pass p (11, 10, 10 bits from the top) and whether the
@@ -1148,16 +1087,21 @@ __device__ __forceinline__ bool radix_digit(int pass, uint32_t key, uint32_t pre
 }
 
 // The select / emit blocks: each tensor that selects owns blocks
-// [hb[s], hb[s+1]) (static); they stride over the tensor's work units, which
-// depend on the path the compaction chose: the dense candidate list in units
-// of kChunk entries, or x itself (in e) in units of kRawChunk elements, each
-// taken as kRawSub chunks of kChunk.  Per-unit counts and statistics sit at
-// the tensor's static bases (cunit_base, runit_base).
+// [hb[s], hb[s+1]) (static) and shares out the tensor's work units among
+// them, which depend on the path the compaction chose: the dense candidate
+// list in units of kChunk entries, or x itself (in e) in units of kRawChunk
+// elements, each taken as kRawSub chunks of kChunk.  The histogram blocks
+// stride over the units; the count and write blocks take contiguous ranges
+// [u0, u1) (block lb: units lb * U / nb .. (lb + 1) * U / nb, rounded up, so
+// the first block's range is never empty), which makes a block's place in
+// the output the counts of the blocks before it.  Per-unit statistics sit
+// at the tensor's static bases (cunit_base, runit_base).
 struct SelBlock {
     int s;
     int lb, nb;      // this block among the tensor's blocks
     bool raw;        // exact fallback: units of x
     uint32_t units;
+    uint32_t u0, u1;  // this block's contiguous range of units
 };
 
 __device__ __forceinline__ SelBlock sel_block(const SegPlan* plan, int32_t nseg, const int32_t* hb,
@@ -1169,6 +1113,9 @@ __device__ __forceinline__ SelBlock sel_block(const SegPlan* plan, int32_t nseg,
     sb.raw = st[sb.s].fallback != 0;
     sb.units = sb.raw ? static_cast<uint32_t>(plan[sb.s].raw_units)
                       : (st[sb.s].ncand + kChunk - 1) / kChunk;
+    const uint64_t U = sb.units, nb = static_cast<uint64_t>(sb.nb);
+    sb.u0 = static_cast<uint32_t>((U * static_cast<uint64_t>(sb.lb) + nb - 1) / nb);
+    sb.u1 = static_cast<uint32_t>((U * static_cast<uint64_t>(sb.lb + 1) + nb - 1) / nb);
     return sb;
 }
 
@@ -1285,25 +1232,26 @@ __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __rest
     flush_hist(h, 1024, radix_hist(rhist, pass, sb.s, blockIdx.x % hcopies, nseg, hcopies));
 }
 
-// 6a. per-unit counts of keys above T and equal to T
+// 6a. per block: the counts of keys above T and equal to T in its range of
+//     units (every block of the tensor writes its word, 0 for an empty range)
 __global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ plan, int32_t nseg,
                                                   const int32_t* __restrict__ hb, SegState* __restrict__ st,
                                                   const uint32_t* __restrict__ rhist, int32_t hcopies,
                                                   const float* __restrict__ dval, const float* __restrict__ e,
-                                                  uint32_t* __restrict__ cgt, uint32_t* __restrict__ ceq,
-                                                  uint32_t* __restrict__ rgt, uint32_t* __restrict__ req) {
+                                                  uint2* __restrict__ btot) {
     __shared__ uint32_t sa[kWavesPerBlock], sbq[kWavesPerBlock];
     const SelBlock sb = sel_block(plan, nseg, hb, st);
-    if (sb.lb > 0 && static_cast<uint32_t>(sb.lb) >= sb.units) return;
+    if (sb.u0 >= sb.u1) {  // never the tensor's first block, which records T and r
+        if (threadIdx.x == 0) btot[blockIdx.x] = make_uint2(0u, 0u);
+        return;
+    }
     uint32_t T, r;
     digits_before(3, sb.s, sb.lb, plan, nseg, st, rhist, hcopies, &T, &r);
     const SegPlan& P = plan[sb.s];
     const SegState& S = st[sb.s];
     const int nsub = sb.raw ? kRawSub : 1;
-    uint32_t* gt = sb.raw ? rgt + P.runit_base : cgt + P.cunit_base;
-    uint32_t* eq = sb.raw ? req + P.runit_base : ceq + P.cunit_base;
-    for (uint32_t u = sb.lb; u < sb.units; u += sb.nb) {
-        uint32_t a = 0, b = 0;
+    uint32_t a = 0, b = 0;
+    for (uint32_t u = sb.u0; u < sb.u1; ++u) {
         for (int j = 0; j < nsub; ++j) {
             const Chunk c = chunk_of(P, S, sb.raw, u, j, dval, nullptr, e);
             if (c.cnt == 0) break;
@@ -1317,101 +1265,67 @@ __global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ pl
                 b += ok && key == T;
             }
         }
-        a = wave_sum(a);
-        b = wave_sum(b);
-        if (lane() == 0) {
-            sa[threadIdx.x / kWave] = a;
-            sbq[threadIdx.x / kWave] = b;
+    }
+    a = wave_sum(a);
+    b = wave_sum(b);
+    if (lane() == 0) {
+        sa[threadIdx.x / kWave] = a;
+        sbq[threadIdx.x / kWave] = b;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t ta = 0, tb = 0;
+        for (int i = 0; i < kWavesPerBlock; ++i) {
+            ta += sa[i];
+            tb += sbq[i];
         }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            uint32_t ta = 0, tb = 0;
-            for (int i = 0; i < kWavesPerBlock; ++i) {
-                ta += sa[i];
-                tb += sbq[i];
-            }
-            gt[u] = ta;
-            eq[u] = tb;
-        }
-        __syncthreads();
+        btot[blockIdx.x] = make_uint2(ta, tb);
     }
 }
 
-// 6b. exclusive scan of the unit counts of each tensor (packed gt:eq in 64
-//     bits): one block per tensor, each thread taking kEmitItems consecutive
-//     units of every tile
-constexpr int kEmitScanBlock = 1024;
-constexpr int kEmitItems = 8;
-__global__ __launch_bounds__(kEmitScanBlock) void k_emit_scan(const SegPlan* __restrict__ plan,
-                                                              const SegState* __restrict__ st,
-                                                              uint32_t* __restrict__ cgt, uint32_t* __restrict__ ceq,
-                                                              uint32_t* __restrict__ rgt, uint32_t* __restrict__ req) {
-    __shared__ uint64_t lds[kEmitScanBlock / kWave + 1];
-    const int s = blockIdx.x;
-    const SegPlan& P = plan[s];
-    if (P.mode != MODE_NORMAL) return;
-    uint32_t *a, *b;
-    int64_t n;
-    if (st[s].fallback) {
-        a = rgt + P.runit_base;
-        b = req + P.runit_base;
-        n = P.raw_units;
-    } else {
-        a = cgt + P.cunit_base;
-        b = ceq + P.cunit_base;
-        n = (st[s].ncand + kChunk - 1) / kChunk;
-    }
-    uint64_t carry = 0;
-    for (int64_t t0 = 0; t0 < n; t0 += static_cast<int64_t>(kEmitScanBlock) * kEmitItems) {
-        const int64_t i0 = t0 + static_cast<int64_t>(threadIdx.x) * kEmitItems;
-        uint64_t v[kEmitItems];
-        uint64_t sum = 0;
-#pragma unroll
-        for (int j = 0; j < kEmitItems; ++j) {
-            // all loads issued before any is used: past the end reads entry n - 1
-            const int64_t i = min(i0 + j, n - 1);
-            const uint64_t w = (static_cast<uint64_t>(a[i]) << 32) | b[i];
-            v[j] = i0 + j < n ? w : 0;
-            sum += v[j];
-        }
-        uint64_t tot;
-        uint64_t ex = block_excl_scan<kEmitScanBlock>(sum, lds, &tot) + carry;
-#pragma unroll
-        for (int j = 0; j < kEmitItems; ++j) {
-            const int64_t i = i0 + j;
-            if (i < n) {
-                a[i] = static_cast<uint32_t>(ex >> 32);
-                b[i] = static_cast<uint32_t>(ex);
-            }
-            ex += v[j];
-        }
-        carry += tot;
-    }
-}
-
-// 6c. the kept entries at their index-ordered places, each chunk read in rows
+// 6b. the kept entries at their index-ordered places, each chunk read in rows
 //     as load_rows lays them out, so loads and (mostly kept-together) stores
 //     coalesce.  An entry's place is (entries with key > T before it) +
-//     min(r, entries with key == T before it): the unit's counts before it
-//     (from k_emit_scan), those of the unit's earlier chunks, of the block's
-//     earlier waves, of the wave's earlier rows, and of the row's lower lanes
-//     (ballots).  Kept entries get e = +0 unless the stream cleared them (key
+//     min(r, entries with key == T before it): the totals of the tensor's
+//     earlier blocks (from k_count), those of the block's earlier chunks, of
+//     its earlier waves, of the wave's earlier rows, and of the row's lower
+//     lanes (ballots).  Kept entries get e = +0 unless the stream cleared them (key
 //     >= thi); dropped ones the stream cleared get x back.
 template <bool STATS>
 __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ plan, int32_t nseg,
                                                   const int32_t* __restrict__ hb, const SegState* __restrict__ st,
                                                   const float* __restrict__ dval, const int32_t* __restrict__ didx,
-                                                  const uint32_t* __restrict__ cgt, const uint32_t* __restrict__ ceq,
-                                                  const uint32_t* __restrict__ rgt, const uint32_t* __restrict__ req,
+                                                  const uint2* __restrict__ btot,
                                                   float* __restrict__ e, float* __restrict__ vals,
                                                   int32_t* __restrict__ idx, double2* __restrict__ cpart,
                                                   double2* __restrict__ rpart, uint32_t* __restrict__ stray) {
     __shared__ uint32_t wgt[kWavesPerBlock], weq[kWavesPerBlock];
     __shared__ double2 lsum[kWavesPerBlock];
     const SelBlock sb = sel_block(plan, nseg, hb, st);
-    if (static_cast<uint32_t>(sb.lb) >= sb.units) return;
+    if (sb.u0 >= sb.u1) return;
     const int wv = threadIdx.x / kWave;
     const int l = lane();
+    // counts before the block's range: the totals of the tensor's earlier blocks
+    uint32_t gtu = 0, equ = 0;
+    for (int b = hb[sb.s] + static_cast<int>(threadIdx.x); b < static_cast<int>(blockIdx.x); b += kBlock) {
+        const uint2 c = btot[b];
+        gtu += c.x;
+        equ += c.y;
+    }
+    gtu = wave_sum(gtu);
+    equ = wave_sum(equ);
+    if (l == 0) {
+        wgt[wv] = gtu;
+        weq[wv] = equ;
+    }
+    __syncthreads();
+    gtu = 0;
+    equ = 0;
+    for (int i = 0; i < kWavesPerBlock; ++i) {
+        gtu += wgt[i];
+        equ += weq[i];
+    }
+    __syncthreads();  // wgt / weq are rewritten by the first chunk
     const SegPlan& P = plan[sb.s];
     const SegState& S = st[sb.s];
     const uint32_t T = S.T, r = S.r;
@@ -1419,11 +1333,8 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
     const int64_t out_off = P.out_off, kseg = P.k;
     const int64_t seg_lo = P.off, seg_hi = P.off + P.n;
     const int nsub = sb.raw ? kRawSub : 1;
-    const uint32_t* gtp = sb.raw ? rgt + P.runit_base : cgt + P.cunit_base;
-    const uint32_t* eqp = sb.raw ? req + P.runit_base : ceq + P.cunit_base;
     double2* part = sb.raw ? (rpart ? rpart + P.runit_base : nullptr) : (cpart ? cpart + P.cunit_base : nullptr);
-    for (uint32_t u = sb.lb; u < sb.units; u += sb.nb) {
-        uint32_t gtu = gtp[u], equ = eqp[u];  // counts before the unit's next chunk
+    for (uint32_t u = sb.u0; u < sb.u1; ++u) {  // gtu, equ: counts before the next chunk
         double sent = 0.0, drop = 0.0;
         for (int j = 0; j < nsub; ++j) {
             const Chunk c = chunk_of(P, S, sb.raw, u, j, dval, didx, e);
@@ -1659,10 +1570,10 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
             if (read_pinned) *read_pinned = true;
         }
     }
-    const int64_t nzero = static_cast<int64_t>((L.zero_end - L.header) / 16);
+    const int64_t nzero = static_cast<int64_t>((L.zero_end - L.state) / 16);
     const unsigned zgrid = static_cast<unsigned>(
         std::min<int64_t>(kMaxGrid, std::max<int64_t>({1, cdiv(nzero, kBlock), cdiv(tvec, kBlock)})));
-    EF_TRY(launch("topk_init", k_init, dim3(zgrid), dim3(kBlock), s, reinterpret_cast<uint4*>(at(L.header)), nzero,
+    EF_TRY(launch("topk_init", k_init, dim3(zgrid), dim3(kBlock), s, reinterpret_cast<uint4*>(at(L.state)), nzero,
                   nonfinite, reinterpret_cast<uint32_t*>(W), first, tsrc, tvec));
 
     const SegPlan* plan = reinterpret_cast<const SegPlan*>(at(L.plan));
@@ -1670,22 +1581,16 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
     const int32_t* gbb = reinterpret_cast<const int32_t*>(at(L.gbb));
     const int32_t* sbb = reinterpret_cast<const int32_t*>(at(L.sbb));
     const int32_t* hb = reinterpret_cast<const int32_t*>(at(L.hb));
-    Header* hdr = reinterpret_cast<Header*>(at(L.header));
     uint32_t* stray = reinterpret_cast<uint32_t*>(at(L.status));
     SegState* st = reinterpret_cast<SegState*>(at(L.state));
     uint32_t* shist = reinterpret_cast<uint32_t*>(at(L.shist));
     uint32_t* rhist = reinterpret_cast<uint32_t*>(at(L.rhist));
     uint32_t* grp_cnt = reinterpret_cast<uint32_t*>(at(L.grp_cnt));
-    uint32_t* grp_off = reinterpret_cast<uint32_t*>(at(L.grp_off));
     uint32_t* region_cnt = reinterpret_cast<uint32_t*>(at(L.region_cnt));
-    uint32_t* ovf = reinterpret_cast<uint32_t*>(at(L.ovf));
     uint2* cpair = reinterpret_cast<uint2*>(at(L.cpair));
     float* dval = reinterpret_cast<float*>(at(L.dval));
     int32_t* didx = reinterpret_cast<int32_t*>(at(L.didx));
-    uint32_t* cgt = reinterpret_cast<uint32_t*>(at(L.cgt));
-    uint32_t* ceq = reinterpret_cast<uint32_t*>(at(L.ceq));
-    uint32_t* rgt = reinterpret_cast<uint32_t*>(at(L.rgt));
-    uint32_t* req = reinterpret_cast<uint32_t*>(at(L.req));
+    uint2* btot = reinterpret_cast<uint2*>(at(L.btot));
     double2* spart = reinterpret_cast<double2*>(at(L.spart));
     double2* cpart = stats ? reinterpret_cast<double2*>(at(L.cpart)) : nullptr;
     double2* rpart = stats ? reinterpret_cast<double2*>(at(L.rpart)) : nullptr;
@@ -1713,8 +1618,7 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
         constexpr int W = decltype(waves)::value;
         constexpr bool ST = decltype(stats_on)::value;
         return launch("topk_stream", k_stream<ST, W>, dim3(static_cast<unsigned>(cdiv(P.R, W))), dim3(W * kWave), s,
-                      g, e, plan, nseg, rb, P.R, st, region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart, hdr,
-                      ovf);
+                      g, e, plan, nseg, rb, P.R, st, region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart);
     };
     using Few = std::integral_constant<int, 1>;
     using Many = std::integral_constant<int, kStreamWaves>;
@@ -1727,28 +1631,20 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
 
     EF_TRY(launch("topk_compact", k_compact, dim3(static_cast<unsigned>(P.CB)), dim3(kBlock), s, plan, nseg,
                   static_cast<const int32_t*>(reinterpret_cast<int32_t*>(at(L.cbb))), gbb, rb, st,
-                  static_cast<const uint32_t*>(grp_cnt), grp_off, static_cast<const uint32_t*>(region_cnt),
+                  static_cast<const uint32_t*>(grp_cnt), static_cast<const uint32_t*>(region_cnt),
                   static_cast<const uint2*>(cpair), dval, didx, rhist, P.hcopies, e, stray,
                   static_cast<uint32_t>((flags & EF_FLAG_FORCE_FALLBACK) ? 1u : 0u)));
-    EF_TRY(launch("topk_recollect", k_recollect, dim3(kRecollectBlocks), dim3(kBlock), s, plan, nseg, rb, gbb,
-                  static_cast<const SegState*>(st), static_cast<const uint32_t*>(region_cnt),
-                  static_cast<const uint32_t*>(grp_off), static_cast<const uint2*>(cpair),
-                  static_cast<const Header*>(hdr), static_cast<const uint32_t*>(ovf), e, dval, didx, rhist,
-                  P.hcopies));
     const dim3 hgrid(static_cast<unsigned>(P.HB));
     for (int pass = 1; pass < 3; ++pass)
         EF_TRY(launch("topk_hist", k_hist, hgrid, dim3(kBlock), s, pass, plan, nseg, hb, st,
                       static_cast<const float*>(dval), static_cast<const float*>(e), rhist, P.hcopies));
     EF_TRY(launch("topk_count", k_count, hgrid, dim3(kBlock), s, plan, nseg, hb, st,
                   static_cast<const uint32_t*>(rhist), P.hcopies, static_cast<const float*>(dval),
-                  static_cast<const float*>(e), cgt, ceq, rgt, req));
-    EF_TRY(launch("topk_emit_scan", k_emit_scan, dim3(static_cast<unsigned>(nseg)), dim3(kEmitScanBlock), s, plan,
-                  static_cast<const SegState*>(st), cgt, ceq, rgt, req));
+                  static_cast<const float*>(e), btot));
     EF_TRY(launch("topk_write", stats ? k_write<true> : k_write<false>, hgrid, dim3(kBlock), s, plan, nseg, hb,
                   static_cast<const SegState*>(st), static_cast<const float*>(dval),
-                  static_cast<const int32_t*>(didx), static_cast<const uint32_t*>(cgt),
-                  static_cast<const uint32_t*>(ceq), static_cast<const uint32_t*>(rgt),
-                  static_cast<const uint32_t*>(req), e, vals, idx, cpart, rpart, stray));
+                  static_cast<const int32_t*>(didx), static_cast<const uint2*>(btot), e, vals, idx, cpart,
+                  rpart, stray));
     return finish_stats();
 }
 
