@@ -99,18 +99,26 @@ constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
 constexpr int kChunk = EFG_CHUNK;                  // entries per block-unit in select and emit
 static_assert(kChunk % kBlock == 0, "k_write: each wave takes kChunk / kBlock rows of 64 entries");
 constexpr int kRadixBins = 2048;
+constexpr int kSpec = 2;  // first digits the exact fallback guesses T's among (second-digit histograms)
 // Every radix histogram keeps, after its fine bins, coarse bins of 32 fine
 // ones each (64 for the 11-bit first digit, 32 for the 10-bit ones): the
 // kernel that needs a tensor's digit finds it from the coarse bins and one
 // slice of 32 fine bins, instead of a digit launch reading every bin.
 constexpr int kCoarse = 64;
 constexpr int kHistWords = kRadixBins + kCoarse;
+// The last radix histogram of each select block is also kept whole, with the
+// block's count of keys above the digits fixed before it.
+constexpr int kBlockHistWords = 1024 + 64;  // 1024 bins, the count above the prefix, padding
 // A fallback tensor's elements are taken in units of kRawChunk (kRawSub
 // chunks of kChunk), so that its per-unit monitoring partials stay few
 // (79,346 units at 1.3e9 elements).
 constexpr int kRawSub = 8;
 constexpr int kRawChunk = kRawSub * kChunk;
 constexpr int kSelectBlocks = 2048;                // select / emit blocks shared out among the tensors
+// 2048 blocks of 256 threads are 8 waves per SIMD on 256 CUs: the histogram
+// and write kernels are held to the registers that let the whole grid run
+// at once (a second round for the blocks that do not fit would double them)
+constexpr int kSelectWaves = 8;
 constexpr int kHistCopies = 8;                     // copies of a histogram when a call has few tensors (1 or this)
 constexpr int64_t kCompactBlocksMax = 2048;        // compaction blocks the GPU holds at once (8 per CU)
 constexpr int kMaxGrid = 2048;
@@ -165,7 +173,12 @@ struct alignas(16) SegState {
     uint32_t p0, w0;    // top 11 key bits of T and the rank left below them (first select pass)
     uint32_t p1, w1;    // top 21 bits and the rank left (second select pass)
     uint32_t T, r;      // the k-th largest key and the ties kept (count pass)
-    uint32_t pad[6];
+    // exact fallback: the first digits [spec_lo, spec_lo + spec_n) that the
+    // sample's window [tlo, thi) spans, whose second-digit histograms the
+    // compaction builds with the first one; hit = 1 + the one that held T's
+    // (its histogram stands in for the first select pass), else 0
+    uint32_t spec_lo, spec_n, hit;
+    uint32_t pad[3];
 };
 static_assert(sizeof(SegState) == 64, "SegState layout");
 
@@ -215,7 +228,7 @@ struct Plan {
 struct Layout {
     size_t status, plan, rb, gbb, sbb, cbb, hb, static_end;
     size_t state, shist, rhist, grp_cnt, zero_end;
-    size_t region_cnt, cpair, dval, didx, btot, spart, gpart, cpart, rpart;
+    size_t region_cnt, cpair, dval, didx, bh, btot, spart, gpart, cpart, rpart;
     size_t total;
 };
 
@@ -237,14 +250,16 @@ static Layout make_layout(const Plan& p) {
     L.static_end = at;
     L.state = take(ns * sizeof(SegState));
     L.shist = take(ns * static_cast<size_t>(p.hcopies) * kSampleBins * 4);
-    L.rhist = take(3 * ns * static_cast<size_t>(p.hcopies) * kHistWords * 4);
+    L.rhist = take((3 + kSpec) * ns * static_cast<size_t>(p.hcopies) * kHistWords * 4);
     L.grp_cnt = take(static_cast<size_t>(p.G) * 4);
     L.zero_end = at;
     L.region_cnt = take(static_cast<size_t>(p.R) * 4);
     L.cpair = take(static_cast<size_t>(p.Ctot) * 8);
     L.dval = take(static_cast<size_t>(p.Ctot) * 4);
     L.didx = take(static_cast<size_t>(p.Ctot) * 4);
-    // per select block: its range's counts of keys above T and equal to T
+    // per select block: its last radix histogram, and its range's counts of
+    // keys above T and equal to T
+    L.bh = take(static_cast<size_t>(p.HB) * kBlockHistWords * 4);
     L.btot = take(static_cast<size_t>(p.HB) * 8);
     // monitoring partials (sent, dropped energy): per region, per candidate unit, per raw unit
     L.spart = take(static_cast<size_t>(p.R) * 16);
@@ -568,6 +583,10 @@ __global__ __launch_bounds__(kBlock) void k_sample_select(const SegPlan* __restr
     if (threadIdx.x == 0) {
         st[s].tlo = s_tlo;
         st[s].thi = s_thi;
+        // T very likely lies in [tlo, thi): its first digit among these
+        const uint32_t lo = s_tlo >> 20, hi = s_thi == kNoKey ? kRadixBins - 1 : (s_thi - 1) >> 20;
+        st[s].spec_lo = lo;
+        st[s].spec_n = hi - lo + 1 <= static_cast<uint32_t>(kSpec) ? hi - lo + 1 : 0u;
     }
 }
 
@@ -884,6 +903,39 @@ __device__ __forceinline__ void wave_find_digit(const uint32_t* gh0, int32_t hco
     *above = above_c + __shfl(cum2, L2, kWave) - __shfl(fv, L2, kWave);
 }
 
+// Calls f(key, ok) for the keys of x[lo, hi), a range that the block reads
+// as a whole: 128-bit non-temporal loads (R per thread in flight, all issued
+// before any is used) over the 16-byte aligned body, one element per thread
+// for the head and tail.  ok is false for the padding a thread's last loads
+// read past the body; f must do nothing then.  Order is not index order.
+template <int R, class F>
+__device__ __forceinline__ void for_keys(const float* __restrict__ x, int64_t lo, int64_t hi, F&& f) {
+    const int t = threadIdx.x;
+    const int64_t a = min(hi, (lo + 3) & ~static_cast<int64_t>(3));
+    const int64_t b = max(a, hi & ~static_cast<int64_t>(3));
+    if (t < a - lo) f(key_of(x[lo + t]), true);
+    if (t < hi - b) f(key_of(x[b + t]), true);
+    const f4* __restrict__ x4 = reinterpret_cast<const f4*>(x + a);
+    const int64_t nv = (b - a) >> 2;
+    for (int64_t v0 = 0; v0 < nv; v0 += static_cast<int64_t>(kBlock) * R) {
+        f4 w[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) w[r] = __builtin_nontemporal_load(x4 + min(v0 + r * kBlock + t, nv - 1));
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const bool ok = v0 + r * kBlock + t < nv;
+            f(key_of(w[r].x), ok);
+            f(key_of(w[r].y), ok);
+            f(key_of(w[r].z), ok);
+            f(key_of(w[r].w), ok);
+        }
+    }
+}
+#ifndef EFG_RAW_LOADS
+#define EFG_RAW_LOADS 6
+#endif
+constexpr int kRawLoads = EFG_RAW_LOADS;  // 128-bit loads per thread in flight in the passes over x
+
 // 3. compaction, one block per group of kGroup regions (compact_split blocks
 //    per group for tensors with many expected candidates, each taking a slice
 //    of the group's regions).  Every block first sums its tensor's group
@@ -901,7 +953,6 @@ __device__ __forceinline__ void wave_find_digit(const uint32_t* gh0, int32_t hco
 //    cleared it (those reads saw +0: the histogram moves each such element
 //    from bin 0 to its own bin).
 constexpr int kCompactItems = 8;
-constexpr int kRawRows = 16;
 constexpr int kRecollectRows = 8;
 __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ plan, int32_t nseg,
                                                     const int32_t* __restrict__ cbb, const int32_t* __restrict__ gbb,
@@ -914,6 +965,7 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
                                                     uint32_t* __restrict__ stray, uint32_t force_fallback) {
     __shared__ uint32_t loff[kGroup];
     __shared__ uint32_t h[kRadixBins];
+    __shared__ uint32_t hs[kSpec][1024];  // exact fallback: second-digit histograms of the guessed first digits
     __shared__ uint32_t lds[kWavesPerBlock + 1];
     __shared__ uint32_t red[2][kWavesPerBlock];
     const int b = blockIdx.x;
@@ -958,19 +1010,21 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
     const int re = min(nr, rs + slice);
     if (rs >= re) return;
     const int64_t cap = P.cap;
+    const uint32_t spec_lo = st[s].spec_lo, spec_n = st[s].spec_n;
     if (fb) {
-        // the first radix histogram of x over the block's elements [a, z); e
-        // reads +0 where the stream cleared a stored candidate
+        // the first radix histogram of x over the block's elements [a, z),
+        // and the second-digit ones of the guessed first digits; e reads +0
+        // where the stream cleared a stored candidate
+        for (int i = t; i < kSpec * 1024; i += kBlock) hs[i / 1024][i % 1024] = 0;
+        __syncthreads();
         const int64_t a = P.off + (static_cast<int64_t>(gl) * kGroup + rs) * kRegion;
         const int64_t z = P.off + min((static_cast<int64_t>(gl) * kGroup + re) * kRegion, P.n);
-        for (int64_t i0 = a + t; i0 < z; i0 += kBlock * kRawRows) {
-            float x[kRawRows];
-#pragma unroll
-            for (int u = 0; u < kRawRows; ++u) x[u] = e[min(i0 + u * kBlock, z - 1)];
-#pragma unroll
-            for (int u = 0; u < kRawRows; ++u)
-                if (i0 + u * kBlock < z) atomicAdd(&h[key_of(x[u]) >> 20], 1u);
-        }
+        for_keys<kRawLoads>(e, a, z, [&](uint32_t key, bool ok) {
+            if (!ok) return;
+            atomicAdd(&h[key >> 20], 1u);
+            const uint32_t j = (key >> 20) - spec_lo;
+            if (j < spec_n) atomicAdd(&hs[j][(key >> 10) & 1023u], 1u);
+        });
         __syncthreads();  // every read of e is done before x is put back
         const uint32_t thi = st[s].thi;
         const int64_t lo = P.off, hi = P.off + P.n;
@@ -989,6 +1043,9 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
                         e[pr.y] = v;
                         atomicSub(&h[0], 1u);
                         atomicAdd(&h[key >> 20], 1u);
+                        if (spec_lo == 0 && spec_n > 0) atomicSub(&hs[0][0], 1u);
+                        const uint32_t j = (key >> 20) - spec_lo;
+                        if (j < spec_n) atomicAdd(&hs[j][(key >> 10) & 1023u], 1u);
                     } else {
                         atomicAdd(stray, 1u);
                     }
@@ -1069,6 +1126,9 @@ __global__ __launch_bounds__(kBlock) void k_compact(const SegPlan* __restrict__ 
         }
     }
     flush_hist(h, kRadixBins, radix_hist(rhist, 0, s, b % hcopies, nseg, hcopies));
+    if (fb)
+        for (uint32_t j = 0; j < spec_n; ++j)
+            flush_hist(hs[j], 1024, radix_hist(rhist, 3 + static_cast<int>(j), s, b % hcopies, nseg, hcopies));
 }
 
 // Radix digit of `key` in pass p (11, 10, 10 bits from the top) and whether the
@@ -1169,7 +1229,10 @@ __device__ __forceinline__ void digits_before(int pass, int s, int lb, const Seg
                                               SegState* st, const uint32_t* rhist, int32_t hcopies,
                                               uint32_t* prefix, uint32_t* want) {
     uint32_t d, above;
-    const uint32_t* gh = radix_hist(const_cast<uint32_t*>(rhist), pass - 1, s, 0, nseg, hcopies);
+    // the previous pass's histogram: after a hit, the guessed first digit's
+    // second-digit histogram stands in for the first select pass's
+    const int slot = (pass == 2 && st[s].hit) ? 2 + static_cast<int>(st[s].hit) : pass - 1;
+    const uint32_t* gh = radix_hist(const_cast<uint32_t*>(rhist), slot, s, 0, nseg, hcopies);
     if (pass == 1) {
         const uint32_t k = static_cast<uint32_t>(plan[s].k);
         wave_find_digit(gh, hcopies, 2048, k, &d, &above);
@@ -1200,46 +1263,77 @@ __device__ __forceinline__ void digits_before(int pass, int s, int lb, const Seg
     }
 }
 
-// 5. radix histograms of passes 1 and 2 (pass 0 came with the compaction)
+
+// 5. radix histograms of passes 1 and 2 (pass 0 came with the compaction),
+//    each block over its contiguous range of units (of x itself: one
+//    element range).  Pass 2 also leaves, per block, its own histogram and
+//    its count of keys above the pass's prefix (bh, kBlockHistWords words
+//    each): k_count takes the block's counts above T and at T from them
+//    instead of reading its entries again.
 __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
                                                  const int32_t* __restrict__ hb, SegState* __restrict__ st,
                                                  const float* __restrict__ dval, const float* __restrict__ e,
-                                                 uint32_t* __restrict__ rhist, int32_t hcopies) {
+                                                 uint32_t* __restrict__ rhist, int32_t hcopies,
+                                                 uint32_t* __restrict__ bh) {
     __shared__ uint32_t h[1024];
+    __shared__ uint32_t s_above[kWavesPerBlock];
     const SelBlock sb = sel_block(plan, nseg, hb, st);
-    if (sb.lb > 0 && static_cast<uint32_t>(sb.lb) >= sb.units) return;
+    if (sb.u0 >= sb.u1) return;  // never the tensor's first block, which records the digits
     uint32_t prefix, want;
     digits_before(pass, sb.s, sb.lb, plan, nseg, st, rhist, hcopies, &prefix, &want);
-    if (static_cast<uint32_t>(sb.lb) >= sb.units) return;
+    if (pass == 1 && sb.raw && prefix - st[sb.s].spec_lo < st[sb.s].spec_n) {
+        // exact fallback, first digit guessed right: the compaction built this pass's histogram
+        if (sb.lb == 0 && threadIdx.x == 0) st[sb.s].hit = 1u + (prefix - st[sb.s].spec_lo);
+        return;
+    }
     for (int i = threadIdx.x; i < 1024; i += kBlock) h[i] = 0;
     __syncthreads();
     const SegPlan& P = plan[sb.s];
     const SegState& S = st[sb.s];
-    const int nsub = sb.raw ? kRawSub : 1;
-    for (uint32_t u = sb.lb; u < sb.units; u += sb.nb) {
-        for (int j = 0; j < nsub; ++j) {
-            const Chunk c = chunk_of(P, S, sb.raw, u, j, dval, nullptr, e);
-            if (c.cnt == 0) break;
+    uint32_t above = 0;  // pass 2: keys whose top 21 bits are above the prefix
+    auto add = [&](uint32_t key, bool ok) {
+        uint32_t d;
+        if (ok && radix_digit(pass, key, prefix, &d)) atomicAdd(&h[d], 1u);
+        if (pass == 2) above += (ok && (key >> 10) > prefix) ? 1u : 0u;
+    };
+    if (sb.raw) {
+        const int64_t lo = P.off + static_cast<int64_t>(sb.u0) * kRawChunk;
+        const int64_t hi = P.off + min(static_cast<int64_t>(sb.u1) * kRawChunk, P.n);
+        for_keys<kRawLoads>(e, lo, hi, add);
+    } else {
+        for (uint32_t u = sb.u0; u < sb.u1; ++u) {
+            const Chunk c = chunk_of(P, S, false, u, 0, dval, nullptr, e);
             float v[kRows];
             const uint32_t j0 = load_rows(c, v);
 #pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                uint32_t d;
-                if (j0 + i * kWave < c.cnt && radix_digit(pass, key_of(v[i]), prefix, &d)) atomicAdd(&h[d], 1u);
-            }
+            for (int i = 0; i < kRows; ++i) add(key_of(v[i]), j0 + i * kWave < c.cnt);
         }
     }
     flush_hist(h, 1024, radix_hist(rhist, pass, sb.s, blockIdx.x % hcopies, nseg, hcopies));
+    if (pass == 2) {
+        above = wave_sum(above);
+        if (lane() == 0) s_above[threadIdx.x / kWave] = above;
+        __syncthreads();
+        uint32_t* mine = bh + static_cast<size_t>(blockIdx.x) * kBlockHistWords;
+        for (int i = threadIdx.x; i < 1024; i += kBlock) mine[i] = h[i];
+        if (threadIdx.x == 0) {
+            uint32_t t = 0;
+            for (int i = 0; i < kWavesPerBlock; ++i) t += s_above[i];
+            mine[1024] = t;
+        }
+    }
 }
 
 // 6a. per block: the counts of keys above T and equal to T in its range of
-//     units (every block of the tensor writes its word, 0 for an empty range)
+//     units (every block of the tensor writes its word, 0 for an empty
+//     range), from the block's pass-2 histogram: above T are the keys above
+//     the pass's prefix and those in the bins above T's last digit; at T,
+//     that digit's bin.
 __global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ plan, int32_t nseg,
                                                   const int32_t* __restrict__ hb, SegState* __restrict__ st,
                                                   const uint32_t* __restrict__ rhist, int32_t hcopies,
-                                                  const float* __restrict__ dval, const float* __restrict__ e,
-                                                  uint2* __restrict__ btot) {
-    __shared__ uint32_t sa[kWavesPerBlock], sbq[kWavesPerBlock];
+                                                  const uint32_t* __restrict__ bh, uint2* __restrict__ btot) {
+    __shared__ uint32_t lds[kWavesPerBlock + 1];
     const SelBlock sb = sel_block(plan, nseg, hb, st);
     if (sb.u0 >= sb.u1) {  // never the tensor's first block, which records T and r
         if (threadIdx.x == 0) btot[blockIdx.x] = make_uint2(0u, 0u);
@@ -1247,39 +1341,151 @@ __global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ pl
     }
     uint32_t T, r;
     digits_before(3, sb.s, sb.lb, plan, nseg, st, rhist, hcopies, &T, &r);
-    const SegPlan& P = plan[sb.s];
-    const SegState& S = st[sb.s];
-    const int nsub = sb.raw ? kRawSub : 1;
-    uint32_t a = 0, b = 0;
-    for (uint32_t u = sb.u0; u < sb.u1; ++u) {
-        for (int j = 0; j < nsub; ++j) {
-            const Chunk c = chunk_of(P, S, sb.raw, u, j, dval, nullptr, e);
-            if (c.cnt == 0) break;
-            float v[kRows];
-            const uint32_t j0 = load_rows(c, v);
+    const uint32_t d = T & 1023u;
+    const uint32_t* mine = bh + static_cast<size_t>(blockIdx.x) * kBlockHistWords;
+    uint32_t a = 0;
+    for (uint32_t i = d + 1 + threadIdx.x; i < 1024; i += kBlock) a += mine[i];
+    uint32_t tot;
+    (void)block_excl_scan<kBlock>(a, lds, &tot);
+    if (threadIdx.x == 0) btot[blockIdx.x] = make_uint2(tot + mine[1024], mine[d]);
+}
+
+// The exact fallback's write over x (in e) for one block's range of raw
+// units, in chunks of kWChunk elements: wave w takes rows w kWRows ..
+// (w + 1) kWRows - 1 of 256 elements, lane l elements 4l .. 4l + 3 of a row
+// (one 128-bit load when the tensor starts 16-byte aligned, else four
+// scalar loads).  Entries are thus ordered (wave, row, lane, element): an
+// entry's place counts the block's entries before the chunk, the chunk's
+// earlier waves (LDS exchange), the wave's earlier rows, the row's lower
+// lanes (one ballot per element position) and the lane's earlier elements.
+// A first sweep counts with ballots and marks the rows that hold any key >=
+// T; only those are placed (every row, when the statistics need each
+// entry's fate).  Kept entries get e = +0; nothing else changes (thi plays
+// no part: the compaction put x back everywhere).
+constexpr int kWRows = 2;                     // rows of 256 elements per wave and chunk
+constexpr int kWChunk = kBlock * 4 * kWRows;  // 4096 elements
+static_assert(kRawChunk % kWChunk == 0, "raw units are whole write chunks");
+
+template <bool STATS>
+__device__ __forceinline__ void write_raw(const SegPlan& P, const SelBlock& sb, uint32_t T, uint32_t r,
+                                          uint32_t gtu, uint32_t equ, uint32_t* wgt, uint32_t* weq,
+                                          double2* lsum, float* __restrict__ e, float* __restrict__ vals,
+                                          int32_t* __restrict__ idx, double2* __restrict__ part) {
+    const int wv = threadIdx.x / kWave;
+    const int l = lane();
+    const bool al = (P.off & 3) == 0;
+    const int64_t lo = P.off + static_cast<int64_t>(sb.u0) * kRawChunk;
+    const int64_t end = min(P.off + static_cast<int64_t>(sb.u1) * kRawChunk, P.off + P.n);
+    const int wo = wv * (kWRows * 256) + 4 * l;  // lane's first offset in the chunk, row 0
+    double sent = 0.0, drop = 0.0;
+    for (int64_t c0 = lo; c0 < end; c0 += kWChunk) {
+        const int rem = static_cast<int>(min(end - c0, static_cast<int64_t>(kWChunk)));  // entries in the chunk
+        float* ec = e + c0;
+        float x[kWRows][4];
 #pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                const bool ok = j0 + i * kWave < c.cnt;
-                const uint32_t key = key_of(v[i]);
-                a += ok && key > T;
-                b += ok && key == T;
+        for (int i = 0; i < kWRows; ++i) {
+            const int o = wo + i * 256;
+            if (al && o + 3 < rem) {
+                const f4 q = __builtin_nontemporal_load(reinterpret_cast<const f4*>(ec + o));
+                x[i][0] = q.x;
+                x[i][1] = q.y;
+                x[i][2] = q.z;
+                x[i][3] = q.w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[i][c] = o + c < rem ? ec[o + c] : 0.0f;
             }
         }
-    }
-    a = wave_sum(a);
-    b = wave_sum(b);
-    if (lane() == 0) {
-        sa[threadIdx.x / kWave] = a;
-        sbq[threadIdx.x / kWave] = b;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t ta = 0, tb = 0;
-        for (int i = 0; i < kWavesPerBlock; ++i) {
-            ta += sa[i];
-            tb += sbq[i];
+        // sweep 1: the wave's counts, and its rows holding a key >= T
+        uint32_t ngt = 0, neq = 0;
+        uint32_t rows = 0;  // bit i: row i holds a key >= T (wave-uniform)
+#pragma unroll
+        for (int i = 0; i < kWRows; ++i) {
+            uint64_t any = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool ok = wo + i * 256 + c < rem;
+                const uint32_t key = key_of(x[i][c]);
+                const uint64_t bg = __ballot(ok && key > T), be = __ballot(ok && key == T);
+                ngt += popc64(bg);
+                neq += popc64(be);
+                any |= bg | be;
+            }
+            rows |= any ? (1u << i) : 0u;
         }
-        btot[blockIdx.x] = make_uint2(ta, tb);
+        if (l == 0) {
+            wgt[wv] = ngt;
+            weq[wv] = neq;
+        }
+        __syncthreads();
+        uint32_t gtb = gtu, eqb = equ;
+        for (int i = 0; i < kWavesPerBlock; ++i) {
+            if (i < wv) {
+                gtb += wgt[i];
+                eqb += weq[i];
+            }
+            gtu += wgt[i];
+            equ += weq[i];
+        }
+        __syncthreads();  // wgt / weq are rewritten by the next chunk
+        // sweep 2: places
+#pragma unroll
+        for (int i = 0; i < kWRows; ++i) {
+            if (!STATS && !(rows & (1u << i))) continue;
+            const int o = wo + i * 256;
+            uint32_t gb = gtb, eb = eqb;  // the row's entries before this lane's first
+            uint32_t tg = 0, te = 0;      // the row's totals
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool ok = o + c < rem;
+                const uint32_t key = key_of(x[i][c]);
+                const uint64_t bg = __ballot(ok && key > T), be = __ballot(ok && key == T);
+                gb += count_below(bg);
+                eb += count_below(be);
+                tg += popc64(bg);
+                te += popc64(be);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool ok = o + c < rem;
+                const uint32_t key = key_of(x[i][c]);
+                const bool gt = ok && key > T, eq = ok && key == T;
+                int64_t pos = -1;
+                if (gt) pos = static_cast<int64_t>(gb) + min(r, eb);
+                else if (eq && eb < r) pos = static_cast<int64_t>(gb) + eb;
+                gb += gt ? 1u : 0u;
+                eb += eq ? 1u : 0u;
+                if (STATS && ok) {
+                    if (pos >= 0) sent += sq_finite(x[i][c], key);
+                    else drop += sq_finite(x[i][c], key);
+                }
+                if (pos >= 0 && pos < P.k) {
+                    vals[P.out_off + pos] = x[i][c];
+                    idx[P.out_off + pos] = static_cast<int32_t>(c0 + o + c);
+                    ec[o + c] = 0.0f;
+                }
+            }
+            gtb += tg;
+            eqb += te;
+        }
+        // a unit ends with this chunk: its partial, a fixed-order block sum
+        if (STATS && ((c0 + kWChunk - lo) % kRawChunk == 0 || c0 + kWChunk >= end)) {
+            sent = wave_sum(sent);
+            drop = wave_sum(drop);
+            if (l == 0) lsum[wv] = make_double2(sent, drop);
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                double2 t = make_double2(0.0, 0.0);
+                for (int i = 0; i < kWavesPerBlock; ++i) {
+                    t.x += lsum[i].x;
+                    t.y += lsum[i].y;
+                }
+                part[sb.u0 + static_cast<uint32_t>((c0 - lo) / kRawChunk)] = t;
+            }
+            __syncthreads();
+            sent = 0.0;
+            drop = 0.0;
+        }
     }
 }
 
@@ -1334,6 +1540,10 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
     const int64_t seg_lo = P.off, seg_hi = P.off + P.n;
     const int nsub = sb.raw ? kRawSub : 1;
     double2* part = sb.raw ? (rpart ? rpart + P.runit_base : nullptr) : (cpart ? cpart + P.cunit_base : nullptr);
+    if (sb.raw) {
+        write_raw<STATS>(P, sb, T, r, gtu, equ, wgt, weq, lsum, e, vals, idx, part);
+        return;
+    }
     for (uint32_t u = sb.u0; u < sb.u1; ++u) {  // gtu, equ: counts before the next chunk
         double sent = 0.0, drop = 0.0;
         for (int j = 0; j < nsub; ++j) {
@@ -1591,6 +1801,7 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
     float* dval = reinterpret_cast<float*>(at(L.dval));
     int32_t* didx = reinterpret_cast<int32_t*>(at(L.didx));
     uint2* btot = reinterpret_cast<uint2*>(at(L.btot));
+    uint32_t* bh = reinterpret_cast<uint32_t*>(at(L.bh));
     double2* spart = reinterpret_cast<double2*>(at(L.spart));
     double2* cpart = stats ? reinterpret_cast<double2*>(at(L.cpart)) : nullptr;
     double2* rpart = stats ? reinterpret_cast<double2*>(at(L.rpart)) : nullptr;
@@ -1637,10 +1848,9 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
     const dim3 hgrid(static_cast<unsigned>(P.HB));
     for (int pass = 1; pass < 3; ++pass)
         EF_TRY(launch("topk_hist", k_hist, hgrid, dim3(kBlock), s, pass, plan, nseg, hb, st,
-                      static_cast<const float*>(dval), static_cast<const float*>(e), rhist, P.hcopies));
+                      static_cast<const float*>(dval), static_cast<const float*>(e), rhist, P.hcopies, bh));
     EF_TRY(launch("topk_count", k_count, hgrid, dim3(kBlock), s, plan, nseg, hb, st,
-                  static_cast<const uint32_t*>(rhist), P.hcopies, static_cast<const float*>(dval),
-                  static_cast<const float*>(e), btot));
+                  static_cast<const uint32_t*>(rhist), P.hcopies, static_cast<const uint32_t*>(bh), btot));
     EF_TRY(launch("topk_write", stats ? k_write<true> : k_write<false>, hgrid, dim3(kBlock), s, plan, nseg, hb,
                   static_cast<const SegState*>(st), static_cast<const float*>(dval),
                   static_cast<const int32_t*>(didx), static_cast<const uint2*>(btot), e, vals, idx, cpart,

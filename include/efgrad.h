@@ -114,7 +114,7 @@ int ef_topk_workspace_status(const void* ws, uint32_t* stray, void* stream);
  * looks its address up (hipGetSymbolAddress).  A call whose scratch need,
  * ef_topk_workspace_bytes(n, k), exceeds the array returns EF_EWS before
  * enqueueing anything (n = 1e6, k = 1e4 needs 1.2 MB; n = 2^26, k = 2^16
- * 14 MB).  The call makes no hipMalloc, hipFree or other allocating call; a
+ * 23 MB).  The call makes no hipMalloc, hipFree or other allocating call; a
  * one-tensor plan is built on the host stack.  Every call on one GPU uses
  * that GPU's array and leaves its contents behind (each call clears what it
  * needs cleared): calls that can overlap on one GPU (different streams) race
