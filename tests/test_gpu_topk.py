@@ -63,9 +63,9 @@ def test_forced_fallback(n, k, kind):
 
 
 def test_forced_fallback_many_units():
-    """The exact path over 20,000,003 elements: about 9,800 units of the select
-    kernels, so the per-tensor scan of their counts spans more than one
-    8192-unit tile, and the last unit is ragged."""
+    """The exact path over 20,000,003 elements: 1,221 units of 16,384 shared
+    out among the write blocks in contiguous ranges (each block's place in
+    the output is the totals of the blocks before it), the last unit ragged."""
     n, k = 20_000_003, 20_000
     g, e = inputs(n, "lognormal", 7)
     say(f"forced fallback n={n} k={k}")
