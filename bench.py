@@ -10,8 +10,10 @@ resident in HBM.
 
 Prints one JSON line: elements/s of the whole step, HBM roofline of the
 streaming kernel (12 algorithmic bytes per element: read g, read e, write e)
-timed with HIP events on its own stream inside the timed region, and the CPU
-oracle on a bounded sample of the same workload.
+timed with HIP events that its own dispatches record on the library's
+stream, over the timed region's K steps run once more right after it
+(events on each launch slow the issue of a short step, so the timed steps
+carry none), and the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -35,6 +37,7 @@ def log(*a):
 
 # committed rocprofv3 traffic summaries of the roofline kernel of other workloads
 TRAFFIC_PROFILES = {"random": "rs_accum_large_1p3e9_traffic", "adam": "onebit_update_adam_340m_traffic",
+                    "decode": "decode_sgd_25p6m_traffic",
                     "sign": "sign_ef_340m_traffic"}
 
 
@@ -177,7 +180,6 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    efg.profile_enable(True, "topk_stream")
     torch.cuda.synchronize()
     start.record(stream)
     for t in range(W, W + K):
@@ -185,8 +187,7 @@ def main():
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    stream_ms, launches = efg.profile_read("topk_stream")
-    efg.profile_enable(False)
+    stream_ms, launches = kernel_ms(step, range(W, W + K), "topk_stream")
     ms_per_step = total_ms / K
     stream_avg_ms = stream_ms / max(1, launches)
     achieved = STREAM_BYTES_PER_ELEM * n / (stream_avg_ms * 1e-3) / 1e9
@@ -390,26 +391,42 @@ def sign_bits_agree(sgn, bits):
     return torch.equal((pos.view(-1, 8) * w).sum(1).to(torch.uint8), bits)
 
 
-def time_steps(step, W, K, kernel_label):
-    """Runs W untimed and K timed steps; returns (ms per step, mean ms of the kernel
-    labelled kernel_label, its launch count) with HIP events on the current stream."""
+def kernel_ms(step, steps, kernel_label):
+    """The steps once more, right after the timed region, with every launch of
+    the kernels labelled kernel_label timed by a HIP event pair that its own
+    dispatch records (on the stream the library launches on): (total ms,
+    launches).  Kept out of the timed region: a launch that records events
+    takes longer to issue, which would show in a short step."""
     import torch
 
     import error_feedback_gradient_amd as efg
+
+    efg.profile_enable(True, kernel_label)
+    for t in steps:
+        step(t)
+    torch.cuda.synchronize()
+    ms, launches = efg.profile_read(kernel_label)
+    efg.profile_enable(False)
+    return ms, launches
+
+
+def time_steps(step, W, K, kernel_label):
+    """Runs W untimed and K timed steps (HIP events on the current stream), then
+    times the labelled kernel over the same K steps (kernel_ms); returns (ms per
+    step, ms of the labelled kernels per step, their launch count)."""
+    import torch
 
     for t in range(W):
         step(t)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    efg.profile_enable(True, kernel_label)
     torch.cuda.synchronize()
     start.record()
     for t in range(W, W + K):
         step(t)
     stop.record()
     torch.cuda.synchronize()
-    kms, launches = efg.profile_read(kernel_label)
-    efg.profile_enable(False)
+    kms, launches = kernel_ms(step, range(W, W + K), kernel_label)
     # time of the labelled kernels per step (equal to the mean launch when one kernel matches)
     return start.elapsed_time(stop) / K, kms / K, launches
 

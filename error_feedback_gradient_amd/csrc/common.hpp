@@ -1,6 +1,7 @@
 // Shared host and device helpers of libefgrad (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -15,12 +16,13 @@ namespace efg {
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int check_launch(const char* label);
 
-// Event pair around one launch when profiling is on (see ef_profile_enable).
+// Event pair of one launch when profiling is on (see ef_profile_enable): the
+// launch records both with the dispatch itself (hipExtLaunchKernelGGL), so
+// their interval is the kernel's own run, without marker packets around it.
+// Nothing is recorded on a stream under graph capture.
 struct ProfScope {
-    int slot = -1;
-    hipStream_t stream;
+    hipEvent_t start = nullptr, stop = nullptr;
     ProfScope(const char* label, hipStream_t s);
-    ~ProfScope();
 };
 
 template <typename... KArgs, typename... Args>
@@ -28,7 +30,10 @@ inline int launch(const char* label, void (*kernel)(KArgs...), dim3 grid, dim3 b
                   hipStream_t s, Args... args) {
     if (grid.x == 0 || grid.y == 0 || grid.z == 0) return EF_OK;
     ProfScope ps(label, s);
-    kernel<<<grid, block, 0, s>>>(static_cast<KArgs>(args)...);
+    if (ps.start)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ps.start, ps.stop, 0u, static_cast<KArgs>(args)...);
+    else
+        kernel<<<grid, block, 0, s>>>(static_cast<KArgs>(args)...);
     return check_launch(label);
 }
 

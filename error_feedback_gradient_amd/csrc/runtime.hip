@@ -51,8 +51,10 @@ void prof_clear_locked() {
 }
 }  // namespace
 
-ProfScope::ProfScope(const char* label, hipStream_t s) : stream(s) {
+ProfScope::ProfScope(const char* label, hipStream_t s) {
     if (!g_prof_armed.load(std::memory_order_acquire)) return;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof_on) return;
     if (!g_prof_only.empty() && !strstr(label, g_prof_only.c_str())) return;
@@ -66,15 +68,9 @@ ProfScope::ProfScope(const char* label, hipStream_t s) : stream(s) {
         if (hipEventCreate(&r.start) != hipSuccess) return;
         if (hipEventCreate(&r.stop) != hipSuccess) { (void)hipEventDestroy(r.start); return; }
     }
-    (void)hipEventRecord(r.start, s);
     g_prof.push_back(r);
-    slot = static_cast<int>(g_prof.size()) - 1;
-}
-
-ProfScope::~ProfScope() {
-    if (slot < 0) return;
-    std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (slot < static_cast<int>(g_prof.size())) (void)hipEventRecord(g_prof[slot].stop, stream);
+    start = r.start;
+    stop = r.stop;
 }
 
 // ------------------------------------------------------------------ utilities
