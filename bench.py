@@ -127,7 +127,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--n", type=int, default=None, help="override N (testing only)")
     ap.add_argument("--k", type=int, default=None, help="override k (testing only)")
-    ap.add_argument("--cpu-sample", type=int, default=40_000_000)
+    ap.add_argument("--cpu-sample", type=int, default=80_000_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stats", action="store_true", help="also compute the fused monitoring statistics")
     ap.add_argument("--workload", default="large", choices=["large", "flat", "bert", "sign", "decode", "quant", "random", "adam"],
