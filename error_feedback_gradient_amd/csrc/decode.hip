@@ -340,6 +340,16 @@ __device__ __forceinline__ bool apply_entry(float* acc, uint32_t* touched, const
 #ifndef EFG_DECODE_WAVES
 #define EFG_DECODE_WAVES 1
 #endif
+// The run of tiles of block b.  Blocks are dealt to the eight XCDs in turn
+// (block b to XCD b mod 8); here the blocks of one XCD take consecutive runs,
+// so the bound searches of neighbouring runs, which probe nearby lines of
+// every packet's indices, meet in that XCD's L2 instead of eight.  A
+// bijection of [0, nb) for any nb.
+__device__ __forceinline__ int64_t xcd_run(int64_t b, int64_t nb) {
+    constexpr int64_t kXcds = 8;
+    const int64_t q = nb / kXcds, rem = nb % kXcds, x = b % kXcds, j = b / kXcds;
+    return x * q + min(x, rem) + j;
+}
 template <bool FUSED, int SLOTS>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(EFG_DECODE_WAVES))) void k_decode_tiles(float* __restrict__ G, int64_t n, int32_t npk,
                                                          const float* __restrict__ vals,
@@ -355,8 +365,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(EFG_DECO
     __shared__ int64_t p_beg[kMaxPk];
     __shared__ uint32_t lds[kBlock / kWave + 1];
 
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * ntiles / gridDim.x;
-    const int64_t t1 = static_cast<int64_t>(blockIdx.x + 1) * ntiles / gridDim.x;
+    const int64_t run = xcd_run(blockIdx.x, gridDim.x);
+    const int64_t t0 = run * ntiles / gridDim.x;
+    const int64_t t1 = (run + 1) * ntiles / gridDim.x;
     const int tid = threadIdx.x, grp = tid / kSearchLanes, gl = tid % kSearchLanes;
     const int g0 = static_cast<int>(lane()) & ~(kSearchLanes - 1);  // the group's first lane in the wave
     for (int i = tid; i < kTile; i += kBlock) {
@@ -630,7 +641,11 @@ __global__ __launch_bounds__(kBlock) void k_sgd(float* __restrict__ w, const flo
 }
 
 // Blocks of the multi-tile kernel that the GPU holds at once (its LDS use
-// sets that), asked once per kernel and device.
+// sets that; at most EFG_DECODE_PER_CU per CU when that is set), asked once
+// per kernel and device.
+#ifndef EFG_DECODE_PER_CU
+#define EFG_DECODE_PER_CU 0
+#endif
 template <bool FUSED, int SLOTS>
 static int resident_blocks(int64_t* out) {
     static int cached[64] = {0};
@@ -643,6 +658,7 @@ static int resident_blocks(int64_t* out) {
                 hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return fail(EF_EHIP, "decode: occupancy query failed");
+        if (EFG_DECODE_PER_CU > 0) per_cu = std::min(per_cu, EFG_DECODE_PER_CU);
         cached[dev] = std::max(1, per_cu) * std::max(1, cus);
     }
     *out = cached[dev];
