@@ -72,7 +72,11 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 #endif
 constexpr int kStreamBlock = EFG_STREAM_BLOCK;     // threads of the streaming kernel
 constexpr int kStreamWaves = kStreamBlock / kWave;
-constexpr int64_t kFewRegions = 4096;             // below: one-wave stream blocks, one copy of each histogram
+constexpr int64_t kFewRegions = 4096;             // below: split stream blocks, one copy of each histogram
+#ifndef EFG_SPLIT
+#define EFG_SPLIT 8
+#endif
+constexpr int kSplit = EFG_SPLIT;                  // waves per region in the split streaming pass
 constexpr int kRegion = EFG_STREAM_REGION;         // elements per wave in the streaming pass
 constexpr int kUnroll = EFG_STREAM_UNROLL;         // 128-bit loads in flight per lane and array
 constexpr int kGroup = 256;                        // regions per group (candidate totals, compaction)
@@ -825,6 +829,189 @@ __global__ __launch_bounds__(WAVES * kWave) void k_stream(const float* __restric
             sum += lcnt[i];
         }
         if (sum) atomicAdd(&grp_cnt[g0], sum);
+    }
+}
+
+// One wave's part [sb, se) of a region that starts at gbeg, in the split
+// streaming pass: the head and tail (at most three elements each, one per
+// lane) and the 16-byte aligned body, NV float4 of g and of e per lane, all
+// loaded before any is used.  Phase 1 counts the wave's candidates into
+// wcnt[wave]; after the block's barrier, phase 2 appends them to the
+// region's slot after the candidates of the block's earlier waves, in index
+// order (head, body rows, tail), and writes e.  *total comes back with the
+// region's candidate count.  Every thread of the block calls it.
+template <int MODE, bool STATS, int NV>
+__device__ __forceinline__ void stream_part(const float* __restrict__ g, float* __restrict__ e, int64_t gbeg,
+                                            int64_t sb, int64_t se, uint32_t tlo, uint32_t thi, uint32_t cap,
+                                            uint2* __restrict__ cp, float* __restrict__ vals,
+                                            int32_t* __restrict__ idx, int64_t out_base, uint32_t* wcnt,
+                                            uint32_t& total, uint32_t& nf, double& acc) {
+    const int q = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const int l = lane();
+    int64_t a = (sb + 3) & ~static_cast<int64_t>(3);
+    int64_t b = se & ~static_cast<int64_t>(3);
+    if (a > b) a = b = se;  // shorter than one aligned quad: all head
+    const int64_t nv = (b - a) >> 2;
+    const int64_t ih = sb + l, it = b + l;
+    const bool okh = ih < a, okt = it < se;
+    const f4* __restrict__ g4 = reinterpret_cast<const f4*>(g + a);
+    f4* __restrict__ e4 = reinterpret_cast<f4*>(e + a);
+    f4 gv[NV], ev[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        const int64_t j = u * kWave + l;
+        if (j < nv) {
+            gv[u] = __builtin_nontemporal_load(g4 + j);
+            ev[u] = __builtin_nontemporal_load(e4 + j);
+        } else {
+            gv[u] = f4{0.f, 0.f, 0.f, 0.f};
+            ev[u] = f4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const float xh = okh ? g[ih] + e[ih] : 0.0f;
+    const float xt = okt ? g[it] + e[it] : 0.0f;
+    f4 xb[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) xb[u] = gv[u] + ev[u];
+    // phase 1: the wave's candidates, non-finite values and known energy
+    uint32_t mine = 0;
+    auto note = [&](float x, bool ok) {
+        if (!ok) return;
+        const uint32_t key = key_of(x);
+        nf += key >= 0x7f800000u ? 1u : 0u;
+        const bool hit = MODE == MODE_NORMAL && key >= tlo;
+        mine += hit ? 1u : 0u;
+        if (STATS && !hit) acc += sq_finite(x, key);
+    };
+    note(xh, okh);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        const bool ok = u * kWave + l < nv;
+        note(xb[u].x, ok);
+        note(xb[u].y, ok);
+        note(xb[u].z, ok);
+        note(xb[u].w, ok);
+    }
+    note(xt, okt);
+    mine = wave_sum(mine);
+    if (l == 0) wcnt[q] = mine;
+    __syncthreads();
+    uint32_t cnt = 0;
+    total = 0;
+    for (int i = 0; i < nw; ++i) {
+        cnt += i < q ? wcnt[i] : 0u;
+        total += wcnt[i];
+    }
+    // phase 2: append after the earlier waves' candidates, write e
+    auto one = [&](float x, bool ok, int64_t i) {
+        const uint32_t key = key_of(x);
+        float xa[1] = {x};
+        bool ha[1] = {MODE == MODE_NORMAL && ok && key >= tlo};
+        bool sa[1] = {false};
+        if (MODE == MODE_NORMAL) append_hits<1>(xa, ha, i, cnt, cap, cp, sa);
+        if (ok) {
+            e[i] = stream_e<MODE>(x, key, sa[0], thi);
+            if (MODE == MODE_ALL) {
+                vals[out_base + (i - gbeg)] = x;
+                idx[out_base + (i - gbeg)] = static_cast<int32_t>(i);
+            }
+        }
+    };
+    one(xh, okh, ih);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        const int64_t j = u * kWave + l;
+        const bool ok = j < nv;
+        float xs[4] = {xb[u].x, xb[u].y, xb[u].z, xb[u].w};
+        uint32_t key[4];
+        bool hit[4], stored[4] = {false, false, false, false};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            key[t] = key_of(xs[t]);
+            hit[t] = MODE == MODE_NORMAL && ok && key[t] >= tlo;
+        }
+        if (MODE == MODE_NORMAL) append_hits<4>(xs, hit, a + 4 * j, cnt, cap, cp, stored);
+        if (ok) {
+            __builtin_nontemporal_store(f4{stream_e<MODE>(xs[0], key[0], stored[0], thi),
+                                           stream_e<MODE>(xs[1], key[1], stored[1], thi),
+                                           stream_e<MODE>(xs[2], key[2], stored[2], thi),
+                                           stream_e<MODE>(xs[3], key[3], stored[3], thi)},
+                                        e4 + j);
+            if (MODE == MODE_ALL) {
+                const int64_t i0 = a + 4 * j;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    vals[out_base + (i0 + t - gbeg)] = xs[t];
+                    idx[out_base + (i0 + t - gbeg)] = static_cast<int32_t>(i0 + t);
+                }
+            }
+        }
+    }
+    one(xt, okt, it);
+}
+
+// 2'. The streaming pass of a call with few regions (fewer than
+// kFewRegions): one block of SPLIT waves per region, wave q taking the
+// region's elements [q L, (q + 1) L), L = kRegion / SPLIT, so that a small
+// call still puts several waves on every CU.  The candidates land in the
+// region's slot in index order, as one wave over the region would put them
+// (stream_part); the block adds the region's count to its group total.
+template <bool STATS, int SPLIT>
+__global__ __launch_bounds__(SPLIT * kWave) void k_stream_split(const float* __restrict__ g, float* __restrict__ e,
+                                                               const SegPlan* __restrict__ plan, int32_t nseg,
+                                                               const int32_t* __restrict__ rb,
+                                                               SegState* __restrict__ st,
+                                                               uint32_t* __restrict__ region_cnt,
+                                                               uint32_t* __restrict__ grp_cnt,
+                                                               uint2* __restrict__ cpair, float* __restrict__ vals,
+                                                               int32_t* __restrict__ idx,
+                                                               uint32_t* __restrict__ nonfinite,
+                                                               double2* __restrict__ spart) {
+    constexpr int L = kRegion / SPLIT;
+    constexpr int NV = L / (4 * kWave);
+    static_assert(L % (4 * kWave) == 0, "a wave's part is whole rows of 64 float4");
+    __shared__ uint32_t wcnt[SPLIT];
+    __shared__ double wacc[SPLIT];
+    const int64_t w = blockIdx.x;  // the region (one block each)
+    const int q = threadIdx.x / kWave;
+    const int s = upper_index_wave(rb, nseg, static_cast<int32_t>(w));
+    const SegPlan& P = plan[s];
+    const int64_t rl = w - rb[s];
+    const int64_t lbeg = rl * kRegion;
+    const int64_t lend = min(lbeg + static_cast<int64_t>(kRegion), P.n);
+    const int64_t gbeg = P.off + lbeg, gend = P.off + lend;
+    const int64_t sb = min(gbeg + static_cast<int64_t>(q) * L, gend), se = min(sb + L, gend);
+    const uint32_t cap = static_cast<uint32_t>(P.cap);
+    uint2* cp = cpair + P.cand_base + rl * P.cap;
+    uint32_t total = 0, nf = 0;
+    double acc = 0.0;
+    if (P.mode == MODE_NORMAL) {
+        const uint32_t tlo = P.direct ? kNoKey : st[s].tlo;  // a direct (dense) selection collects nothing
+        const uint32_t thi = P.direct ? kNoKey : st[s].thi;
+        stream_part<MODE_NORMAL, STATS, NV>(g, e, gbeg, sb, se, tlo, thi, cap, cp, vals, idx, 0, wcnt, total, nf,
+                                            acc);
+    } else if (P.mode == MODE_ALL) {
+        stream_part<MODE_ALL, STATS, NV>(g, e, gbeg, sb, se, 0, 0, 0, cp, vals, idx, P.out_off + lbeg, wcnt, total,
+                                         nf, acc);
+    } else {
+        stream_part<MODE_NONE, STATS, NV>(g, e, gbeg, sb, se, 0, 0, 0, cp, vals, idx, 0, wcnt, total, nf, acc);
+    }
+    nf = wave_sum(nf);
+    if (lane() == 0 && nf && nonfinite) atomicAdd(nonfinite, nf);
+    if (STATS) {
+        acc = wave_sum(acc);
+        if (lane() == 0) wacc[q] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        region_cnt[w] = total;  // the true count: the slot holds the first min(total, cap)
+        if (total) atomicAdd(&grp_cnt[P.group_begin + static_cast<int32_t>(rl / kGroup)], total);
+        if (STATS) {
+            double t = 0.0;
+            for (int i = 0; i < SPLIT; ++i) t += wacc[i];
+            spart[w] = P.mode == MODE_ALL ? make_double2(t, 0.0) : make_double2(0.0, t);
+        }
     }
 }
 
@@ -1823,21 +2010,24 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
         EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
                       static_cast<const uint32_t*>(shist), P.hcopies, st));
     }
-    // A call with few regions streams them with one-wave blocks, so that they
-    // spread over every CU (the flat N = 1e6 call has 245 regions).
-    auto stream = [&](auto waves, auto stats_on) -> int {
-        constexpr int W = decltype(waves)::value;
-        constexpr bool ST = decltype(stats_on)::value;
-        return launch("topk_stream", k_stream<ST, W>, dim3(static_cast<unsigned>(cdiv(P.R, W))), dim3(W * kWave), s,
-                      g, e, plan, nseg, rb, P.R, st, region_cnt, grp_cnt, cpair, vals, idx, nonfinite, spart);
-    };
-    using Few = std::integral_constant<int, 1>;
-    using Many = std::integral_constant<int, kStreamWaves>;
+    // A call with few regions streams each with a block of kSplit waves, so
+    // that a small call still puts several waves on every CU (the flat N = 1e6
+    // call has 245 regions).
     const bool few = P.R < kFewRegions;
+    auto stream = [&](auto stats_on) -> int {
+        constexpr bool ST = decltype(stats_on)::value;
+        if (few)
+            return launch("topk_stream", k_stream_split<ST, kSplit>, dim3(static_cast<unsigned>(P.R)),
+                          dim3(kSplit * kWave), s, g, e, plan, nseg, rb, st, region_cnt, grp_cnt, cpair, vals, idx,
+                          nonfinite, spart);
+        return launch("topk_stream", k_stream<ST, kStreamWaves>, dim3(static_cast<unsigned>(cdiv(P.R, kStreamWaves))),
+                      dim3(kStreamWaves * kWave), s, g, e, plan, nseg, rb, P.R, st, region_cnt, grp_cnt, cpair, vals,
+                      idx, nonfinite, spart);
+    };
     if (stats)
-        EF_TRY(few ? stream(Few{}, std::true_type{}) : stream(Many{}, std::true_type{}));
+        EF_TRY(stream(std::true_type{}));
     else
-        EF_TRY(few ? stream(Few{}, std::false_type{}) : stream(Many{}, std::false_type{}));
+        EF_TRY(stream(std::false_type{}));
     if (!P.any_normal) return finish_stats();
 
     EF_TRY(launch("topk_compact", k_compact, dim3(static_cast<unsigned>(P.CB)), dim3(kBlock), s, plan, nseg,
