@@ -96,6 +96,10 @@ constexpr int kSampleBlockChunks = kSampleChunksPerWave * (kSampleBlock / kWave)
 constexpr int kSampleBlocksTarget = 1024;            // enough sample blocks to fill the chip
 constexpr int kSampleRoundsMax = 8;
 constexpr int kSampleBins = 4096;
+// After its fine bins every sample histogram keeps 64 coarse bins of 64 fine
+// ones each, so that one wave can find a rank in it with two reads.
+constexpr int kSampleCoarse = 64;
+constexpr int kSampleWords = kSampleBins + kSampleCoarse;
 constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
 #ifndef EFG_CHUNK
 #define EFG_CHUNK 2048
@@ -253,7 +257,7 @@ static Layout make_layout(const Plan& p) {
     at = round_up(at, 256);
     L.static_end = at;
     L.state = take(ns * sizeof(SegState));
-    L.shist = take(ns * static_cast<size_t>(p.hcopies) * kSampleBins * 4);
+    L.shist = take(ns * static_cast<size_t>(p.hcopies) * kSampleWords * 4);
     L.rhist = take((3 + kSpec) * ns * static_cast<size_t>(p.hcopies) * kHistWords * 4);
     L.grp_cnt = take(static_cast<size_t>(p.G) * 4);
     L.zero_end = at;
@@ -452,24 +456,21 @@ __global__ __launch_bounds__(kBlock) void k_init(uint4* zero, int64_t nvec, uint
     }
 }
 
-// 1. sample histogram of x = g + e on the top 12 key bits; each block takes
-//    `rounds` consecutive groups of kSampleBlockChunks chunks of its tensor
-__global__ __launch_bounds__(kSampleBlock) void k_sample(const float* __restrict__ g, const float* __restrict__ e,
-                                                   const SegPlan* __restrict__ plan, int32_t nseg,
-                                                   const int32_t* __restrict__ sbb, int32_t rounds,
-                                                   uint32_t* __restrict__ shist, int32_t hcopies) {
-    __shared__ uint32_t h[kSampleBins];
-    const int b = blockIdx.x;
-    const int s = upper_index_wave(sbb, nseg, b);
-    const int64_t off = plan[s].off, n = plan[s].n;
-    const int S = plan[s].sample_chunks;
-    const bool exhaustive = plan[s].exhaustive != 0;
+// The sample histogram (top 12 key bits of x = g + e) of one block's
+// `rounds` consecutive groups of kSampleBlockChunks chunks of a tensor
+// (block bl of the tensor), in the LDS histogram h, which it clears first.
+// Every thread of the block calls it; h is complete on return.
+__device__ __forceinline__ void sample_block(const float* __restrict__ g, const float* __restrict__ e,
+                                             const SegPlan& P, int bl, int32_t rounds, uint32_t* h) {
+    const int64_t off = P.off, n = P.n;
+    const int S = P.sample_chunks;
+    const bool exhaustive = P.exhaustive != 0;
     for (int i = threadIdx.x; i < kSampleBins; i += kSampleBlock) h[i] = 0;
     __syncthreads();
     const int w = threadIdx.x / kWave;
     const int l = lane();
     for (int rd = 0; rd < rounds; ++rd) {
-        const int c0 = ((b - sbb[s]) * rounds + rd) * kSampleBlockChunks + w * kSampleChunksPerWave;
+        const int c0 = (bl * rounds + rd) * kSampleBlockChunks + w * kSampleChunksPerWave;
         if (c0 >= S) break;  // wave-uniform: the rest of this block's chunks lie past the sample
         float xs[kSampleChunksPerWave][4];
         bool ok[kSampleChunksPerWave][4];
@@ -497,7 +498,31 @@ __global__ __launch_bounds__(kSampleBlock) void k_sample(const float* __restrict
                 if (ok[u][j]) atomicAdd(&h[key_of(xs[u][j]) >> kSampleShift], 1u);
     }
     __syncthreads();
-    uint32_t* gh = shist + (static_cast<size_t>(s) * hcopies + blockIdx.x % hcopies) * kSampleBins;
+}
+
+// Coarse bin c of an LDS sample histogram, read with a rotation so that the
+// lanes hit different banks.
+__device__ __forceinline__ uint32_t sample_coarse(const uint32_t* h, int c) {
+    uint32_t t = 0;
+    for (int i = 0; i < 64; ++i) t += h[c * 64 + ((i + c) & 63)];
+    return t;
+}
+
+// 1. sample histograms, each block adding its own to copy b % hcopies of its
+//    tensor's (fine bins, then the coarse sums)
+__global__ __launch_bounds__(kSampleBlock) void k_sample(const float* __restrict__ g, const float* __restrict__ e,
+                                                   const SegPlan* __restrict__ plan, int32_t nseg,
+                                                   const int32_t* __restrict__ sbb, int32_t rounds,
+                                                   uint32_t* __restrict__ shist, int32_t hcopies) {
+    __shared__ uint32_t h[kSampleBins];
+    const int b = blockIdx.x;
+    const int s = upper_index_wave(sbb, nseg, b);
+    sample_block(g, e, plan[s], b - sbb[s], rounds, h);
+    uint32_t* gh = shist + (static_cast<size_t>(s) * hcopies + blockIdx.x % hcopies) * kSampleWords;
+    for (int c = threadIdx.x; c < kSampleCoarse; c += kSampleBlock) {
+        const uint32_t t = sample_coarse(h, c);
+        if (t) atomicAdd(&gh[kSampleBins + c], t);
+    }
     for (int i = threadIdx.x; i < kSampleBins; i += kSampleBlock)
         if (h[i]) atomicAdd(&gh[i], h[i]);
 }
@@ -568,9 +593,9 @@ __global__ __launch_bounds__(kBlock) void k_sample_select(const SegPlan* __restr
         s_thi = kNoKey;   // nothing found: no element is cleared in the stream
     }
     // the tensor's sample histogram is the sum of its copies
-    const uint32_t* h = shist + static_cast<size_t>(s) * hcopies * kSampleBins;
+    const uint32_t* h = shist + static_cast<size_t>(s) * hcopies * kSampleWords;
     if (hcopies > 1) {
-        sum_copies<kSampleBins / 4 / kBlock>(reinterpret_cast<const uint4*>(h), kSampleBins / 4, hsum);
+        sum_copies<kSampleBins / 4 / kBlock>(reinterpret_cast<const uint4*>(h), kSampleWords / 4, hsum);
         h = reinterpret_cast<const uint32_t*>(hsum);
     }
     __syncthreads();
@@ -592,6 +617,46 @@ __global__ __launch_bounds__(kBlock) void k_sample_select(const SegPlan* __restr
         st[s].spec_lo = lo;
         st[s].spec_n = hi - lo + 1 <= static_cast<uint32_t>(kSpec) ? hi - lo + 1 : 0u;
     }
+}
+
+// The sample histogram's bin of rank `want` counted from the top, found by
+// one wave from the coarse bins and then one coarse bin's 64 fine ones (the
+// hcopies copies summed): the bin d with (samples above d) < want <=
+// (samples from d up), as find_rank_bin gives.  False when the histogram
+// holds fewer than want samples.  Every lane of the wave calls it.
+__device__ __forceinline__ bool wave_sample_rank(const uint32_t* gh0, int32_t hcopies, uint32_t want, uint32_t* d) {
+    const int l = static_cast<int>(lane());
+    uint32_t cv = 0;
+    for (int c = 0; c < hcopies; ++c) cv += gh0[static_cast<size_t>(c) * kSampleWords + kSampleBins + 63 - l];
+    const uint32_t cum = wave_incl_scan(cv);  // samples in the top l + 1 coarse bins
+    if (__shfl(cum, kWave - 1, kWave) < want) return false;
+    const uint64_t hit = __ballot(cum >= want);
+    const int L = static_cast<int>(__ffsll(static_cast<long long>(hit))) - 1;
+    const int cb = 63 - L;
+    const uint32_t above_c = __shfl(cum, L, kWave) - __shfl(cv, L, kWave);
+    uint32_t fv = 0;
+    for (int c = 0; c < hcopies; ++c) fv += gh0[static_cast<size_t>(c) * kSampleWords + 64 * cb + 63 - l];
+    const uint32_t cum2 = wave_incl_scan(fv);
+    const uint64_t hit2 = __ballot(above_c + cum2 >= want);
+    const int L2 = static_cast<int>(__ffsll(static_cast<long long>(hit2))) - 1;
+    *d = static_cast<uint32_t>(64 * cb + 63 - L2);
+    return true;
+}
+
+// T_lo, T_hi and the guessed first digits of tensor s from its sample
+// histogram, as k_sample_select finds them (one wave; every lane calls it).
+__device__ __forceinline__ void wave_sample_edges(const uint32_t* shist, int32_t hcopies, const SegPlan& P, int s,
+                                                  uint32_t* tlo, uint32_t* thi, uint32_t* spec_lo,
+                                                  uint32_t* spec_n) {
+    const uint32_t* gh0 = shist + static_cast<size_t>(s) * hcopies * kSampleWords;
+    uint32_t d;
+    *tlo = wave_sample_rank(gh0, hcopies, static_cast<uint32_t>(P.sample_rank), &d) ? d << kSampleShift : 0u;
+    *thi = kNoKey;
+    const uint32_t mhi = static_cast<uint32_t>(P.sample_rank_hi);
+    if (mhi > 0 && wave_sample_rank(gh0, hcopies, mhi, &d)) *thi = (d + 1) << kSampleShift;
+    const uint32_t lo = *tlo >> 20, hi = *thi == kNoKey ? kRadixBins - 1 : (*thi - 1) >> 20;
+    *spec_lo = lo;
+    *spec_n = hi - lo + 1 <= static_cast<uint32_t>(kSpec) ? hi - lo + 1 : 0u;
 }
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -840,9 +905,9 @@ __global__ __launch_bounds__(WAVES * kWave) void k_stream(const float* __restric
 // region's slot after the candidates of the block's earlier waves, in index
 // order (head, body rows, tail), and writes e.  *total comes back with the
 // region's candidate count.  Every thread of the block calls it.
-template <int MODE, bool STATS, int NV>
+template <int MODE, bool STATS, int NV, class Edges>
 __device__ __forceinline__ void stream_part(const float* __restrict__ g, float* __restrict__ e, int64_t gbeg,
-                                            int64_t sb, int64_t se, uint32_t tlo, uint32_t thi, uint32_t cap,
+                                            int64_t sb, int64_t se, Edges&& edges, uint32_t cap,
                                             uint2* __restrict__ cp, float* __restrict__ vals,
                                             int32_t* __restrict__ idx, int64_t out_base, uint32_t* wcnt,
                                             uint32_t& total, uint32_t& nf, double& acc) {
@@ -874,6 +939,10 @@ __device__ __forceinline__ void stream_part(const float* __restrict__ g, float* 
     f4 xb[NV];
 #pragma unroll
     for (int u = 0; u < NV; ++u) xb[u] = gv[u] + ev[u];
+    // the edges, with the loads in flight (edges() may read the sample
+    // histogram and synchronise the block)
+    uint32_t tlo = kNoKey, thi = kNoKey;
+    edges(tlo, thi);
     // phase 1: the wave's candidates, non-finite values and known energy
     uint32_t mine = 0;
     auto note = [&](float x, bool ok) {
@@ -967,12 +1036,15 @@ __global__ __launch_bounds__(SPLIT * kWave) void k_stream_split(const float* __r
                                                                uint2* __restrict__ cpair, float* __restrict__ vals,
                                                                int32_t* __restrict__ idx,
                                                                uint32_t* __restrict__ nonfinite,
-                                                               double2* __restrict__ spart) {
+                                                               double2* __restrict__ spart,
+                                                               const uint32_t* __restrict__ shist,
+                                                               int32_t hcopies) {
     constexpr int L = kRegion / SPLIT;
     constexpr int NV = L / (4 * kWave);
     static_assert(L % (4 * kWave) == 0, "a wave's part is whole rows of 64 float4");
     __shared__ uint32_t wcnt[SPLIT];
     __shared__ double wacc[SPLIT];
+    __shared__ uint32_t s_edge[2];
     const int64_t w = blockIdx.x;  // the region (one block each)
     const int q = threadIdx.x / kWave;
     const int s = upper_index_wave(rb, nseg, static_cast<int32_t>(w));
@@ -986,16 +1058,38 @@ __global__ __launch_bounds__(SPLIT * kWave) void k_stream_split(const float* __r
     uint2* cp = cpair + P.cand_base + rl * P.cap;
     uint32_t total = 0, nf = 0;
     double acc = 0.0;
+    auto none = [](uint32_t&, uint32_t&) {};
     if (P.mode == MODE_NORMAL) {
-        const uint32_t tlo = P.direct ? kNoKey : st[s].tlo;  // a direct (dense) selection collects nothing
-        const uint32_t thi = P.direct ? kNoKey : st[s].thi;
-        stream_part<MODE_NORMAL, STATS, NV>(g, e, gbeg, sb, se, tlo, thi, cap, cp, vals, idx, 0, wcnt, total, nf,
-                                            acc);
+        // T_lo and T_hi straight from the sample histogram (no select launch):
+        // the first wave reads them off while the block's loads are in
+        // flight; the tensor's first block records them for later kernels.
+        // A direct (dense) selection collects nothing.
+        auto edges = [&](uint32_t& tlo, uint32_t& thi) {
+            if (P.direct) return;
+            if (q == 0) {
+                uint32_t lo, hi, sl, sn;
+                wave_sample_edges(shist, hcopies, P, s, &lo, &hi, &sl, &sn);
+                if (lane() == 0) {
+                    s_edge[0] = lo;
+                    s_edge[1] = hi;
+                    if (rl == 0) {
+                        st[s].tlo = lo;
+                        st[s].thi = hi;
+                        st[s].spec_lo = sl;
+                        st[s].spec_n = sn;
+                    }
+                }
+            }
+            __syncthreads();
+            tlo = s_edge[0];
+            thi = s_edge[1];
+        };
+        stream_part<MODE_NORMAL, STATS, NV>(g, e, gbeg, sb, se, edges, cap, cp, vals, idx, 0, wcnt, total, nf, acc);
     } else if (P.mode == MODE_ALL) {
-        stream_part<MODE_ALL, STATS, NV>(g, e, gbeg, sb, se, 0, 0, 0, cp, vals, idx, P.out_off + lbeg, wcnt, total,
+        stream_part<MODE_ALL, STATS, NV>(g, e, gbeg, sb, se, none, 0, cp, vals, idx, P.out_off + lbeg, wcnt, total,
                                          nf, acc);
     } else {
-        stream_part<MODE_NONE, STATS, NV>(g, e, gbeg, sb, se, 0, 0, 0, cp, vals, idx, 0, wcnt, total, nf, acc);
+        stream_part<MODE_NONE, STATS, NV>(g, e, gbeg, sb, se, none, 0, cp, vals, idx, 0, wcnt, total, nf, acc);
     }
     nf = wave_sum(nf);
     if (lane() == 0 && nf && nonfinite) atomicAdd(nonfinite, nf);
@@ -2004,22 +2098,24 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
                       static_cast<const double2*>(reinterpret_cast<double2*>(at(L.rpart))), stats);
     };
 
+    // A call with few regions streams each with a block of kSplit waves, so
+    // that a small call still puts several waves on every CU (the flat N = 1e6
+    // call has 245 regions); those blocks read T_lo and T_hi off the sample
+    // histogram themselves.
+    const bool few = P.R < kFewRegions;
     if (P.any_normal && P.SB > 0) {
         EF_TRY(launch("topk_sample_hist", k_sample, dim3(static_cast<unsigned>(P.SB)), dim3(kSampleBlock), s, g,
                       static_cast<const float*>(e), plan, nseg, sbb, P.sample_rounds, shist, P.hcopies));
-        EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s, plan,
-                      static_cast<const uint32_t*>(shist), P.hcopies, st));
+        if (!few)
+            EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s,
+                          plan, static_cast<const uint32_t*>(shist), P.hcopies, st));
     }
-    // A call with few regions streams each with a block of kSplit waves, so
-    // that a small call still puts several waves on every CU (the flat N = 1e6
-    // call has 245 regions).
-    const bool few = P.R < kFewRegions;
     auto stream = [&](auto stats_on) -> int {
         constexpr bool ST = decltype(stats_on)::value;
         if (few)
             return launch("topk_stream", k_stream_split<ST, kSplit>, dim3(static_cast<unsigned>(P.R)),
                           dim3(kSplit * kWave), s, g, e, plan, nseg, rb, st, region_cnt, grp_cnt, cpair, vals, idx,
-                          nonfinite, spart);
+                          nonfinite, spart, static_cast<const uint32_t*>(shist), P.hcopies);
         return launch("topk_stream", k_stream<ST, kStreamWaves>, dim3(static_cast<unsigned>(cdiv(P.R, kStreamWaves))),
                       dim3(kStreamWaves * kWave), s, g, e, plan, nseg, rb, P.R, st, region_cnt, grp_cnt, cpair, vals,
                       idx, nonfinite, spart);
