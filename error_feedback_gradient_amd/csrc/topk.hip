@@ -7,15 +7,17 @@
 //
 // How (per tensor, "segment"; the flat call is one segment):
 //   1. sample     a strided sample of x = g + e is histogrammed on the top 12
-//                 bits of its magnitude key.  Two bin edges are read off it:
-//                 T_lo, with (by a wide statistical margin) at least k
-//                 elements of the tensor above it, and T_hi, with (very
-//                 likely) fewer than k above it.
-//   2. stream     ONE pass over the tensor, one wave per 4096 elements: read
-//                 g and e (128-bit non-temporal loads, all 16 of the region in
-//                 flight per lane and array), write e (128-bit stores), and
-//                 append every element with key >= T_lo to the wave's
-//                 candidate slot, in index order, with wave ballots.
+//                 bits of its magnitude key.  Two bin edges are read off it
+//                 (by one block per tensor; in a call with few regions, by the
+//                 stream's blocks themselves): T_lo, with (by a wide
+//                 statistical margin) at least k elements of the tensor above
+//                 it, and T_hi, with (very likely) fewer than k above it.
+//   2. stream     ONE pass over the tensor, one wave per 4096-element region
+//                 (eight waves per region in a call with few regions): read g
+//                 and e (128-bit non-temporal loads, all of a wave's in flight
+//                 per lane and array), write e (128-bit stores), and append
+//                 every element with key >= T_lo to the region's candidate
+//                 slot, in index order, with wave ballots.
 //                 Candidates with key >= T_hi are almost surely kept, so the
 //                 stream already writes e = 0 for them.  Each block adds its
 //                 regions' candidate counts to their group totals with one
@@ -39,10 +41,13 @@
 //                 write block starts after the totals of the blocks before it.
 //                 Their residual becomes +0 unless the stream already cleared
 //                 it; a dropped candidate that the stream cleared gets x back.
-// The exact fallback runs steps 4-5 over the whole tensor (x sits in e): its
-// compaction blocks histogram x for the first digit and put x back wherever
-// the stream cleared it.  Only integer atomics are used, so results do not
-// depend on timing.
+// The exact fallback runs steps 4-5 over the whole tensor (x sits in e) in
+// three reads of x: its compaction blocks histogram x for the first digit
+// (and, for the first digits the sample's window spans, the second one) and
+// put x back wherever the stream cleared it; one more radix pass, which
+// also keeps each block's histogram, from which the count kernel takes the
+// blocks' totals; and the write.  Only integer atomics are used, so results
+// do not depend on timing.
 #include <math.h>
 #include <string.h>
 
