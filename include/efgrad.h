@@ -29,9 +29,10 @@
  *  - Floating-point data problems (Inf/NaN) are not call errors: the calls that
  *    can meet them count them into an optional device uint32 `nonfinite`
  *    (overwritten by each call).
- *  - HIP graph capture: with ef_profile_enable off, every call only launches
- *    kernels (no memset, no host wait), so a captured call replays exactly
- *    like the eager one.  ef_topk_compress_segmented with more than 11 tensors
+ *  - HIP graph capture: every call only launches kernels (no memset, no host
+ *    wait; ef_profile_enable records nothing on a stream under capture), so a
+ *    captured call replays exactly like the eager one.
+ *    ef_topk_compress_segmented with more than 11 tensors
  *    reads its cached plan from pinned host memory when called eagerly; under
  *    capture it passes the plan in kernel arguments instead (one small launch
  *    per 500 words, about 17 tensors), so a replay never depends on the cache.
@@ -374,12 +375,14 @@ int decode_blocks(const uint8_t* mask, const uint8_t* counts_m1, const uint8_t* 
 
 /* ------------------------------------------------------------------------
  * Kernel timing with HIP events on the stream each kernel is launched on.
- * ef_profile_enable(1, only) starts recording an event pair around every later
+ * ef_profile_enable(1, only) starts recording an event pair for every later
  * kernel launch of the process whose label contains `only` (host string; NULL
- * or "" = every launch); ef_profile_enable(0, NULL) stops and clears.
+ * or "" = every launch), recorded by the dispatch itself (hipExtLaunchKernel),
+ * so each pair spans the kernel's own run; launches on a stream under graph
+ * capture are not recorded.  ef_profile_enable(0, NULL) stops and clears.
  * ef_profile_read() waits for the recorded events and returns the summed
  * duration (ms) and launch count of recorded kernels whose label contains
- * `name`.  Meant for benchmarks: each recorded launch costs two event records.
+ * `name`.  Meant for benchmarks: a recorded launch takes longer to issue.
  * Labels are "topk_stream", "topk_sample_hist", ..., "sign_ef", "decode_scatter",
  * "sgd_apply", "bitmap_*", "delta_*", "blocks_*".
  * ------------------------------------------------------------------------ */
