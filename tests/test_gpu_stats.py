@@ -61,7 +61,8 @@ def test_stats_do_not_change_outputs_and_repeat():
     assert np.array_equal(outs[1][3].view(np.uint64), outs[2][3].view(np.uint64))
 
 
-def test_segmented_stats_per_tensor():
+@pytest.mark.parametrize("flags", [0, efg.EF_FLAG_FORCE_FALLBACK])
+def test_segmented_stats_per_tensor(flags):
     dev = device()
     sizes = [7, 0, 1, 300, 64, 1001, 5, 16385, 40_000, 70_001, 2]
     ks = [3, 0, 1, 0, 64, 17, 5, 160, 400, 701, 2]
@@ -71,9 +72,11 @@ def test_segmented_stats_per_tensor():
     e = gen.normal_small(n, 505, scale=0.2)
     ed = to_dev(e, dev)
     st = torch.full((2 * len(ks),), -1.0, dtype=torch.float64, device=dev)
-    efg.ef_topk_compress_segmented(to_dev(g, dev), ed, off, ks, stats=st)
+    v, i = efg.ef_topk_compress_segmented(to_dev(g, dev), ed, off, ks, stats=st, flags=flags)
     st = host(st)
     ov, oi, oe, _ = oracle.topk_segmented(g, e, off, ks)
+    assert_bits_equal(host(i), oi, "idx")
+    assert_bits_equal(host(ed), oe, "e")
     o = 0
     for s in range(len(ks)):
         a, b = off[s], off[s + 1]
