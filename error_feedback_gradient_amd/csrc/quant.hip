@@ -19,15 +19,26 @@ namespace quant {
 
 constexpr int kBlock = 256;
 constexpr int kMaxGrid = 1024;
+#ifndef EFG_QUANT_PER
+#define EFG_QUANT_PER 4
+#endif
+constexpr int kPer = EFG_QUANT_PER;  // entries per thread and step
 
 __global__ __launch_bounds__(kBlock) void k_amax(const float* __restrict__ vals, int64_t k,
                                                  uint32_t* __restrict__ part) {
     __shared__ uint32_t w[kBlock / kWave];
     uint32_t m = 0;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < k; j += stride) {
-        const uint32_t key = key_of(vals[j]);
-        if (key < 0x7f800000u) m = max(m, key);  // finite values only
+    // kPer entries per thread and step, all loaded before any is used
+    for (int64_t j0 = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j0 < k; j0 += stride * kPer) {
+        float v[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) v[u] = vals[min(j0 + u * stride, k - 1)];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const uint32_t key = key_of(v[u]);
+            if (j0 + u * stride < k && key < 0x7f800000u) m = max(m, key);  // finite values only
+        }
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(m, d, kWave)));
@@ -58,20 +69,34 @@ __global__ __launch_bounds__(kBlock) void k_quant(const float* __restrict__ vals
     const float scale = amax > 0.0f ? amax / 127.0f : 0.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = scale;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
-    for (int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j < k; j += stride) {
-        const float v = vals[j];
-        int qi = 0;
-        if (amax > 0.0f && key_of(v) < 0x7f800000u) {
-            const float t = v * inv;
-            float r = rintf(t);
-            if (r != r) r = 0.0f;  // 0 * inf when amax is below 127 / FLT_MAX
-            r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
-            qi = static_cast<int>(r);
+    // kPer entries per thread and step, all loaded before any is used, so
+    // that a thread has kPer scattered residual writes in flight
+    for (int64_t j0 = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; j0 < k; j0 += stride * kPer) {
+        float v[kPer];
+        int32_t ix[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int64_t j = min(j0 + u * stride, k - 1);
+            v[u] = vals[j];
+            ix[u] = idx[j];
         }
-        const float deq = static_cast<float>(qi) * scale;
-        q[j] = static_cast<int8_t>(qi);
-        const int64_t i = idx[j];
-        if (i >= 0 && i < n) e[i] = v - deq;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int64_t j = j0 + u * stride;
+            if (j >= k) break;
+            int qi = 0;
+            if (amax > 0.0f && key_of(v[u]) < 0x7f800000u) {
+                const float t = v[u] * inv;
+                float r = rintf(t);
+                if (r != r) r = 0.0f;  // 0 * inf when amax is below 127 / FLT_MAX
+                r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
+                qi = static_cast<int>(r);
+            }
+            const float deq = static_cast<float>(qi) * scale;
+            q[j] = static_cast<int8_t>(qi);
+            const int64_t i = ix[u];
+            if (i >= 0 && i < n) e[i] = v[u] - deq;
+        }
     }
 }
 
