@@ -247,7 +247,9 @@ int ef_onebit_adam_update_var(const int8_t* qsum, int32_t nworkers, float* m, fl
  *   q[j]  = rint(vals[j] * inv) clamped to [-127, 127]   (round half to even;
  *           0 for a non-finite value, when amax = 0, or for a NaN product)
  *   e[idx[j]] = vals[j] - q[j] * scale         (float32; the receiver gets
- *           q[j] * scale, and q*scale + e' equals vals[j] exactly)
+ *           q[j] * scale, and q*scale + e' equals vals[j] exactly unless
+ *           q*scale overflows: possible only when amax lies within 2^-24 of
+ *           FLT_MAX, and then e' = -/+Inf at the entries coded +/-127)
  *   *scale_out = scale                          (device float)
  * Entries whose idx lies outside [0, n) update no residual.  ws: at least
  * ef_quantize_workspace_bytes(k) bytes, 4-byte aligned.
