@@ -106,6 +106,21 @@ constexpr int kSampleBins = 4096;
 constexpr int kSampleCoarse = 64;
 constexpr int kSampleWords = kSampleBins + kSampleCoarse;
 constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
+// Each copy of a sample histogram also keeps a window of fine bins around the
+// tensor's threshold of the previous call on the workspace (its hint):
+// kFineBins bins of 2^kFineShift key units (1/1024 octave) over two octaves,
+// their sums in groups of 64, and the count of samples above the window.
+// Where the residual has crowded values just below the threshold (the steady
+// state of error feedback under a gradient with a drift), a 12-bit bin below
+// T can hold many times k elements; the fine window puts T_lo within 1/1024
+// octave of the sample rank it stands for, so the candidates stay few.
+constexpr int kFineShift = 13;
+constexpr int kFineBins = 2048;
+constexpr int kFineGroups = kFineBins / 64;
+constexpr uint32_t kFineSpan = static_cast<uint32_t>(kFineBins) << kFineShift;
+constexpr int kFineWords = kFineBins + kFineGroups + 32;  // bins, group sums, count above, padding
+constexpr int kSampleStride = kSampleWords + kFineWords;  // words of one histogram copy
+static_assert(kSampleStride % 4 == 0, "histogram copies stay 16-byte aligned");
 #ifndef EFG_CHUNK
 #define EFG_CHUNK 2048
 #endif
@@ -239,7 +254,7 @@ struct Plan {
 };
 
 struct Layout {
-    size_t status, plan, rb, gbb, sbb, cbb, hb, static_end;
+    size_t status, plan, rb, gbb, sbb, cbb, hb, static_end, hint;
     size_t state, shist, rhist, grp_cnt, zero_end;
     size_t region_cnt, cpair, dval, didx, bh, btot, spart, gpart, cpart, rpart;
     size_t total;
@@ -261,8 +276,11 @@ static Layout make_layout(const Plan& p) {
     L.hb = at; at += (ns + 1) * 4;
     at = round_up(at, 256);
     L.static_end = at;
+    // each tensor's exact threshold of the last call, kept from call to call
+    // (neither the tables' copy nor the clearing touches it)
+    L.hint = take(ns * 4);
     L.state = take(ns * sizeof(SegState));
-    L.shist = take(ns * static_cast<size_t>(p.hcopies) * kSampleWords * 4);
+    L.shist = take(ns * static_cast<size_t>(p.hcopies) * kSampleStride * 4);
     L.rhist = take((3 + kSpec) * ns * static_cast<size_t>(p.hcopies) * kHistWords * 4);
     L.grp_cnt = take(static_cast<size_t>(p.G) * 4);
     L.zero_end = at;
@@ -461,19 +479,35 @@ __global__ __launch_bounds__(kBlock) void k_init(uint4* zero, int64_t nvec, uint
     }
 }
 
-// The sample histogram (top 12 key bits of x = g + e) of one block's
-// `rounds` consecutive groups of kSampleBlockChunks chunks of a tensor
-// (block bl of the tensor), in the LDS histogram h, which it clears first.
-// Every thread of the block calls it; h is complete on return.
+// The window of fine sample bins of a tensor whose previous exact threshold
+// was `hint`: [base, base + kFineSpan), from one octave below the hint's
+// 12-bit bin up.  Any 32-bit value is a valid hint (a workspace holding
+// something else only leaves the window where no rank falls).
+__device__ __forceinline__ uint32_t fine_base(uint32_t hint) {
+    const uint32_t c = (hint & 0x7fffffffu) & ~((1u << kSampleShift) - 1u);
+    return c >= (1u << 23) ? c - (1u << 23) : 0u;
+}
+
+// The sample histograms (top 12 key bits of x = g + e, and with FINE the fine
+// window at fbase) of one block's `rounds` consecutive groups of
+// kSampleBlockChunks chunks of a tensor (block bl of the tensor), in the LDS
+// histograms h and hf, which it clears first; *above_lds gets the block's
+// count of samples above the fine window.  Every thread of the block calls
+// it; the histograms are complete on return.
 __device__ __forceinline__ void sample_block(const float* __restrict__ g, const float* __restrict__ e,
-                                             const SegPlan& P, int bl, int32_t rounds, uint32_t* h) {
+                                             const SegPlan& P, int bl, int32_t rounds, bool fine, uint32_t fbase,
+                                             uint32_t* h, uint32_t* hf, uint32_t* above_lds) {
     const int64_t off = P.off, n = P.n;
     const int S = P.sample_chunks;
     const bool exhaustive = P.exhaustive != 0;
     for (int i = threadIdx.x; i < kSampleBins; i += kSampleBlock) h[i] = 0;
+    if (fine)
+        for (int i = threadIdx.x; i < kFineBins; i += kSampleBlock) hf[i] = 0;
+    if (threadIdx.x == 0) *above_lds = 0;
     __syncthreads();
     const int w = threadIdx.x / kWave;
     const int l = lane();
+    uint32_t above = 0;
     for (int rd = 0; rd < rounds; ++rd) {
         const int c0 = (bl * rounds + rd) * kSampleBlockChunks + w * kSampleChunksPerWave;
         if (c0 >= S) break;  // wave-uniform: the rest of this block's chunks lie past the sample
@@ -500,13 +534,25 @@ __device__ __forceinline__ void sample_block(const float* __restrict__ g, const 
         for (int u = 0; u < kSampleChunksPerWave; ++u)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (ok[u][j]) atomicAdd(&h[key_of(xs[u][j]) >> kSampleShift], 1u);
+                if (ok[u][j]) {
+                    const uint32_t key = key_of(xs[u][j]);
+                    atomicAdd(&h[key >> kSampleShift], 1u);
+                    if (fine) {
+                        const uint32_t d = key - fbase;  // wraps for keys below the window
+                        if (d < kFineSpan) atomicAdd(&hf[d >> kFineShift], 1u);
+                        else above += key >= fbase ? 1u : 0u;
+                    }
+                }
+    }
+    if (fine) {
+        above = wave_sum(above);
+        if (l == 0 && above) atomicAdd(above_lds, above);
     }
     __syncthreads();
 }
 
-// Coarse bin c of an LDS sample histogram, read with a rotation so that the
-// lanes hit different banks.
+// Coarse bin c (64 fine bins) of an LDS sample histogram, read with a
+// rotation so that the lanes hit different banks.
 __device__ __forceinline__ uint32_t sample_coarse(const uint32_t* h, int c) {
     uint32_t t = 0;
     for (int i = 0; i < 64; ++i) t += h[c * 64 + ((i + c) & 63)];
@@ -514,154 +560,136 @@ __device__ __forceinline__ uint32_t sample_coarse(const uint32_t* h, int c) {
 }
 
 // 1. sample histograms, each block adding its own to copy b % hcopies of its
-//    tensor's (fine bins, then the coarse sums)
+//    tensor's (12-bit bins and their coarse sums; with `fine`, the fine window
+//    around the tensor's hint, its group sums and the count above it)
 __global__ __launch_bounds__(kSampleBlock) void k_sample(const float* __restrict__ g, const float* __restrict__ e,
                                                    const SegPlan* __restrict__ plan, int32_t nseg,
                                                    const int32_t* __restrict__ sbb, int32_t rounds,
-                                                   uint32_t* __restrict__ shist, int32_t hcopies) {
+                                                   uint32_t* __restrict__ shist, int32_t hcopies,
+                                                   const uint32_t* __restrict__ hint, int32_t fine) {
     __shared__ uint32_t h[kSampleBins];
+    __shared__ uint32_t hf[kFineBins];
+    __shared__ uint32_t above;
     const int b = blockIdx.x;
     const int s = upper_index_wave(sbb, nseg, b);
-    sample_block(g, e, plan[s], b - sbb[s], rounds, h);
-    uint32_t* gh = shist + (static_cast<size_t>(s) * hcopies + blockIdx.x % hcopies) * kSampleWords;
+    const uint32_t fbase = fine ? fine_base(hint[s]) : 0u;
+    sample_block(g, e, plan[s], b - sbb[s], rounds, fine != 0, fbase, h, hf, &above);
+    uint32_t* gh = shist + (static_cast<size_t>(s) * hcopies + blockIdx.x % hcopies) * kSampleStride;
     for (int c = threadIdx.x; c < kSampleCoarse; c += kSampleBlock) {
         const uint32_t t = sample_coarse(h, c);
         if (t) atomicAdd(&gh[kSampleBins + c], t);
     }
     for (int i = threadIdx.x; i < kSampleBins; i += kSampleBlock)
         if (h[i]) atomicAdd(&gh[i], h[i]);
-}
-
-// hsum[i] = sum over the kHistCopies copies (each `stride` uint4 apart) of
-// g4[i], for the PER * kBlock uint4 of a histogram; all of a thread's loads
-// are issued before any is used
-template <int PER>
-__device__ __forceinline__ void sum_copies(const uint4* g4, int stride, uint4* hsum) {
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-        const int i = threadIdx.x + r * kBlock;
-        uint4 w[kHistCopies];
-#pragma unroll
-        for (int c = 0; c < kHistCopies; ++c) w[c] = g4[c * stride + i];
-        uint4 v = w[0];
-#pragma unroll
-        for (int c = 1; c < kHistCopies; ++c) {
-            v.x += w[c].x;
-            v.y += w[c].y;
-            v.z += w[c].z;
-            v.w += w[c].w;
-        }
-        hsum[i] = v;
+    if (!fine) return;
+    uint32_t* gf = gh + kSampleWords;
+    for (int c = threadIdx.x; c < kFineGroups; c += kSampleBlock) {
+        const uint32_t t = sample_coarse(hf, c);
+        if (t) atomicAdd(&gf[kFineBins + c], t);
     }
-}
-
-// Finds, in a histogram of PER*kBlock bins, the bin d such that the count
-// strictly above d is < want <= count from d upward.  Every thread of the block
-// must call it; returns true in exactly one thread when the total reaches
-// want, with *d and *above set there.
-template <int PER>
-__device__ __forceinline__ bool find_rank_bin(const uint32_t* hist, uint32_t want, int* d, uint32_t* above,
-                                              uint32_t* lds) {
-    const int r = kBlock - 1 - static_cast<int>(threadIdx.x);  // thread 0 owns the top range
-    uint32_t c[PER];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        c[i] = hist[r * PER + i];
-        sum += c[i];
-    }
-    uint32_t total;
-    uint32_t run = block_excl_scan<kBlock>(sum, lds, &total);
-    bool found = false;
-#pragma unroll
-    for (int i = PER - 1; i >= 0; --i) {
-        if (!found && run < want && run + c[i] >= want) {
-            found = true;
-            *d = r * PER + i;
-            *above = run;
-        }
-        run += c[i];
-    }
-    return found;
-}
-
-__global__ __launch_bounds__(kBlock) void k_sample_select(const SegPlan* __restrict__ plan,
-                                                          const uint32_t* __restrict__ shist, int32_t hcopies,
-                                                          SegState* __restrict__ st) {
-    __shared__ uint32_t lds[kWavesPerBlock + 1];
-    __shared__ uint32_t s_tlo, s_thi;
-    __shared__ uint4 hsum[kSampleBins / 4];
-    const int s = blockIdx.x;
-    if (plan[s].mode != MODE_NORMAL || plan[s].direct) return;
-    if (threadIdx.x == 0) {
-        s_tlo = 0;        // nothing found: every element is a candidate
-        s_thi = kNoKey;   // nothing found: no element is cleared in the stream
-    }
-    // the tensor's sample histogram is the sum of its copies
-    const uint32_t* h = shist + static_cast<size_t>(s) * hcopies * kSampleWords;
-    if (hcopies > 1) {
-        sum_copies<kSampleBins / 4 / kBlock>(reinterpret_cast<const uint4*>(h), kSampleWords / 4, hsum);
-        h = reinterpret_cast<const uint32_t*>(hsum);
-    }
-    __syncthreads();
-    int d;
-    uint32_t above;
-    if (find_rank_bin<kSampleBins / kBlock>(h, static_cast<uint32_t>(plan[s].sample_rank), &d, &above, lds))
-        s_tlo = static_cast<uint32_t>(d) << kSampleShift;
-    const uint32_t mhi = static_cast<uint32_t>(plan[s].sample_rank_hi);
-    if (mhi > 0) {
-        if (find_rank_bin<kSampleBins / kBlock>(h, mhi, &d, &above, lds))
-            s_thi = static_cast<uint32_t>(d + 1) << kSampleShift;  // upper edge: fewer than mhi samples above
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        st[s].tlo = s_tlo;
-        st[s].thi = s_thi;
-        // T very likely lies in [tlo, thi): its first digit among these
-        const uint32_t lo = s_tlo >> 20, hi = s_thi == kNoKey ? kRadixBins - 1 : (s_thi - 1) >> 20;
-        st[s].spec_lo = lo;
-        st[s].spec_n = hi - lo + 1 <= static_cast<uint32_t>(kSpec) ? hi - lo + 1 : 0u;
-    }
-}
-
-// The sample histogram's bin of rank `want` counted from the top, found by
-// one wave from the coarse bins and then one coarse bin's 64 fine ones (the
-// hcopies copies summed): the bin d with (samples above d) < want <=
-// (samples from d up), as find_rank_bin gives.  False when the histogram
-// holds fewer than want samples.  Every lane of the wave calls it.
-__device__ __forceinline__ bool wave_sample_rank(const uint32_t* gh0, int32_t hcopies, uint32_t want, uint32_t* d) {
-    const int l = static_cast<int>(lane());
-    uint32_t cv = 0;
-    for (int c = 0; c < hcopies; ++c) cv += gh0[static_cast<size_t>(c) * kSampleWords + kSampleBins + 63 - l];
-    const uint32_t cum = wave_incl_scan(cv);  // samples in the top l + 1 coarse bins
-    if (__shfl(cum, kWave - 1, kWave) < want) return false;
-    const uint64_t hit = __ballot(cum >= want);
-    const int L = static_cast<int>(__ffsll(static_cast<long long>(hit))) - 1;
-    const int cb = 63 - L;
-    const uint32_t above_c = __shfl(cum, L, kWave) - __shfl(cv, L, kWave);
-    uint32_t fv = 0;
-    for (int c = 0; c < hcopies; ++c) fv += gh0[static_cast<size_t>(c) * kSampleWords + 64 * cb + 63 - l];
-    const uint32_t cum2 = wave_incl_scan(fv);
-    const uint64_t hit2 = __ballot(above_c + cum2 >= want);
-    const int L2 = static_cast<int>(__ffsll(static_cast<long long>(hit2))) - 1;
-    *d = static_cast<uint32_t>(64 * cb + 63 - L2);
-    return true;
+    for (int i = threadIdx.x; i < kFineBins; i += kSampleBlock)
+        if (hf[i]) atomicAdd(&gf[i], hf[i]);
+    if (threadIdx.x == 0 && above) atomicAdd(&gf[kFineBins + kFineGroups], above);
 }
 
 // T_lo, T_hi and the guessed first digits of tensor s from its sample
-// histogram, as k_sample_select finds them (one wave; every lane calls it).
+// histograms (the hcopies <= C copies summed), found by one wave; every lane
+// calls it and gets the results.  T_lo is the lower edge of the bin holding
+// the sample's rank P.sample_rank (0 when the sample holds fewer), T_hi the
+// upper edge of the bin holding rank P.sample_rank_hi (none when that rank is
+// 0 or the sample holds fewer), counting from the top, each rank taken in the
+// fine window at fbase when the window holds it and in the 12-bit bins
+// otherwise.  Both ranks are searched together in two rounds of loads: the
+// group sums of the 12-bit bins and of the fine window (with the count above
+// the window), then the 64 bins of the group each rank falls in.
+template <int C>
 __device__ __forceinline__ void wave_sample_edges(const uint32_t* shist, int32_t hcopies, const SegPlan& P, int s,
-                                                  uint32_t* tlo, uint32_t* thi, uint32_t* spec_lo,
+                                                  uint32_t fbase, uint32_t* tlo, uint32_t* thi, uint32_t* spec_lo,
                                                   uint32_t* spec_n) {
-    const uint32_t* gh0 = shist + static_cast<size_t>(s) * hcopies * kSampleWords;
-    uint32_t d;
-    *tlo = wave_sample_rank(gh0, hcopies, static_cast<uint32_t>(P.sample_rank), &d) ? d << kSampleShift : 0u;
-    *thi = kNoKey;
-    const uint32_t mhi = static_cast<uint32_t>(P.sample_rank_hi);
-    if (mhi > 0 && wave_sample_rank(gh0, hcopies, mhi, &d)) *thi = (d + 1) << kSampleShift;
+    const int l = static_cast<int>(lane());
+    const uint32_t* h0 = shist + static_cast<size_t>(s) * hcopies * kSampleStride;
+    const uint32_t rank[2] = {static_cast<uint32_t>(P.sample_rank), static_cast<uint32_t>(P.sample_rank_hi)};
+    // round 1 (lane l: 12-bit group 63 - l, fine group 31 - l, the top first)
+    uint32_t cw[C], gw[C], aw[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const uint32_t* hc = h0 + static_cast<size_t>(c < hcopies ? c : 0) * kSampleStride;
+        cw[c] = hc[kSampleBins + 63 - l];
+        gw[c] = hc[kSampleWords + kFineBins + (l < kFineGroups ? kFineGroups - 1 - l : 0)];
+        aw[c] = hc[kSampleWords + kFineBins + kFineGroups];
+    }
+    uint32_t cv = 0, gv = 0, ab = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        if (c >= hcopies) break;
+        cv += cw[c];
+        gv += l < kFineGroups ? gw[c] : 0u;
+        ab += aw[c];
+    }
+    const uint32_t ccum = wave_incl_scan(cv);  // samples in the top l + 1 groups of 12-bit bins
+    const uint32_t gcum = wave_incl_scan(gv);  // samples in the top l + 1 fine groups
+    const uint32_t ctot = __shfl(ccum, kWave - 1, kWave), wtot = __shfl(gcum, kWave - 1, kWave);
+    bool found[2], fine[2];
+    uint32_t grp[2], abv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t want = rank[i];
+        fine[i] = want > ab && want - ab <= wtot;
+        found[i] = want > 0 && ctot >= want;
+        const uint64_t hit = fine[i] ? __ballot(l < kFineGroups && ab + gcum >= want) : __ballot(ccum >= want);
+        const int L = hit ? static_cast<int>(__ffsll(static_cast<long long>(hit))) - 1 : 0;
+        grp[i] = fine[i] ? static_cast<uint32_t>(kFineGroups - 1 - L) : static_cast<uint32_t>(63 - L);
+        abv[i] = fine[i] ? ab + __shfl(gcum, L, kWave) - __shfl(gv, L, kWave)
+                         : __shfl(ccum, L, kWave) - __shfl(cv, L, kWave);
+    }
+    // round 2 (lane l: bin 64 grp + 63 - l of each rank's group)
+    uint32_t bw[2][C];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const uint32_t* hc = h0 + static_cast<size_t>(c < hcopies ? c : 0) * kSampleStride;
+            bw[i][c] = hc[(fine[i] ? kSampleWords : 0) + 64 * grp[i] + 63 - l];
+        }
+    uint32_t edge[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            if (c >= hcopies) break;
+            v += bw[i][c];
+        }
+        const uint32_t cum = wave_incl_scan(v);
+        const uint64_t hit = __ballot(abv[i] + cum >= rank[i]);
+        const int L = hit ? static_cast<int>(__ffsll(static_cast<long long>(hit))) - 1 : 63;
+        const uint32_t bin = 64 * grp[i] + 63 - static_cast<uint32_t>(L) + (i == 1 ? 1u : 0u);  // T_hi: upper edge
+        edge[i] = fine[i] ? fbase + (bin << kFineShift) : bin << kSampleShift;
+    }
+    *tlo = found[0] ? edge[0] : 0u;
+    *thi = found[1] ? edge[1] : kNoKey;
     const uint32_t lo = *tlo >> 20, hi = *thi == kNoKey ? kRadixBins - 1 : (*thi - 1) >> 20;
     *spec_lo = lo;
     *spec_n = hi - lo + 1 <= static_cast<uint32_t>(kSpec) ? hi - lo + 1 : 0u;
+}
+
+// 1b. T_lo and T_hi of each tensor (one wave per tensor), for calls whose
+//     stream blocks do not find them themselves
+__global__ __launch_bounds__(kWave) void k_sample_select(const SegPlan* __restrict__ plan,
+                                                         const uint32_t* __restrict__ shist, int32_t hcopies,
+                                                         const uint32_t* __restrict__ hint,
+                                                         SegState* __restrict__ st) {
+    const int s = blockIdx.x;
+    const SegPlan& P = plan[s];
+    if (P.mode != MODE_NORMAL || P.direct) return;
+    uint32_t lo, hi, sl, sn;
+    wave_sample_edges<kHistCopies>(shist, hcopies, P, s, fine_base(hint[s]), &lo, &hi, &sl, &sn);
+    if (lane() == 0) {
+        st[s].tlo = lo;
+        st[s].thi = hi;
+        st[s].spec_lo = sl;
+        st[s].spec_n = sn;
+    }
 }
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -1043,7 +1071,8 @@ __global__ __launch_bounds__(SPLIT * kWave) void k_stream_split(const float* __r
                                                                uint32_t* __restrict__ nonfinite,
                                                                double2* __restrict__ spart,
                                                                const uint32_t* __restrict__ shist,
-                                                               int32_t hcopies) {
+                                                               int32_t hcopies,
+                                                               const uint32_t* __restrict__ hint) {
     constexpr int L = kRegion / SPLIT;
     constexpr int NV = L / (4 * kWave);
     static_assert(L % (4 * kWave) == 0, "a wave's part is whole rows of 64 float4");
@@ -1073,7 +1102,7 @@ __global__ __launch_bounds__(SPLIT * kWave) void k_stream_split(const float* __r
             if (P.direct) return;
             if (q == 0) {
                 uint32_t lo, hi, sl, sn;
-                wave_sample_edges(shist, hcopies, P, s, &lo, &hi, &sl, &sn);
+                wave_sample_edges<1>(shist, hcopies, P, s, fine_base(hint[s]), &lo, &hi, &sl, &sn);
                 if (lane() == 0) {
                     s_edge[0] = lo;
                     s_edge[1] = hi;
@@ -1513,7 +1542,7 @@ __device__ __forceinline__ uint32_t load_rows(const Chunk& c, float (&v)[kRows])
 // block records them for the later kernels.
 __device__ __forceinline__ void digits_before(int pass, int s, int lb, const SegPlan* plan, int32_t nseg,
                                               SegState* st, const uint32_t* rhist, int32_t hcopies,
-                                              uint32_t* prefix, uint32_t* want) {
+                                              uint32_t* prefix, uint32_t* want, uint32_t* hint = nullptr) {
     uint32_t d, above;
     // the previous pass's histogram: after a hit, the guessed first digit's
     // second-digit histogram stands in for the first select pass's
@@ -1545,6 +1574,7 @@ __device__ __forceinline__ void digits_before(int pass, int s, int lb, const Seg
         if (lb == 0 && threadIdx.x == 0) {
             st[s].T = *prefix;
             st[s].r = *want;
+            if (hint) hint[s] = *prefix;  // the next call's fine sample window
         }
     }
 }
@@ -1618,7 +1648,8 @@ __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __rest
 __global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ plan, int32_t nseg,
                                                   const int32_t* __restrict__ hb, SegState* __restrict__ st,
                                                   const uint32_t* __restrict__ rhist, int32_t hcopies,
-                                                  const uint32_t* __restrict__ bh, uint2* __restrict__ btot) {
+                                                  const uint32_t* __restrict__ bh, uint2* __restrict__ btot,
+                                                  uint32_t* __restrict__ hint) {
     __shared__ uint32_t lds[kWavesPerBlock + 1];
     const SelBlock sb = sel_block(plan, nseg, hb, st);
     if (sb.u0 >= sb.u1) {  // never the tensor's first block, which records T and r
@@ -1626,7 +1657,7 @@ __global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ pl
         return;
     }
     uint32_t T, r;
-    digits_before(3, sb.s, sb.lb, plan, nseg, st, rhist, hcopies, &T, &r);
+    digits_before(3, sb.s, sb.lb, plan, nseg, st, rhist, hcopies, &T, &r, hint);
     const uint32_t d = T & 1023u;
     const uint32_t* mine = bh + static_cast<size_t>(blockIdx.x) * kBlockHistWords;
     uint32_t a = 0;
@@ -2080,6 +2111,7 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
     uint32_t* stray = reinterpret_cast<uint32_t*>(at(L.status));
     SegState* st = reinterpret_cast<SegState*>(at(L.state));
     uint32_t* shist = reinterpret_cast<uint32_t*>(at(L.shist));
+    uint32_t* hint = reinterpret_cast<uint32_t*>(at(L.hint));
     uint32_t* rhist = reinterpret_cast<uint32_t*>(at(L.rhist));
     uint32_t* grp_cnt = reinterpret_cast<uint32_t*>(at(L.grp_cnt));
     uint32_t* region_cnt = reinterpret_cast<uint32_t*>(at(L.region_cnt));
@@ -2108,19 +2140,28 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
     // call has 245 regions); those blocks read T_lo and T_hi off the sample
     // histogram themselves.
     const bool few = P.R < kFewRegions;
+    // (such calls keep one copy of each histogram, which is all the split
+    // stream's edge search reads)
+    if (few && P.hcopies != 1) return fail(EF_EINVAL, "internal: split stream with %d histogram copies", P.hcopies);
     if (P.any_normal && P.SB > 0) {
+        // the fine window is left out when the statistics are asked for: their
+        // fixed-order sums run over a split of the elements that depends on
+        // T_lo, which then depends on the call's inputs alone
         EF_TRY(launch("topk_sample_hist", k_sample, dim3(static_cast<unsigned>(P.SB)), dim3(kSampleBlock), s, g,
-                      static_cast<const float*>(e), plan, nseg, sbb, P.sample_rounds, shist, P.hcopies));
+                      static_cast<const float*>(e), plan, nseg, sbb, P.sample_rounds, shist, P.hcopies,
+                      static_cast<const uint32_t*>(hint), static_cast<int32_t>(stats ? 0 : 1)));
         if (!few)
-            EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kBlock), s,
-                          plan, static_cast<const uint32_t*>(shist), P.hcopies, st));
+            EF_TRY(launch("topk_sample_select", k_sample_select, dim3(static_cast<unsigned>(nseg)), dim3(kWave), s,
+                          plan, static_cast<const uint32_t*>(shist), P.hcopies, static_cast<const uint32_t*>(hint),
+                          st));
     }
     auto stream = [&](auto stats_on) -> int {
         constexpr bool ST = decltype(stats_on)::value;
         if (few)
             return launch("topk_stream", k_stream_split<ST, kSplit>, dim3(static_cast<unsigned>(P.R)),
                           dim3(kSplit * kWave), s, g, e, plan, nseg, rb, st, region_cnt, grp_cnt, cpair, vals, idx,
-                          nonfinite, spart, static_cast<const uint32_t*>(shist), P.hcopies);
+                          nonfinite, spart, static_cast<const uint32_t*>(shist), P.hcopies,
+                          static_cast<const uint32_t*>(hint));
         return launch("topk_stream", k_stream<ST, kStreamWaves>, dim3(static_cast<unsigned>(cdiv(P.R, kStreamWaves))),
                       dim3(kStreamWaves * kWave), s, g, e, plan, nseg, rb, P.R, st, region_cnt, grp_cnt, cpair, vals,
                       idx, nonfinite, spart);
@@ -2141,7 +2182,7 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
         EF_TRY(launch("topk_hist", k_hist, hgrid, dim3(kBlock), s, pass, plan, nseg, hb, st,
                       static_cast<const float*>(dval), static_cast<const float*>(e), rhist, P.hcopies, bh));
     EF_TRY(launch("topk_count", k_count, hgrid, dim3(kBlock), s, plan, nseg, hb, st,
-                  static_cast<const uint32_t*>(rhist), P.hcopies, static_cast<const uint32_t*>(bh), btot));
+                  static_cast<const uint32_t*>(rhist), P.hcopies, static_cast<const uint32_t*>(bh), btot, hint));
     EF_TRY(launch("topk_write", stats ? k_write<true> : k_write<false>, hgrid, dim3(kBlock), s, plan, nseg, hb,
                   static_cast<const SegState*>(st), static_cast<const float*>(dval),
                   static_cast<const int32_t*>(didx), static_cast<const uint2*>(btot), e, vals, idx, cpart,
