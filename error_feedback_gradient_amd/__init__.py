@@ -31,6 +31,7 @@ SIGNATURES = {
     "ef_topk_compress": (C.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _sz, _p, _p, _u32, _p]),
     "ef_topk_compress_noalloc": (C.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _p, _u32, _p]),
     "ef_topk_workspace_status": (C.c_int, [_p, _p, _p]),
+    "ef_topk_workspace_paths": (C.c_int, [_p, _i32, _p, _p]),
     "ef_topk_segmented_workspace_bytes": (_sz, [_i32, _p, _p]),
     "ef_topk_compress_segmented": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _sz, _p, _p, _u32, _p]),
     "ef_sign_workspace_bytes": (_sz, [_i64]),
@@ -165,6 +166,20 @@ def ef_topk_workspace_status(ws, stray=None, device=None):
     _need(stray, torch.int32, dev, "stray", 1)
     _check(lib().ef_topk_workspace_status(_ptr(ws), _ptr(stray), _stream(dev)), "ef_topk_workspace_status")
     return stray
+
+
+def ef_topk_workspace_paths(ws, nseg=1, out=None, device=None):
+    """Device int32 [nseg, 2]: per tensor of the last top-k call on ws (nseg
+    tensors), 1 if it took the exact full-pass selection else 0, and the
+    candidates its streaming pass collected.  ws=None: the allocation-free
+    call's static scratch on `device`."""
+    dev = ws.device if ws is not None else torch.device(device if device is not None else "cuda")
+    if out is None:
+        out = torch.empty((max(0, nseg), 2), dtype=torch.int32, device=dev)
+    _need(out, torch.int32, dev, "out", 2 * nseg)
+    _check(lib().ef_topk_workspace_paths(_ptr(ws), nseg, _ptr(out), _stream(dev)),
+           "ef_topk_workspace_paths")
+    return out
 
 
 EF_TOPK_NOALLOC_SCRATCH_BYTES = 32 << 20

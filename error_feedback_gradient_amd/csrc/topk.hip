@@ -260,11 +260,11 @@ struct Layout {
     size_t total;
 };
 
-static Layout make_layout(const Plan& p) {
-    Layout L{};
+// The part of the layout that depends on the number of tensors alone: the
+// tables, the hints and the per-tensor state (L.status .. L.state).
+static size_t layout_prefix(size_t ns, Layout& L) {
     size_t at = 0;
     auto take = [&](size_t bytes) { size_t o = at; at = round_up(at + bytes, 256); return o; };
-    const size_t ns = static_cast<size_t>(p.nseg);
     // word 0: indices the call found out of their tensor's range in its own
     // workspace entries (written as part of the tables, so it starts at 0)
     L.status = take(256);
@@ -280,6 +280,14 @@ static Layout make_layout(const Plan& p) {
     // (neither the tables' copy nor the clearing touches it)
     L.hint = take(ns * 4);
     L.state = take(ns * sizeof(SegState));
+    return at;
+}
+
+static Layout make_layout(const Plan& p) {
+    Layout L{};
+    size_t at = layout_prefix(static_cast<size_t>(p.nseg), L);
+    auto take = [&](size_t bytes) { size_t o = at; at = round_up(at + bytes, 256); return o; };
+    const size_t ns = static_cast<size_t>(p.nseg);
     L.shist = take(ns * static_cast<size_t>(p.hcopies) * kSampleStride * 4);
     L.rhist = take((3 + kSpec) * ns * static_cast<size_t>(p.hcopies) * kHistWords * 4);
     L.grp_cnt = take(static_cast<size_t>(p.G) * 4);
@@ -2408,6 +2416,13 @@ int ef_topk_compress_noalloc(const float* g, float* e, int64_t n, int64_t k, flo
 
 __global__ void k_copy_status(const uint32_t* __restrict__ status, uint32_t* __restrict__ out) { *out = *status; }
 
+__global__ void k_copy_paths(const topk::SegState* __restrict__ st, int32_t nseg, uint32_t* __restrict__ out) {
+    for (int s = blockIdx.x * blockDim.x + threadIdx.x; s < nseg; s += gridDim.x * blockDim.x) {
+        out[2 * s] = st[s].fallback;
+        out[2 * s + 1] = st[s].ncand;
+    }
+}
+
 int ef_topk_workspace_status(const void* ws, uint32_t* stray, void* stream) {
     if (!stray) return fail(EF_EINVAL, "ef_topk_workspace_status: stray must not be NULL");
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -2415,6 +2430,21 @@ int ef_topk_workspace_status(const void* ws, uint32_t* stray, void* stream) {
     if (!w) EF_TRY(topk::scratch_address(s, &w));
     if (!aligned256(w)) return fail(EF_EINVAL, "ef_topk_workspace_status: workspace must be 256-byte aligned");
     return launch("topk_status", k_copy_status, dim3(1), dim3(1), s, static_cast<const uint32_t*>(w), stray);
+}
+
+int ef_topk_workspace_paths(const void* ws, int32_t nseg, uint32_t* out, void* stream) {
+    if (nseg < 0) return fail(EF_EINVAL, "ef_topk_workspace_paths: nseg must be >= 0 (got %d)", nseg);
+    if (nseg == 0) return EF_OK;
+    if (!out) return fail(EF_EINVAL, "ef_topk_workspace_paths: out must not be NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* w = const_cast<void*>(ws);
+    if (!w) EF_TRY(topk::scratch_address(s, &w));
+    if (!aligned256(w)) return fail(EF_EINVAL, "ef_topk_workspace_paths: workspace must be 256-byte aligned");
+    topk::Layout L{};
+    (void)topk::layout_prefix(static_cast<size_t>(nseg), L);
+    const topk::SegState* st = reinterpret_cast<const topk::SegState*>(static_cast<const uint8_t*>(w) + L.state);
+    return launch("topk_paths", k_copy_paths, dim3(static_cast<unsigned>(std::min<int64_t>(1024, cdiv(nseg, 256)))),
+                  dim3(256), s, st, nseg, out);
 }
 
 size_t ef_topk_segmented_workspace_bytes(int32_t nseg, const int64_t* seg_off, const int64_t* seg_k) {

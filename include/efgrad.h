@@ -88,7 +88,13 @@ const char* ef_version(void);
  *              are reduced in a fixed order, so they repeat bit for bit)
  * g is read only.  0 <= k <= n <= 2^31 - 1.  vals/idx may be NULL when k = 0.
  * ws: device workspace of at least ef_topk_workspace_bytes(n, k) bytes, 256-byte
- * aligned; its contents on entry do not matter.
+ * aligned; its contents on entry do not change the results.  A call leaves its
+ * exact threshold in the workspace, and the next call on it uses that value
+ * to sample the magnitudes around it at a finer resolution (error feedback
+ * crowds values just below the threshold, and the finer sample keeps the
+ * candidate set small there); any other contents only forgo that gain.  A
+ * call that asks for stats does not use it, so its statistics depend on its
+ * inputs alone.
  * flags: 0 or EF_FLAG_FORCE_FALLBACK.
  * ------------------------------------------------------------------------ */
 size_t ef_topk_workspace_bytes(int64_t n, int64_t k);
@@ -103,6 +109,17 @@ int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals
  * else wrote to the workspace during the call.  *stray is a device uint32;
  * the copy is enqueued on `stream` after the calls before it. */
 int ef_topk_workspace_status(const void* ws, uint32_t* stray, void* stream);
+
+/* Which path each tensor of the last top-k call on a workspace took (ws; NULL
+ * = the static scratch of ef_topk_compress_noalloc on the stream's device),
+ * for monitoring how often the sample misjudges the threshold.  nseg is the
+ * number of tensors of that call (1 for ef_topk_compress).  out (device
+ * uint32[2 * nseg]): out[2s] = 1 when tensor s took the exact full-pass
+ * selection, else 0; out[2s + 1] = the candidates its streaming pass
+ * collected (keys >= T_lo), 0 for a tensor with k = 0 or k = n.  The copy is
+ * enqueued on `stream` after the calls before it; it reads what a call with
+ * nseg tensors and at least one element left in the workspace. */
+int ef_topk_workspace_paths(const void* ws, int32_t nseg, uint32_t* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Allocation-free top-k, for callers that cannot allocate device memory

@@ -449,3 +449,104 @@ def test_workspace_status_zero_after_calls():
     for flags in (0, efg.EF_FLAG_FORCE_FALLBACK):
         efg.ef_topk_compress(to_dev(g, dev), to_dev(e, dev), k, ws=ws, flags=flags)
         assert int(host(efg.ef_topk_workspace_status(ws))[0]) == 0
+
+
+def drift_chain(g, n, k, steps, with_stats, dev):
+    """`steps` error-feedback steps with the same gradient every step (the
+    residual of the slow coordinates grows until it is kept, so values crowd
+    just below the threshold); per step the path and candidates of the call
+    (ef_topk_workspace_paths).  Returns them, e before the last step and the
+    last step's outputs."""
+    e = torch.zeros(n, dtype=torch.float32, device=dev)
+    ws = efg.workspace(efg.ef_topk_workspace_bytes(n, k), dev)
+    vals = torch.empty(k, dtype=torch.float32, device=dev)
+    idx = torch.empty(k, dtype=torch.int32, device=dev)
+    st = torch.zeros(2, dtype=torch.float64, device=dev) if with_stats else None
+    paths = torch.empty((steps, 2), dtype=torch.int32, device=dev)
+    e_before = None
+    for t in range(steps):
+        if t == steps - 1:
+            e_before = host(e).copy()
+        efg.ef_topk_compress(g, e, k, vals=vals, idx=idx, ws=ws, stats=st)
+        efg.ef_topk_workspace_paths(ws, 1, out=paths[t])
+    return host(paths), e_before, host(vals), host(idx), host(e)
+
+
+@pytest.mark.parametrize("n", [4_000_000, 20_000_000])  # split stream / one wave per region
+def test_drift_chain_keeps_candidates_few(n):
+    """Under a gradient with a drift the residual crowds just below the
+    threshold.  The call samples the magnitudes around its previous
+    threshold at 1/1024 octave, so the candidates stay near k and no step
+    takes the exact fallback; a call that asks for statistics samples the
+    12-bit bins only and, as the control, collects many times k.  Both
+    chains keep identical results at every step (the path never changes
+    them), and the last step matches the oracle."""
+    dev = device()
+    k = n // 200
+    steps = 500
+    g_np = gen.large_gradient(3, n=n)
+    g = to_dev(g_np, dev)
+    p_fine, e_prev, v, i, e_last = drift_chain(g, n, k, steps, False, dev)
+    p_ctrl, _, v2, i2, e2 = drift_chain(g, n, k, steps, True, dev)
+    tail = p_fine[-100:]
+    say(f"n={n} k={k}: fine max {p_fine[:, 1].max() / k:.2f} k, control max {p_ctrl[:, 1].max() / k:.2f} k, "
+        f"control fallbacks {int(p_ctrl[:, 0].sum())}")
+    assert int(p_fine[:, 0].sum()) == 0, "a step took the exact fallback with the fine window"
+    assert tail[:, 1].max() <= 2.5 * k, tail[:, 1].max() / k
+    assert p_ctrl[:, 1].max() >= 3 * k or int(p_ctrl[:, 0].sum()) > 0, "the control chain did not crowd"
+    assert_bits_equal(i2, i, "idx fine vs control")
+    assert_bits_equal(v2, v, "vals fine vs control")
+    assert_bits_equal(e2, e_last, "e fine vs control")
+    ov, oi, oe, _ = oracle.topk(g_np, e_prev, k)
+    assert_bits_equal(i, oi, "idx last step")
+    assert_bits_equal(v, ov, "vals last step")
+    assert_bits_equal(e_last, oe, "e last step")
+
+
+def test_workspace_garbage_changes_nothing():
+    """Workspace bytes left by anything (the hint of the last threshold
+    included) only change the path: random bytes in the workspace, then the
+    same call on a cleared workspace, both equal to the oracle."""
+    dev = device()
+    n, k = 6_000_011, 6000
+    g, e = inputs(n, "lognormal", 12)
+    ov, oi, oe, _ = oracle.topk(g, e, k)
+    nb = efg.ef_topk_workspace_bytes(n, k)
+    gz = torch.Generator(device=dev)
+    gz.manual_seed(77)
+    for fill in ("random", "zero", "ones"):
+        ws = efg.workspace(nb, dev)
+        if fill == "random":
+            ws.copy_(torch.randint(0, 256, (ws.numel(),), generator=gz, device=dev, dtype=torch.int32).to(torch.uint8))
+        elif fill == "zero":
+            ws.zero_()
+        else:
+            ws.fill_(255)
+        ed = to_dev(e, dev)
+        v, i = efg.ef_topk_compress(to_dev(g, dev), ed, k, ws=ws)
+        assert_bits_equal(host(i), oi, f"idx {fill}")
+        assert_bits_equal(host(v), ov, f"vals {fill}")
+        assert_bits_equal(host(ed), oe, f"e {fill}")
+
+
+def test_workspace_paths_segmented():
+    """ef_topk_workspace_paths over a layer-wise call: 1 for every selecting
+    tensor after a forced fallback, 0 on the sampled path; 0 and no
+    candidates for tensors with k = 0 or k = n; candidates >= k otherwise."""
+    dev = device()
+    sizes = [70_000, 5, 300_000, 1000, 2_000_000]
+    ks = [700, 0, 3000, 1000, 20_000]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    kk = np.array(ks, np.int64)
+    n = int(off[-1])
+    g, e = inputs(n, "normal", 21)
+    ws = efg.workspace(efg.ef_topk_segmented_workspace_bytes(off, kk), dev)
+    for flags, want in ((efg.EF_FLAG_FORCE_FALLBACK, 1), (0, 0)):
+        efg.ef_topk_compress_segmented(to_dev(g, dev), to_dev(e, dev), off, kk, ws=ws, flags=flags)
+        p = host(efg.ef_topk_workspace_paths(ws, len(ks)))
+        for s_, (sz, kv) in enumerate(zip(sizes, ks)):
+            if kv in (0, sz):
+                assert p[s_, 0] == 0 and p[s_, 1] == 0, (flags, s_, p[s_])
+            else:
+                assert p[s_, 0] == want, (flags, s_, p[s_])
+                assert p[s_, 1] >= kv, (flags, s_, p[s_])
