@@ -108,17 +108,21 @@ constexpr int kSampleWords = kSampleBins + kSampleCoarse;
 constexpr int kSampleShift = 19;                   // 31-bit key >> 19 = 12 bits
 // Each copy of a sample histogram also keeps a window of fine bins around the
 // tensor's threshold of the previous call on the workspace (its hint):
-// kFineBins bins of 2^kFineShift key units (1/1024 octave) over two octaves,
-// their sums in groups of 64, and the count of samples above the window.
+// kFineBins bins of 2^kFineShift key units (1/1024 octave) over the hint
+// +-1/4 octave, their sums in groups of 64, and the count of samples above
+// the window.  The sample ranks for T_lo and T_hi lie within about a tenth
+// of an octave of T, and T moves little from one step to the next; when it
+// moves farther, the 12-bit bins decide as they would without a hint.
 // Where the residual has crowded values just below the threshold (the steady
 // state of error feedback under a gradient with a drift), a 12-bit bin below
 // T can hold many times k elements; the fine window puts T_lo within 1/1024
 // octave of the sample rank it stands for, so the candidates stay few.
 constexpr int kFineShift = 13;
-constexpr int kFineBins = 2048;
+constexpr int kFineBins = 512;
 constexpr int kFineGroups = kFineBins / 64;
 constexpr uint32_t kFineSpan = static_cast<uint32_t>(kFineBins) << kFineShift;
-constexpr int kFineWords = kFineBins + kFineGroups + 32;  // bins, group sums, count above, padding
+constexpr int kFineWords = kFineBins + 32;  // bins, group sums, count above, padding
+static_assert(kFineGroups + 1 <= 32, "group sums and the count above fit the padding");
 constexpr int kSampleStride = kSampleWords + kFineWords;  // words of one histogram copy
 static_assert(kSampleStride % 4 == 0, "histogram copies stay 16-byte aligned");
 #ifndef EFG_CHUNK
@@ -488,12 +492,12 @@ __global__ __launch_bounds__(kBlock) void k_init(uint4* zero, int64_t nvec, uint
 }
 
 // The window of fine sample bins of a tensor whose previous exact threshold
-// was `hint`: [base, base + kFineSpan), from one octave below the hint's
-// 12-bit bin up.  Any 32-bit value is a valid hint (a workspace holding
-// something else only leaves the window where no rank falls).
+// was `hint`: [base, base + kFineSpan), centred on the hint (rounded down to
+// a fine bin edge).  Any 32-bit value is a valid hint: a workspace holding
+// something else only leaves the window where no rank falls.
 __device__ __forceinline__ uint32_t fine_base(uint32_t hint) {
-    const uint32_t c = (hint & 0x7fffffffu) & ~((1u << kSampleShift) - 1u);
-    return c >= (1u << 23) ? c - (1u << 23) : 0u;
+    const uint32_t c = (hint & 0x7fffffffu) & ~((1u << kFineShift) - 1u);
+    return c >= kFineSpan / 2 ? c - kFineSpan / 2 : 0u;
 }
 
 // The sample histograms (top 12 key bits of x = g + e, and with FINE the fine
