@@ -550,3 +550,54 @@ def test_workspace_paths_segmented():
             else:
                 assert p[s_, 0] == want, (flags, s_, p[s_])
                 assert p[s_, 1] >= kv, (flags, s_, p[s_])
+
+
+def test_drift_chain_segmented_keeps_candidates_few():
+    """The same drift chain over a layer-wise call of 24 tensors of mixed
+    sizes and scales (both stream shapes' sizes: the call has more than 4096
+    regions): each tensor keeps its own hint, so every tensor's candidates
+    stay near its k and none falls back; the chain's results equal those of
+    the statistics control (12-bit bins only) at the end, and the last step
+    matches the oracle."""
+    dev = device()
+    rs = np.random.default_rng(2026)
+    sizes = [int(x) for x in rs.choice([3000, 50_000, 300_007, 1_000_000, 2_400_000], size=24)]
+    ks = [max(1, s_ // 200) for s_ in sizes]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    kk = np.array(ks, np.int64)
+    n, K = int(off[-1]), int(kk.sum())
+    g_np = gen.large_gradient(5, n=n)
+    for t in range(len(sizes)):
+        g_np[off[t]:off[t + 1]] *= np.float32(10.0 ** rs.uniform(-3, 1))
+    g = to_dev(g_np, dev)
+    steps = 400
+    res = []
+    for with_stats in (False, True):
+        e = torch.zeros(n, dtype=torch.float32, device=dev)
+        ws = efg.workspace(efg.ef_topk_segmented_workspace_bytes(off, kk), dev)
+        vals = torch.empty(K, dtype=torch.float32, device=dev)
+        idx = torch.empty(K, dtype=torch.int32, device=dev)
+        st = torch.zeros(2 * len(ks), dtype=torch.float64, device=dev) if with_stats else None
+        paths = torch.empty((steps, len(ks), 2), dtype=torch.int32, device=dev)
+        e_prev = None
+        for t in range(steps):
+            if t == steps - 1:
+                e_prev = host(e).copy()
+            efg.ef_topk_compress_segmented(g, e, off, kk, vals=vals, idx=idx, ws=ws, stats=st)
+            efg.ef_topk_workspace_paths(ws, len(ks), out=paths[t])
+        res.append((host(paths), e_prev, host(vals), host(idx), host(e)))
+    (pf, e_prev, v, i, e_last), (pc, _, v2, i2, e2) = res
+    ratio_f = (pf[-100:, :, 1] / kk[None, :]).max()
+    ratio_c = (pc[:, :, 1] / kk[None, :]).max()
+    say(f"segmented drift: fine max {ratio_f:.2f} k, control max {ratio_c:.2f} k, "
+        f"control fallbacks {int(pc[:, :, 0].sum())}")
+    assert int(pf[:, :, 0].sum()) == 0, "a tensor took the exact fallback with the fine window"
+    assert ratio_f <= 2.5, ratio_f
+    assert ratio_c >= 3.0 or int(pc[:, :, 0].sum()) > 0, "the control chain did not crowd"
+    assert_bits_equal(i2, i, "idx fine vs control")
+    assert_bits_equal(v2, v, "vals fine vs control")
+    assert_bits_equal(e2, e_last, "e fine vs control")
+    ov, oi, oe, _ = oracle.topk_segmented(g_np, e_prev, off, kk)
+    assert_bits_equal(i, oi, "idx last step")
+    assert_bits_equal(v, ov, "vals last step")
+    assert_bits_equal(e_last, oe, "e last step")
