@@ -240,6 +240,10 @@ def main():
     efg.profile_enable(False)
     bare_gbps = STREAM_BYTES_PER_ELEM * n / (bare_ms / max(1, bare_n) * 1e-3) / 1e9
     log(f"bench: forced fallback {forced_ms['median']:.3f} ms/step, bare stream {bare_gbps:.0f} GB/s")
+    drift = drift_chain(lambda g_, e_: efg.ef_topk_compress(g_, e_, k, vals=vals, idx=idx, ws=ws),
+                        grads[:2], n, ws, [k], 1000 if args.n is None else 200, dev)
+    log(f"bench: {drift['steps']} drifted steps: median {drift['median_ms']:.3f} ms, "
+        f"{drift['fallback_steps']} on the exact fallback")
 
     del grads
     add_gbps = add_ceiling(dev)  # before the copies: those calibrate the counters
@@ -284,6 +288,7 @@ def main():
         "bare_stream_GBps": bare_gbps,
         "bare_stream_frac": bare_gbps / PEAK_HBM_GBPS,
         "forced_fallback_ms": forced_ms,
+        "drift_chain": drift,
         "torch_copy_GBps": copy_gbps,
         "torch_add_GBps": add_gbps,
         "kernel_ms_one_step": breakdown,
@@ -429,6 +434,42 @@ def time_steps(step, W, K, kernel_label):
     kms, launches = kernel_ms(step, range(W, W + K), kernel_label)
     # time of the labelled kernels per step (equal to the mean launch when one kernel matches)
     return start.elapsed_time(stop) / K, kms / K, launches
+
+
+def drift_chain(call, g_pair, n, ws, ks, steps, dev):
+    """Outside the timed region: `steps` chained top-k calls from a zero
+    residual with two gradients alternating.  That is a drift: the residual of
+    every coordinate that is not kept grows step after step until it is, so
+    the values crowd just below the threshold, the regime where the sample's
+    candidate window matters most.  Each call is timed by its own HIP events,
+    and ef_topk_workspace_paths records each tensor's path and candidates.
+    Returns {"steps", "median_ms", "p90_ms", "fallback_steps" (steps on which
+    some tensor took the exact full-pass selection), "max_candidates_over_k"}."""
+    import numpy as np
+    import torch
+
+    import error_feedback_gradient_amd as efg
+
+    ks = np.asarray(ks, np.int64)
+    e = torch.zeros(n, dtype=torch.float32, device=dev)
+    paths = torch.empty((steps, ks.size, 2), dtype=torch.int32, device=dev)
+    evs = []
+    for t in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call(g_pair[t % 2], e)
+        b.record()
+        efg.ef_topk_workspace_paths(ws, int(ks.size), out=paths[t])
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    p = paths.cpu().numpy()
+    sel = ks > 0
+    ratio = float((p[:, sel, 1] / ks[sel][None, :]).max()) if sel.any() else 0.0
+    del e
+    return {"steps": steps, "gradients": "two of the workload's gradients alternating, from a zero residual",
+            "median_ms": ms[len(ms) // 2], "p90_ms": ms[int(0.9 * (len(ms) - 1))],
+            "fallback_steps": int((p[:, :, 0].sum(axis=1) > 0).sum()), "max_candidates_over_k": ratio}
 
 
 def per_step_ms(step, steps, dev, flush_bytes=0):
@@ -650,6 +691,14 @@ def other_workload(args):
             step(t)
         extra["host_issue_us"] = (time.perf_counter() - t0) / K * 1e6
         torch.cuda.synchronize()
+        if wl == "flat":
+            extra["drift_chain"] = drift_chain(
+                lambda g_, e_: efg.ef_topk_compress(g_, e_, k, vals=vals, idx=idx, ws=ws), grads[:2], n, ws, [k],
+                400, dev)
+        else:
+            extra["drift_chain"] = drift_chain(
+                lambda g_, e_: efg.ef_topk_compress_segmented(g_, e_, off, ks, vals=vals, idx=idx, ws=ws),
+                grads[:2], n, ws, ks, 400, dev)
     if wl in ("flat", "decode"):
         # inputs fit the 256 MB Infinity Cache: also time each step after a 1 GiB write
         extra["cold_step_ms"] = per_step_ms(step, range(W, W + K), dev, flush_bytes=1 << 30)
