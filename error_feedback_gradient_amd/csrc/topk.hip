@@ -7,11 +7,15 @@
 //
 // How (per tensor, "segment"; the flat call is one segment):
 //   1. sample     a strided sample of x = g + e is histogrammed on the top 12
-//                 bits of its magnitude key.  Two bin edges are read off it
-//                 (by one block per tensor; in a call with few regions, by the
-//                 stream's blocks themselves): T_lo, with (by a wide
-//                 statistical margin) at least k elements of the tensor above
-//                 it, and T_hi, with (very likely) fewer than k above it.
+//                 bits of its magnitude key, and at 1/1024 octave around the
+//                 tensor's threshold of the previous call on the workspace.
+//                 Two bin edges are read off it (by one wave per tensor; in a
+//                 call with few regions, by the stream's blocks themselves),
+//                 in the fine bins where they hold the rank: T_lo, with (by a
+//                 wide statistical margin) at least k elements of the tensor
+//                 above it, and T_hi, with (very likely) fewer than k above
+//                 it.  The fine bins keep the window tight where error
+//                 feedback crowds the residual just below T.
 //   2. stream     ONE pass over the tensor, one wave per 4096-element region
 //                 (eight waves per region in a call with few regions): read g
 //                 and e (128-bit non-temporal loads, all of a wave's in flight
@@ -46,8 +50,9 @@
 // (and, for the first digits the sample's window spans, the second one) and
 // put x back wherever the stream cleared it; one more radix pass, which
 // also keeps each block's histogram, from which the count kernel takes the
-// blocks' totals; and the write.  Only integer atomics are used, so results
-// do not depend on timing.
+// blocks' totals; and the write.  The count kernel leaves T in the workspace
+// as the next call's hint.  Only integer atomics are used, so results do not
+// depend on timing, and no path (nor the hint) changes them.
 #include <math.h>
 #include <string.h>
 
