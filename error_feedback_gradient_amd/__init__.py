@@ -31,7 +31,7 @@ SIGNATURES = {
     "ef_topk_compress": (C.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _sz, _p, _p, _u32, _p]),
     "ef_topk_compress_noalloc": (C.c_int, [_p, _p, _i64, _i64, _p, _p, _p, _p, _u32, _p]),
     "ef_topk_workspace_status": (C.c_int, [_p, _p, _p]),
-    "ef_topk_workspace_paths": (C.c_int, [_p, _i32, _p, _p]),
+    "ef_topk_workspace_paths": (C.c_int, [_p, _sz, _i32, _p, _p]),
     "ef_topk_segmented_workspace_bytes": (_sz, [_i32, _p, _p]),
     "ef_topk_compress_segmented": (C.c_int, [_p, _p, _i32, _p, _p, _p, _p, _p, _sz, _p, _p, _u32, _p]),
     "ef_sign_workspace_bytes": (_sz, [_i64]),
@@ -177,7 +177,8 @@ def ef_topk_workspace_paths(ws, nseg=1, out=None, device=None):
     if out is None:
         out = torch.empty((max(0, nseg), 2), dtype=torch.int32, device=dev)
     _need(out, torch.int32, dev, "out", 2 * nseg)
-    _check(lib().ef_topk_workspace_paths(_ptr(ws), nseg, _ptr(out), _stream(dev)),
+    _check(lib().ef_topk_workspace_paths(_ptr(ws), 0 if ws is None else ws.numel(), nseg, _ptr(out),
+                                         _stream(dev)),
            "ef_topk_workspace_paths")
     return out
 

@@ -2441,16 +2441,20 @@ int ef_topk_workspace_status(const void* ws, uint32_t* stray, void* stream) {
     return launch("topk_status", k_copy_status, dim3(1), dim3(1), s, static_cast<const uint32_t*>(w), stray);
 }
 
-int ef_topk_workspace_paths(const void* ws, int32_t nseg, uint32_t* out, void* stream) {
+int ef_topk_workspace_paths(const void* ws, size_t ws_bytes, int32_t nseg, uint32_t* out, void* stream) {
     if (nseg < 0) return fail(EF_EINVAL, "ef_topk_workspace_paths: nseg must be >= 0 (got %d)", nseg);
     if (nseg == 0) return EF_OK;
     if (!out) return fail(EF_EINVAL, "ef_topk_workspace_paths: out must not be NULL");
+    topk::Layout L{};
+    const size_t need = topk::layout_prefix(static_cast<size_t>(nseg), L);
+    if (!ws) ws_bytes = EF_TOPK_NOALLOC_SCRATCH_BYTES;
+    if (ws_bytes < need)
+        return fail(EF_EWS, "ef_topk_workspace_paths: %d tensors need a workspace of at least %zu bytes (got %zu)",
+                    nseg, need, ws_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* w = const_cast<void*>(ws);
     if (!w) EF_TRY(topk::scratch_address(s, &w));
     if (!aligned256(w)) return fail(EF_EINVAL, "ef_topk_workspace_paths: workspace must be 256-byte aligned");
-    topk::Layout L{};
-    (void)topk::layout_prefix(static_cast<size_t>(nseg), L);
     const topk::SegState* st = reinterpret_cast<const topk::SegState*>(static_cast<const uint8_t*>(w) + L.state);
     return launch("topk_paths", k_copy_paths, dim3(static_cast<unsigned>(std::min<int64_t>(1024, cdiv(nseg, 256)))),
                   dim3(256), s, st, nseg, out);

@@ -110,16 +110,18 @@ int ef_topk_compress(const float* g, float* e, int64_t n, int64_t k, float* vals
  * the copy is enqueued on `stream` after the calls before it. */
 int ef_topk_workspace_status(const void* ws, uint32_t* stray, void* stream);
 
-/* Which path each tensor of the last top-k call on a workspace took (ws; NULL
- * = the static scratch of ef_topk_compress_noalloc on the stream's device),
- * for monitoring how often the sample misjudges the threshold.  nseg is the
+/* Which path each tensor of the last top-k call on a workspace took (ws of
+ * ws_bytes bytes; NULL = the static scratch of ef_topk_compress_noalloc on the
+ * stream's device, ws_bytes ignored), for monitoring how often the sample
+ * misjudges the threshold.  nseg is the
  * number of tensors of that call (1 for ef_topk_compress).  out (device
  * uint32[2 * nseg]): out[2s] = 1 when tensor s took the exact full-pass
  * selection, else 0; out[2s + 1] = the candidates its streaming pass
  * collected (keys >= T_lo), 0 for a tensor with k = 0 or k = n.  The copy is
  * enqueued on `stream` after the calls before it; it reads what a call with
- * nseg tensors and at least one element left in the workspace. */
-int ef_topk_workspace_paths(const void* ws, int32_t nseg, uint32_t* out, void* stream);
+ * nseg tensors and at least one element left in the workspace.  EF_EWS when
+ * ws_bytes is too small to hold the state of nseg tensors. */
+int ef_topk_workspace_paths(const void* ws, size_t ws_bytes, int32_t nseg, uint32_t* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Allocation-free top-k, for callers that cannot allocate device memory

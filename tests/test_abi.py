@@ -133,6 +133,23 @@ def test_segmented_argument_checks():
     assert L.ef_topk_compress_segmented(FAKE, FAKE, -1, None, None, FAKE, FAKE, FAKE, 0, None, None, 0, None) == efg.EF_EINVAL
 
 
+def test_workspace_paths_argument_checks():
+    """ef_topk_workspace_paths refuses, on the host, a workspace too small for
+    the state of nseg tensors (its kernel would read past it), a NULL output
+    and a negative nseg; nseg = 0 is a no-op."""
+    L = efg.lib()
+    off = np.array([0, 100_000, 300_000], np.int64)
+    ks = np.array([100, 200], np.int64)
+    p = lambda a: a.ctypes.data_as(C.c_void_p)
+    need = L.ef_topk_segmented_workspace_bytes(2, p(off), p(ks))
+    assert L.ef_topk_workspace_paths(FAKE, 256, 2, FAKE, None) == efg.EF_EWS
+    assert "workspace" in efg.last_error()
+    assert L.ef_topk_workspace_paths(FAKE, need, 1_000_000, FAKE, None) == efg.EF_EWS
+    assert L.ef_topk_workspace_paths(FAKE, need, 2, None, None) == efg.EF_EINVAL
+    assert L.ef_topk_workspace_paths(FAKE, need, -1, FAKE, None) == efg.EF_EINVAL
+    assert L.ef_topk_workspace_paths(FAKE, 0, 0, None, None) == efg.EF_OK
+
+
 def test_bert_layout_workspace():
     import gen
     off, ks = gen.bert_segments()
