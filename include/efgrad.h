@@ -225,7 +225,9 @@ int ef_sign_compress(const float* g, float* e, float* m, int64_t n, float beta1,
  * signs (ef_sign_compress with m = NULL) were summed into qsum (exact integer
  * sum, 1 <= nworkers <= 127):
  *   ghat = qsum / nworkers;  m = beta1*m + (1-beta1)*ghat;  v unchanged
- *   (frozen after warm-up: only the signs are exchanged);  w as above.
+ *   (frozen at its value after warm-up, as the published 1-bit Adam does; the
+ *   pages give v no rule here, and ef_onebit_adam_update_var is the other
+ *   reading);  w as above.
  *   With nworkers = 1, m matches ef_sign_compress's fused momentum bit for bit.
  * *nonfinite (device uint32, nullable, overwritten) counts non-finite new m,
  * v (warm-up only) and w.  g, m, v, w 16-byte aligned; qsum 4-byte aligned;

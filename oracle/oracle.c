@@ -634,9 +634,11 @@ int orc_adam_step(const float* g, float* m, float* v, float* w, int64_t n, float
  * (orc_sign with m = NULL), so the averaged compressed gradient is
  *   ghat = qsum / nworkers                      (float32 division)
  * [ONEBIT] "2.2 动量修正策略": m' = beta1 * m + (1 - beta1) * ghat.
- * READING: the variance is frozen during compression (only the signs are
- * exchanged, so no worker holds the averaged full-precision gradient that a
- * shared v would need); v is read, never written.  w' = adam_param(w, m', v).
+ * READING: the pages list a variance in the state ("3.1 关键数据结构设计") but
+ * give it no rule during compression.  This function keeps v frozen at its
+ * value after warm-up (the choice of the published 1-bit Adam algorithm, made
+ * outside these pages); v is read, never written.  w' = adam_param(w, m', v).
+ * The other reading, v updated from ghat, is orc_adam_step fed ghat.
  * With one worker ghat = q and m' is exactly orc_sign's momentum.
  * 1 <= nworkers <= 127 (the sum fits int8).
  */
