@@ -198,7 +198,7 @@ def main():
     step(0)
     torch.cuda.synchronize()
     labels = ["topk_init", "topk_sample_hist", "topk_sample_select", "topk_stream", "topk_compact",
-              "topk_hist", "topk_count", "topk_write",
+              "topk_hist", "topk_write",
               "blocks_clear", "blocks_count", "blocks_scan", "blocks_write", "blocks_mask"]
     breakdown = {}
     for lab in labels:

@@ -40,18 +40,19 @@
 //                 10 and 10 bits, each histogram (LDS-privatised) built by one
 //                 kernel and its digit found by the blocks of the next one.
 //   5. emit       entries with key > T, plus the first r entries with key == T
-//                 in index order, are written in index order: a count kernel
-//                 totals each block's contiguous range of the list, and every
-//                 write block starts after the totals of the blocks before it.
+//                 in index order, are written in index order: the last radix
+//                 pass leaves the suffix sums of each block's histogram of its
+//                 contiguous range of the list, and every write block finds T
+//                 itself and starts after the totals of the blocks before it
+//                 (two words of each one's suffix sums).
 //                 Their residual becomes +0 unless the stream already cleared
 //                 it; a dropped candidate that the stream cleared gets x back.
 // The exact fallback runs steps 4-5 over the whole tensor (x sits in e) in
 // three reads of x: its compaction blocks histogram x for the first digit
 // (and, for the first digits the sample's window spans, the second one) and
 // put x back wherever the stream cleared it; one more radix pass, which
-// also keeps each block's histogram, from which the count kernel takes the
-// blocks' totals; and the write.  The count kernel leaves T in the workspace
-// as the next call's hint.  Only integer atomics are used, so results do not
+// also keeps each block's suffix sums; and the write.  The write kernel
+// leaves T in the workspace as the next call's hint.  Only integer atomics are used, so results do not
 // depend on timing, and no path (nor the hint) changes them.
 #include <math.h>
 #include <string.h>
@@ -265,7 +266,7 @@ struct Plan {
 struct Layout {
     size_t status, plan, rb, gbb, sbb, cbb, hb, static_end, hint;
     size_t state, shist, rhist, grp_cnt, zero_end;
-    size_t region_cnt, cpair, dval, didx, bh, btot, spart, gpart, cpart, rpart;
+    size_t region_cnt, cpair, dval, didx, bh, spart, gpart, cpart, rpart;
     size_t total;
 };
 
@@ -305,10 +306,8 @@ static Layout make_layout(const Plan& p) {
     L.cpair = take(static_cast<size_t>(p.Ctot) * 8);
     L.dval = take(static_cast<size_t>(p.Ctot) * 4);
     L.didx = take(static_cast<size_t>(p.Ctot) * 4);
-    // per select block: its last radix histogram, and its range's counts of
-    // keys above T and equal to T
+    // per select block: the suffix sums of its last radix histogram
     L.bh = take(static_cast<size_t>(p.HB) * kBlockHistWords * 4);
-    L.btot = take(static_cast<size_t>(p.HB) * 8);
     // monitoring partials (sent, dropped energy): per region, per candidate unit, per raw unit
     L.spart = take(static_cast<size_t>(p.R) * 16);
     L.gpart = take(static_cast<size_t>(p.G) * 16);
@@ -1599,10 +1598,12 @@ __device__ __forceinline__ void digits_before(int pass, int s, int lb, const Seg
 
 // 5. radix histograms of passes 1 and 2 (pass 0 came with the compaction),
 //    each block over its contiguous range of units (of x itself: one
-//    element range).  Pass 2 also leaves, per block, its own histogram and
-//    its count of keys above the pass's prefix (bh, kBlockHistWords words
-//    each): k_count takes the block's counts above T and at T from them
-//    instead of reading its entries again.
+//    element range).  Pass 2 also leaves, per block, the suffix sums of its
+//    own histogram (bh, kBlockHistWords words each: word i counts the
+//    block's keys whose top 21 bits are above the pass's prefix or equal to
+//    it with a last digit >= i; word 1024 those above the prefix), so that
+//    the write kernel finds any block's counts above T and at T with two
+//    loads instead of reading its entries again.
 __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
                                                  const int32_t* __restrict__ hb, SegState* __restrict__ st,
                                                  const float* __restrict__ dval, const float* __restrict__ e,
@@ -1610,6 +1611,7 @@ __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __rest
                                                  uint32_t* __restrict__ bh) {
     __shared__ uint32_t h[1024];
     __shared__ uint32_t s_above[kWavesPerBlock];
+    __shared__ uint32_t s_scan[kWavesPerBlock + 1];
     const SelBlock sb = sel_block(plan, nseg, hb, st);
     if (sb.u0 >= sb.u1) return;  // never the tensor's first block, which records the digits
     uint32_t prefix, want;
@@ -1647,41 +1649,24 @@ __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __rest
         above = wave_sum(above);
         if (lane() == 0) s_above[threadIdx.x / kWave] = above;
         __syncthreads();
+        uint32_t ab = 0;
+        for (int i = 0; i < kWavesPerBlock; ++i) ab += s_above[i];
+        // thread t owns bins 4t .. 4t + 3; the bins above them sum to the
+        // block total less the threads up to t
+        static_assert(1024 == 4 * kBlock, "pass-2 suffix sums: four bins per thread");
+        const int t4 = 4 * static_cast<int>(threadIdx.x);
+        const uint32_t b0 = h[t4], b1 = h[t4 + 1], b2 = h[t4 + 2], b3 = h[t4 + 3];
+        const uint32_t mine4 = b0 + b1 + b2 + b3;
+        uint32_t tot;
+        const uint32_t before = block_excl_scan<kBlock>(mine4, s_scan, &tot);
         uint32_t* mine = bh + static_cast<size_t>(blockIdx.x) * kBlockHistWords;
-        for (int i = threadIdx.x; i < 1024; i += kBlock) mine[i] = h[i];
-        if (threadIdx.x == 0) {
-            uint32_t t = 0;
-            for (int i = 0; i < kWavesPerBlock; ++i) t += s_above[i];
-            mine[1024] = t;
-        }
+        const uint32_t s3 = ab + (tot - before - mine4) + b3;
+        mine[t4 + 3] = s3;
+        mine[t4 + 2] = s3 + b2;
+        mine[t4 + 1] = s3 + b2 + b1;
+        mine[t4] = s3 + b2 + b1 + b0;
+        if (threadIdx.x == 0) mine[1024] = ab;
     }
-}
-
-// 6a. per block: the counts of keys above T and equal to T in its range of
-//     units (every block of the tensor writes its word, 0 for an empty
-//     range), from the block's pass-2 histogram: above T are the keys above
-//     the pass's prefix and those in the bins above T's last digit; at T,
-//     that digit's bin.
-__global__ __launch_bounds__(kBlock) void k_count(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                  const int32_t* __restrict__ hb, SegState* __restrict__ st,
-                                                  const uint32_t* __restrict__ rhist, int32_t hcopies,
-                                                  const uint32_t* __restrict__ bh, uint2* __restrict__ btot,
-                                                  uint32_t* __restrict__ hint) {
-    __shared__ uint32_t lds[kWavesPerBlock + 1];
-    const SelBlock sb = sel_block(plan, nseg, hb, st);
-    if (sb.u0 >= sb.u1) {  // never the tensor's first block, which records T and r
-        if (threadIdx.x == 0) btot[blockIdx.x] = make_uint2(0u, 0u);
-        return;
-    }
-    uint32_t T, r;
-    digits_before(3, sb.s, sb.lb, plan, nseg, st, rhist, hcopies, &T, &r, hint);
-    const uint32_t d = T & 1023u;
-    const uint32_t* mine = bh + static_cast<size_t>(blockIdx.x) * kBlockHistWords;
-    uint32_t a = 0;
-    for (uint32_t i = d + 1 + threadIdx.x; i < 1024; i += kBlock) a += mine[i];
-    uint32_t tot;
-    (void)block_excl_scan<kBlock>(a, lds, &tot);
-    if (threadIdx.x == 0) btot[blockIdx.x] = make_uint2(tot + mine[1024], mine[d]);
 }
 
 // The exact fallback's write over x (in e) for one block's range of raw
@@ -1823,34 +1808,46 @@ __device__ __forceinline__ void write_raw(const SegPlan& P, const SelBlock& sb, 
     }
 }
 
-// 6b. the kept entries at their index-ordered places, each chunk read in rows
-//     as load_rows lays them out, so loads and (mostly kept-together) stores
-//     coalesce.  An entry's place is (entries with key > T before it) +
-//     min(r, entries with key == T before it): the totals of the tensor's
-//     earlier blocks (from k_count), those of the block's earlier chunks, of
-//     its earlier waves, of the wave's earlier rows, and of the row's lower
-//     lanes (ballots).  Kept entries get e = +0 unless the stream cleared them (key
-//     >= thi); dropped ones the stream cleared get x back.
+// 6. the kept entries at their index-ordered places, each chunk read in rows
+//    as load_rows lays them out, so loads and (mostly kept-together) stores
+//    coalesce.  Every block first finds T and r from the last histogram (the
+//    tensor's first block records them, and T as the next call's hint).  An
+//    entry's place is (entries with key > T before it) + min(r, entries with
+//    key == T before it): the totals of the tensor's earlier blocks (two words
+//    of each one's pass-2 suffix sums), those of the block's earlier chunks,
+//    of its earlier waves, of the wave's earlier rows, and of the row's lower
+//    lanes (ballots).  Kept entries get e = +0 unless the stream cleared them
+//    (key >= thi); dropped ones the stream cleared get x back.
 template <bool STATS>
 __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ plan, int32_t nseg,
-                                                  const int32_t* __restrict__ hb, const SegState* __restrict__ st,
+                                                  const int32_t* __restrict__ hb, SegState* __restrict__ st,
+                                                  const uint32_t* __restrict__ rhist, int32_t hcopies,
+                                                  const uint32_t* __restrict__ bh, uint32_t* __restrict__ hint,
                                                   const float* __restrict__ dval, const int32_t* __restrict__ didx,
-                                                  const uint2* __restrict__ btot,
                                                   float* __restrict__ e, float* __restrict__ vals,
                                                   int32_t* __restrict__ idx, double2* __restrict__ cpart,
                                                   double2* __restrict__ rpart, uint32_t* __restrict__ stray) {
     __shared__ uint32_t wgt[kWavesPerBlock], weq[kWavesPerBlock];
     __shared__ double2 lsum[kWavesPerBlock];
     const SelBlock sb = sel_block(plan, nseg, hb, st);
-    if (sb.u0 >= sb.u1) return;
+    if (sb.u0 >= sb.u1) return;  // never the tensor's first block, which records T and r
     const int wv = threadIdx.x / kWave;
     const int l = lane();
-    // counts before the block's range: the totals of the tensor's earlier blocks
+    uint32_t T, r;
+    digits_before(3, sb.s, sb.lb, plan, nseg, st, rhist, hcopies, &T, &r, hint);
+    const uint32_t d = T & 1023u;
+    // counts before the block's range: the tensor's earlier blocks' keys
+    // above T (suffix word d + 1) and at T (word d less word d + 1); a block
+    // with no units ran no pass 2 and counts nothing
     uint32_t gtu = 0, equ = 0;
+    const uint64_t U = sb.units, nbk = static_cast<uint64_t>(sb.nb);
     for (int b = hb[sb.s] + static_cast<int>(threadIdx.x); b < static_cast<int>(blockIdx.x); b += kBlock) {
-        const uint2 c = btot[b];
-        gtu += c.x;
-        equ += c.y;
+        const uint64_t lb = static_cast<uint64_t>(b - hb[sb.s]);
+        if ((U * lb + nbk - 1) / nbk >= (U * (lb + 1) + nbk - 1) / nbk) continue;
+        const uint32_t* m = bh + static_cast<size_t>(b) * kBlockHistWords;
+        const uint32_t gt = m[d + 1], ge = m[d];
+        gtu += gt;
+        equ += ge - gt;
     }
     gtu = wave_sum(gtu);
     equ = wave_sum(equ);
@@ -1868,7 +1865,6 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
     __syncthreads();  // wgt / weq are rewritten by the first chunk
     const SegPlan& P = plan[sb.s];
     const SegState& S = st[sb.s];
-    const uint32_t T = S.T, r = S.r;
     const uint32_t thi = sb.raw ? kNoKey : S.thi;
     const int64_t out_off = P.out_off, kseg = P.k;
     const int64_t seg_lo = P.off, seg_hi = P.off + P.n;
@@ -2135,7 +2131,6 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
     uint2* cpair = reinterpret_cast<uint2*>(at(L.cpair));
     float* dval = reinterpret_cast<float*>(at(L.dval));
     int32_t* didx = reinterpret_cast<int32_t*>(at(L.didx));
-    uint2* btot = reinterpret_cast<uint2*>(at(L.btot));
     uint32_t* bh = reinterpret_cast<uint32_t*>(at(L.bh));
     double2* spart = reinterpret_cast<double2*>(at(L.spart));
     double2* cpart = stats ? reinterpret_cast<double2*>(at(L.cpart)) : nullptr;
@@ -2198,12 +2193,10 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
     for (int pass = 1; pass < 3; ++pass)
         EF_TRY(launch("topk_hist", k_hist, hgrid, dim3(kBlock), s, pass, plan, nseg, hb, st,
                       static_cast<const float*>(dval), static_cast<const float*>(e), rhist, P.hcopies, bh));
-    EF_TRY(launch("topk_count", k_count, hgrid, dim3(kBlock), s, plan, nseg, hb, st,
-                  static_cast<const uint32_t*>(rhist), P.hcopies, static_cast<const uint32_t*>(bh), btot, hint));
     EF_TRY(launch("topk_write", stats ? k_write<true> : k_write<false>, hgrid, dim3(kBlock), s, plan, nseg, hb,
-                  static_cast<const SegState*>(st), static_cast<const float*>(dval),
-                  static_cast<const int32_t*>(didx), static_cast<const uint2*>(btot), e, vals, idx, cpart,
-                  rpart, stray));
+                  st, static_cast<const uint32_t*>(rhist), P.hcopies, static_cast<const uint32_t*>(bh), hint,
+                  static_cast<const float*>(dval), static_cast<const int32_t*>(didx), e, vals, idx, cpart, rpart,
+                  stray));
     return finish_stats();
 }
 
