@@ -48,11 +48,16 @@
 //                 Their residual becomes +0 unless the stream already cleared
 //                 it; a dropped candidate that the stream cleared gets x back.
 // The exact fallback runs steps 4-5 over the whole tensor (x sits in e) in
-// three reads of x: its compaction blocks histogram x for the first digit
-// (and, for the first digits the sample's window spans, the second one) and
-// put x back wherever the stream cleared it; one more radix pass, which
-// also keeps each block's suffix sums; and the write.  The write kernel
-// leaves T in the workspace as the next call's hint.  Only integer atomics are used, so results do not
+// two reads of x (three when T's first digit lies outside the sample's
+// window): its compaction blocks histogram x for the first digit (and, for
+// the first digits the window spans, the second one) and put x back wherever
+// the stream cleared it; then the last radix pass, which also keeps each
+// block's suffix sums and appends, in index order, every key whose top 21
+// bits are T's or above to the block's segment of the (otherwise unused)
+// dense list.  The write places from those segments; it reads x once more
+// only for a block whose segment overflowed, or when statistics, which need
+// every entry's fate, are asked for.  The write kernel leaves T in the
+// workspace as the next call's hint.  Only integer atomics are used, so results do not
 // depend on timing, and no path (nor the hint) changes them.
 #include <math.h>
 #include <string.h>
@@ -1596,6 +1601,117 @@ __device__ __forceinline__ void digits_before(int pass, int s, int lb, const Seg
 }
 
 
+// The exact fallback's ordered passes over x (in e) take a block's range of
+// raw units in chunks of kWChunk elements: wave w takes rows w kWRows ..
+// (w + 1) kWRows - 1 of 256 elements, lane l elements 4l .. 4l + 3 of a row
+// (one 128-bit load when the tensor starts 16-byte aligned, else four scalar
+// loads), so entries are ordered (chunk, wave, row, lane, element).
+constexpr int kWRows = 2;                     // rows of 256 elements per wave and chunk
+constexpr int kWChunk = kBlock * 4 * kWRows;  // 4096 elements
+static_assert(kRawChunk % kWChunk == 0, "raw units are whole write chunks");
+
+// The segment of the tensor's dense list that exact-fallback select block lb
+// (of nb) collects its possible survivors into: the dense list, sized for the
+// candidate slots, is otherwise unused on that path.  0 entries for a tensor
+// with no candidate slots (a dense selection).
+__device__ __forceinline__ uint32_t seg_cap(const SegPlan& P, int nb) {
+    return static_cast<uint32_t>(min(static_cast<int64_t>(P.nregions) * P.cap / nb, static_cast<int64_t>(0x7fffffff)));
+}
+
+// Exact fallback, last select pass over x: in the same ordered read, the
+// histogram of the last digit of the keys whose top 21 bits equal the pass's
+// prefix p1 (LDS h), the count of keys above it (*above, per thread), and the
+// keys that can be kept (top 21 bits >= p1) appended in index order to the
+// block's segment sv / si (the first segcap of them).  Returns how many such
+// keys the range holds (also past segcap).  Every thread of the block calls
+// it; wcnt needs 2 * kWavesPerBlock words.
+__device__ uint32_t collect_raw(const SegPlan& P, const SelBlock& sb, uint32_t p1, const float* __restrict__ e,
+                                float* __restrict__ sv, int32_t* __restrict__ si, uint32_t segcap, uint32_t* h,
+                                uint32_t* above, uint32_t* wcnt) {
+    const int wv = threadIdx.x / kWave;
+    const int l = lane();
+    const bool al = (P.off & 3) == 0;
+    const int64_t lo = P.off + static_cast<int64_t>(sb.u0) * kRawChunk;
+    const int64_t end = min(P.off + static_cast<int64_t>(sb.u1) * kRawChunk, P.off + P.n);
+    const int wo = wv * (kWRows * 256) + 4 * l;  // lane's first offset in the chunk, row 0
+    auto load_chunk = [&](int64_t c0, float (&x)[kWRows][4]) {
+        const int rem = static_cast<int>(min(end - c0, static_cast<int64_t>(kWChunk)));
+        const float* ec = e + c0;
+#pragma unroll
+        for (int i = 0; i < kWRows; ++i) {
+            const int o = wo + i * 256;
+            if (al && o + 3 < rem) {
+                const f4 q = __builtin_nontemporal_load(reinterpret_cast<const f4*>(ec + o));
+                x[i][0] = q.x;
+                x[i][1] = q.y;
+                x[i][2] = q.z;
+                x[i][3] = q.w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[i][c] = o + c < rem ? ec[o + c] : 0.0f;
+            }
+        }
+    };
+    uint32_t before = 0;  // collected in the earlier chunks (block-uniform)
+    uint32_t ab = 0;
+    float xn[kWRows][4];
+    if (lo < end) load_chunk(lo, xn);
+    int par = 0;  // wcnt half of this chunk: a wave may write the next chunk's half while another reads this one
+    for (int64_t c0 = lo; c0 < end; c0 += kWChunk, par ^= 1) {
+        const int rem = static_cast<int>(min(end - c0, static_cast<int64_t>(kWChunk)));
+        float x[kWRows][4];
+#pragma unroll
+        for (int i = 0; i < kWRows; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) x[i][c] = xn[i][c];
+        if (c0 + kWChunk < end) load_chunk(c0 + kWChunk, xn);
+        uint64_t bal[kWRows][4];
+        uint32_t n = 0;
+#pragma unroll
+        for (int i = 0; i < kWRows; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool ok = wo + i * 256 + c < rem;
+                const uint32_t key = key_of(x[i][c]);
+                const uint32_t top = key >> 10;
+                if (ok && top == p1) atomicAdd(&h[key & 1023u], 1u);
+                ab += (ok && top > p1) ? 1u : 0u;
+                bal[i][c] = __ballot(ok && top >= p1);
+                n += popc64(bal[i][c]);
+            }
+        uint32_t* wc = wcnt + par * kWavesPerBlock;
+        if (l == 0) wc[wv] = n;
+        __syncthreads();
+        uint32_t base = before;
+        for (int i = 0; i < kWavesPerBlock; ++i) {
+            if (i < wv) base += wc[i];
+            before += wc[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kWRows; ++i) {
+            const uint64_t any = bal[i][0] | bal[i][1] | bal[i][2] | bal[i][3];
+            if (!any) continue;  // wave-uniform
+            uint32_t pos = base;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) pos += count_below(bal[i][c]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if ((bal[i][c] >> l) & 1u) {
+                    if (pos < segcap) {
+                        sv[pos] = x[i][c];
+                        si[pos] = static_cast<int32_t>(c0 + wo + i * 256 + c);
+                    }
+                    ++pos;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) base += popc64(bal[i][c]);
+        }
+    }
+    *above = ab;
+    return before;
+}
+
 // 5. radix histograms of passes 1 and 2 (pass 0 came with the compaction),
 //    each block over its contiguous range of units (of x itself: one
 //    element range).  Pass 2 also leaves, per block, the suffix sums of its
@@ -1604,14 +1720,17 @@ __device__ __forceinline__ void digits_before(int pass, int s, int lb, const Seg
 //    it with a last digit >= i; word 1024 those above the prefix), so that
 //    the write kernel finds any block's counts above T and at T with two
 //    loads instead of reading its entries again.
-__global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
+// (eight waves per SIMD: all 2048 select blocks of a call run at once)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(8))) void k_hist(int pass, const SegPlan* __restrict__ plan, int32_t nseg,
                                                  const int32_t* __restrict__ hb, SegState* __restrict__ st,
                                                  const float* __restrict__ dval, const float* __restrict__ e,
                                                  uint32_t* __restrict__ rhist, int32_t hcopies,
-                                                 uint32_t* __restrict__ bh) {
+                                                 uint32_t* __restrict__ bh, int32_t collect,
+                                                 float* __restrict__ seg_v, int32_t* __restrict__ seg_i) {
     __shared__ uint32_t h[1024];
     __shared__ uint32_t s_above[kWavesPerBlock];
     __shared__ uint32_t s_scan[kWavesPerBlock + 1];
+    __shared__ uint32_t s_wcnt[2 * kWavesPerBlock];
     const SelBlock sb = sel_block(plan, nseg, hb, st);
     if (sb.u0 >= sb.u1) return;  // never the tensor's first block, which records the digits
     uint32_t prefix, want;
@@ -1631,7 +1750,13 @@ __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __rest
         if (ok && radix_digit(pass, key, prefix, &d)) atomicAdd(&h[d], 1u);
         if (pass == 2) above += (ok && (key >> 10) > prefix) ? 1u : 0u;
     };
-    if (sb.raw) {
+    const uint32_t segcap = seg_cap(P, sb.nb);
+    if (sb.raw && pass == 2 && collect && segcap > 0) {
+        // exact fallback: the possible survivors of the block's range go to its
+        // segment of the dense list, so the write need not read x again
+        const int64_t seg = P.cand_base + static_cast<int64_t>(sb.lb) * segcap;
+        (void)collect_raw(P, sb, prefix, e, seg_v + seg, seg_i + seg, segcap, h, &above, s_wcnt);
+    } else if (sb.raw) {
         const int64_t lo = P.off + static_cast<int64_t>(sb.u0) * kRawChunk;
         const int64_t hi = P.off + min(static_cast<int64_t>(sb.u1) * kRawChunk, P.n);
         for_keys<kRawLoads>(e, lo, hi, add);
@@ -1681,9 +1806,6 @@ __global__ __launch_bounds__(kBlock) void k_hist(int pass, const SegPlan* __rest
 // T; only those are placed (every row, when the statistics need each
 // entry's fate).  Kept entries get e = +0; nothing else changes (thi plays
 // no part: the compaction put x back everywhere).
-constexpr int kWRows = 2;                     // rows of 256 elements per wave and chunk
-constexpr int kWChunk = kBlock * 4 * kWRows;  // 4096 elements
-static_assert(kRawChunk % kWChunk == 0, "raw units are whole write chunks");
 
 template <bool STATS>
 __device__ __forceinline__ void write_raw(const SegPlan& P, const SelBlock& sb, uint32_t T, uint32_t r,
@@ -1697,10 +1819,10 @@ __device__ __forceinline__ void write_raw(const SegPlan& P, const SelBlock& sb, 
     const int64_t end = min(P.off + static_cast<int64_t>(sb.u1) * kRawChunk, P.off + P.n);
     const int wo = wv * (kWRows * 256) + 4 * l;  // lane's first offset in the chunk, row 0
     double sent = 0.0, drop = 0.0;
-    for (int64_t c0 = lo; c0 < end; c0 += kWChunk) {
-        const int rem = static_cast<int>(min(end - c0, static_cast<int64_t>(kWChunk)));  // entries in the chunk
-        float* ec = e + c0;
-        float x[kWRows][4];
+    // the lane's entries of the chunk at c0 (+0 past the range)
+    auto load_chunk = [&](int64_t c0, float (&x)[kWRows][4]) {
+        const int rem = static_cast<int>(min(end - c0, static_cast<int64_t>(kWChunk)));
+        const float* ec = e + c0;
 #pragma unroll
         for (int i = 0; i < kWRows; ++i) {
             const int o = wo + i * 256;
@@ -1715,6 +1837,20 @@ __device__ __forceinline__ void write_raw(const SegPlan& P, const SelBlock& sb, 
                 for (int c = 0; c < 4; ++c) x[i][c] = o + c < rem ? ec[o + c] : 0.0f;
             }
         }
+    };
+    // each chunk's loads are issued before the chunk before it is swept and
+    // placed, so they are in flight across its two barriers
+    float xn[kWRows][4];
+    if (lo < end) load_chunk(lo, xn);
+    for (int64_t c0 = lo; c0 < end; c0 += kWChunk) {
+        const int rem = static_cast<int>(min(end - c0, static_cast<int64_t>(kWChunk)));  // entries in the chunk
+        float* ec = e + c0;
+        float x[kWRows][4];
+#pragma unroll
+        for (int i = 0; i < kWRows; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) x[i][c] = xn[i][c];
+        if (c0 + kWChunk < end) load_chunk(c0 + kWChunk, xn);
         // sweep 1: the wave's counts, and its rows holding a key >= T
         uint32_t ngt = 0, neq = 0;
         uint32_t rows = 0;  // bit i: row i holds a key >= T (wave-uniform)
@@ -1868,87 +2004,103 @@ __global__ __launch_bounds__(kBlock) void k_write(const SegPlan* __restrict__ pl
     const uint32_t thi = sb.raw ? kNoKey : S.thi;
     const int64_t out_off = P.out_off, kseg = P.k;
     const int64_t seg_lo = P.off, seg_hi = P.off + P.n;
-    const int nsub = sb.raw ? kRawSub : 1;
     double2* part = sb.raw ? (rpart ? rpart + P.runit_base : nullptr) : (cpart ? cpart + P.cunit_base : nullptr);
+    // places one chunk of dense entries (values with their indices)
+    auto place_chunk = [&](const Chunk& c, double& sent, double& drop) {
+        float v[kRows];
+        const uint32_t j0 = load_rows(c, v);
+        int32_t ids[kRows];  // the entries' indices, loaded with the values
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) ids[i] = c.id[min(j0 + i * kWave, c.cnt - 1)];
+        // per row: the entries above T, equal to T, and with a key >= thi (a
+        // dropped one of those gets x back); wave-uniform, kept for the
+        // placing loop, which skips rows where all three are empty
+        uint64_t bgs[kRows], bes[kRows], bhs[kRows];
+        uint32_t ngt = 0, neq = 0;  // this wave's counts (wave-uniform)
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const bool ok = j0 + i * kWave < c.cnt;
+            const uint32_t key = key_of(v[i]);
+            bgs[i] = __ballot(ok && key > T);
+            bes[i] = __ballot(ok && key == T);
+            bhs[i] = __ballot(ok && key >= thi);
+            ngt += popc64(bgs[i]);
+            neq += popc64(bes[i]);
+        }
+        if (l == 0) {
+            wgt[wv] = ngt;
+            weq[wv] = neq;
+        }
+        __syncthreads();
+        uint32_t gtb = gtu, eqb = equ;
+        for (int i = 0; i < kWavesPerBlock; ++i) {
+            if (i < wv) {
+                gtb += wgt[i];
+                eqb += weq[i];
+            }
+            gtu += wgt[i];
+            equ += weq[i];
+        }
+        __syncthreads();  // wgt / weq are rewritten by the next chunk
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const uint32_t jj = j0 + i * kWave;
+            const bool ok = jj < c.cnt;
+            const uint32_t key = key_of(v[i]);
+            const uint64_t bg = bgs[i], be = bes[i];
+            if (!STATS && (bg | be | bhs[i]) == 0) continue;  // nothing to place or restore in this row
+            const bool gt = ok && key > T, eq = ok && key == T;
+            const uint32_t g_before = gtb + count_below(bg), e_before = eqb + count_below(be);
+            gtb += popc64(bg);
+            eqb += popc64(be);
+            if (!ok) continue;
+            int64_t pos = -1;
+            if (gt) pos = static_cast<int64_t>(g_before) + min(r, e_before);
+            else if (eq && e_before < r) pos = static_cast<int64_t>(g_before) + e_before;
+            if (STATS) {
+                if (pos >= 0) sent += sq_finite(v[i], key);
+                else drop += sq_finite(v[i], key);
+            }
+            const int64_t id = static_cast<int64_t>(ids[i]);
+            if (id < seg_lo || id >= seg_hi) {  // only if the workspace was overwritten meanwhile
+                atomicAdd(stray, 1u);
+                continue;
+            }
+            if (pos >= 0 && pos < kseg) {
+                vals[out_off + pos] = v[i];
+                idx[out_off + pos] = static_cast<int32_t>(id);
+                if (key < thi) e[id] = 0.0f;
+            } else if (pos < 0 && key >= thi) {
+                e[id] = v[i];
+            }
+        }
+    };
     if (sb.raw) {
+        // exact fallback: from the block's segment of the dense list when the
+        // last select pass collected every possible survivor of its range
+        // there (their count is word 0 of its suffix sums: the keys whose top
+        // 21 bits are T's or above), else by a pass over x
+        const uint32_t segcap = seg_cap(P, sb.nb);
+        const uint32_t ncol = bh[static_cast<size_t>(blockIdx.x) * kBlockHistWords];
+        if (!STATS && segcap > 0 && ncol <= segcap) {
+            const int64_t seg = P.cand_base + static_cast<int64_t>(sb.lb) * segcap;
+            double sent = 0.0, drop = 0.0;
+            for (uint32_t q = 0; q < ncol; q += kChunk) {
+                Chunk c;
+                c.v = dval + seg + q;
+                c.id = didx + seg + q;
+                c.idx_base = 0;
+                c.cnt = min(static_cast<uint32_t>(kChunk), ncol - q);
+                place_chunk(c, sent, drop);
+            }
+            return;
+        }
         write_raw<STATS>(P, sb, T, r, gtu, equ, wgt, weq, lsum, e, vals, idx, part);
         return;
     }
     for (uint32_t u = sb.u0; u < sb.u1; ++u) {  // gtu, equ: counts before the next chunk
         double sent = 0.0, drop = 0.0;
-        for (int j = 0; j < nsub; ++j) {
-            const Chunk c = chunk_of(P, S, sb.raw, u, j, dval, didx, e);
-            if (c.cnt == 0) break;
-            float v[kRows];
-            const uint32_t j0 = load_rows(c, v);
-            int32_t ids[kRows];  // the entries' indices (candidate units), loaded with the values
-            if (!sb.raw) {
-#pragma unroll
-                for (int i = 0; i < kRows; ++i) ids[i] = c.id[min(j0 + i * kWave, c.cnt - 1)];
-            }
-            // per row: the entries above T, equal to T, and with a key >= thi (a
-            // dropped one of those gets x back); wave-uniform, kept for the
-            // placing loop, which skips rows where all three are empty
-            uint64_t bgs[kRows], bes[kRows], bhs[kRows];
-            uint32_t ngt = 0, neq = 0;  // this wave's counts (wave-uniform)
-#pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                const bool ok = j0 + i * kWave < c.cnt;
-                const uint32_t key = key_of(v[i]);
-                bgs[i] = __ballot(ok && key > T);
-                bes[i] = __ballot(ok && key == T);
-                bhs[i] = __ballot(ok && key >= thi);
-                ngt += popc64(bgs[i]);
-                neq += popc64(bes[i]);
-            }
-            if (l == 0) {
-                wgt[wv] = ngt;
-                weq[wv] = neq;
-            }
-            __syncthreads();
-            uint32_t gtb = gtu, eqb = equ;
-            for (int i = 0; i < kWavesPerBlock; ++i) {
-                if (i < wv) {
-                    gtb += wgt[i];
-                    eqb += weq[i];
-                }
-                gtu += wgt[i];
-                equ += weq[i];
-            }
-            __syncthreads();  // wgt / weq are rewritten by the next chunk
-#pragma unroll
-            for (int i = 0; i < kRows; ++i) {
-                const uint32_t jj = j0 + i * kWave;
-                const bool ok = jj < c.cnt;
-                const uint32_t key = key_of(v[i]);
-                const uint64_t bg = bgs[i], be = bes[i];
-                if (!STATS && (bg | be | bhs[i]) == 0) continue;  // nothing to place or restore in this row
-                const bool gt = ok && key > T, eq = ok && key == T;
-                const uint32_t g_before = gtb + count_below(bg), e_before = eqb + count_below(be);
-                gtb += popc64(bg);
-                eqb += popc64(be);
-                if (!ok) continue;
-                int64_t pos = -1;
-                if (gt) pos = static_cast<int64_t>(g_before) + min(r, e_before);
-                else if (eq && e_before < r) pos = static_cast<int64_t>(g_before) + e_before;
-                if (STATS) {
-                    if (pos >= 0) sent += sq_finite(v[i], key);
-                    else drop += sq_finite(v[i], key);
-                }
-                const int64_t id = sb.raw ? c.idx_base + jj : static_cast<int64_t>(ids[i]);
-                if (id < seg_lo || id >= seg_hi) {  // only if the workspace was overwritten meanwhile
-                    atomicAdd(stray, 1u);
-                    continue;
-                }
-                if (pos >= 0 && pos < kseg) {
-                    vals[out_off + pos] = v[i];
-                    idx[out_off + pos] = static_cast<int32_t>(id);
-                    if (key < thi) e[id] = 0.0f;
-                } else if (pos < 0 && key >= thi) {
-                    e[id] = v[i];
-                }
-            }
-        }
+        place_chunk(chunk_of(P, S, false, u, 0, dval, didx, e), sent, drop);
         if (STATS) {
             // fixed-order block sum of the unit's sent and dropped energy
             sent = wave_sum(sent);
@@ -2192,7 +2344,8 @@ static int run(const float* g, float* e, const Plan& P, const Layout& L, Tables 
     const dim3 hgrid(static_cast<unsigned>(P.HB));
     for (int pass = 1; pass < 3; ++pass)
         EF_TRY(launch("topk_hist", k_hist, hgrid, dim3(kBlock), s, pass, plan, nseg, hb, st,
-                      static_cast<const float*>(dval), static_cast<const float*>(e), rhist, P.hcopies, bh));
+                      static_cast<const float*>(dval), static_cast<const float*>(e), rhist, P.hcopies, bh,
+                      static_cast<int32_t>(stats ? 0 : 1), dval, didx));
     EF_TRY(launch("topk_write", stats ? k_write<true> : k_write<false>, hgrid, dim3(kBlock), s, plan, nseg, hb,
                   st, static_cast<const uint32_t*>(rhist), P.hcopies, static_cast<const uint32_t*>(bh), hint,
                   static_cast<const float*>(dval), static_cast<const int32_t*>(didx), e, vals, idx, cpart, rpart,
