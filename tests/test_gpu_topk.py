@@ -72,6 +72,24 @@ def test_forced_fallback_many_units():
     check(g, e, k, flags=efg.EF_FLAG_FORCE_FALLBACK, what=f"fallback n={n} k={k}")
 
 
+def test_forced_fallback_mixed_segments():
+    """The exact path's last select pass collects each block's possible
+    survivors (keys with T's top 21 bits or above) into the block's segment;
+    a block whose segment overflows places by reading x again.  Here a
+    stretch of 300,000 copies of T itself overflows the segments of the
+    blocks that cover it while every other block places from its segment,
+    and the r ties kept are the lowest-indexed ones."""
+    n = 2_000_003
+    g = gen.normal_small(n, 211)
+    e = np.zeros(n, np.float32)
+    v = np.float32(3.0)
+    g[700_001:1_000_001] = v
+    k = int((np.abs(g) > v).sum()) + 1000
+    say(f"forced fallback, mixed segments n={n} k={k}")
+    check(g, e, k, flags=efg.EF_FLAG_FORCE_FALLBACK, what="fallback mixed segments")
+    check(g, e, k, what="fast path, same input")
+
+
 def test_clustered_magnitudes_overflow():
     # all large values sit in a few regions: their candidate slots overflow and
     # the rest of their candidates are read again from e
