@@ -215,7 +215,7 @@ struct alignas(16) SegState {
     uint32_t ncand;     // candidates found (compaction)
     uint32_t p0, w0;    // top 11 key bits of T and the rank left below them (first select pass)
     uint32_t p1, w1;    // top 21 bits and the rank left (second select pass)
-    uint32_t T, r;      // the k-th largest key and the ties kept (count pass)
+    uint32_t T, r;      // the k-th largest key and the ties kept (write pass, the first block)
     // exact fallback: the first digits [spec_lo, spec_lo + spec_n) that the
     // sample's window [tlo, thi) spans, whose second-digit histograms the
     // compaction builds with the first one; hit = 1 + the one that held T's
